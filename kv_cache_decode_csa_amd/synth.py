@@ -1,0 +1,189 @@
+"""Seeded synthetic inputs for the five decode workloads.
+
+This module holds data recipes only (shapes, seeds, value distributions and
+the float32 -> bf16 cast of generated values); it contains none of the
+method's arithmetic and imports nothing from the library or the oracle.
+Both the GPU path and the checker draw their inputs from here.
+
+Every tensor has its own stream, keyed by (seed, tensor id, leading index), so
+one sequence of a batch can be regenerated on its own:
+``np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, tid, b])))``.
+Seeds are 20261200 + workload number.
+"""
+
+from dataclasses import dataclass, field
+
+import numpy as np
+
+SEED_BASE = 20261200
+
+# fixed tensor ids
+T_X, T_WKV, T_WGATE, T_APE = 1, 2, 3, 4
+T_IWKV, T_IWGATE, T_IAPE = 5, 6, 7
+T_WINDOW, T_Q, T_QIDX, T_WIDX, T_SINK = 8, 9, 10, 11, 12
+T_ENTRIES, T_IKEYS, T_XTAIL, T_TOPK, T_SCORES = 13, 14, 15, 16, 17
+
+
+@dataclass
+class Workload:
+    """Shape and distribution recipe of one decode workload."""
+    num: int
+    name: str
+    B: int
+    ctx: int                  # tokens of context; the query sits at t = ctx - 1
+    ratio: int                # 4 (CSA) or 128 (HCA)
+    n_entries: int            # compressed entries per sequence = ctx // ratio
+    H: int = 64               # query heads (dim 512)
+    Hi: int = 64              # indexer heads (dim 128)
+    topk: int = 512
+    dim: int = 4096           # hidden size feeding the compressor
+    theta: float = 160000.0
+    yarn: bool = True
+    q_fmt: str = "bf16"       # storage of q / q_idx / outputs
+    ent_fmt: str = "bf16"     # main KV rows
+    win_fmt: str = "bf16"     # window rows
+    key_fmt: str = "bf16"     # index keys
+    kv_std: float = 1.0       # std of entries / window / q
+    ikey_std: float = 1.0
+    extra: dict = field(default_factory=dict)
+
+    @property
+    def t(self):
+        return self.ctx - 1
+
+    @property
+    def seed(self):
+        return SEED_BASE + self.num
+
+
+WORKLOADS = {
+    # tiny whole path from hidden states, fp32
+    1: Workload(1, "csa_tiny_f32", B=1, ctx=2048, ratio=4, n_entries=512, H=16, Hi=4, topk=64,
+                dim=1024, yarn=False, q_fmt="f32", ent_fmt="f32", win_fmt="f32", key_fmt="f32"),
+    # CSA decode, bf16, 64K context, V4-Flash shape with 32 indexer heads
+    2: Workload(2, "csa_64k_bf16", B=32, ctx=65536, ratio=4, n_entries=16384, H=64, Hi=32,
+                topk=512, kv_std=512 ** -0.5),
+    # HCA decode, bf16, 1M context
+    3: Workload(3, "hca_1m_bf16", B=16, ctx=1048576, ratio=128, n_entries=8192, H=64, Hi=0,
+                topk=0),
+    # chunked prefill: 32768 new tokens on a 262144-token prefix
+    4: Workload(4, "csa_prefill_32k_bf16", B=1, ctx=262144 + 32768, ratio=4,
+                n_entries=(262144 + 32768) // 4, H=64, Hi=64, topk=512,
+                extra={"prefix": 262144, "new": 32768}),
+    # quantized CSA decode at 1M: FP8-528 main KV and window, FP8-132 index keys
+    5: Workload(5, "csa_1m_fp8", B=8, ctx=1048576, ratio=4, n_entries=262144, H=64, Hi=64,
+                topk=512, ent_fmt="fp8_mx32", win_fmt="fp8_mx32", key_fmt="fp8_mx32"),
+}
+
+
+def mxfp4_variant(w):
+    """The workload-5 variant whose main KV rows are MXFP4 (E2M1 + E4M3/16)."""
+    import dataclasses
+    return dataclasses.replace(w, name="csa_1m_mxfp4", ent_fmt="fp4_e4m3_16")
+
+
+def rng(seed, tid, idx=0):
+    return np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, tid, idx])))
+
+
+def normal(seed, tid, shape, std=1.0, idx=0):
+    """float32 N(0, std^2) of the given shape from stream (seed, tid, idx)."""
+    g = rng(seed, tid, idx)
+    out = g.standard_normal(size=shape, dtype=np.float32)
+    if std != 1.0:
+        out *= np.float32(std)
+    return out
+
+
+def normal_batched(seed, tid, B, shape, std=1.0, b_range=None):
+    """[len(b_range), *shape]; element b comes from stream (seed, tid, b)."""
+    bs = range(B) if b_range is None else b_range
+    return np.stack([normal(seed, tid, shape, std, idx=b) for b in bs])
+
+
+def bf16_round(x):
+    """Round float32 values to the nearest bf16 (ties to even), as float32."""
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    r = ((u + 0x7FFF + ((u >> 16) & 1)) >> 16) << 16
+    return r.astype(np.uint32).view(np.float32)
+
+
+def as_fmt_values(x, fmt):
+    """Values of generated float32 data as stored before any method codec:
+    bf16 inputs are rounded to bf16; f32 and quantized inputs stay float32
+    (quantized formats are produced by each side's own codec)."""
+    return bf16_round(x) if fmt == "bf16" else np.asarray(x, dtype=np.float32)
+
+
+# ----------------------------------------------------------------------------
+# per-workload tensors (float32 values; bf16 tensors already rounded)
+# ----------------------------------------------------------------------------
+
+def queries(w, b_range=None):
+    """q [B, H, 512] and sink [H]."""
+    q = normal_batched(w.seed, T_Q, w.B, (w.H, 512), w.kv_std, b_range)
+    sink = normal(w.seed, T_SINK, (w.H,))
+    return as_fmt_values(q, w.q_fmt), sink
+
+
+def index_queries(w, b_range=None):
+    """q_idx [B, Hi, 128] and pre-scaled head weights w [B, Hi]."""
+    qi = normal_batched(w.seed, T_QIDX, w.B, (w.Hi, 128), 1.0, b_range)
+    wi = normal_batched(w.seed, T_WIDX, w.B, (w.Hi,), (128 * w.Hi) ** -0.5, b_range)
+    return as_fmt_values(qi, w.q_fmt), wi
+
+
+def window_rows(w, b_range=None):
+    """Raw window ring [B, 128, 512] (stored, already-rotated form)."""
+    return as_fmt_values(normal_batched(w.seed, T_WINDOW, w.B, (128, 512), w.kv_std, b_range),
+                         w.win_fmt)
+
+
+def entries(w, b_range=None):
+    """Compressed main KV [B, N, 512] (stored form, before any codec)."""
+    return as_fmt_values(normal_batched(w.seed, T_ENTRIES, w.B, (w.n_entries, 512), w.kv_std,
+                                        b_range), w.ent_fmt)
+
+
+def index_keys(w, b_range=None):
+    """Index keys [B, N, 128] (stored form, before any codec)."""
+    return as_fmt_values(normal_batched(w.seed, T_IKEYS, w.B, (w.n_entries, 128), w.ikey_std,
+                                        b_range), w.key_fmt)
+
+
+def compressor_weights(w, head_dim, ratio, indexer=False):
+    """W_kv, W_gate [coff*d, dim] ~ N(0, 0.02^2), ape [r, coff*d] ~ N(0, 0.02^2),
+    norm weight ones [d]."""
+    coff = 2 if ratio == 4 else 1
+    tids = (T_IWKV, T_IWGATE, T_IAPE) if indexer else (T_WKV, T_WGATE, T_APE)
+    wkv = normal(w.seed, tids[0], (coff * head_dim, w.dim), 0.02)
+    wg = normal(w.seed, tids[1], (coff * head_dim, w.dim), 0.02)
+    ape = normal(w.seed, tids[2], (ratio, coff * head_dim), 0.02)
+    fmt = w.q_fmt
+    return as_fmt_values(wkv, fmt), as_fmt_values(wg, fmt), ape, np.ones(head_dim, np.float32)
+
+
+def hidden(w, T, idx=0, tid=T_X):
+    """Hidden states [T, dim] ~ N(0, 1) for sequence idx."""
+    return as_fmt_values(normal(w.seed, tid, (T, w.dim), 1.0, idx=idx), w.q_fmt)
+
+
+def random_topk_ids(seed, n_vis, k, n_pad=0, idx=0):
+    """Distinct compressed ids < n_vis in random order, then n_pad -1 slots."""
+    g = rng(seed, T_TOPK, idx)
+    m = min(k - n_pad, n_vis)
+    ids = g.choice(n_vis, size=m, replace=False).astype(np.int32)
+    return np.concatenate([ids, np.full(k - m, -1, np.int32)])
+
+
+def random_scores(seed, n, idx=0, ties=True):
+    """float32 scores with planted exact ties and a signed zero."""
+    g = rng(seed, T_SCORES, idx)
+    s = g.standard_normal(n, dtype=np.float32)
+    if ties and n >= 16:
+        pick = g.choice(n, size=n // 8, replace=False)
+        s[pick] = s[pick[0]]
+        z = g.choice(n, size=4, replace=False)
+        s[z[:2]] = np.float32(0.0)
+        s[z[2:]] = np.float32(-0.0)
+    return s
