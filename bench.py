@@ -1,0 +1,214 @@
+"""Decode-step benchmark: one MI355X, one CSA (or HCA) layer, synthetic data.
+
+Default workload: CSA decode at 1M context with a quantized cache -- batch 8,
+262,144 compressed entries per sequence stored FP8-MX32 (528 B rows), FP8
+index keys (132 B), 64 query heads x 512, 64 indexer heads x 128, top-512,
+128-row FP8 window.  One step = compress the new token (main KV and index
+keys), score every visible index key and select the top 512, then attend over
+the window plus the selection.  All inputs are resident in HBM before timing.
+
+Prints one JSON line.  value = tokens/s per layer = B / step time.  The
+roofline object is for the dominant phase, csa_index_topk (its algorithmic
+bytes are the visible index keys plus q_idx, w and the output ids), timed with
+HIP events on the stream it runs on.  cpu_baseline times the float64 oracle
+(test infrastructure) on a bounded sample of the same workload.
+
+  python bench.py [--steps K] [--warmup W] [--workload csa_1m_fp8|csa_1m_mxfp4|
+                  csa_64k_bf16|hca_1m_bf16] [--copies C] [--no-cpu-baseline]
+"""
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+HBM_PEAK_GBS = 8000.0
+
+WORKLOADS = {"csa_1m_fp8": 5, "csa_1m_mxfp4": 5, "csa_64k_bf16": 2, "hca_1m_bf16": 3}
+
+
+def row_bytes(fmt, dim):
+    return {"f32": 4 * dim, "bf16": 2 * dim, "fp8_mx32": dim + dim // 32,
+            "fp4_e4m3_16": dim // 2 + dim // 16}[fmt]
+
+
+def algorithmic_bytes(w):
+    """Bytes the method must move per step (whole batch), by phase."""
+    B, N = w.B, w.n_entries
+    qb = 2 if w.q_fmt == "bf16" else 4
+    out = {}
+    # compressors: weights once per step, x, slot states read+written, one emitted row
+    dim = w.dim
+    coff = 2 if w.ratio == 4 else 1
+    comp_main = (2 * coff * 512 * dim * qb + B * dim * qb
+                 + 2 * 2 * B * coff * w.ratio * coff * 512 * 4 + B * row_bytes(w.ent_fmt, 512))
+    out["csa_compress_main"] = comp_main
+    if w.ratio == 4:
+        out["csa_compress_index"] = (2 * coff * 128 * dim * qb + B * dim * qb
+                                     + 2 * 2 * B * coff * 4 * coff * 128 * 4
+                                     + B * row_bytes(w.key_fmt, 128))
+        n_vis = min((w.t + 1) // w.ratio, N)
+        out["csa_index_topk"] = B * (n_vis * row_bytes(w.key_fmt, 128) + w.Hi * 128 * qb
+                                     + w.Hi * 4 + w.topk * 4)
+        k = min(w.topk, n_vis)
+        out["csa_sparse_attn_decode"] = B * (k * row_bytes(w.ent_fmt, 512) + k * 4
+                                             + 128 * row_bytes(w.win_fmt, 512)
+                                             + 2 * w.H * 512 * qb) + w.H * 4
+    else:
+        n_vis = min((w.t + 1) // w.ratio, N)
+        out["hca_attn_decode"] = B * (n_vis * row_bytes(w.ent_fmt, 512)
+                                      + 128 * row_bytes(w.win_fmt, 512)
+                                      + 2 * w.H * 512 * qb) + w.H * 4
+    return out
+
+
+def time_steps(layer, steps, torch):
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for _ in range(steps):
+        layer.step()
+    end.record()
+    torch.cuda.synchronize()
+    return start.elapsed_time(end) / steps
+
+
+def time_phases(layer, steps, torch):
+    """Average duration of every phase, each bracketed by events on its stream."""
+    acc = {}
+    pairs = []
+    torch.cuda.synchronize()
+    for _ in range(steps):
+        for name, fn in layer.phases():
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            a.record()
+            fn()
+            b.record()
+            pairs.append((name, a, b))
+        layer.step_no += 1
+    torch.cuda.synchronize()
+    for name, a, b in pairs:
+        acc.setdefault(name, []).append(a.elapsed_time(b))
+    return {k: float(np.mean(v)) for k, v in acc.items()}
+
+
+def cpu_baseline(w, n_seq):
+    """The oracle on n_seq sequences of the workload: decode the stored index
+    keys, score, select, gather and attend (untimed: building the stored
+    bytes with the oracle's codec)."""
+    from kv_cache_decode_csa_amd import synth
+    from oracle import attention, codec, indexer, rope
+    from oracle import topk as TK
+    om = rope.frequencies(160000.0, rope.V4_YARN if w.yarn else None)
+    threads = os.environ.get("OMP_NUM_THREADS") or str(len(os.sched_getaffinity(0)))
+    t_total = 0.0
+    for b in range(n_seq):
+        br = [b]
+        q, sink = synth.queries(w, br)
+        win = synth.window_rows(w, br)[0]
+        ent = synth.entries(w, br)[0]
+        win_st = codec.store(win, w.win_fmt)[0]
+        t = w.t
+        if w.ratio == 4:
+            qi, wi = synth.index_queries(w, br)
+            keys_st = codec.store(synth.index_keys(w, br)[0], w.key_fmt)[0]
+            t0 = time.perf_counter()
+            K = codec.load(keys_st, w.key_fmt, 128)
+            nv = int(indexer.n_visible(t, 4, w.n_entries))
+            S = indexer.scores(qi[0].astype(np.float64), wi[0], K, nv)
+            ids = TK.topk(S.astype(np.float32), w.topk, nv)
+            t_total += time.perf_counter() - t0
+            rows_st = codec.store(ent[np.maximum(ids, 0)], w.ent_fmt)[0]   # the stored rows read
+        else:
+            ids = attention.hca_ids(t, w.ratio, w.n_entries)
+            rows_st = codec.store(ent[ids], w.ent_fmt)[0]
+        t0 = time.perf_counter()
+        E = codec.load(rows_st, w.ent_fmt, 512)
+        Wv = codec.load(win_st, w.win_fmt, 512)
+        wid = attention.window_ids(t)
+        rows = np.concatenate([Wv[np.maximum(wid, 0)], E])
+        valid = np.concatenate([wid >= 0, ids >= 0])
+        attention.attend(q[0].astype(np.float64), rows, valid, sink, 512 ** -0.5, t, om)
+        t_total += time.perf_counter() - t0
+    return {"value": n_seq / t_total, "unit": "tokens/s/layer", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"{n_seq} of {w.B} sequences of the same workload, full context "
+                      f"({w.n_entries} entries each); timed: key decode, scoring, top-k, row "
+                      f"decode and attention in float64 NumPy; {t_total:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="csa_1m_fp8", choices=sorted(WORKLOADS))
+    ap.add_argument("--copies", type=int, default=2,
+                    help="independent cache copies rotated per step (defeats the 256 MB MALL)")
+    ap.add_argument("--cpu-seqs", type=int, default=2)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    a = ap.parse_args()
+    if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(see the sharding note in DESIGN.md); run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from kv_cache_decode_csa_amd import decode, synth
+
+    w = synth.WORKLOADS[WORKLOADS[a.workload]]
+    if a.workload == "csa_1m_mxfp4":
+        w = synth.mxfp4_variant(w)
+    print(f"# building {a.workload}: B={w.B} ctx={w.ctx} entries={w.n_entries}", file=sys.stderr,
+          flush=True)
+    t0 = time.time()
+    Layer = decode.CsaDecodeLayer if w.ratio == 4 else decode.HcaDecodeLayer
+    layer = Layer(w, copies=a.copies)
+    torch.cuda.synchronize()
+    print(f"# inputs resident in {time.time() - t0:.1f} s", file=sys.stderr, flush=True)
+
+    for _ in range(a.warmup):
+        layer.step()
+    ms = time_steps(layer, a.steps, torch)
+    phases = time_phases(layer, a.steps, torch)
+    ab = algorithmic_bytes(w)
+    dom = "csa_index_topk" if w.ratio == 4 else "hca_attn_decode"
+    dom_gbs = ab[dom] / (phases[dom] * 1e-3) / 1e9
+    step_bytes = sum(ab.values())
+    res = {
+        "metric": "CSA top-512 decode tokens/s per layer at 1M ctx; achieved HBM GB/s vs peak",
+        "value": w.B / (ms * 1e-3),
+        "unit": "tokens/s/layer",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "batch": w.B, "context": w.ctx, "entries": w.n_entries,
+                   "heads": w.H, "index_heads": w.Hi, "topk": w.topk, "ratio": w.ratio,
+                   "kv_format": w.ent_fmt, "window_format": w.win_fmt,
+                   "index_key_format": w.key_fmt, "cache_copies": a.copies},
+        "roofline": {"bound": "hbm", "achieved": dom_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": dom_gbs / HBM_PEAK_GBS, "traffic": None, "kernel": dom,
+                     "bytes_per_launch": ab[dom], "ms_per_launch": phases[dom]},
+        "step_hbm_GBps": step_bytes / (ms * 1e-3) / 1e9,
+        "phases_ms": phases,
+        "algorithmic_bytes": ab,
+    }
+    if not a.no_cpu_baseline:
+        print("# cpu baseline (oracle)", file=sys.stderr, flush=True)
+        res["cpu_baseline"] = cpu_baseline(w, a.cpu_seqs)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,240 @@
+/*
+ * libcsa -- DeepSeek-V4-style compressed-attention decode for one layer on
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The method is the one described in "DeepSeek-V4 deep dive" (gangliao.me):
+ *   - a learned gated-pooling compressor turns every m = 4 (CSA) or m = 128
+ *     (HCA) tokens into one 512-d entry that is both key and value for all
+ *     query heads (sections 3.1, 4.1-4.3);
+ *   - a lightning indexer scores every completed entry with 128-d index heads
+ *     and keeps the top k (section 5.2);
+ *   - shared-KV multi-query attention runs one softmax with a per-head sink over
+ *     the raw 128-token window plus the selected entries, with RoPE on the last
+ *     64 dims undone on the output (sections 3.3, 3.4 Eq. 27, 5.3, 6.1).
+ * Cache row formats follow the V4-Flash model record (528 B FP8 rows, 288 B
+ * FP4 rows) and the V4.1-Flash diagram page (E2M1 + E4M3 scale per 16).
+ *
+ * Conventions for every entry point
+ *   - Pointers are DEVICE pointers unless marked (host).  The caller owns every
+ *     buffer; the library never allocates or frees and keeps no state between
+ *     calls.  Scratch memory is passed in as a workspace sized by the matching
+ *     *_workspace_size() call.
+ *   - Tensors are dense, row-major, last dimension contiguous, and must start
+ *     on a 16-byte boundary.
+ *   - Work is enqueued on `stream`; calls return without synchronising.
+ *   - Arguments are validated on the host before anything is enqueued.  On a
+ *     validation failure nothing is written, the return value is non-zero and
+ *     csa_last_error_detail() describes the problem.  A failed launch returns
+ *     CSA_ELAUNCH.  Nothing throws across this interface.  Calls are
+ *     thread-safe; the error detail is per thread.
+ *   - Values stored in device memory cannot be checked on the host.  Position
+ *     arrays and index lists are clamped or masked by the kernels as stated per
+ *     function; they never cause an out-of-bounds access.
+ *   - Results are bitwise reproducible run to run and batch-invariant: the
+ *     output for one sequence does not depend on the batch it is part of.
+ *   - Positions are absolute token positions (0-based).  Compressed entry ids
+ *     are 0-based in compressed space; -1 means "no row".
+ */
+#ifndef CSA_H_
+#define CSA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct ihipStream_t* csa_stream_t; /* a hipStream_t; NULL = default stream */
+typedef int csa_status;
+
+enum {
+  CSA_OK = 0,
+  CSA_EINVAL = 1,       /* bad argument (null pointer, size, alignment)        */
+  CSA_EUNSUPPORTED = 2, /* valid but unsupported combination of formats/shapes */
+  CSA_EWORKSPACE = 3,   /* workspace missing or smaller than required          */
+  CSA_ELAUNCH = 4       /* a kernel launch failed                              */
+};
+
+/* Storage formats of a row of `dim` values. */
+enum {
+  CSA_F32 = 0,          /* 4*dim bytes                                                   */
+  CSA_BF16 = 1,         /* 2*dim bytes                                                   */
+  CSA_FP8_MX32 = 2,     /* dim OCP-E4M3FN codes, then dim/32 E8M0 scale bytes (e + 127):
+                           528 B for dim 512, 132 B for dim 128                          */
+  CSA_FP4_E4M3_16 = 3   /* dim/2 bytes of E2M1 codes (element 2j in the low nibble of
+                           byte j), then dim/16 E4M3 scale bytes: 288 B for dim 512      */
+};
+
+/* Addressing of the raw sliding-window rows. */
+enum {
+  CSA_WIN_RING128 = 0,  /* decode: the row of position p is p mod 128 of a 128-row ring  */
+  CSA_WIN_LINEAR = 1    /* prefill: the row of position p is p - win_base[b]             */
+};
+
+const char* csa_strerror(csa_status s);
+/* Text of the last failure on the calling thread ("" when none). */
+const char* csa_last_error_detail(void);
+/* Bytes per row of `dim` values in `fmt`; 0 if the pair is invalid. */
+size_t kv_row_bytes(int fmt, int dim);
+
+/* ------------------------------------------------------------------------ RoPE
+ * cos/sin table for the partial RoPE of "DeepSeek-V4 deep dive" section 3.3 and
+ * the YaRN settings of section 9.1.  Pair k (dims D-64+2k, D-64+2k+1 of a row)
+ * turns by angle p * omega_k with omega_k = theta^(-2k/64); when yarn_factor > 0
+ * the frequencies are blended as omega' = omega/factor*(1-s) + omega*s with
+ * s = 1 - clamp((k-lo)/(hi-lo), 0, 1) and (lo, hi) the YaRN correction range
+ * of (beta_fast, beta_slow) over yarn_orig_len positions.  The angle is
+ * formed in double precision and cos/sin are rounded once to float.
+ * Writes cos_out[rows][32] and sin_out[rows][32] (device) for positions
+ * 0 .. rows-1.  Errors: CSA_EINVAL for null outputs, rows < 1, theta <= 1.   */
+csa_status csa_rope_table(double theta, double yarn_factor, int64_t yarn_orig_len,
+                          double beta_fast, double beta_slow, int64_t rows, float* cos_out,
+                          float* sin_out, csa_stream_t stream);
+
+/* ------------------------------------------------------------------------ codec
+ * Storage rounding of cache rows (the FP8 / FP4 row layouts of the V4-Flash
+ * model record; V4.1 page: E2M1 with an E4M3 scale per 16 channels).
+ * kv_quantize: src [rows][dim] in CSA_F32 or CSA_BF16 -> dst rows in dst_fmt
+ *   (any format).  FP8_MX32: per 32 values the scale is 2^e with e the smallest
+ *   integer such that max|x| <= 448 * 2^e (clamped to [-127,127]; all-zero
+ *   groups use -127); codes are x * 2^-e rounded to nearest even E4M3FN,
+ *   saturating at +-448.  FP4_E4M3_16: per 16 values scale = E4M3(RNE(max|x| /
+ *   6)) in IEEE float32, codes = RNE onto the E2M1 grid of x / scale, ties to
+ *   the even code, saturating at 6; a zero scale gives zero codes.  NaN or Inf
+ *   inputs become NaN codes (FP8) or a NaN scale (FP4) so that they propagate.
+ * kv_dequantize: src rows in src_fmt -> dst [rows][dim] in CSA_F32 or CSA_BF16
+ *   (bf16 rounds to nearest even).
+ * dim must be a positive multiple of 32 (of 128 for FP8_MX32, whose rows must
+ * stay 4-byte aligned).  rows may be 0 (no work).                           */
+csa_status kv_quantize(const void* src, int src_fmt, void* dst, int dst_fmt, int64_t rows,
+                       int dim, csa_stream_t stream);
+csa_status kv_dequantize(const void* src, int src_fmt, void* dst, int dst_fmt, int64_t rows,
+                         int dim, csa_stream_t stream);
+
+/* ------------------------------------------------------------------------ compressor
+ * "DeepSeek-V4 deep dive" sections 4.1-4.3 and 5.2.  For each token at
+ * position p = start_pos[b] + i (i < T) of sequence b:
+ *   v = W_kv x,  s = W_gate x + ape[p mod ratio]          (each coff*head_dim wide)
+ * The projections are written into the caller's slot state (layout below).
+ * Whenever a block completes ((p+1) mod ratio == 0) entry p/ratio is emitted:
+ *   ratio 4 (overlap, coff 2): 8 slots = previous block's tokens on channels
+ *     [0, d) followed by the current block's tokens on channels [d, 2d);
+ *   ratio 128 (coff 1): the block's 128 tokens;  ratio 1: the single token;
+ *   C_c = sum_j softmax_j(s_{j,c}) v_{j,c}  per channel, in float32;
+ *   y = C / sqrt(mean(C^2) + eps) * norm_w;  RoPE on the last 64 dims at
+ *   position (p/ratio)*ratio;  if rotate: y = H y / sqrt(head_dim) with H the
+ *   Sylvester Hadamard matrix (head_dim 128 index keys only);  then storage
+ *   rounding to entry_fmt, written to entries[b][p/ratio] (skipped when
+ *   p/ratio >= entries_cap).
+ * Slot state (in/out, float32, [B][coff*ratio][coff*head_dim] each): the slot
+ * of position p is ratio + p mod ratio when coff == 2, else p mod ratio.  On a
+ * completed block with coff == 2 the current slots are copied into the
+ * previous slots [0, ratio).  A fresh state is kv = 0 and score = -inf.
+ * Positions before start_pos[b] are taken from the state as it holds them.
+ * x: [B][T][dim] in x_fmt (F32 or BF16); w_kv, w_gate: [coff*head_dim][dim] in
+ * w_fmt (F32 or BF16); ape: [ratio][coff*head_dim] float; norm_w: [head_dim]
+ * float; rope tables [rope_rows][32] float (positions beyond rope_rows - 1 are
+ * clamped to the last row); start_pos: [B] int32.
+ * Requirements: ratio in {1, 4, 128}; head_dim in {128, 512}; rotate only with
+ * head_dim 128; dim % 32 == 0; entry_fmt any; B >= 1, T >= 1.            */
+typedef struct {
+  int B, T, dim, ratio, head_dim, rotate;
+  const void* x;
+  int x_fmt;
+  const void* w_kv;
+  const void* w_gate;
+  int w_fmt;
+  const float* ape;
+  const float* norm_w;
+  float eps;
+  const float* rope_cos;
+  const float* rope_sin;
+  int64_t rope_rows;
+  const int32_t* start_pos;
+  float* kv_state;
+  float* score_state;
+  void* entries;
+  int entry_fmt;
+  int64_t entries_cap;
+} csa_compress_args;
+
+size_t csa_compress_workspace_size(const csa_compress_args* a);
+csa_status csa_compress(const csa_compress_args* a, void* ws, size_t ws_bytes,
+                        csa_stream_t stream);
+
+/* ------------------------------------------------------------------------ indexer + top-k
+ * "DeepSeek-V4 deep dive" section 5.2:  for query (b, q) at position
+ * pos[b][q] the visible blocks are s < n_vis = min(floor((pos+1)/ratio), Nmax);
+ *   score[s] = sum_h w[b][q][h] * max(0, q_idx[b][q][h] . k[b][s])
+ * computed with float32 accumulation (bf16 products are exact in float32;
+ * FP8 keys are decoded exactly), then the top min(topk, n_vis) entries are
+ * returned in out_idx[b][q][0..topk) ordered by descending score, equal scores
+ * by ascending index, -0 == +0, NaN last; the remaining slots hold -1.
+ * q_idx: [B][Q][Hi][128] in q_fmt (F32 or BF16); w_idx: [B][Q][Hi] float, with
+ * the 128^-1/2 * Hi^-1/2 factor already applied; k_idx: [B][Nmax] rows of 128
+ * values in k_fmt (F32, BF16 or FP8_MX32 = 132 B); pos: [B][Q] int32.
+ * out_scores (nullable): [B][Q][Nmax] float, entries s < n_vis are written.
+ * Requirements: Hi % 16 == 0 and Hi <= 128 (any Hi for F32); 1 <= topk <= 2048;
+ * k_fmt F32 requires q_fmt F32 and BF16/FP8 require q_fmt BF16.             */
+size_t csa_index_topk_workspace_size(int B, int Q, int64_t Nmax, int topk);
+csa_status csa_index_topk(const void* q_idx, int q_fmt, const float* w_idx, const void* k_idx,
+                          int k_fmt, const int32_t* pos, int ratio, int B, int Q, int Hi,
+                          int64_t Nmax, int topk, int32_t* out_idx, float* out_scores, void* ws,
+                          size_t ws_bytes, csa_stream_t stream);
+
+/* Top-k alone over given float32 scores [R][ld]: row r ranks its first
+ * n_valid[r] entries (clamped to [0, ld]) with the same order rule as above.
+ * Requirements: 1 <= topk <= 2048, ld >= 1.                                  */
+size_t csa_topk_workspace_size(int64_t R, int64_t ld, int topk);
+csa_status csa_topk(const float* scores, const int32_t* n_valid, int64_t R, int64_t ld, int topk,
+                    int32_t* out_idx, void* ws, size_t ws_bytes, csa_stream_t stream);
+
+/* ------------------------------------------------------------------------ attention
+ * Shared-KV MQA with a sink ("DeepSeek-V4 deep dive" section 3.4, Eq. 27) over
+ * the list [128 window rows ; selected entries] of each query unit (b, q):
+ *   window row j (0..127) is position t-127+j with t = pos[b][q]; it is absent
+ *   when that position is negative, else read from win[b] at row
+ *   (position mod 128) in CSA_WIN_RING128 mode or (position - win_base[b]) in
+ *   CSA_WIN_LINEAR mode (absent when outside [0, win_rows));
+ *   csa_sparse_attn_decode: entry rows topk_idx[b][q][0..topk), -1 or any id
+ *   outside [0, Nmax) is absent;
+ *   hca_attn_decode: entry rows 0 .. min(floor((t+1)/ratio), Nmax) - 1.
+ * Per head h, with q' = RoPE(q[b][q][h], t) on the last 64 dims and rows c_j
+ * in stored (already rotated) form:
+ *   z_j = (q' . c_j) * scale,  m = max_j z_j,
+ *   o = sum_j e^{z_j - m} c_j / (sum_j e^{z_j - m} + e^{sink[h] - m}),
+ *   out = RoPE^-1(o, t) on the last 64 dims   (duplicates are kept);
+ * no present row gives out = 0.  Products use bf16 MFMA with float32
+ * accumulation (the softmax weights are rounded to bf16 for the second
+ * product) except for q_fmt F32, which runs in float32 throughout.
+ * q: [B][Q][H][512] in q_fmt (F32 or BF16), passed UN-rotated; win: [B][win_rows]
+ * rows of 512 in win_fmt; entries: [B][Nmax] rows of 512 in ent_fmt; formats
+ * F32 (only with q_fmt F32), BF16, FP8_MX32, FP4_E4M3_16; sink: [H] float;
+ * rope tables [rope_rows][32] (positions clamped to the last row); out:
+ * [B][Q][H][512] in out_fmt (F32 or BF16, rounded once).
+ * Requirements: H % 16 == 0; win_rows >= 128 in ring mode; 0 <= topk <= 8192.
+ */
+size_t csa_sparse_attn_workspace_size(int B, int Q, int H, int topk);
+csa_status csa_sparse_attn_decode(const void* q, int q_fmt, const void* win, int win_fmt,
+                                  int win_mode, const int32_t* win_base, int64_t win_rows,
+                                  const void* entries, int ent_fmt, int64_t Nmax,
+                                  const int32_t* topk_idx, int topk, const int32_t* pos, int B,
+                                  int Q, int H, const float* sink, float scale,
+                                  const float* rope_cos, const float* rope_sin, int64_t rope_rows,
+                                  void* out, int out_fmt, void* ws, size_t ws_bytes,
+                                  csa_stream_t stream);
+
+size_t hca_attn_workspace_size(int B, int Q, int H, int64_t Nmax);
+csa_status hca_attn_decode(const void* q, int q_fmt, const void* win, int win_fmt, int win_mode,
+                           const int32_t* win_base, int64_t win_rows, const void* entries,
+                           int ent_fmt, int64_t Nmax, int ratio, const int32_t* pos, int B, int Q,
+                           int H, const float* sink, float scale, const float* rope_cos,
+                           const float* rope_sin, int64_t rope_rows, void* out, int out_fmt,
+                           void* ws, size_t ws_bytes, csa_stream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* CSA_H_ */

@@ -1,0 +1,76 @@
+// Internal declarations shared by the host API (api.cpp) and the kernel files.
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime.h>
+
+#include "../../include/csa.h"
+
+namespace csa {
+
+constexpr int kWindow = 128;      // raw sliding window rows per query
+constexpr int kHeadDim = 512;     // main KV / query head width
+constexpr int kIndexDim = 128;    // indexer head width
+constexpr int kRopeDims = 64;     // rotated tail of every head
+constexpr int kTopkMax = 2048;    // largest k handled by the selection kernels
+constexpr int kHistBins = 4096;   // first radix digit: key bits 31..20
+constexpr int kCandCap = 8192;    // boundary-bin candidates kept per row
+
+inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+// ---- launchers (kernel files); each returns hipSuccess or the launch error
+hipError_t launch_rope_table(const double* omega_host, int64_t rows, float* cos_out,
+                             float* sin_out, hipStream_t s);
+
+hipError_t launch_quantize(const void* src, int src_fmt, void* dst, int dst_fmt, int64_t rows,
+                           int dim, hipStream_t s);
+hipError_t launch_dequantize(const void* src, int src_fmt, void* dst, int dst_fmt, int64_t rows,
+                             int dim, hipStream_t s);
+
+// top-k workspace layout for R rows
+struct TopkWs {
+  uint32_t* hist;    // [R][kHistBins]
+  uint32_t* ctr;     // [R][4]: n_hi, n_eq, done, pad
+  uint32_t* cand;    // [R][kCandCap][2] (key, idx) for the boundary bin
+  uint32_t* hi;      // [R][kTopkMax][2] (key, idx) above the boundary bin
+};
+size_t topk_ws_bytes(int64_t R);
+TopkWs topk_ws_carve(void* ws, int64_t R);
+
+hipError_t launch_topk_clear(TopkWs w, int64_t R, hipStream_t s);
+hipError_t launch_topk_hist(const float* scores, const int32_t* n_valid, int64_t R, int64_t ld,
+                            TopkWs w, hipStream_t s);
+hipError_t launch_topk_select(const float* scores, const int32_t* n_valid, int64_t R, int64_t ld,
+                              int topk, int32_t* out_idx, TopkWs w, hipStream_t s);
+
+// indexer scores: writes scores[row][s] for s < n_vis and the radix histogram
+hipError_t launch_index_scores(const void* q_idx, int q_fmt, const float* w_idx,
+                               const void* k_idx, int k_fmt, const int32_t* pos, int ratio, int B,
+                               int Q, int Hi, int64_t Nmax, float* scores, int32_t* n_vis,
+                               TopkWs w, hipStream_t s);
+
+struct AttnArgs {
+  const void* q; int q_fmt;
+  const void* win; int win_fmt; int win_mode; const int32_t* win_base; int64_t win_rows;
+  const void* entries; int ent_fmt; int64_t Nmax;
+  int dense;                           // 0: top-k list (CSA), 1: all completed entries (HCA)
+  const int32_t* topk_idx; int topk;   // CSA list
+  int ratio;                           // HCA visibility ratio
+  const int32_t* pos; int B, Q, H;
+  const float* sink; float scale;
+  const float* rope_cos; const float* rope_sin; int64_t rope_rows;
+  void* out; int out_fmt;
+  size_t win_rb, ent_rb;               // row bytes (set by the launcher)
+  int64_t unit_off;                    // first unit of a sub-grid (set by the launcher)
+};
+int attn_chunk_rows(const AttnArgs& a);            // rows per work-group chunk
+int64_t attn_list_len(const AttnArgs& a);          // max rows in a unit's list
+size_t attn_ws_bytes(const AttnArgs& a);
+hipError_t launch_attention(const AttnArgs& a, void* ws, hipStream_t s);
+
+size_t compress_ws_bytes(const csa_compress_args* a);
+hipError_t launch_compress(const csa_compress_args* a, void* ws, hipStream_t s);
+
+}  // namespace csa

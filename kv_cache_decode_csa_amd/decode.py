@@ -1,0 +1,213 @@
+"""One decode step of a CSA or HCA layer, driven through the C ABI.
+
+This module owns device buffers (torch tensors) and calls the library's entry
+points in order; it computes nothing itself.  A CSA step at position t is:
+
+  csa_compress (main KV, ratio 4, 512 wide)        -> maybe emits entry t//4
+  csa_compress (index keys, ratio 4, 128 wide, rotated)
+  csa_index_topk                                   -> top-k entry ids
+  csa_sparse_attn_decode                           -> [B, H, 512]
+
+and an HCA step is csa_compress (ratio 128) followed by hca_attn_decode.
+"""
+
+import torch
+
+from . import _lib
+from . import synth
+
+
+def _dev_rows(x, fmt, device):
+    """float32 host values -> device rows in fmt (quantized by the library)."""
+    src = torch.from_numpy(x).to(device)
+    if fmt == "f32":
+        return src
+    if fmt == "bf16":
+        return src.to(torch.bfloat16)
+    D = x.shape[-1]
+    rb = _lib.kv_row_bytes(fmt, D)
+    out = torch.empty(x.shape[:-1] + (rb,), dtype=torch.uint8, device=device)
+    _lib.kv_quantize(src, "f32", out, fmt, src.numel() // D, D)
+    return out
+
+
+class Compressor:
+    """Weights, slot state and output rows of one compressor on the device."""
+
+    def __init__(self, w, head_dim, ratio, rotate, entries, entry_fmt, rope, device="cuda",
+                 indexer=False):
+        wkv, wg, ape, norm = synth.compressor_weights(w, head_dim, ratio, indexer=indexer)
+        dt = torch.bfloat16 if w.q_fmt == "bf16" else torch.float32
+        self.wkv = torch.from_numpy(wkv).to(device).to(dt)
+        self.wg = torch.from_numpy(wg).to(device).to(dt)
+        self.ape = torch.from_numpy(ape).to(device)
+        self.norm = torch.from_numpy(norm).to(device)
+        coff = 2 if ratio == 4 else 1
+        shape = (w.B, coff * ratio, coff * head_dim)
+        self.kv = torch.zeros(shape, dtype=torch.float32, device=device)
+        self.sc = torch.full(shape, float("-inf"), dtype=torch.float32, device=device)
+        self.w, self.head_dim, self.ratio, self.rotate = w, head_dim, ratio, rotate
+        self.entries, self.entry_fmt = entries, entry_fmt
+        self.cos, self.sin = rope
+        self.x_fmt = w.q_fmt
+        self._ws = None
+
+    def args(self, x, start_pos):
+        B, T = x.shape[0], x.shape[1]
+        return _lib.make_compress_args(
+            B=B, T=T, dim=self.w.dim, ratio=self.ratio, head_dim=self.head_dim,
+            rotate=self.rotate, x=x, x_fmt=self.x_fmt, w_kv=self.wkv, w_gate=self.wg,
+            w_fmt=self.x_fmt, ape=self.ape, norm_w=self.norm, eps=1e-6, rope_cos=self.cos,
+            rope_sin=self.sin, start_pos=start_pos, kv_state=self.kv, score_state=self.sc,
+            entries=self.entries, entry_fmt=self.entry_fmt, entries_cap=self.entries.shape[1])
+
+    def __call__(self, x, start_pos):
+        a = self.args(x, start_pos)
+        need = _lib.csa_compress_workspace_size(a)
+        if self._ws is None or self._ws.numel() < need:
+            self._ws = _lib.workspace(need)
+        _lib.csa_compress(a, self._ws)
+
+
+def rope_tables(rows, yarn, device="cuda"):
+    cos = torch.empty((rows, 32), dtype=torch.float32, device=device)
+    sin = torch.empty_like(cos)
+    if yarn:
+        _lib.csa_rope_table(160000.0, 16.0, 65536, 32.0, 1.0, rows, cos, sin)
+    else:
+        _lib.csa_rope_table(160000.0, 0.0, 0, 0.0, 0.0, rows, cos, sin)
+    return cos, sin
+
+
+class CsaDecodeLayer:
+    """All device state of a CSA layer decoding one token per sequence."""
+
+    def __init__(self, w, device="cuda", copies=1, hidden_tail=7):
+        self.w = w
+        B, N = w.B, w.n_entries
+        self.rope = rope_tables(w.ctx + 1, w.yarn, device)
+        # cache contents: N(0,1) rows stored in the workload's formats; `copies`
+        # independent sets rotate between steps so no step reuses the last one's
+        # lines from the 256 MB last-level cache
+        ent = _dev_rows(synth.entries(w), w.ent_fmt, device)
+        keys = _dev_rows(synth.index_keys(w), w.key_fmt, device)
+        self.sets = [(ent, keys)] + [(ent.clone(), keys.clone()) for _ in range(copies - 1)]
+        self.win = _dev_rows(synth.window_rows(w), w.win_fmt, device)
+        q, sink = synth.queries(w)
+        qi, wi = synth.index_queries(w)
+        qdt = torch.bfloat16 if w.q_fmt == "bf16" else torch.float32
+        self.q = torch.from_numpy(q).to(device).to(qdt).reshape(B, 1, w.H, 512)
+        self.sink = torch.from_numpy(sink).to(device)
+        self.qi = torch.from_numpy(qi).to(device).to(qdt).reshape(B, 1, w.Hi, 128)
+        self.wi = torch.from_numpy(wi).to(device).reshape(B, 1, w.Hi)
+        self.t = w.t
+        self.pos = torch.full((B, 1), self.t, dtype=torch.int32, device=device)
+        self.start = torch.full((B,), self.t, dtype=torch.int32, device=device)
+        self.x = torch.from_numpy(
+            synth.normal_batched(w.seed, synth.T_X, B, (1, w.dim))).to(device).to(qdt)
+        self.topk = torch.empty((B, 1, w.topk), dtype=torch.int32, device=device)
+        self.out = torch.empty((B, 1, w.H, 512), dtype=qdt, device=device)
+        self.ws_idx = _lib.workspace(_lib.csa_index_topk_workspace_size(B, 1, N, w.topk))
+        self.ws_att = _lib.workspace(_lib.csa_sparse_attn_workspace_size(B, 1, w.H, w.topk))
+        self.comp = []
+        for c in range(copies):
+            ent, keys = self.sets[c]
+            self.comp.append((
+                Compressor(w, 512, w.ratio, 0, ent, w.ent_fmt, self.rope, device),
+                Compressor(w, 128, w.ratio, 1, keys, w.key_fmt, self.rope, device, indexer=True)))
+        # fill the compressor states from the tokens before t (positions t-7 .. t-1)
+        if hidden_tail:
+            tail = torch.from_numpy(synth.normal_batched(
+                w.seed, synth.T_XTAIL, B, (hidden_tail, w.dim))).to(device).to(qdt)
+            st = torch.full((B,), self.t - hidden_tail, dtype=torch.int32, device=device)
+            for cm, ci in self.comp:
+                cm(tail, st)
+                ci(tail, st)
+        self.step_no = 0
+
+    def phases(self):
+        """The step as a list of (name, callable) in stream order."""
+        w = self.w
+        c = self.step_no % len(self.sets)
+        ent, keys = self.sets[c]
+        cm, ci = self.comp[c]
+        win_fmt, ent_fmt, key_fmt = w.win_fmt, w.ent_fmt, w.key_fmt
+        B, N = w.B, w.n_entries
+
+        def compress_main():
+            cm(self.x, self.start)
+
+        def compress_index():
+            ci(self.x, self.start)
+
+        def index_topk():
+            _lib.csa_index_topk(self.qi, w.q_fmt, self.wi, keys, key_fmt, self.pos, w.ratio, B, 1,
+                                w.Hi, N, w.topk, self.topk, None, self.ws_idx)
+
+        def sparse_attn():
+            _lib.csa_sparse_attn_decode(self.q, w.q_fmt, self.win, win_fmt, _lib.WIN_RING128,
+                                        None, 128, ent, ent_fmt, N, self.topk, w.topk, self.pos, B,
+                                        1, w.H, self.sink, 512 ** -0.5, self.rope[0],
+                                        self.rope[1], self.out, w.q_fmt, self.ws_att)
+
+        return [("csa_compress_main", compress_main), ("csa_compress_index", compress_index),
+                ("csa_index_topk", index_topk), ("csa_sparse_attn_decode", sparse_attn)]
+
+    def step(self):
+        for _, f in self.phases():
+            f()
+        self.step_no += 1
+
+
+class HcaDecodeLayer:
+    """All device state of an HCA layer decoding one token per sequence."""
+
+    def __init__(self, w, device="cuda", copies=1, hidden_tail=7):
+        self.w = w
+        B, N = w.B, w.n_entries
+        self.rope = rope_tables(w.ctx + 1, w.yarn, device)
+        ent = _dev_rows(synth.entries(w), w.ent_fmt, device)
+        self.sets = [ent] + [ent.clone() for _ in range(copies - 1)]
+        self.win = _dev_rows(synth.window_rows(w), w.win_fmt, device)
+        q, sink = synth.queries(w)
+        qdt = torch.bfloat16 if w.q_fmt == "bf16" else torch.float32
+        self.q = torch.from_numpy(q).to(device).to(qdt).reshape(B, 1, w.H, 512)
+        self.sink = torch.from_numpy(sink).to(device)
+        self.t = w.t
+        self.pos = torch.full((B, 1), self.t, dtype=torch.int32, device=device)
+        self.start = torch.full((B,), self.t, dtype=torch.int32, device=device)
+        self.x = torch.from_numpy(
+            synth.normal_batched(w.seed, synth.T_X, B, (1, w.dim))).to(device).to(qdt)
+        self.out = torch.empty((B, 1, w.H, 512), dtype=qdt, device=device)
+        self.ws_att = _lib.workspace(_lib.hca_attn_workspace_size(B, 1, w.H, N))
+        self.comp = [Compressor(w, 512, w.ratio, 0, e, w.ent_fmt, self.rope, device)
+                     for e in self.sets]
+        if hidden_tail:
+            tail = torch.from_numpy(synth.normal_batched(
+                w.seed, synth.T_XTAIL, B, (hidden_tail, w.dim))).to(device).to(qdt)
+            st = torch.full((B,), self.t - hidden_tail, dtype=torch.int32, device=device)
+            for cm in self.comp:
+                cm(tail, st)
+        self.step_no = 0
+
+    def phases(self):
+        w = self.w
+        c = self.step_no % len(self.sets)
+        ent = self.sets[c]
+        cm = self.comp[c]
+
+        def compress_main():
+            cm(self.x, self.start)
+
+        def hca_attn():
+            _lib.hca_attn_decode(self.q, w.q_fmt, self.win, w.win_fmt, _lib.WIN_RING128, None, 128,
+                                 ent, w.ent_fmt, w.n_entries, w.ratio, self.pos, w.B, 1, w.H,
+                                 self.sink, 512 ** -0.5, self.rope[0], self.rope[1], self.out,
+                                 w.q_fmt, self.ws_att)
+
+        return [("csa_compress_main", compress_main), ("hca_attn_decode", hca_attn)]
+
+    def step(self):
+        for _, f in self.phases():
+            f()
+        self.step_no += 1

@@ -28,13 +28,19 @@ from . import rope as _rope
 WINDOW = 128
 
 
-def window_ids(t, mode="ring", base=0, window=WINDOW):
-    """Window row ids for a query at position t (-1 where position < 0)."""
+def window_ids(t, mode="ring", base=0, window=WINDOW, n_rows=None):
+    """Window row ids for a query at position t (-1 where position < 0).
+
+    ring: row = position mod window; linear: row = position - base, and -1
+    when that row falls outside [0, n_rows) (reading: a row the buffer does
+    not hold is absent, like a -1 id)."""
     p = t - (window - 1) + np.arange(window)
     if mode == "ring":
         ids = np.where(p >= 0, p % window, -1)
     elif mode == "linear":
         ids = np.where(p >= 0, p - base, -1)
+        if n_rows is not None:
+            ids = np.where((ids >= 0) & (ids < n_rows), ids, -1)
     else:
         raise ValueError(mode)
     return ids.astype(np.int64)

@@ -1,0 +1,152 @@
+"""The C-ABI library loads, exports every symbol include/csa.h declares, and
+rejects bad arguments on the host before touching a GPU (CPU only)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from kv_cache_decode_csa_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "csa.h")
+
+if not os.path.exists(_lib.LIB_PATH):
+    pytest.skip("libcsa.so not built (python -m kv_cache_decode_csa_amd.build)",
+                allow_module_level=True)
+
+EINVAL, EUNSUP, EWS = 1, 2, 3
+A16 = 0x10000  # a fake, 16-byte aligned address: validation never dereferences it
+
+
+def declared():
+    text = open(HEADER).read()
+    names = re.findall(r"^\s*(?:csa_status|size_t|const char\*)\s+(\w+)\s*\(", text, re.M)
+    return sorted(set(names))
+
+
+def test_header_symbols_exported():
+    L = _lib.lib()
+    names = declared()
+    assert len(names) >= 16
+    for n in names:
+        assert hasattr(L, n), n
+    # the binding wraps exactly the declared entry points
+    assert sorted(_lib.EXPORTS) == names
+
+
+def test_row_bytes_and_strings():
+    L = _lib.lib()
+    assert L.kv_row_bytes(_lib.FP8_MX32, 512) == 528
+    assert L.kv_row_bytes(_lib.FP4_E4M3_16, 512) == 288
+    assert L.kv_row_bytes(_lib.FP8_MX32, 128) == 132
+    assert L.kv_row_bytes(_lib.BF16, 512) == 1024
+    assert L.kv_row_bytes(_lib.FP8_MX32, 100) == 0
+    assert L.kv_row_bytes(9, 512) == 0
+    assert L.csa_strerror(0) == b"ok"
+    assert L.csa_strerror(3) == b"workspace too small"
+
+
+def _detail():
+    return _lib.lib().csa_last_error_detail().decode()
+
+
+def test_codec_validation():
+    L = _lib.lib()
+    assert L.kv_quantize(None, 0, A16, 2, 4, 512, None) == EINVAL
+    assert "src" in _detail()
+    assert L.kv_quantize(A16, 0, A16, 2, 4, 500, None) == EINVAL       # dim % 32
+    assert L.kv_quantize(A16, 2, A16, 2, 4, 512, None) == EUNSUP       # src must be F32/BF16
+    assert L.kv_quantize(A16, 0, A16, 7, 4, 512, None) == EUNSUP
+    assert L.kv_quantize(A16 + 4, 0, A16, 2, 4, 512, None) == EINVAL  # misaligned
+    assert L.kv_quantize(None, 0, None, 2, 0, 512, None) == 0          # empty: no work
+    assert L.kv_dequantize(A16, 2, A16, 2, 4, 512, None) == EUNSUP     # dst must be F32/BF16
+
+
+def test_topk_validation():
+    L = _lib.lib()
+    assert L.csa_topk(A16, A16, 4, 100, 0, A16, A16, 1 << 30, None) == EUNSUP      # topk 0
+    assert L.csa_topk(A16, A16, 4, 100, 4096, A16, A16, 1 << 30, None) == EUNSUP   # > max
+    assert L.csa_topk(A16, A16, 4, 0, 8, A16, A16, 1 << 30, None) == EINVAL        # ld
+    need = L.csa_topk_workspace_size(4, 100, 8)
+    assert need > 0
+    assert L.csa_topk(A16, A16, 4, 100, 8, A16, A16, need - 1, None) == EWS
+    assert L.csa_topk(A16, A16, 4, 100, 8, A16, None, need, None) == EWS
+
+
+def test_index_topk_validation():
+    L = _lib.lib()
+    ws = L.csa_index_topk_workspace_size(2, 1, 1000, 64)
+    args = lambda **kw: dict(dict(q=A16, qf=1, w=A16, k=A16, kf=2, pos=A16, ratio=4, B=2, Q=1,
+                                  Hi=64, N=1000, topk=64, out=A16, sc=None, ws=A16, wsb=ws), **kw)
+
+    def call(d):
+        return L.csa_index_topk(d["q"], d["qf"], d["w"], d["k"], d["kf"], d["pos"], d["ratio"],
+                                d["B"], d["Q"], d["Hi"], d["N"], d["topk"], d["out"], d["sc"],
+                                d["ws"], d["wsb"], None)
+
+    assert call(args(Hi=24)) == EUNSUP          # multiple of 16 on the MFMA path
+    assert call(args(Hi=256)) == EUNSUP
+    assert call(args(kf=3)) == EUNSUP           # FP4 keys: not on this path
+    assert call(args(qf=0)) == EUNSUP           # bf16/fp8 keys need bf16 queries
+    assert call(args(kf=0)) == EUNSUP           # f32 keys need f32 queries
+    assert call(args(topk=0)) == EUNSUP
+    assert call(args(N=0)) == EINVAL
+    assert call(args(q=None)) == EINVAL
+    assert call(args(wsb=ws - 1)) == EWS
+
+
+def _attn_call(L, **kw):
+    d = dict(q=A16, qf=1, win=A16, wf=1, wm=0, wb=None, wr=128, ent=A16, ef=2, N=1000, idx=A16,
+             topk=64, pos=A16, B=1, Q=1, H=64, sink=A16, scale=0.044, cos=A16, sin=A16,
+             rr=2048, out=A16, of=1)
+    d.update(kw)
+    ws = L.csa_sparse_attn_workspace_size(d["B"], d["Q"], d["H"], d["topk"])
+    return L.csa_sparse_attn_decode(d["q"], d["qf"], d["win"], d["wf"], d["wm"], d["wb"], d["wr"],
+                                    d["ent"], d["ef"], d["N"], d["idx"], d["topk"], d["pos"],
+                                    d["B"], d["Q"], d["H"], d["sink"], d["scale"], d["cos"],
+                                    d["sin"], d["rr"], d["out"], d["of"], kw.get("ws", A16),
+                                    kw.get("wsb", ws), None)
+
+
+def test_attention_validation():
+    L = _lib.lib()
+    assert _attn_call(L, H=40) == EUNSUP
+    assert _attn_call(L, wr=64) == EINVAL            # ring needs 128 rows
+    assert _attn_call(L, wm=1) == EINVAL             # linear mode needs win_base
+    assert _attn_call(L, ef=0) == EUNSUP             # f32 rows need f32 queries
+    assert _attn_call(L, of=2) == EUNSUP
+    assert _attn_call(L, topk=10000) == EUNSUP
+    assert _attn_call(L, idx=None) == EINVAL
+    assert _attn_call(L, scale=float("nan")) == EINVAL
+    assert _attn_call(L, ws=None) == EWS
+    ws = L.hca_attn_workspace_size(16, 1, 64, 8192)
+    assert ws > 0
+    assert L.hca_attn_decode(A16, 1, A16, 1, 0, None, 128, A16, 1, 8192, 0, A16, 16, 1, 64, A16,
+                             0.044, A16, A16, 100, A16, 1, A16, ws, None) == EINVAL  # ratio 0
+
+
+def test_compress_validation():
+    L = _lib.lib()
+    a = _lib.CompressArgs(1, 4, 1024, 4, 512, 0, A16, 0, A16, A16, 0, A16, A16, 1e-6, A16, A16,
+                          100, A16, A16, A16, A16, 0, 16)
+    assert L.csa_compress_workspace_size(ctypes.byref(a)) == 4 * 2 * 1024 * 4
+    a.ratio = 8
+    assert L.csa_compress(ctypes.byref(a), A16, 1 << 20, None) == EUNSUP
+    a.ratio = 4
+    a.rotate = 1
+    assert L.csa_compress(ctypes.byref(a), A16, 1 << 20, None) == EUNSUP  # rotate needs d 128
+    a.rotate = 0
+    a.x = None
+    assert L.csa_compress(ctypes.byref(a), A16, 1 << 20, None) == EINVAL
+    a.x = A16
+    assert L.csa_compress(ctypes.byref(a), A16, 10, None) == EWS
+    assert L.csa_compress(None, A16, 10, None) == EINVAL
+
+
+def test_rope_table_validation():
+    L = _lib.lib()
+    assert L.csa_rope_table(160000.0, 16.0, 65536, 32.0, 1.0, 0, A16, A16, None) == EINVAL
+    assert L.csa_rope_table(1.0, 0.0, 0, 0.0, 0.0, 10, A16, A16, None) == EINVAL
+    assert L.csa_rope_table(160000.0, 16.0, 0, 32.0, 1.0, 10, A16, A16, None) == EINVAL

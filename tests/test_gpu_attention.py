@@ -1,0 +1,182 @@
+"""Sparse (CSA) and dense (HCA) attention parity against the oracle (GPU).
+
+The index lists are generated inputs (distinct ids, -1 padding, duplicates,
+ids outside the entry buffer), so attention is checked on its own; the fused
+path is covered by the whole-path tests.  bf16 outputs: |g - r| <= 1e-2 +
+2e-2 |r|; float32 path: 1e-5.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+from kv_cache_decode_csa_amd import _lib, synth
+from oracle import attention as A
+from oracle import codec, rope
+
+from gpu_util import (bf16, close_bf16, close_f32, f32, i32, need_gpu, rope_tables, say, to_np,
+                      upload_rows)
+
+pytestmark = pytest.mark.gpu
+OM = rope.frequencies(160000.0, rope.V4_YARN)
+ROPE_ROWS = 1 << 20
+
+
+@pytest.fixture(scope="module")
+def tables():
+    need_gpu()
+    return rope_tables(ROPE_ROWS)
+
+
+def gen_ids(rng, n_vis, k, n_max):
+    """k ids: mostly distinct visible ids, plus -1s, a duplicate and an id past Nmax."""
+    m = min(k, n_vis)
+    ids = rng.choice(n_vis, size=m, replace=False).astype(np.int32) if m else np.zeros(0, np.int32)
+    ids = np.concatenate([ids, np.full(k - m, -1, np.int32)])
+    if k >= 8 and m >= 4:
+        ids[1] = ids[0]          # duplicate row
+        ids[3] = -1
+        ids[5] = n_max + 7       # outside the buffer: absent
+    return ids
+
+
+def oracle_sparse(qv, winv, entv, ids, sink, pos, mode="ring", base=0, n_rows=128, scale=None):
+    scale = 512 ** -0.5 if scale is None else scale
+    wid = A.window_ids(pos, mode, base, n_rows=n_rows if mode == "linear" else None)
+    ids = np.where((ids >= 0) & (ids < len(entv)), ids, -1)
+    return A.sparse_decode(qv, winv, wid, entv, ids, sink, scale, pos, OM)
+
+
+@pytest.mark.parametrize("efmt,wfmt", [("bf16", "bf16"), ("fp8_mx32", "fp8_mx32"),
+                                       ("fp4_e4m3_16", "fp8_mx32"), ("bf16", "fp8_mx32")])
+@pytest.mark.parametrize("k", [512, 37, 0])
+def test_csa_decode(tables, efmt, wfmt, k):
+    cos, sin = tables
+    B, H, N = 3, 64, 3000
+    rng = np.random.default_rng(hash((efmt, wfmt, k)) % 1000)
+    q = synth.bf16_round(rng.standard_normal((B, 1, H, 512)).astype(np.float32))
+    win = rng.standard_normal((B, 128, 512)).astype(np.float32)
+    ent = rng.standard_normal((B, N, 512)).astype(np.float32)
+    if efmt == "bf16":
+        ent = synth.bf16_round(ent)
+    if wfmt == "bf16":
+        win = synth.bf16_round(win)
+    sink = rng.standard_normal(H).astype(np.float32)
+    pos = np.array([[4 * N - 1], [60], [1000]], np.int32)
+    ids = np.stack([gen_ids(rng, min((int(pos[b, 0]) + 1) // 4, N), k, N) for b in range(B)])
+    ids = ids.reshape(B, 1, k)
+    say(f"csa attn {efmt}/{wfmt} k={k}")
+    out = torch.empty((B, 1, H, 512), dtype=torch.bfloat16, device="cuda")
+    ws = _lib.workspace(_lib.csa_sparse_attn_workspace_size(B, 1, H, k))
+    _lib.csa_sparse_attn_decode(bf16(q), "bf16", upload_rows(win, wfmt), wfmt, _lib.WIN_RING128,
+                                None, 128, upload_rows(ent, efmt), efmt, N,
+                                i32(ids) if k else None, k, i32(pos), B, 1, H, f32(sink),
+                                512 ** -0.5, cos, sin, out, "bf16", ws)
+    got = to_np(out)
+    winv = codec.store(win, wfmt)[1]
+    entv = codec.store(ent, efmt)[1]
+    for b in range(B):
+        ref = oracle_sparse(q[b, 0].astype(np.float64), winv[b], entv[b], ids[b, 0], sink,
+                            int(pos[b, 0]))
+        close_bf16(got[b, 0], ref)
+
+
+def test_csa_multi_query_linear_window_and_heads(tables):
+    cos, sin = tables
+    B, Q, H, N, k = 2, 3, 128, 800, 100
+    rng = np.random.default_rng(21)
+    q = synth.bf16_round(rng.standard_normal((B, Q, H, 512)).astype(np.float32))
+    WR = 300
+    win = synth.bf16_round(rng.standard_normal((B, WR, 512)).astype(np.float32))
+    ent = rng.standard_normal((B, N, 512)).astype(np.float32)
+    sink = rng.standard_normal(H).astype(np.float32)
+    base = np.array([1000, 0], np.int32)
+    pos = np.array([[1100, 1299, 1350], [5, 250, 299]], np.int32)  # 1350 > base+WR-1: rows absent
+    ids = np.stack([np.stack([gen_ids(rng, min((int(p) + 1) // 4, N), k, N) for p in pos[b]])
+                    for b in range(B)])
+    out = torch.empty((B, Q, H, 512), dtype=torch.bfloat16, device="cuda")
+    ws = _lib.workspace(_lib.csa_sparse_attn_workspace_size(B, Q, H, k))
+    _lib.csa_sparse_attn_decode(bf16(q), "bf16", bf16(win), "bf16", _lib.WIN_LINEAR, i32(base), WR,
+                                upload_rows(ent, "fp8_mx32"), "fp8_mx32", N, i32(ids), k, i32(pos),
+                                B, Q, H, f32(sink), 512 ** -0.5, cos, sin, out, "bf16", ws)
+    got = to_np(out)
+    entv = codec.store(ent, "fp8_mx32")[1]
+    for b in range(B):
+        for qq in range(Q):
+            ref = oracle_sparse(q[b, qq].astype(np.float64), win[b].astype(np.float64), entv[b],
+                                ids[b, qq], sink, int(pos[b, qq]), "linear", int(base[b]), WR)
+            close_bf16(got[b, qq], ref)
+
+
+@pytest.mark.parametrize("efmt", ["bf16", "fp8_mx32", "fp4_e4m3_16"])
+def test_hca_decode(tables, efmt):
+    cos, sin = tables
+    B, H, N = 3, 64, 2500
+    rng = np.random.default_rng(31)
+    q = synth.bf16_round(rng.standard_normal((B, 1, H, 512)).astype(np.float32))
+    win = synth.bf16_round(rng.standard_normal((B, 128, 512)).astype(np.float32))
+    ent = rng.standard_normal((B, N, 512)).astype(np.float32)
+    if efmt == "bf16":
+        ent = synth.bf16_round(ent)
+    sink = rng.standard_normal(H).astype(np.float32)
+    pos = np.array([[128 * N + 5000], [5000], [50]], np.int32)  # all / 39 entries / window only
+    say(f"hca attn {efmt}")
+    out = torch.empty((B, 1, H, 512), dtype=torch.bfloat16, device="cuda")
+    ws = _lib.workspace(_lib.hca_attn_workspace_size(B, 1, H, N))
+    _lib.hca_attn_decode(bf16(q), "bf16", bf16(win), "bf16", _lib.WIN_RING128, None, 128,
+                         upload_rows(ent, efmt), efmt, N, 128, i32(pos), B, 1, H, f32(sink),
+                         512 ** -0.5, cos, sin, out, "bf16", ws)
+    got = to_np(out)
+    entv = codec.store(ent, efmt)[1]
+    for b in range(B):
+        t = int(pos[b, 0])
+        ref = A.hca_decode(q[b, 0].astype(np.float64), win[b].astype(np.float64), A.window_ids(t),
+                           entv[b], sink, 512 ** -0.5, t, OM)
+        close_bf16(got[b, 0], ref)
+
+
+def test_f32_path_and_single_head_group(tables):
+    cos, sin = tables
+    B, H, N, k = 1, 16, 512, 64
+    rng = np.random.default_rng(41)
+    q = rng.standard_normal((B, 1, H, 512)).astype(np.float32)
+    win = rng.standard_normal((B, 128, 512)).astype(np.float32)
+    ent = rng.standard_normal((B, N, 512)).astype(np.float32)
+    sink = rng.standard_normal(H).astype(np.float32)
+    pos = np.array([[2047]], np.int32)
+    ids = gen_ids(rng, N, k, N).reshape(1, 1, k)
+    out = torch.empty((B, 1, H, 512), dtype=torch.float32, device="cuda")
+    ws = _lib.workspace(_lib.csa_sparse_attn_workspace_size(B, 1, H, k))
+    _lib.csa_sparse_attn_decode(f32(q), "f32", f32(win), "f32", _lib.WIN_RING128, None, 128,
+                                f32(ent), "f32", N, i32(ids), k, i32(pos), B, 1, H, f32(sink),
+                                512 ** -0.5, cos, sin, out, "f32", ws)
+    ref = oracle_sparse(q[0, 0].astype(np.float64), win[0].astype(np.float64),
+                        ent[0].astype(np.float64), ids[0, 0], sink, 2047)
+    close_f32(to_np(out)[0, 0], ref)
+
+
+def test_permutation_padding_and_determinism(tables):
+    cos, sin = tables
+    B, H, N, k = 2, 64, 2000, 512
+    rng = np.random.default_rng(51)
+    q = bf16(synth.bf16_round(rng.standard_normal((B, 1, H, 512)).astype(np.float32)))
+    win = bf16(synth.bf16_round(rng.standard_normal((B, 128, 512)).astype(np.float32)))
+    ent = upload_rows(rng.standard_normal((B, N, 512)).astype(np.float32), "fp8_mx32")
+    sink = f32(rng.standard_normal(H).astype(np.float32))
+    pos = i32(np.array([[8191], [8191]]))
+    ids = np.stack([rng.choice(N, size=k, replace=False) for _ in range(B)]).astype(np.int32)
+
+    def run(idx):
+        kk = idx.shape[-1]
+        out = torch.empty((B, 1, H, 512), dtype=torch.bfloat16, device="cuda")
+        ws = _lib.workspace(_lib.csa_sparse_attn_workspace_size(B, 1, H, kk))
+        _lib.csa_sparse_attn_decode(q, "bf16", win, "bf16", 0, None, 128, ent, "fp8_mx32", N,
+                                    i32(idx.reshape(B, 1, kk)), kk, pos, B, 1, H, sink,
+                                    512 ** -0.5, cos, sin, out, "bf16", ws)
+        return to_np(out)
+
+    a = run(ids)
+    assert np.array_equal(a, run(ids))                     # bitwise run to run
+    close_bf16(run(ids[:, ::-1].copy()), a)                # permutation
+    padded = np.concatenate([ids, np.full((B, 100), -1, np.int32)], axis=1)
+    close_bf16(run(padded), a)                             # -1 rows are absent

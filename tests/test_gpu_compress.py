@@ -1,0 +1,167 @@
+"""Compressor parity against the oracle (GPU): bulk calls, token-by-token
+decode calls and chunked calls all match the oracle's entries and slot state.
+Quantized entries are compared after decoding, within one quantization step
+of the element's group (a float32 result may straddle a rounding boundary
+that the float64 one does not)."""
+
+import numpy as np
+import pytest
+import torch
+
+from kv_cache_decode_csa_amd import _lib, synth
+from oracle import codec, compressor, rope
+
+from gpu_util import bf16, close_f32, f32, i32, need_gpu, rope_tables, say, to_np
+
+pytestmark = pytest.mark.gpu
+ROPE_ROWS = 1 << 16
+
+
+class GpuCompressor:
+    """Device state + weights for one compressor; calls csa_compress."""
+
+    def __init__(self, B, dim, ratio, d, rotate, wkv, wg, ape, fmt, entry_fmt, n_entries, tables,
+                 state=None):
+        self.B, self.dim, self.ratio, self.d, self.rotate = B, dim, ratio, d, rotate
+        self.fmt, self.entry_fmt, self.cap = fmt, entry_fmt, n_entries
+        up = bf16 if fmt == "bf16" else f32
+        self.wkv, self.wg = up(wkv), up(wg)
+        self.ape = f32(ape)
+        self.norm = f32(np.ones(d, np.float32))
+        co = 2 if ratio == 4 else 1
+        shape = (B, co * ratio, co * d)
+        if state is None:
+            self.kv = torch.zeros(shape, dtype=torch.float32, device="cuda")
+            self.sc = torch.full(shape, float("-inf"), dtype=torch.float32, device="cuda")
+        else:
+            self.kv, self.sc = f32(state[0]), f32(state[1])
+        rb = _lib.kv_row_bytes(entry_fmt, d)
+        self.entries = torch.zeros((B, n_entries, rb), dtype=torch.uint8, device="cuda")
+        self.cos, self.sin = tables
+
+    def __call__(self, x, start):
+        B, T = x.shape[0], x.shape[1]
+        xd = (bf16 if self.fmt == "bf16" else f32)(x)
+        sp = i32(np.asarray(start, np.int32).reshape(B))
+        a = _lib.make_compress_args(
+            B=B, T=T, dim=self.dim, ratio=self.ratio, head_dim=self.d, rotate=self.rotate, x=xd,
+            x_fmt=self.fmt, w_kv=self.wkv, w_gate=self.wg, w_fmt=self.fmt, ape=self.ape,
+            norm_w=self.norm, eps=1e-6, rope_cos=self.cos, rope_sin=self.sin, start_pos=sp,
+            kv_state=self.kv, score_state=self.sc, entries=self.entries, entry_fmt=self.entry_fmt,
+            entries_cap=self.cap)
+        ws = _lib.workspace(_lib.csa_compress_workspace_size(a))
+        _lib.csa_compress(a, ws)
+        torch.cuda.synchronize()
+
+    def entry_values(self):
+        e = self.entries.cpu().numpy()
+        if self.entry_fmt == "f32":
+            return e.view(np.float32).astype(np.float64)
+        if self.entry_fmt == "bf16":
+            return codec.bf16_bits_to_f64(e.view(np.uint16))
+        return codec.load(e, self.entry_fmt, self.d)
+
+
+def step_bound(ref, fmt, d):
+    """One quantization step of each element's group at the oracle's value."""
+    if fmt in ("f32",):
+        return 1e-5 + 1e-5 * np.abs(ref)
+    if fmt == "bf16":
+        return 1e-3 + 2.0 ** -7 * np.abs(ref)
+    g = 32 if fmt == "fp8_mx32" else 16
+    amax = np.abs(ref).reshape(ref.shape[:-1] + (d // g, g)).max(-1, keepdims=True)
+    if fmt == "fp8_mx32":
+        step = amax / 448 * 2.0 ** -3 * 2      # coarsest e4m3 spacing in the group, x2 margin
+    else:
+        step = amax / 6 * 2.0 * 1.2            # coarsest e2m1 spacing (2) times the scale
+    return np.broadcast_to(step, ref.shape[:-1] + (d // g, g)).reshape(ref.shape) + 1e-6
+
+
+def weights(rng, dim, d, ratio, scale=0.02):
+    co = 2 if ratio == 4 else 1
+    return ((rng.standard_normal((co * d, dim)) * scale).astype(np.float32),
+            (rng.standard_normal((co * d, dim)) * scale).astype(np.float32),
+            (rng.standard_normal((ratio, co * d)) * scale).astype(np.float32))
+
+
+@pytest.fixture(scope="module")
+def tables():
+    need_gpu()
+    return rope_tables(ROPE_ROWS, yarn=False)
+
+
+OM = rope.frequencies(160000.0)
+
+
+@pytest.mark.parametrize("ratio,d,rotate", [(4, 512, 0), (4, 128, 1), (128, 512, 0), (1, 512, 0)])
+def test_bulk_f32(tables, ratio, d, rotate):
+    B, dim, T = 2, 256, 700
+    rng = np.random.default_rng(ratio * 10 + d)
+    wkv, wg, ape = weights(rng, dim, d, ratio)
+    x = rng.standard_normal((B, T, dim)).astype(np.float32)
+    n = T // ratio + 2
+    g = GpuCompressor(B, dim, ratio, d, rotate, wkv, wg, ape, "f32", "f32", n, tables)
+    starts = [0, 0]
+    say(f"compress bulk r={ratio} d={d}")
+    g(x, starts)
+    got = g.entry_values()
+    for b in range(B):
+        ref, st = compressor.compress_bulk(x[b].astype(np.float64), 0, wkv, wg, ape, np.ones(d),
+                                           OM, ratio, d, rotate=bool(rotate))
+        for i, v in ref.items():
+            close_f32(got[b, i], v, tol=2e-5)
+        close_f32(to_np(g.kv)[b], st[0], tol=2e-5)
+        sc = to_np(g.sc)[b]
+        assert np.array_equal(np.isinf(sc), np.isinf(st[1]))
+        fin = np.isfinite(st[1])
+        close_f32(sc[fin], st[1][fin], tol=2e-5)
+
+
+@pytest.mark.parametrize("entry_fmt", ["bf16", "fp8_mx32", "fp4_e4m3_16", "f32"])
+def test_decode_steps_bf16(tables, entry_fmt):
+    """Token-by-token calls from a state built by an earlier chunked call; each
+    sequence sits at a different offset inside its block."""
+    B, dim, d, ratio = 3, 512, 512, 4
+    rng = np.random.default_rng(7)
+    wkv, wg, ape = (synth.bf16_round(w) for w in weights(rng, dim, d, ratio))
+    ape = weights(rng, dim, d, ratio)[2]
+    prefix = np.array([37, 40, 42])
+    steps = 9
+    x = synth.bf16_round(rng.standard_normal((B, 60, dim)).astype(np.float32))
+    g = GpuCompressor(B, dim, ratio, d, 0, wkv, wg, ape, "bf16", entry_fmt, 32, tables)
+    # prefix: one chunked call per sequence (different lengths -> separate calls)
+    for b in range(B):
+        gb = GpuCompressor(1, dim, ratio, d, 0, wkv, wg, ape, "bf16", entry_fmt, 32, tables)
+        gb(x[b:b + 1, :prefix[b]], [0])
+        g.kv[b], g.sc[b], g.entries[b] = gb.kv[0], gb.sc[0], gb.entries[0]
+    for s in range(steps):
+        g(x[np.arange(B), prefix + s][:, None, :], prefix + s)
+    got = g.entry_values()
+    for b in range(B):
+        T = prefix[b] + steps
+        ref, st = compressor.compress_stream(x[b, :T].astype(np.float64), 0, wkv, wg, ape,
+                                             np.ones(d), OM, ratio, d)
+        for i, v in ref.items():
+            stored = codec.store(v, entry_fmt)[1]
+            err = np.abs(got[b, i] - stored)
+            assert np.all(err <= step_bound(v, entry_fmt, d)), (b, i, err.max())
+        close_f32(to_np(g.kv)[b], st[0], tol=1e-4)
+
+
+def test_hca_chunked_calls(tables):
+    B, dim, d, ratio = 1, 256, 512, 128
+    rng = np.random.default_rng(8)
+    wkv, wg, ape = weights(rng, dim, d, ratio)
+    x = rng.standard_normal((B, 420, dim)).astype(np.float32)
+    g = GpuCompressor(B, dim, ratio, d, 0, wkv, wg, ape, "f32", "f32", 8, tables)
+    p = 0
+    for c in (100, 50, 1, 150, 119):   # completes blocks 0, 1, 2 across calls
+        g(x[:, p:p + c], [p])
+        p += c
+    ref, st = compressor.compress_stream(x[0].astype(np.float64), 0, wkv, wg, ape, np.ones(d), OM,
+                                         ratio, d)
+    assert sorted(ref) == [0, 1, 2]
+    got = g.entry_values()
+    for i, v in ref.items():
+        close_f32(got[0, i], v, tol=2e-5)
+    close_f32(to_np(g.kv)[0], st[0], tol=2e-5)

@@ -1,0 +1,144 @@
+"""Indexer-score and fused top-k parity (GPU).
+
+Scores: the library's float32 scores against the oracle's float64 scores on
+the same bf16 / FP8 inputs, within an error bound derived from float32
+accumulation (two dot-product levels: 128 dims, then the weighted head sum).
+Indices: every returned list is checked for validity against the library's
+own scores, and against the oracle's selection wherever the oracle's boundary
+gap exceeds the score tolerance.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+from kv_cache_decode_csa_amd import _lib, synth
+from oracle import codec, indexer
+from oracle import topk as TK
+
+from gpu_util import bf16, f32, i32, need_gpu, say, upload_rows
+
+pytestmark = pytest.mark.gpu
+
+U = 2.0 ** -24
+
+
+def score_bound(q, w, K):
+    """|fp32 result - exact| bound: sum_h |w_h| (130 u sum_c |q_hc k_c|) + 70 u sum_h |w_h relu_h|."""
+    a = np.abs(K) @ np.abs(q).T  # [n, H]
+    d = np.maximum(K @ q.T, 0)
+    return 130 * U * (a @ np.abs(w)) + 70 * U * (d @ np.abs(w)) + 1e-30
+
+
+def check_selection(idx, S_gpu, S_ref, tol, nv, k):
+    ke = min(k, nv)
+    sel = idx[:ke]
+    assert np.all(idx[ke:] == -1)
+    assert len(set(sel.tolist())) == ke and np.all((sel >= 0) & (sel < nv))
+    # ordered by the library's own scores, ties by index
+    g = S_gpu[sel]
+    for a in range(ke - 1):
+        assert g[a] > g[a + 1] or (g[a] == g[a + 1] and sel[a] < sel[a + 1])
+    if ke < nv:
+        rest = np.setdiff1d(np.arange(nv), sel)
+        last = g[-1]
+        assert np.all((S_gpu[rest] < last) | ((S_gpu[rest] == last) & (rest > sel[-1])))
+    # against the oracle's own selection, away from near-ties
+    want = TK.topk(S_ref[:nv].astype(np.float32), k, nv)[:ke]
+    diff = np.setxor1d(sel, want)
+    if len(diff):
+        thr = np.sort(S_ref[:nv])[::-1][ke - 1] if ke > 0 else 0
+        assert np.all(np.abs(S_ref[diff] - thr) <= 2 * tol[diff] + 1e-12), diff[:10]
+
+
+@pytest.mark.parametrize("kfmt", ["bf16", "fp8_mx32"])
+@pytest.mark.parametrize("Hi", [32, 64])
+def test_scores_and_topk(kfmt, Hi):
+    need_gpu()
+    B, Q, N, k = 3, 2, 3000, 512
+    w = synth.Workload(90, "t", B=B, ctx=4 * N, ratio=4, n_entries=N, Hi=Hi, key_fmt=kfmt)
+    qi = synth.bf16_round(synth.normal_batched(w.seed, synth.T_QIDX, B, (Q, Hi, 128)))
+    wi = synth.normal_batched(w.seed, synth.T_WIDX, B, (Q, Hi), (128 * Hi) ** -0.5)
+    K = synth.index_keys(w)                                           # [B, N, 128] f32 values
+    pos = np.array([[4 * N - 1, 2047], [5, 0], [601, 4 * N + 900]], np.int32)  # n_vis clamps
+    say(f"index_topk {kfmt} Hi={Hi}")
+    kdev = upload_rows(K, kfmt)
+    out = torch.empty((B, Q, k), dtype=torch.int32, device="cuda")
+    sc = torch.full((B, Q, N), float("nan"), dtype=torch.float32, device="cuda")
+    ws = _lib.workspace(_lib.csa_index_topk_workspace_size(B, Q, N, k))
+    _lib.csa_index_topk(bf16(qi), "bf16", f32(wi), kdev, kfmt, i32(pos), 4, B, Q, Hi, N, k, out,
+                        sc, ws)
+    out = out.cpu().numpy()
+    sc = sc.cpu().numpy()
+    Kv = codec.store(K, kfmt)[1] if kfmt != "bf16" else K.astype(np.float64)
+    for b in range(B):
+        for qq in range(Q):
+            nv = int(indexer.n_visible(pos[b, qq], 4, N))
+            S_ref = indexer.scores(qi[b, qq].astype(np.float64), wi[b, qq], Kv[b], nv)
+            tol = score_bound(qi[b, qq].astype(np.float64), wi[b, qq].astype(np.float64),
+                              Kv[b][:nv])
+            err = np.abs(sc[b, qq, :nv] - S_ref)
+            assert np.all(err <= tol), (b, qq, err.max(), tol[err.argmax()])
+            check_selection(out[b, qq], sc[b, qq], S_ref, tol, nv, k)
+
+
+def test_without_score_output_matches():
+    """out_scores is optional: the indices are the same either way."""
+    need_gpu()
+    B, N, Hi, k = 2, 5000, 64, 64
+    rng = np.random.default_rng(4)
+    qi = synth.bf16_round(rng.standard_normal((B, 1, Hi, 128)).astype(np.float32))
+    wi = rng.standard_normal((B, 1, Hi)).astype(np.float32)
+    K = rng.standard_normal((B, N, 128)).astype(np.float32)
+    kd = upload_rows(K, "fp8_mx32")
+    pos = i32(np.array([[4 * N - 1], [4 * N - 1]]))
+    ws = _lib.workspace(_lib.csa_index_topk_workspace_size(B, 1, N, k))
+    o1 = torch.empty((B, 1, k), dtype=torch.int32, device="cuda")
+    o2 = torch.empty_like(o1)
+    sc = torch.empty((B, 1, N), dtype=torch.float32, device="cuda")
+    _lib.csa_index_topk(bf16(qi), "bf16", f32(wi), kd, "fp8_mx32", pos, 4, B, 1, Hi, N, k, o1, sc,
+                        ws)
+    _lib.csa_index_topk(bf16(qi), "bf16", f32(wi), kd, "fp8_mx32", pos, 4, B, 1, Hi, N, k, o2,
+                        None, ws)
+    assert torch.equal(o1, o2)
+
+
+def test_batch_invariance():
+    """A sequence's selection and scores do not depend on its batch neighbours."""
+    need_gpu()
+    B, N, Hi, k = 5, 4000, 64, 512
+    rng = np.random.default_rng(5)
+    qi = synth.bf16_round(rng.standard_normal((B, 1, Hi, 128)).astype(np.float32))
+    wi = rng.standard_normal((B, 1, Hi)).astype(np.float32)
+    K = synth.bf16_round(rng.standard_normal((B, N, 128)).astype(np.float32))
+    pos = np.full((B, 1), 4 * N - 1, np.int32)
+    res = []
+    for bs in (list(range(B)), [2]):
+        ws = _lib.workspace(_lib.csa_index_topk_workspace_size(len(bs), 1, N, k))
+        o = torch.empty((len(bs), 1, k), dtype=torch.int32, device="cuda")
+        sc = torch.empty((len(bs), 1, N), dtype=torch.float32, device="cuda")
+        _lib.csa_index_topk(bf16(qi[bs]), "bf16", f32(wi[bs]), bf16(K[bs]), "bf16", i32(pos[bs]), 4,
+                            len(bs), 1, Hi, N, k, o, sc, ws)
+        res.append((o.cpu().numpy(), sc.cpu().numpy()))
+    assert np.array_equal(res[0][0][2], res[1][0][0])
+    assert np.array_equal(res[0][1][2], res[1][1][0])
+
+
+def test_f32_path():
+    need_gpu()
+    B, N, Hi, k = 1, 512, 4, 64
+    rng = np.random.default_rng(6)
+    qi = rng.standard_normal((B, 1, Hi, 128)).astype(np.float32)
+    wi = (rng.standard_normal((B, 1, Hi)) * (128 * Hi) ** -0.5).astype(np.float32)
+    K = rng.standard_normal((B, N, 128)).astype(np.float32)
+    pos = np.array([[2047]], np.int32)
+    ws = _lib.workspace(_lib.csa_index_topk_workspace_size(B, 1, N, k))
+    o = torch.empty((B, 1, k), dtype=torch.int32, device="cuda")
+    sc = torch.empty((B, 1, N), dtype=torch.float32, device="cuda")
+    _lib.csa_index_topk(f32(qi), "f32", f32(wi), f32(K), "f32", i32(pos), 4, B, 1, Hi, N, k, o, sc,
+                        ws)
+    S_ref = indexer.scores(qi[0, 0].astype(np.float64), wi[0, 0], K[0].astype(np.float64), N)
+    tol = score_bound(qi[0, 0].astype(np.float64), wi[0, 0].astype(np.float64),
+                      K[0].astype(np.float64))
+    assert np.all(np.abs(sc.cpu().numpy()[0, 0] - S_ref) <= tol)
+    check_selection(o.cpu().numpy()[0, 0], sc.cpu().numpy()[0, 0], S_ref, tol, N, k)
