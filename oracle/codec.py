@@ -89,7 +89,7 @@ def e4m3_encode(y):
     a0 = np.where(finite, a, 0.0)
     # subnormal / small branch
     small = a0 < 2.0 ** -6
-    k = np.rint(a0 * 512.0)  # 0..8 (8 == smallest normal, code 0x08)
+    k = np.rint(np.where(small, a0, 0.0) * 512.0)  # 0..8 (8 == smallest normal, code 0x08)
     # normal branch
     f, ex = np.frexp(np.where(small, 1.0, a0))  # a = f * 2**ex, f in [0.5, 1)
     E = ex.astype(np.int64) - 1
