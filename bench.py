@@ -97,49 +97,61 @@ def time_phases(layer, steps, torch):
     return {k: float(np.mean(v)) for k, v in acc.items()}
 
 
-def cpu_baseline(w, n_seq):
+def cpu_baseline(w, n_seq, min_seconds=10.0):
     """The oracle on n_seq sequences of the workload: decode the stored index
     keys, score, select, gather and attend (untimed: building the stored
-    bytes with the oracle's codec)."""
+    bytes with the oracle's codec).  The timed part is repeated over the same
+    sequences until it has run for at least min_seconds."""
     from kv_cache_decode_csa_amd import synth
     from oracle import attention, codec, indexer, rope
     from oracle import topk as TK
     om = rope.frequencies(160000.0, rope.V4_YARN if w.yarn else None)
     threads = os.environ.get("OMP_NUM_THREADS") or str(len(os.sched_getaffinity(0)))
     t_total = 0.0
+    prepared = []
     for b in range(n_seq):
         br = [b]
         q, sink = synth.queries(w, br)
         win = synth.window_rows(w, br)[0]
         ent = synth.entries(w, br)[0]
         win_st = codec.store(win, w.win_fmt)[0]
-        t = w.t
+        keys_st = None
+        qi = wi = None
         if w.ratio == 4:
             qi, wi = synth.index_queries(w, br)
             keys_st = codec.store(synth.index_keys(w, br)[0], w.key_fmt)[0]
+        prepared.append((q, sink, win_st, ent, keys_st, qi, wi))
+    t = w.t
+    passes = 0
+    while t_total < min_seconds and passes < 50:
+        passes += 1
+        for (q, sink, win_st, ent, keys_st, qi, wi) in prepared:
+            if w.ratio == 4:
+                t0 = time.perf_counter()
+                K = codec.load(keys_st, w.key_fmt, 128)
+                nv = int(indexer.n_visible(t, 4, w.n_entries))
+                S = indexer.scores(qi[0].astype(np.float64), wi[0], K, nv)
+                ids = TK.topk(S.astype(np.float32), w.topk, nv)
+                t_total += time.perf_counter() - t0
+                rows_st = codec.store(ent[np.maximum(ids, 0)], w.ent_fmt)[0]  # stored rows read
+            else:
+                ids = attention.hca_ids(t, w.ratio, w.n_entries)
+                rows_st = codec.store(ent[ids], w.ent_fmt)[0]
             t0 = time.perf_counter()
-            K = codec.load(keys_st, w.key_fmt, 128)
-            nv = int(indexer.n_visible(t, 4, w.n_entries))
-            S = indexer.scores(qi[0].astype(np.float64), wi[0], K, nv)
-            ids = TK.topk(S.astype(np.float32), w.topk, nv)
+            E = codec.load(rows_st, w.ent_fmt, 512)
+            Wv = codec.load(win_st, w.win_fmt, 512)
+            wid = attention.window_ids(t)
+            rows = np.concatenate([Wv[np.maximum(wid, 0)], E])
+            valid = np.concatenate([wid >= 0, ids >= 0])
+            attention.attend(q[0].astype(np.float64), rows, valid, sink, 512 ** -0.5, t, om)
             t_total += time.perf_counter() - t0
-            rows_st = codec.store(ent[np.maximum(ids, 0)], w.ent_fmt)[0]   # the stored rows read
-        else:
-            ids = attention.hca_ids(t, w.ratio, w.n_entries)
-            rows_st = codec.store(ent[ids], w.ent_fmt)[0]
-        t0 = time.perf_counter()
-        E = codec.load(rows_st, w.ent_fmt, 512)
-        Wv = codec.load(win_st, w.win_fmt, 512)
-        wid = attention.window_ids(t)
-        rows = np.concatenate([Wv[np.maximum(wid, 0)], E])
-        valid = np.concatenate([wid >= 0, ids >= 0])
-        attention.attend(q[0].astype(np.float64), rows, valid, sink, 512 ** -0.5, t, om)
-        t_total += time.perf_counter() - t0
-    return {"value": n_seq / t_total, "unit": "tokens/s/layer", "cores": int(threads),
+    n_tok = passes * n_seq
+    return {"value": n_tok / t_total, "unit": "tokens/s/layer", "cores": int(threads),
             "kind": "oracle",
-            "sample": f"{n_seq} of {w.B} sequences of the same workload, full context "
-                      f"({w.n_entries} entries each); timed: key decode, scoring, top-k, row "
-                      f"decode and attention in float64 NumPy; {t_total:.1f} s"}
+            "sample": f"{n_seq} of {w.B} sequences of the same workload at full context "
+                      f"({w.n_entries} entries each), {passes} passes ({n_tok} token-steps); "
+                      f"timed: key decode, scoring, top-k, row decode and attention in float64 "
+                      f"NumPy, {t_total:.1f} s"}
 
 
 def main():

@@ -11,9 +11,11 @@
 //     MFMA A-operand layout and forms a partial q.c over its slice; the four
 //     partials are summed through LDS in a fixed order, so every wave holds the
 //     full logits and runs the same online softmax;
-//   * for the value product the wave writes its slice transposed into LDS
-//     (rows contiguous per dim) and multiplies P (16 heads x 32 rows, bf16) by
-//     it, keeping O for 16 heads x its 128 dims in 32 accumulators;
+//   * for the value product the wave stores its slice row-major in LDS and
+//     reads it back with the transposing 16-bit LDS read, which hands every
+//     lane 4 rows of one dim; P (16 heads x 32 rows, bf16) times that slice
+//     accumulates O for 16 heads x its 128 dims in 32 accumulators;
+//   * the next tile's rows are fetched while the current one is computed;
 //   * each chunk leaves (m, l, O) per head; a merge kernel combines the chunks
 //     in a fixed order, adds the sink, normalises and undoes the RoPE.
 // Row formats are decoded exactly to bf16 on load (E4M3 x 2^e and E2M1 x E4M3
@@ -28,7 +30,6 @@ constexpr int kAttnThreads = 256;
 constexpr int kTile = 32;             // rows per tile
 constexpr int kChunkCsa = 128;        // rows per work-group, top-k lists
 constexpr int kChunkHca = 1024;       // rows per work-group, dense lists
-constexpr int kTPitch = kTile + 8;    // LDS pitch (bf16) of the transposed slice
 constexpr float kLog2e = 1.4426950408889634f;
 
 struct RowRef {
@@ -68,32 +69,6 @@ __device__ __forceinline__ RowRef resolve_row(const AttnArgs& a, int64_t unit, i
   return r;
 }
 
-// 8 consecutive values starting at dim d0 (d0 % 8 == 0) as exact bf16.
-__device__ __forceinline__ uint4 load8_bf16(const RowRef& r, int d0) {
-  if (r.p == nullptr) return make_uint4(0, 0, 0, 0);
-  if (r.fmt == CSA_BF16) return *(const uint4*)(r.p + 2 * d0);
-  if (r.fmt == CSA_FP8_MX32) {
-    uint32_t lo = *(const uint32_t*)(r.p + d0);
-    uint32_t hi = *(const uint32_t*)(r.p + d0 + 4);
-    float sc = exp2i((int)r.p[kHeadDim + (d0 >> 5)] - 127);
-    uint4 o;
-    o.x = pack_bf16x2_exact(e4m3_to_f32(lo) * sc, e4m3_to_f32(lo >> 8) * sc);
-    o.y = pack_bf16x2_exact(e4m3_to_f32(lo >> 16) * sc, e4m3_to_f32(lo >> 24) * sc);
-    o.z = pack_bf16x2_exact(e4m3_to_f32(hi) * sc, e4m3_to_f32(hi >> 8) * sc);
-    o.w = pack_bf16x2_exact(e4m3_to_f32(hi >> 16) * sc, e4m3_to_f32(hi >> 24) * sc);
-    return o;
-  }
-  // FP4_E4M3_16
-  uint32_t c = *(const uint32_t*)(r.p + (d0 >> 1));
-  float sc = e4m3_to_f32(r.p[kHeadDim / 2 + (d0 >> 4)]);
-  uint4 o;
-  o.x = pack_bf16x2_exact(e2m1_to_f32(c & 15u) * sc, e2m1_to_f32((c >> 4) & 15u) * sc);
-  o.y = pack_bf16x2_exact(e2m1_to_f32((c >> 8) & 15u) * sc, e2m1_to_f32((c >> 12) & 15u) * sc);
-  o.z = pack_bf16x2_exact(e2m1_to_f32((c >> 16) & 15u) * sc, e2m1_to_f32((c >> 20) & 15u) * sc);
-  o.w = pack_bf16x2_exact(e2m1_to_f32((c >> 24) & 15u) * sc, e2m1_to_f32(c >> 28) * sc);
-  return o;
-}
-
 __device__ __forceinline__ float row_val_f32(const RowRef& r, int d) {
   if (r.fmt == CSA_F32) return ((const float*)r.p)[d];
   if (r.fmt == CSA_BF16) return bf16_to_f32(((const uint16_t*)r.p)[d]);
@@ -130,9 +105,205 @@ __device__ __forceinline__ void store_out(const AttnArgs& a, int64_t unit, int h
 }
 
 // ------------------------------------------------------------------ MFMA kernel
+typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2_t;
+typedef short v4i16_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4i16_t lds_v4i16_t;
+
+// Transposed 16-bit LDS read: inside each 16-lane group, lane j supplies the 4
+// values at its address and lane c receives value c%4 of lane 4i + c/4 as its
+// element i.
+__device__ __forceinline__ uint2 lds_read_tr16(const uint16_t* p) {
+  const v4i16_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (lds_v4i16_t*)((__attribute__((address_space(3))) uint16_t*)p));
+  return __builtin_bit_cast(uint2, v);
+}
+
+// Raw bytes of one row's 128-dim slice [128 w, 128 w + 128) as this lane
+// needs them (dims 128 w + 32 s + 8 kq .. +8 for s = 0..3), per format.
+template <int F> struct Raw;
+template <> struct Raw<CSA_BF16> { uint4 v[4]; };
+template <> struct Raw<CSA_FP8_MX32> { uint2 v[4]; uint32_t sc; };   // sc: groups 4w..4w+3
+template <> struct Raw<CSA_FP4_E4M3_16> { uint32_t v[4]; uint2 sc; }; // sc: groups 8w..8w+7
+
+template <int F>
+__device__ __forceinline__ void load_raw(const uint8_t* p, int w, int kq, Raw<F>& r) {
+  if (F == CSA_BF16) {
+    Raw<CSA_BF16>& q = (Raw<CSA_BF16>&)r;
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+      q.v[s] = p ? *(const uint4*)(p + 2 * (128 * w + 32 * s + 8 * kq)) : make_uint4(0, 0, 0, 0);
+  } else if (F == CSA_FP8_MX32) {
+    Raw<CSA_FP8_MX32>& q = (Raw<CSA_FP8_MX32>&)r;
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+      q.v[s] = p ? *(const uint2*)(p + 128 * w + 32 * s + 8 * kq) : make_uint2(0, 0);
+    q.sc = p ? *(const uint32_t*)(p + kHeadDim + 4 * w) : 0u;
+  } else {
+    Raw<CSA_FP4_E4M3_16>& q = (Raw<CSA_FP4_E4M3_16>&)r;
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+      q.v[s] = p ? *(const uint32_t*)(p + 64 * w + 16 * s + 4 * kq) : 0u;
+    q.sc = p ? *(const uint2*)(p + kHeadDim / 2 + 8 * w) : make_uint2(0, 0);
+  }
+}
+
+// exact bf16 values of fragment s
+template <int F>
+__device__ __forceinline__ uint4 frag_bf16(const Raw<F>& r, int s, int kq) {
+  if (F == CSA_BF16) {
+    return ((const Raw<CSA_BF16>&)r).v[s];
+  } else if (F == CSA_FP8_MX32) {
+    const Raw<CSA_FP8_MX32>& q = (const Raw<CSA_FP8_MX32>&)r;
+    const float sc = exp2i((int)((q.sc >> (8 * s)) & 0xffu) - 127);
+    const bf16x2_t a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(q.v[s].x, sc, false);
+    const bf16x2_t b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(q.v[s].x, sc, true);
+    const bf16x2_t c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(q.v[s].y, sc, false);
+    const bf16x2_t d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(q.v[s].y, sc, true);
+    return make_uint4(__builtin_bit_cast(uint32_t, a), __builtin_bit_cast(uint32_t, b),
+                      __builtin_bit_cast(uint32_t, c), __builtin_bit_cast(uint32_t, d));
+  } else {
+    const Raw<CSA_FP4_E4M3_16>& q = (const Raw<CSA_FP4_E4M3_16>&)r;
+    const int g = 2 * s + (kq >> 1);  // group 8w + g
+    const uint32_t sb = g < 4 ? (q.sc.x >> (8 * g)) : (q.sc.y >> (8 * (g - 4)));
+    const float sc = e4m3_to_f32(sb & 0xffu);
+    const uint32_t c = q.v[s];
+    return make_uint4(
+        pack_bf16x2_exact(e2m1_to_f32(c & 15u) * sc, e2m1_to_f32((c >> 4) & 15u) * sc),
+        pack_bf16x2_exact(e2m1_to_f32((c >> 8) & 15u) * sc, e2m1_to_f32((c >> 12) & 15u) * sc),
+        pack_bf16x2_exact(e2m1_to_f32((c >> 16) & 15u) * sc, e2m1_to_f32((c >> 20) & 15u) * sc),
+        pack_bf16x2_exact(e2m1_to_f32((c >> 24) & 15u) * sc, e2m1_to_f32(c >> 28) * sc));
+  }
+}
+
+constexpr int kRPitch = 128 + 16;  // bf16 per LDS row of a wave's 128-dim slice
+constexpr int kMaxIdsPerLane = kChunkCsa / 16;
+
+struct SoftmaxState {
+  float m;      // running max (log2 units) of head r16
+  float l;      // running denominator (without the sink)
+  f32x4_t o[8]; // O for heads 4 kq + r, dims 128 w + 16 dt + r16
+};
+
+// One 32-row tile: partial logits over this wave's dims, fixed-order sum of
+// the 4 waves' partials through LDS, online softmax, O += P C.
+__device__ __forceinline__ void attend_tile(const uint4 (&fr)[2][4], uint32_t vmask,
+                                            const uint4 (&qa)[4], float zscale, int w, int lane,
+                                            uint16_t* R, float4 (*Sp)[64][2], SoftmaxState& st) {
+  const int r16 = lane & 15, kq = lane >> 4;
+  f32x4_t sacc[2];
+#pragma unroll
+  for (int rt = 0; rt < 2; ++rt) {
+    sacc[rt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+      sacc[rt] = mfma16x16x32(as_bf16x8(fr[rt][s]), as_bf16x8(qa[s]), sacc[rt]);
+  }
+  __syncthreads();  // the previous tile's readers of Sp / R are done
+  Sp[w][lane][0] = make_float4(sacc[0][0], sacc[0][1], sacc[0][2], sacc[0][3]);
+  Sp[w][lane][1] = make_float4(sacc[1][0], sacc[1][1], sacc[1][2], sacc[1][3]);
+#pragma unroll
+  for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+      *(uint4*)(R + (16 * rt + r16) * kRPitch + 32 * s + 8 * kq) = fr[rt][s];
+  __syncthreads();
+
+  float z[2][4];
+#pragma unroll
+  for (int rt = 0; rt < 2; ++rt) {
+    float4 acc = Sp[0][lane][rt];
+#pragma unroll
+    for (int ww = 1; ww < 4; ++ww) {
+      const float4 v = Sp[ww][lane][rt];
+      acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
+    }
+    z[rt][0] = acc.x; z[rt][1] = acc.y; z[rt][2] = acc.z; z[rt][3] = acc.w;
+  }
+  float tmax = -INFINITY;
+#pragma unroll
+  for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const bool ok = (vmask >> (16 * rt + 4 * kq + r)) & 1u;
+      z[rt][r] = ok ? z[rt][r] * zscale : -INFINITY;
+      tmax = fmaxf(tmax, z[rt][r]);
+    }
+  tmax = fmaxf(tmax, shfl_xor_f(tmax, 16));
+  tmax = fmaxf(tmax, shfl_xor_f(tmax, 32));
+  const float m_new = fmaxf(st.m, tmax);
+  const float alpha = (m_new == -INFINITY) ? 1.f : exp2f(st.m - m_new);
+  float p[2][4];
+  float psum = 0.f;
+#pragma unroll
+  for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      p[rt][r] = (z[rt][r] == -INFINITY) ? 0.f : exp2f(z[rt][r] - m_new);
+      psum += p[rt][r];
+    }
+  psum += shfl_xor_f(psum, 16);
+  psum += shfl_xor_f(psum, 32);
+  st.l = st.l * alpha + psum;
+  st.m = m_new;
+  // k index 8 kq + i <-> row 4 kq + i (i < 4) or 16 + 4 kq + i - 4, as in the logits
+  float al[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) al[r] = __shfl(alpha, 4 * kq + r, 64);
+  const bf16x8_t pa = as_bf16x8(make_uint4(pack_bf16x2(p[0][0], p[0][1]),
+                                           pack_bf16x2(p[0][2], p[0][3]),
+                                           pack_bf16x2(p[1][0], p[1][1]),
+                                           pack_bf16x2(p[1][2], p[1][3])));
+  const uint16_t* rb0 = R + (4 * kq + (r16 >> 2)) * kRPitch + 4 * (r16 & 3);
+  const uint16_t* rb1 = rb0 + 16 * kRPitch;
+#pragma unroll
+  for (int dt = 0; dt < 8; ++dt) {
+    const uint2 c0 = lds_read_tr16(rb0 + 16 * dt);
+    const uint2 c1 = lds_read_tr16(rb1 + 16 * dt);
+    f32x4_t acc = st.o[dt];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) acc[r] *= al[r];
+    st.o[dt] = mfma16x16x32(pa, as_bf16x8(make_uint4(c0.x, c0.y, c1.x, c1.y)), acc);
+  }
+}
+
+// Rows [j0, j1) of the list, all in format F: pipelined tile loop.
+template <int F, class RowFn>
+__device__ __forceinline__ void run_rows(int64_t j0, int64_t j1, RowFn row_of, const uint4 (&qa)[4],
+                                         float zscale, int w, int lane, uint16_t* R,
+                                         float4 (*Sp)[64][2], SoftmaxState& st) {
+  const int r16 = lane & 15, kq = lane >> 4;
+  Raw<F> cur[2], nxt[2];
+  uint32_t vm_cur = 0, vm_nxt = 0;
+  auto load_tile = [&](int64_t jt, Raw<F> (&f)[2], uint32_t& vm) {
+    vm = 0;
+#pragma unroll
+    for (int rt = 0; rt < 2; ++rt) {
+      const int64_t j = jt + 16 * rt + r16;
+      const uint8_t* p = j < j1 ? row_of(j) : nullptr;
+      const unsigned long long bal = __ballot(p != nullptr);
+      vm |= (uint32_t)(bal & 0xffffull) << (16 * rt);
+      load_raw<F>(p, w, kq, f[rt]);
+    }
+  };
+  if (j0 < j1) load_tile(j0, cur, vm_cur);
+  for (int64_t jt = j0; jt < j1; jt += kTile) {
+    if (jt + kTile < j1) load_tile(jt + kTile, nxt, vm_nxt);
+    uint4 fr[2][4];
+#pragma unroll
+    for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+      for (int s = 0; s < 4; ++s) fr[rt][s] = frag_bf16<F>(cur[rt], s, kq);
+    attend_tile(fr, vm_cur, qa, zscale, w, lane, R, Sp, st);
+    cur[0] = nxt[0];
+    cur[1] = nxt[1];
+    vm_cur = vm_nxt;
+  }
+}
+
+template <int WF, int EF>
 __global__ void __launch_bounds__(kAttnThreads) attn_mfma_kernel(AttnArgs a, int chunk_rows,
                                                                  int nchunks, Partial* part) {
-  __shared__ uint16_t Tl[4][128 * kTPitch];
+  __shared__ uint16_t Rl[4][kTile * kRPitch];
   __shared__ float4 Sp[4][64][2];
 
   const int tid = threadIdx.x;
@@ -150,12 +321,10 @@ __global__ void __launch_bounds__(kAttnThreads) attn_mfma_kernel(AttnArgs a, int
   const int64_t j_begin = (int64_t)chunk * chunk_rows;
   int64_t j_end = j_begin + chunk_rows;
   if (j_end > list_len) j_end = list_len;
-  const size_t win_rb = a.win_rb;
-  const size_t ent_rb = a.ent_rb;
   const int rr = rope_row(a, t);
   const float zscale = a.scale * kLog2e;
 
-  // query slice: head 16*hg + r16, dims 128*w + 32*s + 8*kq .. +8, rotated
+  // query slice: head 16 hg + r16, dims 128 w + 32 s + 8 kq .. +8, rotated
   uint4 qa[4];
   {
     const int head = 16 * hg + r16;
@@ -166,7 +335,7 @@ __global__ void __launch_bounds__(kAttnThreads) attn_mfma_kernel(AttnArgs a, int
       uint4 raw = *(const uint4*)(qp + d0);
       if (d0 >= kHeadDim - kRopeDims) {
         float v[8];
-        uint32_t u[4] = {raw.x, raw.y, raw.z, raw.w};
+        const uint32_t u[4] = {raw.x, raw.y, raw.z, raw.w};
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           v[2 * j] = __uint_as_float(u[j] << 16);
@@ -188,113 +357,52 @@ __global__ void __launch_bounds__(kAttnThreads) attn_mfma_kernel(AttnArgs a, int
     }
   }
 
-  float m_run = -INFINITY;  // running max (log2 units) for head r16
-  float l_run = 0.f;
-  f32x4_t o[8];
+  // top-k ids of this chunk, fetched once: lane holds rows j_begin + 16 i + r16
+  int32_t ids[kMaxIdsPerLane];
+  if (!a.dense) {
 #pragma unroll
-  for (int dt = 0; dt < 8; ++dt) o[dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-
-  uint16_t* T = Tl[w];
-
-  for (int64_t j0 = j_begin; j0 < j_end; j0 += kTile) {
-    // ---- load this wave's dim slice of rows j0 + 16*rt + r16
-    uint4 fr[2][4];
-    uint32_t vmask = 0;
-#pragma unroll
-    for (int rt = 0; rt < 2; ++rt) {
-      const int64_t j = j0 + 16 * rt + r16;
-      RowRef rf{nullptr, a.win_fmt};
-      if (j < j_end) rf = resolve_row(a, unit, b, t, j, nvis, win_rb, ent_rb);
-      unsigned long long bal = __ballot(rf.p != nullptr);
-      vmask |= (uint32_t)(bal & 0xffffull) << (16 * rt);
-#pragma unroll
-      for (int s = 0; s < 4; ++s) fr[rt][s] = load8_bf16(rf, 128 * w + 32 * s + 8 * kq);
+    for (int i = 0; i < kMaxIdsPerLane; ++i) {
+      const int64_t jj = j_begin + 16 * i + r16;
+      ids[i] = (jj >= kWindow && jj < j_end) ? a.topk_idx[unit * a.topk + (jj - kWindow)] : -1;
     }
-    __syncthreads();  // previous tile's readers of Sp / T are done
+  }
 
-    // ---- partial logits over this wave's 128 dims
-    f32x4_t sacc[2];
+  SoftmaxState st;
+  st.m = -INFINITY;
+  st.l = 0.f;
 #pragma unroll
-    for (int rt = 0; rt < 2; ++rt) {
-      sacc[rt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int s = 0; s < 4; ++s) sacc[rt] = mfma16x16x32(as_bf16x8(fr[rt][s]), as_bf16x8(qa[s]), sacc[rt]);
-    }
-    Sp[w][lane][0] = make_float4(sacc[0][0], sacc[0][1], sacc[0][2], sacc[0][3]);
-    Sp[w][lane][1] = make_float4(sacc[1][0], sacc[1][1], sacc[1][2], sacc[1][3]);
-    // ---- transposed slice for the value product: T[dim][row]
-#pragma unroll
-    for (int rt = 0; rt < 2; ++rt)
-#pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        const uint4 f = fr[rt][s];
-        const uint32_t u[4] = {f.x, f.y, f.z, f.w};
-        const int row = 16 * rt + r16;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int d = 32 * s + 8 * kq + 2 * j;
-          T[d * kTPitch + row] = (uint16_t)(u[j] & 0xffffu);
-          T[(d + 1) * kTPitch + row] = (uint16_t)(u[j] >> 16);
-        }
-      }
-    __syncthreads();
+  for (int dt = 0; dt < 8; ++dt) st.o[dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  uint16_t* R = Rl[w];
 
-    // ---- full logits: fixed-order sum of the four partials
-    float z[2][4];
+  // window rows [j_begin, min(j_end, 128))
+  const int64_t jw = j_end < kWindow ? j_end : kWindow;
+  if (j_begin < jw) {
+    auto win_row = [&](int64_t j) -> const uint8_t* {
+      return resolve_row(a, unit, b, t, j, nvis, a.win_rb, a.ent_rb).p;
+    };
+    run_rows<WF>(j_begin, jw, win_row, qa, zscale, w, lane, R, Sp, st);
+  }
+  // entry rows [max(j_begin, 128), j_end)
+  const int64_t je = j_begin > kWindow ? j_begin : kWindow;
+  if (je < j_end) {
+    const uint8_t* ebase = (const uint8_t*)a.entries + (size_t)b * (size_t)a.Nmax * a.ent_rb;
+    if (a.dense) {
+      auto ent_row = [&](int64_t j) -> const uint8_t* {
+        const int64_t e = j - kWindow;
+        return e < nvis ? ebase + (size_t)e * a.ent_rb : nullptr;
+      };
+      run_rows<EF>(je, j_end, ent_row, qa, zscale, w, lane, R, Sp, st);
+    } else {
+      auto ent_row = [&](int64_t j) -> const uint8_t* {
+        // this lane's id slot for row j (rows are 16 r16-strided within the chunk)
+        const int slot = (int)((j - j_begin) >> 4);
+        int32_t e = -1;
 #pragma unroll
-    for (int rt = 0; rt < 2; ++rt) {
-      float4 acc = Sp[0][lane][rt];
-#pragma unroll
-      for (int ww = 1; ww < 4; ++ww) {
-        float4 v = Sp[ww][lane][rt];
-        acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
-      }
-      z[rt][0] = acc.x; z[rt][1] = acc.y; z[rt][2] = acc.z; z[rt][3] = acc.w;
-    }
-    // ---- online softmax for head r16 over rows 16*rt + 4*kq + r
-    float tmax = -INFINITY;
-#pragma unroll
-    for (int rt = 0; rt < 2; ++rt)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const bool ok = (vmask >> (16 * rt + 4 * kq + r)) & 1u;
-        z[rt][r] = ok ? z[rt][r] * zscale : -INFINITY;
-        tmax = fmaxf(tmax, z[rt][r]);
-      }
-    tmax = fmaxf(tmax, shfl_xor_f(tmax, 16));
-    tmax = fmaxf(tmax, shfl_xor_f(tmax, 32));
-    const float m_new = fmaxf(m_run, tmax);
-    const float alpha = (m_new == -INFINITY) ? 1.f : exp2f(m_run - m_new);
-    float p[2][4];
-    float psum = 0.f;
-#pragma unroll
-    for (int rt = 0; rt < 2; ++rt)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        p[rt][r] = (z[rt][r] == -INFINITY) ? 0.f : exp2f(z[rt][r] - m_new);
-        psum += p[rt][r];
-      }
-    psum += shfl_xor_f(psum, 16);
-    psum += shfl_xor_f(psum, 32);
-    l_run = l_run * alpha + psum;
-    m_run = m_new;
-
-    // ---- O = alpha * O + P C over this wave's dims
-    float al[4];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) al[r] = __shfl(alpha, 4 * kq + r, 64);
-    const uint4 pu = make_uint4(pack_bf16x2(p[0][0], p[0][1]), pack_bf16x2(p[0][2], p[0][3]),
-                                pack_bf16x2(p[1][0], p[1][1]), pack_bf16x2(p[1][2], p[1][3]));
-    const bf16x8_t pa = as_bf16x8(pu);
-#pragma unroll
-    for (int dt = 0; dt < 8; ++dt) {
-      const int d = 16 * dt + r16;
-      const uint2 c0 = *(const uint2*)(T + d * kTPitch + 4 * kq);
-      const uint2 c1 = *(const uint2*)(T + d * kTPitch + 16 + 4 * kq);
-      f32x4_t acc = o[dt];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) acc[r] *= al[r];
-      o[dt] = mfma16x16x32(pa, as_bf16x8(make_uint4(c0.x, c0.y, c1.x, c1.y)), acc);
+        for (int i = 0; i < kMaxIdsPerLane; ++i)
+          if (i == slot) e = ids[i];
+        return (e >= 0 && e < a.Nmax) ? ebase + (size_t)e * a.ent_rb : nullptr;
+      };
+      run_rows<EF>(je, j_end, ent_row, qa, zscale, w, lane, R, Sp, st);
     }
   }
 
@@ -302,19 +410,19 @@ __global__ void __launch_bounds__(kAttnThreads) attn_mfma_kernel(AttnArgs a, int
   if (nchunks > 1) {
     Partial* P = part + (unit * (a.H / 16) + hg) * (int64_t)nchunks + chunk;
     if (w == 0 && lane < 16) {
-      P->m[lane] = m_run;
-      P->l[lane] = l_run;
+      P->m[lane] = st.m;
+      P->l[lane] = st.l;
     }
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt)
 #pragma unroll
       for (int r = 0; r < 4; ++r)
-        P->o[(4 * kq + r) * kHeadDim + 128 * w + 16 * dt + r16] = o[dt][r];
+        P->o[(4 * kq + r) * kHeadDim + 128 * w + 16 * dt + r16] = st.o[dt][r];
     return;
   }
   // single chunk: finish here
   const float sink2 = a.sink[16 * hg + r16] * kLog2e;
-  const float den = (m_run == -INFINITY) ? 0.f : l_run + exp2f(sink2 - m_run);
+  const float den = (st.m == -INFINITY) ? 0.f : st.l + exp2f(sink2 - st.m);
   const float inv = den > 0.f ? 1.f / den : 0.f;
   float iv[4];
 #pragma unroll
@@ -324,7 +432,7 @@ __global__ void __launch_bounds__(kAttnThreads) attn_mfma_kernel(AttnArgs a, int
     const int d = 128 * w + 16 * dt + r16;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      float v = o[dt][r] * iv[r];
+      float v = st.o[dt][r] * iv[r];
       const float nb = shfl_xor_f(v, 1);  // pair partner (d ^ 1)
       if (d >= kHeadDim - kRopeDims) {
         const int k = (d - (kHeadDim - kRopeDims)) >> 1;
@@ -338,6 +446,8 @@ __global__ void __launch_bounds__(kAttnThreads) attn_mfma_kernel(AttnArgs a, int
 }
 
 // ------------------------------------------------------------------ merge
+// One work-group per (unit, head group); thread t owns head t/16 and dims
+// [32 (t%16), +32).  Chunks are combined in index order.
 __global__ void __launch_bounds__(kAttnThreads) attn_merge_kernel(AttnArgs a, int nchunks,
                                                                   const Partial* part) {
   __shared__ float sM[16], sInv[16];
@@ -346,7 +456,6 @@ __global__ void __launch_bounds__(kAttnThreads) attn_merge_kernel(AttnArgs a, in
   const int hg = blockIdx.x;
   const Partial* P = part + (unit * (a.H / 16) + hg) * (int64_t)nchunks;
   const int rr = rope_row(a, a.pos[unit]);
-  // per head: global max, chunk-weighted sum and the sink
   if (tid < 16) {
     float M = -INFINITY;
     for (int c = 0; c < nchunks; ++c) M = fmaxf(M, P[c].m[tid]);
@@ -361,30 +470,51 @@ __global__ void __launch_bounds__(kAttnThreads) attn_merge_kernel(AttnArgs a, in
     sInv[tid] = den > 0.f ? 1.f / den : 0.f;
   }
   __syncthreads();
-  // thread -> dim pair (2*tid, 2*tid+1), all 16 heads; chunks in a fixed order
-  const int d = 2 * tid;
-  for (int h = 0; h < 16; ++h) {
-    const float M = sM[h];
-    float x = 0.f, y = 0.f;
-    for (int c = 0; c < nchunks; ++c) {
-      const float mc = P[c].m[h];
-      if (mc == -INFINITY) continue;
-      const float wgt = exp2f(mc - M);
-      x += P[c].o[h * kHeadDim + d] * wgt;
-      y += P[c].o[h * kHeadDim + d + 1] * wgt;
+  const int h = tid >> 4;
+  const int d0 = 32 * (tid & 15);
+  const float M = sM[h];
+  float4 acc[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) acc[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int c = 0; c < nchunks; ++c) {
+    const float mc = P[c].m[h];
+    const float wgt = (mc == -INFINITY) ? 0.f : exp2f(mc - M);
+    const float4* src = (const float4*)(P[c].o + h * kHeadDim + d0);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const float4 v = src[i];
+      acc[i].x += v.x * wgt; acc[i].y += v.y * wgt; acc[i].z += v.z * wgt; acc[i].w += v.w * wgt;
     }
-    x *= sInv[h];
-    y *= sInv[h];
-    if (d >= kHeadDim - kRopeDims) {
-      const int k = (d - (kHeadDim - kRopeDims)) >> 1;
+  }
+  const float inv = sInv[h];
+  float v[32];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    v[4 * i] = acc[i].x * inv; v[4 * i + 1] = acc[i].y * inv;
+    v[4 * i + 2] = acc[i].z * inv; v[4 * i + 3] = acc[i].w * inv;
+  }
+  if (d0 >= kHeadDim - kRopeDims) {
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const int k = (d0 - (kHeadDim - kRopeDims)) / 2 + j;
       const float c = a.rope_cos[(int64_t)rr * 32 + k];
       const float sn = a.rope_sin[(int64_t)rr * 32 + k];
-      const float nx = x * c + y * sn, ny = -x * sn + y * c;
-      x = nx;
-      y = ny;
+      const float x = v[2 * j], y = v[2 * j + 1];
+      v[2 * j] = x * c + y * sn;
+      v[2 * j + 1] = -x * sn + y * c;
     }
-    store_out(a, unit, 16 * hg + h, d, x);
-    store_out(a, unit, 16 * hg + h, d + 1, y);
+  }
+  const int64_t obase = (unit * a.H + 16 * hg + h) * (int64_t)kHeadDim + d0;
+  if (a.out_fmt == CSA_F32) {
+    float4* o = (float4*)((float*)a.out + obase);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) o[i] = make_float4(v[4 * i], v[4 * i + 1], v[4 * i + 2], v[4 * i + 3]);
+  } else {
+    uint4* o = (uint4*)((uint16_t*)a.out + obase);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      o[i] = make_uint4(pack_bf16x2(v[8 * i], v[8 * i + 1]), pack_bf16x2(v[8 * i + 2], v[8 * i + 3]),
+                        pack_bf16x2(v[8 * i + 4], v[8 * i + 5]), pack_bf16x2(v[8 * i + 6], v[8 * i + 7]));
   }
 }
 
@@ -469,6 +599,23 @@ size_t attn_ws_bytes(const AttnArgs& a) {
   return (size_t)a.B * a.Q * (a.H / 16) * nc * sizeof(Partial);
 }
 
+template <int WF>
+static void launch_mfma_w(const AttnArgs& a, int nc, dim3 grid, Partial* part, hipStream_t s) {
+  const int cr = attn_chunk_rows(a);
+  if (a.ent_fmt == CSA_BF16)
+    hipLaunchKernelGGL((attn_mfma_kernel<WF, CSA_BF16>), grid, dim3(kAttnThreads), 0, s, a, cr, nc, part);
+  else if (a.ent_fmt == CSA_FP8_MX32)
+    hipLaunchKernelGGL((attn_mfma_kernel<WF, CSA_FP8_MX32>), grid, dim3(kAttnThreads), 0, s, a, cr, nc, part);
+  else
+    hipLaunchKernelGGL((attn_mfma_kernel<WF, CSA_FP4_E4M3_16>), grid, dim3(kAttnThreads), 0, s, a, cr, nc, part);
+}
+
+static void launch_mfma(const AttnArgs& a, int nc, dim3 grid, Partial* part, hipStream_t s) {
+  if (a.win_fmt == CSA_BF16) launch_mfma_w<CSA_BF16>(a, nc, grid, part, s);
+  else if (a.win_fmt == CSA_FP8_MX32) launch_mfma_w<CSA_FP8_MX32>(a, nc, grid, part, s);
+  else launch_mfma_w<CSA_FP4_E4M3_16>(a, nc, grid, part, s);
+}
+
 hipError_t launch_attention(const AttnArgs& a0, void* ws, hipStream_t s) {
   AttnArgs a = a0;
   a.win_rb = kv_row_bytes(a.win_fmt, kHeadDim);
@@ -482,8 +629,7 @@ hipError_t launch_attention(const AttnArgs& a0, void* ws, hipStream_t s) {
       hipLaunchKernelGGL(attn_f32_kernel, dim3(a.H, nu), dim3(kAttnThreads), 0, s, a);
       continue;
     }
-    hipLaunchKernelGGL(attn_mfma_kernel, dim3(nc, a.H / 16, nu), dim3(kAttnThreads), 0, s, a,
-                       attn_chunk_rows(a), nc, (Partial*)ws);
+    launch_mfma(a, nc, dim3(nc, a.H / 16, nu), (Partial*)ws, s);
     if (nc > 1)
       hipLaunchKernelGGL(attn_merge_kernel, dim3(a.H / 16, nu), dim3(kAttnThreads), 0, s, a, nc,
                          (const Partial*)ws);

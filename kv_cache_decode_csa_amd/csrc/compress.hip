@@ -74,6 +74,95 @@ __global__ void __launch_bounds__(kThreads) proj_gemv_kernel(const void* __restr
   }
 }
 
+// MFMA projection for bf16 x and W with M = B*T <= 64 (decode): each work-group
+// streams 16 weight rows over the whole of K with 8 waves, each wave taking
+// 1/8 of K in steps of 8 x 32 (eight 16-byte loads in flight per lane).  The
+// waves' 16x16 partial products are summed in LDS in a fixed order.  A lane
+// holds x[m][k + 8 kq .. +8] (A) and W[n][k + 8 kq .. +8] (B): contiguous
+// 16-byte loads.  Single-token calls write the result straight into the slot
+// state (score gets its slot bias); otherwise into P[M][N].
+constexpr int kMfmaMaxM = 64;
+constexpr int kProjThreads = 512;
+
+struct ProjOut {
+  float* P;                   // [M][N] when not direct
+  int direct;                 // 1: T == 1, write state slots
+  const int32_t* start_pos;   // [B]
+  const float* ape;           // [ratio][CD]
+  int ratio, coff;
+  float* kv_state;            // [B][coff*ratio][CD]
+  float* score_state;
+};
+
+template <int MT>
+__global__ void __launch_bounds__(kProjThreads) proj_mfma_kernel(const uint16_t* __restrict__ x,
+                                                                 const uint16_t* __restrict__ wkv,
+                                                                 const uint16_t* __restrict__ wg,
+                                                                 int M, int K, int CD, ProjOut po) {
+  __shared__ f32x4_t red[8][MT][64];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int r16 = lane & 15, kq = lane >> 4;
+  const int N = 2 * CD;
+  const int n = blockIdx.x * 16 + r16;
+  const uint16_t* wrow = n < CD ? wkv + (int64_t)n * K : wg + (int64_t)(n - CD) * K;
+  const int kwave = K / 8;
+  const int kb = wave * kwave;
+  f32x4_t acc[MT];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) acc[mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  for (int k = kb; k < kb + kwave; k += 256) {
+    uint4 bw[8];
+    uint4 ax[8][MT];
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      bw[u] = k + 32 * u < kb + kwave ? *(const uint4*)(wrow + k + 32 * u + 8 * kq)
+                                      : make_uint4(0, 0, 0, 0);
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        const int m = 16 * mt + r16;
+        ax[u][mt] = (m < M && k + 32 * u < kb + kwave)
+                        ? *(const uint4*)(x + (int64_t)m * K + k + 32 * u + 8 * kq)
+                        : make_uint4(0, 0, 0, 0);
+      }
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+        acc[mt] = mfma16x16x32(as_bf16x8(ax[u][mt]), as_bf16x8(bw[u]), acc[mt]);
+  }
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) red[wave][mt][lane] = acc[mt];
+  __syncthreads();
+  const int t = threadIdx.x;
+  if (t < MT * 64) {
+    const int mt = t >> 6, l = t & 63;
+    f32x4_t v = red[0][mt][l];
+#pragma unroll
+    for (int w = 1; w < 8; ++w) {
+      const f32x4_t u = red[w][mt][l];
+      v[0] += u[0]; v[1] += u[1]; v[2] += u[2]; v[3] += u[3];
+    }
+    const int nn = blockIdx.x * 16 + (l & 15);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int m = 16 * mt + 4 * (l >> 4) + r;
+      if (m >= M) continue;
+      if (!po.direct) {
+        po.P[(int64_t)m * N + nn] = v[r];
+        continue;
+      }
+      const int64_t p = po.start_pos[m];
+      if (p < 0) continue;
+      const int slot = (po.coff == 2 ? po.ratio : 0) + (int)(p % po.ratio);
+      const int64_t base = ((int64_t)m * po.coff * po.ratio + slot) * CD;
+      if (nn < CD) po.kv_state[base + nn] = v[r];
+      else po.score_state[base + nn - CD] = v[r] + po.ape[(p % po.ratio) * CD + nn - CD];
+    }
+  }
+}
+
 // Tiled GEMM, float32 FMA: P[m][n] = sum_k x[m][k] W[n][k], 64x64 tiles.
 constexpr int kTM = 64, kTN = 64, kTK = 32;
 
@@ -172,58 +261,60 @@ __device__ __forceinline__ void token_vs(const CompArgs& a, int64_t b, int64_t p
 }
 
 // ------------------------------------------------------------------ emit
-__global__ void __launch_bounds__(kThreads) emit_kernel(CompArgs a) {
-  __shared__ float y[512];
-  __shared__ float red[4];
+// Pool block i of sequence b into y[0, d) (reads only); returns this thread's
+// sum of squares.
+__device__ float pool_block(const CompArgs& a, int64_t b, int64_t p0, int64_t i, float* y) {
   const int tid = threadIdx.x;
-  const int64_t b = blockIdx.y;
-  const int64_t p0 = a.start_pos[b];
   const int r = a.ratio;
-  const int64_t i = p0 / r + blockIdx.x;              // candidate block
-  if (p0 < 0 || (i + 1) * r - 1 >= p0 + a.T) return;  // not completed by this call
   const int d = a.d;
-
-  // pool each channel over its slots
+  // pool each channel over its slots: loads of 8 slots are issued together and
+  // folded into a running max / sum (online softmax over the slot axis)
   float sq = 0.f;
+  const int nslots = a.coff * r;
   for (int c = tid; c < d; c += kThreads) {
-    float mx = -INFINITY;
-    // first pass: max score
-    const int nslots = a.coff * r;
-    for (int sl = 0; sl < nslots; ++sl) {
-      int64_t p;
-      int col;
-      if (a.coff == 2) {
-        p = sl < r ? (i - 1) * r + sl : i * r + (sl - r);
-        col = sl < r ? c : d + c;
-      } else {
-        p = i * r + sl;
-        col = c;
+    float m = -INFINITY, l = 0.f, acc = 0.f;
+    for (int sl0 = 0; sl0 < nslots; sl0 += 8) {
+      float vv[8], ss[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int sl = sl0 + j;
+        if (sl >= nslots) { vv[j] = 0.f; ss[j] = -INFINITY; continue; }
+        int64_t p;
+        int col;
+        if (a.coff == 2) {
+          p = sl < r ? (i - 1) * r + sl : i * r + (sl - r);
+          col = sl < r ? c : d + c;
+        } else {
+          p = i * r + sl;
+          col = c;
+        }
+        token_vs(a, b, p0, p, col, vv[j], ss[j]);
       }
-      float v, s;
-      token_vs(a, b, p0, p, col, v, s);
-      mx = fmaxf(mx, s);
-    }
-    float num = 0.f, den = 0.f;
-    for (int sl = 0; sl < nslots; ++sl) {
-      int64_t p;
-      int col;
-      if (a.coff == 2) {
-        p = sl < r ? (i - 1) * r + sl : i * r + (sl - r);
-        col = sl < r ? c : d + c;
-      } else {
-        p = i * r + sl;
-        col = c;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        if (ss[j] == -INFINITY) continue;
+        const float mn = fmaxf(m, ss[j]);
+        const float sc = expf(m - mn);  // 0 while m is -inf
+        const float e = expf(ss[j] - mn);
+        l = l * sc + e;
+        acc = acc * sc + e * vv[j];
+        m = mn;
       }
-      float v, s;
-      token_vs(a, b, p0, p, col, v, s);
-      const float e = (s == -INFINITY) ? 0.f : expf(s - mx);
-      num = fmaf(e, v, num);
-      den += e;
     }
-    const float C = num / den;
+    const float C = acc / l;
     y[c] = C;
     sq = fmaf(C, C, sq);
   }
+  return sq;
+}
+
+// RMSNorm -> RoPE at position i * r -> optional Hadamard -> storage rounding of
+// the pooled block in y; writes entry i of sequence b.
+__device__ void finish_block(const CompArgs& a, int64_t b, int64_t i, float* y, float* red,
+                             float sq) {
+  const int tid = threadIdx.x;
+  const int r = a.ratio;
+  const int d = a.d;
   sq = wave_sum(sq);
   if ((tid & 63) == 0) red[tid >> 6] = sq;
   __syncthreads();
@@ -272,6 +363,18 @@ __global__ void __launch_bounds__(kThreads) emit_kernel(CompArgs a) {
   }
 }
 
+__global__ void __launch_bounds__(kThreads) emit_kernel(CompArgs a) {
+  __shared__ float y[512];
+  __shared__ float red[4];
+  const int64_t b = blockIdx.y;
+  const int64_t p0 = a.start_pos[b];
+  const int r = a.ratio;
+  const int64_t i = p0 / r + blockIdx.x;              // candidate block
+  if (p0 < 0 || (i + 1) * r - 1 >= p0 + a.T) return;  // not completed by this call
+  const float sq = pool_block(a, b, p0, i, y);
+  finish_block(a, b, i, y, red, sq);
+}
+
 // ------------------------------------------------------------------ state
 // New slot contents after the call, as the token-by-token decode state machine
 // leaves them: the unfinished block's tokens in their current slots; if a
@@ -279,10 +382,7 @@ __global__ void __launch_bounds__(kThreads) emit_kernel(CompArgs a) {
 // every previous slot) holds the last completed block.  Slots whose token
 // precedes the call keep their value, except the overlap shift, which copies
 // current slots into previous ones -- done from values read before any write.
-__global__ void __launch_bounds__(kThreads) state_kernel(CompArgs a) {
-  const int64_t b = blockIdx.y;
-  const int col = blockIdx.x * kThreads + threadIdx.x;
-  if (col >= a.CD) return;
+__device__ void state_column(const CompArgs& a, int64_t b, int col) {
   const int64_t p0 = a.start_pos[b];
   if (p0 < 0) return;
   const int r = a.ratio;
@@ -343,11 +443,85 @@ __global__ void __launch_bounds__(kThreads) state_kernel(CompArgs a) {
   }
 }
 
+__global__ void __launch_bounds__(kThreads) state_kernel(CompArgs a) {
+  const int col = blockIdx.x * kThreads + threadIdx.x;
+  if (col < a.CD) state_column(a, blockIdx.y, col);
+}
+
+// Single-token calls: the projection already wrote the token into its slot.
+// One work-group per sequence whose block just completed pools the block from
+// the slot state, shifts the current slots into the previous ones (overlap),
+// then finishes the entry.
+__global__ void __launch_bounds__(kThreads) emit_t1_kernel(CompArgs a) {
+  __shared__ float y[512];
+  __shared__ float red[4];
+  const int64_t b = blockIdx.x;
+  const int64_t p0 = a.start_pos[b];
+  const int r = a.ratio;
+  if (p0 < 0 || (p0 + 1) % r != 0) return;
+  const int64_t i = p0 / r;
+  const int d = a.d, tid = threadIdx.x;
+  const int nslots = a.coff * r;
+  const int64_t sb = b * (int64_t)nslots * a.CD;
+  float sq = 0.f;
+  for (int c = tid; c < d; c += kThreads) {
+    float m = -INFINITY, l = 0.f, acc = 0.f;
+    for (int sl0 = 0; sl0 < nslots; sl0 += 8) {
+      float vv[8], ss[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int sl = sl0 + j;
+        const int col = (a.coff == 2 && sl >= r) ? d + c : c;
+        const int64_t si = sb + (int64_t)sl * a.CD + col;
+        vv[j] = sl < nslots ? a.kv_state[si] : 0.f;
+        ss[j] = sl < nslots ? a.score_state[si] : -INFINITY;
+      }
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        if (ss[j] == -INFINITY) continue;
+        const float mn = fmaxf(m, ss[j]);
+        const float scl = expf(m - mn);
+        const float e = expf(ss[j] - mn);
+        l = l * scl + e;
+        acc = acc * scl + e * vv[j];
+        m = mn;
+      }
+    }
+    const float C = acc / l;
+    y[c] = C;
+    sq = fmaf(C, C, sq);
+  }
+  __syncthreads();  // every read of the slots is done
+  if (a.coff == 2) {
+    for (int col = tid; col < a.CD; col += kThreads) {
+      float kv[4], sc[4];  // all loads first, then all stores
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        kv[q] = a.kv_state[sb + (int64_t)(r + q) * a.CD + col];
+        sc[q] = a.score_state[sb + (int64_t)(r + q) * a.CD + col];
+      }
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        a.kv_state[sb + (int64_t)q * a.CD + col] = kv[q];
+        a.score_state[sb + (int64_t)q * a.CD + col] = sc[q];
+      }
+    }
+  }
+  finish_block(a, b, i, y, red, sq);
+}
+
 }  // namespace
+
+// The MFMA projection serves bf16 calls with B*T <= 64 and dim % 256 == 0.
+static bool use_mfma_proj(const csa_compress_args* a) {
+  const int64_t M = (int64_t)a->B * a->T;
+  return a->x_fmt == CSA_BF16 && a->w_fmt == CSA_BF16 && M <= kMfmaMaxM && a->dim % 256 == 0;
+}
 
 size_t compress_ws_bytes(const csa_compress_args* a) {
   const int coff = a->ratio == 4 ? 2 : 1;
   const int CD = coff * a->head_dim;
+  if (a->T == 1 && use_mfma_proj(a)) return 0;  // written straight into the slot state
   return align_up((size_t)a->B * a->T * 2 * CD * sizeof(float), 256);
 }
 
@@ -377,7 +551,20 @@ hipError_t launch_compress(const csa_compress_args* in, void* ws, hipStream_t s)
   a.P = P;
   const int64_t M = (int64_t)in->B * in->T;
   const int N = 2 * a.CD;
-  if (M <= kGemvMaxM) {
+  const bool direct = in->T == 1 && use_mfma_proj(in);
+  if (use_mfma_proj(in)) {
+    const int mt = (int)((M + 15) / 16);
+    ProjOut po{P, direct ? 1 : 0, in->start_pos, in->ape, in->ratio, a.coff, in->kv_state,
+               in->score_state};
+    dim3 grid(N / 16);
+    const uint16_t* xp = (const uint16_t*)in->x;
+    const uint16_t* wk = (const uint16_t*)in->w_kv;
+    const uint16_t* wgp = (const uint16_t*)in->w_gate;
+    if (mt == 1) hipLaunchKernelGGL(proj_mfma_kernel<1>, grid, dim3(kProjThreads), 0, s, xp, wk, wgp, (int)M, in->dim, a.CD, po);
+    else if (mt == 2) hipLaunchKernelGGL(proj_mfma_kernel<2>, grid, dim3(kProjThreads), 0, s, xp, wk, wgp, (int)M, in->dim, a.CD, po);
+    else if (mt == 3) hipLaunchKernelGGL(proj_mfma_kernel<3>, grid, dim3(kProjThreads), 0, s, xp, wk, wgp, (int)M, in->dim, a.CD, po);
+    else hipLaunchKernelGGL(proj_mfma_kernel<4>, grid, dim3(kProjThreads), 0, s, xp, wk, wgp, (int)M, in->dim, a.CD, po);
+  } else if (M <= kGemvMaxM) {
     hipLaunchKernelGGL(proj_gemv_kernel, dim3((N + 7) / 8), dim3(kThreads), 0, s, in->x,
                        in->x_fmt, in->w_kv, in->w_gate, in->w_fmt, (int)M, in->dim, a.CD, P);
   } else {
@@ -391,6 +578,10 @@ hipError_t launch_compress(const csa_compress_args* in, void* ws, hipStream_t s)
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
+  if (direct) {
+    hipLaunchKernelGGL(emit_t1_kernel, dim3(in->B), dim3(kThreads), 0, s, a);
+    return hipGetLastError();
+  }
   const int max_blocks = in->T / in->ratio + 1;
   hipLaunchKernelGGL(emit_kernel, dim3(max_blocks, in->B), dim3(kThreads), 0, s, a);
   e = hipGetLastError();

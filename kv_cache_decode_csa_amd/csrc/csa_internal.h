@@ -31,8 +31,8 @@ hipError_t launch_dequantize(const void* src, int src_fmt, void* dst, int dst_fm
 
 // top-k workspace layout for R rows
 struct TopkWs {
-  uint32_t* hist;    // [R][kHistBins]
-  uint32_t* ctr;     // [R][4]: n_hi, n_eq, done, pad
+  uint32_t* hist;    // [R][kHistBins] first digit (key bits 31..20)
+  uint32_t* ctr;     // [R][8]: per-row counters and boundary-bin info
   uint32_t* cand;    // [R][kCandCap][2] (key, idx) for the boundary bin
   uint32_t* hi;      // [R][kTopkMax][2] (key, idx) above the boundary bin
 };

@@ -14,18 +14,65 @@ namespace csa {
 namespace {
 
 constexpr int kIdxThreads = 256;
-constexpr int kKeysPerWave = 16;
-constexpr int kIters = 16;                                     // 16-key groups per wave
-constexpr int kKeysPerWg = kKeysPerWave * 4 * kIters;          // 1024
+constexpr int kKeysPerWg = 4096;                               // keys scored by one work-group
+// 16-key MFMA tiles per wave step: FP8 rows are small enough to keep four
+// tiles (64 keys, 8.4 KB per wave) and their successors in flight.
+template <int KFMT> constexpr int tiles_per_iter() { return KFMT == CSA_FP8_MX32 ? 4 : 2; }
 
-// 8 E4M3 codes (two dwords) times 2**e -> 8 exact bf16 values
-__device__ __forceinline__ uint4 fp8x8_to_bf16x8(uint32_t lo, uint32_t hi, float scale) {
-  uint4 r;
-  r.x = pack_bf16x2_exact(e4m3_to_f32(lo) * scale, e4m3_to_f32(lo >> 8) * scale);
-  r.y = pack_bf16x2_exact(e4m3_to_f32(lo >> 16) * scale, e4m3_to_f32(lo >> 24) * scale);
-  r.z = pack_bf16x2_exact(e4m3_to_f32(hi) * scale, e4m3_to_f32(hi >> 8) * scale);
-  r.w = pack_bf16x2_exact(e4m3_to_f32(hi >> 16) * scale, e4m3_to_f32(hi >> 24) * scale);
-  return r;
+// Keys are read with a permuted contraction order: lane (r16, kq) holds, for
+// key r16 of its tile, the 32 contiguous dims [32 kq, 32 kq + 32) -- one FP8
+// scale group -- and MFMA k-step s covers dims {32 kq + 8 s + j}.  The query
+// fragments use the same order, so every dot product is unchanged while each
+// lane issues one contiguous 32-byte (FP8) or 64-byte (bf16) read per key.
+struct KeyRaw {
+  uint32_t w[16];   // fp8: w[0..7] codes, w[8] scale byte; bf16: w[0..15]
+};
+
+template <int KFMT>
+__device__ __forceinline__ void load_key(const uint8_t* kr, int kq, bool valid, KeyRaw& r) {
+  if (KFMT == CSA_FP8_MX32) {
+    if (valid) {
+      const uint32_t* p = (const uint32_t*)(kr + 32 * kq);  // rows of 132 B: dword aligned
+#pragma unroll
+      for (int i = 0; i < 8; ++i) r.w[i] = p[i];
+      r.w[8] = kr[128 + kq];
+    } else {
+#pragma unroll
+      for (int i = 0; i < 9; ++i) r.w[i] = 0;
+    }
+  } else {
+    if (valid) {
+      const uint4* p = (const uint4*)(kr + 64 * kq);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        uint4 v = p[i];
+        r.w[4 * i] = v.x; r.w[4 * i + 1] = v.y; r.w[4 * i + 2] = v.z; r.w[4 * i + 3] = v.w;
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) r.w[i] = 0;
+    }
+  }
+}
+
+// k-step s operand (8 bf16) from the raw lane data; FP8 codes are decoded by
+// the hardware scaled conversion (exact: E4M3 x 2^e fits bf16).
+template <int KFMT>
+__device__ __forceinline__ bf16x8_t key_frag(const KeyRaw& r, int s) {
+  if (KFMT == CSA_FP8_MX32) {
+    const float sc = exp2i((int)(r.w[8] & 0xffu) - 127);
+    const uint32_t lo = r.w[2 * s], hi = r.w[2 * s + 1];
+    typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2_t;
+    bf16x2_t a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, sc, false);
+    bf16x2_t b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, sc, true);
+    bf16x2_t c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, sc, false);
+    bf16x2_t d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, sc, true);
+    uint4 u = make_uint4(__builtin_bit_cast(uint32_t, a), __builtin_bit_cast(uint32_t, b),
+                         __builtin_bit_cast(uint32_t, c), __builtin_bit_cast(uint32_t, d));
+    return as_bf16x8(u);
+  } else {
+    return as_bf16x8(make_uint4(r.w[4 * s], r.w[4 * s + 1], r.w[4 * s + 2], r.w[4 * s + 3]));
+  }
 }
 
 template <int HT, int KFMT>
@@ -36,6 +83,8 @@ __global__ void __launch_bounds__(kIdxThreads) index_scores_mfma(
     uint32_t* __restrict__ hist_g) {
   constexpr int Hi = HT * 16;
   constexpr int64_t kRowBytes = KFMT == CSA_FP8_MX32 ? 132 : 256;
+  constexpr int kTilesPerIter = tiles_per_iter<KFMT>();
+  constexpr int kKeysPerIter = 16 * kTilesPerIter;
   __shared__ uint32_t hist[kHistBins];
 
   const int t = threadIdx.x;
@@ -51,17 +100,17 @@ __global__ void __launch_bounds__(kIdxThreads) index_scores_mfma(
 
   for (int i = t; i < kHistBins; i += kIdxThreads) hist[i] = 0;
 
-  // query fragments (MFMA A operand): head 16*mt + lane%16, dims 32*s + 8*(lane/16) .. +8
   const int r16 = lane & 15;
   const int kq = lane >> 4;
+  // query fragments (A operand): head 16 mt + r16, dims 32 kq + 8 s .. +8
   uint4 qa[HT][4];
   const uint16_t* qrow = q_idx + row * (int64_t)Hi * kIndexDim;
 #pragma unroll
   for (int mt = 0; mt < HT; ++mt)
 #pragma unroll
     for (int s = 0; s < 4; ++s)
-      qa[mt][s] = *(const uint4*)(qrow + (16 * mt + r16) * kIndexDim + 32 * s + 8 * kq);
-  // head weights for the D layout: head 16*mt + 4*(lane/16) + r
+      qa[mt][s] = *(const uint4*)(qrow + (16 * mt + r16) * kIndexDim + 32 * kq + 8 * s);
+  // head weights in the D layout: head 16 mt + 4 kq + r
   float wv[HT][4];
   const float* wrow = w_idx + row * (int64_t)Hi;
 #pragma unroll
@@ -72,51 +121,47 @@ __global__ void __launch_bounds__(kIdxThreads) index_scores_mfma(
 
   const uint8_t* kbase = k_idx + b * Nmax * kRowBytes;
   float* srow = scores + row * Nmax;
-
-  for (int it = 0; it < kIters; ++it) {
-    const int64_t key0 = base + (int64_t)kKeysPerWave * (wave + 4 * it);
-    if (key0 >= nv) break;
-    const int64_t key = key0 + r16;
-    const bool valid = key < nv;
-    uint4 kb[4];
-    if (KFMT == CSA_FP8_MX32) {
-      const uint8_t* kr = kbase + key * kRowBytes;
-      uint32_t lo[4], hi[4], sc = 0;
-      if (valid) {
-        sc = *(const uint32_t*)(kr + 128);
+  int64_t end = base + kKeysPerWg;
+  if (end > nv) end = nv;
+  // wave w scores keys [base + K (w + 4 i), +K) for i = 0, 1, ... (K keys per step)
+  int64_t k0 = base + (int64_t)kKeysPerIter * wave;
+  KeyRaw cur[kTilesPerIter], nxt[kTilesPerIter];
 #pragma unroll
-        for (int s = 0; s < 4; ++s) {
-          lo[s] = *(const uint32_t*)(kr + 32 * s + 8 * kq);
-          hi[s] = *(const uint32_t*)(kr + 32 * s + 8 * kq + 4);
-        }
-      } else {
+  for (int nt = 0; nt < kTilesPerIter; ++nt) {
+    const int64_t key = k0 + 16 * nt + r16;
+    load_key<KFMT>(kbase + key * kRowBytes, kq, key < end, cur[nt]);
+  }
+  for (; k0 < end; k0 += 4 * kKeysPerIter) {
+    const int64_t k1 = k0 + 4 * kKeysPerIter;
 #pragma unroll
-        for (int s = 0; s < 4; ++s) lo[s] = hi[s] = 0;
+    for (int nt = 0; nt < kTilesPerIter; ++nt) {  // prefetch the next step
+      const int64_t key = k1 + 16 * nt + r16;
+      load_key<KFMT>(kbase + key * kRowBytes, kq, key < end, nxt[nt]);
+    }
+#pragma unroll
+    for (int nt = 0; nt < kTilesPerIter; ++nt) {
+      bf16x8_t kb[4];
+#pragma unroll
+      for (int s = 0; s < 4; ++s) kb[s] = key_frag<KFMT>(cur[nt], s);
+      float p = 0.f;
+#pragma unroll
+      for (int mt = 0; mt < HT; ++mt) {
+        f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < 4; ++s) acc = mfma16x16x32(as_bf16x8(qa[mt][s]), kb[s], acc);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) p += wv[mt][r] * fmaxf(acc[r], 0.f);
       }
-#pragma unroll
-      for (int s = 0; s < 4; ++s)
-        kb[s] = fp8x8_to_bf16x8(lo[s], hi[s], exp2i((int)((sc >> (8 * s)) & 0xffu) - 127));
-    } else {
-      const uint16_t* kr = (const uint16_t*)(kbase + key * kRowBytes);
-#pragma unroll
-      for (int s = 0; s < 4; ++s)
-        kb[s] = valid ? *(const uint4*)(kr + 32 * s + 8 * kq) : make_uint4(0, 0, 0, 0);
+      p += shfl_xor_f(p, 16);
+      p += shfl_xor_f(p, 32);
+      const int64_t key = k0 + 16 * nt + r16;
+      if (kq == 0 && key < end) {
+        srow[key] = p;
+        atomicAdd(&hist[score_key(p) >> 20], 1u);
+      }
     }
-    float p = 0.f;
 #pragma unroll
-    for (int mt = 0; mt < HT; ++mt) {
-      f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int s = 0; s < 4; ++s) acc = mfma16x16x32(as_bf16x8(qa[mt][s]), as_bf16x8(kb[s]), acc);
-#pragma unroll
-      for (int r = 0; r < 4; ++r) p += wv[mt][r] * fmaxf(acc[r], 0.f);
-    }
-    p += shfl_xor_f(p, 16);
-    p += shfl_xor_f(p, 32);
-    if (kq == 0 && valid) {
-      srow[key] = p;
-      atomicAdd(&hist[score_key(p) >> 20], 1u);
-    }
+    for (int nt = 0; nt < kTilesPerIter; ++nt) cur[nt] = nxt[nt];
   }
   __syncthreads();
   uint32_t* g = hist_g + row * kHistBins;

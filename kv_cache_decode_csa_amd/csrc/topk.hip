@@ -25,30 +25,9 @@ constexpr int kChunk = 8192;       // elements scanned per work-group
 constexpr int kSortCap = kTopkMax; // winners above the threshold
 constexpr int kTieCap = kCandCap;  // equal-to-threshold entries sorted by index
 
-struct RowCtr {
-  uint32_t n_hi, n_eq, done, pad;
-};
 
 __device__ __forceinline__ bool before(uint32_t ka, uint32_t ia, uint32_t kb, uint32_t ib) {
   return ka > kb || (ka == kb && ia < ib);
-}
-
-// Bitonic sort of n (power of two) (key, idx) pairs in LDS, key desc / idx asc.
-__device__ void bitonic_pairs(uint32_t* key, uint32_t* idx, int n) {
-  for (int k = 2; k <= n; k <<= 1) {
-    for (int j = k >> 1; j > 0; j >>= 1) {
-      for (int i = threadIdx.x; i < n; i += blockDim.x) {
-        int p = i ^ j;
-        if (p > i) {
-          bool up = (i & k) == 0;
-          uint32_t ki = key[i], kp = key[p], ii = idx[i], ip = idx[p];
-          bool swap = up ? before(kp, ip, ki, ii) : before(ki, ii, kp, ip);
-          if (swap) { key[i] = kp; key[p] = ki; idx[i] = ip; idx[p] = ii; }
-        }
-      }
-      __syncthreads();
-    }
-  }
 }
 
 // Bitonic sort of n (power of two) uint32 ascending.
@@ -75,48 +54,79 @@ __device__ __forceinline__ int pow2_at_least(int n) {
 }
 
 // Find the largest bin b with sum_{b' >= b} hist[b'] >= need (need >= 1 and the
-// total >= need).  hist lives in LDS, nbins is a multiple of kSelThreads.
-// Returns b and writes the count strictly above b to *above.  Ends synced.
+// total >= need).  hist lives in LDS; nbins is a multiple of kSelThreads.
+// Returns b and writes the count strictly above b to *above.  Every thread
+// sums its own bins, a wave-level suffix scan plus the higher waves' totals
+// gives each thread the count at and above its bins, and the single thread
+// whose range crosses `need` resolves the bin.  Ends synced.
 __device__ int suffix_find(const uint32_t* hist, int nbins, uint32_t need, uint32_t* above,
-                           uint32_t* scratch /* LDS, kSelThreads + 2 */) {
+                           uint32_t* scratch /* LDS, kSelThreads + 8 */) {
   const int per = nbins / kSelThreads;
-  const int t = threadIdx.x;
+  const int t = threadIdx.x, lane = t & 63, w = t >> 6;
   uint32_t local = 0;
   for (int j = 0; j < per; ++j) local += hist[t * per + j];
-  scratch[t] = local;
+  uint32_t v = local;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    uint32_t n = __shfl_down(v, off, 64);
+    if (lane + off < 64) v += n;
+  }
+  if (lane == 0) scratch[w] = v;
   __syncthreads();
-  if (t == 0) {
-    // serial suffix over thread totals (256 adds), then within the owner
-    uint32_t acc = 0;
-    int owner = 0;
-    for (int u = kSelThreads - 1; u >= 0; --u) {
-      if (acc + scratch[u] >= need) { owner = u; break; }
-      acc += scratch[u];
-    }
-    int b = owner * per;
+  uint32_t S = v;
+  for (int u = w + 1; u < kSelThreads / 64; ++u) S += scratch[u];
+  const uint32_t prev = S - local;
+  if (S >= need && prev < need) {
+    uint32_t acc = prev;
+    int b = t * per;
     for (int j = per - 1; j >= 0; --j) {
-      uint32_t h = hist[owner * per + j];
-      if (acc + h >= need) { b = owner * per + j; break; }
+      const uint32_t h = hist[t * per + j];
+      if (acc + h >= need) { b = t * per + j; break; }
       acc += h;
     }
     scratch[kSelThreads] = (uint32_t)b;
     scratch[kSelThreads + 1] = acc;
   }
   __syncthreads();
-  int b = (int)scratch[kSelThreads];
+  const int b = (int)scratch[kSelThreads];
   *above = scratch[kSelThreads + 1];
   __syncthreads();
   return b;
 }
 
+// Sort n pairs (n <= kSortCap) by (key desc, idx asc) and write the indices to
+// out[0, n).  The pair is packed as key << 32 | ~idx, so one descending 64-bit
+// bitonic network over the next power of two orders both keys at once.
+__device__ void sort_store(const uint32_t* key, const uint32_t* idx, int n, uint64_t* tmp,
+                           int32_t* out) {
+  int p2 = 1;
+  while (p2 < n) p2 <<= 1;
+  for (int i = threadIdx.x; i < p2; i += blockDim.x)
+    tmp[i] = i < n ? (((uint64_t)key[i] << 32) | (uint64_t)(~idx[i])) : 0ull;
+  __syncthreads();
+  for (int k = 2; k <= p2; k <<= 1) {
+    for (int j = k >> 1; j > 0; j >>= 1) {
+      for (int i = threadIdx.x; i < p2 / 2; i += blockDim.x) {
+        const int lo = (i / j) * 2 * j + (i % j), hi = lo + j;
+        const bool desc = (lo & k) == 0;
+        const uint64_t a = tmp[lo], b = tmp[hi];
+        if (desc ? (a < b) : (a > b)) { tmp[lo] = b; tmp[hi] = a; }
+      }
+      __syncthreads();
+    }
+  }
+  for (int i = threadIdx.x; i < n; i += blockDim.x) out[i] = (int32_t)(~(uint32_t)tmp[i]);
+}
+
 struct LdsSel {
   uint32_t hist[kHistBins];
-  uint32_t scratch[kSelThreads + 8];
+  uint32_t scratch[kSelThreads + 16];
   uint32_t skey[kSortCap];
   uint32_t sidx[kSortCap];
-  uint32_t ties[kTieCap];
+  uint32_t ties[kTieCap];          // also the 64-bit sort buffer (kTieCap / 2 >= kSortCap)
   uint32_t n_sel, n_ties, flag;
 };
+static_assert(kTieCap / 2 >= kSortCap, "sort buffer");
 
 // Source of (key, idx) pairs for the refinement: either the boundary-bin list
 // of a row (unordered) or the whole row of scores (index order).
@@ -244,7 +254,7 @@ __global__ void __launch_bounds__(kSelThreads) topk_clear_kernel(uint32_t* hist,
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
        i += (int64_t)gridDim.x * blockDim.x) {
     hist[i] = 0;
-    if (i < R * 4) ctr[i] = 0;
+    if (i < R * 8) ctr[i] = 0;
   }
 }
 
@@ -269,11 +279,84 @@ __global__ void __launch_bounds__(kSelThreads) topk_hist_kernel(const float* __r
     if (h[i]) atomicAdd(&g[i], h[i]);
 }
 
-__global__ void __launch_bounds__(kSelThreads) topk_select_kernel(
+constexpr int kCandPerThread = kCandCap / kSelThreads;   // 32
+constexpr int kHiPerThread = kTopkMax / kSelThreads;      // 8
+
+// Descending sort of 512 packed values held two per lane (element
+// e = 128 wave + 2 lane + i).  Bitonic network: partners within a lane or a
+// wave are exchanged with register moves and cross-lane shuffles; only the
+// stages whose partner lives in another wave go through LDS (3 of 45).
+__device__ void sort512_desc(uint64_t (&v)[2], uint64_t* lds) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int e0 = 128 * wave + 2 * lane;
+  for (int k = 2; k <= 512; k <<= 1) {
+    for (int j = k >> 1; j > 0; j >>= 1) {
+      if (j == 1) {
+        const bool desc = (e0 & k) == 0;
+        if (desc ? (v[0] < v[1]) : (v[0] > v[1])) { const uint64_t x = v[0]; v[0] = v[1]; v[1] = x; }
+      } else if (j < 128) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+          const uint32_t lo = __shfl_xor((uint32_t)v[i], j >> 1, 64);
+          const uint32_t hi = __shfl_xor((uint32_t)(v[i] >> 32), j >> 1, 64);
+          const uint64_t pv = ((uint64_t)hi << 32) | lo;
+          const int e = e0 + i;
+          const bool keep_max = ((e & j) == 0) == ((e & k) == 0);
+          v[i] = keep_max ? (v[i] > pv ? v[i] : pv) : (v[i] < pv ? v[i] : pv);
+        }
+      } else {
+        __syncthreads();
+        lds[e0] = v[0];
+        lds[e0 + 1] = v[1];
+        __syncthreads();
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+          const int e = e0 + i;
+          const uint64_t pv = lds[e ^ j];
+          const bool keep_max = ((e & j) == 0) == ((e & k) == 0);
+          v[i] = keep_max ? (v[i] > pv ? v[i] : pv) : (v[i] < pv ? v[i] : pv);
+        }
+      }
+    }
+  }
+}
+
+// Write the indices of n <= kSortCap (key, idx) pairs ordered by key desc,
+// idx asc (pairs packed as key << 32 | ~idx).
+__device__ void order_store(const uint32_t* key, const uint32_t* idx, int n, uint64_t* tmp,
+                            int32_t* out) {
+  if (n <= 512) {
+    const int e0 = 128 * (threadIdx.x >> 6) + 2 * (threadIdx.x & 63);
+    uint64_t v[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int e = e0 + i;
+      v[i] = e < n ? (((uint64_t)key[e] << 32) | (uint64_t)(~idx[e])) : 0ull;
+    }
+    sort512_desc(v, tmp);
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+      if (e0 + i < n) out[e0 + i] = (int32_t)(~(uint32_t)v[i]);
+    return;
+  }
+  sort_store(key, idx, n, tmp, out);
+}
+
+struct RowInfo {       // written by work-group 0 of each row's collect pass
+  unsigned long long counts;  // n_hi | n_eq << 32 (atomic)
+  uint32_t b1, above, eq, pad;
+};
+
+// Pass 1, every chunk of every row: the first digit's boundary bin from the
+// row histogram, then this chunk's entries above the bin go to the row's hi
+// list and those inside it to the candidate list.  Each thread keeps its keys
+// in registers, a block-wide prefix gives every entry its slot, and one
+// 64-bit atomic per work-group reserves its ranges in both lists.
+__global__ void __launch_bounds__(kSelThreads) topk_collect_kernel(
     const float* __restrict__ scores, const int32_t* __restrict__ n_valid, int64_t ld, int topk,
-    int32_t* __restrict__ out_idx, const uint32_t* hist_g, RowCtr* ctr_g, uint32_t* cand_g,
-    uint32_t* hi_g) {
-  __shared__ LdsSel L;
+    const uint32_t* hist_g, RowInfo* info_g, uint32_t* cand_g, uint32_t* hi_g) {
+  __shared__ uint32_t hist[kHistBins];
+  __shared__ uint32_t scratch[kSelThreads + 16];
   const int t = threadIdx.x;
   const int64_t row = blockIdx.y;
   int64_t nv64 = n_valid[row];
@@ -281,91 +364,219 @@ __global__ void __launch_bounds__(kSelThreads) topk_select_kernel(
   const uint32_t nv = (uint32_t)nv64;
   const uint32_t k_eff = nv < (uint32_t)topk ? nv : (uint32_t)topk;
   const uint32_t nchunks = (nv + kChunk - 1) / kChunk;
-  RowCtr* ctr = ctr_g + row;
+  if (k_eff == 0 || blockIdx.x >= nchunks) return;
+  RowInfo* info = info_g + row;
   uint32_t* cand = cand_g + row * (int64_t)kCandCap * 2;
   uint32_t* hi = hi_g + row * (int64_t)kTopkMax * 2;
-  int32_t* out = out_idx + row * (int64_t)topk;
   const float* s = scores + row * ld;
 
-  if (k_eff == 0) {  // nothing visible: one work-group pads the row
-    if (blockIdx.x == 0)
-      for (int i = t; i < topk; i += kSelThreads) out[i] = -1;
-    return;
-  }
-  if (blockIdx.x >= nchunks) return;
-
-  // boundary bin from the row histogram
-  for (int i = t; i < kHistBins; i += kSelThreads) L.hist[i] = hist_g[row * kHistBins + i];
-  __syncthreads();
-  uint32_t above;
-  const uint32_t b1 = (uint32_t)suffix_find(L.hist, kHistBins, k_eff, &above, L.scratch);
-  const uint32_t eq = L.hist[b1];
-  const bool keep_eq = eq <= (uint32_t)kCandCap;
-
-  // append this chunk's entries above / inside the boundary bin
   const uint32_t base = blockIdx.x * (uint32_t)kChunk;
   const uint32_t end = base + kChunk < nv ? base + kChunk : nv;
-  for (uint32_t i = base + t; i < end; i += kSelThreads) {
-    uint32_t k = score_key(s[i]);
-    uint32_t b = k >> 20;
+  constexpr int kPer = kChunk / kSelThreads;
+  uint32_t kk[kPer];
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) {  // scores first: their latency overlaps the histogram's
+    const uint32_t i = base + t + j * kSelThreads;
+    kk[j] = i < end ? score_key(s[i]) : 0u;
+  }
+  {
+    uint32_t hv[kHistBins / kSelThreads];
+#pragma unroll
+    for (int j = 0; j < kHistBins / kSelThreads; ++j) hv[j] = hist_g[row * kHistBins + t + j * kSelThreads];
+#pragma unroll
+    for (int j = 0; j < kHistBins / kSelThreads; ++j) hist[t + j * kSelThreads] = hv[j];
+  }
+  __syncthreads();
+  uint32_t above;
+  const uint32_t b1 = (uint32_t)suffix_find(hist, kHistBins, k_eff, &above, scratch);
+  const uint32_t eq = hist[b1];
+  const bool keep_eq = eq <= (uint32_t)kCandCap;
+  if (blockIdx.x == 0 && t == 0) {
+    info->b1 = b1;
+    info->above = above;
+    info->eq = eq;
+  }
+  uint32_t n_hi_t = 0, n_eq_t = 0;
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) {
+    const uint32_t i = base + t + j * kSelThreads;
+    const uint32_t b = kk[j] >> 20;
+    if (i < end && b > b1) ++n_hi_t;
+    if (i < end && b == b1) ++n_eq_t;
+  }
+  const int lane = t & 63, wv = t >> 6;
+  uint32_t ph = n_hi_t, pe = n_eq_t;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const uint32_t a1 = __shfl_up(ph, off, 64), a2 = __shfl_up(pe, off, 64);
+    if (lane >= off) { ph += a1; pe += a2; }
+  }
+  if (lane == 63) { scratch[wv] = ph; scratch[4 + wv] = pe; }
+  __syncthreads();
+  uint32_t off_h = ph - n_hi_t, off_e = pe - n_eq_t;
+  for (int u = 0; u < wv; ++u) { off_h += scratch[u]; off_e += scratch[4 + u]; }
+  if (t == 0) {
+    const uint32_t th = scratch[0] + scratch[1] + scratch[2] + scratch[3];
+    const uint32_t te = keep_eq ? scratch[4] + scratch[5] + scratch[6] + scratch[7] : 0u;
+    const unsigned long long old =
+        (th | te) ? atomicAdd(&info->counts, (unsigned long long)th | ((unsigned long long)te << 32))
+                  : 0ull;
+    scratch[8] = (uint32_t)old;
+    scratch[9] = (uint32_t)(old >> 32);
+  }
+  __syncthreads();
+  uint32_t sh = scratch[8] + off_h, se = scratch[9] + off_e;
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) {
+    const uint32_t i = base + t + j * kSelThreads;
+    if (i >= end) continue;
+    const uint32_t b = kk[j] >> 20;
     if (b > b1) {
-      uint32_t slot = atomicAdd(&ctr->n_hi, 1u);
-      if (slot < (uint32_t)kTopkMax) {  // always true: fewer than k_eff lie above b1
-        hi[2 * slot] = k;
-        hi[2 * slot + 1] = i;
+      if (sh < (uint32_t)kTopkMax) {  // always true: fewer than k_eff lie above b1
+        hi[2 * sh] = kk[j];
+        hi[2 * sh + 1] = i;
       }
+      ++sh;
     } else if (b == b1 && keep_eq) {
-      uint32_t slot = atomicAdd(&ctr->n_eq, 1u);
-      if (slot < (uint32_t)kCandCap) {  // always true: eq <= kCandCap
-        cand[2 * slot] = k;
-        cand[2 * slot + 1] = i;
+      if (se < (uint32_t)kCandCap) {  // always true: eq <= kCandCap
+        cand[2 * se] = kk[j];
+        cand[2 * se + 1] = i;
       }
+      ++se;
     }
   }
-  __threadfence();
-  __syncthreads();
-  if (t == 0) L.flag = (atomicAdd(&ctr->done, 1u) == nchunks - 1) ? 1u : 0u;
-  __syncthreads();
-  if (!L.flag) return;
-  __threadfence();
+}
 
-  // ---- last work-group of the row: finish the selection
+// Pass 2, one work-group per row: refine the boundary bin with the remaining
+// 20 bits (12 + 8) from the register-resident candidates, resolve ties at the
+// threshold by index, order the winners and write the row.  When the
+// boundary bin held more entries than the candidate list, the refinement
+// runs over the whole row instead.
+__global__ void __launch_bounds__(kSelThreads) topk_final_kernel(
+    const float* __restrict__ scores, const int32_t* __restrict__ n_valid, int64_t ld, int topk,
+    int32_t* __restrict__ out_idx, const RowInfo* info_g, const uint32_t* cand_g,
+    const uint32_t* hi_g) {
+  __shared__ LdsSel L;
+  const int t = threadIdx.x;
+  const int64_t row = blockIdx.x;
+  int64_t nv64 = n_valid[row];
+  nv64 = nv64 < 0 ? 0 : (nv64 > ld ? ld : nv64);
+  const uint32_t nv = (uint32_t)nv64;
+  const uint32_t k_eff = nv < (uint32_t)topk ? nv : (uint32_t)topk;
+  int32_t* out = out_idx + row * (int64_t)topk;
+  if (k_eff == 0) {
+    for (int i = t; i < topk; i += kSelThreads) out[i] = -1;
+    return;
+  }
+  const RowInfo* info = info_g + row;
+  const uint32_t* cand = cand_g + row * (int64_t)kCandCap * 2;
+  const uint32_t* hi = hi_g + row * (int64_t)kTopkMax * 2;
+  const float* s = scores + row * ld;
+  const uint32_t b1 = info->b1, above = info->above, eq = info->eq;
+  const bool keep_eq = eq <= (uint32_t)kCandCap;
+  const uint32_t need = k_eff - above;
   if (t == 0) { L.n_sel = 0; L.n_ties = 0; }
+  uint32_t hk[kHiPerThread], hx[kHiPerThread];
+#pragma unroll
+  for (int j = 0; j < kHiPerThread; ++j) {
+    const uint32_t i = t + j * kSelThreads;
+    hk[j] = i < above ? hi[2 * i] : 0u;
+    hx[j] = i < above ? hi[2 * i + 1] : 0u;
+  }
+  if (!keep_eq) {
+#pragma unroll
+    for (int j = 0; j < kHiPerThread; ++j) {
+      const uint32_t i = t + j * kSelThreads;
+      if (i < above) { L.skey[i] = hk[j]; L.sidx[i] = hx[j]; }
+    }
+    if (t == 0) L.n_sel = above;
+    __syncthreads();
+    RowSrc src{s, nv};
+    refine_and_collect(src, b1, need, true, L);
+    const int n_sel = (int)L.n_sel < kSortCap ? (int)L.n_sel : kSortCap;
+    // ties (already in index order) follow the ordered winners
+    for (int i = t; i < topk; i += kSelThreads)
+      if (i >= n_sel) out[i] = (uint32_t)i < k_eff ? (int32_t)L.ties[i - n_sel] : -1;
+    __syncthreads();  // L.ties is reused as the sort buffer
+    order_store(L.skey, L.sidx, n_sel, (uint64_t*)L.ties, out);
+    return;
+  }
+  uint32_t ck[kCandPerThread], cx[kCandPerThread];
+#pragma unroll
+  for (int j = 0; j < kCandPerThread; ++j) {
+    const uint32_t i = t + j * kSelThreads;
+    ck[j] = i < eq ? cand[2 * i] : 0u;
+    cx[j] = i < eq ? cand[2 * i + 1] : 0u;
+  }
+  // second digit: bits 19..8 within b1
+  for (int i = t; i < kHistBins; i += kSelThreads) L.hist[i] = 0;
   __syncthreads();
-  // entries above the boundary bin (fewer than k_eff)
-  for (uint32_t i = t; i < above && i < (uint32_t)kSortCap; i += kSelThreads) {
-    L.skey[i] = hi[2 * i];
-    L.sidx[i] = hi[2 * i + 1];
+#pragma unroll
+  for (int j = 0; j < kCandPerThread; ++j) {
+    const uint32_t i = t + j * kSelThreads;
+    if (i < eq) atomicAdd(&L.hist[(ck[j] >> 8) & 0xfffu], 1u);
+  }
+  __syncthreads();
+  uint32_t above2;
+  const uint32_t b2 = (uint32_t)suffix_find(L.hist, kHistBins, need, &above2, L.scratch);
+  const uint32_t pre = (b1 << 12) | b2;
+  // third digit: bits 7..0 within (b1, b2)
+  for (int i = t; i < kHistBins; i += kSelThreads) L.hist[i] = 0;
+  __syncthreads();
+#pragma unroll
+  for (int j = 0; j < kCandPerThread; ++j) {
+    const uint32_t i = t + j * kSelThreads;
+    if (i < eq && (ck[j] >> 8) == pre) atomicAdd(&L.hist[ck[j] & 0xffu], 1u);
+  }
+  __syncthreads();
+  uint32_t above3;
+  const uint32_t b3 = (uint32_t)suffix_find(L.hist, kHistBins, need - above2, &above3, L.scratch);
+  const uint32_t T = (pre << 8) | b3;
+  const uint32_t need_t = need - above2 - above3;  // >= 1 entries equal to T are taken
+  // winners: the hi list, candidates above T, and ties at T (by index)
+#pragma unroll
+  for (int j = 0; j < kHiPerThread; ++j) {
+    const uint32_t i = t + j * kSelThreads;
+    if (i < above) { L.skey[i] = hk[j]; L.sidx[i] = hx[j]; }
   }
   if (t == 0) L.n_sel = above;
   __syncthreads();
-  const uint32_t need = k_eff - above;
-  if (keep_eq) {
-    ListSrc src{cand, eq};
-    refine_and_collect(src, b1, need, false, L);
-  } else {
-    RowSrc src{s, nv};
-    refine_and_collect(src, b1, need, true, L);
+#pragma unroll
+  for (int j = 0; j < kCandPerThread; ++j) {
+    const uint32_t i = t + j * kSelThreads;
+    if (i < eq) {
+      if (ck[j] > T) {
+        const uint32_t slot = atomicAdd(&L.n_sel, 1u);
+        if (slot < (uint32_t)kSortCap) { L.skey[slot] = ck[j]; L.sidx[slot] = cx[j]; }
+      } else if (ck[j] == T) {
+        const uint32_t slot = atomicAdd(&L.n_ties, 1u);
+        if (slot < (uint32_t)kTieCap) L.ties[slot] = cx[j];
+      }
+    }
   }
-  // sort the winners above the threshold, then append the ties in index order
-  const int n_sel = (int)L.n_sel < kSortCap ? (int)L.n_sel : kSortCap;
-  const int p2 = pow2_at_least(n_sel < 1 ? 1 : n_sel);
-  for (int i = n_sel + t; i < p2; i += kSelThreads) { L.skey[i] = 0u; L.sidx[i] = 0xffffffffu; }
   __syncthreads();
-  bitonic_pairs(L.skey, L.sidx, p2);
-  for (int i = t; i < topk; i += kSelThreads) {
-    int32_t v = -1;
-    if (i < n_sel) v = (int32_t)L.sidx[i];
-    else if ((uint32_t)i < k_eff) v = (int32_t)L.ties[i - n_sel];
-    out[i] = v;
+  const int n_sel = (int)L.n_sel < kSortCap ? (int)L.n_sel : kSortCap;
+  const int n_ties = (int)L.n_ties < kTieCap ? (int)L.n_ties : kTieCap;
+  if ((uint32_t)n_ties > need_t) {  // keep the need_t smallest indices among the ties
+    const int p2 = pow2_at_least(n_ties);
+    for (int i = n_ties + t; i < p2; i += kSelThreads) L.ties[i] = 0xffffffffu;
+    __syncthreads();
+    bitonic_u32(L.ties, p2);
   }
+  for (int i = t; i < (int)need_t; i += kSelThreads) {
+    if (n_sel + i < kSortCap) { L.skey[n_sel + i] = T; L.sidx[n_sel + i] = L.ties[i]; }
+  }
+  __syncthreads();
+  const int n_all = n_sel + (int)need_t < kSortCap ? n_sel + (int)need_t : kSortCap;
+  order_store(L.skey, L.sidx, n_all, (uint64_t*)L.ties, out);
+  for (int i = n_all + t; i < topk; i += kSelThreads) out[i] = -1;
 }
 
 }  // namespace
 
 size_t topk_ws_bytes(int64_t R) {
   size_t b = align_up((size_t)R * kHistBins * 4, 256);
-  b += align_up((size_t)R * 16, 256);
+  b += align_up((size_t)R * 32, 256);
   b += align_up((size_t)R * kCandCap * 8, 256);
   b += align_up((size_t)R * kTopkMax * 8, 256);
   return b;
@@ -377,7 +588,7 @@ TopkWs topk_ws_carve(void* ws, int64_t R) {
   w.hist = (uint32_t*)p;
   p += align_up((size_t)R * kHistBins * 4, 256);
   w.ctr = (uint32_t*)p;
-  p += align_up((size_t)R * 16, 256);
+  p += align_up((size_t)R * 32, 256);
   w.cand = (uint32_t*)p;
   p += align_up((size_t)R * kCandCap * 8, 256);
   w.hi = (uint32_t*)p;
@@ -406,13 +617,21 @@ hipError_t launch_topk_hist(const float* scores, const int32_t* n_valid, int64_t
 
 hipError_t launch_topk_select(const float* scores, const int32_t* n_valid, int64_t R, int64_t ld,
                               int topk, int32_t* out_idx, TopkWs w, hipStream_t s) {
+  static_assert(sizeof(RowInfo) <= 32, "row info slot");
   int64_t gx = (ld + kChunk - 1) / kChunk;
   for (int64_t r0 = 0; r0 < R; r0 += 65535) {
     int64_t nr = R - r0 < 65535 ? R - r0 : 65535;
-    hipLaunchKernelGGL(topk_select_kernel, dim3((unsigned)gx, (unsigned)nr), dim3(kSelThreads), 0,
-                       s, scores + r0 * ld, n_valid + r0, ld, topk, out_idx + r0 * topk,
-                       w.hist + r0 * kHistBins, (RowCtr*)w.ctr + r0,
-                       w.cand + r0 * (int64_t)kCandCap * 2, w.hi + r0 * (int64_t)kTopkMax * 2);
+    hipLaunchKernelGGL(topk_collect_kernel, dim3((unsigned)gx, (unsigned)nr), dim3(kSelThreads), 0,
+                       s, scores + r0 * ld, n_valid + r0, ld, topk, w.hist + r0 * kHistBins,
+                       (RowInfo*)w.ctr + r0, w.cand + r0 * (int64_t)kCandCap * 2,
+                       w.hi + r0 * (int64_t)kTopkMax * 2);
+  }
+  for (int64_t r0 = 0; r0 < R; r0 += (int64_t)1 << 30) {
+    int64_t nr = R - r0 < ((int64_t)1 << 30) ? R - r0 : ((int64_t)1 << 30);
+    hipLaunchKernelGGL(topk_final_kernel, dim3((unsigned)nr), dim3(kSelThreads), 0, s,
+                       scores + r0 * ld, n_valid + r0, ld, topk, out_idx + r0 * topk,
+                       (const RowInfo*)w.ctr + r0, w.cand + r0 * (int64_t)kCandCap * 2,
+                       w.hi + r0 * (int64_t)kTopkMax * 2);
   }
   return hipGetLastError();
 }

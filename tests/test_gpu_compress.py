@@ -117,21 +117,25 @@ def test_bulk_f32(tables, ratio, d, rotate):
         close_f32(sc[fin], st[1][fin], tol=2e-5)
 
 
-@pytest.mark.parametrize("entry_fmt", ["bf16", "fp8_mx32", "fp4_e4m3_16", "f32"])
-def test_decode_steps_bf16(tables, entry_fmt):
+@pytest.mark.parametrize("entry_fmt,dim,d,rotate", [("bf16", 512, 512, 0), ("fp8_mx32", 512, 512, 0),
+                                                    ("fp4_e4m3_16", 512, 512, 0), ("f32", 512, 512, 0),
+                                                    ("fp8_mx32", 4096, 512, 0), ("fp8_mx32", 4096, 128, 1),
+                                                    ("bf16", 4096, 128, 1)])
+def test_decode_steps_bf16(tables, entry_fmt, dim, d, rotate):
     """Token-by-token calls from a state built by an earlier chunked call; each
-    sequence sits at a different offset inside its block."""
-    B, dim, d, ratio = 3, 512, 512, 4
+    sequence sits at a different offset inside its block.  dim 4096 runs the
+    K-sliced MFMA projection."""
+    B, ratio = 3, 4
     rng = np.random.default_rng(7)
     wkv, wg, ape = (synth.bf16_round(w) for w in weights(rng, dim, d, ratio))
     ape = weights(rng, dim, d, ratio)[2]
     prefix = np.array([37, 40, 42])
     steps = 9
     x = synth.bf16_round(rng.standard_normal((B, 60, dim)).astype(np.float32))
-    g = GpuCompressor(B, dim, ratio, d, 0, wkv, wg, ape, "bf16", entry_fmt, 32, tables)
+    g = GpuCompressor(B, dim, ratio, d, rotate, wkv, wg, ape, "bf16", entry_fmt, 32, tables)
     # prefix: one chunked call per sequence (different lengths -> separate calls)
     for b in range(B):
-        gb = GpuCompressor(1, dim, ratio, d, 0, wkv, wg, ape, "bf16", entry_fmt, 32, tables)
+        gb = GpuCompressor(1, dim, ratio, d, rotate, wkv, wg, ape, "bf16", entry_fmt, 32, tables)
         gb(x[b:b + 1, :prefix[b]], [0])
         g.kv[b], g.sc[b], g.entries[b] = gb.kv[0], gb.sc[0], gb.entries[0]
     for s in range(steps):
@@ -140,7 +144,7 @@ def test_decode_steps_bf16(tables, entry_fmt):
     for b in range(B):
         T = prefix[b] + steps
         ref, st = compressor.compress_stream(x[b, :T].astype(np.float64), 0, wkv, wg, ape,
-                                             np.ones(d), OM, ratio, d)
+                                             np.ones(d), OM, ratio, d, rotate=bool(rotate))
         for i, v in ref.items():
             stored = codec.store(v, entry_fmt)[1]
             err = np.abs(got[b, i] - stored)
