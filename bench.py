@@ -15,6 +15,7 @@ HIP events on the stream it runs on.  cpu_baseline times the float64 oracle
 
   python bench.py [--steps K] [--warmup W] [--workload csa_1m_fp8|csa_1m_mxfp4|
                   csa_64k_bf16|hca_1m_bf16] [--copies C] [--no-cpu-baseline]
+  python bench.py --copy-calibration     # known-size copy for HBM byte counters
 """
 
 import argparse
@@ -164,6 +165,9 @@ def main():
                     help="independent cache copies rotated per step (defeats the 256 MB MALL)")
     ap.add_argument("--cpu-seqs", type=int, default=2)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 1 GiB device-to-device copy three times (the known-size "
+                         "reference for HBM byte counters) and exit")
     a = ap.parse_args()
     if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -171,6 +175,15 @@ def main():
         sys.exit(2)
 
     import torch
+    if a.copy_calibration:
+        n = 1 << 30
+        src = torch.ones(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes": n, "launches": 3}), flush=True)
+        return
     from kv_cache_decode_csa_amd import decode, synth
 
     w = synth.WORKLOADS[WORKLOADS[a.workload]]

@@ -6,15 +6,17 @@
 // threshold key in three digits (12 + 12 + 8 bits):
 //   1. a 4096-bin histogram of key >> 20 per row (built by the scoring kernel
 //      or by topk_hist_kernel) gives the boundary bin;
-//   2. every work-group of the row re-reads its chunk and appends the entries
-//      above the boundary bin and those inside it to per-row lists;
-//   3. the last work-group of the row to finish refines the boundary bin with
-//      the remaining 20 bits, resolves ties at the threshold by index, sorts
-//      the winners and writes the row.  If the boundary bin overflows its list
+//   2. collect: every work-group re-reads its chunk of the row, finds the
+//      boundary bin from the histogram and appends the entries above it and
+//      those inside it to per-row lists (positions from one 64-bit atomic per
+//      work-group);
+//   3. final: one work-group per row refines the boundary bin with the
+//      remaining 20 bits, resolves ties at the threshold by index, sorts the
+//      winners and writes the row.  If the boundary bin overflowed its list
 //      the same refinement runs over the whole row instead.
-// Counters use integer atomics only, and every list is sorted by a total order
-// before it is used, so the result does not depend on scheduling.
-#include "common.h"
+// The lists are gathered in scheduling order, but every one is reduced to a
+// total order (key, then index) before it is used, so the result does not
+// depend on scheduling.
 
 namespace csa {
 
