@@ -28,7 +28,7 @@ namespace {
 
 constexpr int kAttnThreads = 256;
 constexpr int kTile = 32;             // rows per tile
-constexpr int kChunkCsa = 128;        // rows per work-group, top-k lists
+constexpr int kChunkCsa = 64;         // rows per work-group, top-k lists
 constexpr int kChunkHca = 1024;       // rows per work-group, dense lists
 constexpr float kLog2e = 1.4426950408889634f;
 
@@ -125,25 +125,25 @@ template <> struct Raw<CSA_BF16> { uint4 v[4]; };
 template <> struct Raw<CSA_FP8_MX32> { uint2 v[4]; uint32_t sc; };   // sc: groups 4w..4w+3
 template <> struct Raw<CSA_FP4_E4M3_16> { uint32_t v[4]; uint2 sc; }; // sc: groups 8w..8w+7
 
+// Loads are unconditional: an absent row is read from a stand-in row of the
+// same buffer and zeroed when its fragments are formed, so the wait before a
+// tile's MFMAs covers only that tile's loads.
 template <int F>
 __device__ __forceinline__ void load_raw(const uint8_t* p, int w, int kq, Raw<F>& r) {
   if (F == CSA_BF16) {
     Raw<CSA_BF16>& q = (Raw<CSA_BF16>&)r;
 #pragma unroll
-    for (int s = 0; s < 4; ++s)
-      q.v[s] = p ? *(const uint4*)(p + 2 * (128 * w + 32 * s + 8 * kq)) : make_uint4(0, 0, 0, 0);
+    for (int s = 0; s < 4; ++s) q.v[s] = *(const uint4*)(p + 2 * (128 * w + 32 * s + 8 * kq));
   } else if (F == CSA_FP8_MX32) {
     Raw<CSA_FP8_MX32>& q = (Raw<CSA_FP8_MX32>&)r;
 #pragma unroll
-    for (int s = 0; s < 4; ++s)
-      q.v[s] = p ? *(const uint2*)(p + 128 * w + 32 * s + 8 * kq) : make_uint2(0, 0);
-    q.sc = p ? *(const uint32_t*)(p + kHeadDim + 4 * w) : 0u;
+    for (int s = 0; s < 4; ++s) q.v[s] = *(const uint2*)(p + 128 * w + 32 * s + 8 * kq);
+    q.sc = *(const uint32_t*)(p + kHeadDim + 4 * w);
   } else {
     Raw<CSA_FP4_E4M3_16>& q = (Raw<CSA_FP4_E4M3_16>&)r;
 #pragma unroll
-    for (int s = 0; s < 4; ++s)
-      q.v[s] = p ? *(const uint32_t*)(p + 64 * w + 16 * s + 4 * kq) : 0u;
-    q.sc = p ? *(const uint2*)(p + kHeadDim / 2 + 8 * w) : make_uint2(0, 0);
+    for (int s = 0; s < 4; ++s) q.v[s] = *(const uint32_t*)(p + 64 * w + 16 * s + 4 * kq);
+    q.sc = *(const uint2*)(p + kHeadDim / 2 + 8 * w);
   }
 }
 
@@ -266,14 +266,16 @@ __device__ __forceinline__ void attend_tile(const uint4 (&fr)[2][4], uint32_t vm
   }
 }
 
-// Rows [j0, j1) of the list, all in format F: pipelined tile loop.
+// Rows [j0, j1) of the list, all in format F.  Two register sets alternate:
+// while one tile is computed the next tile's rows are in flight.  Absent rows
+// (and rows past j1) are loaded from `stand_in`, a row of the same buffer, and
+// zeroed by the validity mask.
 template <int F, class RowFn>
-__device__ __forceinline__ void run_rows(int64_t j0, int64_t j1, RowFn row_of, const uint4 (&qa)[4],
+__device__ __forceinline__ void run_rows(int64_t j0, int64_t j1, RowFn row_of,
+                                         const uint8_t* stand_in, const uint4 (&qa)[4],
                                          float zscale, int w, int lane, uint16_t* R,
                                          float4 (*Sp)[64][2], SoftmaxState& st) {
   const int r16 = lane & 15, kq = lane >> 4;
-  Raw<F> cur[2], nxt[2];
-  uint32_t vm_cur = 0, vm_nxt = 0;
   auto load_tile = [&](int64_t jt, Raw<F> (&f)[2], uint32_t& vm) {
     vm = 0;
 #pragma unroll
@@ -282,38 +284,73 @@ __device__ __forceinline__ void run_rows(int64_t j0, int64_t j1, RowFn row_of, c
       const uint8_t* p = j < j1 ? row_of(j) : nullptr;
       const unsigned long long bal = __ballot(p != nullptr);
       vm |= (uint32_t)(bal & 0xffffull) << (16 * rt);
-      load_raw<F>(p, w, kq, f[rt]);
+      load_raw<F>(p ? p : stand_in, w, kq, f[rt]);
     }
   };
-  if (j0 < j1) load_tile(j0, cur, vm_cur);
-  for (int64_t jt = j0; jt < j1; jt += kTile) {
-    if (jt + kTile < j1) load_tile(jt + kTile, nxt, vm_nxt);
+  auto compute_tile = [&](const Raw<F> (&f)[2], uint32_t vm) {
     uint4 fr[2][4];
 #pragma unroll
-    for (int rt = 0; rt < 2; ++rt)
+    for (int rt = 0; rt < 2; ++rt) {
+      const bool ok = (vm >> (16 * rt + r16)) & 1u;
 #pragma unroll
-      for (int s = 0; s < 4; ++s) fr[rt][s] = frag_bf16<F>(cur[rt], s, kq);
-    attend_tile(fr, vm_cur, qa, zscale, w, lane, R, Sp, st);
-    cur[0] = nxt[0];
-    cur[1] = nxt[1];
-    vm_cur = vm_nxt;
+      for (int s = 0; s < 4; ++s) {
+        const uint4 v = frag_bf16<F>(f[rt], s, kq);
+        fr[rt][s] = ok ? v : make_uint4(0u, 0u, 0u, 0u);
+      }
+    }
+    attend_tile(fr, vm, qa, zscale, w, lane, R, Sp, st);
+  };
+  Raw<F> fa[2], fb[2];
+  uint32_t va = 0, vb = 0;
+  load_tile(j0, fa, va);
+  for (int64_t jt = j0; jt < j1; jt += 2 * kTile) {
+    load_tile(jt + kTile, fb, vb);
+    compute_tile(fa, va);
+    load_tile(jt + 2 * kTile, fa, va);
+    if (jt + kTile < j1) compute_tile(fb, vb);
   }
+}
+
+// Work-group -> (chunk, unit, head group).  Work-groups are handed to the 8
+// XCDs round-robin by linear id, so the head groups of one (chunk, unit) are
+// given ids 8 apart: they run on the same XCD at about the same time and
+// read the chunk's rows through one L2.
+struct AttnItem {
+  int chunk, hg;
+  int64_t unit;
+  bool live;
+};
+
+__device__ __forceinline__ AttnItem attn_item(const AttnArgs& a, int nchunks, int64_t units) {
+  const int64_t L = blockIdx.x;
+  const int G = a.H / 16;
+  const int64_t k = L >> 3;
+  const int64_t item = (k / G) * 8 + (L & 7);
+  AttnItem it;
+  it.hg = (int)(k % G);
+  it.chunk = (int)(item % nchunks);
+  it.unit = a.unit_off + item / nchunks;
+  it.live = item < (int64_t)nchunks * units;
+  return it;
 }
 
 template <int WF, int EF>
 __global__ void __launch_bounds__(kAttnThreads) attn_mfma_kernel(AttnArgs a, int chunk_rows,
-                                                                 int nchunks, Partial* part) {
+                                                                 int nchunks, int64_t units,
+                                                                 Partial* part) {
   __shared__ uint16_t Rl[4][kTile * kRPitch];
   __shared__ float4 Sp[4][64][2];
 
+  const AttnItem it = attn_item(a, nchunks, units);
+  if (!it.live) return;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int w = tid >> 6;
   const int r16 = lane & 15;
   const int kq = lane >> 4;
-  const int64_t unit = a.unit_off + blockIdx.z;
-  const int hg = blockIdx.y;
-  const int chunk = blockIdx.x;
+  const int64_t unit = it.unit;
+  const int hg = it.hg;
+  const int chunk = it.chunk;
   const int64_t b = unit / a.Q;
   const int t = a.pos[unit];
   const int64_t nvis = unit_nvis(a, t);
@@ -380,18 +417,19 @@ __global__ void __launch_bounds__(kAttnThreads) attn_mfma_kernel(AttnArgs a, int
     auto win_row = [&](int64_t j) -> const uint8_t* {
       return resolve_row(a, unit, b, t, j, nvis, a.win_rb, a.ent_rb).p;
     };
-    run_rows<WF>(j_begin, jw, win_row, qa, zscale, w, lane, R, Sp, st);
+    const uint8_t* win0 = (const uint8_t*)a.win + (size_t)b * (size_t)a.win_rows * a.win_rb;
+    run_rows<WF>(j_begin, jw, win_row, win0, qa, zscale, w, lane, R, Sp, st);
   }
   // entry rows [max(j_begin, 128), j_end)
   const int64_t je = j_begin > kWindow ? j_begin : kWindow;
-  if (je < j_end) {
+  if (je < j_end && a.Nmax > 0) {
     const uint8_t* ebase = (const uint8_t*)a.entries + (size_t)b * (size_t)a.Nmax * a.ent_rb;
     if (a.dense) {
       auto ent_row = [&](int64_t j) -> const uint8_t* {
         const int64_t e = j - kWindow;
         return e < nvis ? ebase + (size_t)e * a.ent_rb : nullptr;
       };
-      run_rows<EF>(je, j_end, ent_row, qa, zscale, w, lane, R, Sp, st);
+      run_rows<EF>(je, j_end, ent_row, ebase, qa, zscale, w, lane, R, Sp, st);
     } else {
       auto ent_row = [&](int64_t j) -> const uint8_t* {
         // this lane's id slot for row j (rows are 16 r16-strided within the chunk)
@@ -402,7 +440,7 @@ __global__ void __launch_bounds__(kAttnThreads) attn_mfma_kernel(AttnArgs a, int
           if (i == slot) e = ids[i];
         return (e >= 0 && e < a.Nmax) ? ebase + (size_t)e * a.ent_rb : nullptr;
       };
-      run_rows<EF>(je, j_end, ent_row, qa, zscale, w, lane, R, Sp, st);
+      run_rows<EF>(je, j_end, ent_row, ebase, qa, zscale, w, lane, R, Sp, st);
     }
   }
 
@@ -446,56 +484,51 @@ __global__ void __launch_bounds__(kAttnThreads) attn_mfma_kernel(AttnArgs a, int
 }
 
 // ------------------------------------------------------------------ merge
-// One work-group per (unit, head group); thread t owns head t/16 and dims
-// [32 (t%16), +32).  Chunks are combined in index order.
+// One work-group per (unit, head group, 64-dim slice); thread t owns head t/16
+// and 4 dims.  Chunks are combined in index order; each batch of 8 chunks is
+// loaded before any is combined, so the loads overlap.
+constexpr int kMergeBatch = 8;
+
 __global__ void __launch_bounds__(kAttnThreads) attn_merge_kernel(AttnArgs a, int nchunks,
                                                                   const Partial* part) {
-  __shared__ float sM[16], sInv[16];
   const int tid = threadIdx.x;
   const int64_t unit = a.unit_off + blockIdx.y;
-  const int hg = blockIdx.x;
-  const Partial* P = part + (unit * (a.H / 16) + hg) * (int64_t)nchunks;
+  const int G = a.H / 16;
+  const int hg = blockIdx.x % G;
+  const int slice = blockIdx.x / G;
+  const Partial* P = part + (unit * G + hg) * (int64_t)nchunks;
   const int rr = rope_row(a, a.pos[unit]);
-  if (tid < 16) {
-    float M = -INFINITY;
-    for (int c = 0; c < nchunks; ++c) M = fmaxf(M, P[c].m[tid]);
-    float L = 0.f;
-    for (int c = 0; c < nchunks; ++c) {
-      const float mc = P[c].m[tid];
-      L += (mc == -INFINITY) ? 0.f : P[c].l[tid] * exp2f(mc - M);
-    }
-    const float sink2 = a.sink[16 * hg + tid] * kLog2e;
-    const float den = (M == -INFINITY) ? 0.f : L + exp2f(sink2 - M);
-    sM[tid] = M;
-    sInv[tid] = den > 0.f ? 1.f / den : 0.f;
-  }
-  __syncthreads();
   const int h = tid >> 4;
-  const int d0 = 32 * (tid & 15);
-  const float M = sM[h];
-  float4 acc[8];
+  const int d0 = 64 * slice + 4 * (tid & 15);
+  float M = -INFINITY;
+  for (int c = 0; c < nchunks; ++c) M = fmaxf(M, P[c].m[h]);
+  float L = 0.f;
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int c0 = 0; c0 < nchunks; c0 += kMergeBatch) {
+    float mc[kMergeBatch], lc[kMergeBatch];
+    float4 oc[kMergeBatch];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) acc[i] = make_float4(0.f, 0.f, 0.f, 0.f);
-  for (int c = 0; c < nchunks; ++c) {
-    const float mc = P[c].m[h];
-    const float wgt = (mc == -INFINITY) ? 0.f : exp2f(mc - M);
-    const float4* src = (const float4*)(P[c].o + h * kHeadDim + d0);
+    for (int i = 0; i < kMergeBatch; ++i) {
+      const int c = c0 + i < nchunks ? c0 + i : nchunks - 1;
+      mc[i] = P[c].m[h];
+      lc[i] = P[c].l[h];
+      oc[i] = *(const float4*)(P[c].o + h * kHeadDim + d0);
+    }
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const float4 v = src[i];
-      acc[i].x += v.x * wgt; acc[i].y += v.y * wgt; acc[i].z += v.z * wgt; acc[i].w += v.w * wgt;
+    for (int i = 0; i < kMergeBatch; ++i) {
+      if (c0 + i >= nchunks || mc[i] == -INFINITY) continue;
+      const float wgt = exp2f(mc[i] - M);
+      L += lc[i] * wgt;
+      acc.x += oc[i].x * wgt; acc.y += oc[i].y * wgt; acc.z += oc[i].z * wgt; acc.w += oc[i].w * wgt;
     }
   }
-  const float inv = sInv[h];
-  float v[32];
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    v[4 * i] = acc[i].x * inv; v[4 * i + 1] = acc[i].y * inv;
-    v[4 * i + 2] = acc[i].z * inv; v[4 * i + 3] = acc[i].w * inv;
-  }
+  const float sink2 = a.sink[16 * hg + h] * kLog2e;
+  const float den = (M == -INFINITY) ? 0.f : L + exp2f(sink2 - M);
+  const float inv = den > 0.f ? 1.f / den : 0.f;
+  float v[4] = {acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv};
   if (d0 >= kHeadDim - kRopeDims) {
 #pragma unroll
-    for (int j = 0; j < 16; ++j) {
+    for (int j = 0; j < 2; ++j) {
       const int k = (d0 - (kHeadDim - kRopeDims)) / 2 + j;
       const float c = a.rope_cos[(int64_t)rr * 32 + k];
       const float sn = a.rope_sin[(int64_t)rr * 32 + k];
@@ -505,17 +538,10 @@ __global__ void __launch_bounds__(kAttnThreads) attn_merge_kernel(AttnArgs a, in
     }
   }
   const int64_t obase = (unit * a.H + 16 * hg + h) * (int64_t)kHeadDim + d0;
-  if (a.out_fmt == CSA_F32) {
-    float4* o = (float4*)((float*)a.out + obase);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) o[i] = make_float4(v[4 * i], v[4 * i + 1], v[4 * i + 2], v[4 * i + 3]);
-  } else {
-    uint4* o = (uint4*)((uint16_t*)a.out + obase);
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      o[i] = make_uint4(pack_bf16x2(v[8 * i], v[8 * i + 1]), pack_bf16x2(v[8 * i + 2], v[8 * i + 3]),
-                        pack_bf16x2(v[8 * i + 4], v[8 * i + 5]), pack_bf16x2(v[8 * i + 6], v[8 * i + 7]));
-  }
+  if (a.out_fmt == CSA_F32)
+    *(float4*)((float*)a.out + obase) = make_float4(v[0], v[1], v[2], v[3]);
+  else
+    *(uint2*)((uint16_t*)a.out + obase) = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
 }
 
 // ------------------------------------------------------------------ float32 kernel
@@ -600,20 +626,24 @@ size_t attn_ws_bytes(const AttnArgs& a) {
 }
 
 template <int WF>
-static void launch_mfma_w(const AttnArgs& a, int nc, dim3 grid, Partial* part, hipStream_t s) {
+static void launch_mfma_w(const AttnArgs& a, int nc, int64_t nu, dim3 grid, Partial* part,
+                          hipStream_t s) {
   const int cr = attn_chunk_rows(a);
   if (a.ent_fmt == CSA_BF16)
-    hipLaunchKernelGGL((attn_mfma_kernel<WF, CSA_BF16>), grid, dim3(kAttnThreads), 0, s, a, cr, nc, part);
+    hipLaunchKernelGGL((attn_mfma_kernel<WF, CSA_BF16>), grid, dim3(kAttnThreads), 0, s, a, cr, nc, nu, part);
   else if (a.ent_fmt == CSA_FP8_MX32)
-    hipLaunchKernelGGL((attn_mfma_kernel<WF, CSA_FP8_MX32>), grid, dim3(kAttnThreads), 0, s, a, cr, nc, part);
+    hipLaunchKernelGGL((attn_mfma_kernel<WF, CSA_FP8_MX32>), grid, dim3(kAttnThreads), 0, s, a, cr, nc, nu, part);
   else
-    hipLaunchKernelGGL((attn_mfma_kernel<WF, CSA_FP4_E4M3_16>), grid, dim3(kAttnThreads), 0, s, a, cr, nc, part);
+    hipLaunchKernelGGL((attn_mfma_kernel<WF, CSA_FP4_E4M3_16>), grid, dim3(kAttnThreads), 0, s, a, cr, nc, nu, part);
 }
 
-static void launch_mfma(const AttnArgs& a, int nc, dim3 grid, Partial* part, hipStream_t s) {
-  if (a.win_fmt == CSA_BF16) launch_mfma_w<CSA_BF16>(a, nc, grid, part, s);
-  else if (a.win_fmt == CSA_FP8_MX32) launch_mfma_w<CSA_FP8_MX32>(a, nc, grid, part, s);
-  else launch_mfma_w<CSA_FP4_E4M3_16>(a, nc, grid, part, s);
+static void launch_mfma(const AttnArgs& a, int nc, int64_t nu, Partial* part, hipStream_t s) {
+  // (chunk, unit) items padded to a multiple of 8, times the head groups
+  const int64_t items = ((int64_t)nc * nu + 7) / 8 * 8;
+  const dim3 grid((unsigned)(items * (a.H / 16)));
+  if (a.win_fmt == CSA_BF16) launch_mfma_w<CSA_BF16>(a, nc, nu, grid, part, s);
+  else if (a.win_fmt == CSA_FP8_MX32) launch_mfma_w<CSA_FP8_MX32>(a, nc, nu, grid, part, s);
+  else launch_mfma_w<CSA_FP4_E4M3_16>(a, nc, nu, grid, part, s);
 }
 
 hipError_t launch_attention(const AttnArgs& a0, void* ws, hipStream_t s) {
@@ -622,16 +652,23 @@ hipError_t launch_attention(const AttnArgs& a0, void* ws, hipStream_t s) {
   a.ent_rb = kv_row_bytes(a.ent_fmt, kHeadDim);
   const int64_t units = (int64_t)a.B * a.Q;
   const int nc = attn_nchunks(a);
-  for (int64_t u0 = 0; u0 < units; u0 += 65535) {
-    const unsigned nu = (unsigned)(units - u0 < 65535 ? units - u0 : 65535);
+  // units per launch: at most 65535 (grid y of the merge) and few enough that
+  // the 1-D MFMA grid stays below 2^32 work-items
+  const int64_t max_items = (((int64_t)1 << 32) - 1) / ((int64_t)kAttnThreads * (a.H / 16)) - 8;
+  if (a.q_fmt != CSA_F32 && nc > max_items) return hipErrorInvalidConfiguration;
+  int64_t ustep = max_items / nc;
+  ustep = ustep < 1 ? 1 : (ustep > 65535 ? 65535 : ustep);
+  for (int64_t u0 = 0; u0 < units; u0 += ustep) {
+    const unsigned nu = (unsigned)(units - u0 < ustep ? units - u0 : ustep);
     a.unit_off = u0;
     if (a.q_fmt == CSA_F32) {
       hipLaunchKernelGGL(attn_f32_kernel, dim3(a.H, nu), dim3(kAttnThreads), 0, s, a);
       continue;
     }
-    launch_mfma(a, nc, dim3(nc, a.H / 16, nu), (Partial*)ws, s);
+    launch_mfma(a, nc, nu, (Partial*)ws, s);
     if (nc > 1)
-      hipLaunchKernelGGL(attn_merge_kernel, dim3(a.H / 16, nu), dim3(kAttnThreads), 0, s, a, nc,
+      hipLaunchKernelGGL(attn_merge_kernel, dim3((a.H / 16) * (kHeadDim / 64), nu),
+                         dim3(kAttnThreads), 0, s, a, nc,
                          (const Partial*)ws);
   }
   return hipGetLastError();

@@ -14,7 +14,12 @@ namespace csa {
 namespace {
 
 constexpr int kIdxThreads = 256;
-constexpr int kKeysPerWg = 4096;                               // keys scored by one work-group
+// Work-groups per row: Nmax / 4096 .. Nmax / 512 keys' worth, the fewest that
+// give about 512 work-groups for the launch (a per-key score does not depend
+// on it).
+constexpr int kMinKeysPerWg = 512;
+constexpr int kMaxKeysPerWg = 4096;
+constexpr int64_t kTargetWgs = 512;
 // 16-key MFMA tiles per wave step: FP8 rows are small enough to keep four
 // tiles (64 keys, 8.4 KB per wave) and their successors in flight.
 template <int KFMT> constexpr int tiles_per_iter() { return KFMT == CSA_FP8_MX32 ? 4 : 2; }
@@ -28,29 +33,22 @@ struct KeyRaw {
   uint32_t w[16];   // fp8: w[0..7] codes, w[8] scale byte; bf16: w[0..15]
 };
 
+// Loads are unconditional (callers clamp the key index into the visible range)
+// so that the wait before a step's MFMAs only covers that step's loads and the
+// following step's loads stay in flight.
 template <int KFMT>
-__device__ __forceinline__ void load_key(const uint8_t* kr, int kq, bool valid, KeyRaw& r) {
+__device__ __forceinline__ void load_key(const uint8_t* kr, int kq, KeyRaw& r) {
   if (KFMT == CSA_FP8_MX32) {
-    if (valid) {
-      const uint32_t* p = (const uint32_t*)(kr + 32 * kq);  // rows of 132 B: dword aligned
+    const uint32_t* p = (const uint32_t*)(kr + 32 * kq);  // rows of 132 B: dword aligned
 #pragma unroll
-      for (int i = 0; i < 8; ++i) r.w[i] = p[i];
-      r.w[8] = kr[128 + kq];
-    } else {
-#pragma unroll
-      for (int i = 0; i < 9; ++i) r.w[i] = 0;
-    }
+    for (int i = 0; i < 8; ++i) r.w[i] = p[i];
+    r.w[8] = kr[128 + kq];
   } else {
-    if (valid) {
-      const uint4* p = (const uint4*)(kr + 64 * kq);
+    const uint4* p = (const uint4*)(kr + 64 * kq);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        uint4 v = p[i];
-        r.w[4 * i] = v.x; r.w[4 * i + 1] = v.y; r.w[4 * i + 2] = v.z; r.w[4 * i + 3] = v.w;
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < 16; ++i) r.w[i] = 0;
+    for (int i = 0; i < 4; ++i) {
+      uint4 v = p[i];
+      r.w[4 * i] = v.x; r.w[4 * i + 1] = v.y; r.w[4 * i + 2] = v.z; r.w[4 * i + 3] = v.w;
     }
   }
 }
@@ -75,17 +73,70 @@ __device__ __forceinline__ bf16x8_t key_frag(const KeyRaw& r, int s) {
   }
 }
 
+// Native 4 x u32 vectors (HIP's uint4 is a union-wrapped struct whose copies
+// the compiler keeps in private memory).
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+// ---- LDS staging of one step's keys (one wave's region)
+// FP8: the step's 64 rows of 132 B are stored as the contiguous byte stream
+// (528 pieces of 16 B; the last load's spare lanes land in unused slots).
+// bf16: each 256-B row holds exactly 16 pieces; rows are padded to 272 B so
+// the lanes of a fragment read hit distinct banks.
+template <int KFMT> constexpr int stage_pieces() {
+  return (16 * tiles_per_iter<KFMT>() * (KFMT == CSA_FP8_MX32 ? 132 : 256)) / 16;
+}
+template <int KFMT> constexpr int stage_slots() {
+  return KFMT == CSA_FP8_MX32 ? (stage_pieces<KFMT>() + 63) / 64 * 64
+                              : 16 * tiles_per_iter<KFMT>() * 17;
+}
+template <int KFMT> __device__ __forceinline__ int stage_slot(int piece) {
+  if (KFMT == CSA_FP8_MX32) return piece;
+  const int p = piece < stage_pieces<KFMT>() ? piece : stage_pieces<KFMT>() - 1;
+  return (p >> 4) * 17 + (p & 15);
+}
+// Fragment data of key `r` of the step for lane quarter kq, as load_key gives it.
+template <int KFMT>
+__device__ __forceinline__ void stage_read(const u32x4_t* st, int r, int kq, KeyRaw& f) {
+  if (KFMT == CSA_FP8_MX32) {
+    const uint32_t* L = (const uint32_t*)st + r * 33;  // 132 B = 33 dwords per row
+#pragma unroll
+    for (int i = 0; i < 8; ++i) f.w[i] = L[8 * kq + i];
+    f.w[8] = L[32] >> (8 * kq);
+  } else {
+    const u32x4_t* L = st + r * 17 + 4 * kq;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const u32x4_t v = L[i];
+      f.w[4 * i] = v.x; f.w[4 * i + 1] = v.y; f.w[4 * i + 2] = v.z; f.w[4 * i + 3] = v.w;
+    }
+  }
+}
+template <int N> struct U4Array {
+  u32x4_t v[N];
+};
+
+// Orders this wave's LDS accesses around a write of data that other lanes of
+// the same wave read (LDS operations of one wave execute in order).
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
 template <int HT, int KFMT>
 __global__ void __launch_bounds__(kIdxThreads) index_scores_mfma(
     const uint16_t* __restrict__ q_idx, const float* __restrict__ w_idx,
     const uint8_t* __restrict__ k_idx, const int32_t* __restrict__ pos, int ratio, int Q,
-    int64_t Nmax, int64_t row_off, float* __restrict__ scores, int32_t* __restrict__ n_vis_out,
-    uint32_t* __restrict__ hist_g) {
+    int64_t Nmax, int64_t row_off, float* __restrict__ scores,
+    int32_t* __restrict__ n_vis_out, uint32_t* __restrict__ hist_g) {
   constexpr int Hi = HT * 16;
   constexpr int64_t kRowBytes = KFMT == CSA_FP8_MX32 ? 132 : 256;
   constexpr int kTilesPerIter = tiles_per_iter<KFMT>();
   constexpr int kKeysPerIter = 16 * kTilesPerIter;
+  constexpr int kStagePieces = stage_pieces<KFMT>();
+  constexpr int kStageLoads = (kStagePieces + 63) / 64;
   __shared__ uint32_t hist[kHistBins];
+  __shared__ u32x4_t stage[4][stage_slots<KFMT>()];
 
   const int t = threadIdx.x;
   const int lane = t & 63;
@@ -95,8 +146,10 @@ __global__ void __launch_bounds__(kIdxThreads) index_scores_mfma(
   int64_t nv = ((int64_t)pos[row] + 1) / ratio;
   nv = nv < 0 ? 0 : (nv > Nmax ? Nmax : nv);
   if (blockIdx.x == 0 && t == 0) n_vis_out[row] = (int32_t)nv;
-  const int64_t base = (int64_t)blockIdx.x * kKeysPerWg;
-  if (base >= nv) return;
+  // The G = gridDim.x work-groups of a row sweep it together: step i of wave w
+  // in work-group x covers keys [((i G + x) 4 + w) K, +K).
+  const int64_t G = gridDim.x;
+  if ((int64_t)blockIdx.x * 4 * kKeysPerIter >= nv) return;
 
   for (int i = t; i < kHistBins; i += kIdxThreads) hist[i] = 0;
 
@@ -121,47 +174,87 @@ __global__ void __launch_bounds__(kIdxThreads) index_scores_mfma(
 
   const uint8_t* kbase = k_idx + b * Nmax * kRowBytes;
   float* srow = scores + row * Nmax;
-  int64_t end = base + kKeysPerWg;
-  if (end > nv) end = nv;
-  // wave w scores keys [base + K (w + 4 i), +K) for i = 0, 1, ... (K keys per step)
-  int64_t k0 = base + (int64_t)kKeysPerIter * wave;
-  KeyRaw cur[kTilesPerIter], nxt[kTilesPerIter];
+  const int64_t end = nv;
+  // A full step (all K keys below `end`) is read as one contiguous, coalesced
+  // byte stream (lane l takes 16-byte pieces l, l + 64, ...), put in the
+  // wave's own LDS region and read back in the MFMA operand layout.  Two
+  // register sets alternate, so the next step's stream is in flight while the
+  // current one is scored.  A partial step at the end of the row (if any) is
+  // read key by key with the index clamped to end - 1.
+  const int64_t stride = G * 4 * (int64_t)kKeysPerIter;
+  const int64_t k0 = ((int64_t)blockIdx.x * 4 + wave) * kKeysPerIter;
+  auto score_tile = [&](int64_t k, int nt, const KeyRaw& f) __attribute__((always_inline)) {
+    bf16x8_t kb[4];
 #pragma unroll
-  for (int nt = 0; nt < kTilesPerIter; ++nt) {
-    const int64_t key = k0 + 16 * nt + r16;
-    load_key<KFMT>(kbase + key * kRowBytes, kq, key < end, cur[nt]);
-  }
-  for (; k0 < end; k0 += 4 * kKeysPerIter) {
-    const int64_t k1 = k0 + 4 * kKeysPerIter;
+    for (int s = 0; s < 4; ++s) kb[s] = key_frag<KFMT>(f, s);
+    // the HT head tiles are independent accumulation chains: issue them
+    // round-robin so consecutive MFMAs do not wait on each other
+    f32x4_t acc[HT];
 #pragma unroll
-    for (int nt = 0; nt < kTilesPerIter; ++nt) {  // prefetch the next step
-      const int64_t key = k1 + 16 * nt + r16;
-      load_key<KFMT>(kbase + key * kRowBytes, kq, key < end, nxt[nt]);
+    for (int mt = 0; mt < HT; ++mt) acc[mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+#pragma unroll
+      for (int mt = 0; mt < HT; ++mt) acc[mt] = mfma16x16x32(as_bf16x8(qa[mt][s]), kb[s], acc[mt]);
+    float p = 0.f;
+#pragma unroll
+    for (int mt = 0; mt < HT; ++mt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) p += wv[mt][r] * fmaxf(acc[mt][r], 0.f);
+    p += shfl_xor_f(p, 16);
+    p += shfl_xor_f(p, 32);
+    const int64_t key = k + 16 * nt + r16;
+    if (kq == 0 && key < end) {
+      srow[key] = p;
+      atomicAdd(&hist[score_key(p) >> 20], 1u);
     }
+  };
+
+  int64_t n_full = end - k0 >= kKeysPerIter ? (end - k0 - kKeysPerIter) / stride + 1 : 0;
+  if (n_full > 0) {
+    u32x4_t* st_lds = stage[wave];
+    auto gload = [&](int64_t i) __attribute__((always_inline)) {
+      const u32x4_t* src = (const u32x4_t*)(kbase + (k0 + i * stride) * kRowBytes);
+      U4Array<kStageLoads> v;
+#pragma unroll
+      for (int j = 0; j < kStageLoads; ++j) {
+        int piece = lane + 64 * j;
+        piece = piece < kStagePieces ? piece : kStagePieces - 1;
+        v.v[j] = src[piece];
+      }
+      return v;
+    };
+    auto stage_and_score = [&](int64_t i, const U4Array<kStageLoads>& v)
+                               __attribute__((always_inline)) {
+      wave_lds_sync();  // earlier reads of the region are ordered before these writes
+#pragma unroll
+      for (int j = 0; j < kStageLoads; ++j) st_lds[stage_slot<KFMT>(lane + 64 * j)] = v.v[j];
+      wave_lds_sync();
+#pragma unroll
+      for (int nt = 0; nt < kTilesPerIter; ++nt) {
+        KeyRaw f;
+        stage_read<KFMT>(st_lds, 16 * nt + r16, kq, f);
+        score_tile(k0 + i * stride, nt, f);
+      }
+    };
+    U4Array<kStageLoads> sa = gload(0), sb;
+    for (int64_t i = 0; i < n_full; i += 2) {
+      sb = gload(i + 1 < n_full ? i + 1 : n_full - 1);
+      stage_and_score(i, sa);
+      sa = gload(i + 2 < n_full ? i + 2 : n_full - 1);
+      if (i + 1 < n_full) stage_and_score(i + 1, sb);
+    }
+  }
+  const int64_t kt = k0 + n_full * stride;
+  if (kt < end) {
 #pragma unroll
     for (int nt = 0; nt < kTilesPerIter; ++nt) {
-      bf16x8_t kb[4];
-#pragma unroll
-      for (int s = 0; s < 4; ++s) kb[s] = key_frag<KFMT>(cur[nt], s);
-      float p = 0.f;
-#pragma unroll
-      for (int mt = 0; mt < HT; ++mt) {
-        f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int s = 0; s < 4; ++s) acc = mfma16x16x32(as_bf16x8(qa[mt][s]), kb[s], acc);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) p += wv[mt][r] * fmaxf(acc[r], 0.f);
-      }
-      p += shfl_xor_f(p, 16);
-      p += shfl_xor_f(p, 32);
-      const int64_t key = k0 + 16 * nt + r16;
-      if (kq == 0 && key < end) {
-        srow[key] = p;
-        atomicAdd(&hist[score_key(p) >> 20], 1u);
-      }
+      int64_t key = kt + 16 * nt + r16;
+      key = key < end ? key : end - 1;
+      KeyRaw f;
+      load_key<KFMT>(kbase + key * kRowBytes, kq, f);
+      score_tile(kt, nt, f);
     }
-#pragma unroll
-    for (int nt = 0; nt < kTilesPerIter; ++nt) cur[nt] = nxt[nt];
   }
   __syncthreads();
   uint32_t* g = hist_g + row * kHistBins;
@@ -217,7 +310,9 @@ template <int HT>
 hipError_t launch_mfma(const void* q_idx, const float* w_idx, const void* k_idx, int k_fmt,
                        const int32_t* pos, int ratio, int Q, int64_t R, int64_t Nmax,
                        float* scores, int32_t* n_vis, uint32_t* hist, hipStream_t s) {
-  int64_t gx = (Nmax + kKeysPerWg - 1) / kKeysPerWg;
+  int kpw = kMaxKeysPerWg;
+  while (kpw > kMinKeysPerWg && R * ((Nmax + kpw - 1) / kpw) < kTargetWgs) kpw >>= 1;
+  const int64_t gx = (Nmax + kpw - 1) / kpw;
   for (int64_t r0 = 0; r0 < R; r0 += 65535) {
     int64_t nr = R - r0 < 65535 ? R - r0 : 65535;
     if (k_fmt == CSA_FP8_MX32)

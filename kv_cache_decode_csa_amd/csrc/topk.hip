@@ -18,6 +18,8 @@
 // total order (key, then index) before it is used, so the result does not
 // depend on scheduling.
 
+#include "common.h"
+
 namespace csa {
 
 namespace {

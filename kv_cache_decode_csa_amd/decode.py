@@ -9,6 +9,12 @@ points in order; it computes nothing itself.  A CSA step at position t is:
   csa_sparse_attn_decode                           -> [B, H, 512]
 
 and an HCA step is csa_compress (ratio 128) followed by hca_attn_decode.
+
+In `step()` the main-KV compressor of a CSA layer runs on a second stream (of
+default priority): only the attention reads what it writes, so it overlaps
+the index compressor, the scoring and the selection, and the attention waits
+for it with an event.  `phases()` runs the same calls one after another on
+the current stream, for per-call timing.
 """
 
 import torch
@@ -123,6 +129,7 @@ class CsaDecodeLayer:
             for cm, ci in self.comp:
                 cm(tail, st)
                 ci(tail, st)
+        self.side = torch.cuda.Stream(device=device)
         self.step_no = 0
 
     def phases(self):
@@ -154,8 +161,19 @@ class CsaDecodeLayer:
                 ("csa_index_topk", index_topk), ("csa_sparse_attn_decode", sparse_attn)]
 
     def step(self):
-        for _, f in self.phases():
-            f()
+        ph = dict(self.phases())
+        main = torch.cuda.current_stream()
+        ready = torch.cuda.Event()
+        ready.record(main)
+        with torch.cuda.stream(self.side):
+            self.side.wait_event(ready)
+            ph["csa_compress_main"]()
+            done = torch.cuda.Event()
+            done.record(self.side)
+        ph["csa_compress_index"]()
+        ph["csa_index_topk"]()
+        main.wait_event(done)
+        ph["csa_sparse_attn_decode"]()
         self.step_no += 1
 
 

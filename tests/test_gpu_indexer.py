@@ -51,17 +51,20 @@ def check_selection(idx, S_gpu, S_ref, tol, nv, k):
         assert np.all(np.abs(S_ref[diff] - thr) <= 2 * tol[diff] + 1e-12), diff[:10]
 
 
-@pytest.mark.parametrize("kfmt", ["bf16", "fp8_mx32"])
-@pytest.mark.parametrize("Hi", [32, 64])
-def test_scores_and_topk(kfmt, Hi):
+@pytest.mark.parametrize("kfmt,Hi,N", [("bf16", 32, 3000), ("bf16", 64, 3000),
+                                        ("fp8_mx32", 32, 3000), ("fp8_mx32", 64, 3000),
+                                        ("fp8_mx32", 64, 3001), ("bf16", 16, 1029)])
+def test_scores_and_topk(kfmt, Hi, N):
+    """Several work-groups per row, partial last steps, n_vis clamping; N = 3001
+    puts the per-sequence key bases off 16-byte alignment (132-B rows)."""
     need_gpu()
-    B, Q, N, k = 3, 2, 3000, 512
+    B, Q, k = 3, 2, 512
     w = synth.Workload(90, "t", B=B, ctx=4 * N, ratio=4, n_entries=N, Hi=Hi, key_fmt=kfmt)
     qi = synth.bf16_round(synth.normal_batched(w.seed, synth.T_QIDX, B, (Q, Hi, 128)))
     wi = synth.normal_batched(w.seed, synth.T_WIDX, B, (Q, Hi), (128 * Hi) ** -0.5)
     K = synth.index_keys(w)                                           # [B, N, 128] f32 values
     pos = np.array([[4 * N - 1, 2047], [5, 0], [601, 4 * N + 900]], np.int32)  # n_vis clamps
-    say(f"index_topk {kfmt} Hi={Hi}")
+    say(f"index_topk {kfmt} Hi={Hi} N={N}")
     kdev = upload_rows(K, kfmt)
     out = torch.empty((B, Q, k), dtype=torch.int32, device="cuda")
     sc = torch.full((B, Q, N), float("nan"), dtype=torch.float32, device="cuda")
