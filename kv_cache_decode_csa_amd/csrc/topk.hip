@@ -325,6 +325,43 @@ __device__ void sort512_desc(uint64_t (&v)[2], uint64_t* lds) {
   }
 }
 
+// Descending sort of 512 packed values inside one wave, 8 per lane (element
+// e = 8 lane + i): bitonic network with in-register stages for partners in
+// the same lane and cross-lane shuffles for the rest; no LDS, no barrier.
+__device__ __forceinline__ void sort512_wave_desc(uint64_t (&v)[8]) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int k = 2; k <= 512; k <<= 1) {
+#pragma unroll
+    for (int j = k >> 1; j > 0; j >>= 1) {
+      if (j < 8) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const int p = i ^ j;
+          if (p > i) {
+            const bool desc = ((8 * lane + i) & k) == 0;
+            const uint64_t a = v[i], b = v[p];
+            const bool swap = desc ? (a < b) : (a > b);
+            v[i] = swap ? b : a;
+            v[p] = swap ? a : b;
+          }
+        }
+      } else {
+        const int lx = j >> 3;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const uint32_t lo = __shfl_xor((uint32_t)v[i], lx, 64);
+          const uint32_t hi = __shfl_xor((uint32_t)(v[i] >> 32), lx, 64);
+          const uint64_t pv = ((uint64_t)hi << 32) | lo;
+          const int e = 8 * lane + i;
+          const bool keep_max = ((e & j) == 0) == ((e & k) == 0);
+          v[i] = keep_max ? (v[i] > pv ? v[i] : pv) : (v[i] < pv ? v[i] : pv);
+        }
+      }
+    }
+  }
+}
+
 // Write the indices of n <= kSortCap (key, idx) pairs ordered by key desc,
 // idx asc (pairs packed as key << 32 | ~idx).
 __device__ void order_store(const uint32_t* key, const uint32_t* idx, int n, uint64_t* tmp,
@@ -377,18 +414,32 @@ __global__ void __launch_bounds__(kSelThreads) topk_collect_kernel(
   const uint32_t base = blockIdx.x * (uint32_t)kChunk;
   const uint32_t end = base + kChunk < nv ? base + kChunk : nv;
   constexpr int kPer = kChunk / kSelThreads;
+  // element of (thread t, slot j): base + 4 (t + 256 (j / 4)) + j % 4, read as
+  // float4 (scores first: their latency overlaps the histogram's)
   uint32_t kk[kPer];
+  const bool full = base + kChunk <= nv && (ld & 3) == 0;
+  if (full) {
 #pragma unroll
-  for (int j = 0; j < kPer; ++j) {  // scores first: their latency overlaps the histogram's
-    const uint32_t i = base + t + j * kSelThreads;
-    kk[j] = i < end ? score_key(s[i]) : 0u;
+    for (int q = 0; q < kPer / 4; ++q) {
+      const float4 v = *(const float4*)(s + base + 4 * (t + kSelThreads * q));
+      kk[4 * q] = score_key(v.x); kk[4 * q + 1] = score_key(v.y);
+      kk[4 * q + 2] = score_key(v.z); kk[4 * q + 3] = score_key(v.w);
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+      const uint32_t i = base + 4 * (t + kSelThreads * (j >> 2)) + (j & 3);
+      kk[j] = i < end ? score_key(s[i]) : 0u;
+    }
   }
   {
-    uint32_t hv[kHistBins / kSelThreads];
+    uint4 hv[kHistBins / kSelThreads / 4];
 #pragma unroll
-    for (int j = 0; j < kHistBins / kSelThreads; ++j) hv[j] = hist_g[row * kHistBins + t + j * kSelThreads];
+    for (int q = 0; q < kHistBins / kSelThreads / 4; ++q)
+      hv[q] = *(const uint4*)(hist_g + row * kHistBins + 4 * (t + kSelThreads * q));
 #pragma unroll
-    for (int j = 0; j < kHistBins / kSelThreads; ++j) hist[t + j * kSelThreads] = hv[j];
+    for (int q = 0; q < kHistBins / kSelThreads / 4; ++q)
+      *(uint4*)(hist + 4 * (t + kSelThreads * q)) = hv[q];
   }
   __syncthreads();
   uint32_t above;
@@ -403,7 +454,7 @@ __global__ void __launch_bounds__(kSelThreads) topk_collect_kernel(
   uint32_t n_hi_t = 0, n_eq_t = 0;
 #pragma unroll
   for (int j = 0; j < kPer; ++j) {
-    const uint32_t i = base + t + j * kSelThreads;
+    const uint32_t i = base + 4 * (t + kSelThreads * (j >> 2)) + (j & 3);
     const uint32_t b = kk[j] >> 20;
     if (i < end && b > b1) ++n_hi_t;
     if (i < end && b == b1) ++n_eq_t;
@@ -432,7 +483,7 @@ __global__ void __launch_bounds__(kSelThreads) topk_collect_kernel(
   uint32_t sh = scratch[8] + off_h, se = scratch[9] + off_e;
 #pragma unroll
   for (int j = 0; j < kPer; ++j) {
-    const uint32_t i = base + t + j * kSelThreads;
+    const uint32_t i = base + 4 * (t + kSelThreads * (j >> 2)) + (j & 3);
     if (i >= end) continue;
     const uint32_t b = kk[j] >> 20;
     if (b > b1) {
@@ -476,9 +527,40 @@ __global__ void __launch_bounds__(kSelThreads) topk_final_kernel(
   const uint32_t* cand = cand_g + row * (int64_t)kCandCap * 2;
   const uint32_t* hi = hi_g + row * (int64_t)kTopkMax * 2;
   const float* s = scores + row * ld;
+  // Both lists' first 512 pairs are read before their lengths are known (the
+  // workspace always holds them), so the two reads overlap.
+  const int lane = t & 63, wv = t >> 6;
+  uint64_t fv[8];
+  if (wv < 2) {
+    const uint2* src = (const uint2*)(wv == 0 ? hi : cand) + 8 * lane;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const uint2 pr = src[i];
+      fv[i] = ((uint64_t)pr.x << 32) | (uint64_t)(~pr.y);
+    }
+  }
   const uint32_t b1 = info->b1, above = info->above, eq = info->eq;
   const bool keep_eq = eq <= (uint32_t)kCandCap;
   const uint32_t need = k_eff - above;
+  // Fast path: every entry of the hi list outranks every entry of the
+  // boundary bin, so the answer is the sorted hi list followed by the first
+  // `need` entries of the sorted boundary list.  One wave sorts each list.
+  if (keep_eq && above <= 512u && eq <= 512u) {
+    if (wv < 2) {
+      const uint32_t n = wv == 0 ? above : eq;
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        if ((uint32_t)(8 * lane + i) >= n) fv[i] = 0ull;  // padding sorts last
+      sort512_wave_desc(fv);
+      const uint32_t lim = wv == 0 ? above : need;
+      int32_t* o = out + (wv == 0 ? 0u : above);
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        if ((uint32_t)(8 * lane + i) < lim) o[8 * lane + i] = (int32_t)(~(uint32_t)fv[i]);
+    }
+    for (int i = (int)k_eff + t; i < topk; i += kSelThreads) out[i] = -1;
+    return;
+  }
   if (t == 0) { L.n_sel = 0; L.n_ties = 0; }
   uint32_t hk[kHiPerThread], hx[kHiPerThread];
 #pragma unroll

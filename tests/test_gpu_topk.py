@@ -65,6 +65,24 @@ def test_boundary_bin_overflow_falls_back():
     check(S, np.array([ld, ld, ld - 1], np.int32), 512)
 
 
+def test_boundary_bin_refinement_path():
+    """Between 512 and the candidate capacity share the boundary bin: the
+    two-digit refinement with index ties at the threshold decides; rows with a
+    small boundary bin and ties inside it take the sort-only path."""
+    need_gpu()
+    ld = 6000
+    rng = np.random.default_rng(4)
+    S = np.zeros((4, ld), np.float32)
+    S[0] = (1.0 + rng.integers(0, 4096, ld) * 2.0 ** -20).astype(np.float32)  # one 12-bit bin
+    S[1] = (1.0 + rng.integers(0, 40, ld) * 2.0 ** -20).astype(np.float32)    # heavy ties
+    S[2] = rng.standard_normal(ld).astype(np.float32)
+    S[2, rng.choice(ld, 300, replace=False)] = np.float32(2.5)                 # ties in the tail
+    S[3] = S[0]
+    S[3, :700] = np.float32(3.0)                                               # hi list > 512
+    check(S, np.array([ld, ld - 1, ld, ld], np.int32), 512)
+    check(S, np.array([ld, 5000, 4000, ld], np.int32), 1024)
+
+
 def test_run_to_run_bitwise():
     need_gpu()
     ld = 100000
