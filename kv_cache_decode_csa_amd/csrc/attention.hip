@@ -485,9 +485,9 @@ __global__ void __launch_bounds__(kAttnThreads) attn_mfma_kernel(AttnArgs a, int
 
 // ------------------------------------------------------------------ merge
 // One work-group per (unit, head group, 64-dim slice); thread t owns head t/16
-// and 4 dims.  Chunks are combined in index order; each batch of 8 chunks is
+// and 4 dims.  Chunks are combined in index order; each batch of 16 chunks is
 // loaded before any is combined, so the loads overlap.
-constexpr int kMergeBatch = 8;
+constexpr int kMergeBatch = 16;
 
 __global__ void __launch_bounds__(kAttnThreads) attn_merge_kernel(AttnArgs a, int nchunks,
                                                                   const Partial* part) {
@@ -500,29 +500,50 @@ __global__ void __launch_bounds__(kAttnThreads) attn_merge_kernel(AttnArgs a, in
   const int rr = rope_row(a, a.pos[unit]);
   const int h = tid >> 4;
   const int d0 = 64 * slice + 4 * (tid & 15);
+  const float sink2 = a.sink[16 * hg + h] * kLog2e;
   float M = -INFINITY;
-  for (int c = 0; c < nchunks; ++c) M = fmaxf(M, P[c].m[h]);
   float L = 0.f;
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-  for (int c0 = 0; c0 < nchunks; c0 += kMergeBatch) {
+  auto fold = [&](float mc, float lc, float4 oc) {
+    if (mc == -INFINITY) return;
+    const float wgt = exp2f(mc - M);
+    L += lc * wgt;
+    acc.x += oc.x * wgt; acc.y += oc.y * wgt; acc.z += oc.z * wgt; acc.w += oc.w * wgt;
+  };
+  if (nchunks <= kMergeBatch) {
+    // every chunk's values in one round of loads
     float mc[kMergeBatch], lc[kMergeBatch];
     float4 oc[kMergeBatch];
 #pragma unroll
     for (int i = 0; i < kMergeBatch; ++i) {
-      const int c = c0 + i < nchunks ? c0 + i : nchunks - 1;
+      const int c = i < nchunks ? i : nchunks - 1;
       mc[i] = P[c].m[h];
       lc[i] = P[c].l[h];
       oc[i] = *(const float4*)(P[c].o + h * kHeadDim + d0);
     }
 #pragma unroll
-    for (int i = 0; i < kMergeBatch; ++i) {
-      if (c0 + i >= nchunks || mc[i] == -INFINITY) continue;
-      const float wgt = exp2f(mc[i] - M);
-      L += lc[i] * wgt;
-      acc.x += oc[i].x * wgt; acc.y += oc[i].y * wgt; acc.z += oc[i].z * wgt; acc.w += oc[i].w * wgt;
+    for (int i = 0; i < kMergeBatch; ++i)
+      if (i < nchunks) M = fmaxf(M, mc[i]);
+#pragma unroll
+    for (int i = 0; i < kMergeBatch; ++i)
+      if (i < nchunks) fold(mc[i], lc[i], oc[i]);
+  } else {
+    for (int c = 0; c < nchunks; ++c) M = fmaxf(M, P[c].m[h]);
+    for (int c0 = 0; c0 < nchunks; c0 += kMergeBatch) {
+      float mc[kMergeBatch], lc[kMergeBatch];
+      float4 oc[kMergeBatch];
+#pragma unroll
+      for (int i = 0; i < kMergeBatch; ++i) {
+        const int c = c0 + i < nchunks ? c0 + i : nchunks - 1;
+        mc[i] = P[c].m[h];
+        lc[i] = P[c].l[h];
+        oc[i] = *(const float4*)(P[c].o + h * kHeadDim + d0);
+      }
+#pragma unroll
+      for (int i = 0; i < kMergeBatch; ++i)
+        if (c0 + i < nchunks) fold(mc[i], lc[i], oc[i]);
     }
   }
-  const float sink2 = a.sink[16 * hg + h] * kLog2e;
   const float den = (M == -INFINITY) ? 0.f : L + exp2f(sink2 - M);
   const float inv = den > 0.f ? 1.f / den : 0.f;
   float v[4] = {acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv};

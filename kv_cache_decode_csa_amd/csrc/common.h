@@ -15,6 +15,9 @@ namespace csa {
 typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8_t;
 typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4_t;
 typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4_t;
+// Native 4 x u32 vector: unlike HIP's uint4 (a union-wrapped struct) its
+// copies stay in registers.
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
 // ---------------------------------------------------------------- bf16 bits
 __device__ __forceinline__ float bf16_to_f32(uint16_t b) {
@@ -173,6 +176,7 @@ __device__ __forceinline__ f32x4_t mfma16x16x32(const bf16x8_t& a, const bf16x8_
 }
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(uint4 u) { return __builtin_bit_cast(bf16x8_t, u); }
+__device__ __forceinline__ bf16x8_t as_bf16x8(u32x4_t u) { return __builtin_bit_cast(bf16x8_t, u); }
 
 // order-preserving float -> uint32 key for a descending top-k (-0 == +0, NaN lowest)
 __device__ __forceinline__ uint32_t score_key(float s) {

@@ -20,6 +20,13 @@ namespace {
 
 constexpr int kThreads = 256;
 
+// Orders one wave's LDS accesses (LDS operations of a wave execute in order).
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
 __device__ __forceinline__ float ldv(const void* p, int fmt, int64_t i) {
   return fmt == CSA_F32 ? ((const float*)p)[i] : bf16_to_f32(((const uint16_t*)p)[i]);
 }
@@ -105,46 +112,69 @@ __global__ void __launch_bounds__(kProjThreads) proj_mfma_kernel(const uint16_t*
   const int N = 2 * CD;
   const int n = blockIdx.x * 16 + r16;
   const uint16_t* wrow = n < CD ? wkv + (int64_t)n * K : wg + (int64_t)(n - CD) * K;
-  const int kwave = K / 8;
-  const int kb = wave * kwave;
+  // epilogue inputs of the direct (single-token) mode, fetched up front: the
+  // position of each of this thread's 4 output rows and the score columns'
+  // slot bias
+  const int tt = threadIdx.x;
+  const int emt = tt >> 6, el = tt & 63;
+  const int enn = blockIdx.x * 16 + (el & 15);
+  int64_t ep[4];
+  float eape[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int m = 16 * emt + 4 * (el >> 4) + r;
+    ep[r] = -1;
+    eape[r] = 0.f;
+    if (po.direct && tt < MT * 64 && m < M) {
+      ep[r] = po.start_pos[m];
+      if (enn >= CD && ep[r] >= 0) eape[r] = po.ape[(ep[r] % po.ratio) * CD + enn - CD];
+    }
+  }
+  // wave w covers k in [w K/8, (w+1) K/8): nks steps of 32.  All of a batch's
+  // loads are issued before its MFMAs (addresses clamped to valid steps and
+  // rows, out-of-range operands zeroed), so they are in flight together.
+  constexpr int kB = MT <= 2 ? 16 : 8;
+  const int nks = K / 256;
+  const int kb = wave * (K / 8);
   f32x4_t acc[MT];
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) acc[mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  for (int k = kb; k < kb + kwave; k += 256) {
-    uint4 bw[8];
-    uint4 ax[8][MT];
+  for (int ks0 = 0; ks0 < nks; ks0 += kB) {
+    u32x4_t bw[kB];
+    u32x4_t ax[kB][MT];
 #pragma unroll
-    for (int u = 0; u < 8; ++u)
-      bw[u] = k + 32 * u < kb + kwave ? *(const uint4*)(wrow + k + 32 * u + 8 * kq)
-                                      : make_uint4(0, 0, 0, 0);
-#pragma unroll
-    for (int u = 0; u < 8; ++u)
+    for (int u = 0; u < kB; ++u) {
+      const int ks = ks0 + u < nks ? ks0 + u : nks - 1;
+      const int k = kb + 32 * ks + 8 * kq;
+      bw[u] = *(const u32x4_t*)(wrow + k);
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
-        const int m = 16 * mt + r16;
-        ax[u][mt] = (m < M && k + 32 * u < kb + kwave)
-                        ? *(const uint4*)(x + (int64_t)m * K + k + 32 * u + 8 * kq)
-                        : make_uint4(0, 0, 0, 0);
+        const int m = 16 * mt + r16 < M ? 16 * mt + r16 : M - 1;
+        ax[u][mt] = *(const u32x4_t*)(x + (int64_t)m * K + k);
       }
+    }
 #pragma unroll
-    for (int u = 0; u < 8; ++u)
+    for (int u = 0; u < kB; ++u) {
+      const bool step_ok = ks0 + u < nks;  // a clamped repeat of the last step adds zero
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt)
-        acc[mt] = mfma16x16x32(as_bf16x8(ax[u][mt]), as_bf16x8(bw[u]), acc[mt]);
+      for (int mt = 0; mt < MT; ++mt) {
+        const u32x4_t av = (step_ok && 16 * mt + r16 < M) ? ax[u][mt] : u32x4_t{0u, 0u, 0u, 0u};
+        acc[mt] = mfma16x16x32(as_bf16x8(av), as_bf16x8(bw[u]), acc[mt]);
+      }
+    }
   }
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) red[wave][mt][lane] = acc[mt];
   __syncthreads();
-  const int t = threadIdx.x;
-  if (t < MT * 64) {
-    const int mt = t >> 6, l = t & 63;
+  if (tt < MT * 64) {
+    const int mt = emt, l = el;
     f32x4_t v = red[0][mt][l];
 #pragma unroll
     for (int w = 1; w < 8; ++w) {
       const f32x4_t u = red[w][mt][l];
       v[0] += u[0]; v[1] += u[1]; v[2] += u[2]; v[3] += u[3];
     }
-    const int nn = blockIdx.x * 16 + (l & 15);
+    const int nn = enn;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int m = 16 * mt + 4 * (l >> 4) + r;
@@ -153,12 +183,12 @@ __global__ void __launch_bounds__(kProjThreads) proj_mfma_kernel(const uint16_t*
         po.P[(int64_t)m * N + nn] = v[r];
         continue;
       }
-      const int64_t p = po.start_pos[m];
+      const int64_t p = ep[r];
       if (p < 0) continue;
       const int slot = (po.coff == 2 ? po.ratio : 0) + (int)(p % po.ratio);
       const int64_t base = ((int64_t)m * po.coff * po.ratio + slot) * CD;
       if (nn < CD) po.kv_state[base + nn] = v[r];
-      else po.score_state[base + nn - CD] = v[r] + po.ape[(p % po.ratio) * CD + nn - CD];
+      else po.score_state[base + nn - CD] = v[r] + eape[r];
     }
   }
 }
@@ -308,63 +338,128 @@ __device__ float pool_block(const CompArgs& a, int64_t b, int64_t p0, int64_t i,
   return sq;
 }
 
+// Store element c of a finished row: lanes c .. c+31 (FP8) or c .. c+15 (FP4)
+// of one group are consecutive lanes of a wave, so the group's amax is a
+// shuffle reduction and every lane encodes its own value (the same per-value
+// arithmetic as the one-thread group encoders).  Every lane of the wave must
+// call it (values past d are passed as 0 with live = false).
+__device__ __forceinline__ void store_elem(int fmt, float v, int c, int d, bool live, uint8_t* row) {
+  const float av = __builtin_fabsf(v);
+  const bool fin = av <= 3.402823466e38f;
+  if (fmt == CSA_FP8_MX32) {
+    float amax = fin ? av : 0.f;
+#pragma unroll
+    for (int m = 1; m < 32; m <<= 1) amax = fmaxf(amax, shfl_xor_f(amax, m));
+    const int e = mx32_exponent(amax);
+    const uint32_t code = f32_to_e4m3(ldexpf(v, -e));
+    // gather 4 codes into the lane holding the first one (rows are 4-byte aligned)
+    const uint32_t c1 = __shfl_down(code, 1, 64), c2 = __shfl_down(code, 2, 64),
+                   c3 = __shfl_down(code, 3, 64);
+    if (live && (c & 3) == 0) *(uint32_t*)(row + c) = code | (c1 << 8) | (c2 << 16) | (c3 << 24);
+    if (live && (c & 31) == 0) row[d + (c >> 5)] = (uint8_t)(e + 127);
+  } else {
+    float amax = fin ? av : 0.f;
+    float bad = fin ? 0.f : 1.f;
+#pragma unroll
+    for (int m = 1; m < 16; m <<= 1) {
+      amax = fmaxf(amax, shfl_xor_f(amax, m));
+      bad = fmaxf(bad, shfl_xor_f(bad, m));
+    }
+    const bool allfin = bad == 0.f;
+    const uint32_t sc = allfin ? f32_to_e4m3(__fdiv_rn(amax, 6.0f)) : 0x7fu;
+    const float sv = e4m3_to_f32(sc);
+    const uint32_t code = (allfin && sv > 0.f) ? f32_to_e2m1(__fdiv_rn(v, sv)) : 0u;
+    const uint32_t odd = __shfl_down(code, 1, 64);
+    if (live && (c & 1) == 0) row[c >> 1] = (uint8_t)(code | (odd << 4));
+    if (live && (c & 15) == 0) row[d / 2 + (c >> 4)] = (uint8_t)sc;
+  }
+}
+
 // RMSNorm -> RoPE at position i * r -> optional Hadamard -> storage rounding of
-// the pooled block in y; writes entry i of sequence b.
-__device__ void finish_block(const CompArgs& a, int64_t b, int64_t i, float* y, float* red,
-                             float sq) {
+// the pooled block in y; writes entry i of sequence b.  z: LDS scratch of d
+// floats.
+__device__ void finish_block(const CompArgs& a, int64_t b, int64_t i, float* y, float* z,
+                             float* red, float sq) {
   const int tid = threadIdx.x;
   const int r = a.ratio;
   const int d = a.d;
+  // norm weights and rotation factors of this thread's channels (d <= 512 =
+  // 2 kThreads), fetched before the reduction so their latency overlaps it
+  int64_t rrow = i * r;
+  if (rrow >= a.rope_rows) rrow = a.rope_rows - 1;
+  float gw[2], gp[2], cs[2], sn[2];
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const int c = tid + u * kThreads;
+    gw[u] = gp[u] = cs[u] = 1.f;
+    sn[u] = 0.f;
+    if (c < d) {
+      gw[u] = a.norm_w[c];
+      if (c >= d - kRopeDims) {
+        const int k = (c - (d - kRopeDims)) >> 1;
+        gp[u] = a.norm_w[c ^ 1];
+        cs[u] = a.rope_cos[rrow * 32 + k];
+        sn[u] = a.rope_sin[rrow * 32 + k];
+      }
+    }
+  }
   sq = wave_sum(sq);
   if ((tid & 63) == 0) red[tid >> 6] = sq;
   __syncthreads();
   const float ms = ((red[0] + red[1]) + (red[2] + red[3])) / (float)d;
   const float inv = 1.0f / sqrtf(ms + a.eps);
-  for (int c = tid; c < d; c += kThreads) y[c] = y[c] * inv * a.norm_w[c];
-  __syncthreads();
-  // RoPE on the last 64 dims at position i * r
-  {
-    int64_t rrow = i * r;
-    if (rrow >= a.rope_rows) rrow = a.rope_rows - 1;
-    if (tid < kRopeDims / 2) {
-      const int c0 = d - kRopeDims + 2 * tid;
-      const float cs = a.rope_cos[rrow * 32 + tid], sn = a.rope_sin[rrow * 32 + tid];
-      const float x0 = y[c0], x1 = y[c0 + 1];
-      y[c0] = x0 * cs - x1 * sn;
-      y[c0 + 1] = x0 * sn + x1 * cs;
+  // normalise, and rotate the last 64 dims at position i * r (pairs 2k, 2k+1)
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const int c = tid + u * kThreads;
+    if (c >= d) continue;
+    const float v = y[c] * inv * gw[u];
+    float out = v;
+    if (c >= d - kRopeDims) {
+      const float vp = y[c ^ 1] * inv * gp[u];
+      out = (c & 1) ? (vp * sn[u] + v * cs[u]) : (v * cs[u] - vp * sn[u]);
     }
-    __syncthreads();
+    z[c] = out;
   }
-  // Sylvester Hadamard (butterflies a+b, a-b at strides 1..d/2), scaled by d^-1/2
+  __syncthreads();
+  // Sylvester Hadamard (butterflies a+b, a-b at strides 1..d/2), scaled by
+  // d^-1/2; with d <= 128 all butterflies belong to wave 0
   if (a.rotate) {
-    for (int h = 1; h < d; h <<= 1) {
-      for (int q = tid; q < d / 2; q += kThreads) {
-        const int lo = (q / h) * 2 * h + (q % h);
-        const float u = y[lo], v = y[lo + h];
-        y[lo] = u + v;
-        y[lo + h] = u - v;
+    const bool one_wave = d <= 128;
+    if (!one_wave || tid < 64) {
+      for (int h = 1; h < d; h <<= 1) {
+        for (int q = tid; q < d / 2; q += kThreads) {
+          const int lo = (q / h) * 2 * h + (q % h);
+          const float u = z[lo], v = z[lo + h];
+          z[lo] = u + v;
+          z[lo + h] = u - v;
+        }
+        if (one_wave) wave_lds_sync(); else __syncthreads();
       }
-      __syncthreads();
     }
+    if (one_wave) __syncthreads();
     const float sc = 1.0f / sqrtf((float)d);
-    for (int c = tid; c < d; c += kThreads) y[c] *= sc;
+    for (int c = tid; c < d; c += kThreads) z[c] *= sc;
     __syncthreads();
   }
   if (i >= a.entries_cap) return;
   uint8_t* row = a.entries + ((size_t)b * (size_t)a.entries_cap + (size_t)i) * a.entry_rb;
   if (a.entry_fmt == CSA_F32) {
-    for (int c = tid; c < d; c += kThreads) ((float*)row)[c] = y[c];
+    for (int c = tid; c < d; c += kThreads) ((float*)row)[c] = z[c];
   } else if (a.entry_fmt == CSA_BF16) {
-    for (int c = tid; c < d; c += kThreads) ((uint16_t*)row)[c] = f32_to_bf16(y[c]);
-  } else if (a.entry_fmt == CSA_FP8_MX32) {
-    if (tid < d / 32) encode_fp8_group(y + 32 * tid, row + 32 * tid, row + d + tid);
+    for (int c = tid; c < d; c += kThreads) ((uint16_t*)row)[c] = f32_to_bf16(z[c]);
   } else {
-    if (tid < d / 16) encode_fp4_group(y + 16 * tid, row + 8 * tid, row + d / 2 + tid);
+    for (int c0 = 0; c0 < d; c0 += kThreads) {  // uniform trip count: whole waves call
+      const int c = c0 + tid;
+      const bool live = c < d;
+      store_elem(a.entry_fmt, live ? z[c] : 0.f, c, d, live, row);
+    }
   }
 }
 
 __global__ void __launch_bounds__(kThreads) emit_kernel(CompArgs a) {
   __shared__ float y[512];
+  __shared__ float z[512];
   __shared__ float red[4];
   const int64_t b = blockIdx.y;
   const int64_t p0 = a.start_pos[b];
@@ -372,7 +467,7 @@ __global__ void __launch_bounds__(kThreads) emit_kernel(CompArgs a) {
   const int64_t i = p0 / r + blockIdx.x;              // candidate block
   if (p0 < 0 || (i + 1) * r - 1 >= p0 + a.T) return;  // not completed by this call
   const float sq = pool_block(a, b, p0, i, y);
-  finish_block(a, b, i, y, red, sq);
+  finish_block(a, b, i, y, z, red, sq);
 }
 
 // ------------------------------------------------------------------ state
@@ -454,18 +549,31 @@ __global__ void __launch_bounds__(kThreads) state_kernel(CompArgs a) {
 // then finishes the entry.
 __global__ void __launch_bounds__(kThreads) emit_t1_kernel(CompArgs a) {
   __shared__ float y[512];
+  __shared__ float z[512];
   __shared__ float red[4];
   const int64_t b = blockIdx.x;
   const int64_t p0 = a.start_pos[b];
   const int r = a.ratio;
-  if (p0 < 0 || (p0 + 1) % r != 0) return;
-  const int64_t i = p0 / r;
   const int d = a.d, tid = threadIdx.x;
   const int nslots = a.coff * r;
   const int64_t sb = b * (int64_t)nslots * a.CD;
+  if (p0 < 0 || (p0 + 1) % r != 0) return;
+  const int64_t i = p0 / r;
   float sq = 0.f;
   for (int c = tid; c < d; c += kThreads) {
+    // with overlap, the shift moves current slots r..2r-1 of columns c and
+    // d + c into slots 0..r-1: the first half's values are loaded together
+    // with the pooled ones, and this thread alone touches these columns
+    float shv[4], shs[4];
+    if (a.coff == 2) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        shv[q] = a.kv_state[sb + (int64_t)(r + q) * a.CD + c];
+        shs[q] = a.score_state[sb + (int64_t)(r + q) * a.CD + c];
+      }
+    }
     float m = -INFINITY, l = 0.f, acc = 0.f;
+    float cur_v[4], cur_s[4];
     for (int sl0 = 0; sl0 < nslots; sl0 += 8) {
       float vv[8], ss[8];
 #pragma unroll
@@ -475,6 +583,10 @@ __global__ void __launch_bounds__(kThreads) emit_t1_kernel(CompArgs a) {
         const int64_t si = sb + (int64_t)sl * a.CD + col;
         vv[j] = sl < nslots ? a.kv_state[si] : 0.f;
         ss[j] = sl < nslots ? a.score_state[si] : -INFINITY;
+      }
+      if (a.coff == 2) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) { cur_v[q] = vv[4 + q]; cur_s[q] = ss[4 + q]; }
       }
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
@@ -487,27 +599,20 @@ __global__ void __launch_bounds__(kThreads) emit_t1_kernel(CompArgs a) {
         m = mn;
       }
     }
+    if (a.coff == 2) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        a.kv_state[sb + (int64_t)q * a.CD + c] = shv[q];
+        a.score_state[sb + (int64_t)q * a.CD + c] = shs[q];
+        a.kv_state[sb + (int64_t)q * a.CD + d + c] = cur_v[q];
+        a.score_state[sb + (int64_t)q * a.CD + d + c] = cur_s[q];
+      }
+    }
     const float C = acc / l;
     y[c] = C;
     sq = fmaf(C, C, sq);
   }
-  __syncthreads();  // every read of the slots is done
-  if (a.coff == 2) {
-    for (int col = tid; col < a.CD; col += kThreads) {
-      float kv[4], sc[4];  // all loads first, then all stores
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        kv[q] = a.kv_state[sb + (int64_t)(r + q) * a.CD + col];
-        sc[q] = a.score_state[sb + (int64_t)(r + q) * a.CD + col];
-      }
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        a.kv_state[sb + (int64_t)q * a.CD + col] = kv[q];
-        a.score_state[sb + (int64_t)q * a.CD + col] = sc[q];
-      }
-    }
-  }
-  finish_block(a, b, i, y, red, sq);
+  finish_block(a, b, i, y, z, red, sq);
 }
 
 }  // namespace

@@ -73,9 +73,6 @@ __device__ __forceinline__ bf16x8_t key_frag(const KeyRaw& r, int s) {
   }
 }
 
-// Native 4 x u32 vectors (HIP's uint4 is a union-wrapped struct whose copies
-// the compiler keeps in private memory).
-typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
 // ---- LDS staging of one step's keys (one wave's region)
 // FP8: the step's 64 rows of 132 B are stored as the contiguous byte stream

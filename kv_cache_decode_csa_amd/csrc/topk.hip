@@ -325,41 +325,92 @@ __device__ void sort512_desc(uint64_t (&v)[2], uint64_t* lds) {
   }
 }
 
-// Descending sort of 512 packed values inside one wave, 8 per lane (element
-// e = 8 lane + i): bitonic network with in-register stages for partners in
-// the same lane and cross-lane shuffles for the rest; no LDS, no barrier.
-__device__ __forceinline__ void sort512_wave_desc(uint64_t (&v)[8]) {
-  const int lane = threadIdx.x & 63;
+// Lane exchange lane <-> lane ^ M within a wave, for a compile-time M: quad
+// permutes (1, 2) and a row rotate (8) on the DPP path, swizzles (4, 16),
+// a permute through LDS only for 32.
+template <int M>
+__device__ __forceinline__ uint32_t lane_xor(uint32_t x) {
+  if constexpr (M == 1) return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0xB1, 0xF, 0xF, true);
+  else if constexpr (M == 2) return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x4E, 0xF, 0xF, true);
+  else if constexpr (M == 8) return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x128, 0xF, 0xF, true);
+  else if constexpr (M == 4) return (uint32_t)__builtin_amdgcn_ds_swizzle((int)x, 0x1F | (4 << 10));
+  else if constexpr (M == 16) return (uint32_t)__builtin_amdgcn_ds_swizzle((int)x, 0x1F | (16 << 10));
+  else return (uint32_t)__builtin_amdgcn_ds_bpermute((int)(((threadIdx.x & 63) ^ M) << 2), (int)x);
+}
+
+// Bitonic network over 512 packed values held by a pair of waves, 4 per lane
+// (element e = 4 (64 pw + lane) + i, pw = this wave's place in the pair),
+// sorted descending.  Stage (K, J) compares e with e ^ J: inside a lane for
+// J < 4, across lanes (lane ^ J/4) for 4 <= J < 256, across the pair through
+// LDS for J = 256.  Every lane exchange of a stage is issued before any result
+// is used.  Called by all threads of the work-group (the J = 256 stage
+// synchronises it).
+template <int K, int J>
+__device__ __forceinline__ void bitonic_stage(uint64_t (&v)[4], int e0, uint64_t* lds) {
+  if constexpr (J < 4) {
 #pragma unroll
-  for (int k = 2; k <= 512; k <<= 1) {
-#pragma unroll
-    for (int j = k >> 1; j > 0; j >>= 1) {
-      if (j < 8) {
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const int p = i ^ j;
-          if (p > i) {
-            const bool desc = ((8 * lane + i) & k) == 0;
-            const uint64_t a = v[i], b = v[p];
-            const bool swap = desc ? (a < b) : (a > b);
-            v[i] = swap ? b : a;
-            v[p] = swap ? a : b;
-          }
-        }
-      } else {
-        const int lx = j >> 3;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const uint32_t lo = __shfl_xor((uint32_t)v[i], lx, 64);
-          const uint32_t hi = __shfl_xor((uint32_t)(v[i] >> 32), lx, 64);
-          const uint64_t pv = ((uint64_t)hi << 32) | lo;
-          const int e = 8 * lane + i;
-          const bool keep_max = ((e & j) == 0) == ((e & k) == 0);
-          v[i] = keep_max ? (v[i] > pv ? v[i] : pv) : (v[i] < pv ? v[i] : pv);
-        }
+    for (int i = 0; i < 4; ++i) {
+      constexpr int jj = J;
+      const int p = i ^ jj;
+      if (p > i) {
+        const bool desc = ((e0 + i) & K) == 0;
+        const uint64_t a = v[i], b = v[p];
+        const bool swap = desc ? (a < b) : (a > b);
+        v[i] = swap ? b : a;
+        v[p] = swap ? a : b;
       }
     }
+  } else {
+    uint64_t pv[4];
+    if constexpr (J < 256) {
+      uint32_t lo[4], hi[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        lo[i] = lane_xor<J / 4>((uint32_t)v[i]);
+        hi[i] = lane_xor<J / 4>((uint32_t)(v[i] >> 32));
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) pv[i] = ((uint64_t)hi[i] << 32) | lo[i];
+    } else {
+      __syncthreads();
+#pragma unroll
+      for (int i = 0; i < 4; ++i) lds[e0 + i] = v[i];
+      __syncthreads();
+#pragma unroll
+      for (int i = 0; i < 4; ++i) pv[i] = lds[(e0 + i) ^ J];
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int e = e0 + i;
+      const bool keep_max = ((e & J) == 0) == ((e & K) == 0);
+      v[i] = keep_max ? (v[i] > pv[i] ? v[i] : pv[i]) : (v[i] < pv[i] ? v[i] : pv[i]);
+    }
   }
+}
+
+template <int K, int J> struct BitonicJ {
+  static __device__ __forceinline__ void run(uint64_t (&v)[4], int e0, uint64_t* lds) {
+    bitonic_stage<K, J>(v, e0, lds);
+    BitonicJ<K, J / 2>::run(v, e0, lds);
+  }
+};
+template <int K> struct BitonicJ<K, 0> {
+  static __device__ __forceinline__ void run(uint64_t (&)[4], int, uint64_t*) {}
+};
+template <int K> struct BitonicK {
+  static __device__ __forceinline__ void run(uint64_t (&v)[4], int e0, uint64_t* lds) {
+    BitonicJ<K, K / 2>::run(v, e0, lds);
+    BitonicK<2 * K>::run(v, e0, lds);
+  }
+};
+template <> struct BitonicK<1024> {
+  static __device__ __forceinline__ void run(uint64_t (&)[4], int, uint64_t*) {}
+};
+
+// lds: 512 uint64 for this pair of waves
+__device__ __forceinline__ void sort512_pair_desc(uint64_t (&v)[4], int pw, uint64_t* lds) {
+  const int e0 = 4 * (64 * pw + (threadIdx.x & 63));
+  BitonicK<2>::run(v, e0, lds);
 }
 
 // Write the indices of n <= kSortCap (key, idx) pairs ordered by key desc,
@@ -528,13 +579,16 @@ __global__ void __launch_bounds__(kSelThreads) topk_final_kernel(
   const uint32_t* hi = hi_g + row * (int64_t)kTopkMax * 2;
   const float* s = scores + row * ld;
   // Both lists' first 512 pairs are read before their lengths are known (the
-  // workspace always holds them), so the two reads overlap.
+  // workspace always holds them), so the two reads overlap.  Waves 0-1 hold
+  // the hi list, waves 2-3 the boundary list, 4 entries per lane.
   const int lane = t & 63, wv = t >> 6;
-  uint64_t fv[8];
-  if (wv < 2) {
-    const uint2* src = (const uint2*)(wv == 0 ? hi : cand) + 8 * lane;
+  const int lst = wv >> 1, pw = wv & 1;
+  const int e0 = 4 * (64 * pw + lane);
+  uint64_t fv[4];
+  {
+    const uint2* src = (const uint2*)(lst == 0 ? hi : cand) + e0;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
+    for (int i = 0; i < 4; ++i) {
       const uint2 pr = src[i];
       fv[i] = ((uint64_t)pr.x << 32) | (uint64_t)(~pr.y);
     }
@@ -544,20 +598,18 @@ __global__ void __launch_bounds__(kSelThreads) topk_final_kernel(
   const uint32_t need = k_eff - above;
   // Fast path: every entry of the hi list outranks every entry of the
   // boundary bin, so the answer is the sorted hi list followed by the first
-  // `need` entries of the sorted boundary list.  One wave sorts each list.
+  // `need` entries of the sorted boundary list.  A pair of waves sorts each.
   if (keep_eq && above <= 512u && eq <= 512u) {
-    if (wv < 2) {
-      const uint32_t n = wv == 0 ? above : eq;
+    const uint32_t n = lst == 0 ? above : eq;
 #pragma unroll
-      for (int i = 0; i < 8; ++i)
-        if ((uint32_t)(8 * lane + i) >= n) fv[i] = 0ull;  // padding sorts last
-      sort512_wave_desc(fv);
-      const uint32_t lim = wv == 0 ? above : need;
-      int32_t* o = out + (wv == 0 ? 0u : above);
+    for (int i = 0; i < 4; ++i)
+      if ((uint32_t)(e0 + i) >= n) fv[i] = 0ull;  // padding sorts last
+    sort512_pair_desc(fv, pw, (uint64_t*)L.ties + 512 * lst);
+    const uint32_t lim = lst == 0 ? above : need;
+    int32_t* o = out + (lst == 0 ? 0u : above);
 #pragma unroll
-      for (int i = 0; i < 8; ++i)
-        if ((uint32_t)(8 * lane + i) < lim) o[8 * lane + i] = (int32_t)(~(uint32_t)fv[i]);
-    }
+    for (int i = 0; i < 4; ++i)
+      if ((uint32_t)(e0 + i) < lim) o[e0 + i] = (int32_t)(~(uint32_t)fv[i]);
     for (int i = (int)k_eff + t; i < topk; i += kSelThreads) out[i] = -1;
     return;
   }
