@@ -1,5 +1,6 @@
-"""Helpers for the GPU parity tests: uploads, the library's RoPE tables and
-tolerance checks.  The oracle is called only by the tests themselves."""
+"""Helpers for the GPU parity tests: uploads, the library's RoPE tables,
+tolerance checks and the selection check (which calls the oracle's top-k;
+this module is test infrastructure like the oracle itself)."""
 
 import sys
 
@@ -8,6 +9,7 @@ import pytest
 import torch
 
 from kv_cache_decode_csa_amd import _lib
+from oracle import topk as _TK
 
 YARN = dict(factor=16.0, orig_len=65536, beta_fast=32.0, beta_slow=1.0)
 
@@ -85,3 +87,51 @@ def to_np(t):
     if t.dtype == torch.bfloat16:
         return t.float().cpu().numpy()
     return t.cpu().numpy()
+
+
+# ---------------------------------------------------------------- shared checks
+
+U = 2.0 ** -24
+
+
+def score_bound(q, w, K):
+    """|fp32 result - exact| bound: sum_h |w_h| (130 u sum_c |q_hc k_c|) + 70 u sum_h |w_h relu_h|."""
+    a = np.abs(K) @ np.abs(q).T  # [n, H]
+    d = np.maximum(K @ q.T, 0)
+    return 130 * U * (a @ np.abs(w)) + 70 * U * (d @ np.abs(w)) + 1e-30
+
+
+def check_selection(idx, S_gpu, S_ref, tol, nv, k):
+    ke = min(k, nv)
+    sel = idx[:ke]
+    assert np.all(idx[ke:] == -1)
+    assert len(set(sel.tolist())) == ke and np.all((sel >= 0) & (sel < nv))
+    # ordered by the library's own scores, ties by index
+    g = S_gpu[sel]
+    for a in range(ke - 1):
+        assert g[a] > g[a + 1] or (g[a] == g[a + 1] and sel[a] < sel[a + 1])
+    if ke < nv:
+        rest = np.setdiff1d(np.arange(nv), sel)
+        last = g[-1]
+        assert np.all((S_gpu[rest] < last) | ((S_gpu[rest] == last) & (rest > sel[-1])))
+    # against the oracle's own selection, away from near-ties
+    want = _TK.topk(S_ref[:nv].astype(np.float32), k, nv)[:ke]
+    diff = np.setxor1d(sel, want)
+    if len(diff):
+        thr = np.sort(S_ref[:nv])[::-1][ke - 1] if ke > 0 else 0
+        assert np.all(np.abs(S_ref[diff] - thr) <= 2 * tol[diff] + 1e-12), diff[:10]
+
+
+def step_bound(ref, fmt, d):
+    """One quantization step of each element's group at the oracle's value."""
+    if fmt in ("f32",):
+        return 1e-5 + 1e-5 * np.abs(ref)
+    if fmt == "bf16":
+        return 1e-3 + 2.0 ** -7 * np.abs(ref)
+    g = 32 if fmt == "fp8_mx32" else 16
+    amax = np.abs(ref).reshape(ref.shape[:-1] + (d // g, g)).max(-1, keepdims=True)
+    if fmt == "fp8_mx32":
+        step = amax / 448 * 2.0 ** -3 * 2      # coarsest e4m3 spacing in the group, x2 margin
+    else:
+        step = amax / 6 * 2.0 * 1.2            # coarsest e2m1 spacing (2) times the scale
+    return np.broadcast_to(step, ref.shape[:-1] + (d // g, g)).reshape(ref.shape) + 1e-6

@@ -11,7 +11,7 @@ import torch
 from kv_cache_decode_csa_amd import _lib, synth
 from oracle import codec, compressor, rope
 
-from gpu_util import bf16, close_f32, f32, i32, need_gpu, rope_tables, say, to_np
+from gpu_util import bf16, close_f32, f32, i32, need_gpu, rope_tables, say, step_bound, to_np
 
 pytestmark = pytest.mark.gpu
 ROPE_ROWS = 1 << 16
@@ -60,21 +60,6 @@ class GpuCompressor:
         if self.entry_fmt == "bf16":
             return codec.bf16_bits_to_f64(e.view(np.uint16))
         return codec.load(e, self.entry_fmt, self.d)
-
-
-def step_bound(ref, fmt, d):
-    """One quantization step of each element's group at the oracle's value."""
-    if fmt in ("f32",):
-        return 1e-5 + 1e-5 * np.abs(ref)
-    if fmt == "bf16":
-        return 1e-3 + 2.0 ** -7 * np.abs(ref)
-    g = 32 if fmt == "fp8_mx32" else 16
-    amax = np.abs(ref).reshape(ref.shape[:-1] + (d // g, g)).max(-1, keepdims=True)
-    if fmt == "fp8_mx32":
-        step = amax / 448 * 2.0 ** -3 * 2      # coarsest e4m3 spacing in the group, x2 margin
-    else:
-        step = amax / 6 * 2.0 * 1.2            # coarsest e2m1 spacing (2) times the scale
-    return np.broadcast_to(step, ref.shape[:-1] + (d // g, g)).reshape(ref.shape) + 1e-6
 
 
 def weights(rng, dim, d, ratio, scale=0.02):

@@ -1,0 +1,173 @@
+"""Full-size parity in the launch configuration bench.py times (GPU).
+
+For each bench workload the decode layer is built as bench.py builds it (same
+shapes, formats, kernels and stream arrangement) and one decode step runs at
+t = context - 1: both compressors, scoring and top-k, attention.  Sampled
+outputs are then checked against the oracle, which starts from the seeded
+synthetic values (never from the library's bytes):
+
+* the entries the compressors emitted (main KV and index key) against the
+  oracle compressor over the same hidden states, within one quantization step;
+* stored cache rows (a sample per sequence) against the oracle codec, bit for
+  bit;
+* index scores of sampled keys and of every selected key, within the float32
+  error bound, and the selection: a valid top-k of the library's scores that
+  equals the oracle's away from near-ties;
+* the attention output of every head of sampled sequences, over the library's
+  own index set, within the bf16 tolerance.
+"""
+
+import gc
+
+import numpy as np
+import pytest
+import torch
+
+from kv_cache_decode_csa_amd import _lib, decode, synth
+from oracle import attention, codec, compressor, indexer, rope
+
+from gpu_util import check_selection, close_bf16, need_gpu, say, score_bound, step_bound, to_np
+
+pytestmark = pytest.mark.gpu
+
+WORKLOADS = {"csa_1m_fp8": 5, "csa_1m_mxfp4": 5, "csa_64k_bf16": 2, "hca_1m_bf16": 3}
+
+
+def workload(name):
+    w = synth.WORKLOADS[WORKLOADS[name]]
+    return synth.mxfp4_variant(w) if name == "csa_1m_mxfp4" else w
+
+
+def oracle_new_entries(w, b, d, indexer_side, om):
+    """Entries the layer's compressor emits from the hidden states at t-7 .. t
+    (the 7 set-up tokens, then the step's token), starting from an empty state."""
+    wkv, wg, ape, norm = synth.compressor_weights(w, d, w.ratio, indexer=indexer_side)
+    tail = synth.normal_batched(w.seed, synth.T_XTAIL, w.B, (7, w.dim), b_range=[b])[0]
+    xs = synth.normal_batched(w.seed, synth.T_X, w.B, (1, w.dim), b_range=[b])[0]
+    x = synth.bf16_round(np.concatenate([tail, xs]))
+    ent, _ = compressor.compress_stream(x.astype(np.float64), w.t - 7, wkv, wg, ape, norm, om,
+                                        w.ratio, d, rotate=indexer_side)
+    return ent
+
+
+def check_entry(got_row, ref, fmt, d):
+    stored = codec.store(ref, fmt)[1]
+    if fmt == "bf16":
+        got = codec.bf16_bits_to_f64(got_row.view(np.uint16))
+    else:
+        got = codec.load(got_row, fmt, d)
+    err = np.abs(got - stored)
+    assert np.all(err <= step_bound(ref, fmt, d)), err.max()
+
+
+def rows_of(t, fmt, d):
+    """Device rows [N, row] (uint8) or bf16 [N, d] as host bytes."""
+    a = t.cpu()
+    if a.dtype == torch.bfloat16:
+        return a.view(torch.int16).numpy().view(np.uint16)
+    return a.numpy()
+
+
+@pytest.mark.parametrize("name", list(WORKLOADS))
+def test_fullsize_decode_step(name):
+    need_gpu()
+    w = workload(name)
+    say(f"full-size step {name}: B={w.B} ctx={w.ctx} entries={w.n_entries}")
+    Layer = decode.CsaDecodeLayer if w.ratio == 4 else decode.HcaDecodeLayer
+    layer = Layer(w, copies=1)
+    layer.step()
+    torch.cuda.synchronize()
+    om = rope.frequencies(w.theta, rope.V4_YARN if w.yarn else None)
+    t, N, B = w.t, w.n_entries, w.B
+    csa = w.ratio == 4
+    ent_dev = layer.sets[0][0] if csa else layer.sets[0]
+    out = to_np(layer.out)[:, 0]                                   # [B, H, 512]
+    ids = layer.topk.cpu().numpy()[:, 0] if csa else None          # [B, k]
+    new_i = [t // w.ratio - 1, t // w.ratio]                       # emitted by set-up and by the step
+    if not csa:
+        new_i = [t // w.ratio]
+
+    # scores with the library's own output buffer (same inputs as the step)
+    S_gpu = None
+    if csa:
+        keys_dev = layer.sets[0][1]
+        sc = torch.empty((B, 1, N), dtype=torch.float32, device="cuda")
+        ids2 = torch.empty_like(layer.topk)
+        _lib.csa_index_topk(layer.qi, w.q_fmt, layer.wi, keys_dev, w.key_fmt, layer.pos, 4, B, 1,
+                            w.Hi, N, w.topk, ids2, sc, layer.ws_idx)
+        torch.cuda.synchronize()
+        assert np.array_equal(ids2.cpu().numpy()[:, 0], ids), "selection differs between calls"
+        S_gpu = sc.cpu().numpy()[:, 0]
+
+    rng = np.random.default_rng(99)
+    check_b = [0, B - 1]
+    for b in range(B):
+        full = b in check_b
+        # 1. emitted entries
+        ref_main = oracle_new_entries(w, b, 512, False, om)
+        main_rows = rows_of(ent_dev[b, new_i[0]:new_i[-1] + 1], w.ent_fmt, 512)
+        for j, i in enumerate(new_i):
+            check_entry(main_rows[j], ref_main[i], w.ent_fmt, 512)
+        if csa:
+            ref_key = oracle_new_entries(w, b, 128, True, om)
+            key_rows = rows_of(keys_dev[b, new_i[0]:new_i[-1] + 1], w.key_fmt, 128)
+            for j, i in enumerate(new_i):
+                check_entry(key_rows[j], ref_key[i], w.key_fmt, 128)
+        if not full and not csa:
+            continue
+        # 2. index scores and selection
+        if csa:
+            qi, wi = synth.index_queries(w, [b])
+            qi, wi = qi[0].astype(np.float64), wi[0].astype(np.float64)
+            nv = int(indexer.n_visible(t, 4, N))
+            if full:
+                kv = synth.index_keys(w, [b])[0]
+                kst, kval = codec.store(kv, w.key_fmt)
+                # stored bytes of sampled rows equal the oracle codec's
+                samp = rng.choice(N - 2, 256, replace=False)
+                got_b = rows_of(keys_dev[b].index_select(
+                    0, torch.from_numpy(samp).cuda()), w.key_fmt, 128)
+                assert np.array_equal(got_b, kst[samp]), "stored index keys differ"
+                for i in new_i:                                     # rows the compressor wrote
+                    kval[i] = codec.store(ref_key[i], w.key_fmt)[1]
+                S_ref = indexer.scores(qi, wi, kval, nv)
+                tol = score_bound(qi, wi, kval[:nv])
+                err = np.abs(S_gpu[b, :nv] - S_ref)
+                assert np.all(err <= tol), (b, err.max())
+                check_selection(ids[b], S_gpu[b], S_ref, tol, nv, w.topk)
+                say(f"  b={b}: scores and selection ok (max err {err.max():.2e})")
+                del kv, kst, kval
+        if not full:
+            continue
+        # 3. attention over the library's own index set
+        q, sink = synth.queries(w, [b])
+        win = codec.store(synth.window_rows(w, [b])[0], w.win_fmt)[1]
+        E = synth.entries(w, [b])[0]
+        wid = attention.window_ids(t)
+        if csa:
+            # the selected rows in list order; slot j of the list reads row j
+            sel = ids[b]
+            rows = codec.store(E[np.maximum(sel, 0)], w.ent_fmt)[1]
+            for i in new_i:
+                rows[sel == i] = codec.store(ref_main[i], w.ent_fmt)[1]
+            slots = np.where(sel >= 0, np.arange(len(sel)), -1)
+            ref = attention.sparse_decode(q[0].astype(np.float64), win, wid, rows, slots, sink,
+                                          512 ** -0.5, t, om)
+        else:
+            Ev = codec.store(E, w.ent_fmt)[1]
+            # stored bytes of sampled rows equal the oracle codec's
+            samp = rng.choice(N - 1, 64, replace=False)
+            got_b = rows_of(ent_dev[b].index_select(0, torch.from_numpy(samp).cuda()), w.ent_fmt, 512)
+            assert np.array_equal(got_b, codec.store(E[samp], w.ent_fmt)[0]), "stored entries differ"
+            for i in new_i:
+                Ev[i] = codec.store(ref_main[i], w.ent_fmt)[1]
+            ref = attention.hca_decode(q[0].astype(np.float64), win, wid, Ev, sink, 512 ** -0.5, t,
+                                       om, ratio=w.ratio)
+            del Ev
+        close_bf16(out[b], ref)
+        say(f"  b={b}: attention ok")
+        del E
+        gc.collect()
+    del layer
+    gc.collect()
+    torch.cuda.empty_cache()

@@ -14,42 +14,10 @@ import torch
 
 from kv_cache_decode_csa_amd import _lib, synth
 from oracle import codec, indexer
-from oracle import topk as TK
 
-from gpu_util import bf16, f32, i32, need_gpu, say, upload_rows
+from gpu_util import bf16, check_selection, f32, i32, need_gpu, say, score_bound, upload_rows
 
 pytestmark = pytest.mark.gpu
-
-U = 2.0 ** -24
-
-
-def score_bound(q, w, K):
-    """|fp32 result - exact| bound: sum_h |w_h| (130 u sum_c |q_hc k_c|) + 70 u sum_h |w_h relu_h|."""
-    a = np.abs(K) @ np.abs(q).T  # [n, H]
-    d = np.maximum(K @ q.T, 0)
-    return 130 * U * (a @ np.abs(w)) + 70 * U * (d @ np.abs(w)) + 1e-30
-
-
-def check_selection(idx, S_gpu, S_ref, tol, nv, k):
-    ke = min(k, nv)
-    sel = idx[:ke]
-    assert np.all(idx[ke:] == -1)
-    assert len(set(sel.tolist())) == ke and np.all((sel >= 0) & (sel < nv))
-    # ordered by the library's own scores, ties by index
-    g = S_gpu[sel]
-    for a in range(ke - 1):
-        assert g[a] > g[a + 1] or (g[a] == g[a + 1] and sel[a] < sel[a + 1])
-    if ke < nv:
-        rest = np.setdiff1d(np.arange(nv), sel)
-        last = g[-1]
-        assert np.all((S_gpu[rest] < last) | ((S_gpu[rest] == last) & (rest > sel[-1])))
-    # against the oracle's own selection, away from near-ties
-    want = TK.topk(S_ref[:nv].astype(np.float32), k, nv)[:ke]
-    diff = np.setxor1d(sel, want)
-    if len(diff):
-        thr = np.sort(S_ref[:nv])[::-1][ke - 1] if ke > 0 else 0
-        assert np.all(np.abs(S_ref[diff] - thr) <= 2 * tol[diff] + 1e-12), diff[:10]
-
 
 @pytest.mark.parametrize("kfmt,Hi,N", [("bf16", 32, 3000), ("bf16", 64, 3000),
                                         ("fp8_mx32", 32, 3000), ("fp8_mx32", 64, 3000),
