@@ -176,6 +176,12 @@ __device__ __forceinline__ uint4 frag_bf16(const Raw<F>& r, int s, int kq) {
 }
 
 constexpr int kRPitch = 128 + 16;  // bf16 per LDS row of a wave's 128-dim slice
+// The 16-byte chunks of LDS row r are stored XOR-swizzled by bit 2 of r, so
+// that both the fragment writes (8 rows per group of lanes) and the
+// transposing reads (4 rows x 4 column pairs) hit distinct banks.
+__device__ __forceinline__ int rswz(int row, int col) {  // bf16 offset of (row, col)
+  return row * kRPitch + ((((col >> 3) ^ (row >> 2)) & 1) | ((col >> 3) & ~1)) * 8 + (col & 7);
+}
 constexpr int kMaxIdsPerLane = kChunkCsa / 16;
 
 struct SoftmaxState {
@@ -188,7 +194,7 @@ struct SoftmaxState {
 // the 4 waves' partials through LDS, online softmax, O += P C.
 __device__ __forceinline__ void attend_tile(const uint4 (&fr)[2][4], uint32_t vmask,
                                             const uint4 (&qa)[4], float zscale, int w, int lane,
-                                            uint16_t* R, float4 (*Sp)[64][2], SoftmaxState& st) {
+                                            uint16_t* R, float4 (*Sp)[2][64], SoftmaxState& st) {
   const int r16 = lane & 15, kq = lane >> 4;
   f32x4_t sacc[2];
 #pragma unroll
@@ -199,22 +205,22 @@ __device__ __forceinline__ void attend_tile(const uint4 (&fr)[2][4], uint32_t vm
       sacc[rt] = mfma16x16x32(as_bf16x8(fr[rt][s]), as_bf16x8(qa[s]), sacc[rt]);
   }
   __syncthreads();  // the previous tile's readers of Sp / R are done
-  Sp[w][lane][0] = make_float4(sacc[0][0], sacc[0][1], sacc[0][2], sacc[0][3]);
-  Sp[w][lane][1] = make_float4(sacc[1][0], sacc[1][1], sacc[1][2], sacc[1][3]);
+  Sp[w][0][lane] = make_float4(sacc[0][0], sacc[0][1], sacc[0][2], sacc[0][3]);
+  Sp[w][1][lane] = make_float4(sacc[1][0], sacc[1][1], sacc[1][2], sacc[1][3]);
 #pragma unroll
   for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
     for (int s = 0; s < 4; ++s)
-      *(uint4*)(R + (16 * rt + r16) * kRPitch + 32 * s + 8 * kq) = fr[rt][s];
+      *(uint4*)(R + rswz(16 * rt + r16, 32 * s + 8 * kq)) = fr[rt][s];
   __syncthreads();
 
   float z[2][4];
 #pragma unroll
   for (int rt = 0; rt < 2; ++rt) {
-    float4 acc = Sp[0][lane][rt];
+    float4 acc = Sp[0][rt][lane];
 #pragma unroll
     for (int ww = 1; ww < 4; ++ww) {
-      const float4 v = Sp[ww][lane][rt];
+      const float4 v = Sp[ww][rt][lane];
       acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
     }
     z[rt][0] = acc.x; z[rt][1] = acc.y; z[rt][2] = acc.z; z[rt][3] = acc.w;
@@ -253,12 +259,11 @@ __device__ __forceinline__ void attend_tile(const uint4 (&fr)[2][4], uint32_t vm
                                            pack_bf16x2(p[0][2], p[0][3]),
                                            pack_bf16x2(p[1][0], p[1][1]),
                                            pack_bf16x2(p[1][2], p[1][3])));
-  const uint16_t* rb0 = R + (4 * kq + (r16 >> 2)) * kRPitch + 4 * (r16 & 3);
-  const uint16_t* rb1 = rb0 + 16 * kRPitch;
+  const int rrow = 4 * kq + (r16 >> 2);
 #pragma unroll
   for (int dt = 0; dt < 8; ++dt) {
-    const uint2 c0 = lds_read_tr16(rb0 + 16 * dt);
-    const uint2 c1 = lds_read_tr16(rb1 + 16 * dt);
+    const uint2 c0 = lds_read_tr16(R + rswz(rrow, 16 * dt + 4 * (r16 & 3)));
+    const uint2 c1 = lds_read_tr16(R + rswz(rrow + 16, 16 * dt + 4 * (r16 & 3)));
     f32x4_t acc = st.o[dt];
 #pragma unroll
     for (int r = 0; r < 4; ++r) acc[r] *= al[r];
@@ -274,7 +279,7 @@ template <int F, class RowFn>
 __device__ __forceinline__ void run_rows(int64_t j0, int64_t j1, RowFn row_of,
                                          const uint8_t* stand_in, const uint4 (&qa)[4],
                                          float zscale, int w, int lane, uint16_t* R,
-                                         float4 (*Sp)[64][2], SoftmaxState& st) {
+                                         float4 (*Sp)[2][64], SoftmaxState& st) {
   const int r16 = lane & 15, kq = lane >> 4;
   auto load_tile = [&](int64_t jt, Raw<F> (&f)[2], uint32_t& vm) {
     vm = 0;
@@ -339,7 +344,7 @@ __global__ void __launch_bounds__(kAttnThreads) attn_mfma_kernel(AttnArgs a, int
                                                                  int nchunks, int64_t units,
                                                                  Partial* part) {
   __shared__ uint16_t Rl[4][kTile * kRPitch];
-  __shared__ float4 Sp[4][64][2];
+  __shared__ float4 Sp[4][2][64];
 
   const AttnItem it = attn_item(a, nchunks, units);
   if (!it.live) return;

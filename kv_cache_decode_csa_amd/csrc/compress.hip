@@ -193,6 +193,63 @@ __global__ void __launch_bounds__(kProjThreads) proj_mfma_kernel(const uint16_t*
   }
 }
 
+// Single-token (decode) projection split over K: work-group (column block,
+// k slice ks) is one wave that takes 16 weight rows over k in [ks K/8,
+// (ks+1) K/8) -- all of its loads in flight together -- and writes the 16x16
+// partial products to part[ks][m][n].  The emit kernel adds the eight slices
+// in order, the same summation as the one-work-group projection above.
+constexpr int kKSlices = 8;
+
+template <int MT>
+__global__ void __launch_bounds__(64) proj_slice_kernel(const uint16_t* __restrict__ x,
+                                                        const uint16_t* __restrict__ wkv,
+                                                        const uint16_t* __restrict__ wg, int M,
+                                                        int K, int CD, float* __restrict__ part) {
+  const int lane = threadIdx.x;
+  const int r16 = lane & 15, kq = lane >> 4;
+  const int N = 2 * CD;
+  const int n = blockIdx.x * 16 + r16;
+  const uint16_t* wrow = n < CD ? wkv + (int64_t)n * K : wg + (int64_t)(n - CD) * K;
+  constexpr int kB = MT <= 2 ? 16 : 8;
+  const int nks = K / 256;
+  const int kb = blockIdx.y * (K / kKSlices);
+  f32x4_t acc[MT];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) acc[mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  for (int ks0 = 0; ks0 < nks; ks0 += kB) {
+    u32x4_t bw[kB];
+    u32x4_t ax[kB][MT];
+#pragma unroll
+    for (int u = 0; u < kB; ++u) {
+      const int ks = ks0 + u < nks ? ks0 + u : nks - 1;
+      const int k = kb + 32 * ks + 8 * kq;
+      bw[u] = *(const u32x4_t*)(wrow + k);
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        const int m = 16 * mt + r16 < M ? 16 * mt + r16 : M - 1;
+        ax[u][mt] = *(const u32x4_t*)(x + (int64_t)m * K + k);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kB; ++u) {
+      const bool step_ok = ks0 + u < nks;
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        const u32x4_t av = (step_ok && 16 * mt + r16 < M) ? ax[u][mt] : u32x4_t{0u, 0u, 0u, 0u};
+        acc[mt] = mfma16x16x32(as_bf16x8(av), as_bf16x8(bw[u]), acc[mt]);
+      }
+    }
+  }
+  float* dst = part + (int64_t)blockIdx.y * M * N + blockIdx.x * 16 + (lane & 15);
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int m = 16 * mt + 4 * (lane >> 4) + r;
+      if (m < M) dst[(int64_t)m * N] = acc[mt][r];
+    }
+}
+
 // Tiled GEMM, float32 FMA: P[m][n] = sum_k x[m][k] W[n][k], 64x64 tiles.
 constexpr int kTM = 64, kTN = 64, kTK = 32;
 
@@ -543,10 +600,11 @@ __global__ void __launch_bounds__(kThreads) state_kernel(CompArgs a) {
   if (col < a.CD) state_column(a, blockIdx.y, col);
 }
 
-// Single-token calls: the projection already wrote the token into its slot.
-// One work-group per sequence whose block just completed pools the block from
-// the slot state, shifts the current slots into the previous ones (overlap),
-// then finishes the entry.
+// Single-token calls, one work-group per sequence: add the projection's k
+// slices for the new token (score gets its slot bias) and write its slot; if
+// the token completes a block, pool the block (the new token's values from
+// registers, the others from the state), shift the current slots into the
+// previous ones (overlap) and finish the entry.
 __global__ void __launch_bounds__(kThreads) emit_t1_kernel(CompArgs a) {
   __shared__ float y[512];
   __shared__ float z[512];
@@ -556,20 +614,48 @@ __global__ void __launch_bounds__(kThreads) emit_t1_kernel(CompArgs a) {
   const int r = a.ratio;
   const int d = a.d, tid = threadIdx.x;
   const int nslots = a.coff * r;
+  const int N = 2 * a.CD;
   const int64_t sb = b * (int64_t)nslots * a.CD;
-  if (p0 < 0 || (p0 + 1) % r != 0) return;
+  if (p0 < 0) return;
+  const int ns = (a.coff == 2 ? r : 0) + (int)(p0 % r);  // the new token's slot
+  const bool done = (p0 + 1) % r == 0;
   const int64_t i = p0 / r;
+  const float* apr = a.ape + (int64_t)(p0 % r) * a.CD;
   float sq = 0.f;
   for (int c = tid; c < d; c += kThreads) {
+    // new token: columns c (and d + c with overlap) of v and of the score
+    float nv[2], nsc[2];
+    const int halves = a.coff;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      if (h >= halves) break;
+      const int col = c + h * d;
+      const float* pp = a.P + b * (int64_t)N + col;
+      float sv = pp[0], ss = pp[a.CD];
+#pragma unroll
+      for (int ks = 1; ks < kKSlices; ++ks) {
+        sv += pp[(int64_t)ks * a.B * N];
+        ss += pp[(int64_t)ks * a.B * N + a.CD];
+      }
+      nv[h] = sv;
+      nsc[h] = ss + apr[col];
+    }
+    if (!done) {
+      for (int h = 0; h < halves; ++h) {
+        a.kv_state[sb + (int64_t)ns * a.CD + c + h * d] = nv[h];
+        a.score_state[sb + (int64_t)ns * a.CD + c + h * d] = nsc[h];
+      }
+      continue;
+    }
     // with overlap, the shift moves current slots r..2r-1 of columns c and
-    // d + c into slots 0..r-1: the first half's values are loaded together
-    // with the pooled ones, and this thread alone touches these columns
+    // d + c into slots 0..r-1; this thread alone touches these columns
     float shv[4], shs[4];
     if (a.coff == 2) {
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        shv[q] = a.kv_state[sb + (int64_t)(r + q) * a.CD + c];
-        shs[q] = a.score_state[sb + (int64_t)(r + q) * a.CD + c];
+        const bool nw = r + q == ns;
+        shv[q] = nw ? nv[0] : a.kv_state[sb + (int64_t)(r + q) * a.CD + c];
+        shs[q] = nw ? nsc[0] : a.score_state[sb + (int64_t)(r + q) * a.CD + c];
       }
     }
     float m = -INFINITY, l = 0.f, acc = 0.f;
@@ -579,10 +665,16 @@ __global__ void __launch_bounds__(kThreads) emit_t1_kernel(CompArgs a) {
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         const int sl = sl0 + j;
-        const int col = (a.coff == 2 && sl >= r) ? d + c : c;
+        const int hh = (a.coff == 2 && sl >= r) ? 1 : 0;
+        const int col = c + hh * d;
         const int64_t si = sb + (int64_t)sl * a.CD + col;
-        vv[j] = sl < nslots ? a.kv_state[si] : 0.f;
-        ss[j] = sl < nslots ? a.score_state[si] : -INFINITY;
+        if (sl == ns) {
+          vv[j] = nv[hh];
+          ss[j] = nsc[hh];
+        } else {
+          vv[j] = sl < nslots ? a.kv_state[si] : 0.f;
+          ss[j] = sl < nslots ? a.score_state[si] : -INFINITY;
+        }
       }
       if (a.coff == 2) {
 #pragma unroll
@@ -607,11 +699,20 @@ __global__ void __launch_bounds__(kThreads) emit_t1_kernel(CompArgs a) {
         a.kv_state[sb + (int64_t)q * a.CD + d + c] = cur_v[q];
         a.score_state[sb + (int64_t)q * a.CD + d + c] = cur_s[q];
       }
+      // the new token's own slot keeps its value (as the state machine does)
+      a.kv_state[sb + (int64_t)ns * a.CD + c] = nv[0];
+      a.score_state[sb + (int64_t)ns * a.CD + c] = nsc[0];
+      a.kv_state[sb + (int64_t)ns * a.CD + d + c] = nv[1];
+      a.score_state[sb + (int64_t)ns * a.CD + d + c] = nsc[1];
+    } else {
+      a.kv_state[sb + (int64_t)ns * a.CD + c] = nv[0];
+      a.score_state[sb + (int64_t)ns * a.CD + c] = nsc[0];
     }
     const float C = acc / l;
     y[c] = C;
     sq = fmaf(C, C, sq);
   }
+  if (!done) return;
   finish_block(a, b, i, y, z, red, sq);
 }
 
@@ -626,7 +727,8 @@ static bool use_mfma_proj(const csa_compress_args* a) {
 size_t compress_ws_bytes(const csa_compress_args* a) {
   const int coff = a->ratio == 4 ? 2 : 1;
   const int CD = coff * a->head_dim;
-  if (a->T == 1 && use_mfma_proj(a)) return 0;  // written straight into the slot state
+  if (a->T == 1 && use_mfma_proj(a))  // per-slice partial products
+    return align_up((size_t)kKSlices * a->B * 2 * CD * sizeof(float), 256);
   return align_up((size_t)a->B * a->T * 2 * CD * sizeof(float), 256);
 }
 
@@ -657,10 +759,19 @@ hipError_t launch_compress(const csa_compress_args* in, void* ws, hipStream_t s)
   const int64_t M = (int64_t)in->B * in->T;
   const int N = 2 * a.CD;
   const bool direct = in->T == 1 && use_mfma_proj(in);
-  if (use_mfma_proj(in)) {
+  if (direct) {
     const int mt = (int)((M + 15) / 16);
-    ProjOut po{P, direct ? 1 : 0, in->start_pos, in->ape, in->ratio, a.coff, in->kv_state,
-               in->score_state};
+    const dim3 grid(N / 16, kKSlices);
+    const uint16_t* xp = (const uint16_t*)in->x;
+    const uint16_t* wk = (const uint16_t*)in->w_kv;
+    const uint16_t* wgp = (const uint16_t*)in->w_gate;
+    if (mt == 1) hipLaunchKernelGGL(proj_slice_kernel<1>, grid, dim3(64), 0, s, xp, wk, wgp, (int)M, in->dim, a.CD, P);
+    else if (mt == 2) hipLaunchKernelGGL(proj_slice_kernel<2>, grid, dim3(64), 0, s, xp, wk, wgp, (int)M, in->dim, a.CD, P);
+    else if (mt == 3) hipLaunchKernelGGL(proj_slice_kernel<3>, grid, dim3(64), 0, s, xp, wk, wgp, (int)M, in->dim, a.CD, P);
+    else hipLaunchKernelGGL(proj_slice_kernel<4>, grid, dim3(64), 0, s, xp, wk, wgp, (int)M, in->dim, a.CD, P);
+  } else if (use_mfma_proj(in)) {
+    const int mt = (int)((M + 15) / 16);
+    ProjOut po{P, 0, in->start_pos, in->ape, in->ratio, a.coff, in->kv_state, in->score_state};
     dim3 grid(N / 16);
     const uint16_t* xp = (const uint16_t*)in->x;
     const uint16_t* wk = (const uint16_t*)in->w_kv;
