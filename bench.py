@@ -19,8 +19,10 @@ HIP events on the stream it runs on.  cpu_baseline times the float64 oracle
 """
 
 import argparse
+import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -64,6 +66,31 @@ def algorithmic_bytes(w):
                                       + 128 * row_bytes(w.win_fmt, 512)
                                       + 2 * w.H * 512 * qb) + w.H * 4
     return out
+
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "csa_1m_fp8_hbm_traffic.md")
+
+
+def measured_traffic(workload):
+    """HBM bytes per csa_index_topk call from the committed counter summary
+    (FETCH_SIZE + WRITE_SIZE runs, copy-calibrated), or None when there is no
+    summary for this workload or the kernel sources changed since it was taken."""
+    if workload != "csa_1m_fp8" or not os.path.exists(TRAFFIC_PROFILE):
+        return None
+    text = open(TRAFFIC_PROFILE).read()
+    m_b = re.search(r"traffic_bytes_per_call: (\d+)", text)
+    m_h = re.search(r"sources_sha256: ([0-9a-f]+)", text)
+    m_s = re.search(r"sources: (.+)", text)
+    if not (m_b and m_h and m_s):
+        return None
+    h = hashlib.sha256()
+    for f in m_s.group(1).split():
+        path = os.path.join(ROOT, f)
+        if not os.path.exists(path):
+            return None
+        h.update(open(path, "rb").read())
+    return int(m_b.group(1)) if h.hexdigest() == m_h.group(1) else None
 
 
 def time_steps(layer, steps, torch):
@@ -223,7 +250,8 @@ def main():
                    "kv_format": w.ent_fmt, "window_format": w.win_fmt,
                    "index_key_format": w.key_fmt, "cache_copies": a.copies},
         "roofline": {"bound": "hbm", "achieved": dom_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": dom_gbs / HBM_PEAK_GBS, "traffic": None, "kernel": dom,
+                     "frac": dom_gbs / HBM_PEAK_GBS, "traffic": measured_traffic(a.workload),
+                     "kernel": dom,
                      "bytes_per_launch": ab[dom], "ms_per_launch": phases[dom]},
         "step_hbm_GBps": step_bytes / (ms * 1e-3) / 1e9,
         "phases_ms": phases,
