@@ -20,6 +20,8 @@
 //     in a fixed order, adds the sink, normalises and undoes the RoPE.
 // Row formats are decoded exactly to bf16 on load (E4M3 x 2^e and E2M1 x E4M3
 // both fit bf16's 8-bit significand).
+#include <type_traits>
+
 #include "common.h"
 
 namespace csa {
@@ -316,6 +318,275 @@ __device__ __forceinline__ void run_rows(int64_t j0, int64_t j1, RowFn row_of,
   }
 }
 
+// Query slices for one wave: head tile ht of the work-group, dims
+// 128 w + 32 s + 8 kq .. +8, with the last 64 dims rotated at row rr.  Every
+// load (the fragments, and the rotation factors the wave needs) is issued
+// before any is used.
+template <int NH>
+__device__ __forceinline__ void load_q_frags(const AttnArgs& a, int64_t unit, int head0, int w,
+                                             int r16, int kq, int rr, uint4 (&qa)[NH][4]) {
+#pragma unroll
+  for (int ht = 0; ht < NH; ++ht) {
+    const uint16_t* qp = (const uint16_t*)a.q + (unit * a.H + head0 + 16 * ht + r16) * (int64_t)kHeadDim;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) qa[ht][s] = *(const uint4*)(qp + 128 * w + 32 * s + 8 * kq);
+  }
+  // dims >= 448 belong to wave 3, k-steps 2 and 3: pair k = 16 (s - 2) + 4 kq + j
+  if (w != 3) return;
+  float cs[2][4], sn[2][4];
+#pragma unroll
+  for (int s = 0; s < 2; ++s)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      cs[s][j] = a.rope_cos[(int64_t)rr * 32 + 16 * s + 4 * kq + j];
+      sn[s][j] = a.rope_sin[(int64_t)rr * 32 + 16 * s + 4 * kq + j];
+    }
+#pragma unroll
+  for (int ht = 0; ht < NH; ++ht)
+#pragma unroll
+    for (int s = 2; s < 4; ++s) {
+      const uint4 raw = qa[ht][s];
+      float v[8];
+      const uint32_t u[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        v[2 * j] = __uint_as_float(u[j] << 16);
+        v[2 * j + 1] = __uint_as_float(u[j] & 0xffff0000u);
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float c = cs[s - 2][j], sv = sn[s - 2][j];
+        const float x = v[2 * j], y = v[2 * j + 1];
+        v[2 * j] = x * c - y * sv;
+        v[2 * j + 1] = x * sv + y * c;
+      }
+      qa[ht][s] = make_uint4(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]),
+                             pack_bf16x2(v[4], v[5]), pack_bf16x2(v[6], v[7]));
+    }
+}
+
+// ------------------------------------------------------------------ dense, all heads
+// Dense lists (HCA) with H <= 64: one work-group serves every head, so each
+// row is read once.  Waves still own 128 of the 512 dims; after the partial
+// logits of all head tiles are summed through LDS, wave w runs the softmax of
+// head tile w, and P and the rescale factors go through LDS so that every
+// wave accumulates O for all heads over its dims.
+constexpr int kChunkDense = 512;  // rows per work-group
+
+template <int HT>
+__device__ __forceinline__ void attend_tile_all(const uint4 (&fr)[2][4], uint32_t vmask,
+                                                const uint4 (&qa)[HT][4], float zscale, int w,
+                                                int lane, uint16_t* R, float4 (*Sp)[HT][2][64],
+                                                uint4* Pl, float* Al, float& sm, float& sl,
+                                                f32x4_t (&o)[HT][8]) {
+  const int r16 = lane & 15, kq = lane >> 4;
+  f32x4_t sacc[HT][2];
+#pragma unroll
+  for (int ht = 0; ht < HT; ++ht)
+#pragma unroll
+    for (int rt = 0; rt < 2; ++rt) sacc[ht][rt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int s = 0; s < 4; ++s)
+#pragma unroll
+    for (int ht = 0; ht < HT; ++ht)
+#pragma unroll
+      for (int rt = 0; rt < 2; ++rt)
+        sacc[ht][rt] = mfma16x16x32(as_bf16x8(fr[rt][s]), as_bf16x8(qa[ht][s]), sacc[ht][rt]);
+  __syncthreads();  // the previous tile's readers of Sp / R / Pl / Al are done
+#pragma unroll
+  for (int ht = 0; ht < HT; ++ht)
+#pragma unroll
+    for (int rt = 0; rt < 2; ++rt)
+      Sp[w][ht][rt][lane] = make_float4(sacc[ht][rt][0], sacc[ht][rt][1], sacc[ht][rt][2],
+                                        sacc[ht][rt][3]);
+#pragma unroll
+  for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+      *(uint4*)(R + rswz(16 * rt + r16, 32 * s + 8 * kq)) = fr[rt][s];
+  __syncthreads();
+  if (w < HT) {  // softmax of head tile w
+    float z[2][4];
+#pragma unroll
+    for (int rt = 0; rt < 2; ++rt) {
+      float4 acc = Sp[0][w][rt][lane];
+#pragma unroll
+      for (int ww = 1; ww < 4; ++ww) {
+        const float4 v = Sp[ww][w][rt][lane];
+        acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
+      }
+      z[rt][0] = acc.x; z[rt][1] = acc.y; z[rt][2] = acc.z; z[rt][3] = acc.w;
+    }
+    float tmax = -INFINITY;
+#pragma unroll
+    for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const bool ok = (vmask >> (16 * rt + 4 * kq + r)) & 1u;
+        z[rt][r] = ok ? z[rt][r] * zscale : -INFINITY;
+        tmax = fmaxf(tmax, z[rt][r]);
+      }
+    tmax = fmaxf(tmax, shfl_xor_f(tmax, 16));
+    tmax = fmaxf(tmax, shfl_xor_f(tmax, 32));
+    const float m_new = fmaxf(sm, tmax);
+    const float alpha = (m_new == -INFINITY) ? 1.f : exp2f(sm - m_new);
+    float p[2][4];
+    float psum = 0.f;
+#pragma unroll
+    for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        p[rt][r] = (z[rt][r] == -INFINITY) ? 0.f : exp2f(z[rt][r] - m_new);
+        psum += p[rt][r];
+      }
+    psum += shfl_xor_f(psum, 16);
+    psum += shfl_xor_f(psum, 32);
+    sl = sl * alpha + psum;
+    sm = m_new;
+    Pl[w * 64 + lane] = make_uint4(pack_bf16x2(p[0][0], p[0][1]), pack_bf16x2(p[0][2], p[0][3]),
+                                   pack_bf16x2(p[1][0], p[1][1]), pack_bf16x2(p[1][2], p[1][3]));
+    if (kq == 0) Al[16 * w + r16] = alpha;
+  }
+  __syncthreads();
+  bf16x8_t pa[HT];
+  float al[HT][4];
+#pragma unroll
+  for (int ht = 0; ht < HT; ++ht) {
+    pa[ht] = as_bf16x8(Pl[ht * 64 + lane]);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) al[ht][r] = Al[16 * ht + 4 * kq + r];
+  }
+  const int rrow = 4 * kq + (r16 >> 2);
+#pragma unroll
+  for (int dt = 0; dt < 8; ++dt) {
+    const uint2 c0 = lds_read_tr16(R + rswz(rrow, 16 * dt + 4 * (r16 & 3)));
+    const uint2 c1 = lds_read_tr16(R + rswz(rrow + 16, 16 * dt + 4 * (r16 & 3)));
+    const bf16x8_t v = as_bf16x8(make_uint4(c0.x, c0.y, c1.x, c1.y));
+#pragma unroll
+    for (int ht = 0; ht < HT; ++ht) {
+      f32x4_t acc = o[ht][dt];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) acc[r] *= al[ht][r];
+      o[ht][dt] = mfma16x16x32(pa[ht], v, acc);
+    }
+  }
+}
+
+// Work-group = (chunk, unit), chunk-major so that the short last chunks of
+// the units run last.  Writes one partial per (unit, head tile, chunk) in the
+// layout of the merge kernel.
+template <int WF, int EF, int HT>
+__global__ void __launch_bounds__(kAttnThreads) attn_dense_all_kernel(AttnArgs a, int nchunks,
+                                                                      int64_t units,
+                                                                      Partial* part) {
+  __shared__ uint16_t Rl[4][kTile * kRPitch];
+  __shared__ float4 Sp[4][HT][2][64];
+  __shared__ uint4 Pl[HT * 64];
+  __shared__ float Al[16 * HT];
+
+  const int64_t item = blockIdx.x;
+  const int chunk = (int)(item / units);
+  const int64_t unit = a.unit_off + item % units;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = tid >> 6;
+  const int r16 = lane & 15;
+  const int kq = lane >> 4;
+  const int64_t b = unit / a.Q;
+  const int t = a.pos[unit];
+  const int64_t nvis = unit_nvis(a, t);
+  const int64_t list_len = kWindow + nvis;
+  const int64_t j_begin = (int64_t)chunk * kChunkDense;
+  int64_t j_end = j_begin + kChunkDense;
+  if (j_end > list_len) j_end = list_len;
+  const int rr = rope_row(a, t);
+  const float zscale = a.scale * kLog2e;
+
+  uint4 qa[HT][4];
+  load_q_frags<HT>(a, unit, 0, w, r16, kq, rr, qa);
+
+  float sm = -INFINITY, sl = 0.f;
+  f32x4_t o[HT][8];
+#pragma unroll
+  for (int ht = 0; ht < HT; ++ht)
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) o[ht][dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  uint16_t* R = Rl[w];
+
+  auto run = [&](auto fmt_tag, int64_t j0, int64_t j1, auto row_of, const uint8_t* stand_in) {
+    constexpr int F = decltype(fmt_tag)::value;
+    auto load_tile = [&](int64_t jt, Raw<F> (&f)[2], uint32_t& vm) {
+      vm = 0;
+#pragma unroll
+      for (int rt = 0; rt < 2; ++rt) {
+        const int64_t j = jt + 16 * rt + r16;
+        const uint8_t* p = j < j1 ? row_of(j) : nullptr;
+        const unsigned long long bal = __ballot(p != nullptr);
+        vm |= (uint32_t)(bal & 0xffffull) << (16 * rt);
+        load_raw<F>(p ? p : stand_in, w, kq, f[rt]);
+      }
+    };
+    auto compute_tile = [&](const Raw<F> (&f)[2], uint32_t vm) {
+      uint4 fr[2][4];
+#pragma unroll
+      for (int rt = 0; rt < 2; ++rt) {
+        const bool ok = (vm >> (16 * rt + r16)) & 1u;
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+          const uint4 v = frag_bf16<F>(f[rt], s, kq);
+          fr[rt][s] = ok ? v : make_uint4(0u, 0u, 0u, 0u);
+        }
+      }
+      attend_tile_all<HT>(fr, vm, qa, zscale, w, lane, R, Sp, Pl, Al, sm, sl, o);
+    };
+    Raw<F> fa[2], fb[2];
+    uint32_t va = 0, vb = 0;
+    load_tile(j0, fa, va);
+    for (int64_t jt = j0; jt < j1; jt += 2 * kTile) {
+      load_tile(jt + kTile, fb, vb);
+      compute_tile(fa, va);
+      load_tile(jt + 2 * kTile, fa, va);
+      if (jt + kTile < j1) compute_tile(fb, vb);
+    }
+  };
+
+  // window rows [j_begin, min(j_end, 128))
+  const int64_t jw = j_end < kWindow ? j_end : kWindow;
+  if (j_begin < jw) {
+    auto win_row = [&](int64_t j) -> const uint8_t* {
+      return resolve_row(a, unit, b, t, j, nvis, a.win_rb, a.ent_rb).p;
+    };
+    const uint8_t* win0 = (const uint8_t*)a.win + (size_t)b * (size_t)a.win_rows * a.win_rb;
+    run(std::integral_constant<int, WF>{}, j_begin, jw, win_row, win0);
+  }
+  // entry rows [max(j_begin, 128), j_end)
+  const int64_t je = j_begin > kWindow ? j_begin : kWindow;
+  if (je < j_end && a.Nmax > 0) {
+    const uint8_t* ebase = (const uint8_t*)a.entries + (size_t)b * (size_t)a.Nmax * a.ent_rb;
+    auto ent_row = [&](int64_t j) -> const uint8_t* {
+      const int64_t e = j - kWindow;
+      return e < nvis ? ebase + (size_t)e * a.ent_rb : nullptr;
+    };
+    run(std::integral_constant<int, EF>{}, je, j_end, ent_row, ebase);
+  }
+
+  const int G = a.H / 16;
+  if (w < HT && lane < 16) {
+    Partial* P = part + (unit * G + w) * (int64_t)nchunks + chunk;
+    P->m[lane] = sm;
+    P->l[lane] = sl;
+  }
+#pragma unroll
+  for (int ht = 0; ht < HT; ++ht) {
+    Partial* P = part + (unit * G + ht) * (int64_t)nchunks + chunk;
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        P->o[(4 * kq + r) * kHeadDim + 128 * w + 16 * dt + r16] = o[ht][dt][r];
+  }
+}
+
 // Work-group -> (chunk, unit, head group).  Work-groups are handed to the 8
 // XCDs round-robin by linear id, so the head groups of one (chunk, unit) are
 // given ids 8 apart: they run on the same XCD at about the same time and
@@ -366,39 +637,6 @@ __global__ void __launch_bounds__(kAttnThreads) attn_mfma_kernel(AttnArgs a, int
   const int rr = rope_row(a, t);
   const float zscale = a.scale * kLog2e;
 
-  // query slice: head 16 hg + r16, dims 128 w + 32 s + 8 kq .. +8, rotated
-  uint4 qa[4];
-  {
-    const int head = 16 * hg + r16;
-    const uint16_t* qp = (const uint16_t*)a.q + (unit * a.H + head) * (int64_t)kHeadDim;
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      const int d0 = 128 * w + 32 * s + 8 * kq;
-      uint4 raw = *(const uint4*)(qp + d0);
-      if (d0 >= kHeadDim - kRopeDims) {
-        float v[8];
-        const uint32_t u[4] = {raw.x, raw.y, raw.z, raw.w};
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          v[2 * j] = __uint_as_float(u[j] << 16);
-          v[2 * j + 1] = __uint_as_float(u[j] & 0xffff0000u);
-        }
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int k = (d0 - (kHeadDim - kRopeDims)) / 2 + j;
-          const float c = a.rope_cos[(int64_t)rr * 32 + k];
-          const float sn = a.rope_sin[(int64_t)rr * 32 + k];
-          const float x = v[2 * j], y = v[2 * j + 1];
-          v[2 * j] = x * c - y * sn;
-          v[2 * j + 1] = x * sn + y * c;
-        }
-        raw = make_uint4(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]),
-                         pack_bf16x2(v[4], v[5]), pack_bf16x2(v[6], v[7]));
-      }
-      qa[s] = raw;
-    }
-  }
-
   // top-k ids of this chunk, fetched once: lane holds rows j_begin + 16 i + r16
   int32_t ids[kMaxIdsPerLane];
   if (!a.dense) {
@@ -408,6 +646,11 @@ __global__ void __launch_bounds__(kAttnThreads) attn_mfma_kernel(AttnArgs a, int
       ids[i] = (jj >= kWindow && jj < j_end) ? a.topk_idx[unit * a.topk + (jj - kWindow)] : -1;
     }
   }
+
+  // query slice: head 16 hg + r16, dims 128 w + 32 s + 8 kq .. +8, rotated
+  uint4 qa1[1][4];
+  load_q_frags<1>(a, unit, 16 * hg, w, r16, kq, rr, qa1);
+  const uint4 qa[4] = {qa1[0][0], qa1[0][1], qa1[0][2], qa1[0][3]};
 
   SoftmaxState st;
   st.m = -INFINITY;
@@ -632,7 +875,15 @@ __global__ void __launch_bounds__(kAttnThreads) attn_f32_kernel(AttnArgs a) {
 
 }  // namespace
 
-int attn_chunk_rows(const AttnArgs& a) { return a.dense ? kChunkHca : kChunkCsa; }
+// Dense lists with at most 64 heads use the all-heads kernel (and always its
+// merge); other lists the 16-head-group kernel.
+static bool attn_all_heads(const AttnArgs& a) {
+  return a.dense && a.H <= 64 && a.q_fmt != CSA_F32;
+}
+
+int attn_chunk_rows(const AttnArgs& a) {
+  return attn_all_heads(a) ? kChunkDense : (a.dense ? kChunkHca : kChunkCsa);
+}
 
 int64_t attn_list_len(const AttnArgs& a) {
   return kWindow + (a.dense ? a.Nmax : (int64_t)a.topk);
@@ -647,7 +898,7 @@ static int attn_nchunks(const AttnArgs& a) {
 size_t attn_ws_bytes(const AttnArgs& a) {
   if (a.q_fmt == CSA_F32) return 0;
   int nc = attn_nchunks(a);
-  if (nc <= 1) return 0;
+  if (nc <= 1 && !attn_all_heads(a)) return 0;
   return (size_t)a.B * a.Q * (a.H / 16) * nc * sizeof(Partial);
 }
 
@@ -661,6 +912,32 @@ static void launch_mfma_w(const AttnArgs& a, int nc, int64_t nu, dim3 grid, Part
     hipLaunchKernelGGL((attn_mfma_kernel<WF, CSA_FP8_MX32>), grid, dim3(kAttnThreads), 0, s, a, cr, nc, nu, part);
   else
     hipLaunchKernelGGL((attn_mfma_kernel<WF, CSA_FP4_E4M3_16>), grid, dim3(kAttnThreads), 0, s, a, cr, nc, nu, part);
+}
+
+template <int WF, int EF>
+static void launch_all_heads_e(const AttnArgs& a, int nc, int64_t nu, Partial* part,
+                               hipStream_t s) {
+  const dim3 grid((unsigned)(nc * nu));
+  switch (a.H / 16) {
+    case 1: hipLaunchKernelGGL((attn_dense_all_kernel<WF, EF, 1>), grid, dim3(kAttnThreads), 0, s, a, nc, nu, part); break;
+    case 2: hipLaunchKernelGGL((attn_dense_all_kernel<WF, EF, 2>), grid, dim3(kAttnThreads), 0, s, a, nc, nu, part); break;
+    case 3: hipLaunchKernelGGL((attn_dense_all_kernel<WF, EF, 3>), grid, dim3(kAttnThreads), 0, s, a, nc, nu, part); break;
+    default: hipLaunchKernelGGL((attn_dense_all_kernel<WF, EF, 4>), grid, dim3(kAttnThreads), 0, s, a, nc, nu, part); break;
+  }
+}
+
+template <int WF>
+static void launch_all_heads_w(const AttnArgs& a, int nc, int64_t nu, Partial* part,
+                               hipStream_t s) {
+  if (a.ent_fmt == CSA_BF16) launch_all_heads_e<WF, CSA_BF16>(a, nc, nu, part, s);
+  else if (a.ent_fmt == CSA_FP8_MX32) launch_all_heads_e<WF, CSA_FP8_MX32>(a, nc, nu, part, s);
+  else launch_all_heads_e<WF, CSA_FP4_E4M3_16>(a, nc, nu, part, s);
+}
+
+static void launch_all_heads(const AttnArgs& a, int nc, int64_t nu, Partial* part, hipStream_t s) {
+  if (a.win_fmt == CSA_BF16) launch_all_heads_w<CSA_BF16>(a, nc, nu, part, s);
+  else if (a.win_fmt == CSA_FP8_MX32) launch_all_heads_w<CSA_FP8_MX32>(a, nc, nu, part, s);
+  else launch_all_heads_w<CSA_FP4_E4M3_16>(a, nc, nu, part, s);
 }
 
 static void launch_mfma(const AttnArgs& a, int nc, int64_t nu, Partial* part, hipStream_t s) {
@@ -691,8 +968,10 @@ hipError_t launch_attention(const AttnArgs& a0, void* ws, hipStream_t s) {
       hipLaunchKernelGGL(attn_f32_kernel, dim3(a.H, nu), dim3(kAttnThreads), 0, s, a);
       continue;
     }
-    launch_mfma(a, nc, nu, (Partial*)ws, s);
-    if (nc > 1)
+    const bool all_heads = attn_all_heads(a);
+    if (all_heads) launch_all_heads(a, nc, nu, (Partial*)ws, s);
+    else launch_mfma(a, nc, nu, (Partial*)ws, s);
+    if (nc > 1 || all_heads)
       hipLaunchKernelGGL(attn_merge_kernel, dim3((a.H / 16) * (kHeadDim / 64), nu),
                          dim3(kAttnThreads), 0, s, a, nc,
                          (const Partial*)ws);
