@@ -163,6 +163,19 @@ size_t csa_compress_workspace_size(const csa_compress_args* a);
 csa_status csa_compress(const csa_compress_args* a, void* ws, size_t ws_bytes,
                         csa_stream_t stream);
 
+/* Several compressors in one call (the same section: a CSA layer runs its
+ * 512-wide main-KV compressor and its 128-wide index-key compressor on the
+ * same token).  The result equals calling csa_compress on a[0], ..., a[n-1]
+ * in order; the calls must not share state or entries buffers.  When every
+ * call is single-token (T == 1) with bf16 x and weights, dim % 256 == 0 and
+ * the same B, their projections run as one launch and their emits as another.
+ * n in [1, 4].  Workspace: csa_compress_many_workspace_size(a, n) bytes
+ * (16-byte aligned); errors as for csa_compress, reported for the first
+ * failing call before anything is enqueued.                             */
+size_t csa_compress_many_workspace_size(const csa_compress_args* a, int n);
+csa_status csa_compress_many(const csa_compress_args* a, int n, void* ws, size_t ws_bytes,
+                             csa_stream_t stream);
+
 /* ------------------------------------------------------------------------ indexer + top-k
  * "DeepSeek-V4 deep dive" section 5.2:  for query (b, q) at position
  * pos[b][q] the visible blocks are s < n_vis = min(floor((pos+1)/ratio), Nmax);

@@ -55,6 +55,8 @@ _SIGS = {
     "kv_dequantize": (_I, [_VP, _I, _VP, _I, _I64, _I, _VP]),
     "csa_compress_workspace_size": (_SZ, [ctypes.POINTER(CompressArgs)]),
     "csa_compress": (_I, [ctypes.POINTER(CompressArgs), _VP, _SZ, _VP]),
+    "csa_compress_many_workspace_size": (_SZ, [ctypes.POINTER(CompressArgs), _I]),
+    "csa_compress_many": (_I, [ctypes.POINTER(CompressArgs), _I, _VP, _SZ, _VP]),
     "csa_index_topk_workspace_size": (_SZ, [_I, _I, _I64, _I]),
     "csa_index_topk": (_I, [_VP, _I, _VP, _VP, _I, _VP, _I, _I, _I, _I, _I64, _I, _VP, _VP, _VP,
                             _SZ, _VP]),
@@ -154,6 +156,25 @@ def make_compress_args(*, B, T, dim, ratio, head_dim, rotate, x, x_fmt, w_kv, w_
 
 def csa_compress_workspace_size(args):
     return int(lib().csa_compress_workspace_size(ctypes.byref(args)))
+
+
+def _args_array(args_list):
+    arr = (CompressArgs * len(args_list))()
+    for i, a in enumerate(args_list):
+        arr[i] = a
+    return arr
+
+
+def csa_compress_many_workspace_size(args_list):
+    arr = _args_array(args_list)
+    return int(lib().csa_compress_many_workspace_size(arr, len(args_list)))
+
+
+def csa_compress_many(args_list, ws, stream=None):
+    arr = _args_array(args_list)
+    _check(lib().csa_compress_many(arr, len(args_list), _ptr(ws),
+                                   ws.numel() if ws is not None else 0, _stream(stream)),
+           "csa_compress_many")
 
 
 def csa_compress(args, ws, stream=None):

@@ -180,6 +180,27 @@ csa_status csa_compress(const csa_compress_args* a, void* ws, size_t ws_bytes,
   return launched(launch_compress(a, ws, (hipStream_t)stream), "csa_compress");
 }
 
+size_t csa_compress_many_workspace_size(const csa_compress_args* a, int n) {
+  if (a == nullptr || n < 1 || n > 4) return 0;
+  for (int i = 0; i < n; ++i)
+    if (check_compress(&a[i]) != CSA_OK) return 0;
+  return compress_many_ws_bytes(a, n);
+}
+
+csa_status csa_compress_many(const csa_compress_args* a, int n, void* ws, size_t ws_bytes,
+                             csa_stream_t stream) {
+  REQUIRE(a != nullptr, CSA_EINVAL, "args must not be null");
+  REQUIRE(n >= 1 && n <= 4, CSA_EUNSUPPORTED, "n must be in [1, 4]");
+  for (int i = 0; i < n; ++i) {
+    csa_status st = check_compress(&a[i]);
+    if (st != CSA_OK) return st;
+  }
+  size_t need = compress_many_ws_bytes(a, n);
+  REQUIRE(need == 0 || (ws != nullptr && aligned16(ws) && ws_bytes >= need), CSA_EWORKSPACE,
+          "workspace of %zu bytes needed (got %zu)", need, ws_bytes);
+  return launched(launch_compress_many(a, n, ws, (hipStream_t)stream), "csa_compress_many");
+}
+
 // ---------------------------------------------------------------- top-k
 size_t csa_topk_workspace_size(int64_t R, int64_t ld, int topk) {
   (void)ld;

@@ -199,17 +199,36 @@ __global__ void __launch_bounds__(kProjThreads) proj_mfma_kernel(const uint16_t*
 // partial products to part[ks][m][n].  The emit kernel adds the eight slices
 // in order, the same summation as the one-work-group projection above.
 constexpr int kKSlices = 8;
+constexpr int kMaxJobs = 4;  // compressors fused into one launch
+
+struct ProjJob {
+  const uint16_t* x;    // [M][K] bf16
+  const uint16_t* wkv;  // [CD][K]
+  const uint16_t* wg;   // [CD][K]
+  int K, CD;
+  int blk0;             // first column block of this job in the launch
+  float* part;          // [kKSlices][M][2 CD]
+};
+struct ProjJobs {
+  ProjJob j[kMaxJobs];
+  int n;
+};
 
 template <int MT>
-__global__ void __launch_bounds__(64) proj_slice_kernel(const uint16_t* __restrict__ x,
-                                                        const uint16_t* __restrict__ wkv,
-                                                        const uint16_t* __restrict__ wg, int M,
-                                                        int K, int CD, float* __restrict__ part) {
+__global__ void __launch_bounds__(64) proj_slice_kernel(ProjJobs jobs, int M) {
+  int jb = 0;
+#pragma unroll
+  for (int q = 1; q < kMaxJobs; ++q)
+    if (q < jobs.n && (int)blockIdx.x >= jobs.j[q].blk0) jb = q;
+  const ProjJob& J = jobs.j[jb];
+  const uint16_t* __restrict__ x = J.x;
+  const int K = J.K, CD = J.CD;
   const int lane = threadIdx.x;
   const int r16 = lane & 15, kq = lane >> 4;
   const int N = 2 * CD;
-  const int n = blockIdx.x * 16 + r16;
-  const uint16_t* wrow = n < CD ? wkv + (int64_t)n * K : wg + (int64_t)(n - CD) * K;
+  const int cb = (int)blockIdx.x - J.blk0;
+  const int n = cb * 16 + r16;
+  const uint16_t* wrow = n < CD ? J.wkv + (int64_t)n * K : J.wg + (int64_t)(n - CD) * K;
   constexpr int kB = MT <= 2 ? 16 : 8;
   const int nks = K / 256;
   const int kb = blockIdx.y * (K / kKSlices);
@@ -240,7 +259,7 @@ __global__ void __launch_bounds__(64) proj_slice_kernel(const uint16_t* __restri
       }
     }
   }
-  float* dst = part + (int64_t)blockIdx.y * M * N + blockIdx.x * 16 + (lane & 15);
+  float* dst = J.part + (int64_t)blockIdx.y * M * N + cb * 16 + (lane & 15);
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
@@ -605,10 +624,15 @@ __global__ void __launch_bounds__(kThreads) state_kernel(CompArgs a) {
 // the token completes a block, pool the block (the new token's values from
 // registers, the others from the state), shift the current slots into the
 // previous ones (overlap) and finish the entry.
-__global__ void __launch_bounds__(kThreads) emit_t1_kernel(CompArgs a) {
+struct CompJobs {
+  CompArgs c[kMaxJobs];
+};
+
+__global__ void __launch_bounds__(kThreads) emit_t1_kernel(CompJobs jobs) {
   __shared__ float y[512];
   __shared__ float z[512];
   __shared__ float red[4];
+  const CompArgs& a = jobs.c[blockIdx.y];
   const int64_t b = blockIdx.x;
   const int64_t p0 = a.start_pos[b];
   const int r = a.ratio;
@@ -732,7 +756,7 @@ size_t compress_ws_bytes(const csa_compress_args* a) {
   return align_up((size_t)a->B * a->T * 2 * CD * sizeof(float), 256);
 }
 
-hipError_t launch_compress(const csa_compress_args* in, void* ws, hipStream_t s) {
+static CompArgs comp_args(const csa_compress_args* in, float* P) {
   CompArgs a;
   a.B = in->B;
   a.T = in->T;
@@ -754,22 +778,74 @@ hipError_t launch_compress(const csa_compress_args* in, void* ws, hipStream_t s)
   a.entries = (uint8_t*)in->entries;
   a.entries_cap = in->entries_cap;
   a.entry_rb = kv_row_bytes(in->entry_fmt, in->head_dim);
-  float* P = (float*)ws;
   a.P = P;
+  return a;
+}
+
+// Single-token bf16 calls with a common batch run as one projection launch
+// and one emit launch.
+static bool fusable(const csa_compress_args* in, int n) {
+  if (n < 1 || n > kMaxJobs) return false;
+  for (int i = 0; i < n; ++i)
+    if (in[i].T != 1 || !use_mfma_proj(&in[i]) || in[i].B != in[0].B) return false;
+  return true;
+}
+
+static hipError_t launch_fused_t1(const csa_compress_args* in, int n, void* ws, hipStream_t s) {
+  ProjJobs pj;
+  CompJobs cj;
+  char* p = (char*)ws;
+  int blocks = 0;
+  for (int i = 0; i < n; ++i) {
+    const int CD = (in[i].ratio == 4 ? 2 : 1) * in[i].head_dim;
+    pj.j[i] = ProjJob{(const uint16_t*)in[i].x, (const uint16_t*)in[i].w_kv,
+                      (const uint16_t*)in[i].w_gate, in[i].dim, CD, blocks, (float*)p};
+    cj.c[i] = comp_args(&in[i], (float*)p);
+    blocks += 2 * CD / 16;
+    p += compress_ws_bytes(&in[i]);
+  }
+  for (int i = n; i < kMaxJobs; ++i) {
+    pj.j[i] = pj.j[0];
+    cj.c[i] = cj.c[0];
+  }
+  pj.n = n;
+  const int M = in[0].B;
+  const int mt = (M + 15) / 16;
+  const dim3 grid(blocks, kKSlices);
+  if (mt == 1) hipLaunchKernelGGL(proj_slice_kernel<1>, grid, dim3(64), 0, s, pj, M);
+  else if (mt == 2) hipLaunchKernelGGL(proj_slice_kernel<2>, grid, dim3(64), 0, s, pj, M);
+  else if (mt == 3) hipLaunchKernelGGL(proj_slice_kernel<3>, grid, dim3(64), 0, s, pj, M);
+  else hipLaunchKernelGGL(proj_slice_kernel<4>, grid, dim3(64), 0, s, pj, M);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(emit_t1_kernel, dim3(M, n), dim3(kThreads), 0, s, cj);
+  return hipGetLastError();
+}
+
+size_t compress_many_ws_bytes(const csa_compress_args* in, int n) {
+  size_t b = 0;
+  for (int i = 0; i < n; ++i) b += compress_ws_bytes(&in[i]);
+  return b;
+}
+
+hipError_t launch_compress_many(const csa_compress_args* in, int n, void* ws, hipStream_t s) {
+  if (fusable(in, n)) return launch_fused_t1(in, n, ws, s);
+  char* p = (char*)ws;
+  for (int i = 0; i < n; ++i) {
+    hipError_t e = launch_compress(&in[i], p, s);
+    if (e != hipSuccess) return e;
+    p += compress_ws_bytes(&in[i]);
+  }
+  return hipSuccess;
+}
+
+hipError_t launch_compress(const csa_compress_args* in, void* ws, hipStream_t s) {
+  if (in->T == 1 && use_mfma_proj(in)) return launch_fused_t1(in, 1, ws, s);
+  CompArgs a = comp_args(in, (float*)ws);
+  float* P = (float*)ws;
   const int64_t M = (int64_t)in->B * in->T;
   const int N = 2 * a.CD;
-  const bool direct = in->T == 1 && use_mfma_proj(in);
-  if (direct) {
-    const int mt = (int)((M + 15) / 16);
-    const dim3 grid(N / 16, kKSlices);
-    const uint16_t* xp = (const uint16_t*)in->x;
-    const uint16_t* wk = (const uint16_t*)in->w_kv;
-    const uint16_t* wgp = (const uint16_t*)in->w_gate;
-    if (mt == 1) hipLaunchKernelGGL(proj_slice_kernel<1>, grid, dim3(64), 0, s, xp, wk, wgp, (int)M, in->dim, a.CD, P);
-    else if (mt == 2) hipLaunchKernelGGL(proj_slice_kernel<2>, grid, dim3(64), 0, s, xp, wk, wgp, (int)M, in->dim, a.CD, P);
-    else if (mt == 3) hipLaunchKernelGGL(proj_slice_kernel<3>, grid, dim3(64), 0, s, xp, wk, wgp, (int)M, in->dim, a.CD, P);
-    else hipLaunchKernelGGL(proj_slice_kernel<4>, grid, dim3(64), 0, s, xp, wk, wgp, (int)M, in->dim, a.CD, P);
-  } else if (use_mfma_proj(in)) {
+  if (use_mfma_proj(in)) {
     const int mt = (int)((M + 15) / 16);
     ProjOut po{P, 0, in->start_pos, in->ape, in->ratio, a.coff, in->kv_state, in->score_state};
     dim3 grid(N / 16);
@@ -794,10 +870,6 @@ hipError_t launch_compress(const csa_compress_args* in, void* ws, hipStream_t s)
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  if (direct) {
-    hipLaunchKernelGGL(emit_t1_kernel, dim3(in->B), dim3(kThreads), 0, s, a);
-    return hipGetLastError();
-  }
   const int max_blocks = in->T / in->ratio + 1;
   hipLaunchKernelGGL(emit_kernel, dim3(max_blocks, in->B), dim3(kThreads), 0, s, a);
   e = hipGetLastError();

@@ -72,5 +72,7 @@ hipError_t launch_attention(const AttnArgs& a, void* ws, hipStream_t s);
 
 size_t compress_ws_bytes(const csa_compress_args* a);
 hipError_t launch_compress(const csa_compress_args* a, void* ws, hipStream_t s);
+size_t compress_many_ws_bytes(const csa_compress_args* a, int n);
+hipError_t launch_compress_many(const csa_compress_args* a, int n, void* ws, hipStream_t s);
 
 }  // namespace csa

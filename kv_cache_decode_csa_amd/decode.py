@@ -3,18 +3,12 @@
 This module owns device buffers (torch tensors) and calls the library's entry
 points in order; it computes nothing itself.  A CSA step at position t is:
 
-  csa_compress (main KV, ratio 4, 512 wide)        -> maybe emits entry t//4
-  csa_compress (index keys, ratio 4, 128 wide, rotated)
+  csa_compress_many (main KV: ratio 4, 512 wide;   -> maybe emits entry t//4
+                     index keys: ratio 4, 128 wide, rotated)
   csa_index_topk                                   -> top-k entry ids
   csa_sparse_attn_decode                           -> [B, H, 512]
 
 and an HCA step is csa_compress (ratio 128) followed by hca_attn_decode.
-
-In `step()` the main-KV compressor of a CSA layer runs on a second stream (of
-default priority): only the attention reads what it writes, so it overlaps
-the index compressor, the scoring and the selection, and the attention waits
-for it with an event.  `phases()` runs the same calls one after another on
-the current stream, for per-call timing.
 """
 
 import torch
@@ -129,7 +123,7 @@ class CsaDecodeLayer:
             for cm, ci in self.comp:
                 cm(tail, st)
                 ci(tail, st)
-        self.side = torch.cuda.Stream(device=device)
+        self.ws_comp = [None] * copies
         self.step_no = 0
 
     def phases(self):
@@ -141,11 +135,12 @@ class CsaDecodeLayer:
         win_fmt, ent_fmt, key_fmt = w.win_fmt, w.ent_fmt, w.key_fmt
         B, N = w.B, w.n_entries
 
-        def compress_main():
-            cm(self.x, self.start)
-
-        def compress_index():
-            ci(self.x, self.start)
+        def compress():
+            args = [cm.args(self.x, self.start), ci.args(self.x, self.start)]
+            need = _lib.csa_compress_many_workspace_size(args)
+            if self.ws_comp[c] is None or self.ws_comp[c].numel() < need:
+                self.ws_comp[c] = _lib.workspace(need)
+            _lib.csa_compress_many(args, self.ws_comp[c])
 
         def index_topk():
             _lib.csa_index_topk(self.qi, w.q_fmt, self.wi, keys, key_fmt, self.pos, w.ratio, B, 1,
@@ -157,23 +152,12 @@ class CsaDecodeLayer:
                                         1, w.H, self.sink, 512 ** -0.5, self.rope[0],
                                         self.rope[1], self.out, w.q_fmt, self.ws_att)
 
-        return [("csa_compress_main", compress_main), ("csa_compress_index", compress_index),
-                ("csa_index_topk", index_topk), ("csa_sparse_attn_decode", sparse_attn)]
+        return [("csa_compress", compress), ("csa_index_topk", index_topk),
+                ("csa_sparse_attn_decode", sparse_attn)]
 
     def step(self):
-        ph = dict(self.phases())
-        main = torch.cuda.current_stream()
-        ready = torch.cuda.Event()
-        ready.record(main)
-        with torch.cuda.stream(self.side):
-            self.side.wait_event(ready)
-            ph["csa_compress_main"]()
-            done = torch.cuda.Event()
-            done.record(self.side)
-        ph["csa_compress_index"]()
-        ph["csa_index_topk"]()
-        main.wait_event(done)
-        ph["csa_sparse_attn_decode"]()
+        for _, f in self.phases():
+            f()
         self.step_no += 1
 
 
@@ -223,7 +207,7 @@ class HcaDecodeLayer:
                                  self.sink, 512 ** -0.5, self.rope[0], self.rope[1], self.out,
                                  w.q_fmt, self.ws_att)
 
-        return [("csa_compress_main", compress_main), ("hca_attn_decode", hca_attn)]
+        return [("csa_compress", compress_main), ("hca_attn_decode", hca_attn)]
 
     def step(self):
         for _, f in self.phases():

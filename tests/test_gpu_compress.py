@@ -154,3 +154,39 @@ def test_hca_chunked_calls(tables):
     for i, v in ref.items():
         close_f32(got[0, i], v, tol=2e-5)
     close_f32(to_np(g.kv)[0], st[0], tol=2e-5)
+
+
+def test_compress_many_equals_separate_calls(tables):
+    """csa_compress_many (the main-KV and index-key compressors of a layer on
+    the same token, fused) leaves exactly the entries and state that separate
+    csa_compress calls leave, over steps that complete blocks."""
+    B, dim, ratio = 3, 512, 4
+    rng = np.random.default_rng(11)
+    specs = [(512, 0, "fp8_mx32"), (128, 1, "fp8_mx32")]
+    ws_ = [tuple(synth.bf16_round(w) for w in weights(rng, dim, d, ratio)) for d, _, _ in specs]
+    x = synth.bf16_round(rng.standard_normal((B, 12, dim)).astype(np.float32))
+    start = np.array([40, 41, 42], np.int32)
+    sides = []
+    for _ in range(2):
+        sides.append([GpuCompressor(B, dim, ratio, d, rot, w[0], w[1], w[2], "bf16", fmt, 32, tables)
+                      for (d, rot, fmt), w in zip(specs, ws_)])
+    fused, sep = sides
+    for s in range(9):
+        pos = start + s
+        xs = x[:, s:s + 1]
+        for g in sep:
+            g(xs, pos)
+        sp = i32(pos)
+        xd = bf16(xs)
+        args = [_lib.make_compress_args(
+            B=B, T=1, dim=dim, ratio=ratio, head_dim=g.d, rotate=g.rotate, x=xd, x_fmt="bf16",
+            w_kv=g.wkv, w_gate=g.wg, w_fmt="bf16", ape=g.ape, norm_w=g.norm, eps=1e-6,
+            rope_cos=g.cos, rope_sin=g.sin, start_pos=sp, kv_state=g.kv, score_state=g.sc,
+            entries=g.entries, entry_fmt=g.entry_fmt, entries_cap=g.cap) for g in fused]
+        ws = _lib.workspace(_lib.csa_compress_many_workspace_size(args))
+        _lib.csa_compress_many(args, ws)
+        torch.cuda.synchronize()
+    for gf, gs in zip(fused, sep):
+        assert torch.equal(gf.entries, gs.entries)
+        assert torch.equal(gf.kv, gs.kv)
+        assert torch.equal(gf.sc, gs.sc)
