@@ -740,6 +740,110 @@ __global__ void __launch_bounds__(kThreads) emit_t1_kernel(CompJobs jobs) {
   finish_block(a, b, i, y, z, red, sq);
 }
 
+// ---- single-token calls of the 128-token (no overlap) compressor
+// Pass 1, work-group (sequence b, 64-channel slice): the new token's slot from
+// the projection slices (score plus slot bias); if the token completes a
+// block, 4 threads per channel pool 32 slots each -- all of their loads in
+// flight together -- and the 4 partial softmax sums are merged in order.
+// Writes the pooled channels and the slice's sum of squares.
+constexpr int kPoolChannels = 64;
+
+__global__ void __launch_bounds__(kThreads) pool128_t1_kernel(CompJobs jobs, float* ybuf,
+                                                                float* sqbuf) {
+  __shared__ float pm[4][kPoolChannels], pl[4][kPoolChannels], pa[4][kPoolChannels];
+  const CompArgs& a = jobs.c[0];
+  const int64_t b = blockIdx.x;
+  const int slice = blockIdx.y;
+  const int64_t p0 = a.start_pos[b];
+  if (p0 < 0) return;
+  const int r = a.ratio;                    // 128, one slot per token
+  const int ns = (int)(p0 % r);
+  const bool done = ns == r - 1;
+  const int tid = threadIdx.x;
+  const int cl = tid & (kPoolChannels - 1), g = tid >> 6;
+  const int c = slice * kPoolChannels + cl;
+  const int N = 2 * a.CD;
+  const int64_t sb = b * (int64_t)r * a.CD;
+  const bool own = (ns >> 5) == g;          // this slot group holds the new token
+  float nv = 0.f, nsc = 0.f;
+  if (own) {
+    const float* pp = a.P + b * (int64_t)N + c;
+    nv = pp[0];
+    nsc = pp[a.CD];
+#pragma unroll
+    for (int ks = 1; ks < kKSlices; ++ks) {
+      nv += pp[(int64_t)ks * a.B * N];
+      nsc += pp[(int64_t)ks * a.B * N + a.CD];
+    }
+    nsc += a.ape[(int64_t)ns * a.CD + c];
+    a.kv_state[sb + (int64_t)ns * a.CD + c] = nv;
+    a.score_state[sb + (int64_t)ns * a.CD + c] = nsc;
+  }
+  if (!done) return;
+  float vv[32], ss[32];
+#pragma unroll
+  for (int j = 0; j < 32; ++j) {
+    const int sl = 32 * g + j;
+    const int64_t si = sb + (int64_t)sl * a.CD + c;
+    vv[j] = sl == ns ? nv : a.kv_state[si];
+    ss[j] = sl == ns ? nsc : a.score_state[si];
+  }
+  float m = -INFINITY, l = 0.f, acc = 0.f;
+#pragma unroll
+  for (int j = 0; j < 32; ++j) {
+    if (ss[j] == -INFINITY) continue;
+    const float mn = fmaxf(m, ss[j]);
+    const float scl = expf(m - mn);
+    const float e = expf(ss[j] - mn);
+    l = l * scl + e;
+    acc = acc * scl + e * vv[j];
+    m = mn;
+  }
+  pm[g][cl] = m;
+  pl[g][cl] = l;
+  pa[g][cl] = acc;
+  __syncthreads();
+  if (g != 0) return;
+  float M = -INFINITY;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) M = fmaxf(M, pm[q][cl]);
+  float L = 0.f, A = 0.f;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    if (pm[q][cl] == -INFINITY) continue;
+    const float wq = expf(pm[q][cl] - M);
+    L += pl[q][cl] * wq;
+    A += pa[q][cl] * wq;
+  }
+  const float C = A / L;
+  ybuf[b * (int64_t)a.d + c] = C;
+  const float sq = wave_sum(C * C);  // wave 0 holds the slice's 64 channels
+  if (tid == 0) sqbuf[b * (a.d / kPoolChannels) + slice] = sq;
+}
+
+// Pass 2, one work-group per sequence whose block completed: RMSNorm -> RoPE
+// -> storage rounding of the pooled row (slice sums of squares added in order).
+__global__ void __launch_bounds__(kThreads) finish128_t1_kernel(CompJobs jobs,
+                                                                  const float* ybuf,
+                                                                  const float* sqbuf) {
+  __shared__ float y[512];
+  __shared__ float z[512];
+  __shared__ float red[4];
+  const CompArgs& a = jobs.c[0];
+  const int64_t b = blockIdx.x;
+  const int64_t p0 = a.start_pos[b];
+  if (p0 < 0 || (p0 + 1) % a.ratio != 0) return;
+  const int tid = threadIdx.x;
+  for (int c = tid; c < a.d; c += kThreads) y[c] = ybuf[b * (int64_t)a.d + c];
+  float sq = 0.f;
+  if (tid == 0) {
+    const int ns = a.d / kPoolChannels;
+    for (int q = 0; q < ns; ++q) sq += sqbuf[b * ns + q];
+  }
+  __syncthreads();
+  finish_block(a, b, p0 / a.ratio, y, z, red, sq);
+}
+
 }  // namespace
 
 // The MFMA projection serves bf16 calls with B*T <= 64 and dim % 256 == 0.
@@ -751,8 +855,13 @@ static bool use_mfma_proj(const csa_compress_args* a) {
 size_t compress_ws_bytes(const csa_compress_args* a) {
   const int coff = a->ratio == 4 ? 2 : 1;
   const int CD = coff * a->head_dim;
-  if (a->T == 1 && use_mfma_proj(a))  // per-slice partial products
-    return align_up((size_t)kKSlices * a->B * 2 * CD * sizeof(float), 256);
+  if (a->T == 1 && use_mfma_proj(a)) {  // per-slice partial products
+    size_t b = align_up((size_t)kKSlices * a->B * 2 * CD * sizeof(float), 256);
+    if (a->ratio == 128)  // pooled rows and slice sums of squares
+      b += align_up((size_t)a->B * a->head_dim * sizeof(float), 256) +
+           align_up((size_t)a->B * (a->head_dim / 64) * sizeof(float), 256);
+    return b;
+  }
   return align_up((size_t)a->B * a->T * 2 * CD * sizeof(float), 256);
 }
 
@@ -787,7 +896,9 @@ static CompArgs comp_args(const csa_compress_args* in, float* P) {
 static bool fusable(const csa_compress_args* in, int n) {
   if (n < 1 || n > kMaxJobs) return false;
   for (int i = 0; i < n; ++i)
-    if (in[i].T != 1 || !use_mfma_proj(&in[i]) || in[i].B != in[0].B) return false;
+    if (in[i].T != 1 || !use_mfma_proj(&in[i]) || in[i].B != in[0].B ||
+        (n > 1 && in[i].ratio == 128))
+      return false;
   return true;
 }
 
@@ -818,6 +929,18 @@ static hipError_t launch_fused_t1(const csa_compress_args* in, int n, void* ws, 
   else hipLaunchKernelGGL(proj_slice_kernel<4>, grid, dim3(64), 0, s, pj, M);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
+  if (n == 1 && in[0].ratio == 128) {  // pooling over 128 slots: split by channels
+    const int CD = in[0].head_dim;
+    float* ybuf = (float*)((char*)ws + align_up((size_t)kKSlices * M * 2 * CD * sizeof(float), 256));
+    float* sqbuf = (float*)((char*)ybuf + align_up((size_t)M * in[0].head_dim * sizeof(float), 256));
+    hipLaunchKernelGGL(pool128_t1_kernel, dim3(M, in[0].head_dim / kPoolChannels), dim3(kThreads),
+                       0, s, cj, ybuf, sqbuf);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(finish128_t1_kernel, dim3(M), dim3(kThreads), 0, s, cj,
+                       (const float*)ybuf, (const float*)sqbuf);
+    return hipGetLastError();
+  }
   hipLaunchKernelGGL(emit_t1_kernel, dim3(M, n), dim3(kThreads), 0, s, cj);
   return hipGetLastError();
 }

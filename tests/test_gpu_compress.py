@@ -190,3 +190,39 @@ def test_compress_many_equals_separate_calls(tables):
         assert torch.equal(gf.entries, gs.entries)
         assert torch.equal(gf.kv, gs.kv)
         assert torch.equal(gf.sc, gs.sc)
+
+
+@pytest.mark.parametrize("entry_fmt", ["bf16", "fp8_mx32"])
+def test_hca_decode_steps_bf16(tables, entry_fmt):
+    """Single-token calls of the 128-token compressor across block boundaries
+    (slot writes without emission, then the emitting token), each sequence at
+    its own offset, against the oracle's streaming state machine."""
+    B, dim, d, ratio = 2, 256, 512, 128
+    rng = np.random.default_rng(12)
+    wkv, wg, ape = (synth.bf16_round(w) for w in weights(rng, dim, d, ratio))
+    ape = weights(rng, dim, d, ratio)[2]
+    prefix = np.array([120, 250])
+    steps = 12
+    x = synth.bf16_round(rng.standard_normal((B, 270, dim)).astype(np.float32))
+    g = GpuCompressor(B, dim, ratio, d, 0, wkv, wg, ape, "bf16", entry_fmt, 4, tables)
+    for b in range(B):
+        gb = GpuCompressor(1, dim, ratio, d, 0, wkv, wg, ape, "bf16", entry_fmt, 4, tables)
+        gb(x[b:b + 1, :prefix[b]], [0])
+        g.kv[b], g.sc[b], g.entries[b] = gb.kv[0], gb.sc[0], gb.entries[0]
+    for s in range(steps):
+        g(x[np.arange(B), prefix + s][:, None, :], prefix + s)
+    got = g.entry_values()
+    for b in range(B):
+        T = prefix[b] + steps
+        ref, st = compressor.compress_stream(x[b, :T].astype(np.float64), 0, wkv, wg, ape,
+                                             np.ones(d), OM, ratio, d)
+        assert sorted(ref) == list(range(T // ratio))
+        for i, v in ref.items():
+            stored = codec.store(v, entry_fmt)[1]
+            err = np.abs(got[b, i] - stored)
+            assert np.all(err <= step_bound(v, entry_fmt, d)), (b, i, err.max())
+        close_f32(to_np(g.kv)[b], st[0], tol=1e-4)
+        sc = to_np(g.sc)[b]
+        assert np.array_equal(np.isinf(sc), np.isinf(st[1]))
+        fin = np.isfinite(st[1])
+        close_f32(sc[fin], st[1][fin], tol=1e-4)
