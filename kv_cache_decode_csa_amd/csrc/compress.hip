@@ -624,6 +624,114 @@ __global__ void __launch_bounds__(kThreads) state_kernel(CompArgs a) {
 // the token completes a block, pool the block (the new token's values from
 // registers, the others from the state), shift the current slots into the
 // previous ones (overlap) and finish the entry.
+// Single-token emit with overlap (ratio 4, 8 slots).  Everything this thread
+// needs -- the projection slices of the new token, all 4 slot-bias rows and
+// the 8 slots of its channels -- is loaded before the token's position is
+// known, so the whole load phase is one round of memory latency.
+__device__ void emit_t1_overlap(const CompArgs& a, int64_t b, int64_t p0, float* y, float* z,
+                                float* red) {
+  const int r = 4, d = a.d, CD = a.CD, tid = threadIdx.x;
+  const int N = 2 * CD;
+  const int64_t sb = b * (int64_t)(2 * r) * CD;
+  constexpr int kPer = 2;  // channels per thread (d <= 512 = 2 kThreads)
+  float pv[kPer][2][kKSlices], ps[kPer][2][kKSlices];  // slices of v and score, halves 0/1
+  float ap[kPer][2][4];                                 // slot bias rows 0..3
+  float sv[kPer][8], ssc[kPer][8];                      // slots 0..7 at their pooled column
+  float c4v[kPer][4], c4s[kPer][4];                     // slots 4..7 at column c (shift)
+#pragma unroll
+  for (int u = 0; u < kPer; ++u) {
+    const int c = tid + u * kThreads < d ? tid + u * kThreads : d - 1;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const float* pp = a.P + b * (int64_t)N + c + h * d;
+#pragma unroll
+      for (int ks = 0; ks < kKSlices; ++ks) {
+        pv[u][h][ks] = pp[(int64_t)ks * a.B * N];
+        ps[u][h][ks] = pp[(int64_t)ks * a.B * N + CD];
+      }
+#pragma unroll
+      for (int q = 0; q < 4; ++q) ap[u][h][q] = a.ape[(int64_t)q * CD + c + h * d];
+    }
+#pragma unroll
+    for (int sl = 0; sl < 8; ++sl) {
+      const int64_t si = sb + (int64_t)sl * CD + c + (sl >= r ? d : 0);
+      sv[u][sl] = a.kv_state[si];
+      ssc[u][sl] = a.score_state[si];
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      c4v[u][q] = a.kv_state[sb + (int64_t)(r + q) * CD + c];
+      c4s[u][q] = a.score_state[sb + (int64_t)(r + q) * CD + c];
+    }
+  }
+  if (p0 < 0) return;
+  const int q0 = (int)(p0 % r);
+  const int ns = r + q0;  // the new token's slot
+  const bool done = q0 == r - 1;
+  float sq = 0.f;
+#pragma unroll
+  for (int u = 0; u < kPer; ++u) {
+    const int c = tid + u * kThreads;
+    if (c >= d) continue;
+    float nv[2], nsc[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      float vs = pv[u][h][0], ss = ps[u][h][0];
+#pragma unroll
+      for (int ks = 1; ks < kKSlices; ++ks) {
+        vs += pv[u][h][ks];
+        ss += ps[u][h][ks];
+      }
+      float apv = ap[u][h][0];
+#pragma unroll
+      for (int q = 1; q < 4; ++q) apv = q == q0 ? ap[u][h][q] : apv;
+      nv[h] = vs;
+      nsc[h] = ss + apv;
+    }
+    if (!done) {
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        a.kv_state[sb + (int64_t)ns * CD + c + h * d] = nv[h];
+        a.score_state[sb + (int64_t)ns * CD + c + h * d] = nsc[h];
+      }
+      continue;
+    }
+    // the block completes: slot 7 is the new token (column c + d pooled)
+    sv[u][7] = nv[1];
+    ssc[u][7] = nsc[1];
+    c4v[u][3] = nv[0];
+    c4s[u][3] = nsc[0];
+    float m = -INFINITY, l = 0.f, acc = 0.f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      if (ssc[u][j] == -INFINITY) continue;
+      const float mn = fmaxf(m, ssc[u][j]);
+      const float scl = expf(m - mn);
+      const float e = expf(ssc[u][j] - mn);
+      l = l * scl + e;
+      acc = acc * scl + e * sv[u][j];
+      m = mn;
+    }
+    // shift: slots 0..3 <- slots 4..7 (both halves); slot 7 keeps the new token
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      a.kv_state[sb + (int64_t)q * CD + c] = c4v[u][q];
+      a.score_state[sb + (int64_t)q * CD + c] = c4s[u][q];
+      a.kv_state[sb + (int64_t)q * CD + d + c] = sv[u][4 + q];
+      a.score_state[sb + (int64_t)q * CD + d + c] = ssc[u][4 + q];
+    }
+    a.kv_state[sb + (int64_t)ns * CD + c] = nv[0];
+    a.score_state[sb + (int64_t)ns * CD + c] = nsc[0];
+    a.kv_state[sb + (int64_t)ns * CD + d + c] = nv[1];
+    a.score_state[sb + (int64_t)ns * CD + d + c] = nsc[1];
+    const float C = acc / l;
+    y[c] = C;
+    sq = fmaf(C, C, sq);
+  }
+  if (!done) return;
+  finish_block(a, b, p0 / r, y, z, red, sq);
+}
+
 struct CompJobs {
   CompArgs c[kMaxJobs];
 };
@@ -640,6 +748,10 @@ __global__ void __launch_bounds__(kThreads) emit_t1_kernel(CompJobs jobs) {
   const int nslots = a.coff * r;
   const int N = 2 * a.CD;
   const int64_t sb = b * (int64_t)nslots * a.CD;
+  if (a.coff == 2) {  // ratio 4 with overlap: 8 slots
+    emit_t1_overlap(a, b, p0, y, z, red);
+    return;
+  }
   if (p0 < 0) return;
   const int ns = (a.coff == 2 ? r : 0) + (int)(p0 % r);  // the new token's slot
   const bool done = (p0 + 1) % r == 0;
