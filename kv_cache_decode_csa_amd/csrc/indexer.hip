@@ -180,30 +180,50 @@ __global__ void __launch_bounds__(kIdxThreads) index_scores_mfma(
   // read key by key with the index clamped to end - 1.
   const int64_t stride = G * 4 * (int64_t)kKeysPerIter;
   const int64_t k0 = ((int64_t)blockIdx.x * 4 + wave) * kKeysPerIter;
-  auto score_tile = [&](int64_t k, int nt, const KeyRaw& f) __attribute__((always_inline)) {
+  // Scoring is split in two so that the MFMAs of one tile can be issued
+  // before the epilogue of the previous one: tile_mfma forms the 16 heads x 16
+  // keys products of every head tile, tile_epilogue applies ReLU and the head
+  // weights, sums the heads and records the score.
+  auto tile_mfma = [&](const KeyRaw& f, f32x4_t (&acc)[HT]) __attribute__((always_inline)) {
     bf16x8_t kb[4];
 #pragma unroll
     for (int s = 0; s < 4; ++s) kb[s] = key_frag<KFMT>(f, s);
     // the HT head tiles are independent accumulation chains: issue them
     // round-robin so consecutive MFMAs do not wait on each other
-    f32x4_t acc[HT];
 #pragma unroll
     for (int mt = 0; mt < HT; ++mt) acc[mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int s = 0; s < 4; ++s)
 #pragma unroll
       for (int mt = 0; mt < HT; ++mt) acc[mt] = mfma16x16x32(as_bf16x8(qa[mt][s]), kb[s], acc[mt]);
+  };
+  // The sum is formed over 2 ReLU(x) = x + |x| (exact, and an abs is free on
+  // the adder) and halved at the end: scaling by two commutes with every
+  // rounding, so the result equals the plain sum of w_h ReLU(x_h) in the same
+  // order, while a max would need its input canonicalized first.
+  auto tile_epilogue = [&](int64_t k, int nt, const f32x4_t (&acc)[HT]) __attribute__((always_inline)) {
     float p = 0.f;
 #pragma unroll
     for (int mt = 0; mt < HT; ++mt)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) p += wv[mt][r] * fmaxf(acc[mt][r], 0.f);
+      for (int r = 0; r < 4; ++r) p += wv[mt][r] * (acc[mt][r] + fabsf(acc[mt][r]));
     p += shfl_xor_f(p, 16);
     p += shfl_xor_f(p, 32);
+    p *= 0.5f;
     const int64_t key = k + 16 * nt + r16;
     if (kq == 0 && key < end) {
       srow[key] = p;
       atomicAdd(&hist[score_key(p) >> 20], 1u);
+    }
+  };
+  // all tiles of a step, the MFMAs of tile nt + 1 ahead of the epilogue of nt
+  auto score_tiles = [&](int64_t k, const KeyRaw (&f)[kTilesPerIter]) __attribute__((always_inline)) {
+    f32x4_t acc[2][HT];
+    tile_mfma(f[0], acc[0]);
+#pragma unroll
+    for (int nt = 0; nt < kTilesPerIter; ++nt) {
+      if (nt + 1 < kTilesPerIter) tile_mfma(f[nt + 1], acc[(nt + 1) & 1]);
+      tile_epilogue(k, nt, acc[nt & 1]);
     }
   };
 
@@ -227,12 +247,10 @@ __global__ void __launch_bounds__(kIdxThreads) index_scores_mfma(
 #pragma unroll
       for (int j = 0; j < kStageLoads; ++j) st_lds[stage_slot<KFMT>(lane + 64 * j)] = v.v[j];
       wave_lds_sync();
+      KeyRaw f[kTilesPerIter];
 #pragma unroll
-      for (int nt = 0; nt < kTilesPerIter; ++nt) {
-        KeyRaw f;
-        stage_read<KFMT>(st_lds, 16 * nt + r16, kq, f);
-        score_tile(k0 + i * stride, nt, f);
-      }
+      for (int nt = 0; nt < kTilesPerIter; ++nt) stage_read<KFMT>(st_lds, 16 * nt + r16, kq, f[nt]);
+      score_tiles(k0 + i * stride, f);
     };
     U4Array<kStageLoads> sa = gload(0), sb;
     for (int64_t i = 0; i < n_full; i += 2) {
@@ -244,14 +262,14 @@ __global__ void __launch_bounds__(kIdxThreads) index_scores_mfma(
   }
   const int64_t kt = k0 + n_full * stride;
   if (kt < end) {
+    KeyRaw f[kTilesPerIter];
 #pragma unroll
     for (int nt = 0; nt < kTilesPerIter; ++nt) {
       int64_t key = kt + 16 * nt + r16;
       key = key < end ? key : end - 1;
-      KeyRaw f;
-      load_key<KFMT>(kbase + key * kRowBytes, kq, f);
-      score_tile(kt, nt, f);
+      load_key<KFMT>(kbase + key * kRowBytes, kq, f[nt]);
     }
+    score_tiles(kt, f);
   }
   __syncthreads();
   uint32_t* g = hist_g + row * kHistBins;
