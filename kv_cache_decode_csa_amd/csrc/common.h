@@ -157,6 +157,25 @@ __device__ __forceinline__ void encode_fp4_group(const float* v, uint8_t* codes,
 // ---------------------------------------------------------------- wave helpers
 __device__ __forceinline__ float shfl_xor_f(float v, int m) { return __shfl_xor(v, m, 64); }
 
+// Row exchanges of gfx950 (vector ALU, no LDS round trip).  A row is 16 lanes.
+// swap_rows16:   x' = [x.r0, y.r0, x.r2, y.r2],  y' = [x.r1, y.r1, x.r3, y.r3]
+// swap_halves32: x' = [x.lo, y.lo],              y' = [x.hi, y.hi]
+// (the returned pair is copied to plain integers before it is reinterpreted)
+__device__ __forceinline__ void swap_rows16(float& x, float& y) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(uint32_t, x),
+                                                  __builtin_bit_cast(uint32_t, y), false, false);
+  const uint32_t a = r[0], b = r[1];
+  x = __builtin_bit_cast(float, a);
+  y = __builtin_bit_cast(float, b);
+}
+__device__ __forceinline__ void swap_halves32(float& x, float& y) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, x),
+                                                  __builtin_bit_cast(uint32_t, y), false, false);
+  const uint32_t a = r[0], b = r[1];
+  x = __builtin_bit_cast(float, a);
+  y = __builtin_bit_cast(float, b);
+}
+
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
   for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, 64);

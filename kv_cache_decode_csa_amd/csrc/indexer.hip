@@ -197,33 +197,50 @@ __global__ void __launch_bounds__(kIdxThreads) index_scores_mfma(
 #pragma unroll
       for (int mt = 0; mt < HT; ++mt) acc[mt] = mfma16x16x32(as_bf16x8(qa[mt][s]), kb[s], acc[mt]);
   };
-  // The sum is formed over 2 ReLU(x) = x + |x| (exact, and an abs is free on
-  // the adder) and halved at the end: scaling by two commutes with every
+  // Partial score of a lane: the sum over its 16 heads (4 per head tile),
+  // formed over 2 ReLU(x) = x + |x| (exact, and an abs is free on the adder);
+  // the total is halved at the end.  Scaling by two commutes with every
   // rounding, so the result equals the plain sum of w_h ReLU(x_h) in the same
   // order, while a max would need its input canonicalized first.
-  auto tile_epilogue = [&](int64_t k, int nt, const f32x4_t (&acc)[HT]) __attribute__((always_inline)) {
+  auto tile_partial = [&](const f32x4_t (&acc)[HT]) __attribute__((always_inline)) {
     float p = 0.f;
 #pragma unroll
     for (int mt = 0; mt < HT; ++mt)
 #pragma unroll
       for (int r = 0; r < 4; ++r) p += wv[mt][r] * (acc[mt][r] + fabsf(acc[mt][r]));
-    p += shfl_xor_f(p, 16);
-    p += shfl_xor_f(p, 32);
-    p *= 0.5f;
-    const int64_t key = k + 16 * nt + r16;
-    if (kq == 0 && key < end) {
-      srow[key] = p;
-      atomicAdd(&hist[score_key(p) >> 20], 1u);
-    }
+    return p;
   };
-  // all tiles of a step, the MFMAs of tile nt + 1 ahead of the epilogue of nt
+  // All tiles of a step, the MFMAs of tile nt + 1 ahead of the partial sums
+  // of tile nt.  The four lane rows (kq) hold partials over different heads;
+  // row exchanges add them up so that row j ends with the scores of tile j
+  // (with two tiles, rows 2 and 3 repeat rows 0 and 1), and the step's scores
+  // are written and counted in one pass.
   auto score_tiles = [&](int64_t k, const KeyRaw (&f)[kTilesPerIter]) __attribute__((always_inline)) {
     f32x4_t acc[2][HT];
+    float p[kTilesPerIter];
     tile_mfma(f[0], acc[0]);
 #pragma unroll
     for (int nt = 0; nt < kTilesPerIter; ++nt) {
       if (nt + 1 < kTilesPerIter) tile_mfma(f[nt + 1], acc[(nt + 1) & 1]);
-      tile_epilogue(k, nt, acc[nt & 1]);
+      p[nt] = tile_partial(acc[nt & 1]);
+    }
+    float a, c;
+    if (kTilesPerIter == 4) {
+      swap_rows16(p[0], p[1]);
+      swap_rows16(p[2], p[3]);
+      a = p[0] + p[1];
+      c = p[2] + p[3];
+    } else {
+      swap_rows16(p[0], p[1]);
+      a = p[0] + p[1];
+      c = a;
+    }
+    swap_halves32(a, c);
+    const float sc = 0.5f * (a + c);
+    const int64_t key = k + 16 * kq + r16;
+    if ((kTilesPerIter == 4 || kq < kTilesPerIter) && key < end) {
+      srow[key] = sc;
+      atomicAdd(&hist[score_key(sc) >> 20], 1u);
     }
   };
 
