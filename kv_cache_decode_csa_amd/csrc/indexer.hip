@@ -269,12 +269,25 @@ __global__ void __launch_bounds__(kIdxThreads) index_scores_mfma(
       for (int nt = 0; nt < kTilesPerIter; ++nt) stage_read<KFMT>(st_lds, 16 * nt + r16, kq, f[nt]);
       score_tiles(k0 + i * stride, f);
     };
+    // The loop body has no conditional part, so at its head only the
+    // current step's loads are pending in every path (a skipped half would
+    // leave loads pending into the other set, and the wait that then guards
+    // that set would stall every iteration); the last one or two steps are
+    // peeled, and no step is read twice.
     U4Array<kStageLoads> sa = gload(0), sb;
-    for (int64_t i = 0; i < n_full; i += 2) {
-      sb = gload(i + 1 < n_full ? i + 1 : n_full - 1);
+    int64_t i = 0;
+    for (; i + 2 < n_full; i += 2) {
+      sb = gload(i + 1);
       stage_and_score(i, sa);
-      sa = gload(i + 2 < n_full ? i + 2 : n_full - 1);
-      if (i + 1 < n_full) stage_and_score(i + 1, sb);
+      sa = gload(i + 2);
+      stage_and_score(i + 1, sb);
+    }
+    if (i + 1 < n_full) {
+      sb = gload(i + 1);
+      stage_and_score(i, sa);
+      stage_and_score(i + 1, sb);
+    } else {
+      stage_and_score(i, sa);
     }
   }
   const int64_t kt = k0 + n_full * stride;
