@@ -161,17 +161,27 @@ __device__ __forceinline__ float shfl_xor_f(float v, int m) { return __shfl_xor(
 // swap_rows16:   x' = [x.r0, y.r0, x.r2, y.r2],  y' = [x.r1, y.r1, x.r3, y.r3]
 // swap_halves32: x' = [x.lo, y.lo],              y' = [x.hi, y.hi]
 // (the returned pair is copied to plain integers before it is reinterpreted)
-__device__ __forceinline__ void swap_rows16(float& x, float& y) {
-  const auto r = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(uint32_t, x),
-                                                  __builtin_bit_cast(uint32_t, y), false, false);
+__device__ __forceinline__ void swap_rows16(uint32_t& x, uint32_t& y) {
+  const auto r = __builtin_amdgcn_permlane16_swap(x, y, false, false);
   const uint32_t a = r[0], b = r[1];
+  x = a;
+  y = b;
+}
+__device__ __forceinline__ void swap_halves32(uint32_t& x, uint32_t& y) {
+  const auto r = __builtin_amdgcn_permlane32_swap(x, y, false, false);
+  const uint32_t a = r[0], b = r[1];
+  x = a;
+  y = b;
+}
+__device__ __forceinline__ void swap_rows16(float& x, float& y) {
+  uint32_t a = __builtin_bit_cast(uint32_t, x), b = __builtin_bit_cast(uint32_t, y);
+  swap_rows16(a, b);
   x = __builtin_bit_cast(float, a);
   y = __builtin_bit_cast(float, b);
 }
 __device__ __forceinline__ void swap_halves32(float& x, float& y) {
-  const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, x),
-                                                  __builtin_bit_cast(uint32_t, y), false, false);
-  const uint32_t a = r[0], b = r[1];
+  uint32_t a = __builtin_bit_cast(uint32_t, x), b = __builtin_bit_cast(uint32_t, y);
+  swap_halves32(a, b);
   x = __builtin_bit_cast(float, a);
   y = __builtin_bit_cast(float, b);
 }

@@ -338,79 +338,79 @@ __device__ __forceinline__ uint32_t lane_xor(uint32_t x) {
   else return (uint32_t)__builtin_amdgcn_ds_bpermute((int)(((threadIdx.x & 63) ^ M) << 2), (int)x);
 }
 
-// Bitonic network over 512 packed values held by a pair of waves, 4 per lane
-// (element e = 4 (64 pw + lane) + i, pw = this wave's place in the pair),
-// sorted descending.  Stage (K, J) compares e with e ^ J: inside a lane for
-// J < 4, across lanes (lane ^ J/4) for 4 <= J < 256, across the pair through
-// LDS for J = 256.  Every lane exchange of a stage is issued before any result
-// is used.  Called by all threads of the work-group (the J = 256 stage
-// synchronises it).
+// Bitonic network over 512 packed values held by the four waves of a
+// work-group, 2 per lane (element e = 2 (64 wave + lane) + i), sorted
+// descending.  Stage (K, J) compares e with e ^ J: inside a lane for J = 1,
+// across lanes (lane ^ J/2) for 2 <= J <= 64, across waves through LDS for
+// J = 128 and 256.  Lane distances 16 and 32 use the gfx950 row swaps, which
+// hand both members of a pair both values, so each keeps the larger or the
+// smaller one directly.  Called by all threads of the work-group.
 template <int K, int J>
-__device__ __forceinline__ void bitonic_stage(uint64_t (&v)[4], int e0, uint64_t* lds) {
-  if constexpr (J < 4) {
+__device__ __forceinline__ void bitonic_stage2(uint64_t (&v)[2], int e0, uint64_t* lds) {
+  if constexpr (J == 1) {
+    const bool desc = (e0 & K) == 0;
+    const uint64_t a = v[0], b = v[1];
+    const bool swap = desc ? (a < b) : (a > b);
+    v[0] = swap ? b : a;
+    v[1] = swap ? a : b;
+  } else if constexpr (J == 32 || J == 64) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      constexpr int jj = J;
-      const int p = i ^ jj;
-      if (p > i) {
-        const bool desc = ((e0 + i) & K) == 0;
-        const uint64_t a = v[i], b = v[p];
-        const bool swap = desc ? (a < b) : (a > b);
-        v[i] = swap ? b : a;
-        v[p] = swap ? a : b;
-      }
+    for (int i = 0; i < 2; ++i) {
+      uint32_t alo = (uint32_t)v[i], blo = alo, ahi = (uint32_t)(v[i] >> 32), bhi = ahi;
+      if constexpr (J == 32) { swap_rows16(alo, blo); swap_rows16(ahi, bhi); }
+      else { swap_halves32(alo, blo); swap_halves32(ahi, bhi); }
+      const uint64_t a = ((uint64_t)ahi << 32) | alo, b = ((uint64_t)bhi << 32) | blo;
+      const int e = e0 + i;
+      const bool keep_max = ((e & J) == 0) == ((e & K) == 0);
+      v[i] = keep_max == (a > b) ? a : b;
     }
   } else {
-    uint64_t pv[4];
-    if constexpr (J < 256) {
-      uint32_t lo[4], hi[4];
+    uint64_t pv[2];
+    if constexpr (J < 128) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        lo[i] = lane_xor<J / 4>((uint32_t)v[i]);
-        hi[i] = lane_xor<J / 4>((uint32_t)(v[i] >> 32));
+      for (int i = 0; i < 2; ++i) {
+        const uint32_t lo = lane_xor<J / 2>((uint32_t)v[i]);
+        const uint32_t hi = lane_xor<J / 2>((uint32_t)(v[i] >> 32));
+        pv[i] = ((uint64_t)hi << 32) | lo;
       }
-#pragma unroll
-      for (int i = 0; i < 4; ++i) pv[i] = ((uint64_t)hi[i] << 32) | lo[i];
     } else {
       __syncthreads();
 #pragma unroll
-      for (int i = 0; i < 4; ++i) lds[e0 + i] = v[i];
+      for (int i = 0; i < 2; ++i) lds[e0 + i] = v[i];
       __syncthreads();
 #pragma unroll
-      for (int i = 0; i < 4; ++i) pv[i] = lds[(e0 + i) ^ J];
+      for (int i = 0; i < 2; ++i) pv[i] = lds[(e0 + i) ^ J];
     }
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < 2; ++i) {
       const int e = e0 + i;
       const bool keep_max = ((e & J) == 0) == ((e & K) == 0);
       v[i] = keep_max ? (v[i] > pv[i] ? v[i] : pv[i]) : (v[i] < pv[i] ? v[i] : pv[i]);
     }
   }
 }
-
-template <int K, int J> struct BitonicJ {
-  static __device__ __forceinline__ void run(uint64_t (&v)[4], int e0, uint64_t* lds) {
-    bitonic_stage<K, J>(v, e0, lds);
-    BitonicJ<K, J / 2>::run(v, e0, lds);
+template <int K, int J> struct Bitonic2J {
+  static __device__ __forceinline__ void run(uint64_t (&v)[2], int e0, uint64_t* lds) {
+    bitonic_stage2<K, J>(v, e0, lds);
+    Bitonic2J<K, J / 2>::run(v, e0, lds);
   }
 };
-template <int K> struct BitonicJ<K, 0> {
-  static __device__ __forceinline__ void run(uint64_t (&)[4], int, uint64_t*) {}
+template <int K> struct Bitonic2J<K, 0> {
+  static __device__ __forceinline__ void run(uint64_t (&)[2], int, uint64_t*) {}
 };
-template <int K> struct BitonicK {
-  static __device__ __forceinline__ void run(uint64_t (&v)[4], int e0, uint64_t* lds) {
-    BitonicJ<K, K / 2>::run(v, e0, lds);
-    BitonicK<2 * K>::run(v, e0, lds);
+template <int K> struct Bitonic2K {
+  static __device__ __forceinline__ void run(uint64_t (&v)[2], int e0, uint64_t* lds) {
+    Bitonic2J<K, K / 2>::run(v, e0, lds);
+    Bitonic2K<2 * K>::run(v, e0, lds);
   }
 };
-template <> struct BitonicK<1024> {
-  static __device__ __forceinline__ void run(uint64_t (&)[4], int, uint64_t*) {}
+template <> struct Bitonic2K<1024> {
+  static __device__ __forceinline__ void run(uint64_t (&)[2], int, uint64_t*) {}
 };
 
-// lds: 512 uint64 for this pair of waves
-__device__ __forceinline__ void sort512_pair_desc(uint64_t (&v)[4], int pw, uint64_t* lds) {
-  const int e0 = 4 * (64 * pw + (threadIdx.x & 63));
-  BitonicK<2>::run(v, e0, lds);
+// lds: 512 uint64
+__device__ __forceinline__ void sort512_wg_desc(uint64_t (&v)[2], uint64_t* lds) {
+  Bitonic2K<2>::run(v, 2 * (int)threadIdx.x, lds);
 }
 
 // Write the indices of n <= kSortCap (key, idx) pairs ordered by key desc,
@@ -553,42 +553,44 @@ __global__ void __launch_bounds__(kSelThreads) topk_collect_kernel(
   }
 }
 
-// Pass 2, one work-group per row: refine the boundary bin with the remaining
-// 20 bits (12 + 8) from the register-resident candidates, resolve ties at the
-// threshold by index, order the winners and write the row.  When the
-// boundary bin held more entries than the candidate list, the refinement
-// runs over the whole row instead.
+// Pass 2, two work-groups per row.  In the common case (the hi list and the
+// boundary list both fit 512 entries and the boundary bin was kept) the first
+// work-group orders the hi list and the second the boundary list, each
+// writing its part of the row.  Otherwise the first work-group alone refines
+// the boundary bin with the remaining 20 bits (12 + 8) from the
+// register-resident candidates, resolves ties at the threshold by index,
+// orders the winners and writes the row; when the boundary bin held more
+// entries than the candidate list, the refinement runs over the whole row.
 __global__ void __launch_bounds__(kSelThreads) topk_final_kernel(
     const float* __restrict__ scores, const int32_t* __restrict__ n_valid, int64_t ld, int topk,
     int32_t* __restrict__ out_idx, const RowInfo* info_g, const uint32_t* cand_g,
     const uint32_t* hi_g) {
   __shared__ LdsSel L;
   const int t = threadIdx.x;
-  const int64_t row = blockIdx.x;
+  const int part = blockIdx.x;  // 0: hi list (and the general path), 1: boundary list
+  const int64_t row = blockIdx.y;
   int64_t nv64 = n_valid[row];
   nv64 = nv64 < 0 ? 0 : (nv64 > ld ? ld : nv64);
   const uint32_t nv = (uint32_t)nv64;
   const uint32_t k_eff = nv < (uint32_t)topk ? nv : (uint32_t)topk;
   int32_t* out = out_idx + row * (int64_t)topk;
   if (k_eff == 0) {
-    for (int i = t; i < topk; i += kSelThreads) out[i] = -1;
+    if (part == 0)
+      for (int i = t; i < topk; i += kSelThreads) out[i] = -1;
     return;
   }
   const RowInfo* info = info_g + row;
   const uint32_t* cand = cand_g + row * (int64_t)kCandCap * 2;
   const uint32_t* hi = hi_g + row * (int64_t)kTopkMax * 2;
   const float* s = scores + row * ld;
-  // Both lists' first 512 pairs are read before their lengths are known (the
-  // workspace always holds them), so the two reads overlap.  Waves 0-1 hold
-  // the hi list, waves 2-3 the boundary list, 4 entries per lane.
-  const int lane = t & 63, wv = t >> 6;
-  const int lst = wv >> 1, pw = wv & 1;
-  const int e0 = 4 * (64 * pw + lane);
-  uint64_t fv[4];
+  // This part's list's first 512 pairs are read before the lengths are known
+  // (the workspace always holds them), 2 per lane.
+  const int e0 = 2 * t;
+  uint64_t fv[2];
   {
-    const uint2* src = (const uint2*)(lst == 0 ? hi : cand) + e0;
+    const uint2* src = (const uint2*)(part == 0 ? hi : cand) + e0;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < 2; ++i) {
       const uint2 pr = src[i];
       fv[i] = ((uint64_t)pr.x << 32) | (uint64_t)(~pr.y);
     }
@@ -598,21 +600,23 @@ __global__ void __launch_bounds__(kSelThreads) topk_final_kernel(
   const uint32_t need = k_eff - above;
   // Fast path: every entry of the hi list outranks every entry of the
   // boundary bin, so the answer is the sorted hi list followed by the first
-  // `need` entries of the sorted boundary list.  A pair of waves sorts each.
+  // `need` entries of the sorted boundary list.
   if (keep_eq && above <= 512u && eq <= 512u) {
-    const uint32_t n = lst == 0 ? above : eq;
+    const uint32_t n = part == 0 ? above : eq;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < 2; ++i)
       if ((uint32_t)(e0 + i) >= n) fv[i] = 0ull;  // padding sorts last
-    sort512_pair_desc(fv, pw, (uint64_t*)L.ties + 512 * lst);
-    const uint32_t lim = lst == 0 ? above : need;
-    int32_t* o = out + (lst == 0 ? 0u : above);
+    sort512_wg_desc(fv, (uint64_t*)L.ties);
+    const uint32_t lim = part == 0 ? above : need;
+    int32_t* o = out + (part == 0 ? 0u : above);
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < 2; ++i)
       if ((uint32_t)(e0 + i) < lim) o[e0 + i] = (int32_t)(~(uint32_t)fv[i]);
-    for (int i = (int)k_eff + t; i < topk; i += kSelThreads) out[i] = -1;
+    if (part == 1)
+      for (int i = (int)k_eff + t; i < topk; i += kSelThreads) out[i] = -1;
     return;
   }
+  if (part != 0) return;
   if (t == 0) { L.n_sel = 0; L.n_ties = 0; }
   uint32_t hk[kHiPerThread], hx[kHiPerThread];
 #pragma unroll
@@ -764,9 +768,9 @@ hipError_t launch_topk_select(const float* scores, const int32_t* n_valid, int64
                        (RowInfo*)w.ctr + r0, w.cand + r0 * (int64_t)kCandCap * 2,
                        w.hi + r0 * (int64_t)kTopkMax * 2);
   }
-  for (int64_t r0 = 0; r0 < R; r0 += (int64_t)1 << 30) {
-    int64_t nr = R - r0 < ((int64_t)1 << 30) ? R - r0 : ((int64_t)1 << 30);
-    hipLaunchKernelGGL(topk_final_kernel, dim3((unsigned)nr), dim3(kSelThreads), 0, s,
+  for (int64_t r0 = 0; r0 < R; r0 += 65535) {
+    int64_t nr = R - r0 < 65535 ? R - r0 : 65535;
+    hipLaunchKernelGGL(topk_final_kernel, dim3(2u, (unsigned)nr), dim3(kSelThreads), 0, s,
                        scores + r0 * ld, n_valid + r0, ld, topk, out_idx + r0 * topk,
                        (const RowInfo*)w.ctr + r0, w.cand + r0 * (int64_t)kCandCap * 2,
                        w.hi + r0 * (int64_t)kTopkMax * 2);
