@@ -58,35 +58,43 @@ __device__ __forceinline__ int pow2_at_least(int n) {
 }
 
 // Find the largest bin b with sum_{b' >= b} hist[b'] >= need (need >= 1 and the
-// total >= need).  hist lives in LDS; nbins is a multiple of kSelThreads.
-// Returns b and writes the count strictly above b to *above.  Every thread
-// sums its own bins, a wave-level suffix scan plus the higher waves' totals
-// gives each thread the count at and above its bins, and the single thread
-// whose range crosses `need` resolves the bin.  Ends synced.
-__device__ int suffix_find(const uint32_t* hist, int nbins, uint32_t need, uint32_t* above,
+// total >= need) over the kHistBins bins of hist (LDS).  Returns b and writes
+// the count strictly above b to *above.  Every thread holds 16 consecutive
+// bins in registers; a wave prefix sum (suffix = wave total - exclusive
+// prefix) plus the higher waves' totals gives each thread the count at and
+// above its bins, and the single thread whose range crosses `need` resolves
+// the bin from its registers.  Ends synced.
+__device__ int suffix_find(const uint32_t* hist, uint32_t need, uint32_t* above,
                            uint32_t* scratch /* LDS, kSelThreads + 8 */) {
-  const int per = nbins / kSelThreads;
+  constexpr int per = kHistBins / kSelThreads;
+  static_assert(per == 16, "16 bins per thread");
   const int t = threadIdx.x, lane = t & 63, w = t >> 6;
-  uint32_t local = 0;
-  for (int j = 0; j < per; ++j) local += hist[t * per + j];
-  uint32_t v = local;
+  uint32_t h[per];
 #pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    uint32_t n = __shfl_down(v, off, 64);
-    if (lane + off < 64) v += n;
+  for (int q = 0; q < per / 4; ++q) {
+    const uint4 v = *(const uint4*)(hist + per * t + 4 * q);
+    h[4 * q] = v.x; h[4 * q + 1] = v.y; h[4 * q + 2] = v.z; h[4 * q + 3] = v.w;
   }
-  if (lane == 0) scratch[w] = v;
+  uint32_t local = 0;
+#pragma unroll
+  for (int j = 0; j < per; ++j) local += h[j];
+  const uint32_t incl = wave_prefix_incl(local);
+  const uint32_t total = (uint32_t)__builtin_amdgcn_readlane((int)incl, 63);
+  if (lane == 0) scratch[w] = total;
   __syncthreads();
-  uint32_t S = v;
+  uint32_t S = total - incl + local;  // this thread's bins and the wave's higher ones
   for (int u = w + 1; u < kSelThreads / 64; ++u) S += scratch[u];
   const uint32_t prev = S - local;
   if (S >= need && prev < need) {
     uint32_t acc = prev;
-    int b = t * per;
+    int b = per * t;
+    bool found = false;
+#pragma unroll
     for (int j = per - 1; j >= 0; --j) {
-      const uint32_t h = hist[t * per + j];
-      if (acc + h >= need) { b = t * per + j; break; }
-      acc += h;
+      const bool hit = !found && acc + h[j] >= need;
+      if (hit) b = per * t + j;
+      if (!found && !hit) acc += h[j];
+      found = found || hit;
     }
     scratch[kSelThreads] = (uint32_t)b;
     scratch[kSelThreads + 1] = acc;
@@ -122,7 +130,7 @@ __device__ void sort_store(const uint32_t* key, const uint32_t* idx, int n, uint
   for (int i = threadIdx.x; i < n; i += blockDim.x) out[i] = (int32_t)(~(uint32_t)tmp[i]);
 }
 
-struct LdsSel {
+struct __align__(16) LdsSel {  // hist is read as 16-byte vectors
   uint32_t hist[kHistBins];
   uint32_t scratch[kSelThreads + 16];
   uint32_t skey[kSortCap];
@@ -172,7 +180,7 @@ __device__ void refine_and_collect(const Src& src, uint32_t b1, uint32_t need, b
   }
   __syncthreads();
   uint32_t above2;
-  uint32_t b2 = (uint32_t)suffix_find(L.hist, kHistBins, need, &above2, L.scratch);
+  uint32_t b2 = (uint32_t)suffix_find(L.hist, need, &above2, L.scratch);
   // digit 3: bits 7..0 within (b1, b2)
   const uint32_t pre = (b1 << 12) | b2;
   for (int i = t; i < kHistBins; i += kSelThreads) L.hist[i] = 0;
@@ -185,7 +193,7 @@ __device__ void refine_and_collect(const Src& src, uint32_t b1, uint32_t need, b
   __syncthreads();
   uint32_t above3;
   // 256 bins: pad the rest of the histogram with zeros (already zero)
-  uint32_t b3 = (uint32_t)suffix_find(L.hist, kHistBins, need - above2, &above3, L.scratch);
+  uint32_t b3 = (uint32_t)suffix_find(L.hist, need - above2, &above3, L.scratch);
   const uint32_t T = (pre << 8) | b3;
   const uint32_t need_t = need - above2 - above3;  // >= 1 ties to take at key T
   // collect key > T within the bin (count above2 + above3 < need <= kSortCap)
@@ -447,7 +455,7 @@ struct RowInfo {       // written by work-group 0 of each row's collect pass
 __global__ void __launch_bounds__(kSelThreads) topk_collect_kernel(
     const float* __restrict__ scores, const int32_t* __restrict__ n_valid, int64_t ld, int topk,
     const uint32_t* hist_g, RowInfo* info_g, uint32_t* cand_g, uint32_t* hi_g) {
-  __shared__ uint32_t hist[kHistBins];
+  __shared__ __align__(16) uint32_t hist[kHistBins];
   __shared__ uint32_t scratch[kSelThreads + 16];
   const int t = threadIdx.x;
   const int64_t row = blockIdx.y;
@@ -494,7 +502,7 @@ __global__ void __launch_bounds__(kSelThreads) topk_collect_kernel(
   }
   __syncthreads();
   uint32_t above;
-  const uint32_t b1 = (uint32_t)suffix_find(hist, kHistBins, k_eff, &above, scratch);
+  const uint32_t b1 = (uint32_t)suffix_find(hist, k_eff, &above, scratch);
   const uint32_t eq = hist[b1];
   const bool keep_eq = eq <= (uint32_t)kCandCap;
   if (blockIdx.x == 0 && t == 0) {
@@ -511,12 +519,9 @@ __global__ void __launch_bounds__(kSelThreads) topk_collect_kernel(
     if (i < end && b == b1) ++n_eq_t;
   }
   const int lane = t & 63, wv = t >> 6;
-  uint32_t ph = n_hi_t, pe = n_eq_t;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const uint32_t a1 = __shfl_up(ph, off, 64), a2 = __shfl_up(pe, off, 64);
-    if (lane >= off) { ph += a1; pe += a2; }
-  }
+  // both counts in one prefix sum (a wave's totals stay below 2^16)
+  const uint32_t pk = wave_prefix_incl(n_hi_t | (n_eq_t << 16));
+  const uint32_t ph = pk & 0xffffu, pe = pk >> 16;
   if (lane == 63) { scratch[wv] = ph; scratch[4 + wv] = pe; }
   __syncthreads();
   uint32_t off_h = ph - n_hi_t, off_e = pe - n_eq_t;
@@ -660,7 +665,7 @@ __global__ void __launch_bounds__(kSelThreads) topk_final_kernel(
   }
   __syncthreads();
   uint32_t above2;
-  const uint32_t b2 = (uint32_t)suffix_find(L.hist, kHistBins, need, &above2, L.scratch);
+  const uint32_t b2 = (uint32_t)suffix_find(L.hist, need, &above2, L.scratch);
   const uint32_t pre = (b1 << 12) | b2;
   // third digit: bits 7..0 within (b1, b2)
   for (int i = t; i < kHistBins; i += kSelThreads) L.hist[i] = 0;
@@ -672,7 +677,7 @@ __global__ void __launch_bounds__(kSelThreads) topk_final_kernel(
   }
   __syncthreads();
   uint32_t above3;
-  const uint32_t b3 = (uint32_t)suffix_find(L.hist, kHistBins, need - above2, &above3, L.scratch);
+  const uint32_t b3 = (uint32_t)suffix_find(L.hist, need - above2, &above3, L.scratch);
   const uint32_t T = (pre << 8) | b3;
   const uint32_t need_t = need - above2 - above3;  // >= 1 entries equal to T are taken
   // winners: the hi list, candidates above T, and ties at T (by index)
