@@ -371,7 +371,11 @@ __device__ __forceinline__ void load_q_frags(const AttnArgs& a, int64_t unit, in
 // logits of all head tiles are summed through LDS, wave w runs the softmax of
 // head tile w, and P and the rescale factors go through LDS so that every
 // wave accumulates O for all heads over its dims.
-constexpr int kChunkDense = 512;  // rows per work-group
+// Rows per work-group: at least 512, and enough that a unit's list has at
+// most kMergeChunks chunks, which the merge then combines in one round of
+// loads (a multiple of the 32-row tile).
+constexpr int kChunkDense = 512;
+constexpr int kMergeChunks = 16;
 
 template <int HT>
 __device__ __forceinline__ void attend_tile_all(const uint4 (&fr)[2][4], uint32_t vmask,
@@ -472,21 +476,33 @@ __device__ __forceinline__ void attend_tile_all(const uint4 (&fr)[2][4], uint32_
   }
 }
 
-// Work-group = (chunk, unit), chunk-major so that the short last chunks of
-// the units run last.  Writes one partial per (unit, head tile, chunk) in the
-// layout of the merge kernel.
+// Work-group = (chunk, unit, head part), chunk-major so that the short last
+// chunks of the units run last.  A work-group takes HT head tiles; with
+// hsplit > 1 the H / 16 head tiles are split over hsplit work-groups whose
+// linear ids are 8 apart, so they run on one XCD at about the same time and
+// read the chunk's rows through one L2 (work-groups are handed to the XCDs
+// round-robin by linear id).  Writes one partial per (unit, head tile, chunk)
+// in the layout of the merge kernel.
 template <int WF, int EF, int HT>
-__global__ void __launch_bounds__(kAttnThreads) attn_dense_all_kernel(AttnArgs a, int nchunks,
-                                                                      int64_t units,
-                                                                      Partial* part) {
+__global__ void __launch_bounds__(kAttnThreads, HT <= 2 ? 2 : 1) attn_dense_all_kernel(AttnArgs a, int chunk_rows,
+                                                                      int nchunks, int64_t units,
+                                                                      int hsplit, Partial* part) {
   __shared__ uint16_t Rl[4][kTile * kRPitch];
   __shared__ float4 Sp[4][HT][2][64];
   __shared__ uint4 Pl[HT * 64];
   __shared__ float Al[16 * HT];
 
-  const int64_t item = blockIdx.x;
+  int64_t item = blockIdx.x;
+  int hs = 0;
+  if (hsplit > 1) {
+    const int64_t k = item >> 3;
+    hs = (int)(k % hsplit);
+    item = (k / hsplit) * 8 + (item & 7);
+  }
+  if (item >= (int64_t)nchunks * units) return;
   const int chunk = (int)(item / units);
   const int64_t unit = a.unit_off + item % units;
+  const int ht0 = HT * hs;  // first head tile of this work-group
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int w = tid >> 6;
@@ -496,14 +512,14 @@ __global__ void __launch_bounds__(kAttnThreads) attn_dense_all_kernel(AttnArgs a
   const int t = a.pos[unit];
   const int64_t nvis = unit_nvis(a, t);
   const int64_t list_len = kWindow + nvis;
-  const int64_t j_begin = (int64_t)chunk * kChunkDense;
-  int64_t j_end = j_begin + kChunkDense;
+  const int64_t j_begin = (int64_t)chunk * chunk_rows;
+  int64_t j_end = j_begin + chunk_rows;
   if (j_end > list_len) j_end = list_len;
   const int rr = rope_row(a, t);
   const float zscale = a.scale * kLog2e;
 
   uint4 qa[HT][4];
-  load_q_frags<HT>(a, unit, 0, w, r16, kq, rr, qa);
+  load_q_frags<HT>(a, unit, 16 * ht0, w, r16, kq, rr, qa);
 
   float sm = -INFINITY, sl = 0.f;
   f32x4_t o[HT][8];
@@ -572,13 +588,13 @@ __global__ void __launch_bounds__(kAttnThreads) attn_dense_all_kernel(AttnArgs a
 
   const int G = a.H / 16;
   if (w < HT && lane < 16) {
-    Partial* P = part + (unit * G + w) * (int64_t)nchunks + chunk;
+    Partial* P = part + (unit * G + ht0 + w) * (int64_t)nchunks + chunk;
     P->m[lane] = sm;
     P->l[lane] = sl;
   }
 #pragma unroll
   for (int ht = 0; ht < HT; ++ht) {
-    Partial* P = part + (unit * G + ht) * (int64_t)nchunks + chunk;
+    Partial* P = part + (unit * G + ht0 + ht) * (int64_t)nchunks + chunk;
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt)
 #pragma unroll
@@ -736,6 +752,7 @@ __global__ void __launch_bounds__(kAttnThreads) attn_mfma_kernel(AttnArgs a, int
 // and 4 dims.  Chunks are combined in index order; each batch of 16 chunks is
 // loaded before any is combined, so the loads overlap.
 constexpr int kMergeBatch = 16;
+static_assert(kMergeChunks <= kMergeBatch, "a dense list merges in one round");
 
 __global__ void __launch_bounds__(kAttnThreads) attn_merge_kernel(AttnArgs a, int nchunks,
                                                                   const Partial* part) {
@@ -881,12 +898,15 @@ static bool attn_all_heads(const AttnArgs& a) {
   return a.dense && a.H <= 64 && a.q_fmt != CSA_F32;
 }
 
-int attn_chunk_rows(const AttnArgs& a) {
-  return attn_all_heads(a) ? kChunkDense : (a.dense ? kChunkHca : kChunkCsa);
-}
-
 int64_t attn_list_len(const AttnArgs& a) {
   return kWindow + (a.dense ? a.Nmax : (int64_t)a.topk);
+}
+
+int attn_chunk_rows(const AttnArgs& a) {
+  if (!attn_all_heads(a)) return a.dense ? kChunkHca : kChunkCsa;
+  const int64_t per = (attn_list_len(a) + kMergeChunks - 1) / kMergeChunks;
+  const int64_t cr = (per + kTile - 1) / kTile * kTile;
+  return (int)(cr > kChunkDense ? cr : kChunkDense);
 }
 
 static int attn_nchunks(const AttnArgs& a) {
@@ -914,15 +934,24 @@ static void launch_mfma_w(const AttnArgs& a, int nc, int64_t nu, dim3 grid, Part
     hipLaunchKernelGGL((attn_mfma_kernel<WF, CSA_FP4_E4M3_16>), grid, dim3(kAttnThreads), 0, s, a, cr, nc, nu, part);
 }
 
+// Fewer than two work-groups per CU would leave one wave per SIMD with a
+// single tile in flight: the head tiles are then split over two work-groups.
+constexpr int64_t kDenseSplitBelow = 512;
+
 template <int WF, int EF>
 static void launch_all_heads_e(const AttnArgs& a, int nc, int64_t nu, Partial* part,
                                hipStream_t s) {
-  const dim3 grid((unsigned)(nc * nu));
-  switch (a.H / 16) {
-    case 1: hipLaunchKernelGGL((attn_dense_all_kernel<WF, EF, 1>), grid, dim3(kAttnThreads), 0, s, a, nc, nu, part); break;
-    case 2: hipLaunchKernelGGL((attn_dense_all_kernel<WF, EF, 2>), grid, dim3(kAttnThreads), 0, s, a, nc, nu, part); break;
-    case 3: hipLaunchKernelGGL((attn_dense_all_kernel<WF, EF, 3>), grid, dim3(kAttnThreads), 0, s, a, nc, nu, part); break;
-    default: hipLaunchKernelGGL((attn_dense_all_kernel<WF, EF, 4>), grid, dim3(kAttnThreads), 0, s, a, nc, nu, part); break;
+  const int G = a.H / 16;
+  const int64_t items = (int64_t)nc * nu;
+  const int hsplit = (G % 2 == 0 && items < kDenseSplitBelow) ? 2 : 1;
+  const int HT = G / hsplit;
+  const int cr = attn_chunk_rows(a);
+  const dim3 grid((unsigned)(hsplit == 1 ? items : (items + 7) / 8 * 8 * hsplit));
+  switch (HT) {
+    case 1: hipLaunchKernelGGL((attn_dense_all_kernel<WF, EF, 1>), grid, dim3(kAttnThreads), 0, s, a, cr, nc, nu, hsplit, part); break;
+    case 2: hipLaunchKernelGGL((attn_dense_all_kernel<WF, EF, 2>), grid, dim3(kAttnThreads), 0, s, a, cr, nc, nu, hsplit, part); break;
+    case 3: hipLaunchKernelGGL((attn_dense_all_kernel<WF, EF, 3>), grid, dim3(kAttnThreads), 0, s, a, cr, nc, nu, hsplit, part); break;
+    default: hipLaunchKernelGGL((attn_dense_all_kernel<WF, EF, 4>), grid, dim3(kAttnThreads), 0, s, a, cr, nc, nu, hsplit, part); break;
   }
 }
 
