@@ -135,6 +135,35 @@ def test_hca_decode(tables, efmt):
         close_bf16(got[b, 0], ref)
 
 
+def test_hca_decode_many_units(tables):
+    """Enough (chunk, unit) items that every work-group takes all 64 heads
+    (the head tiles are split over two work-groups only for small grids):
+    2 sequences x 32 causal queries over 4,096 entries, sampled queries
+    checked."""
+    cos, sin = tables
+    B, Q, H, N = 2, 32, 64, 4096
+    rng = np.random.default_rng(37)
+    q = synth.bf16_round(rng.standard_normal((B, Q, H, 512)).astype(np.float32))
+    win = synth.bf16_round(rng.standard_normal((B, 128, 512)).astype(np.float32))
+    ent = synth.bf16_round(rng.standard_normal((B, N, 512)).astype(np.float32))
+    sink = rng.standard_normal(H).astype(np.float32)
+    # every query sees a different prefix; the last ones see all entries
+    pos = (128 * N - 1 - 4000 * np.arange(Q)[::-1]).astype(np.int32)
+    pos = np.stack([pos, pos - 17]).astype(np.int32)
+    say("hca attn many units")
+    out = torch.empty((B, Q, H, 512), dtype=torch.bfloat16, device="cuda")
+    ws = _lib.workspace(_lib.hca_attn_workspace_size(B, Q, H, N))
+    _lib.hca_attn_decode(bf16(q), "bf16", bf16(win), "bf16", _lib.WIN_RING128, None, 128,
+                         upload_rows(ent, "bf16"), "bf16", N, 128, i32(pos), B, Q, H, f32(sink),
+                         512 ** -0.5, cos, sin, out, "bf16", ws)
+    got = to_np(out)
+    for b, qq in [(0, 0), (0, Q - 1), (1, 5), (1, Q - 1)]:
+        t = int(pos[b, qq])
+        ref = A.hca_decode(q[b, qq].astype(np.float64), win[b].astype(np.float64),
+                           A.window_ids(t), ent[b], sink, 512 ** -0.5, t, OM)
+        close_bf16(got[b, qq], ref)
+
+
 def test_f32_path_and_single_head_group(tables):
     cos, sin = tables
     B, H, N, k = 1, 16, 512, 64
