@@ -181,9 +181,9 @@ __global__ void __launch_bounds__(kIdxThreads) index_scores_mfma(
   const int64_t stride = G * 4 * (int64_t)kKeysPerIter;
   const int64_t k0 = ((int64_t)blockIdx.x * 4 + wave) * kKeysPerIter;
   // Scoring is split in two so that the MFMAs of one tile can be issued
-  // before the epilogue of the previous one: tile_mfma forms the 16 heads x 16
-  // keys products of every head tile, tile_epilogue applies ReLU and the head
-  // weights, sums the heads and records the score.
+  // before the partial sums of the previous one: tile_mfma forms the 16 heads
+  // x 16 keys products of every head tile, tile_partial applies ReLU and the
+  // head weights over the lane's heads.
   auto tile_mfma = [&](const KeyRaw& f, f32x4_t (&acc)[HT]) __attribute__((always_inline)) {
     bf16x8_t kb[4];
 #pragma unroll
