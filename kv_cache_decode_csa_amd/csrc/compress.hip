@@ -451,34 +451,44 @@ __device__ __forceinline__ void store_elem(int fmt, float v, int c, int d, bool 
   }
 }
 
-// RMSNorm -> RoPE at position i * r -> optional Hadamard -> storage rounding of
-// the pooled block in y; writes entry i of sequence b.  z: LDS scratch of d
-// floats.
-__device__ void finish_block(const CompArgs& a, int64_t b, int64_t i, float* y, float* z,
-                             float* red, float sq) {
-  const int tid = threadIdx.x;
-  const int r = a.ratio;
-  const int d = a.d;
-  // norm weights and rotation factors of this thread's channels (d <= 512 =
-  // 2 kThreads), fetched before the reduction so their latency overlaps it
-  int64_t rrow = i * r;
-  if (rrow >= a.rope_rows) rrow = a.rope_rows - 1;
+// Norm weights and rotation factors at position i * r of this thread's
+// channels (d <= 512 = 2 kThreads).
+struct NormRope {
   float gw[2], gp[2], cs[2], sn[2];
+};
+__device__ __forceinline__ NormRope load_norm_rope(const CompArgs& a, int64_t i) {
+  const int tid = threadIdx.x;
+  const int d = a.d;
+  int64_t rrow = i * a.ratio;
+  rrow = rrow < 0 ? 0 : (rrow >= a.rope_rows ? a.rope_rows - 1 : rrow);
+  NormRope f;
 #pragma unroll
   for (int u = 0; u < 2; ++u) {
     const int c = tid + u * kThreads;
-    gw[u] = gp[u] = cs[u] = 1.f;
-    sn[u] = 0.f;
+    f.gw[u] = f.gp[u] = f.cs[u] = 1.f;
+    f.sn[u] = 0.f;
     if (c < d) {
-      gw[u] = a.norm_w[c];
+      f.gw[u] = a.norm_w[c];
       if (c >= d - kRopeDims) {
         const int k = (c - (d - kRopeDims)) >> 1;
-        gp[u] = a.norm_w[c ^ 1];
-        cs[u] = a.rope_cos[rrow * 32 + k];
-        sn[u] = a.rope_sin[rrow * 32 + k];
+        f.gp[u] = a.norm_w[c ^ 1];
+        f.cs[u] = a.rope_cos[rrow * 32 + k];
+        f.sn[u] = a.rope_sin[rrow * 32 + k];
       }
     }
   }
+  return f;
+}
+
+// RMSNorm -> RoPE at position i * r -> optional Hadamard -> storage rounding of
+// the pooled block in y; writes entry i of sequence b.  z: LDS scratch of d
+// floats; f: load_norm_rope(a, i), fetched early so that its latency overlaps
+// earlier work.
+__device__ void finish_block(const CompArgs& a, int64_t b, int64_t i, float* y, float* z,
+                             float* red, float sq, const NormRope& f) {
+  const int tid = threadIdx.x;
+  const int d = a.d;
+  const float (&gw)[2] = f.gw, (&gp)[2] = f.gp, (&cs)[2] = f.cs, (&sn)[2] = f.sn;
   sq = wave_sum(sq);
   if ((tid & 63) == 0) red[tid >> 6] = sq;
   __syncthreads();
@@ -543,7 +553,7 @@ __global__ void __launch_bounds__(kThreads) emit_kernel(CompArgs a) {
   const int64_t i = p0 / r + blockIdx.x;              // candidate block
   if (p0 < 0 || (i + 1) * r - 1 >= p0 + a.T) return;  // not completed by this call
   const float sq = pool_block(a, b, p0, i, y);
-  finish_block(a, b, i, y, z, red, sq);
+  finish_block(a, b, i, y, z, red, sq, load_norm_rope(a, i));
 }
 
 // ------------------------------------------------------------------ state
@@ -625,14 +635,16 @@ __global__ void __launch_bounds__(kThreads) state_kernel(CompArgs a) {
 // registers, the others from the state), shift the current slots into the
 // previous ones (overlap) and finish the entry.
 // Single-token emit with overlap (ratio 4, 8 slots).  Everything this thread
-// needs -- the projection slices of the new token, all 4 slot-bias rows and
-// the 8 slots of its channels -- is loaded before the token's position is
-// known, so the whole load phase is one round of memory latency.
+// needs -- the projection slices of the new token, all 4 slot-bias rows, the
+// 8 slots of its channels, and the norm weights and rotation factors of the
+// block the token belongs to -- is loaded in one round, so the load phase is
+// one round of memory latency.
 __device__ void emit_t1_overlap(const CompArgs& a, int64_t b, int64_t p0, float* y, float* z,
                                 float* red) {
   const int r = 4, d = a.d, CD = a.CD, tid = threadIdx.x;
   const int N = 2 * CD;
   const int64_t sb = b * (int64_t)(2 * r) * CD;
+  const NormRope nr = load_norm_rope(a, p0 < 0 ? 0 : p0 / r);
   constexpr int kPer = 2;  // channels per thread (d <= 512 = 2 kThreads)
   float pv[kPer][2][kKSlices], ps[kPer][2][kKSlices];  // slices of v and score, halves 0/1
   float ap[kPer][2][4];                                 // slot bias rows 0..3
@@ -729,7 +741,7 @@ __device__ void emit_t1_overlap(const CompArgs& a, int64_t b, int64_t p0, float*
     sq = fmaf(C, C, sq);
   }
   if (!done) return;
-  finish_block(a, b, p0 / r, y, z, red, sq);
+  finish_block(a, b, p0 / r, y, z, red, sq, nr);
 }
 
 struct CompJobs {
@@ -849,7 +861,7 @@ __global__ void __launch_bounds__(kThreads) emit_t1_kernel(CompJobs jobs) {
     sq = fmaf(C, C, sq);
   }
   if (!done) return;
-  finish_block(a, b, i, y, z, red, sq);
+  finish_block(a, b, i, y, z, red, sq, load_norm_rope(a, i));
 }
 
 // ---- single-token calls of the 128-token (no overlap) compressor
@@ -953,7 +965,7 @@ __global__ void __launch_bounds__(kThreads) finish128_t1_kernel(CompJobs jobs,
     for (int q = 0; q < ns; ++q) sq += sqbuf[b * ns + q];
   }
   __syncthreads();
-  finish_block(a, b, p0 / a.ratio, y, z, red, sq);
+  finish_block(a, b, p0 / a.ratio, y, z, red, sq, load_norm_rope(a, p0 / a.ratio));
 }
 
 }  // namespace
