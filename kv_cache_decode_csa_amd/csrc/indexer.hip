@@ -120,13 +120,108 @@ __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
+// Scoring of one query row (the same for every kernel below): the query
+// fragments and head weights live in registers; score() takes the fragment
+// data of one step's tiles (get(nt, f)), forms the 16 heads x 16 keys MFMA
+// products of every head tile, applies ReLU and the head weights, adds up the
+// heads and records the step's scores.
+template <int HT, int KFMT>
+struct Scorer {
+  static constexpr int kTiles = tiles_per_iter<KFMT>();
+  uint4 qa[HT][4];  // A operand: head 16 mt + r16, dims 32 kq + 8 s .. +8
+  float wv[HT][4];  // head weights in the D layout: head 16 mt + 4 kq + r
+  int r16, kq;
+
+  __device__ __forceinline__ void load(const uint16_t* q_idx, const float* w_idx, int64_t row,
+                                       int lane) {
+    constexpr int Hi = HT * 16;
+    r16 = lane & 15;
+    kq = lane >> 4;
+    const uint16_t* qrow = q_idx + row * (int64_t)Hi * kIndexDim;
+#pragma unroll
+    for (int mt = 0; mt < HT; ++mt)
+#pragma unroll
+      for (int s = 0; s < 4; ++s)
+        qa[mt][s] = *(const uint4*)(qrow + (16 * mt + r16) * kIndexDim + 32 * kq + 8 * s);
+    const float* wrow = w_idx + row * (int64_t)Hi;
+#pragma unroll
+    for (int mt = 0; mt < HT; ++mt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) wv[mt][r] = wrow[16 * mt + 4 * kq + r];
+  }
+
+  // The HT head tiles are independent accumulation chains: they are issued
+  // round-robin so consecutive MFMAs do not wait on each other.
+  __device__ __forceinline__ void tile_mfma(const KeyRaw& f, f32x4_t (&acc)[HT]) const {
+    bf16x8_t kb[4];
+#pragma unroll
+    for (int s = 0; s < 4; ++s) kb[s] = key_frag<KFMT>(f, s);
+#pragma unroll
+    for (int mt = 0; mt < HT; ++mt) acc[mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+#pragma unroll
+      for (int mt = 0; mt < HT; ++mt) acc[mt] = mfma16x16x32(as_bf16x8(qa[mt][s]), kb[s], acc[mt]);
+  }
+
+  // Partial score of a lane: the sum over its 16 heads (4 per head tile),
+  // formed over 2 ReLU(x) = x + |x| (exact, and an abs is free on the adder);
+  // the total is halved at the end.  Scaling by two commutes with every
+  // rounding, so the result equals the plain sum of w_h ReLU(x_h) in the same
+  // order, while a max would need its input canonicalized first.
+  __device__ __forceinline__ float tile_partial(const f32x4_t (&acc)[HT]) const {
+    float p = 0.f;
+#pragma unroll
+    for (int mt = 0; mt < HT; ++mt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) p += wv[mt][r] * (acc[mt][r] + fabsf(acc[mt][r]));
+    return p;
+  }
+
+  // All tiles of a step (keys k .. k + 16 kTiles).  The four lane rows (kq)
+  // hold partials over different heads; row exchanges add them up so that row
+  // j ends with the scores of tile j (with two tiles, rows 2 and 3 repeat rows
+  // 0 and 1), and the step's scores below `end` are written and counted in one
+  // pass (only if `live`).
+  template <class Get>
+  __device__ __forceinline__ void score(int64_t k, bool live, int64_t end, Get&& get, float* srow,
+                                        uint32_t* hist) const {
+    float p[kTiles];
+#pragma unroll
+    for (int nt = 0; nt < kTiles; ++nt) {
+      KeyRaw f;
+      get(nt, f);
+      f32x4_t acc[HT];
+      tile_mfma(f, acc);
+      p[nt] = tile_partial(acc);
+    }
+    float a, c;
+    if (kTiles == 4) {
+      swap_rows16(p[0], p[1]);
+      swap_rows16(p[2], p[3]);
+      a = p[0] + p[1];
+      c = p[2] + p[3];
+    } else {
+      swap_rows16(p[0], p[1]);
+      a = p[0] + p[1];
+      c = a;
+    }
+    swap_halves32(a, c);
+    const float sc = 0.5f * (a + c);
+    const int64_t key = k + 16 * kq + r16;
+    if (live && (kTiles == 4 || kq < kTiles) && key < end) {
+      srow[key] = sc;
+      atomicAdd(&hist[score_key(sc) >> 20], 1u);
+    }
+  }
+};
+
 template <int HT, int KFMT>
 __global__ void __launch_bounds__(kIdxThreads) index_scores_mfma(
     const uint16_t* __restrict__ q_idx, const float* __restrict__ w_idx,
     const uint8_t* __restrict__ k_idx, const int32_t* __restrict__ pos, int ratio, int Q,
     int64_t Nmax, int64_t row_off, float* __restrict__ scores,
     int32_t* __restrict__ n_vis_out, uint32_t* __restrict__ hist_g) {
-  constexpr int Hi = HT * 16;
   constexpr int64_t kRowBytes = KFMT == CSA_FP8_MX32 ? 132 : 256;
   constexpr int kTilesPerIter = tiles_per_iter<KFMT>();
   constexpr int kKeysPerIter = 16 * kTilesPerIter;
@@ -150,23 +245,9 @@ __global__ void __launch_bounds__(kIdxThreads) index_scores_mfma(
 
   for (int i = t; i < kHistBins; i += kIdxThreads) hist[i] = 0;
 
-  const int r16 = lane & 15;
-  const int kq = lane >> 4;
-  // query fragments (A operand): head 16 mt + r16, dims 32 kq + 8 s .. +8
-  uint4 qa[HT][4];
-  const uint16_t* qrow = q_idx + row * (int64_t)Hi * kIndexDim;
-#pragma unroll
-  for (int mt = 0; mt < HT; ++mt)
-#pragma unroll
-    for (int s = 0; s < 4; ++s)
-      qa[mt][s] = *(const uint4*)(qrow + (16 * mt + r16) * kIndexDim + 32 * kq + 8 * s);
-  // head weights in the D layout: head 16 mt + 4 kq + r
-  float wv[HT][4];
-  const float* wrow = w_idx + row * (int64_t)Hi;
-#pragma unroll
-  for (int mt = 0; mt < HT; ++mt)
-#pragma unroll
-    for (int r = 0; r < 4; ++r) wv[mt][r] = wrow[16 * mt + 4 * kq + r];
+  Scorer<HT, KFMT> sc;
+  sc.load(q_idx, w_idx, row, lane);
+  const int r16 = sc.r16, kq = sc.kq;
   __syncthreads();
 
   const uint8_t* kbase = k_idx + b * Nmax * kRowBytes;
@@ -180,68 +261,8 @@ __global__ void __launch_bounds__(kIdxThreads) index_scores_mfma(
   // read key by key with the index clamped to end - 1.
   const int64_t stride = G * 4 * (int64_t)kKeysPerIter;
   const int64_t k0 = ((int64_t)blockIdx.x * 4 + wave) * kKeysPerIter;
-  // Scoring is split in two so that the MFMAs of one tile can be issued
-  // before the partial sums of the previous one: tile_mfma forms the 16 heads
-  // x 16 keys products of every head tile, tile_partial applies ReLU and the
-  // head weights over the lane's heads.
-  auto tile_mfma = [&](const KeyRaw& f, f32x4_t (&acc)[HT]) __attribute__((always_inline)) {
-    bf16x8_t kb[4];
-#pragma unroll
-    for (int s = 0; s < 4; ++s) kb[s] = key_frag<KFMT>(f, s);
-    // the HT head tiles are independent accumulation chains: issue them
-    // round-robin so consecutive MFMAs do not wait on each other
-#pragma unroll
-    for (int mt = 0; mt < HT; ++mt) acc[mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int s = 0; s < 4; ++s)
-#pragma unroll
-      for (int mt = 0; mt < HT; ++mt) acc[mt] = mfma16x16x32(as_bf16x8(qa[mt][s]), kb[s], acc[mt]);
-  };
-  // Partial score of a lane: the sum over its 16 heads (4 per head tile),
-  // formed over 2 ReLU(x) = x + |x| (exact, and an abs is free on the adder);
-  // the total is halved at the end.  Scaling by two commutes with every
-  // rounding, so the result equals the plain sum of w_h ReLU(x_h) in the same
-  // order, while a max would need its input canonicalized first.
-  auto tile_partial = [&](const f32x4_t (&acc)[HT]) __attribute__((always_inline)) {
-    float p = 0.f;
-#pragma unroll
-    for (int mt = 0; mt < HT; ++mt)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) p += wv[mt][r] * (acc[mt][r] + fabsf(acc[mt][r]));
-    return p;
-  };
-  // All tiles of a step, the MFMAs of tile nt + 1 ahead of the partial sums
-  // of tile nt.  The four lane rows (kq) hold partials over different heads;
-  // row exchanges add them up so that row j ends with the scores of tile j
-  // (with two tiles, rows 2 and 3 repeat rows 0 and 1), and the step's scores
-  // are written and counted in one pass.
   auto score_tiles = [&](int64_t k, const KeyRaw (&f)[kTilesPerIter]) __attribute__((always_inline)) {
-    f32x4_t acc[2][HT];
-    float p[kTilesPerIter];
-    tile_mfma(f[0], acc[0]);
-#pragma unroll
-    for (int nt = 0; nt < kTilesPerIter; ++nt) {
-      if (nt + 1 < kTilesPerIter) tile_mfma(f[nt + 1], acc[(nt + 1) & 1]);
-      p[nt] = tile_partial(acc[nt & 1]);
-    }
-    float a, c;
-    if (kTilesPerIter == 4) {
-      swap_rows16(p[0], p[1]);
-      swap_rows16(p[2], p[3]);
-      a = p[0] + p[1];
-      c = p[2] + p[3];
-    } else {
-      swap_rows16(p[0], p[1]);
-      a = p[0] + p[1];
-      c = a;
-    }
-    swap_halves32(a, c);
-    const float sc = 0.5f * (a + c);
-    const int64_t key = k + 16 * kq + r16;
-    if ((kTilesPerIter == 4 || kq < kTilesPerIter) && key < end) {
-      srow[key] = sc;
-      atomicAdd(&hist[score_key(sc) >> 20], 1u);
-    }
+    sc.score(k, true, end, [&](int nt, KeyRaw& g) { g = f[nt]; }, srow, hist);
   };
 
   int64_t n_full = end - k0 >= kKeysPerIter ? (end - k0 - kKeysPerIter) / stride + 1 : 0;
@@ -307,6 +328,117 @@ __global__ void __launch_bounds__(kIdxThreads) index_scores_mfma(
     if (hist[i]) atomicAdd(&g[i], hist[i]);
 }
 
+// FP8 keys, producer/consumer form.  A work-group of 8 waves takes steps of
+// 256 keys: the G work-groups of a row sweep it together, step i of
+// work-group x covering keys [(i G + x) 256, +256).  Waves 4..7 only load:
+// loader j keeps kSplitDepth steps of its 64-key quarter in flight in
+// registers (the same contiguous stream as above, pieces clamped into the
+// visible rows) and copies the oldest one into a double-buffered LDS region.
+// Waves 0..3 only score: scorer j scores quarter j of the step in LDS.  One
+// work-group barrier per step hands a buffer from the loaders to the scorers
+// and back, so the loads never wait for the scoring.  Every wave runs the
+// same number of steps, rounded up to a multiple of kSplitDepth; steps past
+// the work-group's last one read the row's first keys (in L2 after the first
+// read) and are scored but not recorded.  With about one work-group per CU,
+// two register sets per loader measured fastest: four or six put more
+// requests in flight and made the scan slower, and half the work-groups
+// made it slower too.
+constexpr int kSplitThreads = 512;
+constexpr int kSplitStep = 256;   // keys per work-group step
+constexpr int kSplitDepth = 2;    // loader register sets (even)
+constexpr int64_t kSplitTargetWgs = 256;
+
+template <int HT>
+__global__ void __launch_bounds__(kSplitThreads) index_scores_split(
+    const uint16_t* __restrict__ q_idx, const float* __restrict__ w_idx,
+    const uint8_t* __restrict__ k_idx, const int32_t* __restrict__ pos, int ratio, int Q,
+    int64_t Nmax, int64_t row_off, float* __restrict__ scores,
+    int32_t* __restrict__ n_vis_out, uint32_t* __restrict__ hist_g) {
+  constexpr int KFMT = CSA_FP8_MX32;
+  constexpr int64_t kRowBytes = 132;
+  constexpr int kSub = kSplitStep / 4;                 // keys per quarter (one wave)
+  static_assert(kSub == 16 * tiles_per_iter<KFMT>(), "a quarter is one scorer step");
+  constexpr int kPieces = kSub * (int)kRowBytes / 16;  // 528 pieces of 16 B
+  constexpr int kLoads = (kPieces + 63) / 64;          // 9 per lane
+  static_assert(kSplitDepth % 2 == 0, "buffer parity follows the step");
+  __shared__ uint32_t hist[kHistBins];
+  __shared__ u32x4_t buf[2][4][kLoads * 64];
+
+  const int t = threadIdx.x;
+  const int lane = t & 63;
+  const int wave = t >> 6;
+  const int j = wave & 3;          // quarter of the step
+  const bool loader = wave >= 4;
+  const int64_t row = row_off + blockIdx.y;
+  const int64_t b = row / Q;
+  int64_t nv = ((int64_t)pos[row] + 1) / ratio;
+  nv = nv < 0 ? 0 : (nv > Nmax ? Nmax : nv);
+  if (blockIdx.x == 0 && t == 0) n_vis_out[row] = (int32_t)nv;
+  const int64_t G = gridDim.x;
+  const int64_t x0 = (int64_t)blockIdx.x * kSplitStep;
+  if (x0 >= nv) return;
+  const int64_t n_steps = (nv - x0 + G * kSplitStep - 1) / (G * kSplitStep);
+  const int64_t n_iter = (n_steps + kSplitDepth - 1) / kSplitDepth * kSplitDepth;
+  const uint8_t* kbase = k_idx + b * Nmax * kRowBytes;
+  const int64_t end = nv;
+
+  for (int i = t; i < kHistBins; i += kSplitThreads) hist[i] = 0;
+  __syncthreads();
+
+  if (loader) {
+    // the quarter's stream of step i, clamped to whole visible rows
+    auto gload = [&](int64_t i, U4Array<kLoads>& v) __attribute__((always_inline)) {
+      int64_t k = (i * G + blockIdx.x) * kSplitStep + kSub * j;
+      if (i >= n_steps || k >= end) k = 0;
+      const int64_t nk = end - k < kSub ? end - k : kSub;
+      const int last = (int)((nk * kRowBytes - 1) / 16);
+      const u32x4_t* src = (const u32x4_t*)(kbase + k * kRowBytes);
+#pragma unroll
+      for (int l = 0; l < kLoads; ++l) {
+        const int piece = lane + 64 * l;
+        v.v[l] = src[piece < last ? piece : last];
+      }
+    };
+    auto stage = [&](int bi, const U4Array<kLoads>& v) __attribute__((always_inline)) {
+      u32x4_t* st = buf[bi][j];
+#pragma unroll
+      for (int l = 0; l < kLoads; ++l) st[lane + 64 * l] = v.v[l];
+    };
+    U4Array<kLoads> r[kSplitDepth];
+#pragma unroll
+    for (int u = 0; u < kSplitDepth; ++u) gload(u, r[u]);
+    stage(0, r[0]);
+    __syncthreads();
+    for (int64_t k = 0; k < n_iter; k += kSplitDepth) {
+#pragma unroll
+      for (int u = 0; u < kSplitDepth; ++u) {
+        // r[u] held step k + u, staged before the previous barrier: refill it
+        // with step k + u + kSplitDepth, and stage step k + u + 1 (buffer
+        // parity (u + 1) & 1, as k is even) before the barrier ending step k + u
+        gload(k + u + kSplitDepth, r[u]);
+        stage((u + 1) & 1, r[(u + 1) % kSplitDepth]);
+        __syncthreads();
+      }
+    }
+  } else {
+    Scorer<HT, KFMT> sc;
+    sc.load(q_idx, w_idx, row, lane);
+    float* srow = scores + row * Nmax;
+    __syncthreads();
+    for (int64_t k = 0; k < n_iter; ++k) {
+      const u32x4_t* st = buf[k & 1][j];
+      sc.score((k * G + blockIdx.x) * kSplitStep + kSub * j, k < n_steps, end,
+               [&](int nt, KeyRaw& f) { stage_read<KFMT>(st, 16 * nt + sc.r16, sc.kq, f); },
+               srow, hist);
+      __syncthreads();
+    }
+  }
+  __syncthreads();
+  uint32_t* g = hist_g + row * kHistBins;
+  for (int i = t; i < kHistBins; i += kSplitThreads)
+    if (hist[i]) atomicAdd(&g[i], hist[i]);
+}
+
 // float32 path: one thread per key, q in LDS.
 constexpr int kF32Keys = 256;
 __global__ void __launch_bounds__(kIdxThreads) index_scores_f32(
@@ -355,6 +487,20 @@ template <int HT>
 hipError_t launch_mfma(const void* q_idx, const float* w_idx, const void* k_idx, int k_fmt,
                        const int32_t* pos, int ratio, int Q, int64_t R, int64_t Nmax,
                        float* scores, int32_t* n_vis, uint32_t* hist, hipStream_t s) {
+  if (k_fmt == CSA_FP8_MX32) {
+    // about one work-group per CU in all, at least one step each
+    int64_t gx = (kSplitTargetWgs + R - 1) / R;
+    const int64_t steps = (Nmax + kSplitStep - 1) / kSplitStep;
+    gx = gx < steps ? gx : steps;
+    gx = gx < 1 ? 1 : gx;
+    for (int64_t r0 = 0; r0 < R; r0 += 65535) {
+      int64_t nr = R - r0 < 65535 ? R - r0 : 65535;
+      hipLaunchKernelGGL((index_scores_split<HT>), dim3((unsigned)gx, (unsigned)nr),
+                         dim3(kSplitThreads), 0, s, (const uint16_t*)q_idx, w_idx,
+                         (const uint8_t*)k_idx, pos, ratio, Q, Nmax, r0, scores, n_vis, hist);
+    }
+    return hipGetLastError();
+  }
   int kpw = kMaxKeysPerWg;
   while (kpw > kMinKeysPerWg && R * ((Nmax + kpw - 1) / kpw) < kTargetWgs) kpw >>= 1;
   const int64_t gx = (Nmax + kpw - 1) / kpw;
