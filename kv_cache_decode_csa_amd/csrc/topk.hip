@@ -451,7 +451,10 @@ struct RowInfo {       // written by work-group 0 of each row's collect pass
 // row histogram, then this chunk's entries above the bin go to the row's hi
 // list and those inside it to the candidate list.  Each thread keeps its keys
 // in registers, a block-wide prefix gives every entry its slot, and one
-// 64-bit atomic per work-group reserves its ranges in both lists.
+// 64-bit atomic per work-group reserves its ranges in both lists.  CH
+// scores per work-group (8192, or fewer when the rows are few and short, so
+// that the pass still spreads over the CUs).
+template <int CH>
 __global__ void __launch_bounds__(kSelThreads) topk_collect_kernel(
     const float* __restrict__ scores, const int32_t* __restrict__ n_valid, int64_t ld, int topk,
     const uint32_t* hist_g, RowInfo* info_g, uint32_t* cand_g, uint32_t* hi_g) {
@@ -463,20 +466,20 @@ __global__ void __launch_bounds__(kSelThreads) topk_collect_kernel(
   nv64 = nv64 < 0 ? 0 : (nv64 > ld ? ld : nv64);
   const uint32_t nv = (uint32_t)nv64;
   const uint32_t k_eff = nv < (uint32_t)topk ? nv : (uint32_t)topk;
-  const uint32_t nchunks = (nv + kChunk - 1) / kChunk;
+  const uint32_t nchunks = (nv + CH - 1) / CH;
   if (k_eff == 0 || blockIdx.x >= nchunks) return;
   RowInfo* info = info_g + row;
   uint32_t* cand = cand_g + row * (int64_t)kCandCap * 2;
   uint32_t* hi = hi_g + row * (int64_t)kTopkMax * 2;
   const float* s = scores + row * ld;
 
-  const uint32_t base = blockIdx.x * (uint32_t)kChunk;
-  const uint32_t end = base + kChunk < nv ? base + kChunk : nv;
-  constexpr int kPer = kChunk / kSelThreads;
+  const uint32_t base = blockIdx.x * (uint32_t)CH;
+  const uint32_t end = base + CH < nv ? base + CH : nv;
+  constexpr int kPer = CH / kSelThreads;
   // element of (thread t, slot j): base + 4 (t + 256 (j / 4)) + j % 4, read as
   // float4 (scores first: their latency overlaps the histogram's)
   uint32_t kk[kPer];
-  const bool full = base + kChunk <= nv && (ld & 3) == 0;
+  const bool full = base + CH <= nv && (ld & 3) == 0;
   if (full) {
 #pragma unroll
     for (int q = 0; q < kPer / 4; ++q) {
@@ -765,13 +768,22 @@ hipError_t launch_topk_hist(const float* scores, const int32_t* n_valid, int64_t
 hipError_t launch_topk_select(const float* scores, const int32_t* n_valid, int64_t R, int64_t ld,
                               int topk, int32_t* out_idx, TopkWs w, hipStream_t s) {
   static_assert(sizeof(RowInfo) <= 32, "row info slot");
-  int64_t gx = (ld + kChunk - 1) / kChunk;
+  // at least kCollectWgs work-groups where the rows allow it
+  constexpr int64_t kCollectWgs = 256;
+  int ch = kChunk;
+  while (ch > kChunk / 4 && R * ((ld + ch - 1) / ch) < kCollectWgs) ch >>= 1;
+  const int64_t gx = (ld + ch - 1) / ch;
   for (int64_t r0 = 0; r0 < R; r0 += 65535) {
     int64_t nr = R - r0 < 65535 ? R - r0 : 65535;
-    hipLaunchKernelGGL(topk_collect_kernel, dim3((unsigned)gx, (unsigned)nr), dim3(kSelThreads), 0,
-                       s, scores + r0 * ld, n_valid + r0, ld, topk, w.hist + r0 * kHistBins,
-                       (RowInfo*)w.ctr + r0, w.cand + r0 * (int64_t)kCandCap * 2,
-                       w.hi + r0 * (int64_t)kTopkMax * 2);
+    const dim3 grid((unsigned)gx, (unsigned)nr);
+    auto args = [&](auto kern) {
+      hipLaunchKernelGGL(kern, grid, dim3(kSelThreads), 0, s, scores + r0 * ld, n_valid + r0, ld,
+                         topk, w.hist + r0 * kHistBins, (RowInfo*)w.ctr + r0,
+                         w.cand + r0 * (int64_t)kCandCap * 2, w.hi + r0 * (int64_t)kTopkMax * 2);
+    };
+    if (ch == kChunk) args(topk_collect_kernel<kChunk>);
+    else if (ch == kChunk / 2) args(topk_collect_kernel<kChunk / 2>);
+    else args(topk_collect_kernel<kChunk / 4>);
   }
   for (int64_t r0 = 0; r0 < R; r0 += 65535) {
     int64_t nr = R - r0 < 65535 ? R - r0 : 65535;
