@@ -21,7 +21,8 @@ pytestmark = pytest.mark.gpu
 
 @pytest.mark.parametrize("kfmt,Hi,N", [("bf16", 32, 3000), ("bf16", 64, 3000),
                                         ("fp8_mx32", 32, 3000), ("fp8_mx32", 64, 3000),
-                                        ("fp8_mx32", 64, 3001), ("bf16", 16, 1029)])
+                                        ("fp8_mx32", 64, 3001), ("bf16", 16, 1029),
+                                        ("fp8_mx32", 16, 1029), ("fp8_mx32", 48, 2000)])
 def test_scores_and_topk(kfmt, Hi, N):
     """Several work-groups per row, partial last steps, n_vis clamping; N = 3001
     puts the per-sequence key bases off 16-byte alignment (132-B rows)."""
@@ -74,8 +75,10 @@ def test_without_score_output_matches():
     assert torch.equal(o1, o2)
 
 
-def test_batch_invariance():
-    """A sequence's selection and scores do not depend on its batch neighbours."""
+@pytest.mark.parametrize("kfmt", ["bf16", "fp8_mx32"])
+def test_batch_invariance(kfmt):
+    """A sequence's selection and scores do not depend on its batch neighbours
+    (the work-group split of a row depends on the batch)."""
     need_gpu()
     B, N, Hi, k = 5, 4000, 64, 512
     rng = np.random.default_rng(5)
@@ -88,8 +91,8 @@ def test_batch_invariance():
         ws = _lib.workspace(_lib.csa_index_topk_workspace_size(len(bs), 1, N, k))
         o = torch.empty((len(bs), 1, k), dtype=torch.int32, device="cuda")
         sc = torch.empty((len(bs), 1, N), dtype=torch.float32, device="cuda")
-        _lib.csa_index_topk(bf16(qi[bs]), "bf16", f32(wi[bs]), bf16(K[bs]), "bf16", i32(pos[bs]), 4,
-                            len(bs), 1, Hi, N, k, o, sc, ws)
+        _lib.csa_index_topk(bf16(qi[bs]), "bf16", f32(wi[bs]), upload_rows(K[bs], kfmt), kfmt,
+                            i32(pos[bs]), 4, len(bs), 1, Hi, N, k, o, sc, ws)
         res.append((o.cpu().numpy(), sc.cpu().numpy()))
     assert np.array_equal(res[0][0][2], res[1][0][0])
     assert np.array_equal(res[0][1][2], res[1][1][0])
