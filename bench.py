@@ -15,7 +15,13 @@ HIP events on the stream it runs on.  cpu_baseline times the float64 oracle
 (test infrastructure) on a bounded sample of the same workload.
 
   python bench.py [--steps K] [--warmup W] [--workload csa_1m_fp8|csa_1m_mxfp4|
-                  csa_64k_bf16|hca_1m_bf16] [--copies C] [--no-cpu-baseline]
+                  csa_64k_bf16|hca_1m_bf16|csa_prefill_32k_bf16] [--copies C]
+                  [--no-cpu-baseline]
+
+The chunked-prefill workload (32,768 new tokens on a 262,144-token prefix,
+batch 1) reports prefill tokens/s per layer; its roofline object is the
+indexer's MFMA rate (bf16 TFLOP/s of the heads x 128 x visible-keys
+contraction) during csa_index_topk.
   python bench.py --copy-calibration     # known-size copy for HBM byte counters
 """
 
@@ -30,8 +36,10 @@ import time
 import numpy as np
 
 HBM_PEAK_GBS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0
 
-WORKLOADS = {"csa_1m_fp8": 5, "csa_1m_mxfp4": 5, "csa_64k_bf16": 2, "hca_1m_bf16": 3}
+WORKLOADS = {"csa_1m_fp8": 5, "csa_1m_mxfp4": 5, "csa_64k_bf16": 2, "hca_1m_bf16": 3,
+             "csa_prefill_32k_bf16": 4}
 
 
 def row_bytes(fmt, dim):
@@ -67,6 +75,65 @@ def algorithmic_bytes(w):
                                       + 128 * row_bytes(w.win_fmt, 512)
                                       + 2 * w.H * 512 * qb) + w.H * 4
     return out
+
+
+def prefill_flops(w):
+    """Dense-contraction FLOPs of one prefill chunk, by phase (2 per MAC).
+    Indexer: every query scores its visible keys with Hi heads x 128 dims.
+    Attention: 64 heads x (q.c and p.c over 512 dims) per list row (window +
+    top-k).  Compressors: x times both projections of both compressors."""
+    from kv_cache_decode_csa_amd import synth
+    P, T, N0, N = synth.prefill_shape(w)
+    vis = sum(min((P + i + 1) // w.ratio, N) for i in range(T))
+    return {"csa_compress": 2.0 * T * w.dim * 2 * (2 * 512 + 2 * 128),
+            "csa_index_topk": 2.0 * vis * w.Hi * 128,
+            "csa_sparse_attn_decode": 2.0 * 2 * T * w.H * 512 * (128 + w.topk)}
+
+
+def cpu_baseline_prefill(w, n_q=64, n_tok=1024):
+    """The oracle on a bounded sample of the prefill chunk: the bulk
+    compressor (both compressors) over n_tok tokens, and n_q sampled queries
+    (scoring over every visible key, top-k, gather and attention).  Per-token
+    cost = compressor time per token + query time per query; value = 1 / that."""
+    from kv_cache_decode_csa_amd import synth
+    from oracle import attention, compressor, indexer, rope
+    from oracle import topk as TK
+    om = rope.frequencies(160000.0, rope.V4_YARN if w.yarn else None)
+    threads = os.environ.get("OMP_NUM_THREADS") or str(len(os.sched_getaffinity(0)))
+    P, T, N0, N = synth.prefill_shape(w)
+    x = synth.prefill_hidden(w, 0, n_tok).astype(np.float64)
+    t0 = time.perf_counter()
+    for d, idx in ((512, False), (128, True)):
+        wkv, wg, ape, norm = synth.compressor_weights(w, d, 4, indexer=idx)
+        compressor.compress_bulk(x, P, wkv, wg, ape, norm, om, 4, d, rotate=idx)
+    t_comp = (time.perf_counter() - t0) / n_tok
+    keys = np.concatenate([synth.prefill_index_keys(w, 0, N0),
+                           synth.prefill_index_keys(w, 0, N - N0)]).astype(np.float64)
+    ent = synth.prefill_entries(w, 0, N0).astype(np.float64)
+    sink = synth.prefill_sink(w)
+    rng = np.random.default_rng(5)
+    qs = rng.choice(T, n_q, replace=False)
+    t_q = 0.0
+    for i in qs:
+        q = synth.prefill_queries(w, i, i + 1)[0].astype(np.float64)
+        qi, wi = synth.prefill_index_queries(w, i, i + 1)
+        win = synth.prefill_window(w, i, i + 128).astype(np.float64)
+        t0 = time.perf_counter()
+        nv = int(indexer.n_visible(P + i, 4, N))
+        S = indexer.scores(qi[0].astype(np.float64), wi[0], keys, nv)
+        ids = TK.topk(S.astype(np.float32), w.topk, nv)
+        rows = ent[np.minimum(np.maximum(ids, 0), N0 - 1)]
+        attention.attend(q, np.concatenate([win, rows]),
+                         np.concatenate([np.ones(128, bool), ids >= 0]), sink, 512 ** -0.5,
+                         P + i, om)
+        t_q += time.perf_counter() - t0
+    per_tok = t_comp + t_q / n_q
+    return {"value": 1.0 / per_tok, "unit": "prefill tokens/s/layer", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"bulk compressor (main + index) over {n_tok} of {T} new tokens "
+                      f"({t_comp * n_tok:.1f} s) plus {n_q} of {T} queries (scoring over all "
+                      f"visible keys, top-k, attention; {t_q:.1f} s) in float64 NumPy, "
+                      f"extrapolated per token"}
 
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
@@ -215,6 +282,8 @@ def main():
     from kv_cache_decode_csa_amd import decode, synth
 
     w = synth.WORKLOADS[WORKLOADS[a.workload]]
+    if a.workload == "csa_prefill_32k_bf16":
+        return main_prefill(a, w, torch)
     if a.workload == "csa_1m_mxfp4":
         w = synth.mxfp4_variant(w)
     print(f"# building {a.workload}: B={w.B} ctx={w.ctx} entries={w.n_entries}", file=sys.stderr,
@@ -261,6 +330,46 @@ def main():
     if not a.no_cpu_baseline:
         print("# cpu baseline (oracle)", file=sys.stderr, flush=True)
         res["cpu_baseline"] = cpu_baseline(w, a.cpu_seqs)
+    print(json.dumps(res), flush=True)
+
+
+def main_prefill(a, w, torch):
+    from kv_cache_decode_csa_amd import prefill, synth
+    P, T, N0, N = synth.prefill_shape(w)
+    print(f"# building {a.workload}: {T} new tokens on a {P}-token prefix", file=sys.stderr,
+          flush=True)
+    t0 = time.time()
+    layer = prefill.CsaPrefillChunk(w)
+    torch.cuda.synchronize()
+    print(f"# inputs resident in {time.time() - t0:.1f} s", file=sys.stderr, flush=True)
+    for _ in range(a.warmup):
+        layer.step()
+    ms = time_steps(layer, a.steps, torch)
+    phases = time_phases(layer, a.steps, torch)
+    fl = prefill_flops(w)
+    dom = "csa_index_topk"
+    tf = fl[dom] / (phases[dom] * 1e-3) / 1e12
+    res = {
+        "metric": "CSA chunked-prefill tokens/s per layer (32K new tokens on a 256K prefix); "
+                  "indexer MFMA TFLOP/s vs peak",
+        "value": T / (ms * 1e-3),
+        "unit": "prefill tokens/s/layer",
+        "n_gpus": 1, "steps": a.steps, "warmup": a.warmup, "ms_per_step": ms,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": w.name, "batch": 1, "prefix": P, "new_tokens": T,
+                   "entries_after": N, "heads": w.H, "index_heads": w.Hi, "topk": w.topk,
+                   "ratio": w.ratio, "kv_format": "bf16", "window": "linear"},
+        "roofline": {"bound": "mfma", "achieved": tf, "peak": MFMA_BF16_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": tf / MFMA_BF16_PEAK_TFLOPS, "traffic": None,
+                     "kernel": dom, "flops_per_launch": fl[dom], "ms_per_launch": phases[dom]},
+        "phases_ms": phases,
+        "phase_tflops": {k: fl[k] / (phases[k] * 1e-3) / 1e12 for k in fl},
+        "flops": fl,
+    }
+    if not a.no_cpu_baseline:
+        print("# cpu baseline (oracle)", file=sys.stderr, flush=True)
+        res["cpu_baseline"] = cpu_baseline_prefill(w)
     print(json.dumps(res), flush=True)
 
 

@@ -187,3 +187,103 @@ def random_scores(seed, n, idx=0, ties=True):
         s[z[:2]] = np.float32(0.0)
         s[z[2:]] = np.float32(-0.0)
     return s
+
+
+# ----------------------------------------------------------------------------
+# chunked prefill (workload 4): one sequence, many rows per tensor.  Rows come
+# in blocks of PREFILL_BLOCK, each block from its own stream (seed, tid, block),
+# so a sampled query, token or cache row is regenerated without the rest.
+# ----------------------------------------------------------------------------
+
+PREFILL_BLOCK = 256
+
+
+def _bf16_round_finite(x):
+    """In-place bf16 RNE of finite float32 values (same result as bf16_round;
+    32-bit arithmetic cannot overflow below the NaN/Inf patterns)."""
+    u = x.reshape(-1).view(np.uint32)
+    r = (u >> 16) & 1
+    r += 0x7FFF
+    u += r
+    u &= np.uint32(0xFFFF0000)
+    return x
+
+
+def blocked_normal(seed, tid, row_shape, lo, hi, std=1.0, threads=8, bf16=False):
+    """Rows [lo, hi) of a float32 N(0, std^2) tensor [*, *row_shape] whose
+    block j of PREFILL_BLOCK rows is drawn from stream (seed, tid, j); with
+    bf16=True each value is then rounded to the nearest bf16 (ties to even)."""
+    import concurrent.futures as cf
+    n = hi - lo
+    out = np.empty((n,) + tuple(row_shape), dtype=np.float32)
+    if n <= 0:
+        return out
+    B = PREFILL_BLOCK
+    blocks = range(lo // B, (hi - 1) // B + 1)
+
+    def fill(j):
+        blk = normal(seed, tid, (B,) + tuple(row_shape), std, idx=j)
+        if bf16:
+            _bf16_round_finite(blk)
+        a, b = max(lo, j * B), min(hi, (j + 1) * B)
+        out[a - lo:b - lo] = blk[a - j * B:b - j * B]
+
+    if len(blocks) == 1 or threads <= 1:
+        for j in blocks:
+            fill(j)
+    else:
+        with cf.ThreadPoolExecutor(max_workers=threads) as ex:
+            list(ex.map(fill, blocks))
+    return out
+
+
+def prefill_shape(w):
+    """(prefix tokens P, new tokens T, existing entries N0, entries after the chunk N)."""
+    P, T = w.extra["prefix"], w.extra["new"]
+    return P, T, P // w.ratio, (P + T) // w.ratio
+
+
+def prefill_rows(w, tid, row_shape, lo, hi, std=1.0):
+    """Rows [lo, hi) of a prefill tensor in its stored values (bf16-rounded)."""
+    return blocked_normal(w.seed, tid, row_shape, lo, hi, std, bf16=w.q_fmt == "bf16")
+
+
+def prefill_queries(w, lo, hi):
+    """q [hi - lo, H, 512] of new tokens lo .. hi-1 (query i sits at P + i)."""
+    return prefill_rows(w, T_Q, (w.H, 512), lo, hi)
+
+
+def prefill_index_queries(w, lo, hi):
+    """q_idx [hi - lo, Hi, 128] and head weights [hi - lo, Hi] (pre-scaled)."""
+    qi = prefill_rows(w, T_QIDX, (w.Hi, 128), lo, hi)
+    wi = blocked_normal(w.seed, T_WIDX, (w.Hi,), lo, hi, (128 * w.Hi) ** -0.5)
+    return qi, wi
+
+
+def prefill_hidden(w, lo, hi):
+    """Hidden states [hi - lo, dim] of new tokens lo .. hi-1."""
+    return prefill_rows(w, T_X, (w.dim,), lo, hi)
+
+
+def prefill_tail(w):
+    """Hidden states [4, dim] of the prefix's last block (positions P-4 .. P-1)."""
+    return as_fmt_values(normal(w.seed, T_XTAIL, (4, w.dim)), w.q_fmt)
+
+
+def prefill_window(w, lo, hi):
+    """Raw window KV rows [hi - lo, 512]; row r holds position P - 127 + r."""
+    return prefill_rows(w, T_WINDOW, (512,), lo, hi)
+
+
+def prefill_entries(w, lo, hi):
+    """Existing compressed entries [hi - lo, 512] of the prefix (ids lo .. hi-1 < N0)."""
+    return prefill_rows(w, T_ENTRIES, (512,), lo, hi)
+
+
+def prefill_index_keys(w, lo, hi):
+    """Existing index keys [hi - lo, 128] of the prefix."""
+    return prefill_rows(w, T_IKEYS, (128,), lo, hi)
+
+
+def prefill_sink(w):
+    return normal(w.seed, T_SINK, (w.H,))
