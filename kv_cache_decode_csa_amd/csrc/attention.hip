@@ -31,6 +31,13 @@ namespace {
 constexpr int kAttnThreads = 256;
 constexpr int kTile = 32;             // rows per tile
 constexpr int kChunkCsa = 64;         // rows per work-group, top-k lists
+// With many queries per sequence (chunked prefill) there are enough (query,
+// head group) units to fill the chip without splitting a list: a work-group
+// then takes 640 rows -- the whole window + top-512 list -- and finishes the
+// output itself, with no partials to write and merge.  The choice depends on
+// the number of queries per sequence only, never on the batch.
+constexpr int kChunkCsaLong = 640;
+constexpr int kLongChunkMinQ = 16;
 constexpr int kChunkHca = 1024;       // rows per work-group, dense lists
 constexpr float kLog2e = 1.4426950408889634f;
 
@@ -626,12 +633,15 @@ __device__ __forceinline__ AttnItem attn_item(const AttnArgs& a, int nchunks, in
   return it;
 }
 
-template <int WF, int EF>
+// LONG: chunks of kChunkCsaLong rows, whose top-k ids are staged in LDS
+// (otherwise chunks of kChunkCsa rows, ids held in registers).
+template <int WF, int EF, bool LONG>
 __global__ void __launch_bounds__(kAttnThreads) attn_mfma_kernel(AttnArgs a, int chunk_rows,
                                                                  int nchunks, int64_t units,
                                                                  Partial* part) {
   __shared__ uint16_t Rl[4][kTile * kRPitch];
   __shared__ float4 Sp[4][2][64];
+  __shared__ int32_t Ids[LONG ? kChunkCsaLong : 1];
 
   const AttnItem it = attn_item(a, nchunks, units);
   if (!it.live) return;
@@ -653,13 +663,22 @@ __global__ void __launch_bounds__(kAttnThreads) attn_mfma_kernel(AttnArgs a, int
   const int rr = rope_row(a, t);
   const float zscale = a.scale * kLog2e;
 
-  // top-k ids of this chunk, fetched once: lane holds rows j_begin + 16 i + r16
-  int32_t ids[kMaxIdsPerLane];
+  // top-k ids of this chunk, fetched once: in registers (lane holds rows
+  // j_begin + 16 i + r16), or for long chunks in LDS (slot j - j_begin)
+  int32_t ids[LONG ? 1 : kMaxIdsPerLane];
   if (!a.dense) {
+    if (LONG) {
+      for (int i = tid; i < kChunkCsaLong; i += kAttnThreads) {
+        const int64_t jj = j_begin + i;
+        Ids[i] = (jj >= kWindow && jj < j_end) ? a.topk_idx[unit * a.topk + (jj - kWindow)] : -1;
+      }
+      __syncthreads();
+    } else {
 #pragma unroll
-    for (int i = 0; i < kMaxIdsPerLane; ++i) {
-      const int64_t jj = j_begin + 16 * i + r16;
-      ids[i] = (jj >= kWindow && jj < j_end) ? a.topk_idx[unit * a.topk + (jj - kWindow)] : -1;
+      for (int i = 0; i < kMaxIdsPerLane; ++i) {
+        const int64_t jj = j_begin + 16 * i + r16;
+        ids[i] = (jj >= kWindow && jj < j_end) ? a.topk_idx[unit * a.topk + (jj - kWindow)] : -1;
+      }
     }
   }
 
@@ -696,12 +715,16 @@ __global__ void __launch_bounds__(kAttnThreads) attn_mfma_kernel(AttnArgs a, int
       run_rows<EF>(je, j_end, ent_row, ebase, qa, zscale, w, lane, R, Sp, st);
     } else {
       auto ent_row = [&](int64_t j) -> const uint8_t* {
-        // this lane's id slot for row j (rows are 16 r16-strided within the chunk)
-        const int slot = (int)((j - j_begin) >> 4);
         int32_t e = -1;
+        if (LONG) {
+          e = Ids[j - j_begin];
+        } else {
+          // this lane's id slot for row j (rows are 16 r16-strided within the chunk)
+          const int slot = (int)((j - j_begin) >> 4);
 #pragma unroll
-        for (int i = 0; i < kMaxIdsPerLane; ++i)
-          if (i == slot) e = ids[i];
+          for (int i = 0; i < kMaxIdsPerLane; ++i)
+            if (i == slot) e = ids[i];
+        }
         return (e >= 0 && e < a.Nmax) ? ebase + (size_t)e * a.ent_rb : nullptr;
       };
       run_rows<EF>(je, j_end, ent_row, ebase, qa, zscale, w, lane, R, Sp, st);
@@ -902,8 +925,13 @@ int64_t attn_list_len(const AttnArgs& a) {
   return kWindow + (a.dense ? a.Nmax : (int64_t)a.topk);
 }
 
+static bool attn_long_chunks(const AttnArgs& a) {
+  return !a.dense && a.Q >= kLongChunkMinQ && a.q_fmt != CSA_F32;
+}
+
 int attn_chunk_rows(const AttnArgs& a) {
-  if (!attn_all_heads(a)) return a.dense ? kChunkHca : kChunkCsa;
+  if (!attn_all_heads(a))
+    return a.dense ? kChunkHca : (attn_long_chunks(a) ? kChunkCsaLong : kChunkCsa);
   const int64_t per = (attn_list_len(a) + kMergeChunks - 1) / kMergeChunks;
   const int64_t cr = (per + kTile - 1) / kTile * kTile;
   return (int)(cr > kChunkDense ? cr : kChunkDense);
@@ -922,16 +950,23 @@ size_t attn_ws_bytes(const AttnArgs& a) {
   return (size_t)a.B * a.Q * (a.H / 16) * nc * sizeof(Partial);
 }
 
+template <int WF, bool LONG>
+static void launch_mfma_wl(const AttnArgs& a, int nc, int64_t nu, dim3 grid, Partial* part,
+                           hipStream_t s) {
+  const int cr = attn_chunk_rows(a);
+  if (a.ent_fmt == CSA_BF16)
+    hipLaunchKernelGGL((attn_mfma_kernel<WF, CSA_BF16, LONG>), grid, dim3(kAttnThreads), 0, s, a, cr, nc, nu, part);
+  else if (a.ent_fmt == CSA_FP8_MX32)
+    hipLaunchKernelGGL((attn_mfma_kernel<WF, CSA_FP8_MX32, LONG>), grid, dim3(kAttnThreads), 0, s, a, cr, nc, nu, part);
+  else
+    hipLaunchKernelGGL((attn_mfma_kernel<WF, CSA_FP4_E4M3_16, LONG>), grid, dim3(kAttnThreads), 0, s, a, cr, nc, nu, part);
+}
+
 template <int WF>
 static void launch_mfma_w(const AttnArgs& a, int nc, int64_t nu, dim3 grid, Partial* part,
                           hipStream_t s) {
-  const int cr = attn_chunk_rows(a);
-  if (a.ent_fmt == CSA_BF16)
-    hipLaunchKernelGGL((attn_mfma_kernel<WF, CSA_BF16>), grid, dim3(kAttnThreads), 0, s, a, cr, nc, nu, part);
-  else if (a.ent_fmt == CSA_FP8_MX32)
-    hipLaunchKernelGGL((attn_mfma_kernel<WF, CSA_FP8_MX32>), grid, dim3(kAttnThreads), 0, s, a, cr, nc, nu, part);
-  else
-    hipLaunchKernelGGL((attn_mfma_kernel<WF, CSA_FP4_E4M3_16>), grid, dim3(kAttnThreads), 0, s, a, cr, nc, nu, part);
+  if (attn_long_chunks(a)) launch_mfma_wl<WF, true>(a, nc, nu, grid, part, s);
+  else launch_mfma_wl<WF, false>(a, nc, nu, grid, part, s);
 }
 
 // Fewer than two work-groups per CU would leave one wave per SIMD with a

@@ -269,6 +269,109 @@ __global__ void __launch_bounds__(64) proj_slice_kernel(ProjJobs jobs, int M) {
     }
 }
 
+// Many-token (prefill) projection on MFMA: P[m][n] = sum_k x[m][k] W[n][k]
+// with bf16 operands and float32 accumulation; x and W are both k-contiguous,
+// so each operand row is read straight in the MFMA operand layout.  A
+// work-group of 4 waves takes a 128 x 128 tile of P (each wave 64 x 64, 16
+// accumulator tiles) and walks k in blocks of 64: a block's x and W tiles
+// (16 KB each) are fetched into registers while the previous block is
+// multiplied from LDS, then written to the other LDS buffer; one barrier per
+// block.  LDS rows are padded to 72 bf16 so the 16-byte fragment reads of 16
+// consecutive rows hit distinct banks.
+constexpr int kGM = 128, kGN = 128, kGK = 64;
+constexpr int kGPitch = kGK + 8;
+constexpr int kGThreads = 256;
+
+__global__ void __launch_bounds__(kGThreads) proj_tile_kernel(const uint16_t* __restrict__ x,
+                                                              const uint16_t* __restrict__ wkv,
+                                                              const uint16_t* __restrict__ wg,
+                                                              int64_t M, int K, int CD,
+                                                              float* __restrict__ P) {
+  __shared__ uint16_t As[2][kGM * kGPitch];
+  __shared__ uint16_t Bs[2][kGN * kGPitch];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int r16 = lane & 15, kq = lane >> 4;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int N = 2 * CD;
+  const int64_t m0 = (int64_t)blockIdx.y * kGM;
+  const int n0 = blockIdx.x * kGN;
+  // loader mapping: piece i = tid + 256 u (u < 4) is row i / 8, 16-byte column i % 8
+  const uint16_t* asrc[4];
+  const uint16_t* bsrc[4];
+  int soff[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int i = tid + kGThreads * u;
+    const int r = i >> 3, c = (i & 7) * 8;
+    int64_t m = m0 + r;
+    m = m < M ? m : M - 1;  // ragged last tile: repeat the last row, never stored
+    asrc[u] = x + m * K + c;
+    const int n = n0 + r;
+    bsrc[u] = (n < CD ? wkv + (int64_t)n * K : wg + (int64_t)(n - CD) * K) + c;
+    soff[u] = r * kGPitch + c;
+  }
+  u32x4_t ra[4], rb[4];
+  auto gload = [&](int k0) __attribute__((always_inline)) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      ra[u] = *(const u32x4_t*)(asrc[u] + k0);
+      rb[u] = *(const u32x4_t*)(bsrc[u] + k0);
+    }
+  };
+  auto lstore = [&](int buf) __attribute__((always_inline)) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      *(u32x4_t*)(&As[buf][soff[u]]) = ra[u];
+      *(u32x4_t*)(&Bs[buf][soff[u]]) = rb[u];
+    }
+  };
+  f32x4_t acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  const int nk = K / kGK;
+  gload(0);
+  lstore(0);
+  __syncthreads();
+  for (int kb = 0; kb < nk; ++kb) {
+    const int buf = kb & 1;
+    if (kb + 1 < nk) gload((kb + 1) * kGK);
+#pragma unroll
+    for (int s = 0; s < kGK / 32; ++s) {
+      u32x4_t af[4], bf[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        af[i] = *(const u32x4_t*)(&As[buf][(wm * 64 + 16 * i + r16) * kGPitch + 32 * s + 8 * kq]);
+        bf[i] = *(const u32x4_t*)(&Bs[buf][(wn * 64 + 16 * i + r16) * kGPitch + 32 * s + 8 * kq]);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          acc[i][j] = mfma16x16x32(as_bf16x8(af[i]), as_bf16x8(bf[j]), acc[i][j]);
+    }
+    if (kb + 1 < nk) lstore(buf ^ 1);
+    __syncthreads();
+  }
+  // D layout: row 4 kq + r of the A tile, column r16 of the B tile
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int64_t m = m0 + wm * 64 + 16 * i + 4 * kq + r;
+      if (m >= M) continue;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) P[m * N + n0 + wn * 64 + 16 * j + r16] = acc[i][j][r];
+    }
+}
+
+static bool use_tile_proj(const csa_compress_args* a) {
+  return a->x_fmt == CSA_BF16 && a->w_fmt == CSA_BF16 && a->dim % kGK == 0 &&
+         (2 * (a->ratio == 4 ? 2 : 1) * a->head_dim) % kGN == 0;
+}
+
 // Tiled GEMM, float32 FMA: P[m][n] = sum_k x[m][k] W[n][k], 64x64 tiles.
 constexpr int kTM = 64, kTN = 64, kTK = 32;
 
@@ -1103,6 +1206,14 @@ hipError_t launch_compress(const csa_compress_args* in, void* ws, hipStream_t s)
     else if (mt == 2) hipLaunchKernelGGL(proj_mfma_kernel<2>, grid, dim3(kProjThreads), 0, s, xp, wk, wgp, (int)M, in->dim, a.CD, po);
     else if (mt == 3) hipLaunchKernelGGL(proj_mfma_kernel<3>, grid, dim3(kProjThreads), 0, s, xp, wk, wgp, (int)M, in->dim, a.CD, po);
     else hipLaunchKernelGGL(proj_mfma_kernel<4>, grid, dim3(kProjThreads), 0, s, xp, wk, wgp, (int)M, in->dim, a.CD, po);
+  } else if (use_tile_proj(in)) {
+    const uint16_t* xp = (const uint16_t*)in->x;
+    for (int64_t m0 = 0; m0 < M; m0 += (int64_t)65535 * kGM) {
+      const int64_t mm = M - m0 < (int64_t)65535 * kGM ? M - m0 : (int64_t)65535 * kGM;
+      hipLaunchKernelGGL(proj_tile_kernel, dim3(N / kGN, (unsigned)((mm + kGM - 1) / kGM)),
+                         dim3(kGThreads), 0, s, xp + m0 * in->dim, (const uint16_t*)in->w_kv,
+                         (const uint16_t*)in->w_gate, mm, in->dim, a.CD, P + m0 * N);
+    }
   } else if (M <= kGemvMaxM) {
     hipLaunchKernelGGL(proj_gemv_kernel, dim3((N + 7) / 8), dim3(kThreads), 0, s, in->x,
                        in->x_fmt, in->w_kv, in->w_gate, in->w_fmt, (int)M, in->dim, a.CD, P);

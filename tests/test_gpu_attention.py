@@ -108,6 +108,41 @@ def test_csa_multi_query_linear_window_and_heads(tables):
             close_bf16(got[b, qq], ref)
 
 
+@pytest.mark.parametrize("k,efmt", [(512, "bf16"), (1300, "fp8_mx32"), (45, "fp4_e4m3_16")])
+def test_csa_many_queries_long_chunks(tables, k, efmt):
+    """16+ queries per sequence: a work-group takes up to 640 list rows (the
+    whole window + top-512 list finishes without partials; longer lists are
+    split into 640-row chunks and merged)."""
+    cos, sin = tables
+    B, Q, H, N = 2, 20, 64, 2500
+    rng = np.random.default_rng(1000 + k)
+    q = synth.bf16_round(rng.standard_normal((B, Q, H, 512)).astype(np.float32))
+    WR = Q + 127
+    win = synth.bf16_round(rng.standard_normal((B, WR, 512)).astype(np.float32))
+    ent = rng.standard_normal((B, N, 512)).astype(np.float32)
+    if efmt == "bf16":
+        ent = synth.bf16_round(ent)
+    sink = rng.standard_normal(H).astype(np.float32)
+    P = np.array([4 * N - Q, 700], np.int32)             # first new position per sequence
+    base = P - 127
+    pos = P[:, None] + np.arange(Q, dtype=np.int32)[None]
+    ids = np.stack([np.stack([gen_ids(rng, min((int(p) + 1) // 4, N), k, N) for p in pos[b]])
+                    for b in range(B)])
+    say(f"csa attn long chunks k={k} {efmt}")
+    out = torch.empty((B, Q, H, 512), dtype=torch.bfloat16, device="cuda")
+    ws = _lib.workspace(_lib.csa_sparse_attn_workspace_size(B, Q, H, k))
+    _lib.csa_sparse_attn_decode(bf16(q), "bf16", bf16(win), "bf16", _lib.WIN_LINEAR, i32(base), WR,
+                                upload_rows(ent, efmt), efmt, N, i32(ids), k, i32(pos),
+                                B, Q, H, f32(sink), 512 ** -0.5, cos, sin, out, "bf16", ws)
+    got = to_np(out)
+    entv = codec.store(ent, efmt)[1]
+    for b in range(B):
+        for qq in range(Q):
+            ref = oracle_sparse(q[b, qq].astype(np.float64), win[b].astype(np.float64), entv[b],
+                                ids[b, qq], sink, int(pos[b, qq]), "linear", int(base[b]), WR)
+            close_bf16(got[b, qq], ref)
+
+
 @pytest.mark.parametrize("efmt", ["bf16", "fp8_mx32", "fp4_e4m3_16"])
 def test_hca_decode(tables, efmt):
     cos, sin = tables

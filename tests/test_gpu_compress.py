@@ -102,6 +102,37 @@ def test_bulk_f32(tables, ratio, d, rotate):
         close_f32(sc[fin], st[1][fin], tol=2e-5)
 
 
+@pytest.mark.parametrize("ratio,d,rotate,entry_fmt", [(4, 512, 0, "bf16"), (4, 128, 1, "bf16"),
+                                                      (128, 512, 0, "fp8_mx32")])
+def test_bulk_bf16_tiled_projection(tables, ratio, d, rotate, entry_fmt):
+    """Many-token bf16 calls (more than 64 rows) use the tiled MFMA
+    projection: 2 x 333 tokens (a ragged last 128-row tile), then a second
+    call that continues from the state."""
+    B, dim, T1, T2 = 2, 512, 333, 270
+    rng = np.random.default_rng(7 * ratio + d)
+    wkv, wg, ape = weights(rng, dim, d, ratio)
+    wkv, wg = synth.bf16_round(wkv), synth.bf16_round(wg)
+    x = synth.bf16_round(rng.standard_normal((B, T1 + T2, dim)).astype(np.float32))
+    n = (T1 + T2) // ratio + 1
+    g = GpuCompressor(B, dim, ratio, d, rotate, wkv, wg, ape, "bf16", entry_fmt, n, tables)
+    say(f"compress bulk bf16 r={ratio} d={d}")
+    g(x[:, :T1], [0, 0])
+    g(x[:, T1:], [T1, T1])
+    got = g.entry_values()
+    for b in range(B):
+        ref, st = compressor.compress_bulk(x[b].astype(np.float64), 0, wkv, wg, ape, np.ones(d),
+                                           OM, ratio, d, rotate=bool(rotate))
+        assert len(ref) == (T1 + T2) // ratio
+        for i, v in ref.items():
+            err = np.abs(got[b, i] - codec.store(v, entry_fmt)[1])
+            assert np.all(err <= step_bound(v, entry_fmt, d)), (b, i, err.max())
+        close_f32(to_np(g.kv)[b], st[0], tol=1e-4)
+        sc = to_np(g.sc)[b]
+        assert np.array_equal(np.isinf(sc), np.isinf(st[1]))
+        fin = np.isfinite(st[1])
+        close_f32(sc[fin], st[1][fin], tol=1e-4)
+
+
 @pytest.mark.parametrize("entry_fmt,dim,d,rotate", [("bf16", 512, 512, 0), ("fp8_mx32", 512, 512, 0),
                                                     ("fp4_e4m3_16", 512, 512, 0), ("f32", 512, 512, 0),
                                                     ("fp8_mx32", 4096, 512, 0), ("fp8_mx32", 4096, 128, 1),
