@@ -183,7 +183,8 @@ struct Scorer {
   // j ends with the scores of tile j (with two tiles, rows 2 and 3 repeat rows
   // 0 and 1), and the step's scores below `end` are written and counted in one
   // pass (only if `live`).
-  template <class Get>
+  // PACKED: hist holds two 16-bit counters per word (bin b in word b / 2, half b % 2).
+  template <bool PACKED = false, class Get>
   __device__ __forceinline__ void score(int64_t k, bool live, int64_t end, Get&& get, float* srow,
                                         uint32_t* hist) const {
     float p[kTiles];
@@ -211,7 +212,9 @@ struct Scorer {
     const int64_t key = k + 16 * kq + r16;
     if (live && (kTiles == 4 || kq < kTiles) && key < end) {
       srow[key] = sc;
-      atomicAdd(&hist[score_key(sc) >> 20], 1u);
+      const uint32_t bin = score_key(sc) >> 20;
+      if (PACKED) atomicAdd(&hist[bin >> 1], 1u << ((bin & 1u) << 4));
+      else atomicAdd(&hist[bin], 1u);
     }
   }
 };
@@ -439,6 +442,117 @@ __global__ void __launch_bounds__(kSplitThreads) index_scores_split(
     if (hist[i]) atomicAdd(&g[i], hist[i]);
 }
 
+// Many queries per sequence (chunked prefill), bf16 keys: the work is a
+// dense contraction, so each key is read once per tile of kQT consecutive
+// queries instead of once per query.  A work-group of kQT waves takes the
+// tile's queries (wave j scores query j, with the query fragments of the
+// per-query kernels) over a range of at most kQKeysPerWg keys: all threads
+// load a step of 64 keys (16 KB) into registers while the previous step is
+// scored from LDS, then store it to the other LDS buffer; one barrier per
+// step.  Per key the scoring is the same MFMA chain, epilogue and order as the
+// per-query bf16 kernel, so the scores are bit-identical to it.  The top
+// radix digit is counted in LDS with two 16-bit counters per word (a range
+// holds fewer than 2^16 keys) and flushed to the row histograms at the end.
+constexpr int kQT = 8;                 // queries per work-group
+constexpr int kQThreads = 64 * kQT;
+constexpr int kQStep = 64;             // keys per step
+constexpr int kQKeysPerWg = 32768;     // keys per work-group at most (16-bit counters)
+constexpr int kQStageSlots = kQStep * 17;  // 64 rows of 16 pieces, padded to 17
+
+template <int HT>
+__global__ void __launch_bounds__(kQThreads) index_scores_qtile(
+    const uint16_t* __restrict__ q_idx, const float* __restrict__ w_idx,
+    const uint8_t* __restrict__ k_idx, const int32_t* __restrict__ pos, int ratio, int Q,
+    int64_t Nmax, int keys_per_wg, int64_t tile_off, float* __restrict__ scores,
+    int32_t* __restrict__ n_vis_out, uint32_t* __restrict__ hist_g) {
+  constexpr int KFMT = CSA_BF16;
+  constexpr int64_t kRowBytes = 256;
+  static_assert(tiles_per_iter<KFMT>() == 2, "a step is two scorer calls of 32 keys");
+  __shared__ uint32_t hist[kQT][kHistBins / 2];
+  __shared__ u32x4_t buf[2][kQStageSlots];
+
+  const int t = threadIdx.x;
+  const int lane = t & 63;
+  const int wave = t >> 6;
+  const int tiles_per_seq = (Q + kQT - 1) / kQT;
+  const int64_t tile = tile_off + blockIdx.y;
+  const int64_t b = tile / tiles_per_seq;
+  const int q0 = (int)(tile % tiles_per_seq) * kQT;
+  const int qq = q0 + wave;
+  const bool has_q = qq < Q;
+  const int64_t row = b * Q + (has_q ? qq : Q - 1);
+  auto visible = [&](int64_t r) {
+    int64_t nv = ((int64_t)pos[r] + 1) / ratio;
+    return nv < 0 ? 0 : (nv > Nmax ? Nmax : nv);
+  };
+  const int64_t nv = has_q ? visible(row) : 0;
+  if (blockIdx.x == 0 && lane == 0 && has_q) n_vis_out[row] = (int32_t)nv;
+  // the tile's key range: [x0, x1) clipped to the largest visible count
+  int64_t nv_max = 0;
+  for (int j = 0; j < kQT && q0 + j < Q; ++j) {
+    const int64_t v = visible(b * Q + q0 + j);
+    nv_max = v > nv_max ? v : nv_max;
+  }
+  const int64_t x0 = (int64_t)blockIdx.x * keys_per_wg;
+  if (x0 >= nv_max) return;
+  const int64_t x1 = x0 + keys_per_wg < nv_max ? x0 + keys_per_wg : nv_max;
+  const int64_t n_steps = (x1 - x0 + kQStep - 1) / kQStep;
+  const int64_t end = nv < x1 ? nv : x1;  // this query's keys in the range
+
+  for (int i = t; i < kQT * kHistBins / 2; i += kQThreads) (&hist[0][0])[i] = 0;
+
+  Scorer<HT, KFMT> sc;
+  if (has_q) sc.load(q_idx, w_idx, row, lane);
+  float* srow = scores + row * Nmax;
+  const uint8_t* kbase = k_idx + b * Nmax * kRowBytes;
+  // thread t loads pieces t and t + 512 of a step: row p / 16, 16-byte column
+  // p % 16, the row clamped into the range
+  u32x4_t rg[2];
+  auto gload = [&](int64_t i) __attribute__((always_inline)) {
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int p = t + kQThreads * u;
+      int64_t key = x0 + i * kQStep + (p >> 4);
+      key = key < x1 ? key : x1 - 1;
+      rg[u] = ((const u32x4_t*)(kbase + key * kRowBytes))[p & 15];
+    }
+  };
+  auto stage = [&](int bi) __attribute__((always_inline)) {
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int p = t + kQThreads * u;
+      buf[bi][(p >> 4) * 17 + (p & 15)] = rg[u];
+    }
+  };
+  gload(0);
+  stage(0);
+  __syncthreads();
+  for (int64_t i = 0; i < n_steps; ++i) {
+    if (i + 1 < n_steps) gload(i + 1);
+    if (has_q) {
+      const u32x4_t* st = buf[i & 1];
+      const int64_t k = x0 + i * kQStep;
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+        sc.template score<true>(k + 32 * h, true, end, [&](int nt, KeyRaw& f) {
+          stage_read<KFMT>(st + 32 * h * 17, 16 * nt + sc.r16, sc.kq, f);
+        }, srow, hist[wave]);
+    }
+    if (i + 1 < n_steps) stage((i + 1) & 1);
+    __syncthreads();
+  }
+  // flush the nonzero counters of every query row of the tile
+  for (int i = t; i < kQT * kHistBins / 2; i += kQThreads) {
+    const int j = i / (kHistBins / 2), wd = i % (kHistBins / 2);
+    if (q0 + j >= Q) continue;
+    const uint32_t v = hist[j][wd];
+    if (!v) continue;
+    uint32_t* g = hist_g + (b * Q + q0 + j) * kHistBins + 2 * wd;
+    if (v & 0xffffu) atomicAdd(&g[0], v & 0xffffu);
+    if (v >> 16) atomicAdd(&g[1], v >> 16);
+  }
+}
+
 // float32 path: one thread per key, q in LDS.
 constexpr int kF32Keys = 256;
 __global__ void __launch_bounds__(kIdxThreads) index_scores_f32(
@@ -487,6 +601,21 @@ template <int HT>
 hipError_t launch_mfma(const void* q_idx, const float* w_idx, const void* k_idx, int k_fmt,
                        const int32_t* pos, int ratio, int Q, int64_t R, int64_t Nmax,
                        float* scores, int32_t* n_vis, uint32_t* hist, hipStream_t s) {
+  if (k_fmt == CSA_BF16 && Q >= kQT) {
+    // even ranges of at most kQKeysPerWg keys, whole steps
+    const int64_t splits = (Nmax + kQKeysPerWg - 1) / kQKeysPerWg;
+    int64_t kpw = (Nmax + splits - 1) / splits;
+    kpw = (kpw + kQStep - 1) / kQStep * kQStep;
+    const int64_t tiles = R / Q * ((Q + kQT - 1) / kQT);
+    for (int64_t y0 = 0; y0 < tiles; y0 += 65535) {
+      const int64_t ny = tiles - y0 < 65535 ? tiles - y0 : 65535;
+      hipLaunchKernelGGL((index_scores_qtile<HT>), dim3((unsigned)splits, (unsigned)ny),
+                         dim3(kQThreads), 0, s, (const uint16_t*)q_idx, w_idx,
+                         (const uint8_t*)k_idx, pos, ratio, Q, Nmax, (int)kpw, y0, scores, n_vis,
+                         hist);
+    }
+    return hipGetLastError();
+  }
   if (k_fmt == CSA_FP8_MX32) {
     // about one work-group per CU in all, at least one step each
     int64_t gx = (kSplitTargetWgs + R - 1) / R;

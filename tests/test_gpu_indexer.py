@@ -54,6 +54,50 @@ def test_scores_and_topk(kfmt, Hi, N):
             check_selection(out[b, qq], sc[b, qq], S_ref, tol, nv, k)
 
 
+@pytest.mark.parametrize("Hi", [64, 32])
+def test_many_queries_query_tiles(Hi):
+    """8+ queries per sequence with bf16 keys (chunked prefill) take the
+    query-tiled kernel: 21 queries (a ragged tile of 5), 70,000 keys (three key
+    ranges, a partial last step), causal visibility per query including an
+    empty one.  Scores match the oracle, are bit-identical to one-query calls
+    (the per-query kernel), and nothing past a query's visible count is written."""
+    need_gpu()
+    B, Q, N, k = 2, 21, 70000, 512
+    w = synth.Workload(91, "t", B=B, ctx=4 * N, ratio=4, n_entries=N, Hi=Hi, key_fmt="bf16")
+    qi = synth.bf16_round(synth.normal_batched(w.seed, synth.T_QIDX, B, (Q, Hi, 128)))
+    wi = synth.normal_batched(w.seed, synth.T_WIDX, B, (Q, Hi), (128 * Hi) ** -0.5)
+    K = synth.index_keys(w)
+    pos = np.stack([4 * N - Q - 40 + np.arange(Q), 1 + 37 * np.arange(Q)]).astype(np.int32)
+    say(f"index_topk query tiles Hi={Hi}")
+    kdev = upload_rows(K, "bf16")
+    qd, wd = bf16(qi), f32(wi)
+    out = torch.empty((B, Q, k), dtype=torch.int32, device="cuda")
+    sc = torch.full((B, Q, N), float("nan"), dtype=torch.float32, device="cuda")
+    ws = _lib.workspace(_lib.csa_index_topk_workspace_size(B, Q, N, k))
+    _lib.csa_index_topk(qd, "bf16", wd, kdev, "bf16", i32(pos), 4, B, Q, Hi, N, k, out, sc, ws)
+    out = out.cpu().numpy()
+    sc = sc.cpu().numpy()
+    # one-query calls through the per-query kernel
+    ws1 = _lib.workspace(_lib.csa_index_topk_workspace_size(1, 1, N, k))
+    for b in range(B):
+        for qq in range(Q):
+            o1 = torch.empty((1, 1, k), dtype=torch.int32, device="cuda")
+            s1 = torch.full((1, 1, N), float("nan"), dtype=torch.float32, device="cuda")
+            _lib.csa_index_topk(qd[b, qq].contiguous(), "bf16", wd[b, qq].contiguous(),
+                                kdev[b].contiguous(), "bf16", i32(pos[b, qq:qq + 1]), 4, 1, 1,
+                                Hi, N, k, o1, s1, ws1)
+            nv = int(indexer.n_visible(pos[b, qq], 4, N))
+            s1 = s1.cpu().numpy()[0, 0]
+            assert np.array_equal(s1[:nv].view(np.uint32), sc[b, qq, :nv].view(np.uint32)), (b, qq)
+            assert np.all(np.isnan(sc[b, qq, nv:])), (b, qq)
+            assert np.array_equal(o1.cpu().numpy()[0, 0], out[b, qq]), (b, qq)
+            S_ref = indexer.scores(qi[b, qq].astype(np.float64), wi[b, qq], K[b], nv)
+            tol = score_bound(qi[b, qq].astype(np.float64), wi[b, qq].astype(np.float64), K[b][:nv])
+            err = np.abs(sc[b, qq, :nv] - S_ref)
+            assert np.all(err <= tol), (b, qq, err.max())
+            check_selection(out[b, qq], sc[b, qq], S_ref, tol, nv, k)
+
+
 def test_without_score_output_matches():
     """out_scores is optional: the indices are the same either way."""
     need_gpu()
