@@ -490,7 +490,12 @@ __device__ __forceinline__ void attend_tile_all(const uint4 (&fr)[2][4], uint32_
 // read the chunk's rows through one L2 (work-groups are handed to the XCDs
 // round-robin by linear id).  Writes one partial per (unit, head tile, chunk)
 // in the layout of the merge kernel.
-template <int WF, int EF, int HT>
+//
+// SPARSE: a top-k list (CSA with many queries per sequence) in chunks of
+// kChunkCsaLong rows, whose ids are staged in LDS.  A single-chunk list (the
+// window + top-512) is finished here -- sink, normalisation, inverse RoPE,
+// one rounding -- with no partials or merge.
+template <int WF, int EF, int HT, bool SPARSE = false>
 __global__ void __launch_bounds__(kAttnThreads, HT <= 2 ? 2 : 1) attn_dense_all_kernel(AttnArgs a, int chunk_rows,
                                                                       int nchunks, int64_t units,
                                                                       int hsplit, Partial* part) {
@@ -498,6 +503,7 @@ __global__ void __launch_bounds__(kAttnThreads, HT <= 2 ? 2 : 1) attn_dense_all_
   __shared__ float4 Sp[4][HT][2][64];
   __shared__ uint4 Pl[HT * 64];
   __shared__ float Al[16 * HT];
+  __shared__ int32_t Ids[SPARSE ? kChunkCsaLong : 1];
 
   int64_t item = blockIdx.x;
   int hs = 0;
@@ -518,12 +524,20 @@ __global__ void __launch_bounds__(kAttnThreads, HT <= 2 ? 2 : 1) attn_dense_all_
   const int64_t b = unit / a.Q;
   const int t = a.pos[unit];
   const int64_t nvis = unit_nvis(a, t);
-  const int64_t list_len = kWindow + nvis;
+  const int64_t list_len = kWindow + (SPARSE ? (int64_t)a.topk : nvis);
   const int64_t j_begin = (int64_t)chunk * chunk_rows;
   int64_t j_end = j_begin + chunk_rows;
   if (j_end > list_len) j_end = list_len;
   const int rr = rope_row(a, t);
   const float zscale = a.scale * kLog2e;
+
+  if (SPARSE) {  // the chunk's top-k ids (slot j - j_begin), -1 where absent
+    for (int i = tid; i < kChunkCsaLong; i += kAttnThreads) {
+      const int64_t jj = j_begin + i;
+      Ids[i] = (jj >= kWindow && jj < j_end) ? a.topk_idx[unit * a.topk + (jj - kWindow)] : -1;
+    }
+    __syncthreads();
+  }
 
   uint4 qa[HT][4];
   load_q_frags<HT>(a, unit, 16 * ht0, w, r16, kq, rr, qa);
@@ -587,10 +601,51 @@ __global__ void __launch_bounds__(kAttnThreads, HT <= 2 ? 2 : 1) attn_dense_all_
   if (je < j_end && a.Nmax > 0) {
     const uint8_t* ebase = (const uint8_t*)a.entries + (size_t)b * (size_t)a.Nmax * a.ent_rb;
     auto ent_row = [&](int64_t j) -> const uint8_t* {
+      if (SPARSE) {
+        const int32_t e = Ids[j - j_begin];
+        return (e >= 0 && e < a.Nmax) ? ebase + (size_t)e * a.ent_rb : nullptr;
+      }
       const int64_t e = j - kWindow;
       return e < nvis ? ebase + (size_t)e * a.ent_rb : nullptr;
     };
     run(std::integral_constant<int, EF>{}, je, j_end, ent_row, ebase);
+  }
+
+  if (SPARSE && nchunks == 1) {
+    // finish: 1 / (l + e^{sink - m}) per head, shared through LDS (wave w holds
+    // the softmax state of head tile w), then the inverse rotation of the
+    // output's last 64 dims at the query's position and one rounding.  (Every
+    // wave is past its last read of Al first.)
+    __syncthreads();
+    if (w < HT && kq == 0) {
+      const float sink2 = a.sink[16 * (ht0 + w) + r16] * kLog2e;
+      const float den = (sm == -INFINITY) ? 0.f : sl + exp2f(sink2 - sm);
+      Al[16 * w + r16] = den > 0.f ? 1.f / den : 0.f;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int ht = 0; ht < HT; ++ht) {
+      float iv[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) iv[r] = Al[16 * ht + 4 * kq + r];
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt) {
+        const int d = 128 * w + 16 * dt + r16;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          float v = o[ht][dt][r] * iv[r];
+          const float nb = shfl_xor_f(v, 1);  // pair partner (d ^ 1)
+          if (d >= kHeadDim - kRopeDims) {
+            const int k = (d - (kHeadDim - kRopeDims)) >> 1;
+            const float c = a.rope_cos[(int64_t)rr * 32 + k];
+            const float sn = a.rope_sin[(int64_t)rr * 32 + k];
+            v = (d & 1) ? (-nb * sn + v * c) : (v * c + nb * sn);
+          }
+          store_out(a, unit, 16 * (ht0 + ht) + 4 * kq + r, d, v);
+        }
+      }
+    }
+    return;
   }
 
   const int G = a.H / 16;
@@ -915,23 +970,32 @@ __global__ void __launch_bounds__(kAttnThreads) attn_f32_kernel(AttnArgs a) {
 
 }  // namespace
 
+static bool attn_long_chunks(const AttnArgs& a) {
+  return !a.dense && a.Q >= kLongChunkMinQ && a.q_fmt != CSA_F32;
+}
+
 // Dense lists with at most 64 heads use the all-heads kernel (and always its
-// merge); other lists the 16-head-group kernel.
+// merge); so do top-k lists with 64 heads and many queries per sequence
+// (long chunks; a single-chunk list needs no merge).  Other lists use the
+// 16-head-group kernel.
+// Two work-groups of two head tiles each per item (ids 8 apart: one XCD, one
+// L2 read of the rows): half the registers of one all-heads work-group, so two
+// fit per SIMD; measured faster than one work-group of four head tiles.
+constexpr int kSparseHsplit = 2;
+static bool attn_sparse_all_heads(const AttnArgs& a) {
+  return attn_long_chunks(a) && a.H == 64;
+}
 static bool attn_all_heads(const AttnArgs& a) {
-  return a.dense && a.H <= 64 && a.q_fmt != CSA_F32;
+  return (a.dense && a.H <= 64 && a.q_fmt != CSA_F32) || attn_sparse_all_heads(a);
 }
 
 int64_t attn_list_len(const AttnArgs& a) {
   return kWindow + (a.dense ? a.Nmax : (int64_t)a.topk);
 }
 
-static bool attn_long_chunks(const AttnArgs& a) {
-  return !a.dense && a.Q >= kLongChunkMinQ && a.q_fmt != CSA_F32;
-}
-
 int attn_chunk_rows(const AttnArgs& a) {
-  if (!attn_all_heads(a))
-    return a.dense ? kChunkHca : (attn_long_chunks(a) ? kChunkCsaLong : kChunkCsa);
+  if (attn_long_chunks(a)) return kChunkCsaLong;
+  if (!attn_all_heads(a)) return a.dense ? kChunkHca : kChunkCsa;
   const int64_t per = (attn_list_len(a) + kMergeChunks - 1) / kMergeChunks;
   const int64_t cr = (per + kTile - 1) / kTile * kTile;
   return (int)(cr > kChunkDense ? cr : kChunkDense);
@@ -946,7 +1010,7 @@ static int attn_nchunks(const AttnArgs& a) {
 size_t attn_ws_bytes(const AttnArgs& a) {
   if (a.q_fmt == CSA_F32) return 0;
   int nc = attn_nchunks(a);
-  if (nc <= 1 && !attn_all_heads(a)) return 0;
+  if (nc <= 1 && !(attn_all_heads(a) && a.dense)) return 0;
   return (size_t)a.B * a.Q * (a.H / 16) * nc * sizeof(Partial);
 }
 
@@ -976,6 +1040,18 @@ constexpr int64_t kDenseSplitBelow = 512;
 template <int WF, int EF>
 static void launch_all_heads_e(const AttnArgs& a, int nc, int64_t nu, Partial* part,
                                hipStream_t s) {
+  const int cr0 = attn_chunk_rows(a);
+  if (attn_sparse_all_heads(a)) {  // 64 heads over kSparseHsplit work-groups per item
+    const int64_t items = (int64_t)nc * nu;
+    if (kSparseHsplit == 1)
+      hipLaunchKernelGGL((attn_dense_all_kernel<WF, EF, 4, true>), dim3((unsigned)items),
+                         dim3(kAttnThreads), 0, s, a, cr0, nc, nu, 1, part);
+    else
+      hipLaunchKernelGGL((attn_dense_all_kernel<WF, EF, 4 / kSparseHsplit, true>),
+                         dim3((unsigned)((items + 7) / 8 * 8 * kSparseHsplit)), dim3(kAttnThreads),
+                         0, s, a, cr0, nc, nu, kSparseHsplit, part);
+    return;
+  }
   const int G = a.H / 16;
   const int64_t items = (int64_t)nc * nu;
   const int hsplit = (G % 2 == 0 && items < kDenseSplitBelow) ? 2 : 1;
@@ -1035,7 +1111,7 @@ hipError_t launch_attention(const AttnArgs& a0, void* ws, hipStream_t s) {
     const bool all_heads = attn_all_heads(a);
     if (all_heads) launch_all_heads(a, nc, nu, (Partial*)ws, s);
     else launch_mfma(a, nc, nu, (Partial*)ws, s);
-    if (nc > 1 || all_heads)
+    if (nc > 1 || (all_heads && a.dense))
       hipLaunchKernelGGL(attn_merge_kernel, dim3((a.H / 16) * (kHeadDim / 64), nu),
                          dim3(kAttnThreads), 0, s, a, nc,
                          (const Partial*)ws);
