@@ -447,7 +447,7 @@ __global__ void __launch_bounds__(kSplitThreads) index_scores_split(
 // queries instead of once per query.  A work-group of kQT waves takes the
 // tile's queries (wave j scores query j, with the query fragments of the
 // per-query kernels) over a range of at most kQKeysPerWg keys: all threads
-// load a step of 64 keys (16 KB) into registers while the previous step is
+// load a step of 128 keys (32 KB) into registers while the previous step is
 // scored from LDS, then store it to the other LDS buffer; one barrier per
 // step.  Per key the scoring is the same MFMA chain, epilogue and order as the
 // per-query bf16 kernel, so the scores are bit-identical to it.  The top
@@ -455,9 +455,10 @@ __global__ void __launch_bounds__(kSplitThreads) index_scores_split(
 // holds fewer than 2^16 keys) and flushed to the row histograms at the end.
 constexpr int kQT = 8;                 // queries per work-group
 constexpr int kQThreads = 64 * kQT;
-constexpr int kQStep = 64;             // keys per step
+constexpr int kQStep = 128;            // keys per step
 constexpr int kQKeysPerWg = 32768;     // keys per work-group at most (16-bit counters)
-constexpr int kQStageSlots = kQStep * 17;  // 64 rows of 16 pieces, padded to 17
+constexpr int kQStageSlots = kQStep * 17;  // rows of 16 pieces, padded to 17
+constexpr int kQLoads = kQStep * 16 / kQThreads;  // 16-byte pieces per thread per step
 
 template <int HT>
 __global__ void __launch_bounds__(kQThreads) index_scores_qtile(
@@ -505,12 +506,12 @@ __global__ void __launch_bounds__(kQThreads) index_scores_qtile(
   if (has_q) sc.load(q_idx, w_idx, row, lane);
   float* srow = scores + row * Nmax;
   const uint8_t* kbase = k_idx + b * Nmax * kRowBytes;
-  // thread t loads pieces t and t + 512 of a step: row p / 16, 16-byte column
+  // thread t loads pieces t + 512 u of a step: row p / 16, 16-byte column
   // p % 16, the row clamped into the range
-  u32x4_t rg[2];
+  u32x4_t rg[kQLoads];
   auto gload = [&](int64_t i) __attribute__((always_inline)) {
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
+    for (int u = 0; u < kQLoads; ++u) {
       const int p = t + kQThreads * u;
       int64_t key = x0 + i * kQStep + (p >> 4);
       key = key < x1 ? key : x1 - 1;
@@ -519,7 +520,7 @@ __global__ void __launch_bounds__(kQThreads) index_scores_qtile(
   };
   auto stage = [&](int bi) __attribute__((always_inline)) {
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
+    for (int u = 0; u < kQLoads; ++u) {
       const int p = t + kQThreads * u;
       buf[bi][(p >> 4) * 17 + (p & 15)] = rg[u];
     }
@@ -533,7 +534,7 @@ __global__ void __launch_bounds__(kQThreads) index_scores_qtile(
       const u32x4_t* st = buf[i & 1];
       const int64_t k = x0 + i * kQStep;
 #pragma unroll
-      for (int h = 0; h < 2; ++h)
+      for (int h = 0; h < kQStep / 32; ++h)
         sc.template score<true>(k + 32 * h, true, end, [&](int nt, KeyRaw& f) {
           stage_read<KFMT>(st + 32 * h * 17, 16 * nt + sc.r16, sc.kq, f);
         }, srow, hist[wave]);
