@@ -256,8 +256,10 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="csa_1m_fp8", choices=sorted(WORKLOADS))
-    ap.add_argument("--copies", type=int, default=2,
-                    help="independent cache copies rotated per step (defeats the 256 MB MALL)")
+    ap.add_argument("--copies", type=int, default=None,
+                    help="independent cache copies rotated per step (default: at least 4 and "
+                         "at least 1 GB of step reads in all, so that no step finds the cache "
+                         "lines of an earlier step in the 256 MB last-level cache)")
     ap.add_argument("--cpu-seqs", type=int, default=2)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -290,6 +292,9 @@ def main():
           flush=True)
     t0 = time.time()
     Layer = decode.CsaDecodeLayer if w.ratio == 4 else decode.HcaDecodeLayer
+    if a.copies is None:
+        step_bytes = sum(algorithmic_bytes(w).values())
+        a.copies = max(4, -(-1_000_000_000 // step_bytes))
     layer = Layer(w, copies=a.copies)
     torch.cuda.synchronize()
     print(f"# inputs resident in {time.time() - t0:.1f} s", file=sys.stderr, flush=True)
