@@ -176,11 +176,18 @@ __device__ __forceinline__ uint4 frag_bf16(const Raw<F>& r, int s, int kq) {
     const uint32_t sb = g < 4 ? (q.sc.x >> (8 * g)) : (q.sc.y >> (8 * (g - 4)));
     const float sc = e4m3_to_f32(sb & 0xffu);
     const uint32_t c = q.v[s];
-    return make_uint4(
-        pack_bf16x2_exact(e2m1_to_f32(c & 15u) * sc, e2m1_to_f32((c >> 4) & 15u) * sc),
-        pack_bf16x2_exact(e2m1_to_f32((c >> 8) & 15u) * sc, e2m1_to_f32((c >> 12) & 15u) * sc),
-        pack_bf16x2_exact(e2m1_to_f32((c >> 16) & 15u) * sc, e2m1_to_f32((c >> 20) & 15u) * sc),
-        pack_bf16x2_exact(e2m1_to_f32((c >> 24) & 15u) * sc, e2m1_to_f32(c >> 28) * sc));
+    // byte j holds elements 2j (low nibble) and 2j + 1; the hardware
+    // conversion (unit scale: it would apply only a power-of-two scale) gives
+    // their exact E2M1 values, and the E4M3 scale is applied in float32 (the
+    // product of a 2-bit and a 4-bit significand is exact, also in bf16)
+    const auto f0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c, 1.0f, 0);
+    const auto f1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c, 1.0f, 1);
+    const auto f2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c, 1.0f, 2);
+    const auto f3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c, 1.0f, 3);
+    return make_uint4(pack_bf16x2_exact(f0[0] * sc, f0[1] * sc),
+                      pack_bf16x2_exact(f1[0] * sc, f1[1] * sc),
+                      pack_bf16x2_exact(f2[0] * sc, f2[1] * sc),
+                      pack_bf16x2_exact(f3[0] * sc, f3[1] * sc));
   }
 }
 
