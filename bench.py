@@ -173,6 +173,43 @@ def time_steps(layer, steps, torch):
     return start.elapsed_time(end) / steps
 
 
+def step_percentiles(layer, steps, torch):
+    """p10 / p50 / p90 of single-step durations (events around each step)."""
+    evs = []
+    torch.cuda.synchronize()
+    for _ in range(steps):
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record()
+        layer.step()
+        b.record()
+        evs.append((a, b))
+    torch.cuda.synchronize()
+    t = np.array([a.elapsed_time(b) for a, b in evs])
+    return {"p10": float(np.percentile(t, 10)), "p50": float(np.percentile(t, 50)),
+            "p90": float(np.percentile(t, 90))}
+
+
+def copy_bandwidth(torch, nbytes=2 << 30, reps=5):
+    """Measured device-to-device copy rate (read + write bytes per second):
+    the practical streaming ceiling next to the nominal 8 TB/s."""
+    src = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    a.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    b.record()
+    torch.cuda.synchronize()
+    gbs = 2 * nbytes * reps / (a.elapsed_time(b) * 1e-3) / 1e9
+    del src, dst
+    torch.cuda.empty_cache()
+    return gbs
+
+
 def time_phases(layer, steps, torch):
     """Average duration of every phase, each bracketed by events on its stream."""
     acc = {}
@@ -303,6 +340,8 @@ def main():
         layer.step()
     ms = time_steps(layer, a.steps, torch)
     phases = time_phases(layer, a.steps, torch)
+    pct = step_percentiles(layer, a.steps, torch)
+    copy_gbs = copy_bandwidth(torch)
     ab = algorithmic_bytes(w)
     dom = "csa_index_topk" if w.ratio == 4 else "hca_attn_decode"
     dom_gbs = ab[dom] / (phases[dom] * 1e-3) / 1e9
@@ -329,6 +368,9 @@ def main():
                      "kernel": dom,
                      "bytes_per_launch": ab[dom], "ms_per_launch": phases[dom]},
         "step_hbm_GBps": step_bytes / (ms * 1e-3) / 1e9,
+        "step_ms_percentiles": pct,
+        "measured_copy_GBps": copy_gbs,
+        "frac_of_measured_copy": dom_gbs / copy_gbs,
         "phases_ms": phases,
         "algorithmic_bytes": ab,
     }
@@ -351,6 +393,7 @@ def main_prefill(a, w, torch):
         layer.step()
     ms = time_steps(layer, a.steps, torch)
     phases = time_phases(layer, a.steps, torch)
+    pct = step_percentiles(layer, a.steps, torch)
     fl = prefill_flops(w)
     dom = "csa_index_topk"
     tf = fl[dom] / (phases[dom] * 1e-3) / 1e12
@@ -369,6 +412,7 @@ def main_prefill(a, w, torch):
                      "unit": "TFLOP/s", "frac": tf / MFMA_BF16_PEAK_TFLOPS, "traffic": None,
                      "kernel": dom, "flops_per_launch": fl[dom], "ms_per_launch": phases[dom]},
         "phases_ms": phases,
+        "step_ms_percentiles": pct,
         "phase_tflops": {k: fl[k] / (phases[k] * 1e-3) / 1e12 for k in fl},
         "flops": fl,
     }
