@@ -447,18 +447,19 @@ __global__ void __launch_bounds__(kSplitThreads) index_scores_split(
 // queries instead of once per query.  A work-group of kQT waves takes the
 // tile's queries (wave j scores query j, with the query fragments of the
 // per-query kernels) over a range of at most kQKeysPerWg keys: all threads
-// load a step of 128 keys (32 KB) into registers while the previous step is
+// load a step of 96 keys (24 KB) into registers while the previous step is
 // scored from LDS, then store it to the other LDS buffer; one barrier per
 // step.  Per key the scoring is the same MFMA chain, epilogue and order as the
 // per-query bf16 kernel, so the scores are bit-identical to it.  The top
 // radix digit is counted in LDS with two 16-bit counters per word (a range
 // holds fewer than 2^16 keys) and flushed to the row histograms at the end.
-constexpr int kQT = 8;                 // queries per work-group
+constexpr int kQT = 12;                // queries per work-group (3 waves per SIMD)
 constexpr int kQThreads = 64 * kQT;
-constexpr int kQStep = 128;            // keys per step
+constexpr int kQStep = 96;             // keys per step
 constexpr int kQKeysPerWg = 32768;     // keys per work-group at most (16-bit counters)
 constexpr int kQStageSlots = kQStep * 17;  // rows of 16 pieces, padded to 17
 constexpr int kQLoads = kQStep * 16 / kQThreads;  // 16-byte pieces per thread per step
+static_assert(kQLoads * kQThreads == kQStep * 16 && kQStep % 32 == 0, "whole pieces, 32-key calls");
 
 template <int HT>
 __global__ void __launch_bounds__(kQThreads) index_scores_qtile(

@@ -56,8 +56,8 @@ def test_scores_and_topk(kfmt, Hi, N):
 
 @pytest.mark.parametrize("Hi", [64, 32])
 def test_many_queries_query_tiles(Hi):
-    """8+ queries per sequence with bf16 keys (chunked prefill) take the
-    query-tiled kernel: 21 queries (a ragged tile of 5), 70,000 keys (three key
+    """12+ queries per sequence with bf16 keys (chunked prefill) take the
+    query-tiled kernel: 21 queries (a ragged tile of 9), 70,000 keys (three key
     ranges, a partial last step), causal visibility per query including an
     empty one.  Scores match the oracle, are bit-identical to one-query calls
     (the per-query kernel), and nothing past a query's visible count is written."""
