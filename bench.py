@@ -210,6 +210,46 @@ def copy_bandwidth(torch, nbytes=2 << 30, reps=5):
     return gbs
 
 
+def flushed_steps(layer, steps, torch, nbytes=512 << 20):
+    """Median single-step time when 512 MB are written between steps (the
+    last-level cache then holds none of the step's inputs); the flush itself
+    is outside the events."""
+    junk = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    evs = []
+    torch.cuda.synchronize()
+    for i in range(steps):
+        junk.fill_(i & 0xff)
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record()
+        layer.step()
+        b.record()
+        evs.append((a, b))
+    torch.cuda.synchronize()
+    del junk
+    torch.cuda.empty_cache()
+    return float(np.median([a.elapsed_time(b) for a, b in evs]))
+
+
+def read_bandwidth(torch, nbytes=2 << 30, reps=5):
+    """Measured streaming-read rate: a float32 sum over a 2 GiB tensor (torch's
+    reduction kernel), bytes read per second."""
+    x = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda")
+    x.sum()
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    a.record()
+    for _ in range(reps):
+        x.sum()
+    b.record()
+    torch.cuda.synchronize()
+    gbs = nbytes * reps / (a.elapsed_time(b) * 1e-3) / 1e9
+    del x
+    torch.cuda.empty_cache()
+    return gbs
+
+
 def time_phases(layer, steps, torch):
     """Average duration of every phase, each bracketed by events on its stream."""
     acc = {}
@@ -341,7 +381,9 @@ def main():
     ms = time_steps(layer, a.steps, torch)
     phases = time_phases(layer, a.steps, torch)
     pct = step_percentiles(layer, a.steps, torch)
+    flushed_ms = flushed_steps(layer, a.steps, torch)
     copy_gbs = copy_bandwidth(torch)
+    read_gbs = read_bandwidth(torch)
     ab = algorithmic_bytes(w)
     dom = "csa_index_topk" if w.ratio == 4 else "hca_attn_decode"
     dom_gbs = ab[dom] / (phases[dom] * 1e-3) / 1e9
@@ -369,8 +411,10 @@ def main():
                      "bytes_per_launch": ab[dom], "ms_per_launch": phases[dom]},
         "step_hbm_GBps": step_bytes / (ms * 1e-3) / 1e9,
         "step_ms_percentiles": pct,
+        "flushed_step_ms_p50": flushed_ms,
         "measured_copy_GBps": copy_gbs,
         "frac_of_measured_copy": dom_gbs / copy_gbs,
+        "measured_read_GBps": read_gbs,
         "phases_ms": phases,
         "algorithmic_bytes": ab,
     }
