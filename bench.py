@@ -231,25 +231,6 @@ def flushed_steps(layer, steps, torch, nbytes=512 << 20):
     return float(np.median([a.elapsed_time(b) for a, b in evs]))
 
 
-def read_bandwidth(torch, nbytes=2 << 30, reps=5):
-    """Measured streaming-read rate: a float32 sum over a 2 GiB tensor (torch's
-    reduction kernel), bytes read per second."""
-    x = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda")
-    x.sum()
-    a = torch.cuda.Event(enable_timing=True)
-    b = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    a.record()
-    for _ in range(reps):
-        x.sum()
-    b.record()
-    torch.cuda.synchronize()
-    gbs = nbytes * reps / (a.elapsed_time(b) * 1e-3) / 1e9
-    del x
-    torch.cuda.empty_cache()
-    return gbs
-
-
 def time_phases(layer, steps, torch):
     """Average duration of every phase, each bracketed by events on its stream."""
     acc = {}
@@ -383,7 +364,6 @@ def main():
     pct = step_percentiles(layer, a.steps, torch)
     flushed_ms = flushed_steps(layer, a.steps, torch)
     copy_gbs = copy_bandwidth(torch)
-    read_gbs = read_bandwidth(torch)
     ab = algorithmic_bytes(w)
     dom = "csa_index_topk" if w.ratio == 4 else "hca_attn_decode"
     dom_gbs = ab[dom] / (phases[dom] * 1e-3) / 1e9
@@ -414,7 +394,6 @@ def main():
         "flushed_step_ms_p50": flushed_ms,
         "measured_copy_GBps": copy_gbs,
         "frac_of_measured_copy": dom_gbs / copy_gbs,
-        "measured_read_GBps": read_gbs,
         "phases_ms": phases,
         "algorithmic_bytes": ab,
     }
