@@ -143,6 +143,38 @@ def test_csa_many_queries_long_chunks(tables, k, efmt):
             close_bf16(got[b, qq], ref)
 
 
+@pytest.mark.parametrize("H,k", [(32, 512), (128, 700)])
+def test_csa_many_queries_other_head_counts(tables, H, k):
+    """16+ queries per sequence with H != 64 take the 16-head-group kernel in
+    its long-chunk form (640-row chunks, ids staged in LDS), merged when the
+    list spans several chunks."""
+    cos, sin = tables
+    B, Q, N = 1, 17, 1500
+    rng = np.random.default_rng(2000 + H)
+    q = synth.bf16_round(rng.standard_normal((B, Q, H, 512)).astype(np.float32))
+    WR = Q + 127
+    win = synth.bf16_round(rng.standard_normal((B, WR, 512)).astype(np.float32))
+    ent = synth.bf16_round(rng.standard_normal((B, N, 512)).astype(np.float32))
+    sink = rng.standard_normal(H).astype(np.float32)
+    P = np.array([4 * N - Q], np.int32)
+    base = P - 127
+    pos = P[:, None] + np.arange(Q, dtype=np.int32)[None]
+    ids = np.stack([np.stack([gen_ids(rng, min((int(p) + 1) // 4, N), k, N) for p in pos[b]])
+                    for b in range(B)])
+    say(f"csa attn long chunks H={H} k={k}")
+    out = torch.empty((B, Q, H, 512), dtype=torch.bfloat16, device="cuda")
+    ws = _lib.workspace(_lib.csa_sparse_attn_workspace_size(B, Q, H, k))
+    _lib.csa_sparse_attn_decode(bf16(q), "bf16", bf16(win), "bf16", _lib.WIN_LINEAR, i32(base), WR,
+                                bf16(ent), "bf16", N, i32(ids), k, i32(pos), B, Q, H, f32(sink),
+                                512 ** -0.5, cos, sin, out, "bf16", ws)
+    got = to_np(out)
+    for qq in range(Q):
+        ref = oracle_sparse(q[0, qq].astype(np.float64), win[0].astype(np.float64),
+                            ent[0].astype(np.float64), ids[0, qq], sink, int(pos[0, qq]),
+                            "linear", int(base[0]), WR)
+        close_bf16(got[0, qq], ref)
+
+
 @pytest.mark.parametrize("efmt", ["bf16", "fp8_mx32", "fp4_e4m3_16"])
 def test_hca_decode(tables, efmt):
     cos, sin = tables
