@@ -32,6 +32,12 @@
  *     function; they never cause an out-of-bounds access.
  *   - Results are bitwise reproducible run to run and batch-invariant: the
  *     output for one sequence does not depend on the batch it is part of.
+ *     Kernels are chosen by the shape of a call per sequence, never by the
+ *     batch: with 12 or more queries per sequence (bf16 index keys) the
+ *     indexer scores tiles of queries together, bit-identically to one-query
+ *     calls; with 16 or more queries per sequence the sparse attention takes
+ *     640-row chunks (64 heads: all heads per work-group), which may round
+ *     differently from the 64-row chunks of fewer queries.
  *   - Positions are absolute token positions (0-based).  Compressed entry ids
  *     are 0-based in compressed space; -1 means "no row".
  */
