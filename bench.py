@@ -320,6 +320,9 @@ def main():
                          "lines of an earlier step in the 256 MB last-level cache)")
     ap.add_argument("--cpu-seqs", type=int, default=2)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-flush", action="store_true",
+                    help="skip the flushed-cache steps (kernel-trace runs: their averages then "
+                         "cover only the steady-state steps)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy three times (the known-size "
                          "reference for HBM byte counters) and exit")
@@ -362,7 +365,7 @@ def main():
     ms = time_steps(layer, a.steps, torch)
     phases = time_phases(layer, a.steps, torch)
     pct = step_percentiles(layer, a.steps, torch)
-    flushed_ms = flushed_steps(layer, a.steps, torch)
+    flushed_ms = None if a.no_flush else flushed_steps(layer, a.steps, torch)
     copy_gbs = copy_bandwidth(torch)
     ab = algorithmic_bytes(w)
     dom = "csa_index_topk" if w.ratio == 4 else "hca_attn_decode"
