@@ -27,6 +27,17 @@ Readings where the pages are silent (all listed in the design notes):
   codes.  Element 2j sits in the low nibble of byte j.  Row = D/2 code bytes
   followed by D/16 scale bytes.
 * bf16 is the top half of an IEEE float32, rounded to nearest even.
+
+FP4 indexer keys ("DeepSeek-V4 deep dive", section 5.2 implementation notes:
+index keys and queries in MXFP4 after the Hadamard rotation; the OCP MX
+format, E2M1 elements with one E8M0 scale per 32):
+* MXFP4-MX32 group = 32 consecutive dims.  Shared exponent X =
+  floor(log2(amax)) - 2 (2 is E2M1's largest exponent), clamped to
+  [-127, 127]; amax == 0 gives X = -127.  Code = RNE onto the E2M1 grid of
+  x / 2**X, ties to the even code, saturating at 6.  A group holding NaN/Inf
+  gets the E8M0 NaN byte 0xFF and zero codes.  Element 2j sits in the low
+  nibble of byte j.  Row = D/2 code bytes followed by D/32 scale bytes
+  (X + 127): 68 B per 128-d key.
 """
 
 import numpy as np
@@ -213,15 +224,62 @@ def dequantize_fp4_e4m3_16(row, dim):
 
 
 # ----------------------------------------------------------------------------
+# MXFP4 with E8M0 scale per 32 (OCP MX FP4): 68 B per 128-d index key
+# ----------------------------------------------------------------------------
+
+def mx4_exponent(amax):
+    """floor(log2(amax)) - 2, clamped to [-127, 127]; amax == 0 gives -127."""
+    amax = np.asarray(amax, dtype=np.float64)
+    _, ex = np.frexp(np.where(amax > 0, amax, 1.0))
+    X = ex.astype(np.int64) - 1 - 2
+    X = np.where(amax > 0, X, -127)
+    return np.clip(X, -127, 127)
+
+
+def fp4_mx32_row_bytes(dim):
+    return dim // 2 + dim // 32
+
+
+def quantize_fp4_mx32(x):
+    """x: [..., D] float32-representable -> uint8 [..., D/2 + D/32]."""
+    x = np.asarray(x, dtype=np.float32).astype(np.float64)
+    D = x.shape[-1]
+    assert D % 32 == 0
+    g = x.reshape(x.shape[:-1] + (D // 32, 32))
+    fin = np.isfinite(g)
+    allfin = np.all(fin, axis=-1)
+    amax = np.max(np.where(fin, np.abs(g), 0.0), axis=-1)
+    X = mx4_exponent(amax)
+    y = np.where(fin, g, 0.0) * np.exp2(-X.astype(np.float64))[..., None]
+    codes = np.where(allfin[..., None], e2m1_encode(y), 0).astype(np.uint8)
+    codes = codes.reshape(x.shape[:-1] + (D,))
+    packed = (codes[..., 0::2] | (codes[..., 1::2] << 4)).astype(np.uint8)
+    scales = np.where(allfin, X + 127, 0xFF).astype(np.uint8)
+    return np.concatenate([packed, scales], axis=-1)
+
+
+def dequantize_fp4_mx32(row, dim):
+    row = np.asarray(row, dtype=np.uint8)
+    packed = row[..., :dim // 2].astype(np.int64)
+    codes = np.empty(row.shape[:-1] + (dim,), dtype=np.int64)
+    codes[..., 0::2] = packed & 0xF
+    codes[..., 1::2] = packed >> 4
+    sb = row[..., dim // 2:dim // 2 + dim // 32].astype(np.int64)
+    sc = np.where(sb == 0xFF, np.nan, np.exp2((sb - 127).astype(np.float64)))
+    v = e2m1_decode(codes).reshape(row.shape[:-1] + (dim // 32, 32)) * sc[..., None]
+    return v.reshape(row.shape[:-1] + (dim,))
+
+
+# ----------------------------------------------------------------------------
 # generic helpers
 # ----------------------------------------------------------------------------
 
-FORMATS = ("f32", "bf16", "fp8_mx32", "fp4_e4m3_16")
+FORMATS = ("f32", "bf16", "fp8_mx32", "fp4_e4m3_16", "fp4_mx32")
 
 
 def row_bytes(fmt, dim):
     return {"f32": 4 * dim, "bf16": 2 * dim, "fp8_mx32": fp8_mx32_row_bytes(dim),
-            "fp4_e4m3_16": fp4_row_bytes(dim)}[fmt]
+            "fp4_e4m3_16": fp4_row_bytes(dim), "fp4_mx32": fp4_mx32_row_bytes(dim)}[fmt]
 
 
 def store(x, fmt):
@@ -239,6 +297,9 @@ def store(x, fmt):
     if fmt == "fp4_e4m3_16":
         r = quantize_fp4_e4m3_16(x.astype(np.float32))
         return r, dequantize_fp4_e4m3_16(r, x.shape[-1])
+    if fmt == "fp4_mx32":
+        r = quantize_fp4_mx32(x.astype(np.float32))
+        return r, dequantize_fp4_mx32(r, x.shape[-1])
     raise ValueError(fmt)
 
 
@@ -252,4 +313,6 @@ def load(stored, fmt, dim):
         return dequantize_fp8_mx32(stored, dim)
     if fmt == "fp4_e4m3_16":
         return dequantize_fp4_e4m3_16(stored, dim)
+    if fmt == "fp4_mx32":
+        return dequantize_fp4_mx32(stored, dim)
     raise ValueError(fmt)

@@ -195,6 +195,54 @@ def test_fp4_scale_rule_float32():
     assert r[257] == 0 and r[8] == 0
 
 
+def test_fp4_mx32_row_size_and_exponent_rule():
+    # index keys of the FP4 indexer: 132 B (FP8) -> 68 B per 128-d key
+    assert codec.fp4_mx32_row_bytes(128) == 68 and codec.row_bytes("fp4_mx32", 512) == 272
+    # X = floor(log2 amax) - 2, brute force over exact powers of two
+    for amax in [1.0, 1.5, 3.99, 4.0, 6.0, 7.9, 2.0 ** -100, 2.0 ** 100, 1e-45, 3e38]:
+        want = max(-127, min(127, math.floor(math.log2(amax)) - 2))
+        assert int(codec.mx4_exponent(np.array([amax]))[0]) == want, amax
+    assert int(codec.mx4_exponent(np.array([0.0]))[0]) == -127
+
+
+def test_fp4_mx32_codes_bruteforce_and_grid_roundtrip():
+    rng = np.random.default_rng(8)
+    grid = codec.E2M1_GRID
+    # brute force: every element is the nearest grid value times 2**X, ties to
+    # the even code, saturating at 6 * 2**X
+    x = (rng.standard_normal((64, 128)) * rng.choice([1e-3, 1.0, 50.0], (64, 1))).astype(np.float32)
+    r = codec.quantize_fp4_mx32(x)
+    assert r.shape == (64, 68)
+    v = codec.dequantize_fp4_mx32(r, 128)
+    for i in range(64):
+        for gi in range(4):
+            grp = x[i, 32 * gi:32 * gi + 32].astype(np.float64)
+            X = math.floor(math.log2(np.abs(grp).max())) - 2
+            assert r[i, 64 + gi] == X + 127
+            for j, y in enumerate(grp / 2.0 ** X):
+                dist = np.abs(grid - min(abs(y), 6.0))
+                best = np.flatnonzero(dist == dist.min())
+                c = int(best[0]) if len(best) == 1 else int([b for b in best if b % 2 == 0][0])
+                assert v[i, 32 * gi + j] == math.copysign(grid[c], y) * 2.0 ** X
+    # grid values with an amax of 4 or 6 in the top binade survive exactly
+    g = rng.choice(grid, size=(5, 4, 32)) * rng.choice([-1, 1], size=(5, 4, 32))
+    g[..., 0] = rng.choice([4.0, 6.0], size=(5, 4))
+    k = rng.integers(-20, 20, size=(5, 4))
+    xg = (g * np.exp2(k)[..., None]).reshape(5, 128)
+    np.testing.assert_array_equal(codec.dequantize_fp4_mx32(codec.quantize_fp4_mx32(xg), 128), xg)
+    # saturation: amax 7 * 2**k has X = k and stores 6 * 2**k; zero group -> byte 0, codes 0
+    z = np.zeros(128, np.float32)
+    z[0] = 7.0 * 2 ** -3
+    rz = codec.quantize_fp4_mx32(z)
+    assert rz[64] == 127 - 3 and (rz[0] & 0xF) == 7 and rz[65] == 0 and not rz[16:32].any()
+    assert codec.dequantize_fp4_mx32(rz, 128)[0] == 6.0 * 2 ** -3
+    # non-finite group: NaN scale byte, zero codes, decodes to NaN
+    z[40] = np.inf
+    rn = codec.quantize_fp4_mx32(z)
+    assert rn[65] == 0xFF and not rn[16:32].any()
+    assert np.isnan(codec.dequantize_fp4_mx32(rn, 128)[32:64]).all()
+
+
 def test_bf16_rne():
     x = np.array([1.0, 1.0 + 2 ** -8, 1.0 + 3 * 2 ** -8, 1.0 + 2 ** -8 + 2 ** -20], np.float32)
     np.testing.assert_array_equal(codec.round_to_bf16(x),
