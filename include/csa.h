@@ -68,8 +68,15 @@ enum {
   CSA_BF16 = 1,         /* 2*dim bytes                                                   */
   CSA_FP8_MX32 = 2,     /* dim OCP-E4M3FN codes, then dim/32 E8M0 scale bytes (e + 127):
                            528 B for dim 512, 132 B for dim 128                          */
-  CSA_FP4_E4M3_16 = 3   /* dim/2 bytes of E2M1 codes (element 2j in the low nibble of
+  CSA_FP4_E4M3_16 = 3,  /* dim/2 bytes of E2M1 codes (element 2j in the low nibble of
                            byte j), then dim/16 E4M3 scale bytes: 288 B for dim 512      */
+  CSA_FP4_MX32 = 4      /* OCP MX FP4 ("DeepSeek-V4 deep dive" section 5.2 notes: the
+                           FP4 indexer): dim/2 bytes of E2M1 codes (element 2j in the low
+                           nibble of byte j), then dim/32 E8M0 scale bytes X + 127 with
+                           X = floor(log2 amax) - 2 clamped to [-127, 127] (amax 0 ->
+                           -127); codes RNE(x / 2^X) saturating at 6; a non-finite group
+                           gets scale 0xFF and zero codes.  68 B per 128-d index key.
+                           Index keys and kv_quantize / kv_dequantize only.            */
 };
 
 /* Addressing of the raw sliding-window rows. */
@@ -201,6 +208,21 @@ csa_status csa_index_topk(const void* q_idx, int q_fmt, const float* w_idx, cons
                           int k_fmt, const int32_t* pos, int ratio, int B, int Q, int Hi,
                           int64_t Nmax, int topk, int32_t* out_idx, float* out_scores, void* ws,
                           size_t ws_bytes, csa_stream_t stream);
+
+/* The FP4 indexer's scoring ("DeepSeek-V4 deep dive" section 5.2 notes: FP4
+ * index keys and queries after the Hadamard rotation, BF16 index scores):
+ * exactly csa_index_topk, except that every score is rounded to bf16
+ * (round to nearest even; NaN stays NaN) before it is stored in out_scores and
+ * ranked.  Ties that the rounding creates are broken by the smaller index, as
+ * in csa_index_topk.  Meant for k_fmt = CSA_FP4_MX32 keys (68 B per key) with
+ * bf16 queries that carry FP4 values (an E2M1 code times a power of two is
+ * exact in bf16); any k_fmt that csa_index_topk accepts is accepted.  Same
+ * arguments, workspace size and errors.                                      */
+csa_status csa_index_topk_bf16(const void* q_idx, int q_fmt, const float* w_idx,
+                               const void* k_idx, int k_fmt, const int32_t* pos, int ratio,
+                               int B, int Q, int Hi, int64_t Nmax, int topk, int32_t* out_idx,
+                               float* out_scores, void* ws, size_t ws_bytes,
+                               csa_stream_t stream);
 
 /* Top-k alone over given float32 scores [R][ld]: row r ranks its first
  * n_valid[r] entries (clamped to [0, ld]) with the same order rule as above.

@@ -13,9 +13,10 @@ import os
 
 import torch
 
-F32, BF16, FP8_MX32, FP4_E4M3_16 = 0, 1, 2, 3
+F32, BF16, FP8_MX32, FP4_E4M3_16, FP4_MX32 = 0, 1, 2, 3, 4
 WIN_RING128, WIN_LINEAR = 0, 1
-FMT_NAMES = {"f32": F32, "bf16": BF16, "fp8_mx32": FP8_MX32, "fp4_e4m3_16": FP4_E4M3_16}
+FMT_NAMES = {"f32": F32, "bf16": BF16, "fp8_mx32": FP8_MX32, "fp4_e4m3_16": FP4_E4M3_16,
+             "fp4_mx32": FP4_MX32}
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libcsa.so")
 
@@ -60,6 +61,8 @@ _SIGS = {
     "csa_index_topk_workspace_size": (_SZ, [_I, _I, _I64, _I]),
     "csa_index_topk": (_I, [_VP, _I, _VP, _VP, _I, _VP, _I, _I, _I, _I, _I64, _I, _VP, _VP, _VP,
                             _SZ, _VP]),
+    "csa_index_topk_bf16": (_I, [_VP, _I, _VP, _VP, _I, _VP, _I, _I, _I, _I, _I64, _I, _VP, _VP,
+                                 _VP, _SZ, _VP]),
     "csa_topk_workspace_size": (_SZ, [_I64, _I64, _I]),
     "csa_topk": (_I, [_VP, _VP, _I64, _I64, _I, _VP, _VP, _SZ, _VP]),
     "csa_sparse_attn_workspace_size": (_SZ, [_I, _I, _I, _I]),
@@ -193,6 +196,15 @@ def csa_index_topk(q_idx, q_fmt, w_idx, k_idx, k_fmt, pos, ratio, B, Q, Hi, Nmax
                                 int(topk), _ptr(out_idx), _ptr(out_scores), _ptr(ws),
                                 ws.numel() if ws is not None else 0, _stream(stream)),
            "csa_index_topk")
+
+
+def csa_index_topk_bf16(q_idx, q_fmt, w_idx, k_idx, k_fmt, pos, ratio, B, Q, Hi, Nmax, topk,
+                        out_idx, out_scores, ws, stream=None):
+    _check(lib().csa_index_topk_bf16(_ptr(q_idx), _fmt(q_fmt), _ptr(w_idx), _ptr(k_idx),
+                                     _fmt(k_fmt), _ptr(pos), int(ratio), int(B), int(Q), int(Hi),
+                                     int(Nmax), int(topk), _ptr(out_idx), _ptr(out_scores),
+                                     _ptr(ws), ws.numel() if ws is not None else 0,
+                                     _stream(stream)), "csa_index_topk_bf16")
 
 
 def csa_topk_workspace_size(R, ld, topk):

@@ -42,7 +42,10 @@ bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 #define REQUIRE_PTR(p) \
   REQUIRE((p) != nullptr && aligned16(p), CSA_EINVAL, "%s must be a non-null 16-byte aligned pointer", #p)
 
-bool valid_fmt(int f) { return f >= CSA_F32 && f <= CSA_FP4_E4M3_16; }
+bool valid_fmt(int f) { return f >= CSA_F32 && f <= CSA_FP4_MX32; }
+// cache rows that attention and the compressor read or write (MXFP4-MX32 is
+// an index-key format)
+bool row_fmt(int f) { return f >= CSA_F32 && f <= CSA_FP4_E4M3_16; }
 
 }  // namespace
 
@@ -68,6 +71,7 @@ size_t kv_row_bytes(int fmt, int dim) {
     case CSA_BF16: return (size_t)dim * 2;
     case CSA_FP8_MX32: return dim % 32 ? 0 : (size_t)dim + dim / 32;
     case CSA_FP4_E4M3_16: return dim % 32 ? 0 : (size_t)dim / 2 + dim / 16;
+    case CSA_FP4_MX32: return dim % 32 ? 0 : (size_t)dim / 2 + dim / 32;
     default: return 0;
   }
 }
@@ -114,6 +118,8 @@ csa_status kv_quantize(const void* src, int src_fmt, void* dst, int dst_fmt, int
   REQUIRE(valid_fmt(dst_fmt), CSA_EUNSUPPORTED, "unknown dst_fmt %d", dst_fmt);
   REQUIRE(dst_fmt != CSA_FP8_MX32 || dim % 128 == 0, CSA_EUNSUPPORTED,
           "FP8_MX32 rows need dim % 128 == 0 (4-byte aligned rows)");
+  REQUIRE(dst_fmt != CSA_FP4_MX32 || dim % 128 == 0, CSA_EUNSUPPORTED,
+          "FP4_MX32 rows need dim % 128 == 0 (4-byte aligned rows)");
   if (rows == 0) return ok();
   REQUIRE_PTR(src);
   REQUIRE_PTR(dst);
@@ -129,6 +135,8 @@ csa_status kv_dequantize(const void* src, int src_fmt, void* dst, int dst_fmt, i
   REQUIRE(dst_fmt == CSA_F32 || dst_fmt == CSA_BF16, CSA_EUNSUPPORTED, "dst_fmt must be F32 or BF16");
   REQUIRE(src_fmt != CSA_FP8_MX32 || dim % 128 == 0, CSA_EUNSUPPORTED,
           "FP8_MX32 rows need dim % 128 == 0 (4-byte aligned rows)");
+  REQUIRE(src_fmt != CSA_FP4_MX32 || dim % 128 == 0, CSA_EUNSUPPORTED,
+          "FP4_MX32 rows need dim % 128 == 0 (4-byte aligned rows)");
   if (rows == 0) return ok();
   REQUIRE_PTR(src);
   REQUIRE_PTR(dst);
@@ -147,7 +155,9 @@ static csa_status check_compress(const csa_compress_args* a) {
   REQUIRE(!a->rotate || a->head_dim == 128, CSA_EUNSUPPORTED, "rotate needs head_dim 128");
   REQUIRE(a->x_fmt == CSA_F32 || a->x_fmt == CSA_BF16, CSA_EUNSUPPORTED, "x_fmt must be F32 or BF16");
   REQUIRE(a->w_fmt == CSA_F32 || a->w_fmt == CSA_BF16, CSA_EUNSUPPORTED, "w_fmt must be F32 or BF16");
-  REQUIRE(valid_fmt(a->entry_fmt), CSA_EUNSUPPORTED, "unknown entry_fmt");
+  REQUIRE(row_fmt(a->entry_fmt) || (a->entry_fmt == CSA_FP4_MX32 && a->head_dim == 128),
+          CSA_EUNSUPPORTED, "entry_fmt must be F32, BF16, FP8_MX32, FP4_E4M3_16, or FP4_MX32 "
+          "for 128-d index keys");
   REQUIRE(a->rope_rows >= 1, CSA_EINVAL, "rope_rows must be >= 1");
   REQUIRE(a->entries_cap >= 0, CSA_EINVAL, "entries_cap must be >= 0");
   REQUIRE(a->eps >= 0 && isfinite(a->eps), CSA_EINVAL, "eps must be finite and >= 0");
@@ -238,10 +248,10 @@ size_t csa_index_topk_workspace_size(int B, int Q, int64_t Nmax, int topk) {
          align_up((size_t)R * (size_t)Nmax * 4, 256);
 }
 
-csa_status csa_index_topk(const void* q_idx, int q_fmt, const float* w_idx, const void* k_idx,
+static csa_status index_topk(const void* q_idx, int q_fmt, const float* w_idx, const void* k_idx,
                           int k_fmt, const int32_t* pos, int ratio, int B, int Q, int Hi,
                           int64_t Nmax, int topk, int32_t* out_idx, float* out_scores, void* ws,
-                          size_t ws_bytes, csa_stream_t stream) {
+                          size_t ws_bytes, csa_stream_t stream, int bf16_scores) {
   REQUIRE(B >= 1 && Q >= 1, CSA_EINVAL, "B and Q must be >= 1");
   REQUIRE(Nmax >= 1 && Nmax <= (int64_t)1 << 30, CSA_EINVAL, "Nmax must be in [1, 2^30]");
   REQUIRE(ratio >= 1, CSA_EINVAL, "ratio must be >= 1");
@@ -251,8 +261,8 @@ csa_status csa_index_topk(const void* q_idx, int q_fmt, const float* w_idx, cons
     REQUIRE(q_fmt == CSA_F32, CSA_EUNSUPPORTED, "F32 keys need F32 queries");
     REQUIRE(Hi <= 128, CSA_EUNSUPPORTED, "Hi must be <= 128");
   } else {
-    REQUIRE(k_fmt == CSA_BF16 || k_fmt == CSA_FP8_MX32, CSA_EUNSUPPORTED,
-            "k_fmt must be F32, BF16 or FP8_MX32");
+    REQUIRE(k_fmt == CSA_BF16 || k_fmt == CSA_FP8_MX32 || k_fmt == CSA_FP4_MX32,
+            CSA_EUNSUPPORTED, "k_fmt must be F32, BF16, FP8_MX32 or FP4_MX32");
     REQUIRE(q_fmt == CSA_BF16, CSA_EUNSUPPORTED, "BF16/FP8 keys need BF16 queries");
     REQUIRE(Hi % 16 == 0 && Hi <= 128, CSA_EUNSUPPORTED, "Hi must be a multiple of 16, <= 128");
   }
@@ -276,9 +286,26 @@ csa_status csa_index_topk(const void* q_idx, int q_fmt, const float* w_idx, cons
   hipError_t e = launch_topk_clear(w, R, s);
   if (e == hipSuccess)
     e = launch_index_scores(q_idx, q_fmt, w_idx, k_idx, k_fmt, pos, ratio, B, Q, Hi, Nmax,
-                            scores, nvis, w, s);
+                            scores, nvis, w, bf16_scores, s);
   if (e == hipSuccess) e = launch_topk_select(scores, nvis, R, Nmax, topk, out_idx, w, s);
   return launched(e, "csa_index_topk");
+}
+
+csa_status csa_index_topk(const void* q_idx, int q_fmt, const float* w_idx, const void* k_idx,
+                          int k_fmt, const int32_t* pos, int ratio, int B, int Q, int Hi,
+                          int64_t Nmax, int topk, int32_t* out_idx, float* out_scores, void* ws,
+                          size_t ws_bytes, csa_stream_t stream) {
+  return index_topk(q_idx, q_fmt, w_idx, k_idx, k_fmt, pos, ratio, B, Q, Hi, Nmax, topk, out_idx,
+                    out_scores, ws, ws_bytes, stream, 0);
+}
+
+csa_status csa_index_topk_bf16(const void* q_idx, int q_fmt, const float* w_idx,
+                               const void* k_idx, int k_fmt, const int32_t* pos, int ratio,
+                               int B, int Q, int Hi, int64_t Nmax, int topk, int32_t* out_idx,
+                               float* out_scores, void* ws, size_t ws_bytes,
+                               csa_stream_t stream) {
+  return index_topk(q_idx, q_fmt, w_idx, k_idx, k_fmt, pos, ratio, B, Q, Hi, Nmax, topk, out_idx,
+                    out_scores, ws, ws_bytes, stream, 1);
 }
 
 // ---------------------------------------------------------------- attention
@@ -288,7 +315,8 @@ static csa_status check_attn(const AttnArgs& a) {
           "H must be a multiple of 16 in [16, 1024]");
   REQUIRE(a.q_fmt == CSA_F32 || a.q_fmt == CSA_BF16, CSA_EUNSUPPORTED, "q_fmt must be F32 or BF16");
   REQUIRE(a.out_fmt == CSA_F32 || a.out_fmt == CSA_BF16, CSA_EUNSUPPORTED, "out_fmt must be F32 or BF16");
-  REQUIRE(valid_fmt(a.win_fmt) && valid_fmt(a.ent_fmt), CSA_EUNSUPPORTED, "unknown row format");
+  REQUIRE(row_fmt(a.win_fmt) && row_fmt(a.ent_fmt), CSA_EUNSUPPORTED,
+          "window and entry rows must be F32, BF16, FP8_MX32 or FP4_E4M3_16");
   if (a.q_fmt == CSA_BF16)
     REQUIRE(a.win_fmt != CSA_F32 && a.ent_fmt != CSA_F32, CSA_EUNSUPPORTED,
             "F32 rows need F32 queries");

@@ -52,6 +52,16 @@ __device__ __forceinline__ void decode_fp8_group(const uint8_t* codes, uint8_t s
     for (int j = 0; j < 4; ++j) v[4 * q + j] = e4m3_to_f32(w[q] >> (8 * j)) * f;
 }
 
+__device__ __forceinline__ void decode_fp4mx_group(const uint8_t* codes, uint8_t scale, float* v) {
+  const float sv = scale == 0xFFu ? __uint_as_float(0x7fc00000u) : exp2i((int)scale - 127);
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    uint32_t b = codes[j];
+    v[2 * j] = e2m1_to_f32(b & 15u) * sv;
+    v[2 * j + 1] = e2m1_to_f32(b >> 4) * sv;
+  }
+}
+
 __device__ __forceinline__ void decode_fp4_group(const uint8_t* codes, uint8_t scale, float* v) {
   float sv = e4m3_to_f32(scale);
 #pragma unroll
@@ -85,9 +95,12 @@ __global__ void quantize_kernel(const void* __restrict__ src, int src_fmt, uint8
   int gi = (int)(g % gpr);
   float v[32];
   for (int j = 0; j < gsz; ++j) v[j] = load_val(src, src_fmt, r * dim + (int64_t)gi * gsz + j);
-  size_t rb = dst_fmt == CSA_FP8_MX32 ? (size_t)dim + dim / 32 : (size_t)dim / 2 + dim / 16;
+  size_t rb = dst_fmt == CSA_FP8_MX32   ? (size_t)dim + dim / 32
+             : dst_fmt == CSA_FP4_MX32 ? (size_t)dim / 2 + dim / 32
+                                       : (size_t)dim / 2 + dim / 16;
   uint8_t* row = dst + r * rb;
   if (dst_fmt == CSA_FP8_MX32) encode_fp8_group(v, row + gi * 32, row + dim + gi);
+  else if (dst_fmt == CSA_FP4_MX32) encode_fp4mx_group(v, row + gi * 16, row + dim / 2 + gi);
   else encode_fp4_group(v, row + gi * 8, row + dim / 2 + gi);
 }
 
@@ -107,6 +120,9 @@ __global__ void dequantize_kernel(const uint8_t* __restrict__ src, int src_fmt, 
   } else if (src_fmt == CSA_FP8_MX32) {
     const uint8_t* row = src + r * ((size_t)dim + dim / 32);
     decode_fp8_group(row + gi * 32, row[dim + gi], v);
+  } else if (src_fmt == CSA_FP4_MX32) {
+    const uint8_t* row = src + r * ((size_t)dim / 2 + dim / 32);
+    decode_fp4mx_group(row + gi * 16, row[dim / 2 + gi], v);
   } else {
     const uint8_t* row = src + r * ((size_t)dim / 2 + dim / 16);
     decode_fp4_group(row + gi * 8, row[dim / 2 + gi], v);

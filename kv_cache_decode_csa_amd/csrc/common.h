@@ -154,6 +154,40 @@ __device__ __forceinline__ void encode_fp4_group(const float* v, uint8_t* codes,
   }
 }
 
+// MXFP4-MX32: one 32-value group -> 16 code bytes + one E8M0 scale byte.
+// X = floor(log2 amax) - 2 (clamped to [-127, 127], amax 0 -> -127); codes
+// RNE(x / 2^X) onto E2M1 (exact power-of-two scaling), saturating at 6; a
+// group holding a non-finite value gets scale 0xFF and zero codes.
+__device__ __forceinline__ int mx4_exponent(float amax) {
+  const uint32_t b = __float_as_uint(amax);
+  const uint32_t ef = b >> 23;
+  if (ef == 0) return -127;  // zero or below 2**-126: clamps
+  const int X = (int)ef - 127 - 2;
+  return X < -127 ? -127 : (X > 127 ? 127 : X);
+}
+
+__device__ __forceinline__ void encode_fp4mx_group(const float* v, uint8_t* codes,
+                                                   uint8_t* scale) {
+  float amax = 0.f;
+  bool allfin = true;
+#pragma unroll
+  for (int j = 0; j < 32; ++j) {
+    const float a = __builtin_fabsf(v[j]);
+    if (a <= 3.402823466e38f) amax = fmaxf(amax, a); else allfin = false;
+  }
+  const int X = mx4_exponent(amax);
+  *scale = allfin ? (uint8_t)(X + 127) : (uint8_t)0xFF;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {  // rows are 4-byte aligned
+    uint32_t w = 0;
+    if (allfin) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) w |= f32_to_e2m1(ldexpf(v[8 * q + j], -X)) << (4 * j);
+    }
+    ((uint32_t*)codes)[q] = w;
+  }
+}
+
 // ---------------------------------------------------------------- wave helpers
 __device__ __forceinline__ float shfl_xor_f(float v, int m) { return __shfl_xor(v, m, 64); }
 

@@ -536,6 +536,20 @@ __device__ __forceinline__ void store_elem(int fmt, float v, int c, int d, bool 
                    c3 = __shfl_down(code, 3, 64);
     if (live && (c & 3) == 0) *(uint32_t*)(row + c) = code | (c1 << 8) | (c2 << 16) | (c3 << 24);
     if (live && (c & 31) == 0) row[d + (c >> 5)] = (uint8_t)(e + 127);
+  } else if (fmt == CSA_FP4_MX32) {
+    float amax = fin ? av : 0.f;
+    float bad = fin ? 0.f : 1.f;
+#pragma unroll
+    for (int m = 1; m < 32; m <<= 1) {
+      amax = fmaxf(amax, shfl_xor_f(amax, m));
+      bad = fmaxf(bad, shfl_xor_f(bad, m));
+    }
+    const bool allfin = bad == 0.f;
+    const int X = mx4_exponent(amax);
+    const uint32_t code = allfin ? f32_to_e2m1(ldexpf(v, -X)) : 0u;
+    const uint32_t odd = __shfl_down(code, 1, 64);
+    if (live && (c & 1) == 0) row[c >> 1] = (uint8_t)(code | (odd << 4));
+    if (live && (c & 31) == 0) row[d / 2 + (c >> 5)] = allfin ? (uint8_t)(X + 127) : (uint8_t)0xFF;
   } else {
     float amax = fin ? av : 0.f;
     float bad = fin ? 0.f : 1.f;

@@ -49,7 +49,7 @@ hipError_t launch_topk_select(const float* scores, const int32_t* n_valid, int64
 hipError_t launch_index_scores(const void* q_idx, int q_fmt, const float* w_idx,
                                const void* k_idx, int k_fmt, const int32_t* pos, int ratio, int B,
                                int Q, int Hi, int64_t Nmax, float* scores, int32_t* n_vis,
-                               TopkWs w, hipStream_t s);
+                               TopkWs w, int bf16_scores, hipStream_t s);
 
 struct AttnArgs {
   const void* q; int q_fmt;

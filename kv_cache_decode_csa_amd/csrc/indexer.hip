@@ -13,6 +13,13 @@ namespace csa {
 
 namespace {
 
+// RNE to bf16, kept as a float (NaN stays NaN)
+__device__ __forceinline__ float round_bf16(float x) {
+  const uint32_t u = __float_as_uint(x);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return x;
+  return __uint_as_float((u + 0x7fffu + ((u >> 16) & 1u)) & 0xffff0000u);
+}
+
 constexpr int kIdxThreads = 256;
 // Work-groups per row: Nmax / 4096 .. Nmax / 512 keys' worth, the fewest that
 // give about 512 work-groups for the launch (a per-key score does not depend
@@ -22,7 +29,11 @@ constexpr int kMaxKeysPerWg = 4096;
 constexpr int64_t kTargetWgs = 512;
 // 16-key MFMA tiles per wave step: FP8 rows are small enough to keep four
 // tiles (64 keys, 8.4 KB per wave) and their successors in flight.
-template <int KFMT> constexpr int tiles_per_iter() { return KFMT == CSA_FP8_MX32 ? 4 : 2; }
+template <int KFMT> constexpr bool packed_key() { return KFMT == CSA_FP8_MX32 || KFMT == CSA_FP4_MX32; }
+template <int KFMT> constexpr int tiles_per_iter() { return packed_key<KFMT>() ? 4 : 2; }
+template <int KFMT> constexpr int key_row_bytes() {
+  return KFMT == CSA_FP8_MX32 ? 132 : (KFMT == CSA_FP4_MX32 ? 68 : 256);
+}
 
 // Keys are read with a permuted contraction order: lane (r16, kq) holds, for
 // key r16 of its tile, the 32 contiguous dims [32 kq, 32 kq + 32) -- one FP8
@@ -30,7 +41,8 @@ template <int KFMT> constexpr int tiles_per_iter() { return KFMT == CSA_FP8_MX32
 // fragments use the same order, so every dot product is unchanged while each
 // lane issues one contiguous 32-byte (FP8) or 64-byte (bf16) read per key.
 struct KeyRaw {
-  uint32_t w[16];   // fp8: w[0..7] codes, w[8] scale byte; bf16: w[0..15]
+  uint32_t w[16];   // fp8: w[0..7] codes, w[8] scale byte; fp4: w[0..3] codes, w[8] scale
+                    // byte; bf16: w[0..15]
 };
 
 // Loads are unconditional (callers clamp the key index into the visible range)
@@ -43,6 +55,11 @@ __device__ __forceinline__ void load_key(const uint8_t* kr, int kq, KeyRaw& r) {
 #pragma unroll
     for (int i = 0; i < 8; ++i) r.w[i] = p[i];
     r.w[8] = kr[128 + kq];
+  } else if (KFMT == CSA_FP4_MX32) {
+    const uint32_t* p = (const uint32_t*)(kr + 16 * kq);  // rows of 68 B: dword aligned
+#pragma unroll
+    for (int i = 0; i < 4; ++i) r.w[i] = p[i];
+    r.w[8] = kr[64 + kq];
   } else {
     const uint4* p = (const uint4*)(kr + 64 * kq);
 #pragma unroll
@@ -68,6 +85,21 @@ __device__ __forceinline__ bf16x8_t key_frag(const KeyRaw& r, int s) {
     uint4 u = make_uint4(__builtin_bit_cast(uint32_t, a), __builtin_bit_cast(uint32_t, b),
                          __builtin_bit_cast(uint32_t, c), __builtin_bit_cast(uint32_t, d));
     return as_bf16x8(u);
+  } else if (KFMT == CSA_FP4_MX32) {
+    // dword s holds the 8 codes of dims 32 kq + 8 s .. +8 (element 2j low
+    // nibble of byte j); the hardware conversion applies the power-of-two
+    // scale exactly
+    const uint32_t sb = r.w[8] & 0xffu;
+    const float sc = sb == 0xffu ? __uint_as_float(0x7fc00000u) : exp2i((int)sb - 127);
+    const uint32_t x = r.w[s];
+    typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2_t;
+    bf16x2_t a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(x, sc, 0);
+    bf16x2_t b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(x, sc, 1);
+    bf16x2_t c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(x, sc, 2);
+    bf16x2_t d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(x, sc, 3);
+    uint4 u = make_uint4(__builtin_bit_cast(uint32_t, a), __builtin_bit_cast(uint32_t, b),
+                         __builtin_bit_cast(uint32_t, c), __builtin_bit_cast(uint32_t, d));
+    return as_bf16x8(u);
   } else {
     return as_bf16x8(make_uint4(r.w[4 * s], r.w[4 * s + 1], r.w[4 * s + 2], r.w[4 * s + 3]));
   }
@@ -80,14 +112,14 @@ __device__ __forceinline__ bf16x8_t key_frag(const KeyRaw& r, int s) {
 // bf16: each 256-B row holds exactly 16 pieces; rows are padded to 272 B so
 // the lanes of a fragment read hit distinct banks.
 template <int KFMT> constexpr int stage_pieces() {
-  return (16 * tiles_per_iter<KFMT>() * (KFMT == CSA_FP8_MX32 ? 132 : 256)) / 16;
+  return (16 * tiles_per_iter<KFMT>() * key_row_bytes<KFMT>()) / 16;
 }
 template <int KFMT> constexpr int stage_slots() {
-  return KFMT == CSA_FP8_MX32 ? (stage_pieces<KFMT>() + 63) / 64 * 64
-                              : 16 * tiles_per_iter<KFMT>() * 17;
+  return packed_key<KFMT>() ? (stage_pieces<KFMT>() + 63) / 64 * 64
+                            : 16 * tiles_per_iter<KFMT>() * 17;
 }
 template <int KFMT> __device__ __forceinline__ int stage_slot(int piece) {
-  if (KFMT == CSA_FP8_MX32) return piece;
+  if (packed_key<KFMT>()) return piece;
   const int p = piece < stage_pieces<KFMT>() ? piece : stage_pieces<KFMT>() - 1;
   return (p >> 4) * 17 + (p & 15);
 }
@@ -99,6 +131,11 @@ __device__ __forceinline__ void stage_read(const u32x4_t* st, int r, int kq, Key
 #pragma unroll
     for (int i = 0; i < 8; ++i) f.w[i] = L[8 * kq + i];
     f.w[8] = L[32] >> (8 * kq);
+  } else if (KFMT == CSA_FP4_MX32) {
+    const uint32_t* L = (const uint32_t*)st + r * 17;  // 68 B = 17 dwords per row
+#pragma unroll
+    for (int i = 0; i < 4; ++i) f.w[i] = L[4 * kq + i];
+    f.w[8] = L[16] >> (8 * kq);
   } else {
     const u32x4_t* L = st + r * 17 + 4 * kq;
 #pragma unroll
@@ -131,12 +168,14 @@ struct Scorer {
   uint4 qa[HT][4];  // A operand: head 16 mt + r16, dims 32 kq + 8 s .. +8
   float wv[HT][4];  // head weights in the D layout: head 16 mt + 4 kq + r
   int r16, kq;
+  bool bf16s;       // scores rounded to bf16 (RNE) before they are stored and ranked
 
   __device__ __forceinline__ void load(const uint16_t* q_idx, const float* w_idx, int64_t row,
-                                       int lane) {
+                                       int lane, int bf16_scores) {
     constexpr int Hi = HT * 16;
     r16 = lane & 15;
     kq = lane >> 4;
+    bf16s = bf16_scores != 0;
     const uint16_t* qrow = q_idx + row * (int64_t)Hi * kIndexDim;
 #pragma unroll
     for (int mt = 0; mt < HT; ++mt)
@@ -208,7 +247,7 @@ struct Scorer {
       c = a;
     }
     swap_halves32(a, c);
-    const float sc = 0.5f * (a + c);
+    const float sc = bf16s ? round_bf16(0.5f * (a + c)) : 0.5f * (a + c);
     const int64_t key = k + 16 * kq + r16;
     if (live && (kTiles == 4 || kq < kTiles) && key < end) {
       srow[key] = sc;
@@ -224,8 +263,8 @@ __global__ void __launch_bounds__(kIdxThreads) index_scores_mfma(
     const uint16_t* __restrict__ q_idx, const float* __restrict__ w_idx,
     const uint8_t* __restrict__ k_idx, const int32_t* __restrict__ pos, int ratio, int Q,
     int64_t Nmax, int64_t row_off, float* __restrict__ scores,
-    int32_t* __restrict__ n_vis_out, uint32_t* __restrict__ hist_g) {
-  constexpr int64_t kRowBytes = KFMT == CSA_FP8_MX32 ? 132 : 256;
+    int32_t* __restrict__ n_vis_out, uint32_t* __restrict__ hist_g, int bf16_scores) {
+  constexpr int64_t kRowBytes = key_row_bytes<KFMT>();
   constexpr int kTilesPerIter = tiles_per_iter<KFMT>();
   constexpr int kKeysPerIter = 16 * kTilesPerIter;
   constexpr int kStagePieces = stage_pieces<KFMT>();
@@ -249,7 +288,7 @@ __global__ void __launch_bounds__(kIdxThreads) index_scores_mfma(
   for (int i = t; i < kHistBins; i += kIdxThreads) hist[i] = 0;
 
   Scorer<HT, KFMT> sc;
-  sc.load(q_idx, w_idx, row, lane);
+  sc.load(q_idx, w_idx, row, lane, bf16_scores);
   const int r16 = sc.r16, kq = sc.kq;
   __syncthreads();
 
@@ -356,7 +395,7 @@ __global__ void __launch_bounds__(kSplitThreads) index_scores_split(
     const uint16_t* __restrict__ q_idx, const float* __restrict__ w_idx,
     const uint8_t* __restrict__ k_idx, const int32_t* __restrict__ pos, int ratio, int Q,
     int64_t Nmax, int64_t row_off, float* __restrict__ scores,
-    int32_t* __restrict__ n_vis_out, uint32_t* __restrict__ hist_g) {
+    int32_t* __restrict__ n_vis_out, uint32_t* __restrict__ hist_g, int bf16_scores) {
   constexpr int KFMT = CSA_FP8_MX32;
   constexpr int64_t kRowBytes = 132;
   constexpr int kSub = kSplitStep / 4;                 // keys per quarter (one wave)
@@ -425,7 +464,7 @@ __global__ void __launch_bounds__(kSplitThreads) index_scores_split(
     }
   } else {
     Scorer<HT, KFMT> sc;
-    sc.load(q_idx, w_idx, row, lane);
+    sc.load(q_idx, w_idx, row, lane, bf16_scores);
     float* srow = scores + row * Nmax;
     __syncthreads();
     for (int64_t k = 0; k < n_iter; ++k) {
@@ -466,7 +505,7 @@ __global__ void __launch_bounds__(kQThreads) index_scores_qtile(
     const uint16_t* __restrict__ q_idx, const float* __restrict__ w_idx,
     const uint8_t* __restrict__ k_idx, const int32_t* __restrict__ pos, int ratio, int Q,
     int64_t Nmax, int keys_per_wg, int64_t tile_off, float* __restrict__ scores,
-    int32_t* __restrict__ n_vis_out, uint32_t* __restrict__ hist_g) {
+    int32_t* __restrict__ n_vis_out, uint32_t* __restrict__ hist_g, int bf16_scores) {
   constexpr int KFMT = CSA_BF16;
   constexpr int64_t kRowBytes = 256;
   static_assert(tiles_per_iter<KFMT>() == 2, "a step is two scorer calls of 32 keys");
@@ -504,7 +543,7 @@ __global__ void __launch_bounds__(kQThreads) index_scores_qtile(
   for (int i = t; i < kQT * kHistBins / 2; i += kQThreads) (&hist[0][0])[i] = 0;
 
   Scorer<HT, KFMT> sc;
-  if (has_q) sc.load(q_idx, w_idx, row, lane);
+  if (has_q) sc.load(q_idx, w_idx, row, lane, bf16_scores);
   float* srow = scores + row * Nmax;
   const uint8_t* kbase = k_idx + b * Nmax * kRowBytes;
   // thread t loads pieces t + 512 u of a step: row p / 16, 16-byte column
@@ -561,7 +600,7 @@ __global__ void __launch_bounds__(kIdxThreads) index_scores_f32(
     const float* __restrict__ q_idx, const float* __restrict__ w_idx,
     const float* __restrict__ k_idx, const int32_t* __restrict__ pos, int ratio, int Q, int Hi,
     int64_t Nmax, int64_t row_off, float* __restrict__ scores, int32_t* __restrict__ n_vis_out,
-    uint32_t* __restrict__ hist_g) {
+    uint32_t* __restrict__ hist_g, int bf16_scores) {
   __shared__ float qs[128 * kIndexDim];
   __shared__ float ws[128];
   __shared__ uint32_t hist[kHistBins];
@@ -590,6 +629,7 @@ __global__ void __launch_bounds__(kIdxThreads) index_scores_f32(
       for (int c = 0; c < kIndexDim; ++c) d = fmaf(qs[h * kIndexDim + c], kv[c], d);
       p = fmaf(ws[h], fmaxf(d, 0.f), p);
     }
+    if (bf16_scores) p = round_bf16(p);
     scores[row * Nmax + key] = p;
     atomicAdd(&hist[score_key(p) >> 20], 1u);
   }
@@ -602,7 +642,7 @@ __global__ void __launch_bounds__(kIdxThreads) index_scores_f32(
 template <int HT>
 hipError_t launch_mfma(const void* q_idx, const float* w_idx, const void* k_idx, int k_fmt,
                        const int32_t* pos, int ratio, int Q, int64_t R, int64_t Nmax,
-                       float* scores, int32_t* n_vis, uint32_t* hist, hipStream_t s) {
+                       float* scores, int32_t* n_vis, uint32_t* hist, int bf16s, hipStream_t s) {
   if (k_fmt == CSA_BF16 && Q >= kQT) {
     // even ranges of at most kQKeysPerWg keys, whole steps
     const int64_t splits = (Nmax + kQKeysPerWg - 1) / kQKeysPerWg;
@@ -614,7 +654,7 @@ hipError_t launch_mfma(const void* q_idx, const float* w_idx, const void* k_idx,
       hipLaunchKernelGGL((index_scores_qtile<HT>), dim3((unsigned)splits, (unsigned)ny),
                          dim3(kQThreads), 0, s, (const uint16_t*)q_idx, w_idx,
                          (const uint8_t*)k_idx, pos, ratio, Q, Nmax, (int)kpw, y0, scores, n_vis,
-                         hist);
+                         hist, bf16s);
     }
     return hipGetLastError();
   }
@@ -628,7 +668,8 @@ hipError_t launch_mfma(const void* q_idx, const float* w_idx, const void* k_idx,
       int64_t nr = R - r0 < 65535 ? R - r0 : 65535;
       hipLaunchKernelGGL((index_scores_split<HT>), dim3((unsigned)gx, (unsigned)nr),
                          dim3(kSplitThreads), 0, s, (const uint16_t*)q_idx, w_idx,
-                         (const uint8_t*)k_idx, pos, ratio, Q, Nmax, r0, scores, n_vis, hist);
+                         (const uint8_t*)k_idx, pos, ratio, Q, Nmax, r0, scores, n_vis, hist,
+                         bf16s);
     }
     return hipGetLastError();
   }
@@ -637,14 +678,16 @@ hipError_t launch_mfma(const void* q_idx, const float* w_idx, const void* k_idx,
   const int64_t gx = (Nmax + kpw - 1) / kpw;
   for (int64_t r0 = 0; r0 < R; r0 += 65535) {
     int64_t nr = R - r0 < 65535 ? R - r0 : 65535;
-    if (k_fmt == CSA_FP8_MX32)
-      hipLaunchKernelGGL((index_scores_mfma<HT, CSA_FP8_MX32>), dim3((unsigned)gx, (unsigned)nr),
+    if (k_fmt == CSA_FP4_MX32)
+      hipLaunchKernelGGL((index_scores_mfma<HT, CSA_FP4_MX32>), dim3((unsigned)gx, (unsigned)nr),
                          dim3(kIdxThreads), 0, s, (const uint16_t*)q_idx, w_idx,
-                         (const uint8_t*)k_idx, pos, ratio, Q, Nmax, r0, scores, n_vis, hist);
+                         (const uint8_t*)k_idx, pos, ratio, Q, Nmax, r0, scores, n_vis, hist,
+                         bf16s);
     else
       hipLaunchKernelGGL((index_scores_mfma<HT, CSA_BF16>), dim3((unsigned)gx, (unsigned)nr),
                          dim3(kIdxThreads), 0, s, (const uint16_t*)q_idx, w_idx,
-                         (const uint8_t*)k_idx, pos, ratio, Q, Nmax, r0, scores, n_vis, hist);
+                         (const uint8_t*)k_idx, pos, ratio, Q, Nmax, r0, scores, n_vis, hist,
+                         bf16s);
   }
   return hipGetLastError();
 }
@@ -654,7 +697,7 @@ hipError_t launch_mfma(const void* q_idx, const float* w_idx, const void* k_idx,
 hipError_t launch_index_scores(const void* q_idx, int q_fmt, const float* w_idx,
                                const void* k_idx, int k_fmt, const int32_t* pos, int ratio, int B,
                                int Q, int Hi, int64_t Nmax, float* scores, int32_t* n_vis,
-                               TopkWs w, hipStream_t s) {
+                               TopkWs w, int bf16_scores, hipStream_t s) {
   const int64_t R = (int64_t)B * Q;
   if (k_fmt == CSA_F32) {
     int64_t gx = (Nmax + kF32Keys - 1) / kF32Keys;
@@ -662,20 +705,20 @@ hipError_t launch_index_scores(const void* q_idx, int q_fmt, const float* w_idx,
       int64_t nr = R - r0 < 65535 ? R - r0 : 65535;
       hipLaunchKernelGGL(index_scores_f32, dim3((unsigned)gx, (unsigned)nr), dim3(kIdxThreads), 0,
                          s, (const float*)q_idx, w_idx, (const float*)k_idx, pos, ratio, Q, Hi,
-                         Nmax, r0, scores, n_vis, w.hist);
+                         Nmax, r0, scores, n_vis, w.hist, bf16_scores);
     }
     return hipGetLastError();
   }
   (void)q_fmt;
   switch (Hi / 16) {
-    case 1: return launch_mfma<1>(q_idx, w_idx, k_idx, k_fmt, pos, ratio, Q, R, Nmax, scores, n_vis, w.hist, s);
-    case 2: return launch_mfma<2>(q_idx, w_idx, k_idx, k_fmt, pos, ratio, Q, R, Nmax, scores, n_vis, w.hist, s);
-    case 3: return launch_mfma<3>(q_idx, w_idx, k_idx, k_fmt, pos, ratio, Q, R, Nmax, scores, n_vis, w.hist, s);
-    case 4: return launch_mfma<4>(q_idx, w_idx, k_idx, k_fmt, pos, ratio, Q, R, Nmax, scores, n_vis, w.hist, s);
-    case 5: return launch_mfma<5>(q_idx, w_idx, k_idx, k_fmt, pos, ratio, Q, R, Nmax, scores, n_vis, w.hist, s);
-    case 6: return launch_mfma<6>(q_idx, w_idx, k_idx, k_fmt, pos, ratio, Q, R, Nmax, scores, n_vis, w.hist, s);
-    case 7: return launch_mfma<7>(q_idx, w_idx, k_idx, k_fmt, pos, ratio, Q, R, Nmax, scores, n_vis, w.hist, s);
-    case 8: return launch_mfma<8>(q_idx, w_idx, k_idx, k_fmt, pos, ratio, Q, R, Nmax, scores, n_vis, w.hist, s);
+    case 1: return launch_mfma<1>(q_idx, w_idx, k_idx, k_fmt, pos, ratio, Q, R, Nmax, scores, n_vis, w.hist, bf16_scores, s);
+    case 2: return launch_mfma<2>(q_idx, w_idx, k_idx, k_fmt, pos, ratio, Q, R, Nmax, scores, n_vis, w.hist, bf16_scores, s);
+    case 3: return launch_mfma<3>(q_idx, w_idx, k_idx, k_fmt, pos, ratio, Q, R, Nmax, scores, n_vis, w.hist, bf16_scores, s);
+    case 4: return launch_mfma<4>(q_idx, w_idx, k_idx, k_fmt, pos, ratio, Q, R, Nmax, scores, n_vis, w.hist, bf16_scores, s);
+    case 5: return launch_mfma<5>(q_idx, w_idx, k_idx, k_fmt, pos, ratio, Q, R, Nmax, scores, n_vis, w.hist, bf16_scores, s);
+    case 6: return launch_mfma<6>(q_idx, w_idx, k_idx, k_fmt, pos, ratio, Q, R, Nmax, scores, n_vis, w.hist, bf16_scores, s);
+    case 7: return launch_mfma<7>(q_idx, w_idx, k_idx, k_fmt, pos, ratio, Q, R, Nmax, scores, n_vis, w.hist, bf16_scores, s);
+    case 8: return launch_mfma<8>(q_idx, w_idx, k_idx, k_fmt, pos, ratio, Q, R, Nmax, scores, n_vis, w.hist, bf16_scores, s);
     default: return hipErrorInvalidValue;
   }
 }

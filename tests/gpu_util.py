@@ -128,10 +128,12 @@ def step_bound(ref, fmt, d):
         return 1e-5 + 1e-5 * np.abs(ref)
     if fmt == "bf16":
         return 1e-3 + 2.0 ** -7 * np.abs(ref)
-    g = 32 if fmt == "fp8_mx32" else 16
+    g = 16 if fmt == "fp4_e4m3_16" else 32
     amax = np.abs(ref).reshape(ref.shape[:-1] + (d // g, g)).max(-1, keepdims=True)
     if fmt == "fp8_mx32":
         step = amax / 448 * 2.0 ** -3 * 2      # coarsest e4m3 spacing in the group, x2 margin
+    elif fmt == "fp4_mx32":
+        step = amax / 4 * 2.0 * 1.2            # E2M1 spacing 2 at the top, times 2**X <= amax / 4
     else:
         step = amax / 6 * 2.0 * 1.2            # coarsest e2m1 spacing (2) times the scale
     return np.broadcast_to(step, ref.shape[:-1] + (d // g, g)).reshape(ref.shape) + 1e-6

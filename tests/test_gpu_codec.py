@@ -34,8 +34,16 @@ def _edge_rows(D, rng):
     return np.array(rows, dtype=np.float32)
 
 
+def oracle_quantize(x, fmt):
+    if fmt == "fp8_mx32":
+        return codec.quantize_fp8_mx32(np.asarray(x, dtype=np.float64))
+    if fmt == "fp4_mx32":
+        return codec.quantize_fp4_mx32(x)
+    return codec.quantize_fp4_e4m3_16(x)
+
+
 @pytest.mark.parametrize("D", [512, 128])
-@pytest.mark.parametrize("fmt", ["fp8_mx32", "fp4_e4m3_16"])
+@pytest.mark.parametrize("fmt", ["fp8_mx32", "fp4_e4m3_16", "fp4_mx32"])
 def test_quantize_bit_exact(D, fmt):
     need_gpu()
     rng = np.random.default_rng(11)
@@ -45,8 +53,7 @@ def test_quantize_bit_exact(D, fmt):
     dst = torch.empty((len(x), rb), dtype=torch.uint8, device="cuda")
     _lib.kv_quantize(f32(x), "f32", dst, fmt, len(x), D)
     got = dst.cpu().numpy()
-    want = (codec.quantize_fp8_mx32(x.astype(np.float64)) if fmt == "fp8_mx32"
-            else codec.quantize_fp4_e4m3_16(x))
+    want = oracle_quantize(x, fmt)
     mism = np.argwhere(got != want)
     assert len(mism) == 0, f"{len(mism)} bytes differ, first {mism[:5].tolist()}"
     # bf16 input path: same bytes as quantizing the bf16 values
@@ -54,19 +61,16 @@ def test_quantize_bit_exact(D, fmt):
     dst2 = torch.empty((len(x) - 9, rb), dtype=torch.uint8, device="cuda")
     _lib.kv_quantize(xb, "bf16", dst2, fmt, len(x) - 9, D)
     xv = xb.float().cpu().numpy()
-    want2 = (codec.quantize_fp8_mx32(xv.astype(np.float64)) if fmt == "fp8_mx32"
-             else codec.quantize_fp4_e4m3_16(xv))
-    np.testing.assert_array_equal(dst2.cpu().numpy(), want2)
+    np.testing.assert_array_equal(dst2.cpu().numpy(), oracle_quantize(xv, fmt))
 
 
-@pytest.mark.parametrize("fmt", ["fp8_mx32", "fp4_e4m3_16"])
+@pytest.mark.parametrize("fmt", ["fp8_mx32", "fp4_e4m3_16", "fp4_mx32"])
 def test_dequantize_exact(fmt):
     need_gpu()
     D = 512
     rng = np.random.default_rng(12)
     x = np.concatenate([_edge_rows(D, rng), rng.standard_normal((500, D)).astype(np.float32)])
-    rows = (codec.quantize_fp8_mx32(x.astype(np.float64)) if fmt == "fp8_mx32"
-            else codec.quantize_fp4_e4m3_16(x))
+    rows = oracle_quantize(x, fmt)
     src = torch.from_numpy(rows).cuda()
     out = torch.empty((len(x), D), dtype=torch.float32, device="cuda")
     _lib.kv_dequantize(src, fmt, out, "f32", len(x), D)

@@ -136,7 +136,7 @@ def test_bulk_bf16_tiled_projection(tables, ratio, d, rotate, entry_fmt):
 @pytest.mark.parametrize("entry_fmt,dim,d,rotate", [("bf16", 512, 512, 0), ("fp8_mx32", 512, 512, 0),
                                                     ("fp4_e4m3_16", 512, 512, 0), ("f32", 512, 512, 0),
                                                     ("fp8_mx32", 4096, 512, 0), ("fp8_mx32", 4096, 128, 1),
-                                                    ("bf16", 4096, 128, 1)])
+                                                    ("bf16", 4096, 128, 1), ("fp4_mx32", 4096, 128, 1)])
 def test_decode_steps_bf16(tables, entry_fmt, dim, d, rotate):
     """Token-by-token calls from a state built by an earlier chunked call; each
     sequence sits at a different offset inside its block.  dim 4096 runs the

@@ -14,6 +14,7 @@ import torch
 
 from kv_cache_decode_csa_amd import _lib, synth
 from oracle import codec, indexer
+from oracle import topk as _TK
 
 from gpu_util import bf16, check_selection, f32, i32, need_gpu, say, score_bound, upload_rows
 
@@ -96,6 +97,74 @@ def test_many_queries_query_tiles(Hi):
             err = np.abs(sc[b, qq, :nv] - S_ref)
             assert np.all(err <= tol), (b, qq, err.max())
             check_selection(out[b, qq], sc[b, qq], S_ref, tol, nv, k)
+
+
+@pytest.mark.parametrize("Hi,N", [(64, 3000), (32, 5001)])
+def test_fp4_keys_against_oracle(Hi, N):
+    """FP4 indexer keys: MXFP4-MX32 rows (68 B), queries carrying MXFP4 values
+    (exact in bf16); float32 scores against the oracle's scores of the decoded
+    values, and the selection."""
+    need_gpu()
+    B, Q, k = 2, 2, 512
+    w = synth.Workload(92, "t", B=B, ctx=4 * N, ratio=4, n_entries=N, Hi=Hi, key_fmt="fp4_mx32")
+    K = synth.index_keys(w)
+    qraw = synth.normal_batched(w.seed, synth.T_QIDX, B, (Q, Hi, 128))
+    qi = codec.store(qraw, "fp4_mx32")[1].astype(np.float32)
+    assert np.array_equal(synth.bf16_round(qi), qi)            # FP4 values are exact in bf16
+    wi = synth.normal_batched(w.seed, synth.T_WIDX, B, (Q, Hi), (128 * Hi) ** -0.5)
+    pos = np.array([[4 * N - 1, 2047], [5, 4 * N + 900]], np.int32)
+    say(f"index_topk fp4_mx32 Hi={Hi} N={N}")
+    kdev = upload_rows(K, "fp4_mx32")
+    # the library's stored rows are the oracle codec's bytes
+    assert np.array_equal(kdev.cpu().numpy(), codec.store(K, "fp4_mx32")[0])
+    Kv = codec.store(K, "fp4_mx32")[1]
+    out = torch.empty((B, Q, k), dtype=torch.int32, device="cuda")
+    sc = torch.full((B, Q, N), float("nan"), dtype=torch.float32, device="cuda")
+    ws = _lib.workspace(_lib.csa_index_topk_workspace_size(B, Q, N, k))
+    _lib.csa_index_topk(bf16(qi), "bf16", f32(wi), kdev, "fp4_mx32", i32(pos), 4, B, Q, Hi, N, k,
+                        out, sc, ws)
+    out = out.cpu().numpy()
+    sc = sc.cpu().numpy()
+    for b in range(B):
+        for qq in range(Q):
+            nv = int(indexer.n_visible(pos[b, qq], 4, N))
+            S_ref = indexer.scores(qi[b, qq].astype(np.float64), wi[b, qq], Kv[b], nv)
+            tol = score_bound(qi[b, qq].astype(np.float64), wi[b, qq].astype(np.float64),
+                              Kv[b][:nv])
+            err = np.abs(sc[b, qq, :nv] - S_ref)
+            assert np.all(err <= tol), (b, qq, err.max())
+            check_selection(out[b, qq], sc[b, qq], S_ref, tol, nv, k)
+
+
+@pytest.mark.parametrize("kfmt,Q", [("fp4_mx32", 2), ("fp8_mx32", 2), ("bf16", 13)])
+def test_bf16_scores(kfmt, Q):
+    """csa_index_topk_bf16 (every kernel: per-query FP4, split FP8, query-tiled
+    bf16): its scores are the float32 call's scores rounded to bf16 (RNE), bit
+    for bit, and its ids are exactly the oracle's top-k of those scores (ties,
+    which the rounding makes common, go to the smaller index)."""
+    need_gpu()
+    B, N, Hi, k = 2, 4000, 64, 512
+    w = synth.Workload(93, "t", B=B, ctx=4 * N, ratio=4, n_entries=N, Hi=Hi, key_fmt=kfmt)
+    K = synth.index_keys(w)
+    qi = synth.bf16_round(synth.normal_batched(w.seed, synth.T_QIDX, B, (Q, Hi, 128)))
+    wi = synth.normal_batched(w.seed, synth.T_WIDX, B, (Q, Hi), (128 * Hi) ** -0.5)
+    pos = (4 * N - 1 - 37 * np.arange(B * Q)).reshape(B, Q).astype(np.int32)
+    say(f"index_topk_bf16 {kfmt} Q={Q}")
+    kdev = upload_rows(K, kfmt)
+    ws = _lib.workspace(_lib.csa_index_topk_workspace_size(B, Q, N, k))
+    res = []
+    for fn in (_lib.csa_index_topk, _lib.csa_index_topk_bf16):
+        out = torch.empty((B, Q, k), dtype=torch.int32, device="cuda")
+        sc = torch.full((B, Q, N), float("nan"), dtype=torch.float32, device="cuda")
+        fn(bf16(qi), "bf16", f32(wi), kdev, kfmt, i32(pos), 4, B, Q, Hi, N, k, out, sc, ws)
+        res.append((out.cpu().numpy(), sc.cpu().numpy()))
+    (o32, s32), (o16, s16) = res
+    for b in range(B):
+        for qq in range(Q):
+            nv = int(indexer.n_visible(pos[b, qq], 4, N))
+            want = codec.round_to_bf16(s32[b, qq, :nv]).astype(np.float32)
+            assert np.array_equal(s16[b, qq, :nv].view(np.uint32), want.view(np.uint32))
+            assert np.array_equal(o16[b, qq], _TK.topk(s16[b, qq, :nv], k, nv)), (b, qq)
 
 
 def test_without_score_output_matches():
