@@ -38,13 +38,13 @@ import numpy as np
 HBM_PEAK_GBS = 8000.0
 MFMA_BF16_PEAK_TFLOPS = 2500.0
 
-WORKLOADS = {"csa_1m_fp8": 5, "csa_1m_mxfp4": 5, "csa_64k_bf16": 2, "hca_1m_bf16": 3,
-             "csa_prefill_32k_bf16": 4}
+WORKLOADS = {"csa_1m_fp8": 5, "csa_1m_mxfp4": 5, "csa_1m_fp4idx": 5, "csa_64k_bf16": 2,
+             "hca_1m_bf16": 3, "csa_prefill_32k_bf16": 4}
 
 
 def row_bytes(fmt, dim):
     return {"f32": 4 * dim, "bf16": 2 * dim, "fp8_mx32": dim + dim // 32,
-            "fp4_e4m3_16": dim // 2 + dim // 16}[fmt]
+            "fp4_e4m3_16": dim // 2 + dim // 16, "fp4_mx32": dim // 2 + dim // 32}[fmt]
 
 
 def algorithmic_bytes(w):
@@ -210,6 +210,28 @@ def copy_bandwidth(torch, nbytes=2 << 30, reps=5):
     return gbs
 
 
+def fp4_recall(layer, w, torch):
+    """Mean overlap of the FP4 indexer's top-k (MXFP4 keys and queries, bf16
+    scores; the last step's output) with the top-k of float32 scores over the
+    unquantized seeded keys and queries, through the library's float32 path."""
+    from kv_cache_decode_csa_amd import _lib, synth
+    B, N = w.B, w.n_entries
+    keys = torch.from_numpy(synth.index_keys(w)).cuda()        # [B, N, 128] f32 values
+    qi, wi = synth.index_queries(w)
+    qf = torch.from_numpy(qi.astype(np.float32)).cuda().reshape(B, 1, w.Hi, 128)
+    wf = torch.from_numpy(wi).cuda().reshape(B, 1, w.Hi)
+    ids = torch.empty((B, 1, w.topk), dtype=torch.int32, device="cuda")
+    ws = _lib.workspace(_lib.csa_index_topk_workspace_size(B, 1, N, w.topk))
+    _lib.csa_index_topk(qf, "f32", wf, keys, "f32", layer.pos, 4, B, 1, w.Hi, N, w.topk, ids,
+                        None, ws)
+    torch.cuda.synchronize()
+    a_ids, b_ids = layer.topk.cpu().numpy()[:, 0], ids.cpu().numpy()[:, 0]
+    rec = [len(set(a_ids[b].tolist()) & set(b_ids[b].tolist())) / w.topk for b in range(B)]
+    del keys, ws
+    torch.cuda.empty_cache()
+    return float(np.mean(rec))
+
+
 def flushed_steps(layer, steps, torch, nbytes=512 << 20):
     """Median single-step time when 512 MB are written between steps (the
     last-level cache then holds none of the step's inputs); the flush itself
@@ -349,6 +371,8 @@ def main():
         return main_prefill(a, w, torch)
     if a.workload == "csa_1m_mxfp4":
         w = synth.mxfp4_variant(w)
+    if a.workload == "csa_1m_fp4idx":
+        w = synth.fp4_indexer_variant(w)
     print(f"# building {a.workload}: B={w.B} ctx={w.ctx} entries={w.n_entries}", file=sys.stderr,
           flush=True)
     t0 = time.time()
@@ -400,6 +424,8 @@ def main():
         "phases_ms": phases,
         "algorithmic_bytes": ab,
     }
+    if w.key_fmt == "fp4_mx32":
+        res["fp4_indexer_recall_vs_f32"] = fp4_recall(layer, w, torch)
     if not a.no_cpu_baseline:
         print("# cpu baseline (oracle)", file=sys.stderr, flush=True)
         res["cpu_baseline"] = cpu_baseline(w, a.cpu_seqs)

@@ -99,6 +99,14 @@ class CsaDecodeLayer:
         self.q = torch.from_numpy(q).to(device).to(qdt).reshape(B, 1, w.H, 512)
         self.sink = torch.from_numpy(sink).to(device)
         self.qi = torch.from_numpy(qi).to(device).to(qdt).reshape(B, 1, w.Hi, 128)
+        if w.key_fmt == "fp4_mx32":
+            # the FP4 indexer's queries carry MXFP4 values: quantize and decode
+            # them with the library's codec (exact in bf16)
+            n = B * w.Hi
+            rows = torch.empty((n, _lib.kv_row_bytes("fp4_mx32", 128)), dtype=torch.uint8,
+                               device=device)
+            _lib.kv_quantize(self.qi.reshape(n, 128), "bf16", rows, "fp4_mx32", n, 128)
+            _lib.kv_dequantize(rows, "fp4_mx32", self.qi.reshape(n, 128), "bf16", n, 128)
         self.wi = torch.from_numpy(wi).to(device).reshape(B, 1, w.Hi)
         self.t = w.t
         self.pos = torch.full((B, 1), self.t, dtype=torch.int32, device=device)
@@ -142,9 +150,12 @@ class CsaDecodeLayer:
                 self.ws_comp[c] = _lib.workspace(need)
             _lib.csa_compress_many(args, self.ws_comp[c])
 
+        # the FP4 indexer ranks bf16 scores
+        index_fn = _lib.csa_index_topk_bf16 if key_fmt == "fp4_mx32" else _lib.csa_index_topk
+
         def index_topk():
-            _lib.csa_index_topk(self.qi, w.q_fmt, self.wi, keys, key_fmt, self.pos, w.ratio, B, 1,
-                                w.Hi, N, w.topk, self.topk, None, self.ws_idx)
+            index_fn(self.qi, w.q_fmt, self.wi, keys, key_fmt, self.pos, w.ratio, B, 1, w.Hi, N,
+                     w.topk, self.topk, None, self.ws_idx)
 
         def sparse_attn():
             _lib.csa_sparse_attn_decode(self.q, w.q_fmt, self.win, win_fmt, _lib.WIN_RING128,

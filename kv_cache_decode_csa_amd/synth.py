@@ -82,6 +82,13 @@ def mxfp4_variant(w):
     return dataclasses.replace(w, name="csa_1m_mxfp4", ent_fmt="fp4_e4m3_16")
 
 
+def fp4_indexer_variant(w):
+    """The workload-5 variant with the FP4 indexer: MXFP4-MX32 index keys (68 B),
+    index queries carrying MXFP4 values, bf16 index scores."""
+    import dataclasses
+    return dataclasses.replace(w, name="csa_1m_fp4idx", key_fmt="fp4_mx32")
+
+
 def rng(seed, tid, idx=0):
     return np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, tid, idx])))
 

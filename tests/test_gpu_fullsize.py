@@ -25,6 +25,7 @@ import torch
 
 from kv_cache_decode_csa_amd import _lib, decode, synth
 from oracle import attention, codec, compressor, indexer, rope
+from oracle import topk as TK
 
 from gpu_util import check_selection, close_bf16, need_gpu, say, score_bound, step_bound, to_np
 
@@ -168,6 +169,63 @@ def test_fullsize_decode_step(name):
         say(f"  b={b}: attention ok")
         del E
         gc.collect()
+    del layer
+    gc.collect()
+    torch.cuda.empty_cache()
+
+
+def test_fullsize_fp4_indexer():
+    """The FP4 indexer at the 1M-context shape, as bench.py runs it: MXFP4-MX32
+    index keys (68 B), index queries carrying MXFP4 values, bf16 scores.  One
+    decode step, then for the first and last sequence: stored keys bit-exact
+    against the oracle codec, the queries' FP4 values equal the oracle's, every
+    visible bf16 score within the float32 bound plus one bf16 step of the
+    oracle's, and the ids exactly the oracle's top-k of the library's scores."""
+    need_gpu()
+    w = synth.fp4_indexer_variant(synth.WORKLOADS[5])
+    say(f"full-size step {w.name}: B={w.B} ctx={w.ctx} entries={w.n_entries}")
+    layer = decode.CsaDecodeLayer(w, copies=1)
+    layer.step()
+    torch.cuda.synchronize()
+    om = rope.frequencies(w.theta, rope.V4_YARN)
+    t, N, B = w.t, w.n_entries, w.B
+    keys_dev = layer.sets[0][1]
+    sc = torch.empty((B, 1, N), dtype=torch.float32, device="cuda")
+    ids2 = torch.empty_like(layer.topk)
+    _lib.csa_index_topk_bf16(layer.qi, "bf16", layer.wi, keys_dev, "fp4_mx32", layer.pos, 4, B, 1,
+                             w.Hi, N, w.topk, ids2, sc, layer.ws_idx)
+    torch.cuda.synchronize()
+    ids = layer.topk.cpu().numpy()[:, 0]
+    assert np.array_equal(ids2.cpu().numpy()[:, 0], ids), "selection differs between calls"
+    S16 = sc.cpu().numpy()[:, 0]
+    qdev = layer.qi.float().cpu().numpy()[:, 0]
+    rng = np.random.default_rng(98)
+    nv = int(indexer.n_visible(t, 4, N))
+    new_i = [t // 4 - 1, t // 4]
+    for b in (0, B - 1):
+        qraw, wi = synth.index_queries(w, [b])
+        qv = codec.store(qraw[0], "fp4_mx32")[1]
+        assert np.array_equal(qdev[b], qv), "index queries are not the oracle's MXFP4 values"
+        kv = synth.index_keys(w, [b])[0]
+        kst, kval = codec.store(kv, "fp4_mx32")
+        samp = rng.choice(N - 2, 256, replace=False)
+        got_b = keys_dev[b].index_select(0, torch.from_numpy(samp).cuda()).cpu().numpy()
+        assert np.array_equal(got_b, kst[samp]), "stored index keys differ"
+        ref_key = oracle_new_entries(w, b, 128, True, om)
+        for i in new_i:                                     # rows the compressor wrote
+            kval[i] = codec.store(ref_key[i], "fp4_mx32")[1]
+        S_ref = indexer.scores(qv, wi[0].astype(np.float64), kval, nv)
+        tol = score_bound(qv, wi[0].astype(np.float64), kval[:nv])
+        # the compressor's emitted keys may differ from the oracle's by one FP4 step
+        kstep = np.zeros_like(kval[:nv])
+        for i in new_i:
+            kstep[i] = step_bound(ref_key[i], "fp4_mx32", 128)
+        tol = tol + (kstep @ np.abs(qv).T) @ np.abs(wi[0])
+        ulp = np.abs(S_ref) * 2.0 ** -8 + 1e-30             # one bf16 step (RNE: half of it)
+        err = np.abs(S16[b, :nv] - S_ref)
+        assert np.all(err <= tol + ulp), (b, err.max())
+        assert np.array_equal(ids[b], TK.topk(S16[b, :nv], w.topk, nv)), b
+        say(f"  b={b}: FP4 keys, queries, bf16 scores and selection ok (max err {err.max():.2e})")
     del layer
     gc.collect()
     torch.cuda.empty_cache()
