@@ -38,7 +38,8 @@ import numpy as np
 HBM_PEAK_GBS = 8000.0
 MFMA_BF16_PEAK_TFLOPS = 2500.0
 
-WORKLOADS = {"csa_1m_fp8": 5, "csa_1m_mxfp4": 5, "csa_1m_fp4idx": 5, "csa_64k_bf16": 2,
+WORKLOADS = {"csa_1m_fp8": 5, "csa_1m_mxfp4": 5, "csa_1m_fp4idx": 5, "csa_1m_fp8_layer": 5,
+             "csa_64k_bf16": 2,
              "hca_1m_bf16": 3, "csa_prefill_32k_bf16": 4}
 
 
@@ -69,6 +70,15 @@ def algorithmic_bytes(w):
         out["csa_sparse_attn_decode"] = B * (k * row_bytes(w.ent_fmt, 512) + k * 4
                                              + 128 * row_bytes(w.win_fmt, 512)
                                              + 2 * w.H * 512 * qb) + w.H * 4
+        cfg = w.extra.get("layer")
+        if cfg:  # weights once, the token's inputs and outputs (intermediates excluded)
+            qr, g, r = cfg["q_rank"], cfg["groups"], cfg["o_rank"]
+            wts = dim * qr + qr * w.H * 512 + dim * 512 + qr * w.Hi * 128 + dim * w.Hi
+            out["csa_layer_input"] = (2 * wts + 4 * (qr + 512) + B * dim * 2
+                                      + B * (w.H * 512 * 2 + w.Hi * 128 * 2 + w.Hi * 4)
+                                      + B * row_bytes(w.win_fmt, 512))
+            out["csa_layer_output"] = (2 * (r * w.H * 512 + dim * g * r)
+                                       + B * w.H * 512 * 2 + B * dim * 2)
     else:
         n_vis = min((w.t + 1) // w.ratio, N)
         out["hca_attn_decode"] = B * (n_vis * row_bytes(w.ent_fmt, 512)
@@ -298,10 +308,21 @@ def cpu_baseline(w, n_seq, min_seconds=10.0):
             keys_st = codec.store(synth.index_keys(w, br)[0], w.key_fmt)[0]
         prepared.append((q, sink, win_st, ent, keys_st, qi, wi))
     t = w.t
+    cfg = w.extra.get("layer")
+    if cfg:  # the layer's input and output steps are timed too
+        from oracle import layer as OL
+        lw = {k: v.astype(np.float64) for k, v in synth.layer_weights(
+            w.seed, w.dim, cfg["q_rank"], w.H, w.Hi, cfg["groups"], cfg["o_rank"]).items()}
+        lw.update(H=w.H, Hi=w.Hi)
+        xs = [synth.hidden(w, 1, idx=b)[0].astype(np.float64) for b in range(n_seq)]
     passes = 0
     while t_total < min_seconds and passes < 50:
         passes += 1
-        for (q, sink, win_st, ent, keys_st, qi, wi) in prepared:
+        for si, (q, sink, win_st, ent, keys_st, qi, wi) in enumerate(prepared):
+            if cfg:
+                t0 = time.perf_counter()
+                OL.layer_input(xs[si], t, lw, om)
+                t_total += time.perf_counter() - t0
             if w.ratio == 4:
                 t0 = time.perf_counter()
                 K = codec.load(keys_st, w.key_fmt, 128)
@@ -319,15 +340,18 @@ def cpu_baseline(w, n_seq, min_seconds=10.0):
             wid = attention.window_ids(t)
             rows = np.concatenate([Wv[np.maximum(wid, 0)], E])
             valid = np.concatenate([wid >= 0, ids >= 0])
-            attention.attend(q[0].astype(np.float64), rows, valid, sink, 512 ** -0.5, t, om)
+            o = attention.attend(q[0].astype(np.float64), rows, valid, sink, 512 ** -0.5, t, om)
+            if cfg:
+                OL.output_projection(o, lw["wo_a"], lw["wo_b"])
             t_total += time.perf_counter() - t0
     n_tok = passes * n_seq
     return {"value": n_tok / t_total, "unit": "tokens/s/layer", "cores": int(threads),
             "kind": "oracle",
             "sample": f"{n_seq} of {w.B} sequences of the same workload at full context "
                       f"({w.n_entries} entries each), {passes} passes ({n_tok} token-steps); "
-                      f"timed: key decode, scoring, top-k, row decode and attention in float64 "
-                      f"NumPy, {t_total:.1f} s"}
+                      f"timed: {'layer input steps, ' if cfg else ''}key decode, scoring, "
+                      f"top-k, row decode and attention{', output projection' if cfg else ''} "
+                      f"in float64 NumPy, {t_total:.1f} s"}
 
 
 def main():
@@ -373,6 +397,8 @@ def main():
         w = synth.mxfp4_variant(w)
     if a.workload == "csa_1m_fp4idx":
         w = synth.fp4_indexer_variant(w)
+    if a.workload == "csa_1m_fp8_layer":
+        w = synth.layer_variant(w)
     print(f"# building {a.workload}: B={w.B} ctx={w.ctx} entries={w.n_entries}", file=sys.stderr,
           flush=True)
     t0 = time.time()

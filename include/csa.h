@@ -274,6 +274,69 @@ csa_status hca_attn_decode(const void* q, int q_fmt, const void* win, int win_fm
                            const float* rope_sin, int64_t rope_rows, void* out, int out_fmt,
                            void* ws, size_t ws_bytes, csa_stream_t stream);
 
+/* ------------------------------------------------------------------------ layer input / output
+ * The attention layer's steps on either side of the decode path, for M = B*T
+ * tokens (T per sequence, row m = b*T + i at position pos[m]).
+ *
+ * csa_layer_input ("DeepSeek-V4 deep dive" sections 3.2, 3.3, 3.4 notes, 5.2):
+ *   qr = RMSNorm(wq_a x) * q_norm, rounded to bf16 (the shared query latent);
+ *   q[m][h]  = RoPE_p(v_h / sqrt(mean(v_h^2) + eps)),  v = wq_b qr split into
+ *              H heads of 512 (the per-head rescale has no weight);
+ *   kv       = RoPE_p(RMSNorm(wkv x) * kv_norm), stored in win_fmt into row
+ *              p mod 128 of sequence b's window ring win[b][128][row]
+ *              (skipped for p < 0);
+ *   when Hi > 0 (CSA layers):
+ *   q_idx[m][h] = H128 RoPE_p(u_h) / sqrt(128),  u = wq_b_idx qr split into Hi
+ *              heads of 128, H128 the Sylvester Hadamard matrix;
+ *   w_idx[m][h] = (w_proj x)_h / sqrt(128 * Hi).
+ *   RMSNorm(v) = v / sqrt(mean(v^2) + eps); RoPE_p rotates the last 64 dims at
+ *   position p as csa_rope_table describes (p clamped to [0, rope_rows-1]).
+ *   x: [M][dim] bf16.  Outputs: q [M][H][512] bf16, q_idx [M][Hi][128] bf16,
+ *   w_idx [M][Hi] float (both unused when Hi == 0), win in win_fmt (F32, BF16,
+ *   FP8_MX32 or FP4_E4M3_16 rows of 512).
+ * csa_layer_output (section 3.5, grouped low-rank output projection):
+ *   the H heads of o form `groups` groups of H/groups consecutive heads;
+ *   mid[m][g*o_rank + r] = sum_d o[m][g][d] wo_a[g][r][d]   (rounded to bf16)
+ *   y[m][n] = sum_j mid[m][j] wo_b[n][j],  y in y_fmt (F32 or BF16).
+ *   o: [M][H][512] bf16 (the attention output, RoPE already undone).
+ * Weights (device, bf16 unless noted; row-major [out][in]):
+ *   wq_a [q_rank][dim]; q_norm [q_rank] float; wq_b [H*512][q_rank];
+ *   wkv [512][dim]; kv_norm [512] float; wq_b_idx [Hi*128][q_rank];
+ *   w_proj [Hi][dim]; wo_a [groups][o_rank][H/groups*512]; wo_b [dim][groups*o_rank].
+ *   Pointers a call does not use may be NULL (the output weights for
+ *   csa_layer_input, the input weights for csa_layer_output, the index
+ *   weights when Hi == 0).
+ * Products use bf16 operands with float32 accumulation; the K split of each
+ * product depends on the weight shapes only, so results do not depend on B.
+ * Requirements: 1 <= M <= 64; dim and q_rank positive multiples of 256;
+ * 1 <= H <= 128; 0 <= Hi <= 64; groups >= 1 with H % groups == 0; o_rank a
+ * positive multiple of 32; eps finite and >= 0.  Workspaces: the matching
+ * *_workspace_size(w, M) bytes, 16-byte aligned.  Errors: CSA_EINVAL for null
+ * or misaligned pointers and bad sizes, CSA_EUNSUPPORTED for formats,
+ * CSA_EWORKSPACE for a short workspace.                                        */
+typedef struct {
+  int dim, q_rank, H, Hi, groups, o_rank;
+  const void* wq_a;
+  const float* q_norm;
+  const void* wq_b;
+  const void* wkv;
+  const float* kv_norm;
+  const void* wq_b_idx;
+  const void* w_proj;
+  const void* wo_a;
+  const void* wo_b;
+  float eps;
+} csa_layer_weights;
+
+size_t csa_layer_input_workspace_size(const csa_layer_weights* w, int M);
+csa_status csa_layer_input(const csa_layer_weights* w, const void* x, const int32_t* pos, int B,
+                           int T, const float* rope_cos, const float* rope_sin, int64_t rope_rows,
+                           void* q, void* q_idx, float* w_idx, void* win, int win_fmt, void* ws,
+                           size_t ws_bytes, csa_stream_t stream);
+size_t csa_layer_output_workspace_size(const csa_layer_weights* w, int M);
+csa_status csa_layer_output(const csa_layer_weights* w, const void* o, int M, void* y, int y_fmt,
+                            void* ws, size_t ws_bytes, csa_stream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

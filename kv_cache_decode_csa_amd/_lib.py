@@ -44,6 +44,17 @@ class CompressArgs(ctypes.Structure):
     ]
 
 
+class LayerWeights(ctypes.Structure):
+    _fields_ = [
+        ("dim", ctypes.c_int), ("q_rank", ctypes.c_int), ("H", ctypes.c_int), ("Hi", ctypes.c_int),
+        ("groups", ctypes.c_int), ("o_rank", ctypes.c_int),
+        ("wq_a", ctypes.c_void_p), ("q_norm", ctypes.c_void_p), ("wq_b", ctypes.c_void_p),
+        ("wkv", ctypes.c_void_p), ("kv_norm", ctypes.c_void_p), ("wq_b_idx", ctypes.c_void_p),
+        ("w_proj", ctypes.c_void_p), ("wo_a", ctypes.c_void_p), ("wo_b", ctypes.c_void_p),
+        ("eps", ctypes.c_float),
+    ]
+
+
 _VP, _I, _I64, _SZ, _F, _D = (ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_size_t,
                               ctypes.c_float, ctypes.c_double)
 
@@ -71,6 +82,11 @@ _SIGS = {
     "hca_attn_workspace_size": (_SZ, [_I, _I, _I, _I64]),
     "hca_attn_decode": (_I, [_VP, _I, _VP, _I, _I, _VP, _I64, _VP, _I, _I64, _I, _VP, _I, _I, _I,
                              _VP, _F, _VP, _VP, _I64, _VP, _I, _VP, _SZ, _VP]),
+    "csa_layer_input_workspace_size": (_SZ, [ctypes.POINTER(LayerWeights), _I]),
+    "csa_layer_input": (_I, [ctypes.POINTER(LayerWeights), _VP, _VP, _I, _I, _VP, _VP, _I64, _VP,
+                             _VP, _VP, _VP, _I, _VP, _SZ, _VP]),
+    "csa_layer_output_workspace_size": (_SZ, [ctypes.POINTER(LayerWeights), _I]),
+    "csa_layer_output": (_I, [ctypes.POINTER(LayerWeights), _VP, _I, _VP, _I, _VP, _SZ, _VP]),
 }
 
 EXPORTS = tuple(_SIGS)
@@ -245,3 +261,38 @@ def hca_attn_decode(q, q_fmt, win, win_fmt, win_mode, win_base, win_rows, entrie
         int(Q), int(H), _ptr(sink), float(scale), _ptr(rope_cos), _ptr(rope_sin),
         int(rope_cos.shape[0]), _ptr(out), _fmt(out_fmt), _ptr(ws),
         ws.numel() if ws is not None else 0, _stream(stream)), "hca_attn_decode")
+
+
+def make_layer_weights(*, dim, q_rank, H, Hi, groups, o_rank, wq_a=None, q_norm=None, wq_b=None,
+                       wkv=None, kv_norm=None, wq_b_idx=None, w_proj=None, wo_a=None, wo_b=None,
+                       eps=1e-6):
+    """The C struct of device pointers; it keeps the tensors alive, since the
+    struct holds only their addresses."""
+    t = (wq_a, q_norm, wq_b, wkv, kv_norm, wq_b_idx, w_proj, wo_a, wo_b)
+    lw = LayerWeights(int(dim), int(q_rank), int(H), int(Hi), int(groups), int(o_rank),
+                      *[_ptr(x) for x in t], float(eps))
+    lw._tensors = t
+    return lw
+
+
+def csa_layer_input_workspace_size(w, M):
+    return int(lib().csa_layer_input_workspace_size(ctypes.byref(w), int(M)))
+
+
+def csa_layer_input(w, x, pos, B, T, rope_cos, rope_sin, q, q_idx, w_idx, win, win_fmt, ws,
+                    stream=None):
+    _check(lib().csa_layer_input(ctypes.byref(w), _ptr(x), _ptr(pos), int(B), int(T),
+                                 _ptr(rope_cos), _ptr(rope_sin), int(rope_cos.shape[0]), _ptr(q),
+                                 _ptr(q_idx), _ptr(w_idx), _ptr(win), _fmt(win_fmt), _ptr(ws),
+                                 ws.numel() if ws is not None else 0, _stream(stream)),
+           "csa_layer_input")
+
+
+def csa_layer_output_workspace_size(w, M):
+    return int(lib().csa_layer_output_workspace_size(ctypes.byref(w), int(M)))
+
+
+def csa_layer_output(w, o, M, y, y_fmt, ws, stream=None):
+    _check(lib().csa_layer_output(ctypes.byref(w), _ptr(o), int(M), _ptr(y), _fmt(y_fmt), _ptr(ws),
+                                  ws.numel() if ws is not None else 0, _stream(stream)),
+           "csa_layer_output")

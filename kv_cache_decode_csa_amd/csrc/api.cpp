@@ -414,4 +414,84 @@ csa_status hca_attn_decode(const void* q, int q_fmt, const void* win, int win_fm
   return run_attn(a, ws, ws_bytes, (hipStream_t)stream);
 }
 
+// ---------------------------------------------------------------- layer input / output
+static csa_status check_layer_shape(const csa_layer_weights* w, int M) {
+  REQUIRE(w != nullptr, CSA_EINVAL, "weights must not be null");
+  REQUIRE(M >= 1 && M <= 64, CSA_EUNSUPPORTED, "M = B*T must be in [1, 64] (got %d)", M);
+  REQUIRE(w->dim >= 256 && w->dim % 256 == 0, CSA_EINVAL, "dim must be a positive multiple of 256");
+  REQUIRE(w->q_rank >= 256 && w->q_rank % 256 == 0, CSA_EINVAL,
+          "q_rank must be a positive multiple of 256");
+  REQUIRE(w->H >= 1 && w->H <= 128, CSA_EUNSUPPORTED, "H must be in [1, 128]");
+  REQUIRE(w->Hi >= 0 && w->Hi <= 64, CSA_EUNSUPPORTED, "Hi must be in [0, 64]");
+  REQUIRE(w->groups >= 1 && w->H % w->groups == 0, CSA_EINVAL, "groups must divide H");
+  REQUIRE(w->o_rank >= 32 && w->o_rank % 32 == 0, CSA_EINVAL,
+          "o_rank must be a positive multiple of 32");
+  REQUIRE(w->eps >= 0 && isfinite(w->eps), CSA_EINVAL, "eps must be finite and >= 0");
+  return CSA_OK;
+}
+
+size_t csa_layer_input_workspace_size(const csa_layer_weights* w, int M) {
+  if (check_layer_shape(w, M) != CSA_OK) return 0;
+  return layer_input_ws_bytes(w, M);
+}
+
+size_t csa_layer_output_workspace_size(const csa_layer_weights* w, int M) {
+  if (check_layer_shape(w, M) != CSA_OK) return 0;
+  return layer_output_ws_bytes(w, M);
+}
+
+csa_status csa_layer_input(const csa_layer_weights* w, const void* x, const int32_t* pos, int B,
+                           int T, const float* rope_cos, const float* rope_sin, int64_t rope_rows,
+                           void* q, void* q_idx, float* w_idx, void* win, int win_fmt, void* ws,
+                           size_t ws_bytes, csa_stream_t stream) {
+  REQUIRE(B >= 1 && T >= 1, CSA_EINVAL, "B and T must be >= 1");
+  REQUIRE((int64_t)B * T <= 64, CSA_EUNSUPPORTED, "M = B*T must be in [1, 64]");
+  const int M = B * T;
+  csa_status st = check_layer_shape(w, M);
+  if (st != CSA_OK) return st;
+  REQUIRE(row_fmt(win_fmt), CSA_EUNSUPPORTED,
+          "win_fmt must be F32, BF16, FP8_MX32 or FP4_E4M3_16");
+  REQUIRE(rope_rows >= 1, CSA_EINVAL, "rope_rows must be >= 1");
+  REQUIRE_PTR(w->wq_a);
+  REQUIRE_PTR(w->q_norm);
+  REQUIRE_PTR(w->wq_b);
+  REQUIRE_PTR(w->wkv);
+  REQUIRE_PTR(w->kv_norm);
+  REQUIRE_PTR(x);
+  REQUIRE_PTR(pos);
+  REQUIRE_PTR(rope_cos);
+  REQUIRE_PTR(rope_sin);
+  REQUIRE_PTR(q);
+  REQUIRE_PTR(win);
+  if (w->Hi > 0) {
+    REQUIRE_PTR(w->wq_b_idx);
+    REQUIRE_PTR(w->w_proj);
+    REQUIRE_PTR(q_idx);
+    REQUIRE_PTR(w_idx);
+  }
+  const size_t need = layer_input_ws_bytes(w, M);
+  REQUIRE(ws != nullptr && aligned16(ws) && ws_bytes >= need, CSA_EWORKSPACE,
+          "workspace of %zu bytes needed (got %zu)", need, ws_bytes);
+  return launched(launch_layer_input(w, x, pos, B, T, rope_cos, rope_sin, rope_rows, q, q_idx,
+                                     w_idx, win, win_fmt, kv_row_bytes(win_fmt, kHeadDim), ws,
+                                     (hipStream_t)stream),
+                  "csa_layer_input");
+}
+
+csa_status csa_layer_output(const csa_layer_weights* w, const void* o, int M, void* y, int y_fmt,
+                            void* ws, size_t ws_bytes, csa_stream_t stream) {
+  csa_status st = check_layer_shape(w, M);
+  if (st != CSA_OK) return st;
+  REQUIRE(y_fmt == CSA_F32 || y_fmt == CSA_BF16, CSA_EUNSUPPORTED, "y_fmt must be F32 or BF16");
+  REQUIRE_PTR(w->wo_a);
+  REQUIRE_PTR(w->wo_b);
+  REQUIRE_PTR(o);
+  REQUIRE_PTR(y);
+  const size_t need = layer_output_ws_bytes(w, M);
+  REQUIRE(ws != nullptr && aligned16(ws) && ws_bytes >= need, CSA_EWORKSPACE,
+          "workspace of %zu bytes needed (got %zu)", need, ws_bytes);
+  return launched(launch_layer_output(w, o, M, y, y_fmt, ws, (hipStream_t)stream),
+                  "csa_layer_output");
+}
+
 }  // extern "C"

@@ -517,57 +517,6 @@ __device__ float pool_block(const CompArgs& a, int64_t b, int64_t p0, int64_t i,
   return sq;
 }
 
-// Store element c of a finished row: lanes c .. c+31 (FP8) or c .. c+15 (FP4)
-// of one group are consecutive lanes of a wave, so the group's amax is a
-// shuffle reduction and every lane encodes its own value (the same per-value
-// arithmetic as the one-thread group encoders).  Every lane of the wave must
-// call it (values past d are passed as 0 with live = false).
-__device__ __forceinline__ void store_elem(int fmt, float v, int c, int d, bool live, uint8_t* row) {
-  const float av = __builtin_fabsf(v);
-  const bool fin = av <= 3.402823466e38f;
-  if (fmt == CSA_FP8_MX32) {
-    float amax = fin ? av : 0.f;
-#pragma unroll
-    for (int m = 1; m < 32; m <<= 1) amax = fmaxf(amax, shfl_xor_f(amax, m));
-    const int e = mx32_exponent(amax);
-    const uint32_t code = f32_to_e4m3(ldexpf(v, -e));
-    // gather 4 codes into the lane holding the first one (rows are 4-byte aligned)
-    const uint32_t c1 = __shfl_down(code, 1, 64), c2 = __shfl_down(code, 2, 64),
-                   c3 = __shfl_down(code, 3, 64);
-    if (live && (c & 3) == 0) *(uint32_t*)(row + c) = code | (c1 << 8) | (c2 << 16) | (c3 << 24);
-    if (live && (c & 31) == 0) row[d + (c >> 5)] = (uint8_t)(e + 127);
-  } else if (fmt == CSA_FP4_MX32) {
-    float amax = fin ? av : 0.f;
-    float bad = fin ? 0.f : 1.f;
-#pragma unroll
-    for (int m = 1; m < 32; m <<= 1) {
-      amax = fmaxf(amax, shfl_xor_f(amax, m));
-      bad = fmaxf(bad, shfl_xor_f(bad, m));
-    }
-    const bool allfin = bad == 0.f;
-    const int X = mx4_exponent(amax);
-    const uint32_t code = allfin ? f32_to_e2m1(ldexpf(v, -X)) : 0u;
-    const uint32_t odd = __shfl_down(code, 1, 64);
-    if (live && (c & 1) == 0) row[c >> 1] = (uint8_t)(code | (odd << 4));
-    if (live && (c & 31) == 0) row[d / 2 + (c >> 5)] = allfin ? (uint8_t)(X + 127) : (uint8_t)0xFF;
-  } else {
-    float amax = fin ? av : 0.f;
-    float bad = fin ? 0.f : 1.f;
-#pragma unroll
-    for (int m = 1; m < 16; m <<= 1) {
-      amax = fmaxf(amax, shfl_xor_f(amax, m));
-      bad = fmaxf(bad, shfl_xor_f(bad, m));
-    }
-    const bool allfin = bad == 0.f;
-    const uint32_t sc = allfin ? f32_to_e4m3(__fdiv_rn(amax, 6.0f)) : 0x7fu;
-    const float sv = e4m3_to_f32(sc);
-    const uint32_t code = (allfin && sv > 0.f) ? f32_to_e2m1(__fdiv_rn(v, sv)) : 0u;
-    const uint32_t odd = __shfl_down(code, 1, 64);
-    if (live && (c & 1) == 0) row[c >> 1] = (uint8_t)(code | (odd << 4));
-    if (live && (c & 15) == 0) row[d / 2 + (c >> 4)] = (uint8_t)sc;
-  }
-}
-
 // Norm weights and rotation factors at position i * r of this thread's
 // channels (d <= 512 = 2 kThreads).
 struct NormRope {

@@ -75,4 +75,13 @@ hipError_t launch_compress(const csa_compress_args* a, void* ws, hipStream_t s);
 size_t compress_many_ws_bytes(const csa_compress_args* a, int n);
 hipError_t launch_compress_many(const csa_compress_args* a, int n, void* ws, hipStream_t s);
 
+size_t layer_input_ws_bytes(const csa_layer_weights* w, int M);
+size_t layer_output_ws_bytes(const csa_layer_weights* w, int M);
+hipError_t launch_layer_input(const csa_layer_weights* w, const void* x, const int32_t* pos, int B,
+                              int T, const float* rope_cos, const float* rope_sin,
+                              int64_t rope_rows, void* q, void* q_idx, float* w_idx, void* win,
+                              int win_fmt, size_t win_rb, void* ws, hipStream_t s);
+hipError_t launch_layer_output(const csa_layer_weights* w, const void* o, int M, void* y,
+                               int y_fmt, void* ws, hipStream_t s);
+
 }  // namespace csa

@@ -9,6 +9,11 @@ points in order; it computes nothing itself.  A CSA step at position t is:
   csa_sparse_attn_decode                           -> [B, H, 512]
 
 and an HCA step is csa_compress (ratio 128) followed by hca_attn_decode.
+
+With a layer configuration (workload extra "layer") the CSA step also runs
+the layer's steps on either side of the path: csa_layer_input first (query
+path, index queries and head weights, window-entry write, all from the
+token's hidden state) and csa_layer_output last (grouped output projection).
 """
 
 import torch
@@ -133,6 +138,26 @@ class CsaDecodeLayer:
                 ci(tail, st)
         self.ws_comp = [None] * copies
         self.step_no = 0
+        self.lw = None
+        if w.extra.get("layer"):
+            self._init_layer(w.extra["layer"], copies, device)
+
+    def _init_layer(self, cfg, copies, device):
+        w = self.w
+        wn = synth.layer_weights(w.seed, w.dim, cfg["q_rank"], w.H, w.Hi, cfg["groups"],
+                                 cfg["o_rank"])
+        dev = {k: (torch.from_numpy(v).to(device) if k in ("q_norm", "kv_norm")
+                   else torch.from_numpy(v).to(device).to(torch.bfloat16)) for k, v in wn.items()}
+        # weight copies rotate with the cache copies, so a step does not find
+        # the previous step's weights in the last-level cache
+        self.lw_tensors = [dev] + [{k: v.clone() for k, v in dev.items()}
+                                   for _ in range(copies - 1)]
+        self.lw = [_lib.make_layer_weights(dim=w.dim, q_rank=cfg["q_rank"], H=w.H, Hi=w.Hi,
+                                           groups=cfg["groups"], o_rank=cfg["o_rank"], **d)
+                   for d in self.lw_tensors]
+        self.y = torch.empty((w.B, w.dim), dtype=torch.bfloat16, device=device)
+        self.ws_lin = _lib.workspace(_lib.csa_layer_input_workspace_size(self.lw[0], w.B))
+        self.ws_lout = _lib.workspace(_lib.csa_layer_output_workspace_size(self.lw[0], w.B))
 
     def phases(self):
         """The step as a list of (name, callable) in stream order."""
@@ -163,8 +188,20 @@ class CsaDecodeLayer:
                                         1, w.H, self.sink, 512 ** -0.5, self.rope[0],
                                         self.rope[1], self.out, w.q_fmt, self.ws_att)
 
-        return [("csa_compress", compress), ("csa_index_topk", index_topk),
+        core = [("csa_compress", compress), ("csa_index_topk", index_topk),
                 ("csa_sparse_attn_decode", sparse_attn)]
+        if self.lw is None:
+            return core
+        lw = self.lw[c]
+
+        def layer_input():
+            _lib.csa_layer_input(lw, self.x, self.pos, B, 1, self.rope[0], self.rope[1], self.q,
+                                 self.qi, self.wi, self.win, win_fmt, self.ws_lin)
+
+        def layer_output():
+            _lib.csa_layer_output(lw, self.out, B, self.y, "bf16", self.ws_lout)
+
+        return [("csa_layer_input", layer_input)] + core + [("csa_layer_output", layer_output)]
 
     def step(self):
         for _, f in self.phases():

@@ -22,6 +22,7 @@ T_X, T_WKV, T_WGATE, T_APE = 1, 2, 3, 4
 T_IWKV, T_IWGATE, T_IAPE = 5, 6, 7
 T_WINDOW, T_Q, T_QIDX, T_WIDX, T_SINK = 8, 9, 10, 11, 12
 T_ENTRIES, T_IKEYS, T_XTAIL, T_TOPK, T_SCORES = 13, 14, 15, 16, 17
+T_WQA, T_QNORM, T_WQB, T_WKVWIN, T_KVNORM, T_WQBI, T_WPROJ, T_WOA, T_WOB, T_O = range(20, 30)
 
 
 @dataclass
@@ -74,6 +75,16 @@ WORKLOADS = {
     5: Workload(5, "csa_1m_fp8", B=8, ctx=1048576, ratio=4, n_entries=262144, H=64, Hi=64,
                 topk=512, ent_fmt="fp8_mx32", win_fmt="fp8_mx32", key_fmt="fp8_mx32"),
 }
+
+
+def layer_variant(w):
+    """The workload-5 variant that also runs the layer's steps on either side
+    of the path: query path, index-query preparation and window-entry write
+    from the token's hidden state, and the grouped output projection (V4-Flash
+    shapes: q_rank 1024, 8 groups of 8 heads, o_rank 1024)."""
+    import dataclasses
+    return dataclasses.replace(w, name="csa_1m_fp8_layer",
+                               extra=dict(w.extra, layer=dict(q_rank=1024, groups=8, o_rank=1024)))
 
 
 def mxfp4_variant(w):
@@ -294,3 +305,27 @@ def prefill_index_keys(w, lo, hi):
 
 def prefill_sink(w):
     return normal(w.seed, T_SINK, (w.H,))
+
+
+def layer_weights(seed, dim, q_rank, H, Hi, groups, o_rank):
+    """Weights of the layer's input and output steps, as float32 arrays:
+    projections [out, in] ~ N(0, 1/in) rounded to bf16; norm weights
+    1 + N(0, 0.1^2) in float32.  Row block j of 256 rows of a projection
+    comes from stream (seed, tensor id, j)."""
+    def proj(tid, n_out, n_in):
+        return blocked_normal(seed, tid, (n_in,), 0, n_out, n_in ** -0.5, bf16=True)
+
+    gw = H // groups * 512
+    out = {
+        "wq_a": proj(T_WQA, q_rank, dim),
+        "q_norm": 1.0 + normal(seed, T_QNORM, (q_rank,), 0.1),
+        "wq_b": proj(T_WQB, H * 512, q_rank),
+        "wkv": proj(T_WKVWIN, 512, dim),
+        "kv_norm": 1.0 + normal(seed, T_KVNORM, (512,), 0.1),
+        "wo_a": proj(T_WOA, groups * o_rank, gw).reshape(groups, o_rank, gw),
+        "wo_b": proj(T_WOB, dim, groups * o_rank),
+    }
+    if Hi:
+        out["wq_b_idx"] = proj(T_WQBI, Hi * 128, q_rank)
+        out["w_proj"] = proj(T_WPROJ, Hi, dim)
+    return out
