@@ -308,7 +308,8 @@ csa_status hca_attn_decode(const void* q, int q_fmt, const void* win, int win_fm
  *   weights when Hi == 0).
  * Products use bf16 operands with float32 accumulation; the K split of each
  * product depends on the weight shapes only, so results do not depend on B.
- * Requirements: 1 <= M <= 64; dim and q_rank positive multiples of 256;
+ * Requirements: 1 <= M <= 64; dim a positive multiple of 256; q_rank a
+ * multiple of 256 in [256, 2048];
  * 1 <= H <= 128; 0 <= Hi <= 64; groups >= 1 with H % groups == 0; o_rank a
  * positive multiple of 32; eps finite and >= 0.  Workspaces: the matching
  * *_workspace_size(w, M) bytes, 16-byte aligned.  Errors: CSA_EINVAL for null

@@ -419,8 +419,8 @@ static csa_status check_layer_shape(const csa_layer_weights* w, int M) {
   REQUIRE(w != nullptr, CSA_EINVAL, "weights must not be null");
   REQUIRE(M >= 1 && M <= 64, CSA_EUNSUPPORTED, "M = B*T must be in [1, 64] (got %d)", M);
   REQUIRE(w->dim >= 256 && w->dim % 256 == 0, CSA_EINVAL, "dim must be a positive multiple of 256");
-  REQUIRE(w->q_rank >= 256 && w->q_rank % 256 == 0, CSA_EINVAL,
-          "q_rank must be a positive multiple of 256");
+  REQUIRE(w->q_rank >= 256 && w->q_rank % 256 == 0 && w->q_rank <= 2048, CSA_EINVAL,
+          "q_rank must be a multiple of 256 in [256, 2048]");
   REQUIRE(w->H >= 1 && w->H <= 128, CSA_EUNSUPPORTED, "H must be in [1, 128]");
   REQUIRE(w->Hi >= 0 && w->Hi <= 64, CSA_EUNSUPPORTED, "Hi must be in [0, 64]");
   REQUIRE(w->groups >= 1 && w->H % w->groups == 0, CSA_EINVAL, "groups must divide H");

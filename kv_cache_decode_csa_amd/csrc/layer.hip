@@ -113,11 +113,12 @@ hipError_t launch_linear(const LinJobs& J, hipStream_t s) {
   return hipGetLastError();
 }
 
-// Slices of K: enough work-groups to cover the chip (about 2,048 waves),
-// each slice a multiple of 32 wide.  Depends on the weight shapes only.
-int pick_slices(int blocks, int K) {
+// Slices of K: enough work-groups to cover the chip (about 2,048 waves), at
+// most max_ks, each slice a multiple of 32 wide.  Depends on the weight
+// shapes only.
+int pick_slices(int blocks, int K, int max_ks = 16) {
   int ks = 1;
-  while (ks < 16 && blocks * ks < 2048 && K % (64 * ks) == 0) ks *= 2;
+  while (ks < max_ks && blocks * ks < 2048 && K % (64 * ks) == 0) ks *= 2;
   return ks;
 }
 
@@ -145,19 +146,21 @@ int job_blocks(const LinJobs& J) {
 // ---------------------------------------------------------------- epilogues
 constexpr int kThreads = 256;
 
+// Sum of the ks (<= kMaxSlices) partials of element i, added in slice order;
+// the loads are independent, so they are in flight together.
+constexpr int kMaxSlices = 16;
 __device__ __forceinline__ float slice_sum(const float* part, int ks, int64_t stride, int64_t i) {
-  float v = part[i];
-  for (int s = 1; s < ks; ++s) v += part[s * stride + i];
-  return v;
+  float v[kMaxSlices];
+#pragma unroll
+  for (int s = 0; s < kMaxSlices; ++s) v[s] = s < ks ? part[s * stride + i] : 0.f;
+  float acc = v[0];
+#pragma unroll
+  for (int s = 1; s < kMaxSlices; ++s)
+    if (s < ks) acc += v[s];
+  return acc;
 }
 
-__device__ __forceinline__ float block_sum(float v, float* red) {
-  v = wave_sum(v);
-  __syncthreads();
-  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
-  __syncthreads();
-  return (red[0] + red[1]) + (red[2] + red[3]);
-}
+constexpr int kMaxRank = 2048;  // largest q_rank
 
 struct InArgs {
   const float* part;  // [ks][M][ldy]: latent | window entry | head weights
@@ -183,43 +186,67 @@ __device__ __forceinline__ int64_t rope_row(int64_t p, int64_t rows) {
 }
 
 // One work-group per row m: latent RMSNorm -> bf16; window entry RMSNorm ->
-// RoPE -> stored into ring slot pos mod 128; head weights scaled.
+// RoPE -> stored into ring slot pos mod 128; head weights scaled.  Every load
+// that does not depend on another is issued first, so the kernel waits for
+// memory about twice (the loads, then the rotation factors at the position).
 __global__ void __launch_bounds__(kThreads) layer_in_kernel(InArgs a) {
-  __shared__ float red[4];
+  constexpr int kL = kMaxRank / kThreads;
+  __shared__ float red[2][4];
   __shared__ float z[kHeadDim];
   const int m = blockIdx.x, tid = threadIdx.x;
   const int64_t stride = (int64_t)a.M * a.ldy;
   const float* row = a.part + (int64_t)m * a.ldy;
   const int64_t p = a.pos[m];
-  // latent
-  float ss = 0.f;
-  for (int c = tid; c < a.QR; c += kThreads) {
-    const float v = slice_sum(row, a.ks, stride, c);
-    ss += v * v;
+  float lv[kL], gq[kL];
+#pragma unroll
+  for (int u = 0; u < kL; ++u) {
+    const int c = tid + u * kThreads;
+    lv[u] = c < a.QR ? slice_sum(row, a.ks, stride, c) : 0.f;
+    gq[u] = c < a.QR ? a.q_norm[c] : 0.f;
   }
-  float inv = 1.0f / sqrtf(block_sum(ss, red) / (float)a.QR + a.eps);
-  for (int c = tid; c < a.QR; c += kThreads)
-    a.qr[(int64_t)m * a.QR + c] = f32_to_bf16(slice_sum(row, a.ks, stride, c) * inv * a.q_norm[c]);
-  // head weights
-  for (int h = tid; h < a.Hi; h += kThreads)
-    a.w_idx[(int64_t)m * a.Hi + h] = slice_sum(row, a.ks, stride, a.QR + kHeadDim + h) * a.w_scale;
-  // window entry
-  float v[2];
-  ss = 0.f;
+  float v[2], gk[2];
 #pragma unroll
   for (int u = 0; u < 2; ++u) {
     v[u] = slice_sum(row, a.ks, stride, a.QR + tid + u * kThreads);
-    ss += v[u] * v[u];
+    gk[u] = a.kv_norm[tid + u * kThreads];
   }
-  inv = 1.0f / sqrtf(block_sum(ss, red) / (float)kHeadDim + a.eps);
+  const float wv = tid < a.Hi ? slice_sum(row, a.ks, stride, a.QR + kHeadDim + tid) : 0.f;
+  // rotation factors of this thread's second window dim (the rotated dims
+  // 448..511 are all second dims: tid + 256 >= 448)
+  const int64_t rr = rope_row(p, a.rope_rows);
+  const int c1 = tid + kThreads;
+  float cs = 1.f, sn = 0.f;
+  if (c1 >= kHeadDim - kRopeDims) {
+    const int k = (c1 - (kHeadDim - kRopeDims)) >> 1;
+    cs = a.rope_cos[rr * 32 + k];
+    sn = a.rope_sin[rr * 32 + k];
+  }
+  // both sums of squares in one pass
+  float sq = 0.f;
 #pragma unroll
-  for (int u = 0; u < 2; ++u) {
-    const int c = tid + u * kThreads;
-    z[c] = v[u] * inv * a.kv_norm[c];
+  for (int u = 0; u < kL; ++u) sq += lv[u] * lv[u];
+  float sk = v[0] * v[0] + v[1] * v[1];
+  sq = wave_sum(sq);
+  sk = wave_sum(sk);
+  if ((tid & 63) == 0) {
+    red[0][tid >> 6] = sq;
+    red[1][tid >> 6] = sk;
   }
   __syncthreads();
+  const float inv_q =
+      1.0f / sqrtf(((red[0][0] + red[0][1]) + (red[0][2] + red[0][3])) / (float)a.QR + a.eps);
+  const float inv_k =
+      1.0f / sqrtf(((red[1][0] + red[1][1]) + (red[1][2] + red[1][3])) / (float)kHeadDim + a.eps);
+#pragma unroll
+  for (int u = 0; u < kL; ++u) {
+    const int c = tid + u * kThreads;
+    if (c < a.QR) a.qr[(int64_t)m * a.QR + c] = f32_to_bf16(lv[u] * inv_q * gq[u]);
+  }
+  if (tid < a.Hi) a.w_idx[(int64_t)m * a.Hi + tid] = wv * a.w_scale;
+#pragma unroll
+  for (int u = 0; u < 2; ++u) z[tid + u * kThreads] = v[u] * inv_k * gk[u];
+  __syncthreads();
   if (p < 0) return;
-  const int64_t rr = rope_row(p, a.rope_rows);
   const int b = m / a.T;
   uint8_t* dst = a.win + ((int64_t)b * kWindow + p % kWindow) * a.win_rb;
 #pragma unroll
@@ -227,8 +254,6 @@ __global__ void __launch_bounds__(kThreads) layer_in_kernel(InArgs a) {
     const int c = tid + u * kThreads;
     float out = z[c];
     if (c >= kHeadDim - kRopeDims) {
-      const int k = (c - (kHeadDim - kRopeDims)) >> 1;
-      const float cs = a.rope_cos[rr * 32 + k], sn = a.rope_sin[rr * 32 + k];
       const float pv = z[c ^ 1];
       out = (c & 1) ? (pv * sn + out * cs) : (out * cs - pv * sn);
     }
@@ -265,6 +290,15 @@ __global__ void __launch_bounds__(kThreads) layer_q_kernel(QArgs a) {
   const float* row = a.part + (int64_t)m * a.ldy;
   const int64_t rr = rope_row(a.pos[m], a.rope_rows);
   if (head < a.H) {
+    // rotation factors first (lanes 56..63 hold the rotated dims 448..511)
+    const bool rot = 8 * lane >= kHeadDim - kRopeDims;
+    float cs_[4], sn_[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int k = rot ? 4 * (lane - (kHeadDim - kRopeDims) / 8) + j : 0;
+      cs_[j] = a.rope_cos[rr * 32 + k];
+      sn_[j] = a.rope_sin[rr * 32 + k];
+    }
     float v[8];
     float ss = 0.f;
 #pragma unroll
@@ -275,11 +309,10 @@ __global__ void __launch_bounds__(kThreads) layer_q_kernel(QArgs a) {
     const float inv = 1.0f / sqrtf(wave_sum(ss) / (float)kHeadDim + a.eps);
 #pragma unroll
     for (int j = 0; j < 8; ++j) v[j] *= inv;
-    if (8 * lane >= kHeadDim - kRopeDims) {
+    if (rot) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const int k = 4 * (lane - (kHeadDim - kRopeDims) / 8) + j;
-        const float cs = a.rope_cos[rr * 32 + k], sn = a.rope_sin[rr * 32 + k];
+        const float cs = cs_[j], sn = sn_[j];
         const float x0 = v[2 * j], x1 = v[2 * j + 1];
         v[2 * j] = x0 * cs - x1 * sn;
         v[2 * j + 1] = x0 * sn + x1 * cs;
@@ -293,11 +326,10 @@ __global__ void __launch_bounds__(kThreads) layer_q_kernel(QArgs a) {
   }
   const int h = head - a.H;
   const int64_t base = (int64_t)a.H * kHeadDim + (int64_t)h * kIndexDim;
+  const float cs = a.rope_cos[rr * 32 + (lane >> 1)], sn = a.rope_sin[rr * 32 + (lane >> 1)];
   float lo = slice_sum(row, a.ks, stride, base + lane);
   float hi = slice_sum(row, a.ks, stride, base + lane + 64);
-  {  // RoPE on dims 64..127: dim 64 + lane pairs with 64 + (lane ^ 1)
-    const int k = lane >> 1;
-    const float cs = a.rope_cos[rr * 32 + k], sn = a.rope_sin[rr * 32 + k];
+  {  // RoPE on dims 64..127: dim 64 + lane pairs with 64 + (lane ^ 1), pair lane / 2
     const float pv = shfl_xor_f(hi, 1);
     hi = (lane & 1) ? (pv * sn + hi * cs) : (hi * cs - pv * sn);
   }
@@ -343,7 +375,8 @@ InPlan plan_input(const csa_layer_weights* w, int M) {
   add_job(p.a, nullptr, w->dim, 0, w->wq_a, 0, w->dim, w->q_rank, 1, 0);
   add_job(p.a, nullptr, w->dim, 0, w->wkv, 0, w->dim, kHeadDim, 1, w->q_rank);
   if (w->Hi > 0) add_job(p.a, nullptr, w->dim, 0, w->w_proj, 0, w->dim, w->Hi, 1, w->q_rank + kHeadDim);
-  p.a.ks = pick_slices(job_blocks(p.a), w->dim);
+  // few slices: one work-group per row sums them in the epilogue
+  p.a.ks = pick_slices(job_blocks(p.a), w->dim, 4);
   const int64_t ldb = (int64_t)w->H * kHeadDim + (int64_t)w->Hi * kIndexDim;
   p.b.M = M;
   p.b.ldy = ldb;
