@@ -133,7 +133,10 @@ csa_status kv_dequantize(const void* src, int src_fmt, void* dst, int dst_fmt, i
  * Whenever a block completes ((p+1) mod ratio == 0) entry p/ratio is emitted:
  *   ratio 4 (overlap, coff 2): 8 slots = previous block's tokens on channels
  *     [0, d) followed by the current block's tokens on channels [d, 2d);
- *   ratio 128 (coff 1): the block's 128 tokens;  ratio 1: the single token;
+ *   ratio 128 (coff 1): the block's 128 tokens;  ratio 2 (coff 1): the
+ *     block's 2 tokens, without overlap (the CSA2 compressor of the
+ *     V4.1-Flash diagram page at m = 2; its missing slot bias is a zero ape);
+ *   ratio 1: the single token (CSA2 at m = 1);
  *   C_c = sum_j softmax_j(s_{j,c}) v_{j,c}  per channel, in float32;
  *   y = C / sqrt(mean(C^2) + eps) * norm_w;  RoPE on the last 64 dims at
  *   position (p/ratio)*ratio;  if rotate: y = H y / sqrt(head_dim) with H the
@@ -149,7 +152,7 @@ csa_status kv_dequantize(const void* src, int src_fmt, void* dst, int dst_fmt, i
  * w_fmt (F32 or BF16); ape: [ratio][coff*head_dim] float; norm_w: [head_dim]
  * float; rope tables [rope_rows][32] float (positions beyond rope_rows - 1 are
  * clamped to the last row); start_pos: [B] int32.
- * Requirements: ratio in {1, 4, 128}; head_dim in {128, 512}; rotate only with
+ * Requirements: ratio in {1, 2, 4, 128}; head_dim in {128, 512}; rotate only with
  * head_dim 128; dim % 32 == 0; entry_fmt any; B >= 1, T >= 1.            */
 typedef struct {
   int B, T, dim, ratio, head_dim, rotate;

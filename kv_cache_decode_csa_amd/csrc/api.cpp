@@ -149,8 +149,8 @@ static csa_status check_compress(const csa_compress_args* a) {
   REQUIRE(a != nullptr, CSA_EINVAL, "args must not be null");
   REQUIRE(a->B >= 1 && a->T >= 1, CSA_EINVAL, "B and T must be >= 1");
   REQUIRE(a->dim >= 32 && a->dim % 32 == 0, CSA_EINVAL, "dim must be a positive multiple of 32");
-  REQUIRE(a->ratio == 1 || a->ratio == 4 || a->ratio == 128, CSA_EUNSUPPORTED,
-          "ratio must be 1, 4 or 128 (got %d)", a->ratio);
+  REQUIRE(a->ratio == 1 || a->ratio == 2 || a->ratio == 4 || a->ratio == 128, CSA_EUNSUPPORTED,
+          "ratio must be 1, 2, 4 or 128 (got %d)", a->ratio);
   REQUIRE(a->head_dim == 128 || a->head_dim == 512, CSA_EUNSUPPORTED, "head_dim must be 128 or 512");
   REQUIRE(!a->rotate || a->head_dim == 128, CSA_EUNSUPPORTED, "rotate needs head_dim 128");
   REQUIRE(a->x_fmt == CSA_F32 || a->x_fmt == CSA_BF16, CSA_EUNSUPPORTED, "x_fmt must be F32 or BF16");

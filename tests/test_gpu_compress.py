@@ -78,7 +78,8 @@ def tables():
 OM = rope.frequencies(160000.0)
 
 
-@pytest.mark.parametrize("ratio,d,rotate", [(4, 512, 0), (4, 128, 1), (128, 512, 0), (1, 512, 0)])
+@pytest.mark.parametrize("ratio,d,rotate", [(4, 512, 0), (4, 128, 1), (128, 512, 0), (1, 512, 0),
+                                            (2, 512, 0), (2, 128, 1)])
 def test_bulk_f32(tables, ratio, d, rotate):
     B, dim, T = 2, 256, 700
     rng = np.random.default_rng(ratio * 10 + d)
@@ -133,25 +134,29 @@ def test_bulk_bf16_tiled_projection(tables, ratio, d, rotate, entry_fmt):
         close_f32(sc[fin], st[1][fin], tol=1e-4)
 
 
-@pytest.mark.parametrize("entry_fmt,dim,d,rotate", [("bf16", 512, 512, 0), ("fp8_mx32", 512, 512, 0),
-                                                    ("fp4_e4m3_16", 512, 512, 0), ("f32", 512, 512, 0),
-                                                    ("fp8_mx32", 4096, 512, 0), ("fp8_mx32", 4096, 128, 1),
-                                                    ("bf16", 4096, 128, 1), ("fp4_mx32", 4096, 128, 1)])
-def test_decode_steps_bf16(tables, entry_fmt, dim, d, rotate):
+@pytest.mark.parametrize("entry_fmt,dim,d,rotate,ratio", [
+    ("bf16", 512, 512, 0, 4), ("fp8_mx32", 512, 512, 0, 4), ("fp4_e4m3_16", 512, 512, 0, 4),
+    ("f32", 512, 512, 0, 4), ("fp8_mx32", 4096, 512, 0, 4), ("fp8_mx32", 4096, 128, 1, 4),
+    ("bf16", 4096, 128, 1, 4), ("fp4_mx32", 4096, 128, 1, 4),
+    ("fp4_e4m3_16", 4096, 512, 0, 2), ("fp8_mx32", 4096, 128, 1, 2),
+    ("fp4_e4m3_16", 4096, 512, 0, 1)])
+def test_decode_steps_bf16(tables, entry_fmt, dim, d, rotate, ratio):
     """Token-by-token calls from a state built by an earlier chunked call; each
     sequence sits at a different offset inside its block.  dim 4096 runs the
-    K-sliced MFMA projection."""
-    B, ratio = 3, 4
+    K-sliced MFMA projection.  Ratios 2 and 1 are the CSA2 compressor of the
+    V4.1-Flash diagram (no overlap; slot bias zero)."""
+    B = 3
     rng = np.random.default_rng(7)
     wkv, wg, ape = (synth.bf16_round(w) for w in weights(rng, dim, d, ratio))
-    ape = weights(rng, dim, d, ratio)[2]
+    ape = weights(rng, dim, d, ratio)[2] if ratio == 4 else np.zeros_like(ape)
     prefix = np.array([37, 40, 42])
     steps = 9
     x = synth.bf16_round(rng.standard_normal((B, 60, dim)).astype(np.float32))
-    g = GpuCompressor(B, dim, ratio, d, rotate, wkv, wg, ape, "bf16", entry_fmt, 32, tables)
+    cap = 60 // ratio + 2
+    g = GpuCompressor(B, dim, ratio, d, rotate, wkv, wg, ape, "bf16", entry_fmt, cap, tables)
     # prefix: one chunked call per sequence (different lengths -> separate calls)
     for b in range(B):
-        gb = GpuCompressor(1, dim, ratio, d, rotate, wkv, wg, ape, "bf16", entry_fmt, 32, tables)
+        gb = GpuCompressor(1, dim, ratio, d, rotate, wkv, wg, ape, "bf16", entry_fmt, cap, tables)
         gb(x[b:b + 1, :prefix[b]], [0])
         g.kv[b], g.sc[b], g.entries[b] = gb.kv[0], gb.sc[0], gb.entries[0]
     for s in range(steps):

@@ -84,7 +84,7 @@ def test_prompt1000(golden):
 
 
 @pytest.mark.parametrize("ratio,d,rotate", [(4, 64, False), (4, 128, True), (128, 64, False),
-                                            (1, 64, False)])
+                                            (1, 64, False), (2, 64, False), (2, 128, True)])
 def test_stream_equals_bulk_any_chunking(ratio, d, rotate):
     rng = np.random.default_rng(2 + ratio)
     dim = 16
@@ -144,3 +144,31 @@ def test_hadamard_orthogonal():
     H = C.hadamard(128)
     np.testing.assert_array_equal(H @ H.T, 128 * np.eye(128))
     assert set(np.unique(H)) == {-1.0, 1.0}
+
+
+def test_ratio2_without_overlap_or_bias():
+    """The V4.1 CSA2 compressor at m = 2 (V4.1-Flash diagram: encoder layers):
+    no overlap and zero slot bias, so entry i pools exactly tokens 2i, 2i+1
+    with a per-channel softmax of their gate scores -- with equal gates their
+    mean -- then RMSNorm and RoPE at position 2i."""
+    rng = np.random.default_rng(12)
+    dim, d = 8, 64
+    P = _params(rng, dim, d, 2)
+    assert P["w_kv"].shape == (d, dim)  # coff 1: no doubled projection
+    x = rng.standard_normal((9, dim))
+    zero = np.zeros((2, d))
+    out, st = C.compress_bulk(x, 0, P["w_kv"], P["w_gate"], zero, P["norm_w"], OM, 2, d)
+    assert sorted(out) == [0, 1, 2, 3]
+    V, S = x @ P["w_kv"].T, x @ P["w_gate"].T
+    for i in range(4):
+        e = np.exp(S[2 * i:2 * i + 2] - S[2 * i:2 * i + 2].max(axis=0))
+        pooled = (e * V[2 * i:2 * i + 2]).sum(axis=0) / e.sum(axis=0)
+        y = pooled / np.sqrt(np.mean(pooled ** 2) + 1e-6) * P["norm_w"]
+        np.testing.assert_allclose(out[i], rope.rotate(y, 2 * i, OM), rtol=1e-12, atol=1e-12)
+    # token 8 waits in slot 0 for its partner
+    np.testing.assert_allclose(st[0][0], V[8], rtol=1e-12)
+    eq, _ = C.compress_bulk(x, 0, P["w_kv"], np.zeros_like(P["w_gate"]), zero, P["norm_w"], OM,
+                            2, d)
+    m = V[0:2].mean(axis=0)
+    np.testing.assert_allclose(eq[0], rope.rotate(m / np.sqrt(np.mean(m * m) + 1e-6) *
+                                                  P["norm_w"], 0, OM), rtol=1e-12, atol=1e-12)
