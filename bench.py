@@ -39,7 +39,7 @@ HBM_PEAK_GBS = 8000.0
 MFMA_BF16_PEAK_TFLOPS = 2500.0
 
 WORKLOADS = {"csa_1m_fp8": 5, "csa_1m_mxfp4": 5, "csa_1m_fp4idx": 5, "csa_1m_fp8_layer": 5,
-             "csa_64k_bf16": 2,
+             "csa2_m1_256k": 6, "csa_64k_bf16": 2,
              "hca_1m_bf16": 3, "csa_prefill_32k_bf16": 4}
 
 
@@ -59,9 +59,9 @@ def algorithmic_bytes(w):
     comp_main = (2 * coff * 512 * dim * qb + B * dim * qb
                  + 2 * 2 * B * coff * w.ratio * coff * 512 * 4 + B * row_bytes(w.ent_fmt, 512))
     out["csa_compress"] = comp_main
-    if w.ratio == 4:  # the index-key compressor runs in the same call
+    if w.ratio != 128:  # CSA: the index-key compressor runs in the same call
         out["csa_compress"] += (2 * coff * 128 * dim * qb + B * dim * qb
-                                + 2 * 2 * B * coff * 4 * coff * 128 * 4
+                                + 2 * 2 * B * coff * w.ratio * coff * 128 * 4
                                 + B * row_bytes(w.key_fmt, 128))
         n_vis = min((w.t + 1) // w.ratio, N)
         out["csa_index_topk"] = B * (n_vis * row_bytes(w.key_fmt, 128) + w.Hi * 128 * qb
@@ -70,6 +70,8 @@ def algorithmic_bytes(w):
         out["csa_sparse_attn_decode"] = B * (k * row_bytes(w.ent_fmt, 512) + k * 4
                                              + 128 * row_bytes(w.win_fmt, 512)
                                              + 2 * w.H * 512 * qb) + w.H * 4
+        if w.extra.get("reuse"):  # reuse layers: the same reads with their own q, window
+            out["csa_sparse_attn_reuse"] = w.extra["reuse"] * out["csa_sparse_attn_decode"]
         cfg = w.extra.get("layer")
         if cfg:  # weights once, the token's inputs and outputs (intermediates excluded)
             qr, g, r = cfg["q_rank"], cfg["groups"], cfg["o_rank"]
@@ -232,7 +234,7 @@ def fp4_recall(layer, w, torch):
     wf = torch.from_numpy(wi).cuda().reshape(B, 1, w.Hi)
     ids = torch.empty((B, 1, w.topk), dtype=torch.int32, device="cuda")
     ws = _lib.workspace(_lib.csa_index_topk_workspace_size(B, 1, N, w.topk))
-    _lib.csa_index_topk(qf, "f32", wf, keys, "f32", layer.pos, 4, B, 1, w.Hi, N, w.topk, ids,
+    _lib.csa_index_topk(qf, "f32", wf, keys, "f32", layer.pos, w.ratio, B, 1, w.Hi, N, w.topk, ids,
                         None, ws)
     torch.cuda.synchronize()
     a_ids, b_ids = layer.topk.cpu().numpy()[:, 0], ids.cpu().numpy()[:, 0]
@@ -303,10 +305,14 @@ def cpu_baseline(w, n_seq, min_seconds=10.0):
         win_st = codec.store(win, w.win_fmt)[0]
         keys_st = None
         qi = wi = None
-        if w.ratio == 4:
+        if w.ratio != 128:
             qi, wi = synth.index_queries(w, br)
             keys_st = codec.store(synth.index_keys(w, br)[0], w.key_fmt)[0]
-        prepared.append((q, sink, win_st, ent, keys_st, qi, wi))
+        reuse = [synth.reuse_layer_inputs(w, layer, br)
+                 for layer in range(1, w.extra.get("reuse", 0) + 1)]
+        reuse = [(rq[0].astype(np.float64), rs, codec.store(rw[0], w.win_fmt)[0])
+                 for rq, rs, rw in reuse]
+        prepared.append((q, sink, win_st, ent, keys_st, qi, wi, reuse))
     t = w.t
     cfg = w.extra.get("layer")
     if cfg:  # the layer's input and output steps are timed too
@@ -318,15 +324,15 @@ def cpu_baseline(w, n_seq, min_seconds=10.0):
     passes = 0
     while t_total < min_seconds and passes < 50:
         passes += 1
-        for si, (q, sink, win_st, ent, keys_st, qi, wi) in enumerate(prepared):
+        for si, (q, sink, win_st, ent, keys_st, qi, wi, reuse) in enumerate(prepared):
             if cfg:
                 t0 = time.perf_counter()
                 OL.layer_input(xs[si], t, lw, om)
                 t_total += time.perf_counter() - t0
-            if w.ratio == 4:
+            if w.ratio != 128:
                 t0 = time.perf_counter()
                 K = codec.load(keys_st, w.key_fmt, 128)
-                nv = int(indexer.n_visible(t, 4, w.n_entries))
+                nv = int(indexer.n_visible(t, w.ratio, w.n_entries))
                 S = indexer.scores(qi[0].astype(np.float64), wi[0], K, nv)
                 ids = TK.topk(S.astype(np.float32), w.topk, nv)
                 t_total += time.perf_counter() - t0
@@ -343,12 +349,16 @@ def cpu_baseline(w, n_seq, min_seconds=10.0):
             o = attention.attend(q[0].astype(np.float64), rows, valid, sink, 512 ** -0.5, t, om)
             if cfg:
                 OL.output_projection(o, lw["wo_a"], lw["wo_b"])
+            for rq, rs, rw_st in reuse:  # reuse layers: their own q and window
+                Rv = codec.load(rw_st, w.win_fmt, 512)
+                rows = np.concatenate([Rv[np.maximum(wid, 0)], E])
+                attention.attend(rq, rows, valid, rs, 512 ** -0.5, t, om)
             t_total += time.perf_counter() - t0
-    n_tok = passes * n_seq
+    n_tok = passes * n_seq * (1 + len(prepared[0][7]))
     return {"value": n_tok / t_total, "unit": "tokens/s/layer", "cores": int(threads),
             "kind": "oracle",
             "sample": f"{n_seq} of {w.B} sequences of the same workload at full context "
-                      f"({w.n_entries} entries each), {passes} passes ({n_tok} token-steps); "
+                      f"({w.n_entries} entries each), {passes} passes ({n_tok} layer-token steps); "
                       f"timed: {'layer input steps, ' if cfg else ''}key decode, scoring, "
                       f"top-k, row decode and attention{', output projection' if cfg else ''} "
                       f"in float64 NumPy, {t_total:.1f} s"}
@@ -402,7 +412,7 @@ def main():
     print(f"# building {a.workload}: B={w.B} ctx={w.ctx} entries={w.n_entries}", file=sys.stderr,
           flush=True)
     t0 = time.time()
-    Layer = decode.CsaDecodeLayer if w.ratio == 4 else decode.HcaDecodeLayer
+    Layer = decode.CsaDecodeLayer if w.ratio != 128 else decode.HcaDecodeLayer
     if a.copies is None:
         step_bytes = sum(algorithmic_bytes(w).values())
         a.copies = max(4, -(-1_000_000_000 // step_bytes))
@@ -418,12 +428,13 @@ def main():
     flushed_ms = None if a.no_flush else flushed_steps(layer, a.steps, torch)
     copy_gbs = copy_bandwidth(torch)
     ab = algorithmic_bytes(w)
-    dom = "csa_index_topk" if w.ratio == 4 else "hca_attn_decode"
+    dom = "csa_index_topk" if w.ratio != 128 else "hca_attn_decode"
+    layers = 1 + w.extra.get("reuse", 0)  # layers per step (a layer group with reuse)
     dom_gbs = ab[dom] / (phases[dom] * 1e-3) / 1e9
     step_bytes = sum(ab.values())
     res = {
         "metric": "CSA top-512 decode tokens/s per layer at 1M ctx; achieved HBM GB/s vs peak",
-        "value": w.B / (ms * 1e-3),
+        "value": layers * w.B / (ms * 1e-3),
         "unit": "tokens/s/layer",
         "n_gpus": 1,
         "steps": a.steps,
@@ -437,7 +448,8 @@ def main():
         "config": {"workload": w.name, "batch": w.B, "context": w.ctx, "entries": w.n_entries,
                    "heads": w.H, "index_heads": w.Hi, "topk": w.topk, "ratio": w.ratio,
                    "kv_format": w.ent_fmt, "window_format": w.win_fmt,
-                   "index_key_format": w.key_fmt, "cache_copies": a.copies},
+                   "index_key_format": w.key_fmt, "cache_copies": a.copies,
+                   "layers_per_step": layers},
         "roofline": {"bound": "hbm", "achieved": dom_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": dom_gbs / HBM_PEAK_GBS, "traffic": measured_traffic(a.workload),
                      "kernel": dom,

@@ -141,6 +141,16 @@ class CsaDecodeLayer:
         self.lw = None
         if w.extra.get("layer"):
             self._init_layer(w.extra["layer"], copies, device)
+        # reuse layers of a layer group: their own queries, sinks and windows,
+        # the Full layer's entries and top-k ids
+        self.reuse = []
+        for layer in range(1, w.extra.get("reuse", 0) + 1):
+            rq, rsink, rwin = synth.reuse_layer_inputs(w, layer)
+            self.reuse.append((
+                torch.from_numpy(rq).to(device).to(qdt).reshape(B, 1, w.H, 512),
+                torch.from_numpy(rsink).to(device),
+                _dev_rows(rwin, w.win_fmt, device),
+                torch.empty((B, 1, w.H, 512), dtype=qdt, device=device)))
 
     def _init_layer(self, cfg, copies, device):
         w = self.w
@@ -190,6 +200,16 @@ class CsaDecodeLayer:
 
         core = [("csa_compress", compress), ("csa_index_topk", index_topk),
                 ("csa_sparse_attn_decode", sparse_attn)]
+        if self.reuse:
+            def reuse_attn():
+                for rq, rsink, rwin, rout in self.reuse:
+                    _lib.csa_sparse_attn_decode(rq, w.q_fmt, rwin, win_fmt, _lib.WIN_RING128,
+                                                None, 128, ent, ent_fmt, N, self.topk, w.topk,
+                                                self.pos, B, 1, w.H, rsink, 512 ** -0.5,
+                                                self.rope[0], self.rope[1], rout, w.q_fmt,
+                                                self.ws_att)
+
+            core.append(("csa_sparse_attn_reuse", reuse_attn))
         if self.lw is None:
             return core
         lw = self.lw[c]

@@ -23,6 +23,7 @@ T_IWKV, T_IWGATE, T_IAPE = 5, 6, 7
 T_WINDOW, T_Q, T_QIDX, T_WIDX, T_SINK = 8, 9, 10, 11, 12
 T_ENTRIES, T_IKEYS, T_XTAIL, T_TOPK, T_SCORES = 13, 14, 15, 16, 17
 T_WQA, T_QNORM, T_WQB, T_WKVWIN, T_KVNORM, T_WQBI, T_WPROJ, T_WOA, T_WOB, T_O = range(20, 30)
+T_RQ, T_RSINK, T_RWIN = 30, 31, 32
 
 
 @dataclass
@@ -74,6 +75,14 @@ WORKLOADS = {
     # quantized CSA decode at 1M: FP8-528 main KV and window, FP8-132 index keys
     5: Workload(5, "csa_1m_fp8", B=8, ctx=1048576, ratio=4, n_entries=262144, H=64, Hi=64,
                 topk=512, ent_fmt="fp8_mx32", win_fmt="fp8_mx32", key_fmt="fp8_mx32"),
+    # V4.1-style CSA2 decoder layer group at m = 1: one entry per token (256K
+    # context = 262,144 entries, the headline's entry count), MXFP4-288 main KV,
+    # MXFP4-68 index keys with bf16 scores, FP8 window; one Full layer
+    # (compress, index, attend) and 5 Reuse layers that attend with their own
+    # queries and windows over the Full layer's entries and top-512 ids
+    6: Workload(6, "csa2_m1_256k", B=8, ctx=262144, ratio=1, n_entries=262144, H=64, Hi=64,
+                topk=512, ent_fmt="fp4_e4m3_16", win_fmt="fp8_mx32", key_fmt="fp4_mx32",
+                extra={"csa2": True, "reuse": 5}),
 }
 
 
@@ -169,6 +178,18 @@ def index_keys(w, b_range=None):
                                         b_range), w.key_fmt)
 
 
+def reuse_layer_inputs(w, layer, b_range=None):
+    """Queries [B, H, 512], sink [H] and window ring [B, 128, 512] of reuse
+    layer `layer` >= 1 of a layer group; element b of each comes from stream
+    (seed, tensor id, layer * 65536 + b)."""
+    bs = range(w.B) if b_range is None else b_range
+    q = np.stack([normal(w.seed, T_RQ, (w.H, 512), w.kv_std, idx=layer * 65536 + b) for b in bs])
+    sink = normal(w.seed, T_RSINK, (w.H,), idx=layer)
+    win = np.stack([normal(w.seed, T_RWIN, (128, 512), w.kv_std, idx=layer * 65536 + b)
+                    for b in bs])
+    return as_fmt_values(q, w.q_fmt), sink, as_fmt_values(win, w.win_fmt)
+
+
 def compressor_weights(w, head_dim, ratio, indexer=False):
     """W_kv, W_gate [coff*d, dim] ~ N(0, 0.02^2), ape [r, coff*d] ~ N(0, 0.02^2),
     norm weight ones [d]."""
@@ -177,6 +198,8 @@ def compressor_weights(w, head_dim, ratio, indexer=False):
     wkv = normal(w.seed, tids[0], (coff * head_dim, w.dim), 0.02)
     wg = normal(w.seed, tids[1], (coff * head_dim, w.dim), 0.02)
     ape = normal(w.seed, tids[2], (ratio, coff * head_dim), 0.02)
+    if w.extra.get("csa2"):  # the CSA2 compressor has no slot bias
+        ape = np.zeros_like(ape)
     fmt = w.q_fmt
     return as_fmt_values(wkv, fmt), as_fmt_values(wg, fmt), ape, np.ones(head_dim, np.float32)
 
