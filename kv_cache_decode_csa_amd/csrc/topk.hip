@@ -561,6 +561,46 @@ __global__ void __launch_bounds__(kSelThreads) topk_collect_kernel(
   }
 }
 
+// Boundary lists of 513..1024 entries: sort entries [0, 512) (already in fv,
+// two per lane) and [512, eq) separately with the 512-entry network, keep both
+// in LDS, and write the first `need` entries of their descending merge: output
+// i takes A[a] or B[i - a], where the co-rank a (entries of A among the first
+// i outputs) is the smallest a with A[a] < B[i - a - 1] (packed values are
+// distinct: they carry the index).
+__device__ void boundary_two_halves(uint64_t (&fv)[2], const uint32_t* cand, uint32_t eq,
+                                    uint32_t need, int e0, LdsSel& L, int32_t* out) {
+  uint64_t* A = (uint64_t*)L.skey;  // skey and sidx together hold 1024 packed values
+  uint64_t* Bh = A + 512;
+  sort512_wg_desc(fv, (uint64_t*)L.ties);
+  A[e0] = fv[0];
+  A[e0 + 1] = fv[1];
+  const uint2* src = (const uint2*)cand + 512 + e0;
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const uint2 pr = src[i];  // the candidate list always holds these pairs
+    fv[i] = (uint32_t)(512 + e0 + i) < eq ? (((uint64_t)pr.x << 32) | (uint64_t)(~pr.y)) : 0ull;
+  }
+  __syncthreads();  // the first sort's last reads of the buffer are done
+  sort512_wg_desc(fv, (uint64_t*)L.ties);
+  Bh[e0] = fv[0];
+  Bh[e0 + 1] = fv[1];
+  __syncthreads();
+#pragma unroll
+  for (int r = 0; r < 2; ++r) {
+    const int i = e0 + r;
+    if ((uint32_t)i >= need) continue;
+    int lo = i > 512 ? i - 512 : 0, hi = i < 512 ? i : 512;
+    while (lo < hi) {  // first a with !(A[a] > B[i - a - 1])
+      const int mid = (lo + hi) >> 1;
+      if (A[mid] > Bh[i - mid - 1]) lo = mid + 1;
+      else hi = mid;
+    }
+    const int b = i - lo;
+    const uint64_t va = lo < 512 ? A[lo] : 0ull, vb = b < 512 ? Bh[b] : 0ull;
+    out[i] = (int32_t)(~(uint32_t)(va > vb ? va : vb));
+  }
+}
+
 // Pass 2, two work-groups per row.  In the common case (the hi list and the
 // boundary list both fit 512 entries and the boundary bin was kept) the first
 // work-group orders the hi list and the second the boundary list, each
@@ -608,8 +648,16 @@ __global__ void __launch_bounds__(kSelThreads) topk_final_kernel(
   const uint32_t need = k_eff - above;
   // Fast path: every entry of the hi list outranks every entry of the
   // boundary bin, so the answer is the sorted hi list followed by the first
-  // `need` entries of the sorted boundary list.
-  if (keep_eq && above <= 512u && eq <= 512u) {
+  // `need` entries of the sorted boundary list.  A boundary list of up to
+  // 1024 entries is sorted as two halves whose first `need` (<= 512) merged
+  // entries are taken.
+  const bool two_halves = eq > 512u && eq <= 1024u && need <= 512u;
+  if (keep_eq && above <= 512u && (eq <= 512u || two_halves)) {
+    if (part == 1 && two_halves) {
+      boundary_two_halves(fv, cand, eq, need, e0, L, out + above);
+      for (int i = (int)k_eff + t; i < topk; i += kSelThreads) out[i] = -1;
+      return;
+    }
     const uint32_t n = part == 0 ? above : eq;
 #pragma unroll
     for (int i = 0; i < 2; ++i)

@@ -83,6 +83,26 @@ def test_boundary_bin_refinement_path():
     check(S, np.array([ld, 5000, 4000, ld], np.int32), 1024)
 
 
+def test_boundary_bin_two_halves():
+    """513..1024 entries share the boundary bin and at most 512 of them are
+    taken: the two halves of the boundary list are sorted and merged."""
+    need_gpu()
+    ld = 5000
+    rng = np.random.default_rng(6)
+    S = (0.1 * rng.random((5, ld))).astype(np.float32)                 # far below the bin
+    def fill(r, n_eq, n_above, distinct):
+        pos = rng.choice(ld, n_eq + n_above, replace=False)
+        S[r, pos[:n_eq]] = (1.0 + rng.integers(0, distinct, n_eq) * 2.0 ** -20).astype(np.float32)
+        S[r, pos[n_eq:]] = (4.0 + rng.random(n_above)).astype(np.float32)
+    fill(0, 800, 100, 4096)     # need 412 of 800
+    fill(1, 1024, 0, 4096)      # need 512 of 1024
+    fill(2, 513, 300, 8)        # heavy ties at the threshold: by index
+    fill(3, 700, 0, 4096)       # k 1024 below: need > 512 takes the refinement
+    fill(4, 1000, 511, 64)      # need 1
+    check(S, np.full(5, ld, np.int32), 512)
+    check(S, np.array([ld, ld, ld, ld, 4000], np.int32), 1024)
+
+
 def test_run_to_run_bitwise():
     need_gpu()
     ld = 100000
