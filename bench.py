@@ -384,8 +384,8 @@ def main():
                          "reference for HBM byte counters) and exit")
     a = ap.parse_args()
     if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
-              "(see the sharding note in DESIGN.md); run with --gpus 1", file=sys.stderr)
+        print("bench.py measures one GPU only: the library has no multi-GPU path "
+              "(one process drives one GPU); run with --gpus 1", file=sys.stderr)
         sys.exit(2)
 
     import torch

@@ -1,9 +1,9 @@
-"""Seeded synthetic inputs for the five decode workloads.
+"""Seeded synthetic inputs for the benchmark workloads.
 
 This module holds data recipes only (shapes, seeds, value distributions and
 the float32 -> bf16 cast of generated values); it contains none of the
 method's arithmetic and imports nothing from the library or the oracle.
-Both the GPU path and the checker draw their inputs from here.
+Both the GPU path and the oracle draw their inputs from here.
 
 Every tensor has its own stream, keyed by (seed, tensor id, leading index), so
 one sequence of a batch can be regenerated on its own:

@@ -63,6 +63,26 @@ def test_prefill_flops():
     assert fl["csa_compress"] == 2.0 * T * 4096 * (2 * 512 * 2 + 2 * 128 * 2)
 
 
+def test_csa2_and_layer_bytes():
+    """CSA2 at m = 1: 262,144 FP4 index keys of 68 B per sequence, MXFP4 rows
+    of 288 B, and 5 reuse layers reading what the Full layer's attention reads.
+    The layer variant: every weight once (bf16) plus the token's inputs and
+    outputs."""
+    w = synth.WORKLOADS[6]
+    ab = bench.algorithmic_bytes(w)
+    assert ab["csa_index_topk"] == 8 * (262144 * 68 + 64 * 128 * 2 + 64 * 4 + 512 * 4)
+    att = 8 * (512 * 288 + 512 * 4 + 128 * 528 + 2 * 64 * 512 * 2) + 64 * 4
+    assert ab["csa_sparse_attn_decode"] == att
+    assert ab["csa_sparse_attn_reuse"] == 5 * att
+    wl = synth.layer_variant(synth.WORKLOADS[5])
+    ab = bench.algorithmic_bytes(wl)
+    weights = 4096 * 1024 + 1024 * 64 * 512 + 4096 * 512 + 1024 * 64 * 128 + 4096 * 64
+    assert ab["csa_layer_input"] == (2 * weights + 4 * (1024 + 512) + 8 * 4096 * 2
+                                     + 8 * (64 * 512 * 2 + 64 * 128 * 2 + 64 * 4) + 8 * 528)
+    assert ab["csa_layer_output"] == 2 * (1024 * 64 * 512 + 4096 * 8 * 1024) + 8 * 64 * 512 * 2 \
+        + 8 * 4096 * 2
+
+
 def test_multi_gpu_is_refused():
     r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
                        capture_output=True, text=True, timeout=120)
