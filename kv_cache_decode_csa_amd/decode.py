@@ -142,12 +142,8 @@ class CsaDecodeLayer:
         if w.extra.get("layer"):
             self._init_layer(w.extra["layer"], copies, device)
         # reuse layers of a layer group: their own queries, sinks and windows,
-        # the Full layer's entries and top-k ids.  Each runs on a stream of its
-        # own (default priority) with its own workspace, so their launches --
-        # a few hundred work-groups each -- overlap.
+        # the Full layer's entries and top-k ids
         self.reuse = []
-        self.reuse_streams = []
-        self.reuse_ws = []
         for layer in range(1, w.extra.get("reuse", 0) + 1):
             rq, rsink, rwin = synth.reuse_layer_inputs(w, layer)
             self.reuse.append((
@@ -155,9 +151,6 @@ class CsaDecodeLayer:
                 torch.from_numpy(rsink).to(device),
                 _dev_rows(rwin, w.win_fmt, device),
                 torch.empty((B, 1, w.H, 512), dtype=qdt, device=device)))
-            self.reuse_streams.append(torch.cuda.Stream(device=device))
-            self.reuse_ws.append(
-                _lib.workspace(_lib.csa_sparse_attn_workspace_size(B, 1, w.H, w.topk)))
 
     def _init_layer(self, cfg, copies, device):
         w = self.w
@@ -209,19 +202,12 @@ class CsaDecodeLayer:
                 ("csa_sparse_attn_decode", sparse_attn)]
         if self.reuse:
             def reuse_attn():
-                main = torch.cuda.current_stream()
-                ready = torch.cuda.Event()
-                ready.record(main)
-                for (rq, rsink, rwin, rout), st, ws in zip(self.reuse, self.reuse_streams,
-                                                           self.reuse_ws):
-                    st.wait_event(ready)
+                for rq, rsink, rwin, rout in self.reuse:
                     _lib.csa_sparse_attn_decode(rq, w.q_fmt, rwin, win_fmt, _lib.WIN_RING128,
                                                 None, 128, ent, ent_fmt, N, self.topk, w.topk,
                                                 self.pos, B, 1, w.H, rsink, 512 ** -0.5,
-                                                self.rope[0], self.rope[1], rout, w.q_fmt, ws,
-                                                stream=st)
-                for st in self.reuse_streams:
-                    main.wait_stream(st)
+                                                self.rope[0], self.rope[1], rout, w.q_fmt,
+                                                self.ws_att)
 
             core.append(("csa_sparse_attn_reuse", reuse_attn))
         if self.lw is None:
