@@ -70,8 +70,12 @@ def algorithmic_bytes(w):
         out["csa_sparse_attn_decode"] = B * (k * row_bytes(w.ent_fmt, 512) + k * 4
                                              + 128 * row_bytes(w.win_fmt, 512)
                                              + 2 * w.H * 512 * qb) + w.H * 4
-        if w.extra.get("reuse"):  # reuse layers: the same reads with their own q, window
-            out["csa_sparse_attn_reuse"] = w.extra["reuse"] * out["csa_sparse_attn_decode"]
+        if w.extra.get("reuse"):  # the layer group: shared rows and ids once, per-layer
+            L = 1 + w.extra["reuse"]  # window, q, output and sinks
+            out["csa_sparse_attn_group"] = (B * (k * row_bytes(w.ent_fmt, 512) + k * 4)
+                                            + L * B * (128 * row_bytes(w.win_fmt, 512)
+                                                       + 2 * w.H * 512 * qb) + L * w.H * 4)
+            del out["csa_sparse_attn_decode"]
         cfg = w.extra.get("layer")
         if cfg:  # weights once, the token's inputs and outputs (intermediates excluded)
             qr, g, r = cfg["q_rank"], cfg["groups"], cfg["o_rank"]

@@ -269,6 +269,27 @@ csa_status csa_sparse_attn_decode(const void* q, int q_fmt, const void* win, int
                                   void* out, int out_fmt, void* ws, size_t ws_bytes,
                                   csa_stream_t stream);
 
+/* Layers that share main KV and top-k ids (the CSA2 layer groups of the
+ * V4.1-Flash diagram page: a Full layer and its Reuse layers).  The same as
+ * csa_sparse_attn_decode with a decode ring window (CSA_WIN_RING128), for B
+ * sequences that form B / ent_seqs groups of ent_seqs: sequence b attends with
+ * its own q[b], window win[b] and output out[b], reads entry set
+ * entries[b % ent_seqs] through the top-k list topk_idx[b % ent_seqs], and
+ * takes its sinks from sink[b / ent_seqs][H].  Laid out as layer-major
+ * groups: b = layer * ent_seqs + s.  One launch serves every layer.
+ * entries: [ent_seqs][Nmax][row]; topk_idx: [ent_seqs][Q][topk]; q, out:
+ * [B][Q][H][512]; win: [B][128][row]; pos: [B][Q]; sink: [B / ent_seqs][H].
+ * Workspace: csa_sparse_attn_workspace_size(B, Q, H, topk).  Errors as for
+ * csa_sparse_attn_decode, and CSA_EINVAL unless ent_seqs divides B.         */
+csa_status csa_sparse_attn_decode_shared(const void* q, int q_fmt, const void* win, int win_fmt,
+                                         const void* entries, int ent_fmt, int64_t Nmax,
+                                         const int32_t* topk_idx, int topk, const int32_t* pos,
+                                         int B, int Q, int H, int ent_seqs, const float* sink,
+                                         float scale, const float* rope_cos,
+                                         const float* rope_sin, int64_t rope_rows, void* out,
+                                         int out_fmt, void* ws, size_t ws_bytes,
+                                         csa_stream_t stream);
+
 size_t hca_attn_workspace_size(int B, int Q, int H, int64_t Nmax);
 csa_status hca_attn_decode(const void* q, int q_fmt, const void* win, int win_fmt, int win_mode,
                            const int32_t* win_base, int64_t win_rows, const void* entries,

@@ -79,6 +79,9 @@ _SIGS = {
     "csa_sparse_attn_workspace_size": (_SZ, [_I, _I, _I, _I]),
     "csa_sparse_attn_decode": (_I, [_VP, _I, _VP, _I, _I, _VP, _I64, _VP, _I, _I64, _VP, _I, _VP,
                                     _I, _I, _I, _VP, _F, _VP, _VP, _I64, _VP, _I, _VP, _SZ, _VP]),
+    "csa_sparse_attn_decode_shared": (_I, [_VP, _I, _VP, _I, _VP, _I, _I64, _VP, _I, _VP, _I, _I,
+                                           _I, _I, _VP, _F, _VP, _VP, _I64, _VP, _I, _VP, _SZ,
+                                           _VP]),
     "hca_attn_workspace_size": (_SZ, [_I, _I, _I, _I64]),
     "hca_attn_decode": (_I, [_VP, _I, _VP, _I, _I, _VP, _I64, _VP, _I, _I64, _I, _VP, _I, _I, _I,
                              _VP, _F, _VP, _VP, _I64, _VP, _I, _VP, _SZ, _VP]),
@@ -246,6 +249,17 @@ def csa_sparse_attn_decode(q, q_fmt, win, win_fmt, win_mode, win_base, win_rows,
         _ptr(pos), int(B), int(Q), int(H), _ptr(sink), float(scale), _ptr(rope_cos),
         _ptr(rope_sin), int(rope_cos.shape[0]), _ptr(out), _fmt(out_fmt), _ptr(ws),
         ws.numel() if ws is not None else 0, _stream(stream)), "csa_sparse_attn_decode")
+
+
+def csa_sparse_attn_decode_shared(q, q_fmt, win, win_fmt, entries, ent_fmt, Nmax, topk_idx, topk,
+                                  pos, B, Q, H, ent_seqs, sink, scale, rope_cos, rope_sin, out,
+                                  out_fmt, ws, stream=None):
+    _check(lib().csa_sparse_attn_decode_shared(
+        _ptr(q), _fmt(q_fmt), _ptr(win), _fmt(win_fmt), _ptr(entries), _fmt(ent_fmt), int(Nmax),
+        _ptr(topk_idx), int(topk), _ptr(pos), int(B), int(Q), int(H), int(ent_seqs), _ptr(sink),
+        float(scale), _ptr(rope_cos), _ptr(rope_sin), int(rope_cos.shape[0]), _ptr(out),
+        _fmt(out_fmt), _ptr(ws), ws.numel() if ws is not None else 0, _stream(stream)),
+        "csa_sparse_attn_decode_shared")
 
 
 def hca_attn_workspace_size(B, Q, H, Nmax):

@@ -311,6 +311,8 @@ csa_status csa_index_topk_bf16(const void* q_idx, int q_fmt, const float* w_idx,
 // ---------------------------------------------------------------- attention
 static csa_status check_attn(const AttnArgs& a) {
   REQUIRE(a.B >= 1 && a.Q >= 1, CSA_EINVAL, "B and Q must be >= 1");
+  REQUIRE(a.ent_seqs >= 1 && a.B % a.ent_seqs == 0, CSA_EINVAL,
+          "ent_seqs must divide B (got %d for B = %d)", a.ent_seqs, a.B);
   REQUIRE(a.H >= 16 && a.H % 16 == 0 && a.H <= 1024, CSA_EUNSUPPORTED,
           "H must be a multiple of 16 in [16, 1024]");
   REQUIRE(a.q_fmt == CSA_F32 || a.q_fmt == CSA_BF16, CSA_EUNSUPPORTED, "q_fmt must be F32 or BF16");
@@ -372,7 +374,7 @@ static AttnArgs make_attn(const void* q, int q_fmt, const void* win, int win_fmt
   a.win = win; a.win_fmt = win_fmt; a.win_mode = win_mode; a.win_base = win_base;
   a.win_rows = win_rows;
   a.entries = entries; a.ent_fmt = ent_fmt; a.Nmax = Nmax;
-  a.pos = pos; a.B = B; a.Q = Q; a.H = H;
+  a.pos = pos; a.B = B; a.Q = Q; a.H = H; a.ent_seqs = B;
   a.sink = sink; a.scale = scale;
   a.rope_cos = rope_cos; a.rope_sin = rope_sin; a.rope_rows = rope_rows;
   a.out = out; a.out_fmt = out_fmt;
@@ -392,6 +394,29 @@ csa_status csa_sparse_attn_decode(const void* q, int q_fmt, const void* win, int
   AttnArgs a = make_attn(q, q_fmt, win, win_fmt, win_mode, win_base, win_rows, entries, ent_fmt,
                          Nmax, pos, B, Q, H, sink, scale, rope_cos, rope_sin, rope_rows, out,
                          out_fmt);
+  a.dense = 0;
+  a.topk_idx = topk_idx;
+  a.topk = topk;
+  a.ratio = 4;
+  return run_attn(a, ws, ws_bytes, (hipStream_t)stream);
+}
+
+csa_status csa_sparse_attn_decode_shared(const void* q, int q_fmt, const void* win, int win_fmt,
+                                         const void* entries, int ent_fmt, int64_t Nmax,
+                                         const int32_t* topk_idx, int topk, const int32_t* pos,
+                                         int B, int Q, int H, int ent_seqs, const float* sink,
+                                         float scale, const float* rope_cos,
+                                         const float* rope_sin, int64_t rope_rows, void* out,
+                                         int out_fmt, void* ws, size_t ws_bytes,
+                                         csa_stream_t stream) {
+  REQUIRE(topk >= 0 && topk <= 8192, CSA_EUNSUPPORTED, "topk must be in [0, 8192]");
+  REQUIRE(ent_seqs >= 1 && B % ent_seqs == 0, CSA_EINVAL,
+          "ent_seqs must divide B (got %d for B = %d)", ent_seqs, B);
+  if (topk > 0) REQUIRE_PTR(topk_idx);
+  AttnArgs a = make_attn(q, q_fmt, win, win_fmt, CSA_WIN_RING128, nullptr, kWindow, entries,
+                         ent_fmt, Nmax, pos, B, Q, H, sink, scale, rope_cos, rope_sin, rope_rows,
+                         out, out_fmt);
+  a.ent_seqs = ent_seqs;
   a.dense = 0;
   a.topk_idx = topk_idx;
   a.topk = topk;

@@ -71,10 +71,10 @@ __device__ __forceinline__ RowRef resolve_row(const AttnArgs& a, int64_t unit, i
     if (e >= nvis) return r;
   } else {
     if (j - kWindow >= a.topk) return r;
-    e = a.topk_idx[unit * a.topk + (j - kWindow)];
+    e = a.topk_idx[((b % a.ent_seqs) * a.Q + (unit - b * a.Q)) * a.topk + (j - kWindow)];
     if (e < 0 || e >= a.Nmax) return r;
   }
-  r.p = (const uint8_t*)a.entries + ((size_t)b * (size_t)a.Nmax + (size_t)e) * ent_rb;
+  r.p = (const uint8_t*)a.entries + ((size_t)(b % a.ent_seqs) * (size_t)a.Nmax + (size_t)e) * ent_rb;
   return r;
 }
 
@@ -529,6 +529,10 @@ __global__ void __launch_bounds__(kAttnThreads, HT <= 2 ? 2 : 1) attn_dense_all_
   const int r16 = lane & 15;
   const int kq = lane >> 4;
   const int64_t b = unit / a.Q;
+  // sequences share entry set (and top-k list) b % ent_seqs; sinks are [b / ent_seqs][H]
+  const int64_t be = b % a.ent_seqs;
+  const int64_t eunit = be * a.Q + (unit - b * a.Q);
+  const float* sinks = a.sink + (b / a.ent_seqs) * a.H;
   const int t = a.pos[unit];
   const int64_t nvis = unit_nvis(a, t);
   const int64_t list_len = kWindow + (SPARSE ? (int64_t)a.topk : nvis);
@@ -541,7 +545,7 @@ __global__ void __launch_bounds__(kAttnThreads, HT <= 2 ? 2 : 1) attn_dense_all_
   if (SPARSE) {  // the chunk's top-k ids (slot j - j_begin), -1 where absent
     for (int i = tid; i < kChunkCsaLong; i += kAttnThreads) {
       const int64_t jj = j_begin + i;
-      Ids[i] = (jj >= kWindow && jj < j_end) ? a.topk_idx[unit * a.topk + (jj - kWindow)] : -1;
+      Ids[i] = (jj >= kWindow && jj < j_end) ? a.topk_idx[eunit * a.topk + (jj - kWindow)] : -1;
     }
     __syncthreads();
   }
@@ -606,7 +610,7 @@ __global__ void __launch_bounds__(kAttnThreads, HT <= 2 ? 2 : 1) attn_dense_all_
   // entry rows [max(j_begin, 128), j_end)
   const int64_t je = j_begin > kWindow ? j_begin : kWindow;
   if (je < j_end && a.Nmax > 0) {
-    const uint8_t* ebase = (const uint8_t*)a.entries + (size_t)b * (size_t)a.Nmax * a.ent_rb;
+    const uint8_t* ebase = (const uint8_t*)a.entries + (size_t)be * (size_t)a.Nmax * a.ent_rb;
     auto ent_row = [&](int64_t j) -> const uint8_t* {
       if (SPARSE) {
         const int32_t e = Ids[j - j_begin];
@@ -625,7 +629,7 @@ __global__ void __launch_bounds__(kAttnThreads, HT <= 2 ? 2 : 1) attn_dense_all_
     // wave is past its last read of Al first.)
     __syncthreads();
     if (w < HT && kq == 0) {
-      const float sink2 = a.sink[16 * (ht0 + w) + r16] * kLog2e;
+      const float sink2 = sinks[16 * (ht0 + w) + r16] * kLog2e;
       const float den = (sm == -INFINITY) ? 0.f : sl + exp2f(sink2 - sm);
       Al[16 * w + r16] = den > 0.f ? 1.f / den : 0.f;
     }
@@ -716,6 +720,10 @@ __global__ void __launch_bounds__(kAttnThreads) attn_mfma_kernel(AttnArgs a, int
   const int hg = it.hg;
   const int chunk = it.chunk;
   const int64_t b = unit / a.Q;
+  // sequences share entry set (and top-k list) b % ent_seqs; sinks are [b / ent_seqs][H]
+  const int64_t be = b % a.ent_seqs;
+  const int64_t eunit = be * a.Q + (unit - b * a.Q);
+  const float* sinks = a.sink + (b / a.ent_seqs) * a.H;
   const int t = a.pos[unit];
   const int64_t nvis = unit_nvis(a, t);
   const int64_t list_len = kWindow + (a.dense ? nvis : (int64_t)a.topk);
@@ -732,14 +740,14 @@ __global__ void __launch_bounds__(kAttnThreads) attn_mfma_kernel(AttnArgs a, int
     if (LONG) {
       for (int i = tid; i < kChunkCsaLong; i += kAttnThreads) {
         const int64_t jj = j_begin + i;
-        Ids[i] = (jj >= kWindow && jj < j_end) ? a.topk_idx[unit * a.topk + (jj - kWindow)] : -1;
+        Ids[i] = (jj >= kWindow && jj < j_end) ? a.topk_idx[eunit * a.topk + (jj - kWindow)] : -1;
       }
       __syncthreads();
     } else {
 #pragma unroll
       for (int i = 0; i < kMaxIdsPerLane; ++i) {
         const int64_t jj = j_begin + 16 * i + r16;
-        ids[i] = (jj >= kWindow && jj < j_end) ? a.topk_idx[unit * a.topk + (jj - kWindow)] : -1;
+        ids[i] = (jj >= kWindow && jj < j_end) ? a.topk_idx[eunit * a.topk + (jj - kWindow)] : -1;
       }
     }
   }
@@ -768,7 +776,7 @@ __global__ void __launch_bounds__(kAttnThreads) attn_mfma_kernel(AttnArgs a, int
   // entry rows [max(j_begin, 128), j_end)
   const int64_t je = j_begin > kWindow ? j_begin : kWindow;
   if (je < j_end && a.Nmax > 0) {
-    const uint8_t* ebase = (const uint8_t*)a.entries + (size_t)b * (size_t)a.Nmax * a.ent_rb;
+    const uint8_t* ebase = (const uint8_t*)a.entries + (size_t)be * (size_t)a.Nmax * a.ent_rb;
     if (a.dense) {
       auto ent_row = [&](int64_t j) -> const uint8_t* {
         const int64_t e = j - kWindow;
@@ -808,7 +816,7 @@ __global__ void __launch_bounds__(kAttnThreads) attn_mfma_kernel(AttnArgs a, int
     return;
   }
   // single chunk: finish here
-  const float sink2 = a.sink[16 * hg + r16] * kLog2e;
+  const float sink2 = sinks[16 * hg + r16] * kLog2e;
   const float den = (st.m == -INFINITY) ? 0.f : st.l + exp2f(sink2 - st.m);
   const float inv = den > 0.f ? 1.f / den : 0.f;
   float iv[4];
@@ -850,7 +858,7 @@ __global__ void __launch_bounds__(kAttnThreads) attn_merge_kernel(AttnArgs a, in
   const int rr = rope_row(a, a.pos[unit]);
   const int h = tid >> 4;
   const int d0 = 64 * slice + 4 * (tid & 15);
-  const float sink2 = a.sink[16 * hg + h] * kLog2e;
+  const float sink2 = a.sink[(unit / a.Q / a.ent_seqs) * a.H + 16 * hg + h] * kLog2e;
   float M = -INFINITY;
   float L = 0.f;
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
@@ -924,6 +932,7 @@ __global__ void __launch_bounds__(kAttnThreads) attn_f32_kernel(AttnArgs a) {
   const int64_t unit = a.unit_off + blockIdx.y;
   const int head = blockIdx.x;
   const int64_t b = unit / a.Q;
+  const float* sinks = a.sink + (b / a.ent_seqs) * a.H;  // sinks are [b / ent_seqs][H]
   const int t = a.pos[unit];
   const int rr = rope_row(a, t);
   const int64_t nvis = unit_nvis(a, t);
@@ -962,7 +971,7 @@ __global__ void __launch_bounds__(kAttnThreads) attn_f32_kernel(AttnArgs a) {
     oy = oy * al + pz * cy;
     m = mn;
   }
-  const float sink = a.sink[head];
+  const float sink = sinks[head];
   const float den = (m == -INFINITY) ? 0.f : l + expf(sink - m);
   const float inv = den > 0.f ? 1.f / den : 0.f;
   float x = ox * inv, y = oy * inv;

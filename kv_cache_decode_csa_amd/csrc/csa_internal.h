@@ -55,6 +55,8 @@ struct AttnArgs {
   const void* q; int q_fmt;
   const void* win; int win_fmt; int win_mode; const int32_t* win_base; int64_t win_rows;
   const void* entries; int ent_fmt; int64_t Nmax;
+  int ent_seqs;                        // sequence b reads entry set and top-k list b % ent_seqs
+                                       // and sinks [b / ent_seqs][H] (B: one set per sequence)
   int dense;                           // 0: top-k list (CSA), 1: all completed entries (HCA)
   const int32_t* topk_idx; int topk;   // CSA list
   int ratio;                           // HCA visibility ratio

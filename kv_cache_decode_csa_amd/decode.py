@@ -142,7 +142,8 @@ class CsaDecodeLayer:
         if w.extra.get("layer"):
             self._init_layer(w.extra["layer"], copies, device)
         # reuse layers of a layer group: their own queries, sinks and windows,
-        # the Full layer's entries and top-k ids
+        # the Full layer's entries and top-k ids; the whole group attends in
+        # one csa_sparse_attn_decode_shared call (layer-major rows)
         self.reuse = []
         for layer in range(1, w.extra.get("reuse", 0) + 1):
             rq, rsink, rwin = synth.reuse_layer_inputs(w, layer)
@@ -151,6 +152,18 @@ class CsaDecodeLayer:
                 torch.from_numpy(rsink).to(device),
                 _dev_rows(rwin, w.win_fmt, device),
                 torch.empty((B, 1, w.H, 512), dtype=qdt, device=device)))
+        if self.reuse:
+            L = 1 + len(self.reuse)
+            self.q_group = torch.cat([self.q] + [r[0] for r in self.reuse])
+            self.win_group = torch.cat([self.win] + [r[2] for r in self.reuse])
+            self.sink_group = torch.cat([self.sink] + [r[1] for r in self.reuse])
+            self.pos_group = self.pos.repeat(L, 1)
+            self.out_group = torch.empty((L * B, 1, w.H, 512), dtype=qdt, device=device)
+            self.out = self.out_group[:B]
+            self.reuse = [(rq, rs, rw, self.out_group[(i + 1) * B:(i + 2) * B])
+                          for i, (rq, rs, rw, _) in enumerate(self.reuse)]
+            self.ws_group = _lib.workspace(
+                _lib.csa_sparse_attn_workspace_size(L * B, 1, w.H, w.topk))
 
     def _init_layer(self, cfg, copies, device):
         w = self.w
@@ -201,15 +214,15 @@ class CsaDecodeLayer:
         core = [("csa_compress", compress), ("csa_index_topk", index_topk),
                 ("csa_sparse_attn_decode", sparse_attn)]
         if self.reuse:
-            def reuse_attn():
-                for rq, rsink, rwin, rout in self.reuse:
-                    _lib.csa_sparse_attn_decode(rq, w.q_fmt, rwin, win_fmt, _lib.WIN_RING128,
-                                                None, 128, ent, ent_fmt, N, self.topk, w.topk,
-                                                self.pos, B, 1, w.H, rsink, 512 ** -0.5,
-                                                self.rope[0], self.rope[1], rout, w.q_fmt,
-                                                self.ws_att)
+            L = 1 + len(self.reuse)
 
-            core.append(("csa_sparse_attn_reuse", reuse_attn))
+            def group_attn():
+                _lib.csa_sparse_attn_decode_shared(
+                    self.q_group, w.q_fmt, self.win_group, win_fmt, ent, ent_fmt, N, self.topk,
+                    w.topk, self.pos_group, L * B, 1, w.H, B, self.sink_group, 512 ** -0.5,
+                    self.rope[0], self.rope[1], self.out_group, w.q_fmt, self.ws_group)
+
+            core[2] = ("csa_sparse_attn_group", group_attn)
         if self.lw is None:
             return core
         lw = self.lw[c]

@@ -276,3 +276,47 @@ def test_permutation_padding_and_determinism(tables):
     close_bf16(run(ids[:, ::-1].copy()), a)                # permutation
     padded = np.concatenate([ids, np.full((B, 100), -1, np.int32)], axis=1)
     close_bf16(run(padded), a)                             # -1 rows are absent
+
+
+@pytest.mark.parametrize("Q,efmt", [(1, "fp4_e4m3_16"), (1, "fp8_mx32"), (20, "bf16")])
+def test_shared_entries_layer_group(tables, Q, efmt):
+    """csa_sparse_attn_decode_shared: L layers x B sequences in one launch,
+    sharing B entry sets and top-k lists, each layer with its own q, window
+    and sinks, equal bit for bit to one csa_sparse_attn_decode call per layer
+    (20 queries per sequence take the 640-row chunks)."""
+    cos, sin = tables
+    B, L, H, N, k = 3, 4, 64, 2500, 512
+    rng = np.random.default_rng(31 + Q)
+    ent = rng.standard_normal((B, N, 512)).astype(np.float32)
+    if efmt == "bf16":
+        ent = synth.bf16_round(ent)
+    ent_d = upload_rows(ent, efmt)
+    q = synth.bf16_round(rng.standard_normal((L, B, Q, H, 512)).astype(np.float32))
+    win = rng.standard_normal((L, B, 128, 512)).astype(np.float32)
+    win_d = upload_rows(win.reshape(L * B, 128, 512), "fp8_mx32")
+    sink = rng.standard_normal((L, H)).astype(np.float32)
+    pos = (np.array([4 * N - 1, 300, 2000])[:, None] + np.arange(Q)[None, :] * 0).astype(np.int32)
+    ids = np.stack([np.stack([gen_ids(rng, min((int(pos[b, i]) + 1) // 4, N), k, N)
+                              for i in range(Q)]) for b in range(B)])        # [B, Q, k]
+    ids_d = i32(ids)
+    say(f"shared attn L={L} B={B} Q={Q} {efmt}")
+    out = torch.empty((L * B, Q, H, 512), dtype=torch.bfloat16, device="cuda")
+    ws = _lib.workspace(_lib.csa_sparse_attn_workspace_size(L * B, Q, H, k))
+    _lib.csa_sparse_attn_decode_shared(bf16(q.reshape(L * B, Q, H, 512)), "bf16", win_d, "fp8_mx32",
+                                       ent_d, efmt, N, ids_d, k, i32(np.tile(pos, (L, 1))), L * B,
+                                       Q, H, B, f32(sink), 512 ** -0.5, cos, sin, out, "bf16", ws)
+    ws1 = _lib.workspace(_lib.csa_sparse_attn_workspace_size(B, Q, H, k))
+    for lay in range(L):
+        ref = torch.empty((B, Q, H, 512), dtype=torch.bfloat16, device="cuda")
+        _lib.csa_sparse_attn_decode(bf16(q[lay]), "bf16", win_d[lay * B:(lay + 1) * B].contiguous(),
+                                    "fp8_mx32", _lib.WIN_RING128, None, 128, ent_d, efmt, N, ids_d,
+                                    k, i32(pos), B, Q, H, f32(sink[lay]), 512 ** -0.5, cos, sin,
+                                    ref, "bf16", ws1)
+        torch.cuda.synchronize()
+        assert torch.equal(out[lay * B:(lay + 1) * B], ref), lay
+    # ent_seqs must divide B
+    with pytest.raises(_lib.CsaError):
+        _lib.csa_sparse_attn_decode_shared(bf16(q.reshape(L * B, Q, H, 512)), "bf16", win_d,
+                                           "fp8_mx32", ent_d, efmt, N, ids_d, k,
+                                           i32(np.tile(pos, (L, 1))), L * B, Q, H, 5, f32(sink),
+                                           512 ** -0.5, cos, sin, out, "bf16", ws)
