@@ -13,6 +13,11 @@
  *     64 dims undone on the output (sections 3.3, 3.4 Eq. 27, 5.3, 6.1).
  * Cache row formats follow the V4-Flash model record (528 B FP8 rows, 288 B
  * FP4 rows) and the V4.1-Flash diagram page (E2M1 + E4M3 scale per 16).
+ * Around the path: the layer's query path, index-query preparation and
+ * window-entry write (csa_layer_input) and its grouped low-rank output
+ * projection (csa_layer_output), sections 3.2, 3.5 and 5.2; the V4.1 CSA2
+ * compressor at m = 2 and m = 1 and layer groups that share main KV and top-k
+ * ids (csa_sparse_attn_decode_shared), V4.1-Flash diagram page.
  *
  * Conventions for every entry point
  *   - Pointers are DEVICE pointers unless marked (host).  The caller owns every
