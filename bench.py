@@ -43,6 +43,20 @@ WORKLOADS = {"csa_1m_fp8": 5, "csa_1m_mxfp4": 5, "csa_1m_fp4idx": 5, "csa_1m_fp8
              "hca_1m_bf16": 3, "csa_prefill_32k_bf16": 4}
 
 
+# the default workload's metric; the others name what they measure
+METRICS = {
+    "csa_1m_fp8": "CSA top-512 decode tokens/s per layer at 1M ctx; achieved HBM GB/s vs peak",
+    "csa_64k_bf16": "CSA top-512 decode tokens/s per layer at 64K ctx (bf16 cache); achieved HBM "
+                    "GB/s vs peak",
+    "hca_1m_bf16": "HCA decode tokens/s per layer at 1M ctx (bf16 cache); achieved HBM GB/s vs "
+                   "peak",
+    "csa_1m_fp8_layer": "CSA top-512 decode tokens/s per layer at 1M ctx, whole layer (query path, "
+                        "window write and output projection included); achieved HBM GB/s vs peak",
+    "csa2_m1_256k": "CSA2 m=1 layer-group decode tokens/s per layer at 256K ctx (6 layers sharing "
+                    "main KV and top-512 ids); achieved HBM GB/s vs peak",
+}
+
+
 def row_bytes(fmt, dim):
     return {"f32": 4 * dim, "bf16": 2 * dim, "fp8_mx32": dim + dim // 32,
             "fp4_e4m3_16": dim // 2 + dim // 16, "fp4_mx32": dim // 2 + dim // 32}[fmt]
@@ -437,7 +451,7 @@ def main():
     dom_gbs = ab[dom] / (phases[dom] * 1e-3) / 1e9
     step_bytes = sum(ab.values())
     res = {
-        "metric": "CSA top-512 decode tokens/s per layer at 1M ctx; achieved HBM GB/s vs peak",
+        "metric": METRICS.get(w.name, METRICS["csa_1m_fp8"]),
         "value": layers * w.B / (ms * 1e-3),
         "unit": "tokens/s/layer",
         "n_gpus": 1,
