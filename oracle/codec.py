@@ -274,10 +274,53 @@ def dequantize_fp4_mx32(row, dim):
 # generic helpers
 # ----------------------------------------------------------------------------
 
-FORMATS = ("f32", "bf16", "fp8_mx32", "fp4_e4m3_16", "fp4_mx32")
+# ----------------------------------------------------------------------------
+# V4 mixed rows: 448 NoPE dims in FP8, the 64 RoPE dims in bf16 ("DeepSeek-V4
+# deep dive" sections 3.1 and 3.3 notes: 448 + 64 x 2 = 576 bytes, scale bytes
+# not counted; the NoPE dims are rounded to FP8 in blocks of 64)
+# ----------------------------------------------------------------------------
+
+MIX_NOPE = 448
+MIX_GROUP = 64
+MIX_ROW_BYTES = 592  # 448 codes + 128 bf16 bytes + 7 E8M0 scales, padded to 16 B
+
+
+def quantize_mix576(x):
+    """x: [..., 512] float (f32-representable) -> uint8 [..., 592]: E4M3 codes
+    of dims 0..447 with one E8M0 scale per 64 (the MX rule: the smallest e with
+    amax <= 448 * 2**e), the bf16 bits (RNE) of dims 448..511, the 7 scale
+    bytes e + 127, then 9 zero bytes."""
+    x = np.asarray(x, dtype=np.float64)
+    assert x.shape[-1] == 512
+    lead = x.shape[:-1]
+    g = x[..., :MIX_NOPE].reshape(lead + (MIX_NOPE // MIX_GROUP, MIX_GROUP))
+    amax = np.max(np.where(np.isfinite(g), np.abs(g), 0.0), axis=-1)
+    e = mx32_exponent(amax)
+    codes = e4m3_encode(g * np.exp2(-e.astype(np.float64))[..., None]).reshape(lead + (MIX_NOPE,))
+    rope_bits = f32_to_bf16_bits(x[..., MIX_NOPE:].astype(np.float32))
+    rope_bytes = np.ascontiguousarray(rope_bits.astype("<u2")).view(np.uint8).reshape(lead + (128,))
+    scales = (e + 127).astype(np.uint8)
+    pad = np.zeros(lead + (MIX_ROW_BYTES - 576 - 7,), np.uint8)
+    return np.concatenate([codes.astype(np.uint8), rope_bytes, scales, pad], axis=-1)
+
+
+def dequantize_mix576(row):
+    row = np.asarray(row, dtype=np.uint8)
+    lead = row.shape[:-1]
+    sc = row[..., 576:583].astype(np.int64) - 127
+    v = e4m3_decode(row[..., :MIX_NOPE]).reshape(lead + (7, MIX_GROUP))
+    nope = (v * np.exp2(sc.astype(np.float64))[..., None]).reshape(lead + (MIX_NOPE,))
+    bits = np.ascontiguousarray(row[..., MIX_NOPE:576]).view("<u2").reshape(lead + (64,))
+    return np.concatenate([nope, bf16_bits_to_f64(bits)], axis=-1)
+
+
+FORMATS = ("f32", "bf16", "fp8_mx32", "fp4_e4m3_16", "fp4_mx32", "mix576")
 
 
 def row_bytes(fmt, dim):
+    if fmt == "mix576":
+        assert dim == 512
+        return MIX_ROW_BYTES
     return {"f32": 4 * dim, "bf16": 2 * dim, "fp8_mx32": fp8_mx32_row_bytes(dim),
             "fp4_e4m3_16": fp4_row_bytes(dim), "fp4_mx32": fp4_mx32_row_bytes(dim)}[fmt]
 
@@ -300,6 +343,9 @@ def store(x, fmt):
     if fmt == "fp4_mx32":
         r = quantize_fp4_mx32(x.astype(np.float32))
         return r, dequantize_fp4_mx32(r, x.shape[-1])
+    if fmt == "mix576":
+        r = quantize_mix576(x.astype(np.float32).astype(np.float64))
+        return r, dequantize_mix576(r)
     raise ValueError(fmt)
 
 
@@ -315,4 +361,6 @@ def load(stored, fmt, dim):
         return dequantize_fp4_e4m3_16(stored, dim)
     if fmt == "fp4_mx32":
         return dequantize_fp4_mx32(stored, dim)
+    if fmt == "mix576":
+        return dequantize_mix576(stored)
     raise ValueError(fmt)

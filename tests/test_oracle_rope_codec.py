@@ -247,3 +247,43 @@ def test_bf16_rne():
     x = np.array([1.0, 1.0 + 2 ** -8, 1.0 + 3 * 2 ** -8, 1.0 + 2 ** -8 + 2 ** -20], np.float32)
     np.testing.assert_array_equal(codec.round_to_bf16(x),
                                   [1.0, 1.0, 1.0 + 2 ** -6, 1.0 + 2 ** -7])
+
+
+def test_mix576_layout_and_rounding():
+    """The V4 mixed row (deep dive sections 3.1 and 3.3 notes): 448 FP8 + 64
+    bf16 = 576 bytes before scales, FP8 in blocks of 64.  The 64 RoPE dims are
+    RNE bf16 bit patterns, exactly; every NoPE value decodes to the nearest
+    E4M3 grid value of x / 2**e (brute force over all finite codes, ties to
+    the even code) times 2**e, with e the smallest exponent that fits the
+    block's amax under 448."""
+    assert codec.MIX_NOPE * 1 + 64 * 2 == 576
+    assert codec.row_bytes("mix576", 512) == 592 and 592 % 16 == 0
+    rng = np.random.default_rng(21)
+    x = rng.standard_normal((6, 512)) * np.exp2(rng.integers(-12, 12, (6, 1)))
+    x[1, :64] = 0.0                       # an all-zero block
+    x[2, 100] = 448.0 * 3.9               # a block whose amax sets a high scale
+    x = x.astype(np.float32).astype(np.float64)
+    row = codec.quantize_mix576(x)
+    assert row.shape == (6, 592) and np.all(row[:, 583:] == 0)
+    back = codec.dequantize_mix576(row)
+    np.testing.assert_array_equal(back[:, 448:], codec.round_to_bf16(x[:, 448:]))
+    bits = np.ascontiguousarray(row[:, 448:576]).view("<u2")
+    np.testing.assert_array_equal(bits, codec.f32_to_bf16_bits(x[:, 448:].astype(np.float32)))
+    grid = codec.e4m3_decode(np.arange(256, dtype=np.uint8))
+    fin = np.isfinite(grid)
+    codes = np.arange(256)[fin]
+    vals = grid[fin]
+    for r in range(6):
+        for g in range(7):
+            blk = x[r, 64 * g:64 * g + 64]
+            amax = np.abs(blk).max()
+            e = min(k for k in range(-127, 128) if amax <= 448.0 * 2.0 ** k)
+            assert int(row[r, 576 + g]) - 127 == e, (r, g)
+            for j in range(64):
+                y = blk[j] * 2.0 ** -e
+                d = np.abs(vals - y)
+                best = np.flatnonzero(d == d.min())
+                if len(best) > 1:  # tie: the even code
+                    best = best[(codes[best] & 1) == 0]
+                want = vals[best[0]] * 2.0 ** e
+                assert back[r, 64 * g + j] == want or (want == 0 and back[r, 64 * g + j] == 0)
