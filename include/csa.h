@@ -75,13 +75,19 @@ enum {
                            528 B for dim 512, 132 B for dim 128                          */
   CSA_FP4_E4M3_16 = 3,  /* dim/2 bytes of E2M1 codes (element 2j in the low nibble of
                            byte j), then dim/16 E4M3 scale bytes: 288 B for dim 512      */
-  CSA_FP4_MX32 = 4      /* OCP MX FP4 ("DeepSeek-V4 deep dive" section 5.2 notes: the
+  CSA_FP4_MX32 = 4,     /* OCP MX FP4 ("DeepSeek-V4 deep dive" section 5.2 notes: the
                            FP4 indexer): dim/2 bytes of E2M1 codes (element 2j in the low
                            nibble of byte j), then dim/32 E8M0 scale bytes X + 127 with
                            X = floor(log2 amax) - 2 clamped to [-127, 127] (amax 0 ->
                            -127); codes RNE(x / 2^X) saturating at 6; a non-finite group
                            gets scale 0xFF and zero codes.  68 B per 128-d index key.
                            Index keys and kv_quantize / kv_dequantize only.            */
+  CSA_MIX576 = 5        /* the V4 mixed row ("DeepSeek-V4 deep dive" sections 3.1, 3.3
+                           notes: 448 FP8 + 64 bf16 = 576 bytes before scales, FP8 in
+                           blocks of 64), dim 512 only: 448 E4M3 codes (the FP8_MX32 rule
+                           per block of 64), the 64 RoPE dims as bf16 (RNE), 7 E8M0
+                           scale bytes, 9 zero bytes: 592 B.  kv_quantize /
+                           kv_dequantize only.                                          */
 };
 
 /* Addressing of the raw sliding-window rows. */

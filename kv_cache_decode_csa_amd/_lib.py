@@ -13,10 +13,10 @@ import os
 
 import torch
 
-F32, BF16, FP8_MX32, FP4_E4M3_16, FP4_MX32 = 0, 1, 2, 3, 4
+F32, BF16, FP8_MX32, FP4_E4M3_16, FP4_MX32, MIX576 = 0, 1, 2, 3, 4, 5
 WIN_RING128, WIN_LINEAR = 0, 1
 FMT_NAMES = {"f32": F32, "bf16": BF16, "fp8_mx32": FP8_MX32, "fp4_e4m3_16": FP4_E4M3_16,
-             "fp4_mx32": FP4_MX32}
+             "fp4_mx32": FP4_MX32, "mix576": MIX576}
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libcsa.so")
 

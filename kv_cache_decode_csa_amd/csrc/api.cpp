@@ -42,7 +42,7 @@ bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 #define REQUIRE_PTR(p) \
   REQUIRE((p) != nullptr && aligned16(p), CSA_EINVAL, "%s must be a non-null 16-byte aligned pointer", #p)
 
-bool valid_fmt(int f) { return f >= CSA_F32 && f <= CSA_FP4_MX32; }
+bool valid_fmt(int f) { return f >= CSA_F32 && f <= CSA_MIX576; }
 // cache rows that attention and the compressor read or write (MXFP4-MX32 is
 // an index-key format)
 bool row_fmt(int f) { return f >= CSA_F32 && f <= CSA_FP4_E4M3_16; }
@@ -72,6 +72,7 @@ size_t kv_row_bytes(int fmt, int dim) {
     case CSA_FP8_MX32: return dim % 32 ? 0 : (size_t)dim + dim / 32;
     case CSA_FP4_E4M3_16: return dim % 32 ? 0 : (size_t)dim / 2 + dim / 16;
     case CSA_FP4_MX32: return dim % 32 ? 0 : (size_t)dim / 2 + dim / 32;
+    case CSA_MIX576: return dim == 512 ? 592 : 0;
     default: return 0;
   }
 }
@@ -120,6 +121,7 @@ csa_status kv_quantize(const void* src, int src_fmt, void* dst, int dst_fmt, int
           "FP8_MX32 rows need dim % 128 == 0 (4-byte aligned rows)");
   REQUIRE(dst_fmt != CSA_FP4_MX32 || dim % 128 == 0, CSA_EUNSUPPORTED,
           "FP4_MX32 rows need dim % 128 == 0 (4-byte aligned rows)");
+  REQUIRE(dst_fmt != CSA_MIX576 || dim == 512, CSA_EUNSUPPORTED, "MIX576 rows need dim == 512");
   if (rows == 0) return ok();
   REQUIRE_PTR(src);
   REQUIRE_PTR(dst);
@@ -137,6 +139,7 @@ csa_status kv_dequantize(const void* src, int src_fmt, void* dst, int dst_fmt, i
           "FP8_MX32 rows need dim % 128 == 0 (4-byte aligned rows)");
   REQUIRE(src_fmt != CSA_FP4_MX32 || dim % 128 == 0, CSA_EUNSUPPORTED,
           "FP4_MX32 rows need dim % 128 == 0 (4-byte aligned rows)");
+  REQUIRE(src_fmt != CSA_MIX576 || dim == 512, CSA_EUNSUPPORTED, "MIX576 rows need dim == 512");
   if (rows == 0) return ok();
   REQUIRE_PTR(src);
   REQUIRE_PTR(dst);

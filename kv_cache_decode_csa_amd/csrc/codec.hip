@@ -134,8 +134,63 @@ __global__ void dequantize_kernel(const uint8_t* __restrict__ src, int src_fmt, 
   }
 }
 
+// V4 mixed rows (dim 512): bytes [0, 448) E4M3 codes of dims 0..447, [448, 576)
+// bf16 dims 448..511, [576, 583) one E8M0 scale per 64 codes, [583, 592) zero.
+// One thread per (row, block of 64): blocks 0..6 are FP8, block 7 the bf16 tail.
+constexpr int kMixRow = 592;
+__global__ void quantize_mix_kernel(const void* __restrict__ src, int src_fmt,
+                                    uint8_t* __restrict__ dst, int64_t rows) {
+  const int64_t g = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (g >= rows * 8) return;
+  const int64_t r = g >> 3;
+  const int blk = (int)(g & 7);
+  uint8_t* row = dst + r * kMixRow;
+  const int64_t base = r * 512 + 64 * blk;
+  if (blk == 7) {
+    for (int j = 0; j < 64; ++j)
+      ((uint16_t*)(row + 448))[j] = f32_to_bf16(load_val(src, src_fmt, base + j));
+    for (int j = 583; j < kMixRow; ++j) row[j] = 0;
+    return;
+  }
+  float amax = 0.f;
+  for (int j = 0; j < 64; ++j) {
+    const float a = __builtin_fabsf(load_val(src, src_fmt, base + j));
+    if (a <= 3.402823466e38f) amax = fmaxf(amax, a);
+  }
+  const int e = mx32_exponent(amax);
+  row[576 + blk] = (uint8_t)(e + 127);
+  for (int q = 0; q < 16; ++q) {
+    uint32_t w = 0;
+    for (int j = 0; j < 4; ++j)
+      w |= f32_to_e4m3(ldexpf(load_val(src, src_fmt, base + 4 * q + j), -e)) << (8 * j);
+    ((uint32_t*)(row + 64 * blk))[q] = w;
+  }
+}
+
+__global__ void dequantize_mix_kernel(const uint8_t* __restrict__ src, void* __restrict__ dst,
+                                      int dst_fmt, int64_t rows) {
+  const int64_t g = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (g >= rows * 8) return;
+  const int64_t r = g >> 3;
+  const int blk = (int)(g & 7);
+  const uint8_t* row = src + r * kMixRow;
+  const int64_t base = r * 512 + 64 * blk;
+  const float f = blk < 7 ? exp2i((int)row[576 + blk] - 127) : 1.f;
+  for (int j = 0; j < 64; ++j) {
+    const float v = blk == 7 ? bf16_to_f32(((const uint16_t*)(row + 448))[j])
+                             : e4m3_to_f32(row[64 * blk + j]) * f;
+    if (dst_fmt == CSA_F32) ((float*)dst)[base + j] = v;
+    else ((uint16_t*)dst)[base + j] = f32_to_bf16(v);
+  }
+}
+
 hipError_t launch_quantize(const void* src, int src_fmt, void* dst, int dst_fmt, int64_t rows,
                            int dim, hipStream_t s) {
+  if (dst_fmt == CSA_MIX576) {
+    hipLaunchKernelGGL(quantize_mix_kernel, dim3((unsigned)((rows * 8 + 255) / 256)), dim3(256), 0,
+                       s, src, src_fmt, (uint8_t*)dst, rows);
+    return hipGetLastError();
+  }
   int gsz = dst_fmt == CSA_FP4_E4M3_16 ? 16 : 32;
   int64_t n = rows * (dim / gsz);
   int64_t blocks = (n + 255) / 256;
@@ -146,6 +201,11 @@ hipError_t launch_quantize(const void* src, int src_fmt, void* dst, int dst_fmt,
 
 hipError_t launch_dequantize(const void* src, int src_fmt, void* dst, int dst_fmt, int64_t rows,
                              int dim, hipStream_t s) {
+  if (src_fmt == CSA_MIX576) {
+    hipLaunchKernelGGL(dequantize_mix_kernel, dim3((unsigned)((rows * 8 + 255) / 256)), dim3(256),
+                       0, s, (const uint8_t*)src, dst, dst_fmt, rows);
+    return hipGetLastError();
+  }
   int gsz = src_fmt == CSA_FP4_E4M3_16 ? 16 : 32;
   int64_t n = rows * (dim / gsz);
   int64_t blocks = (n + 255) / 256;

@@ -43,6 +43,9 @@ def test_row_bytes_and_strings():
     assert L.kv_row_bytes(_lib.FP8_MX32, 128) == 132
     assert L.kv_row_bytes(_lib.BF16, 512) == 1024
     assert L.kv_row_bytes(_lib.FP8_MX32, 100) == 0
+    assert L.kv_row_bytes(_lib.FP4_MX32, 128) == 68
+    assert L.kv_row_bytes(_lib.MIX576, 512) == 592
+    assert L.kv_row_bytes(_lib.MIX576, 128) == 0
     assert L.kv_row_bytes(9, 512) == 0
     assert L.csa_strerror(0) == b"ok"
     assert L.csa_strerror(3) == b"workspace too small"

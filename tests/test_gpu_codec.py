@@ -35,6 +35,8 @@ def _edge_rows(D, rng):
 
 
 def oracle_quantize(x, fmt):
+    if fmt == "mix576":
+        return codec.quantize_mix576(np.asarray(x, dtype=np.float64))
     if fmt == "fp8_mx32":
         return codec.quantize_fp8_mx32(np.asarray(x, dtype=np.float64))
     if fmt == "fp4_mx32":
@@ -64,7 +66,28 @@ def test_quantize_bit_exact(D, fmt):
     np.testing.assert_array_equal(dst2.cpu().numpy(), oracle_quantize(xv, fmt))
 
 
-@pytest.mark.parametrize("fmt", ["fp8_mx32", "fp4_e4m3_16", "fp4_mx32"])
+def test_mix576_quantize_bit_exact():
+    """The V4 mixed row: device bytes equal the oracle's, from f32 and bf16 input."""
+    need_gpu()
+    rng = np.random.default_rng(13)
+    x = np.concatenate([_edge_rows(512, rng), rng.standard_normal((2000, 512)).astype(np.float32)])
+    x[-1, 448:] = np.float32(np.nan)
+    say(f"quantize mix576 rows={len(x)}")
+    dst = torch.empty((len(x), 592), dtype=torch.uint8, device="cuda")
+    _lib.kv_quantize(f32(x), "f32", dst, "mix576", len(x), 512)
+    got = dst.cpu().numpy()
+    mism = np.argwhere(got != oracle_quantize(x, "mix576"))
+    assert len(mism) == 0, f"{len(mism)} bytes differ, first {mism[:5].tolist()}"
+    xb = torch.from_numpy(x[9:]).to(torch.bfloat16).cuda()
+    dst2 = torch.empty((len(x) - 9, 592), dtype=torch.uint8, device="cuda")
+    _lib.kv_quantize(xb, "bf16", dst2, "mix576", len(x) - 9, 512)
+    np.testing.assert_array_equal(dst2.cpu().numpy(),
+                                  oracle_quantize(xb.float().cpu().numpy(), "mix576"))
+    with pytest.raises(_lib.CsaError):
+        _lib.kv_quantize(f32(x[:, :128]), "f32", dst, "mix576", len(x), 128)
+
+
+@pytest.mark.parametrize("fmt", ["fp8_mx32", "fp4_e4m3_16", "fp4_mx32", "mix576"])
 def test_dequantize_exact(fmt):
     need_gpu()
     D = 512
