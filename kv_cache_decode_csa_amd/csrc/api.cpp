@@ -320,8 +320,10 @@ static csa_status check_attn(const AttnArgs& a) {
           "H must be a multiple of 16 in [16, 1024]");
   REQUIRE(a.q_fmt == CSA_F32 || a.q_fmt == CSA_BF16, CSA_EUNSUPPORTED, "q_fmt must be F32 or BF16");
   REQUIRE(a.out_fmt == CSA_F32 || a.out_fmt == CSA_BF16, CSA_EUNSUPPORTED, "out_fmt must be F32 or BF16");
-  REQUIRE(row_fmt(a.win_fmt) && row_fmt(a.ent_fmt), CSA_EUNSUPPORTED,
-          "window and entry rows must be F32, BF16, FP8_MX32 or FP4_E4M3_16");
+  REQUIRE(row_fmt(a.win_fmt) && (row_fmt(a.ent_fmt) || a.ent_fmt == CSA_MIX576), CSA_EUNSUPPORTED,
+          "window rows must be F32, BF16, FP8_MX32 or FP4_E4M3_16; entry rows also MIX576");
+  REQUIRE(a.ent_fmt != CSA_MIX576 || a.q_fmt == CSA_BF16, CSA_EUNSUPPORTED,
+          "MIX576 entry rows need BF16 queries");
   if (a.q_fmt == CSA_BF16)
     REQUIRE(a.win_fmt != CSA_F32 && a.ent_fmt != CSA_F32, CSA_EUNSUPPORTED,
             "F32 rows need F32 queries");

@@ -133,6 +133,10 @@ template <int F> struct Raw;
 template <> struct Raw<CSA_BF16> { uint4 v[4]; };
 template <> struct Raw<CSA_FP8_MX32> { uint2 v[4]; uint32_t sc; };   // sc: groups 4w..4w+3
 template <> struct Raw<CSA_FP4_E4M3_16> { uint32_t v[4]; uint2 sc; }; // sc: groups 8w..8w+7
+// V4 mixed rows: FP8 codes of dims 0..447 (v[s]; scale bytes of blocks 2w,
+// 2w+1 in sc) and, for wave 3, the bf16 dims 448..479 in v[2], v[3] and
+// 480..511 in t
+template <> struct Raw<CSA_MIX576> { uint2 v[4]; uint4 t; uint32_t sc; };
 
 // Loads are unconditional: an absent row is read from a stand-in row of the
 // same buffer and zeroed when its fragments are formed, so the wait before a
@@ -148,6 +152,21 @@ __device__ __forceinline__ void load_raw(const uint8_t* p, int w, int kq, Raw<F>
 #pragma unroll
     for (int s = 0; s < 4; ++s) q.v[s] = *(const uint2*)(p + 128 * w + 32 * s + 8 * kq);
     q.sc = *(const uint32_t*)(p + kHeadDim + 4 * w);
+  } else if (F == CSA_MIX576) {
+    Raw<CSA_MIX576>& q = (Raw<CSA_MIX576>&)r;
+    q.v[0] = *(const uint2*)(p + 128 * w + 8 * kq);
+    q.v[1] = *(const uint2*)(p + 128 * w + 32 + 8 * kq);
+    if (w < 3) {
+      q.v[2] = *(const uint2*)(p + 128 * w + 64 + 8 * kq);
+      q.v[3] = *(const uint2*)(p + 128 * w + 96 + 8 * kq);
+      q.t = make_uint4(0u, 0u, 0u, 0u);
+    } else {
+      const uint4 a = *(const uint4*)(p + 448 + 16 * kq);
+      q.v[2] = make_uint2(a.x, a.y);
+      q.v[3] = make_uint2(a.z, a.w);
+      q.t = *(const uint4*)(p + 512 + 16 * kq);
+    }
+    q.sc = (uint32_t)p[576 + 2 * w] | ((uint32_t)p[577 + 2 * w] << 8);
   } else {
     Raw<CSA_FP4_E4M3_16>& q = (Raw<CSA_FP4_E4M3_16>&)r;
 #pragma unroll
@@ -164,6 +183,17 @@ __device__ __forceinline__ uint4 frag_bf16(const Raw<F>& r, int s, int kq) {
   } else if (F == CSA_FP8_MX32) {
     const Raw<CSA_FP8_MX32>& q = (const Raw<CSA_FP8_MX32>&)r;
     const float sc = exp2i((int)((q.sc >> (8 * s)) & 0xffu) - 127);
+    const bf16x2_t a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(q.v[s].x, sc, false);
+    const bf16x2_t b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(q.v[s].x, sc, true);
+    const bf16x2_t c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(q.v[s].y, sc, false);
+    const bf16x2_t d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(q.v[s].y, sc, true);
+    return make_uint4(__builtin_bit_cast(uint32_t, a), __builtin_bit_cast(uint32_t, b),
+                      __builtin_bit_cast(uint32_t, c), __builtin_bit_cast(uint32_t, d));
+  } else if (F == CSA_MIX576) {
+    const Raw<CSA_MIX576>& q = (const Raw<CSA_MIX576>&)r;
+    if ((threadIdx.x >> 6) == 3 && s >= 2)  // bf16 RoPE dims of wave 3
+      return s == 2 ? make_uint4(q.v[2].x, q.v[2].y, q.v[3].x, q.v[3].y) : q.t;
+    const float sc = exp2i((int)((q.sc >> (8 * (s >> 1))) & 0xffu) - 127);
     const bf16x2_t a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(q.v[s].x, sc, false);
     const bf16x2_t b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(q.v[s].x, sc, true);
     const bf16x2_t c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(q.v[s].y, sc, false);
@@ -1038,6 +1068,8 @@ static void launch_mfma_wl(const AttnArgs& a, int nc, int64_t nu, dim3 grid, Par
     hipLaunchKernelGGL((attn_mfma_kernel<WF, CSA_BF16, LONG>), grid, dim3(kAttnThreads), 0, s, a, cr, nc, nu, part);
   else if (a.ent_fmt == CSA_FP8_MX32)
     hipLaunchKernelGGL((attn_mfma_kernel<WF, CSA_FP8_MX32, LONG>), grid, dim3(kAttnThreads), 0, s, a, cr, nc, nu, part);
+  else if (a.ent_fmt == CSA_MIX576)
+    hipLaunchKernelGGL((attn_mfma_kernel<WF, CSA_MIX576, LONG>), grid, dim3(kAttnThreads), 0, s, a, cr, nc, nu, part);
   else
     hipLaunchKernelGGL((attn_mfma_kernel<WF, CSA_FP4_E4M3_16, LONG>), grid, dim3(kAttnThreads), 0, s, a, cr, nc, nu, part);
 }
@@ -1087,6 +1119,7 @@ static void launch_all_heads_w(const AttnArgs& a, int nc, int64_t nu, Partial* p
                                hipStream_t s) {
   if (a.ent_fmt == CSA_BF16) launch_all_heads_e<WF, CSA_BF16>(a, nc, nu, part, s);
   else if (a.ent_fmt == CSA_FP8_MX32) launch_all_heads_e<WF, CSA_FP8_MX32>(a, nc, nu, part, s);
+  else if (a.ent_fmt == CSA_MIX576) launch_all_heads_e<WF, CSA_MIX576>(a, nc, nu, part, s);
   else launch_all_heads_e<WF, CSA_FP4_E4M3_16>(a, nc, nu, part, s);
 }
 

@@ -48,7 +48,8 @@ def oracle_sparse(qv, winv, entv, ids, sink, pos, mode="ring", base=0, n_rows=12
 
 
 @pytest.mark.parametrize("efmt,wfmt", [("bf16", "bf16"), ("fp8_mx32", "fp8_mx32"),
-                                       ("fp4_e4m3_16", "fp8_mx32"), ("bf16", "fp8_mx32")])
+                                       ("fp4_e4m3_16", "fp8_mx32"), ("bf16", "fp8_mx32"),
+                                       ("mix576", "fp8_mx32"), ("mix576", "bf16")])
 @pytest.mark.parametrize("k", [512, 37, 0])
 def test_csa_decode(tables, efmt, wfmt, k):
     cos, sin = tables
@@ -108,7 +109,8 @@ def test_csa_multi_query_linear_window_and_heads(tables):
             close_bf16(got[b, qq], ref)
 
 
-@pytest.mark.parametrize("k,efmt", [(512, "bf16"), (1300, "fp8_mx32"), (45, "fp4_e4m3_16")])
+@pytest.mark.parametrize("k,efmt", [(512, "bf16"), (1300, "fp8_mx32"), (45, "fp4_e4m3_16"),
+                                    (512, "mix576")])
 def test_csa_many_queries_long_chunks(tables, k, efmt):
     """16+ queries per sequence: a work-group takes up to 640 list rows (the
     whole window + top-512 list finishes without partials; longer lists are
@@ -175,7 +177,7 @@ def test_csa_many_queries_other_head_counts(tables, H, k):
         close_bf16(got[0, qq], ref)
 
 
-@pytest.mark.parametrize("efmt", ["bf16", "fp8_mx32", "fp4_e4m3_16"])
+@pytest.mark.parametrize("efmt", ["bf16", "fp8_mx32", "fp4_e4m3_16", "mix576"])
 def test_hca_decode(tables, efmt):
     cos, sin = tables
     B, H, N = 3, 64, 2500
