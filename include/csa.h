@@ -86,8 +86,8 @@ enum {
                            notes: 448 FP8 + 64 bf16 = 576 bytes before scales, FP8 in
                            blocks of 64), dim 512 only: 448 E4M3 codes (the FP8_MX32 rule
                            per block of 64), the 64 RoPE dims as bf16 (RNE), 7 E8M0
-                           scale bytes, 9 zero bytes: 592 B.  kv_quantize /
-                           kv_dequantize only.                                          */
+                           scale bytes, 9 zero bytes: 592 B.  Codec, compressor entries
+                           and attention entry rows.                                    */
 };
 
 /* Addressing of the raw sliding-window rows. */

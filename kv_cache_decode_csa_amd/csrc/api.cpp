@@ -158,9 +158,10 @@ static csa_status check_compress(const csa_compress_args* a) {
   REQUIRE(!a->rotate || a->head_dim == 128, CSA_EUNSUPPORTED, "rotate needs head_dim 128");
   REQUIRE(a->x_fmt == CSA_F32 || a->x_fmt == CSA_BF16, CSA_EUNSUPPORTED, "x_fmt must be F32 or BF16");
   REQUIRE(a->w_fmt == CSA_F32 || a->w_fmt == CSA_BF16, CSA_EUNSUPPORTED, "w_fmt must be F32 or BF16");
-  REQUIRE(row_fmt(a->entry_fmt) || (a->entry_fmt == CSA_FP4_MX32 && a->head_dim == 128),
-          CSA_EUNSUPPORTED, "entry_fmt must be F32, BF16, FP8_MX32, FP4_E4M3_16, or FP4_MX32 "
-          "for 128-d index keys");
+  REQUIRE(row_fmt(a->entry_fmt) || (a->entry_fmt == CSA_FP4_MX32 && a->head_dim == 128) ||
+              (a->entry_fmt == CSA_MIX576 && a->head_dim == 512),
+          CSA_EUNSUPPORTED, "entry_fmt must be F32, BF16, FP8_MX32, FP4_E4M3_16, FP4_MX32 "
+          "for 128-d index keys, or MIX576 for 512-d entries");
   REQUIRE(a->rope_rows >= 1, CSA_EINVAL, "rope_rows must be >= 1");
   REQUIRE(a->entries_cap >= 0, CSA_EINVAL, "entries_cap must be >= 0");
   REQUIRE(a->eps >= 0 && isfinite(a->eps), CSA_EINVAL, "eps must be finite and >= 0");

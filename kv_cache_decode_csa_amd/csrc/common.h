@@ -270,6 +270,26 @@ __device__ __forceinline__ uint32_t score_key(float s) {
 __device__ __forceinline__ void store_elem(int fmt, float v, int c, int d, bool live, uint8_t* row) {
   const float av = __builtin_fabsf(v);
   const bool fin = av <= 3.402823466e38f;
+  if (fmt == CSA_MIX576) {
+    // V4 mixed row (d = 512): a wave holds one block of 64 dims; blocks 0..6
+    // are FP8 with an E8M0 scale each, block 7 (dims 448..511) is bf16
+    if (c >= 448) {
+      if (live) ((uint16_t*)(row + 448))[c - 448] = f32_to_bf16(v);
+      if (live && c >= 504) row[583 + (c - 504)] = 0;  // bytes 583..591 stay zero
+      if (live && c == 511) row[591] = 0;
+      return;
+    }
+    float amax = fin ? av : 0.f;
+#pragma unroll
+    for (int m = 1; m < 64; m <<= 1) amax = fmaxf(amax, shfl_xor_f(amax, m));
+    const int e = mx32_exponent(amax);
+    const uint32_t code = f32_to_e4m3(ldexpf(v, -e));
+    const uint32_t c1 = __shfl_down(code, 1, 64), c2 = __shfl_down(code, 2, 64),
+                   c3 = __shfl_down(code, 3, 64);
+    if (live && (c & 3) == 0) *(uint32_t*)(row + c) = code | (c1 << 8) | (c2 << 16) | (c3 << 24);
+    if (live && (c & 63) == 0) row[576 + (c >> 6)] = (uint8_t)(e + 127);
+    return;
+  }
   if (fmt == CSA_FP8_MX32) {
     float amax = fin ? av : 0.f;
 #pragma unroll

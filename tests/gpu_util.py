@@ -128,6 +128,14 @@ def step_bound(ref, fmt, d):
         return 1e-5 + 1e-5 * np.abs(ref)
     if fmt == "bf16":
         return 1e-3 + 2.0 ** -7 * np.abs(ref)
+    if fmt == "mix576":  # FP8 blocks of 64 on dims 0..447, bf16 on 448..511
+        nope = ref[..., :448].reshape(ref.shape[:-1] + (7, 64))
+        amax = np.abs(nope).max(-1, keepdims=True)
+        # one E4M3 step at the element's own value (3 mantissa bits), or the
+        # block's subnormal spacing
+        step = np.maximum(np.abs(nope) * 2.0 ** -3, amax / 448 * 2.0 ** -3 * 2)
+        step = step.reshape(ref.shape[:-1] + (448,))
+        return np.concatenate([step + 1e-6, 1e-3 + 2.0 ** -7 * np.abs(ref[..., 448:])], axis=-1)
     g = 16 if fmt == "fp4_e4m3_16" else 32
     amax = np.abs(ref).reshape(ref.shape[:-1] + (d // g, g)).max(-1, keepdims=True)
     if fmt == "fp8_mx32":

@@ -104,7 +104,8 @@ def test_bulk_f32(tables, ratio, d, rotate):
 
 
 @pytest.mark.parametrize("ratio,d,rotate,entry_fmt", [(4, 512, 0, "bf16"), (4, 128, 1, "bf16"),
-                                                      (128, 512, 0, "fp8_mx32")])
+                                                      (128, 512, 0, "fp8_mx32"),
+                                                      (4, 512, 0, "mix576")])
 def test_bulk_bf16_tiled_projection(tables, ratio, d, rotate, entry_fmt):
     """Many-token bf16 calls (more than 64 rows) use the tiled MFMA
     projection: 2 x 333 tokens (a ragged last 128-row tile), then a second
@@ -139,7 +140,7 @@ def test_bulk_bf16_tiled_projection(tables, ratio, d, rotate, entry_fmt):
     ("f32", 512, 512, 0, 4), ("fp8_mx32", 4096, 512, 0, 4), ("fp8_mx32", 4096, 128, 1, 4),
     ("bf16", 4096, 128, 1, 4), ("fp4_mx32", 4096, 128, 1, 4),
     ("fp4_e4m3_16", 4096, 512, 0, 2), ("fp8_mx32", 4096, 128, 1, 2),
-    ("fp4_e4m3_16", 4096, 512, 0, 1)])
+    ("fp4_e4m3_16", 4096, 512, 0, 1), ("mix576", 4096, 512, 0, 4), ("mix576", 512, 512, 0, 2)])
 def test_decode_steps_bf16(tables, entry_fmt, dim, d, rotate, ratio):
     """Token-by-token calls from a state built by an earlier chunked call; each
     sequence sits at a different offset inside its block.  dim 4096 runs the
