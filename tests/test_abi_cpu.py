@@ -153,3 +153,56 @@ def test_rope_table_validation():
     assert L.csa_rope_table(160000.0, 16.0, 65536, 32.0, 1.0, 0, A16, A16, None) == EINVAL
     assert L.csa_rope_table(1.0, 0.0, 0, 0.0, 0.0, 10, A16, A16, None) == EINVAL
     assert L.csa_rope_table(160000.0, 16.0, 0, 32.0, 1.0, 10, A16, A16, None) == EINVAL
+
+
+def _layer_weights(**kw):
+    d = dict(dim=4096, q_rank=1024, H=64, Hi=64, groups=8, o_rank=1024)
+    d.update(kw)
+    return _lib.LayerWeights(d["dim"], d["q_rank"], d["H"], d["Hi"], d["groups"], d["o_rank"],
+                             A16, A16, A16, A16, A16, A16, A16, A16, A16, 1e-6)
+
+
+def test_layer_validation():
+    L = _lib.lib()
+    w = _layer_weights()
+    need = L.csa_layer_input_workspace_size(ctypes.byref(w), 8)
+    assert need > 0 and L.csa_layer_output_workspace_size(ctypes.byref(w), 8) > 0
+
+    def inp(w, B=8, T=1, win_fmt=2, ws=A16, wsb=1 << 30):
+        return L.csa_layer_input(ctypes.byref(w), A16, A16, B, T, A16, A16, 100, A16, A16, A16,
+                                 A16, win_fmt, ws, wsb, None)
+
+    assert inp(w, B=65) == EUNSUP                     # M = B*T above 64
+    assert inp(w, B=8, T=9) == EUNSUP
+    assert inp(w, win_fmt=4) == EUNSUP                # FP4_MX32 is not a window format
+    assert inp(w, ws=None) == EWS
+    assert inp(w, wsb=need - 1) == EWS
+    assert inp(_layer_weights(q_rank=3072)) == EINVAL  # q_rank above 2048
+    assert inp(_layer_weights(dim=1000)) == EINVAL
+    assert inp(_layer_weights(groups=7)) == EINVAL     # groups must divide H
+    assert inp(_layer_weights(Hi=65)) == EUNSUP
+    w0 = _layer_weights()
+    w0.wq_b = None
+    assert inp(w0) == EINVAL
+    assert L.csa_layer_output(ctypes.byref(w), A16, 8, A16, 2, A16, 1 << 30, None) == EUNSUP
+    assert L.csa_layer_output(ctypes.byref(_layer_weights(o_rank=48)), A16, 8, A16, 1, A16,
+                              1 << 30, None) == EINVAL
+
+
+def test_shared_attention_and_mixed_rows_validation():
+    L = _lib.lib()
+
+    def shared(B=12, ent_seqs=3, ef=2, qf=1):
+        return L.csa_sparse_attn_decode_shared(A16, qf, A16, 2, A16, ef, 1000, A16, 512, A16, B, 1,
+                                               64, ent_seqs, A16, 0.044, A16, A16, 100, A16, 1,
+                                               A16, 1 << 30, None)
+
+    assert shared(ent_seqs=5) == EINVAL               # must divide B
+    assert shared(ent_seqs=0) == EINVAL
+    assert shared(ef=4) == EUNSUP                     # FP4_MX32 is not an entry format
+    assert shared(ef=5, qf=0) == EUNSUP               # mixed rows need bf16 queries
+    assert L.kv_quantize(A16, 0, A16, 5, 4, 128, None) == EUNSUP   # mixed rows are 512-d
+    assert L.kv_dequantize(A16, 5, A16, 0, 4, 256, None) == EUNSUP
+    a = _lib.CompressArgs(1, 4, 1024, 4, 128, 1, A16, 0, A16, A16, 0, A16, A16, 1e-6, A16, A16,
+                          100, A16, A16, A16, A16, 5, 16)
+    assert L.csa_compress(ctypes.byref(a), A16, 1 << 20, None) == EUNSUP  # 128-d mixed rows
