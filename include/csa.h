@@ -315,8 +315,12 @@ csa_status hca_attn_decode(const void* q, int q_fmt, const void* win, int win_fm
  *
  * csa_layer_input ("DeepSeek-V4 deep dive" sections 3.2, 3.3, 3.4 notes, 5.2):
  *   qr = RMSNorm(wq_a x) * q_norm, rounded to bf16 (the shared query latent);
- *   q[m][h]  = RoPE_p(v_h / sqrt(mean(v_h^2) + eps)),  v = wq_b qr split into
- *              H heads of 512 (the per-head rescale has no weight);
+ *   q[m][h]  = v_h / sqrt(mean(v_h^2) + eps),  v = wq_b qr split into H heads
+ *              of 512 (the per-head rescale has no weight).  q is written
+ *              UN-rotated: the page's query is RoPE_p(q[m][h]), and the
+ *              attention calls (csa_sparse_attn_decode, hca_attn_decode) take
+ *              exactly this un-rotated q and rotate it at the query position
+ *              themselves, so the output feeds them directly;
  *   kv       = RoPE_p(RMSNorm(wkv x) * kv_norm), stored in win_fmt into row
  *              p mod 128 of sequence b's window ring win[b][128][row]
  *              (skipped for p < 0);

@@ -277,10 +277,11 @@ struct QArgs {
 };
 
 // One wave per (row, head).  Query heads: lane l holds dims 8l .. 8l+7, RMS
-// over the head, RoPE on dims 448..511 (lanes 56..63, pairs inside a lane).
-// Index heads: lane l holds dims l and l + 64; RoPE pairs across lanes l, l^1
-// of the upper half; Sylvester Hadamard butterflies (stride 64 in-lane, then
-// strides 32..1 across lanes) scaled by 128^-1/2.
+// over the head; they are written un-rotated, since the attention calls rotate
+// q at the query's position themselves.  Index heads: lane l holds dims l and
+// l + 64; RoPE pairs across lanes l, l^1 of the upper half; Sylvester Hadamard
+// butterflies (stride 64 in-lane, then strides 32..1 across lanes) scaled by
+// 128^-1/2.
 __global__ void __launch_bounds__(kThreads) layer_q_kernel(QArgs a) {
   const int m = blockIdx.x;
   const int lane = threadIdx.x & 63;
@@ -288,17 +289,7 @@ __global__ void __launch_bounds__(kThreads) layer_q_kernel(QArgs a) {
   if (head >= a.H + a.Hi) return;
   const int64_t stride = (int64_t)a.M * a.ldy;
   const float* row = a.part + (int64_t)m * a.ldy;
-  const int64_t rr = rope_row(a.pos[m], a.rope_rows);
   if (head < a.H) {
-    // rotation factors first (lanes 56..63 hold the rotated dims 448..511)
-    const bool rot = 8 * lane >= kHeadDim - kRopeDims;
-    float cs_[4], sn_[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int k = rot ? 4 * (lane - (kHeadDim - kRopeDims) / 8) + j : 0;
-      cs_[j] = a.rope_cos[rr * 32 + k];
-      sn_[j] = a.rope_sin[rr * 32 + k];
-    }
     float v[8];
     float ss = 0.f;
 #pragma unroll
@@ -307,23 +298,13 @@ __global__ void __launch_bounds__(kThreads) layer_q_kernel(QArgs a) {
       ss += v[j] * v[j];
     }
     const float inv = 1.0f / sqrtf(wave_sum(ss) / (float)kHeadDim + a.eps);
-#pragma unroll
-    for (int j = 0; j < 8; ++j) v[j] *= inv;
-    if (rot) {
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const float cs = cs_[j], sn = sn_[j];
-        const float x0 = v[2 * j], x1 = v[2 * j + 1];
-        v[2 * j] = x0 * cs - x1 * sn;
-        v[2 * j + 1] = x0 * sn + x1 * cs;
-      }
-    }
     u32x4_t o;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) o[j] = pack_bf16x2(v[2 * j], v[2 * j + 1]);
+    for (int j = 0; j < 4; ++j) o[j] = pack_bf16x2(v[2 * j] * inv, v[2 * j + 1] * inv);
     *(u32x4_t*)(a.q + ((int64_t)m * a.H + head) * kHeadDim + 8 * lane) = o;
     return;
   }
+  const int64_t rr = rope_row(a.pos[m], a.rope_rows);
   const int h = head - a.H;
   const int64_t base = (int64_t)a.H * kHeadDim + (int64_t)h * kIndexDim;
   const float cs = a.rope_cos[rr * 32 + (lane >> 1)], sn = a.rope_sin[rr * 32 + (lane >> 1)];

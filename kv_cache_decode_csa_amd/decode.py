@@ -159,9 +159,15 @@ class CsaDecodeLayer:
             self.sink_group = torch.cat([self.sink] + [r[1] for r in self.reuse])
             self.pos_group = self.pos.repeat(L, 1)
             self.out_group = torch.empty((L * B, 1, w.H, 512), dtype=qdt, device=device)
+            # the Full layer's buffers are views into the group's, so whatever
+            # writes them (csa_layer_input included) is what the group reads
+            self.q = self.q_group[:B]
+            self.win = self.win_group[:B]
             self.out = self.out_group[:B]
-            self.reuse = [(rq, rs, rw, self.out_group[(i + 1) * B:(i + 2) * B])
-                          for i, (rq, rs, rw, _) in enumerate(self.reuse)]
+            self.reuse = [(self.q_group[(i + 1) * B:(i + 2) * B], rs,
+                           self.win_group[(i + 1) * B:(i + 2) * B],
+                           self.out_group[(i + 1) * B:(i + 2) * B])
+                          for i, (_, rs, _, _) in enumerate(self.reuse)]
             self.ws_group = _lib.workspace(
                 _lib.csa_sparse_attn_workspace_size(L * B, 1, w.H, w.topk))
 

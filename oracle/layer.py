@@ -53,15 +53,20 @@ def latent(x, wq_a, q_norm, eps=1e-6):
     return _codec.round_to_bf16(rmsnorm(c, q_norm, eps))
 
 
-def queries(qr, wq_b, H, pos, omega, eps=1e-6):
-    """q [..., H, 512]: wq_b qr per head, each head divided by its own RMS
-    (no weight), then RoPE on the last 64 dims at pos (sections 3.2 steps 3-4,
-    3.3)."""
+def query_heads(qr, wq_b, H, eps=1e-6):
+    """q [..., H, 512] before RoPE: wq_b qr per head, each head divided by its
+    own RMS, no weight (section 3.2 steps 3-4).  This is the form the
+    attention step takes: it rotates the query at its own position."""
     q = np.asarray(qr, dtype=np.float64) @ np.asarray(wq_b, dtype=np.float64).T
     q = q.reshape(q.shape[:-1] + (H, HEAD_DIM))
-    q = rmsnorm(q, 1.0, eps)
+    return rmsnorm(q, 1.0, eps)
+
+
+def queries(qr, wq_b, H, pos, omega, eps=1e-6):
+    """q [..., H, 512]: the query heads with RoPE on the last 64 dims at pos
+    (sections 3.2 steps 3-4, 3.3)."""
     p = np.asarray(pos)[..., None]
-    return _rope.rotate(q, p, omega)
+    return _rope.rotate(query_heads(qr, wq_b, H, eps), p, omega)
 
 
 def index_queries(qr, wq_b_idx, Hi, pos, omega):
@@ -130,11 +135,16 @@ def param_counts(dim, q_rank, H, groups, o_rank, Hi=0):
     }
 
 
-def layer_input(x, pos, wts, omega, eps=1e-6):
+def layer_input(x, pos, wts, omega, eps=1e-6, rotate_q=True):
     """Everything a decode step needs from the token's hidden state x:
-    (q, q_idx or None, w_idx or None, window entry before storage rounding)."""
+    (q, q_idx or None, w_idx or None, window entry before storage rounding).
+    q is the page's rotated query; with rotate_q=False it is the query heads
+    before RoPE, the form the attention step takes."""
     qr = latent(x, wts["wq_a"], wts["q_norm"], eps)
-    q = queries(qr, wts["wq_b"], wts["H"], pos, omega, eps)
+    if rotate_q:
+        q = queries(qr, wts["wq_b"], wts["H"], pos, omega, eps)
+    else:
+        q = query_heads(qr, wts["wq_b"], wts["H"], eps)
     kv = window_entry(x, wts["wkv"], wts["kv_norm"], pos, omega, eps)
     if wts.get("Hi", 0):
         qi = index_queries(qr, wts["wq_b_idx"], wts["Hi"], pos, omega)

@@ -68,8 +68,9 @@ def run_input(seed, B, T, dim, q_rank, H, Hi, win_fmt, pos_list):
 
     wts = dict(wn, H=H, Hi=Hi)
     pq = np.maximum(pos, 0)  # positions are clamped to the table
-    q_ref, qi_ref, wi_ref, kv_ref = OL.layer_input(x.astype(np.float64), pq, wts, OMEGA)
-    close_bf16(to_np(q), q_ref)
+    q_ref, qi_ref, wi_ref, kv_ref = OL.layer_input(x.astype(np.float64), pq, wts, OMEGA,
+                                                  rotate_q=False)
+    close_bf16(to_np(q), q_ref)  # un-rotated: the attention call rotates q itself
     if Hi:
         close_bf16(to_np(qi), qi_ref)
         terms = np.abs(x.astype(np.float64)) @ np.abs(wn["w_proj"].astype(np.float64)).T
@@ -211,7 +212,8 @@ def test_layer_flash_full_size():
     _lib.csa_layer_output(LW, bf16(o), B, y, "bf16", wso)
     torch.cuda.synchronize()
     wts = dict(wn, H=H, Hi=Hi)
-    q_ref, qi_ref, wi_ref, kv_ref = OL.layer_input(x.astype(np.float64), pos, wts, OMEGA)
+    q_ref, qi_ref, wi_ref, kv_ref = OL.layer_input(x.astype(np.float64), pos, wts, OMEGA,
+                                                  rotate_q=False)
     close_bf16(to_np(q), q_ref)
     close_bf16(to_np(qi), qi_ref)
     terms = np.abs(x.astype(np.float64)) @ np.abs(wn["w_proj"].astype(np.float64)).T
