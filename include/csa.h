@@ -238,6 +238,24 @@ csa_status csa_index_topk_bf16(const void* q_idx, int q_fmt, const float* w_idx,
                                float* out_scores, void* ws, size_t ws_bytes,
                                csa_stream_t stream);
 
+/* csa_index_topk for callers that cannot allocate device memory (code under
+ * graph capture, tight serving loops, harnesses that forbid allocation): the
+ * same arguments, results and errors without the workspace.  Its scratch is a
+ * fixed 32 MiB array inside the library, one per device, held until the
+ * process ends; csa_index_topk_workspace_size(B, Q, Nmax, topk) must not
+ * exceed 32 MiB (8 sequences of 262,144 entries need 9.2 MB), else the call
+ * returns CSA_EWORKSPACE before enqueuing anything.  The call makes no
+ * allocation of any kind.  Its first call on a device resolves that device's
+ * scratch address (hipGetSymbolAddress), so make one call before capturing a
+ * graph.  Every call on a device shares that device's scratch: calls that
+ * overlap on one device (different streams, or different threads) race and
+ * must be serialised by the caller.  The scratch keeps the last call's
+ * contents; the call clears what it needs itself.                          */
+csa_status csa_index_topk_noalloc(const void* q_idx, int q_fmt, const float* w_idx,
+                                  const void* k_idx, int k_fmt, const int32_t* pos, int ratio,
+                                  int B, int Q, int Hi, int64_t Nmax, int topk, int32_t* out_idx,
+                                  float* out_scores, csa_stream_t stream);
+
 /* Top-k alone over given float32 scores [R][ld]: row r ranks its first
  * n_valid[r] entries (clamped to [0, ld]) with the same order rule as above.
  * Requirements: 1 <= topk <= 2048, ld >= 1.                                  */

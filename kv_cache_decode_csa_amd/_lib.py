@@ -74,6 +74,8 @@ _SIGS = {
                             _SZ, _VP]),
     "csa_index_topk_bf16": (_I, [_VP, _I, _VP, _VP, _I, _VP, _I, _I, _I, _I, _I64, _I, _VP, _VP,
                                  _VP, _SZ, _VP]),
+    "csa_index_topk_noalloc": (_I, [_VP, _I, _VP, _VP, _I, _VP, _I, _I, _I, _I, _I64, _I, _VP,
+                                    _VP, _VP]),
     "csa_topk_workspace_size": (_SZ, [_I64, _I64, _I]),
     "csa_topk": (_I, [_VP, _VP, _I64, _I64, _I, _VP, _VP, _SZ, _VP]),
     "csa_sparse_attn_workspace_size": (_SZ, [_I, _I, _I, _I]),
@@ -224,6 +226,15 @@ def csa_index_topk_bf16(q_idx, q_fmt, w_idx, k_idx, k_fmt, pos, ratio, B, Q, Hi,
                                      int(Nmax), int(topk), _ptr(out_idx), _ptr(out_scores),
                                      _ptr(ws), ws.numel() if ws is not None else 0,
                                      _stream(stream)), "csa_index_topk_bf16")
+
+
+def csa_index_topk_noalloc(q_idx, q_fmt, w_idx, k_idx, k_fmt, pos, ratio, B, Q, Hi, Nmax, topk,
+                           out_idx, out_scores, stream=None):
+    _check(lib().csa_index_topk_noalloc(_ptr(q_idx), _fmt(q_fmt), _ptr(w_idx), _ptr(k_idx),
+                                        _fmt(k_fmt), _ptr(pos), int(ratio), int(B), int(Q),
+                                        int(Hi), int(Nmax), int(topk), _ptr(out_idx),
+                                        _ptr(out_scores), _stream(stream)),
+           "csa_index_topk_noalloc")
 
 
 def csa_topk_workspace_size(R, ld, topk):

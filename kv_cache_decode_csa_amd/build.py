@@ -18,7 +18,8 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libcsa.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-SOURCES = ["api.cpp", "codec.hip", "topk.hip", "indexer.hip", "attention.hip", "compress.hip", "layer.hip"]
+SOURCES = ["api.cpp", "codec.hip", "topk.hip", "indexer.hip", "attention.hip", "compress.hip", "layer.hip",
+           "noalloc.hip"]
 
 COMMON = ["-O3", "-std=c++17", "-fPIC", "--offload-arch=gfx950",
           # packed FP32 instructions stay off: only ordinary scalar float code

@@ -49,6 +49,16 @@ bool row_fmt(int f) { return f >= CSA_F32 && f <= CSA_FP4_E4M3_16; }
 
 }  // namespace
 
+namespace csa {
+csa_status set_error(csa_status code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_detail, sizeof(g_detail), fmt, ap);
+  va_end(ap);
+  return code;
+}
+}  // namespace csa
+
 extern "C" {
 
 const char* csa_strerror(csa_status s) {

@@ -20,6 +20,9 @@ constexpr int kCandCap = 8192;    // boundary-bin candidates kept per row
 
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
+// Sets the calling thread's error detail (csa_last_error_detail) and returns code.
+csa_status set_error(csa_status code, const char* fmt, ...);
+
 // ---- launchers (kernel files); each returns hipSuccess or the launch error
 hipError_t launch_rope_table(const double* omega_host, int64_t rows, float* cos_out,
                              float* sin_out, hipStream_t s);

@@ -206,3 +206,14 @@ def test_shared_attention_and_mixed_rows_validation():
     a = _lib.CompressArgs(1, 4, 1024, 4, 128, 1, A16, 0, A16, A16, 0, A16, A16, 1e-6, A16, A16,
                           100, A16, A16, A16, A16, 5, 16)
     assert L.csa_compress(ctypes.byref(a), A16, 1 << 20, None) == EUNSUP  # 128-d mixed rows
+
+
+def test_index_topk_noalloc_rejects_oversize_on_host():
+    """The fixed-scratch index call refuses a shape whose workspace exceeds its
+    32 MiB before any device call."""
+    L = _lib.lib()
+    B, N, Hi, k = 64, 262144, 64, 512
+    assert L.csa_index_topk_workspace_size(B, 1, N, k) > 32 << 20
+    r = L.csa_index_topk_noalloc(A16, _lib.BF16, A16, A16, _lib.FP8_MX32, A16, 4, B, 1, Hi, N, k,
+                                 A16, None, None)
+    assert r == EWS and "scratch" in _detail()
