@@ -184,6 +184,23 @@ typedef struct {
   void* entries;
   int entry_fmt;
   int64_t entries_cap;
+  /* Block cache (optional; all zero = the contiguous layout above; see
+   * csa_block_table below).  When block_table is set, `entries` is a pool of
+   * pool_blocks blocks of block_entries rows, entry i of sequence b is
+   * written to row i mod block_entries of block block_table[b][i /
+   * block_entries], and entries_cap is replaced by max_blocks *
+   * block_entries; an entry whose block id is -1 or outside [0, pool_blocks)
+   * is not written.  When state_slot is set, kv_state and score_state are
+   * pools of state_slots slots and sequence b uses slot state_slot[b]; a
+   * sequence whose slot lies outside [0, state_slots) is skipped (nothing
+   * read or written for it).  Two sequences of one call must not share a
+   * slot (the caller's guarantee). */
+  const int32_t* block_table;
+  int64_t max_blocks;
+  int block_entries;
+  int64_t pool_blocks;
+  const int32_t* state_slot;
+  int64_t state_slots;
 } csa_compress_args;
 
 size_t csa_compress_workspace_size(const csa_compress_args* a);
@@ -326,6 +343,74 @@ csa_status hca_attn_decode(const void* q, int q_fmt, const void* win, int win_fm
                            int H, const float* sink, float scale, const float* rope_cos,
                            const float* rope_sin, int64_t rope_rows, void* out, int out_fmt,
                            void* ws, size_t ws_bytes, csa_stream_t stream);
+
+/* ------------------------------------------------------------------------ block cache
+ * The serving layout of "DeepSeek-V4 deep dive" section 9.4: compressed
+ * entries (and, for CSA, their index keys) live in a pool of fixed-size
+ * blocks, each covering a multiple of 128 tokens -- 32 CSA entries or 1 HCA
+ * entry per 128 tokens -- found through a per-sequence block table; what is
+ * still in motion (the 128-row window ring and the compressors' slot state)
+ * lives in one fixed-size state slot per request, drawn from a pool.
+ * Logical entry e of sequence b is row e mod block_entries of pool block
+ * table[b][e / block_entries]; the logical capacity is Nmax = max_blocks *
+ * block_entries.  A pool is [pool_blocks][block_entries][row bytes].
+ * The paged calls compute exactly what their contiguous counterparts compute
+ * on the gathered rows, in the same order: their results are bit-identical
+ * to the contiguous calls' on the same logical data.                      */
+typedef struct {
+  const int32_t* table;   /* [B][max_blocks] int32 (device): the pool block of each
+                             logical block of each sequence; -1 = not allocated   */
+  int64_t max_blocks;     /* length of a table row, >= 1                           */
+  int block_entries;      /* entries per block: a power of two in [1, 1024]; index
+                             keys need >= 32 (one 128-token CSA block)             */
+  int64_t pool_blocks;    /* blocks in the pool, >= 1                              */
+} csa_block_table;
+
+/* csa_index_topk (bf16_scores = 0) or csa_index_topk_bf16 (bf16_scores = 1)
+ * over index keys held in a block pool: k_pool [pool_blocks][block_entries]
+ * rows of 128 values in k_fmt, found through kt (kt->block_entries >= 32).
+ * Nmax = kt->max_blocks * kt->block_entries; out_idx holds logical entry ids,
+ * out_scores (nullable) is [B][Q][Nmax].  A visible key whose block id is -1
+ * or outside [0, pool_blocks) is read as a zero key (score 0); nothing
+ * outside the pool is read.  Workspace: csa_index_topk_workspace_size(B, Q,
+ * Nmax, topk).  Errors as for csa_index_topk, and CSA_EINVAL for a bad
+ * table descriptor.  With 12 or more bf16-key queries per sequence the scan
+ * runs the per-query kernel (bit-identical to the query-tiled one).        */
+csa_status csa_index_topk_paged(const void* q_idx, int q_fmt, const float* w_idx,
+                                const void* k_pool, int k_fmt, const csa_block_table* kt,
+                                const int32_t* pos, int ratio, int B, int Q, int Hi, int topk,
+                                int bf16_scores, int32_t* out_idx, float* out_scores, void* ws,
+                                size_t ws_bytes, csa_stream_t stream);
+
+/* csa_sparse_attn_decode (ring window) and hca_attn_decode over a block pool
+ * and state slots: sequence b's 128-row window ring is win_pool[win_slot[b]]
+ * (win_pool: [win_slots][128] rows; win_slot NULL means slot b, and then
+ * win_slots must be >= B), and its entries are ent_pool rows found through
+ * et (Nmax = et->max_blocks * et->block_entries).  A slot outside
+ * [0, win_slots) leaves the sequence without window rows.  A list id (CSA)
+ * or visible entry (HCA) whose block id is -1 or outside [0, pool_blocks) is
+ * absent, like an id outside [0, Nmax).  Entry pools hold at most 2^31 - 1
+ * rows (pool_blocks * block_entries).
+ * Workspace: csa_sparse_attn_workspace_size(B, Q, H, topk) and
+ * hca_attn_workspace_size(B, Q, H, Nmax).  Errors as for the contiguous
+ * calls, and CSA_EINVAL for a bad table descriptor.                       */
+csa_status csa_sparse_attn_decode_paged(const void* q, int q_fmt, const void* win_pool,
+                                        int win_fmt, const int32_t* win_slot,
+                                        int64_t win_slots, const void* ent_pool, int ent_fmt,
+                                        const csa_block_table* et, const int32_t* topk_idx,
+                                        int topk, const int32_t* pos, int B, int Q, int H,
+                                        const float* sink, float scale, const float* rope_cos,
+                                        const float* rope_sin, int64_t rope_rows, void* out,
+                                        int out_fmt, void* ws, size_t ws_bytes,
+                                        csa_stream_t stream);
+csa_status hca_attn_decode_paged(const void* q, int q_fmt, const void* win_pool, int win_fmt,
+                                 const int32_t* win_slot, int64_t win_slots,
+                                 const void* ent_pool, int ent_fmt,
+                                 const csa_block_table* et, int ratio, const int32_t* pos, int B,
+                                 int Q, int H, const float* sink, float scale,
+                                 const float* rope_cos, const float* rope_sin, int64_t rope_rows,
+                                 void* out, int out_fmt, void* ws, size_t ws_bytes,
+                                 csa_stream_t stream);
 
 /* ------------------------------------------------------------------------ layer input / output
  * The attention layer's steps on either side of the decode path, for M = B*T

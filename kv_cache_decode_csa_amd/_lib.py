@@ -41,6 +41,16 @@ class CompressArgs(ctypes.Structure):
         ("start_pos", ctypes.c_void_p), ("kv_state", ctypes.c_void_p),
         ("score_state", ctypes.c_void_p), ("entries", ctypes.c_void_p),
         ("entry_fmt", ctypes.c_int), ("entries_cap", ctypes.c_int64),
+        ("block_table", ctypes.c_void_p), ("max_blocks", ctypes.c_int64),
+        ("block_entries", ctypes.c_int), ("pool_blocks", ctypes.c_int64),
+        ("state_slot", ctypes.c_void_p), ("state_slots", ctypes.c_int64),
+    ]
+
+
+class BlockTable(ctypes.Structure):
+    _fields_ = [
+        ("table", ctypes.c_void_p), ("max_blocks", ctypes.c_int64),
+        ("block_entries", ctypes.c_int), ("pool_blocks", ctypes.c_int64),
     ]
 
 
@@ -87,6 +97,14 @@ _SIGS = {
     "hca_attn_workspace_size": (_SZ, [_I, _I, _I, _I64]),
     "hca_attn_decode": (_I, [_VP, _I, _VP, _I, _I, _VP, _I64, _VP, _I, _I64, _I, _VP, _I, _I, _I,
                              _VP, _F, _VP, _VP, _I64, _VP, _I, _VP, _SZ, _VP]),
+    "csa_index_topk_paged": (_I, [_VP, _I, _VP, _VP, _I, ctypes.POINTER(BlockTable), _VP, _I, _I,
+                                  _I, _I, _I, _I, _VP, _VP, _VP, _SZ, _VP]),
+    "csa_sparse_attn_decode_paged": (_I, [_VP, _I, _VP, _I, _VP, _I64, _VP, _I,
+                                          ctypes.POINTER(BlockTable), _VP, _I, _VP, _I, _I, _I,
+                                          _VP, _F, _VP, _VP, _I64, _VP, _I, _VP, _SZ, _VP]),
+    "hca_attn_decode_paged": (_I, [_VP, _I, _VP, _I, _VP, _I64, _VP, _I,
+                                   ctypes.POINTER(BlockTable), _I, _VP, _I, _I, _I, _VP, _F, _VP,
+                                   _VP, _I64, _VP, _I, _VP, _SZ, _VP]),
     "csa_layer_input_workspace_size": (_SZ, [ctypes.POINTER(LayerWeights), _I]),
     "csa_layer_input": (_I, [ctypes.POINTER(LayerWeights), _VP, _VP, _I, _I, _VP, _VP, _I64, _VP,
                              _VP, _VP, _VP, _I, _VP, _SZ, _VP]),
@@ -170,12 +188,26 @@ def kv_dequantize(src, src_fmt, dst, dst_fmt, rows, dim, stream=None):
 
 def make_compress_args(*, B, T, dim, ratio, head_dim, rotate, x, x_fmt, w_kv, w_gate, w_fmt,
                        ape, norm_w, eps, rope_cos, rope_sin, start_pos, kv_state, score_state,
-                       entries, entry_fmt, entries_cap):
+                       entries, entry_fmt, entries_cap=0, block_table=None, block_entries=0,
+                       pool_blocks=0, state_slot=None):
+    """block_table ([B, max_blocks] int32) makes `entries` a pool of
+    pool_blocks blocks of block_entries rows; state_slot ([B] int32) makes
+    kv_state / score_state pools of slots (their first dimension)."""
     return CompressArgs(int(B), int(T), int(dim), int(ratio), int(head_dim), int(rotate),
                         _ptr(x), _fmt(x_fmt), _ptr(w_kv), _ptr(w_gate), _fmt(w_fmt), _ptr(ape),
                         _ptr(norm_w), float(eps), _ptr(rope_cos), _ptr(rope_sin),
                         int(rope_cos.shape[0]), _ptr(start_pos), _ptr(kv_state),
-                        _ptr(score_state), _ptr(entries), _fmt(entry_fmt), int(entries_cap))
+                        _ptr(score_state), _ptr(entries), _fmt(entry_fmt), int(entries_cap),
+                        _ptr(block_table),
+                        int(block_table.shape[1]) if block_table is not None else 0,
+                        int(block_entries), int(pool_blocks), _ptr(state_slot),
+                        int(kv_state.shape[0]) if state_slot is not None else 0)
+
+
+def make_block_table(table, block_entries, pool_blocks):
+    """csa_block_table over a [B, max_blocks] int32 device tensor (kept alive
+    by the caller while the struct is in use)."""
+    return BlockTable(_ptr(table), int(table.shape[1]), int(block_entries), int(pool_blocks))
 
 
 def csa_compress_workspace_size(args):
@@ -271,6 +303,38 @@ def csa_sparse_attn_decode_shared(q, q_fmt, win, win_fmt, entries, ent_fmt, Nmax
         float(scale), _ptr(rope_cos), _ptr(rope_sin), int(rope_cos.shape[0]), _ptr(out),
         _fmt(out_fmt), _ptr(ws), ws.numel() if ws is not None else 0, _stream(stream)),
         "csa_sparse_attn_decode_shared")
+
+
+def csa_index_topk_paged(q_idx, q_fmt, w_idx, k_pool, k_fmt, kt, pos, ratio, B, Q, Hi, topk,
+                         bf16_scores, out_idx, out_scores, ws, stream=None):
+    _check(lib().csa_index_topk_paged(_ptr(q_idx), _fmt(q_fmt), _ptr(w_idx), _ptr(k_pool),
+                                      _fmt(k_fmt), ctypes.byref(kt), _ptr(pos), int(ratio),
+                                      int(B), int(Q), int(Hi), int(topk), int(bf16_scores),
+                                      _ptr(out_idx), _ptr(out_scores), _ptr(ws),
+                                      ws.numel() if ws is not None else 0, _stream(stream)),
+           "csa_index_topk_paged")
+
+
+def csa_sparse_attn_decode_paged(q, q_fmt, win_pool, win_fmt, win_slot, win_slots, ent_pool,
+                                 ent_fmt, et, topk_idx, topk, pos, B, Q, H, sink, scale, rope_cos,
+                                 rope_sin, out, out_fmt, ws, stream=None):
+    _check(lib().csa_sparse_attn_decode_paged(
+        _ptr(q), _fmt(q_fmt), _ptr(win_pool), _fmt(win_fmt), _ptr(win_slot), int(win_slots),
+        _ptr(ent_pool), _fmt(ent_fmt), ctypes.byref(et), _ptr(topk_idx), int(topk), _ptr(pos),
+        int(B), int(Q), int(H), _ptr(sink), float(scale), _ptr(rope_cos), _ptr(rope_sin),
+        int(rope_cos.shape[0]), _ptr(out), _fmt(out_fmt), _ptr(ws),
+        ws.numel() if ws is not None else 0, _stream(stream)), "csa_sparse_attn_decode_paged")
+
+
+def hca_attn_decode_paged(q, q_fmt, win_pool, win_fmt, win_slot, win_slots, ent_pool, ent_fmt, et,
+                          ratio, pos, B, Q, H, sink, scale, rope_cos, rope_sin, out, out_fmt, ws,
+                          stream=None):
+    _check(lib().hca_attn_decode_paged(
+        _ptr(q), _fmt(q_fmt), _ptr(win_pool), _fmt(win_fmt), _ptr(win_slot), int(win_slots),
+        _ptr(ent_pool), _fmt(ent_fmt), ctypes.byref(et), int(ratio), _ptr(pos), int(B), int(Q),
+        int(H), _ptr(sink), float(scale), _ptr(rope_cos), _ptr(rope_sin), int(rope_cos.shape[0]),
+        _ptr(out), _fmt(out_fmt), _ptr(ws), ws.numel() if ws is not None else 0, _stream(stream)),
+        "hca_attn_decode_paged")
 
 
 def hca_attn_workspace_size(B, Q, H, Nmax):

@@ -157,6 +157,32 @@ csa_status kv_dequantize(const void* src, int src_fmt, void* dst, int dst_fmt, i
                   "kv_dequantize");
 }
 
+// ---------------------------------------------------------------- block cache
+// Validates a block-table descriptor (entries per block a power of two in
+// [min_entries, 1024]) and turns it into the kernels' PageMap.
+static csa_status page_map(const int32_t* table, int64_t max_blocks, int block_entries,
+                           int64_t pool_blocks, int min_entries, PageMap* out) {
+  REQUIRE_PTR(table);
+  REQUIRE(max_blocks >= 1, CSA_EINVAL, "max_blocks must be >= 1");
+  REQUIRE(pool_blocks >= 1 && pool_blocks <= INT32_MAX, CSA_EINVAL,
+          "pool_blocks must be in [1, 2^31 - 1]");
+  REQUIRE(block_entries >= min_entries && block_entries <= 1024 &&
+              (block_entries & (block_entries - 1)) == 0,
+          CSA_EINVAL, "block_entries must be a power of two in [%d, 1024] (got %d)", min_entries,
+          block_entries);
+  REQUIRE(max_blocks <= ((int64_t)1 << 30) / block_entries, CSA_EINVAL,
+          "max_blocks * block_entries must be <= 2^30");
+  int shift = 0;
+  while ((1 << shift) < block_entries) ++shift;
+  *out = PageMap{table, max_blocks, pool_blocks, shift};
+  return CSA_OK;
+}
+
+static csa_status page_map(const csa_block_table* t, int min_entries, PageMap* out) {
+  REQUIRE(t != nullptr, CSA_EINVAL, "block table descriptor must not be null");
+  return page_map(t->table, t->max_blocks, t->block_entries, t->pool_blocks, min_entries, out);
+}
+
 // ---------------------------------------------------------------- compressor
 static csa_status check_compress(const csa_compress_args* a) {
   REQUIRE(a != nullptr, CSA_EINVAL, "args must not be null");
@@ -185,7 +211,20 @@ static csa_status check_compress(const csa_compress_args* a) {
   REQUIRE_PTR(a->start_pos);
   REQUIRE_PTR(a->kv_state);
   REQUIRE_PTR(a->score_state);
-  if (a->entries_cap > 0) REQUIRE_PTR(a->entries);
+  if (a->block_table) {
+    PageMap pm;
+    csa_status st = page_map(a->block_table, a->max_blocks, a->block_entries, a->pool_blocks, 1,
+                             &pm);
+    if (st != CSA_OK) return st;
+    REQUIRE_PTR(a->entries);
+  } else if (a->entries_cap > 0) {
+    REQUIRE_PTR(a->entries);
+  }
+  if (a->state_slot) {
+    REQUIRE_PTR(a->state_slot);
+    REQUIRE(a->state_slots >= 1 && a->state_slots <= INT32_MAX, CSA_EINVAL,
+            "state_slots must be in [1, 2^31 - 1]");
+  }
   return CSA_OK;
 }
 
@@ -265,7 +304,8 @@ size_t csa_index_topk_workspace_size(int B, int Q, int64_t Nmax, int topk) {
 static csa_status index_topk(const void* q_idx, int q_fmt, const float* w_idx, const void* k_idx,
                           int k_fmt, const int32_t* pos, int ratio, int B, int Q, int Hi,
                           int64_t Nmax, int topk, int32_t* out_idx, float* out_scores, void* ws,
-                          size_t ws_bytes, csa_stream_t stream, int bf16_scores) {
+                          size_t ws_bytes, csa_stream_t stream, int bf16_scores,
+                          PageMap pm = PageMap{nullptr, 0, 0, 0}) {
   REQUIRE(B >= 1 && Q >= 1, CSA_EINVAL, "B and Q must be >= 1");
   REQUIRE(Nmax >= 1 && Nmax <= (int64_t)1 << 30, CSA_EINVAL, "Nmax must be in [1, 2^30]");
   REQUIRE(ratio >= 1, CSA_EINVAL, "ratio must be >= 1");
@@ -300,7 +340,7 @@ static csa_status index_topk(const void* q_idx, int q_fmt, const float* w_idx, c
   hipError_t e = launch_topk_clear(w, R, s);
   if (e == hipSuccess)
     e = launch_index_scores(q_idx, q_fmt, w_idx, k_idx, k_fmt, pos, ratio, B, Q, Hi, Nmax,
-                            scores, nvis, w, bf16_scores, s);
+                            scores, nvis, w, bf16_scores, s, pm);
   if (e == hipSuccess) e = launch_topk_select(scores, nvis, R, Nmax, topk, out_idx, w, s);
   return launched(e, "csa_index_topk");
 }
@@ -320,6 +360,20 @@ csa_status csa_index_topk_bf16(const void* q_idx, int q_fmt, const float* w_idx,
                                csa_stream_t stream) {
   return index_topk(q_idx, q_fmt, w_idx, k_idx, k_fmt, pos, ratio, B, Q, Hi, Nmax, topk, out_idx,
                     out_scores, ws, ws_bytes, stream, 1);
+}
+
+csa_status csa_index_topk_paged(const void* q_idx, int q_fmt, const float* w_idx,
+                                const void* k_pool, int k_fmt, const csa_block_table* kt,
+                                const int32_t* pos, int ratio, int B, int Q, int Hi, int topk,
+                                int bf16_scores, int32_t* out_idx, float* out_scores, void* ws,
+                                size_t ws_bytes, csa_stream_t stream) {
+  PageMap pm;
+  csa_status st = page_map(kt, 32, &pm);
+  if (st != CSA_OK) return st;
+  REQUIRE(bf16_scores == 0 || bf16_scores == 1, CSA_EINVAL, "bf16_scores must be 0 or 1");
+  return index_topk(q_idx, q_fmt, w_idx, k_pool, k_fmt, pos, ratio, B, Q, Hi,
+                    kt->max_blocks * kt->block_entries, topk, out_idx, out_scores, ws, ws_bytes,
+                    stream, bf16_scores, pm);
 }
 
 // ---------------------------------------------------------------- attention
@@ -450,6 +504,65 @@ csa_status hca_attn_decode(const void* q, int q_fmt, const void* win, int win_fm
   AttnArgs a = make_attn(q, q_fmt, win, win_fmt, win_mode, win_base, win_rows, entries, ent_fmt,
                          Nmax, pos, B, Q, H, sink, scale, rope_cos, rope_sin, rope_rows, out,
                          out_fmt);
+  a.dense = 1;
+  a.ratio = ratio;
+  return run_attn(a, ws, ws_bytes, (hipStream_t)stream);
+}
+
+// Block-cache variants: the contiguous calls with entries through a block
+// table and the ring window of sequence b in state slot win_slot[b].
+static csa_status paged_attn(AttnArgs& a, const int32_t* win_slot, int64_t win_slots,
+                             const csa_block_table* et) {
+  csa_status st = page_map(et, 1, &a.ent_pages);
+  if (st != CSA_OK) return st;
+  REQUIRE(et->pool_blocks * et->block_entries <= INT32_MAX, CSA_EINVAL,
+          "an entry pool holds at most 2^31 - 1 rows");
+  REQUIRE(win_slots >= 1 && win_slots <= INT32_MAX, CSA_EINVAL, "win_slots must be in [1, 2^31 - 1]");
+  REQUIRE(win_slot != nullptr || win_slots >= a.B, CSA_EINVAL,
+          "without win_slot the window pool needs win_slots >= B");
+  if (win_slot) REQUIRE_PTR(win_slot);
+  a.win_slot = win_slot;
+  a.win_slots = win_slot ? win_slots : a.B;
+  a.Nmax = et->max_blocks * et->block_entries;
+  return CSA_OK;
+}
+
+csa_status csa_sparse_attn_decode_paged(const void* q, int q_fmt, const void* win_pool,
+                                        int win_fmt, const int32_t* win_slot,
+                                        int64_t win_slots, const void* ent_pool, int ent_fmt,
+                                        const csa_block_table* et, const int32_t* topk_idx,
+                                        int topk, const int32_t* pos, int B, int Q, int H,
+                                        const float* sink, float scale, const float* rope_cos,
+                                        const float* rope_sin, int64_t rope_rows, void* out,
+                                        int out_fmt, void* ws, size_t ws_bytes,
+                                        csa_stream_t stream) {
+  REQUIRE(topk >= 0 && topk <= 8192, CSA_EUNSUPPORTED, "topk must be in [0, 8192]");
+  if (topk > 0) REQUIRE_PTR(topk_idx);
+  AttnArgs a = make_attn(q, q_fmt, win_pool, win_fmt, CSA_WIN_RING128, nullptr, kWindow,
+                         ent_pool, ent_fmt, 0, pos, B, Q, H, sink, scale, rope_cos, rope_sin,
+                         rope_rows, out, out_fmt);
+  csa_status st = paged_attn(a, win_slot, win_slots, et);
+  if (st != CSA_OK) return st;
+  a.dense = 0;
+  a.topk_idx = topk_idx;
+  a.topk = topk;
+  a.ratio = 4;
+  return run_attn(a, ws, ws_bytes, (hipStream_t)stream);
+}
+
+csa_status hca_attn_decode_paged(const void* q, int q_fmt, const void* win_pool, int win_fmt,
+                                 const int32_t* win_slot, int64_t win_slots,
+                                 const void* ent_pool, int ent_fmt, const csa_block_table* et,
+                                 int ratio, const int32_t* pos, int B, int Q, int H,
+                                 const float* sink, float scale, const float* rope_cos,
+                                 const float* rope_sin, int64_t rope_rows, void* out,
+                                 int out_fmt, void* ws, size_t ws_bytes, csa_stream_t stream) {
+  REQUIRE(ratio >= 1, CSA_EINVAL, "ratio must be >= 1");
+  AttnArgs a = make_attn(q, q_fmt, win_pool, win_fmt, CSA_WIN_RING128, nullptr, kWindow,
+                         ent_pool, ent_fmt, 0, pos, B, Q, H, sink, scale, rope_cos, rope_sin,
+                         rope_rows, out, out_fmt);
+  csa_status st = paged_attn(a, win_slot, win_slots, et);
+  if (st != CSA_OK) return st;
   a.dense = 1;
   a.ratio = ratio;
   return run_attn(a, ws, ws_bytes, (hipStream_t)stream);

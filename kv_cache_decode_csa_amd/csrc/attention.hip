@@ -46,14 +46,35 @@ struct RowRef {
   int fmt;
 };
 
-// Resolve logical list row j of unit (b, t).
-__device__ __forceinline__ RowRef resolve_row(const AttnArgs& a, int64_t unit, int64_t b, int t,
-                                              int64_t j, int64_t nvis, size_t win_rb,
-                                              size_t ent_rb) {
+// The window of sequence b: b itself, or its state slot (-1 when the slot
+// lies outside the pool: the window rows are then absent).
+__device__ __forceinline__ int64_t win_seq(const AttnArgs& a, int64_t b) {
+  if (!a.win_slot) return b;
+  const int32_t sl = a.win_slot[b];
+  return (sl >= 0 && sl < a.win_slots) ? sl : -1;
+}
+
+// Row of list id e of entry set be: e itself in the contiguous layout, the
+// pool row through the block table, or -1 when the id is absent.
+__device__ __forceinline__ int32_t ent_row_id(const AttnArgs& a, int64_t be, int32_t e) {
+  if (e < 0 || e >= a.Nmax) return -1;
+  return a.ent_pages.table ? (int32_t)paged_row(a.ent_pages, be, e) : e;
+}
+
+// First row of entry set be (the pool itself through a block table).
+__device__ __forceinline__ const uint8_t* ent_base(const AttnArgs& a, int64_t be) {
+  return (const uint8_t*)a.entries +
+         (a.ent_pages.table ? (size_t)0 : (size_t)be * (size_t)a.Nmax * a.ent_rb);
+}
+
+// Resolve logical list row j of unit (b, t); wsq is win_seq(a, b).
+__device__ __forceinline__ RowRef resolve_row(const AttnArgs& a, int64_t unit, int64_t b,
+                                              int64_t wsq, int t, int64_t j, int64_t nvis,
+                                              size_t win_rb, size_t ent_rb) {
   RowRef r{nullptr, a.win_fmt};
   if (j < kWindow) {
     int64_t p = (int64_t)t - (kWindow - 1) + j;
-    if (p < 0) return r;
+    if (p < 0 || wsq < 0) return r;
     int64_t row;
     if (a.win_mode == CSA_WIN_RING128) {
       row = p & (kWindow - 1);
@@ -61,20 +82,22 @@ __device__ __forceinline__ RowRef resolve_row(const AttnArgs& a, int64_t unit, i
       row = p - (int64_t)a.win_base[b];
       if (row < 0 || row >= a.win_rows) return r;
     }
-    r.p = (const uint8_t*)a.win + ((size_t)b * (size_t)a.win_rows + (size_t)row) * win_rb;
+    r.p = (const uint8_t*)a.win + ((size_t)wsq * (size_t)a.win_rows + (size_t)row) * win_rb;
     return r;
   }
   r.fmt = a.ent_fmt;
-  int64_t e;
+  const int64_t be = b % a.ent_seqs;
+  int32_t e;
   if (a.dense) {
-    e = j - kWindow;
-    if (e >= nvis) return r;
+    if (j - kWindow >= nvis) return r;
+    e = (int32_t)(j - kWindow);
   } else {
     if (j - kWindow >= a.topk) return r;
-    e = a.topk_idx[((b % a.ent_seqs) * a.Q + (unit - b * a.Q)) * a.topk + (j - kWindow)];
-    if (e < 0 || e >= a.Nmax) return r;
+    e = a.topk_idx[(be * a.Q + (unit - b * a.Q)) * a.topk + (j - kWindow)];
   }
-  r.p = (const uint8_t*)a.entries + ((size_t)(b % a.ent_seqs) * (size_t)a.Nmax + (size_t)e) * ent_rb;
+  e = ent_row_id(a, be, e);
+  if (e < 0) return r;
+  r.p = ent_base(a, be) + (size_t)e * ent_rb;
   return r;
 }
 
@@ -320,19 +343,29 @@ __device__ __forceinline__ void attend_tile(const uint4 (&fr)[2][4], uint32_t vm
 // Rows [j0, j1) of the list, all in format F.  Two register sets alternate:
 // while one tile is computed the next tile's rows are in flight.  Absent rows
 // (and rows past j1) are loaded from `stand_in`, a row of the same buffer, and
-// zeroed by the validity mask.
-template <int F, class RowFn>
-__device__ __forceinline__ void run_rows(int64_t j0, int64_t j1, RowFn row_of,
+// zeroed by the validity mask.  pre(j) reads a per-row token (a block id of a
+// block cache; a constant otherwise) that row_of(j, token) turns into the
+// row's address.  Tokens are read two tiles ahead, right after the loads of
+// the tile before, so that waiting for them never waits for a later tile.
+template <int F, class PreFn, class RowFn>
+__device__ __forceinline__ void run_rows(int64_t j0, int64_t j1, PreFn pre, RowFn row_of,
                                          const uint8_t* stand_in, const uint4 (&qa)[4],
                                          float zscale, int w, int lane, uint16_t* R,
                                          float4 (*Sp)[2][64], SoftmaxState& st) {
   const int r16 = lane & 15, kq = lane >> 4;
-  auto load_tile = [&](int64_t jt, Raw<F> (&f)[2], uint32_t& vm) {
+  auto pre_tile = [&](int64_t jt, int32_t (&tk)[2]) {
+#pragma unroll
+    for (int rt = 0; rt < 2; ++rt) {
+      const int64_t j = jt + 16 * rt + r16;
+      tk[rt] = j < j1 ? pre(j) : 0;
+    }
+  };
+  auto load_tile = [&](int64_t jt, const int32_t (&tk)[2], Raw<F> (&f)[2], uint32_t& vm) {
     vm = 0;
 #pragma unroll
     for (int rt = 0; rt < 2; ++rt) {
       const int64_t j = jt + 16 * rt + r16;
-      const uint8_t* p = j < j1 ? row_of(j) : nullptr;
+      const uint8_t* p = j < j1 ? row_of(j, tk[rt]) : nullptr;
       const unsigned long long bal = __ballot(p != nullptr);
       vm |= (uint32_t)(bal & 0xffffull) << (16 * rt);
       load_raw<F>(p ? p : stand_in, w, kq, f[rt]);
@@ -353,14 +386,25 @@ __device__ __forceinline__ void run_rows(int64_t j0, int64_t j1, RowFn row_of,
   };
   Raw<F> fa[2], fb[2];
   uint32_t va = 0, vb = 0;
-  load_tile(j0, fa, va);
+  int32_t ta[2], tb[2];  // tokens of the even / odd tiles
+  pre_tile(j0, ta);
+  load_tile(j0, ta, fa, va);
+  pre_tile(j0 + kTile, tb);
+  pre_tile(j0 + 2 * kTile, ta);
   for (int64_t jt = j0; jt < j1; jt += 2 * kTile) {
-    load_tile(jt + kTile, fb, vb);
+    load_tile(jt + kTile, tb, fb, vb);
+    pre_tile(jt + 3 * kTile, tb);
     compute_tile(fa, va);
-    load_tile(jt + 2 * kTile, fa, va);
+    load_tile(jt + 2 * kTile, ta, fa, va);
+    pre_tile(jt + 4 * kTile, ta);
     if (jt + kTile < j1) compute_tile(fb, vb);
   }
 }
+
+// No per-row token (contiguous rows, or addresses already resolved).
+struct NoToken {
+  __device__ __forceinline__ int32_t operator()(int64_t) const { return 0; }
+};
 
 // Query slices for one wave: head tile ht of the work-group, dims
 // 128 w + 32 s + 8 kq .. +8, with the last 64 dims rotated at row rr.  Every
@@ -572,13 +616,16 @@ __global__ void __launch_bounds__(kAttnThreads, HT <= 2 ? 2 : 1) attn_dense_all_
   const int rr = rope_row(a, t);
   const float zscale = a.scale * kLog2e;
 
-  if (SPARSE) {  // the chunk's top-k ids (slot j - j_begin), -1 where absent
+  if (SPARSE) {  // the chunk's rows of the entry set (slot j - j_begin), -1 where absent
     for (int i = tid; i < kChunkCsaLong; i += kAttnThreads) {
       const int64_t jj = j_begin + i;
-      Ids[i] = (jj >= kWindow && jj < j_end) ? a.topk_idx[eunit * a.topk + (jj - kWindow)] : -1;
+      Ids[i] = (jj >= kWindow && jj < j_end)
+                   ? ent_row_id(a, be, a.topk_idx[eunit * a.topk + (jj - kWindow)])
+                   : -1;
     }
     __syncthreads();
   }
+  const int64_t wsq = win_seq(a, b);
 
   uint4 qa[HT][4];
   load_q_frags<HT>(a, unit, 16 * ht0, w, r16, kq, rr, qa);
@@ -591,14 +638,24 @@ __global__ void __launch_bounds__(kAttnThreads, HT <= 2 ? 2 : 1) attn_dense_all_
     for (int dt = 0; dt < 8; ++dt) o[ht][dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   uint16_t* R = Rl[w];
 
-  auto run = [&](auto fmt_tag, int64_t j0, int64_t j1, auto row_of, const uint8_t* stand_in) {
+  // as run_rows: pre(j) reads a per-row token two tiles ahead, row_of(j, token)
+  // gives the row's address
+  auto run = [&](auto fmt_tag, int64_t j0, int64_t j1, auto pre, auto row_of,
+                 const uint8_t* stand_in) {
     constexpr int F = decltype(fmt_tag)::value;
-    auto load_tile = [&](int64_t jt, Raw<F> (&f)[2], uint32_t& vm) {
+    auto pre_tile = [&](int64_t jt, int32_t (&tk)[2]) {
+#pragma unroll
+      for (int rt = 0; rt < 2; ++rt) {
+        const int64_t j = jt + 16 * rt + r16;
+        tk[rt] = j < j1 ? pre(j) : 0;
+      }
+    };
+    auto load_tile = [&](int64_t jt, const int32_t (&tk)[2], Raw<F> (&f)[2], uint32_t& vm) {
       vm = 0;
 #pragma unroll
       for (int rt = 0; rt < 2; ++rt) {
         const int64_t j = jt + 16 * rt + r16;
-        const uint8_t* p = j < j1 ? row_of(j) : nullptr;
+        const uint8_t* p = j < j1 ? row_of(j, tk[rt]) : nullptr;
         const unsigned long long bal = __ballot(p != nullptr);
         vm |= (uint32_t)(bal & 0xffffull) << (16 * rt);
         load_raw<F>(p ? p : stand_in, w, kq, f[rt]);
@@ -619,11 +676,17 @@ __global__ void __launch_bounds__(kAttnThreads, HT <= 2 ? 2 : 1) attn_dense_all_
     };
     Raw<F> fa[2], fb[2];
     uint32_t va = 0, vb = 0;
-    load_tile(j0, fa, va);
+    int32_t ta[2], tb[2];
+    pre_tile(j0, ta);
+    load_tile(j0, ta, fa, va);
+    pre_tile(j0 + kTile, tb);
+    pre_tile(j0 + 2 * kTile, ta);
     for (int64_t jt = j0; jt < j1; jt += 2 * kTile) {
-      load_tile(jt + kTile, fb, vb);
+      load_tile(jt + kTile, tb, fb, vb);
+      pre_tile(jt + 3 * kTile, tb);
       compute_tile(fa, va);
-      load_tile(jt + 2 * kTile, fa, va);
+      load_tile(jt + 2 * kTile, ta, fa, va);
+      pre_tile(jt + 4 * kTile, ta);
       if (jt + kTile < j1) compute_tile(fb, vb);
     }
   };
@@ -631,25 +694,43 @@ __global__ void __launch_bounds__(kAttnThreads, HT <= 2 ? 2 : 1) attn_dense_all_
   // window rows [j_begin, min(j_end, 128))
   const int64_t jw = j_end < kWindow ? j_end : kWindow;
   if (j_begin < jw) {
-    auto win_row = [&](int64_t j) -> const uint8_t* {
-      return resolve_row(a, unit, b, t, j, nvis, a.win_rb, a.ent_rb).p;
+    auto win_row = [&](int64_t j, int32_t) -> const uint8_t* {
+      return resolve_row(a, unit, b, wsq, t, j, nvis, a.win_rb, a.ent_rb).p;
     };
-    const uint8_t* win0 = (const uint8_t*)a.win + (size_t)b * (size_t)a.win_rows * a.win_rb;
-    run(std::integral_constant<int, WF>{}, j_begin, jw, win_row, win0);
+    const uint8_t* win0 =
+        (const uint8_t*)a.win + (size_t)(wsq < 0 ? 0 : wsq) * (size_t)a.win_rows * a.win_rb;
+    run(std::integral_constant<int, WF>{}, j_begin, jw, NoToken{}, win_row, win0);
   }
   // entry rows [max(j_begin, 128), j_end)
   const int64_t je = j_begin > kWindow ? j_begin : kWindow;
   if (je < j_end && a.Nmax > 0) {
-    const uint8_t* ebase = (const uint8_t*)a.entries + (size_t)be * (size_t)a.Nmax * a.ent_rb;
-    auto ent_row = [&](int64_t j) -> const uint8_t* {
-      if (SPARSE) {
-        const int32_t e = Ids[j - j_begin];
-        return (e >= 0 && e < a.Nmax) ? ebase + (size_t)e * a.ent_rb : nullptr;
-      }
-      const int64_t e = j - kWindow;
-      return e < nvis ? ebase + (size_t)e * a.ent_rb : nullptr;
-    };
-    run(std::integral_constant<int, EF>{}, je, j_end, ent_row, ebase);
+    const uint8_t* ebase = ent_base(a, be);
+    if (!SPARSE && a.ent_pages.table) {
+      // block cache: the token is the row's block id
+      const PageMap pm = a.ent_pages;
+      const int64_t mask = ((int64_t)1 << pm.shift) - 1;
+      auto pre = [&](int64_t j) -> int32_t {
+        const int64_t e = j - kWindow;
+        return e < nvis ? pm.table[be * pm.max_blocks + (e >> pm.shift)] : -1;
+      };
+      auto ent_row = [&](int64_t j, int32_t blk) -> const uint8_t* {
+        const int64_t e = j - kWindow;
+        return (e < nvis && blk >= 0 && blk < pm.pool_blocks)
+                   ? ebase + (size_t)((((int64_t)blk) << pm.shift) + (e & mask)) * a.ent_rb
+                   : nullptr;
+      };
+      run(std::integral_constant<int, EF>{}, je, j_end, pre, ent_row, ebase);
+    } else {
+      auto ent_row = [&](int64_t j, int32_t) -> const uint8_t* {
+        if (SPARSE) {
+          const int32_t e = Ids[j - j_begin];
+          return e >= 0 ? ebase + (size_t)e * a.ent_rb : nullptr;
+        }
+        const int64_t e = j - kWindow;
+        return e < nvis ? ebase + (size_t)e * a.ent_rb : nullptr;
+      };
+      run(std::integral_constant<int, EF>{}, je, j_end, NoToken{}, ent_row, ebase);
+    }
   }
 
   if (SPARSE && nchunks == 1) {
@@ -764,13 +845,17 @@ __global__ void __launch_bounds__(kAttnThreads) attn_mfma_kernel(AttnArgs a, int
   const float zscale = a.scale * kLog2e;
 
   // top-k ids of this chunk, fetched once: in registers (lane holds rows
-  // j_begin + 16 i + r16), or for long chunks in LDS (slot j - j_begin)
+  // j_begin + 16 i + r16), or for long chunks in LDS (slot j - j_begin);
+  // both end up as rows of the entry set (pool rows through a block table),
+  // -1 where absent
   int32_t ids[LONG ? 1 : kMaxIdsPerLane];
   if (!a.dense) {
     if (LONG) {
       for (int i = tid; i < kChunkCsaLong; i += kAttnThreads) {
         const int64_t jj = j_begin + i;
-        Ids[i] = (jj >= kWindow && jj < j_end) ? a.topk_idx[eunit * a.topk + (jj - kWindow)] : -1;
+        Ids[i] = (jj >= kWindow && jj < j_end)
+                     ? ent_row_id(a, be, a.topk_idx[eunit * a.topk + (jj - kWindow)])
+                     : -1;
       }
       __syncthreads();
     } else {
@@ -786,6 +871,13 @@ __global__ void __launch_bounds__(kAttnThreads) attn_mfma_kernel(AttnArgs a, int
   uint4 qa1[1][4];
   load_q_frags<1>(a, unit, 16 * hg, w, r16, kq, rr, qa1);
   const uint4 qa[4] = {qa1[0][0], qa1[0][1], qa1[0][2], qa1[0][3]};
+  // ids to rows after the query loads are issued, so that their round trips
+  // overlap (a block table adds one more)
+  if (!a.dense && !LONG) {
+#pragma unroll
+    for (int i = 0; i < kMaxIdsPerLane; ++i) ids[i] = ent_row_id(a, be, ids[i]);
+  }
+  const int64_t wsq = win_seq(a, b);
 
   SoftmaxState st;
   st.m = -INFINITY;
@@ -797,24 +889,40 @@ __global__ void __launch_bounds__(kAttnThreads) attn_mfma_kernel(AttnArgs a, int
   // window rows [j_begin, min(j_end, 128))
   const int64_t jw = j_end < kWindow ? j_end : kWindow;
   if (j_begin < jw) {
-    auto win_row = [&](int64_t j) -> const uint8_t* {
-      return resolve_row(a, unit, b, t, j, nvis, a.win_rb, a.ent_rb).p;
+    auto win_row = [&](int64_t j, int32_t) -> const uint8_t* {
+      return resolve_row(a, unit, b, wsq, t, j, nvis, a.win_rb, a.ent_rb).p;
     };
-    const uint8_t* win0 = (const uint8_t*)a.win + (size_t)b * (size_t)a.win_rows * a.win_rb;
-    run_rows<WF>(j_begin, jw, win_row, win0, qa, zscale, w, lane, R, Sp, st);
+    const uint8_t* win0 =
+        (const uint8_t*)a.win + (size_t)(wsq < 0 ? 0 : wsq) * (size_t)a.win_rows * a.win_rb;
+    run_rows<WF>(j_begin, jw, NoToken{}, win_row, win0, qa, zscale, w, lane, R, Sp, st);
   }
   // entry rows [max(j_begin, 128), j_end)
   const int64_t je = j_begin > kWindow ? j_begin : kWindow;
   if (je < j_end && a.Nmax > 0) {
-    const uint8_t* ebase = (const uint8_t*)a.entries + (size_t)be * (size_t)a.Nmax * a.ent_rb;
-    if (a.dense) {
-      auto ent_row = [&](int64_t j) -> const uint8_t* {
+    const uint8_t* ebase = ent_base(a, be);
+    if (a.dense && a.ent_pages.table) {
+      // block cache: the token is the row's block id
+      const PageMap pm = a.ent_pages;
+      const int64_t mask = ((int64_t)1 << pm.shift) - 1;
+      auto pre = [&](int64_t j) -> int32_t {
+        const int64_t e = j - kWindow;
+        return e < nvis ? pm.table[be * pm.max_blocks + (e >> pm.shift)] : -1;
+      };
+      auto ent_row = [&](int64_t j, int32_t blk) -> const uint8_t* {
+        const int64_t e = j - kWindow;
+        return (e < nvis && blk >= 0 && blk < pm.pool_blocks)
+                   ? ebase + (size_t)((((int64_t)blk) << pm.shift) + (e & mask)) * a.ent_rb
+                   : nullptr;
+      };
+      run_rows<EF>(je, j_end, pre, ent_row, ebase, qa, zscale, w, lane, R, Sp, st);
+    } else if (a.dense) {
+      auto ent_row = [&](int64_t j, int32_t) -> const uint8_t* {
         const int64_t e = j - kWindow;
         return e < nvis ? ebase + (size_t)e * a.ent_rb : nullptr;
       };
-      run_rows<EF>(je, j_end, ent_row, ebase, qa, zscale, w, lane, R, Sp, st);
+      run_rows<EF>(je, j_end, NoToken{}, ent_row, ebase, qa, zscale, w, lane, R, Sp, st);
     } else {
-      auto ent_row = [&](int64_t j) -> const uint8_t* {
+      auto ent_row = [&](int64_t j, int32_t) -> const uint8_t* {
         int32_t e = -1;
         if (LONG) {
           e = Ids[j - j_begin];
@@ -825,9 +933,9 @@ __global__ void __launch_bounds__(kAttnThreads) attn_mfma_kernel(AttnArgs a, int
           for (int i = 0; i < kMaxIdsPerLane; ++i)
             if (i == slot) e = ids[i];
         }
-        return (e >= 0 && e < a.Nmax) ? ebase + (size_t)e * a.ent_rb : nullptr;
+        return e >= 0 ? ebase + (size_t)e * a.ent_rb : nullptr;
       };
-      run_rows<EF>(je, j_end, ent_row, ebase, qa, zscale, w, lane, R, Sp, st);
+      run_rows<EF>(je, j_end, NoToken{}, ent_row, ebase, qa, zscale, w, lane, R, Sp, st);
     }
   }
 
@@ -983,8 +1091,9 @@ __global__ void __launch_bounds__(kAttnThreads) attn_f32_kernel(AttnArgs a) {
     qy = ny;
   }
   float m = -INFINITY, l = 0.f, ox = 0.f, oy = 0.f;
+  const int64_t wsq = win_seq(a, b);
   for (int64_t j = 0; j < list_len; ++j) {
-    RowRef rf = resolve_row(a, unit, b, t, j, nvis, win_rb, ent_rb);
+    RowRef rf = resolve_row(a, unit, b, wsq, t, j, nvis, win_rb, ent_rb);
     if (rf.p == nullptr) continue;  // uniform across the block
     const float cx = row_val_f32(rf, d), cy = row_val_f32(rf, d + 1);
     float part = fmaf(qx, cx, qy * cy);

@@ -19,6 +19,16 @@ typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4_t;
 // copies stay in registers.
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
+// ---------------------------------------------------------------- block cache
+// Pool row of logical entry e of sequence b through a block table, or -1 when
+// the block id is -1 or outside the pool.  e must lie below max_blocks << shift.
+__device__ __forceinline__ int64_t paged_row(const PageMap& m, int64_t b, int64_t e) {
+  const int32_t blk = m.table[b * m.max_blocks + (e >> m.shift)];
+  return (blk >= 0 && blk < m.pool_blocks)
+             ? ((int64_t)blk << m.shift) + (e & (((int64_t)1 << m.shift) - 1))
+             : -1;
+}
+
 // ---------------------------------------------------------------- bf16 bits
 __device__ __forceinline__ float bf16_to_f32(uint16_t b) {
   return __uint_as_float(((uint32_t)b) << 16);

@@ -443,12 +443,34 @@ struct CompArgs {
   int64_t entries_cap;
   size_t entry_rb;
   const float* P;  // [B*T][2*CD]
+  // block cache: entries through a block table, state in slots of a pool
+  PageMap ent_pages;          // table == nullptr: entries[b][i]
+  const int32_t* state_slot;  // nullptr: state of sequence b is slot b
+  int64_t state_slots;
 };
 
-// (v, s) of token p of sequence b at state column col (0 <= col < CD), where
-// the call starts at p0.  Tokens before p0 are read from the state as given.
-__device__ __forceinline__ void token_vs(const CompArgs& a, int64_t b, int64_t p0, int64_t p,
-                                         int col, float& v, float& s) {
+// State slot of sequence b, or -1 when it lies outside the pool (the
+// sequence is then skipped).
+__device__ __forceinline__ int64_t state_seq(const CompArgs& a, int64_t b) {
+  if (!a.state_slot) return b;
+  const int32_t sl = a.state_slot[b];
+  return (sl >= 0 && sl < a.state_slots) ? sl : -1;
+}
+
+// Row of entry i of sequence b, or nullptr when it is not written (beyond
+// the capacity, or in an unallocated block of a block cache).
+__device__ __forceinline__ uint8_t* entry_row(const CompArgs& a, int64_t b, int64_t i) {
+  if (i < 0 || i >= a.entries_cap) return nullptr;
+  if (!a.ent_pages.table) return a.entries + ((size_t)b * (size_t)a.entries_cap + (size_t)i) * a.entry_rb;
+  const int64_t r = paged_row(a.ent_pages, b, i);
+  return r < 0 ? nullptr : a.entries + (size_t)r * a.entry_rb;
+}
+
+// (v, s) of token p of sequence b (state slot sq) at state column col
+// (0 <= col < CD), where the call starts at p0.  Tokens before p0 are read
+// from the state as given.
+__device__ __forceinline__ void token_vs(const CompArgs& a, int64_t b, int64_t sq, int64_t p0,
+                                         int64_t p, int col, float& v, float& s) {
   if (p < 0) {
     v = 0.f;
     s = -INFINITY;
@@ -464,15 +486,16 @@ __device__ __forceinline__ void token_vs(const CompArgs& a, int64_t b, int64_t p
   int slot;
   if (p / a.ratio == cur) slot = (a.coff == 2 ? a.ratio : 0) + (int)(p % a.ratio);
   else slot = (int)(p % a.ratio);  // previous block (overlap only)
-  const int64_t si = (b * (int64_t)(a.coff * a.ratio) + slot) * a.CD + col;
+  const int64_t si = (sq * (int64_t)(a.coff * a.ratio) + slot) * a.CD + col;
   v = a.kv_state[si];
   s = a.score_state[si];
 }
 
 // ------------------------------------------------------------------ emit
-// Pool block i of sequence b into y[0, d) (reads only); returns this thread's
-// sum of squares.
-__device__ float pool_block(const CompArgs& a, int64_t b, int64_t p0, int64_t i, float* y) {
+// Pool block i of sequence b (state slot st) into y[0, d) (reads only);
+// returns this thread's sum of squares.
+__device__ float pool_block(const CompArgs& a, int64_t b, int64_t st, int64_t p0, int64_t i,
+                            float* y) {
   const int tid = threadIdx.x;
   const int r = a.ratio;
   const int d = a.d;
@@ -497,7 +520,7 @@ __device__ float pool_block(const CompArgs& a, int64_t b, int64_t p0, int64_t i,
           p = i * r + sl;
           col = c;
         }
-        token_vs(a, b, p0, p, col, vv[j], ss[j]);
+        token_vs(a, b, st, p0, p, col, vv[j], ss[j]);
       }
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
@@ -594,8 +617,8 @@ __device__ void finish_block(const CompArgs& a, int64_t b, int64_t i, float* y, 
     for (int c = tid; c < d; c += kThreads) z[c] *= sc;
     __syncthreads();
   }
-  if (i >= a.entries_cap) return;
-  uint8_t* row = a.entries + ((size_t)b * (size_t)a.entries_cap + (size_t)i) * a.entry_rb;
+  uint8_t* row = entry_row(a, b, i);
+  if (row == nullptr) return;
   if (a.entry_fmt == CSA_F32) {
     for (int c = tid; c < d; c += kThreads) ((float*)row)[c] = z[c];
   } else if (a.entry_fmt == CSA_BF16) {
@@ -618,7 +641,9 @@ __global__ void __launch_bounds__(kThreads) emit_kernel(CompArgs a) {
   const int r = a.ratio;
   const int64_t i = p0 / r + blockIdx.x;              // candidate block
   if (p0 < 0 || (i + 1) * r - 1 >= p0 + a.T) return;  // not completed by this call
-  const float sq = pool_block(a, b, p0, i, y);
+  const int64_t st = state_seq(a, b);
+  if (st < 0) return;
+  const float sq = pool_block(a, b, st, p0, i, y);
   finish_block(a, b, i, y, z, red, sq, load_norm_rope(a, i));
 }
 
@@ -632,17 +657,19 @@ __global__ void __launch_bounds__(kThreads) emit_kernel(CompArgs a) {
 __device__ void state_column(const CompArgs& a, int64_t b, int col) {
   const int64_t p0 = a.start_pos[b];
   if (p0 < 0) return;
+  const int64_t sq = state_seq(a, b);
+  if (sq < 0) return;
   const int r = a.ratio;
   const int64_t p1 = p0 + a.T;
   const int64_t first_block = p0 / r, end_block = p1 / r;
   const int nslots = a.coff * r;
-  const int64_t sbase = b * (int64_t)nslots * a.CD + col;
+  const int64_t sbase = sq * (int64_t)nslots * a.CD + col;
   const int64_t unfinished0 = end_block * r > p0 ? end_block * r : p0;
   if (a.coff == 1) {
     // no slot moves: tokens of this call land in slot p mod r
     for (int64_t p = unfinished0; p < p1; ++p) {
       float v, sc;
-      token_vs(a, b, p0, p, col, v, sc);
+      token_vs(a, b, sq, p0, p, col, v, sc);
       a.kv_state[sbase + (p % r) * a.CD] = v;
       a.score_state[sbase + (p % r) * a.CD] = sc;
     }
@@ -652,7 +679,7 @@ __device__ void state_column(const CompArgs& a, int64_t b, int col) {
         const int64_t p = done * r + q;
         if (p < p0) continue;  // already in its slot
         float v, sc;
-        token_vs(a, b, p0, p, col, v, sc);
+        token_vs(a, b, sq, p0, p, col, v, sc);
         a.kv_state[sbase + (int64_t)q * a.CD] = v;
         a.score_state[sbase + (int64_t)q * a.CD] = sc;
       }
@@ -666,14 +693,14 @@ __device__ void state_column(const CompArgs& a, int64_t b, int col) {
   for (int sl = 0; sl < 8; ++sl) wr[sl] = false;
   for (int64_t p = unfinished0; p < p1; ++p) {
     const int sl = r + (int)(p % r);
-    token_vs(a, b, p0, p, col, nv[sl], ns[sl]);
+    token_vs(a, b, sq, p0, p, col, nv[sl], ns[sl]);
     wr[sl] = true;
   }
   if (end_block > first_block) {
     const int64_t done = end_block - 1;
     for (int q = 0; q < r; ++q) {
       const int64_t p = done * r + q;
-      token_vs(a, b, p0, p, col, nv[q], ns[q]);
+      token_vs(a, b, sq, p0, p, col, nv[q], ns[q]);
       wr[q] = true;
       if (!wr[r + q]) {
         nv[r + q] = nv[q];
@@ -705,11 +732,11 @@ __global__ void __launch_bounds__(kThreads) state_kernel(CompArgs a) {
 // 8 slots of its channels, and the norm weights and rotation factors of the
 // block the token belongs to -- is loaded in one round, so the load phase is
 // one round of memory latency.
-__device__ void emit_t1_overlap(const CompArgs& a, int64_t b, int64_t p0, float* y, float* z,
-                                float* red) {
+__device__ void emit_t1_overlap(const CompArgs& a, int64_t b, int64_t st, int64_t p0, float* y,
+                                float* z, float* red) {
   const int r = 4, d = a.d, CD = a.CD, tid = threadIdx.x;
   const int N = 2 * CD;
-  const int64_t sb = b * (int64_t)(2 * r) * CD;
+  const int64_t sb = st * (int64_t)(2 * r) * CD;
   const NormRope nr = load_norm_rope(a, p0 < 0 ? 0 : p0 / r);
   constexpr int kPer = 2;  // channels per thread (d <= 512 = 2 kThreads)
   float pv[kPer][2][kKSlices], ps[kPer][2][kKSlices];  // slices of v and score, halves 0/1
@@ -825,9 +852,11 @@ __global__ void __launch_bounds__(kThreads) emit_t1_kernel(CompJobs jobs) {
   const int d = a.d, tid = threadIdx.x;
   const int nslots = a.coff * r;
   const int N = 2 * a.CD;
-  const int64_t sb = b * (int64_t)nslots * a.CD;
+  const int64_t st = state_seq(a, b);
+  if (st < 0) return;
+  const int64_t sb = st * (int64_t)nslots * a.CD;
   if (a.coff == 2) {  // ratio 4 with overlap: 8 slots
-    emit_t1_overlap(a, b, p0, y, z, red);
+    emit_t1_overlap(a, b, st, p0, y, z, red);
     return;
   }
   if (p0 < 0) return;
@@ -945,7 +974,8 @@ __global__ void __launch_bounds__(kThreads) pool128_t1_kernel(CompJobs jobs, flo
   const int64_t b = blockIdx.x;
   const int slice = blockIdx.y;
   const int64_t p0 = a.start_pos[b];
-  if (p0 < 0) return;
+  const int64_t st = state_seq(a, b);
+  if (p0 < 0 || st < 0) return;
   const int r = a.ratio;                    // 128, one slot per token
   const int ns = (int)(p0 % r);
   const bool done = ns == r - 1;
@@ -953,7 +983,7 @@ __global__ void __launch_bounds__(kThreads) pool128_t1_kernel(CompJobs jobs, flo
   const int cl = tid & (kPoolChannels - 1), g = tid >> 6;
   const int c = slice * kPoolChannels + cl;
   const int N = 2 * a.CD;
-  const int64_t sb = b * (int64_t)r * a.CD;
+  const int64_t sb = st * (int64_t)r * a.CD;
   const bool own = (ns >> 5) == g;          // this slot group holds the new token
   float nv = 0.f, nsc = 0.f;
   if (own) {
@@ -1022,7 +1052,7 @@ __global__ void __launch_bounds__(kThreads) finish128_t1_kernel(CompJobs jobs,
   const CompArgs& a = jobs.c[0];
   const int64_t b = blockIdx.x;
   const int64_t p0 = a.start_pos[b];
-  if (p0 < 0 || (p0 + 1) % a.ratio != 0) return;
+  if (p0 < 0 || (p0 + 1) % a.ratio != 0 || state_seq(a, b) < 0) return;
   const int tid = threadIdx.x;
   for (int c = tid; c < a.d; c += kThreads) y[c] = ybuf[b * (int64_t)a.d + c];
   float sq = 0.f;
@@ -1078,6 +1108,15 @@ static CompArgs comp_args(const csa_compress_args* in, float* P) {
   a.entries_cap = in->entries_cap;
   a.entry_rb = kv_row_bytes(in->entry_fmt, in->head_dim);
   a.P = P;
+  a.ent_pages = PageMap{nullptr, 0, 0, 0};
+  if (in->block_table) {
+    int shift = 0;
+    while ((1 << shift) < in->block_entries) ++shift;
+    a.ent_pages = PageMap{in->block_table, in->max_blocks, in->pool_blocks, shift};
+    a.entries_cap = in->max_blocks * (int64_t)in->block_entries;
+  }
+  a.state_slot = in->state_slot;
+  a.state_slots = in->state_slots;
   return a;
 }
 

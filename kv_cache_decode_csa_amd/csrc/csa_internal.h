@@ -20,6 +20,17 @@ constexpr int kCandCap = 8192;    // boundary-bin candidates kept per row
 
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
+// Block-cache addressing ("DeepSeek-V4 deep dive" section 9.4): logical
+// entry e of sequence b is pool row (table[b][e >> shift] << shift) +
+// (e & (2^shift - 1)).  table == nullptr selects the contiguous layout, in
+// which sequence b's rows start at row b * Nmax.
+struct PageMap {
+  const int32_t* table;  // [B][max_blocks], or nullptr
+  int64_t max_blocks;
+  int64_t pool_blocks;
+  int shift;             // log2(entries per block)
+};
+
 // Sets the calling thread's error detail (csa_last_error_detail) and returns code.
 csa_status set_error(csa_status code, const char* fmt, ...);
 
@@ -52,12 +63,16 @@ hipError_t launch_topk_select(const float* scores, const int32_t* n_valid, int64
 hipError_t launch_index_scores(const void* q_idx, int q_fmt, const float* w_idx,
                                const void* k_idx, int k_fmt, const int32_t* pos, int ratio, int B,
                                int Q, int Hi, int64_t Nmax, float* scores, int32_t* n_vis,
-                               TopkWs w, int bf16_scores, hipStream_t s);
+                               TopkWs w, int bf16_scores, hipStream_t s,
+                               PageMap pm = PageMap{nullptr, 0, 0, 0});
 
 struct AttnArgs {
   const void* q; int q_fmt;
   const void* win; int win_fmt; int win_mode; const int32_t* win_base; int64_t win_rows;
   const void* entries; int ent_fmt; int64_t Nmax;
+  PageMap ent_pages;                   // entries through a block table (table == nullptr: none)
+  const int32_t* win_slot;             // ring window of sequence b is win[win_slot[b]] (nullptr: b)
+  int64_t win_slots;                   // slots in the window pool (a slot outside: no window rows)
   int ent_seqs;                        // sequence b reads entry set and top-k list b % ent_seqs
                                        // and sinks [b / ent_seqs][H] (B: one set per sequence)
   int dense;                           // 0: top-k list (CSA), 1: all completed entries (HCA)

@@ -258,12 +258,16 @@ struct Scorer {
   }
 };
 
-template <int HT, int KFMT>
+// Block cache (PG): as in the split kernel below, a wave step's keys are at
+// most two 32-key halves, each contiguous in one block; the ids of step i + 2
+// are read right after step i's key loads, and a half in an unallocated block
+// is staged as zeros.  The partial step at the end looks its keys up one by one.
+template <int HT, int KFMT, bool PG>
 __global__ void __launch_bounds__(kIdxThreads) index_scores_mfma(
     const uint16_t* __restrict__ q_idx, const float* __restrict__ w_idx,
     const uint8_t* __restrict__ k_idx, const int32_t* __restrict__ pos, int ratio, int Q,
     int64_t Nmax, int64_t row_off, float* __restrict__ scores,
-    int32_t* __restrict__ n_vis_out, uint32_t* __restrict__ hist_g, int bf16_scores) {
+    int32_t* __restrict__ n_vis_out, uint32_t* __restrict__ hist_g, int bf16_scores, PageMap pm) {
   constexpr int64_t kRowBytes = key_row_bytes<KFMT>();
   constexpr int kTilesPerIter = tiles_per_iter<KFMT>();
   constexpr int kKeysPerIter = 16 * kTilesPerIter;
@@ -292,7 +296,7 @@ __global__ void __launch_bounds__(kIdxThreads) index_scores_mfma(
   const int r16 = sc.r16, kq = sc.kq;
   __syncthreads();
 
-  const uint8_t* kbase = k_idx + b * Nmax * kRowBytes;
+  const uint8_t* kbase = PG ? k_idx : k_idx + b * Nmax * kRowBytes;
   float* srow = scores + row * Nmax;
   const int64_t end = nv;
   // A full step (all K keys below `end`) is read as one contiguous, coalesced
@@ -308,24 +312,56 @@ __global__ void __launch_bounds__(kIdxThreads) index_scores_mfma(
   };
 
   int64_t n_full = end - k0 >= kKeysPerIter ? (end - k0 - kKeysPerIter) / stride + 1 : 0;
+  constexpr int kHalf = 32 * (int)kRowBytes / 16;  // pieces of 32 keys
+  static_assert(kStagePieces <= 2 * kHalf, "a wave step spans at most two 32-key halves");
   if (n_full > 0) {
     u32x4_t* st_lds = stage[wave];
-    auto gload = [&](int64_t i) __attribute__((always_inline)) {
-      const u32x4_t* src = (const u32x4_t*)(kbase + (k0 + i * stride) * kRowBytes);
+    // block ids of step i's halves (lane 0: first, lane 1: second), read with
+    // a lane-dependent address so that they are vector loads
+    auto tload = [&](int64_t i) __attribute__((always_inline)) {
+      if (!PG) return 0;
+      const int64_t k = k0 + (i < n_full ? i : 0) * stride;
+      int64_t l = (k + 32 * (lane & 1)) >> pm.shift;
+      l = l < pm.max_blocks ? l : pm.max_blocks - 1;
+      return pm.table[b * pm.max_blocks + l];
+    };
+    struct Step {
       U4Array<kStageLoads> v;
+      int zero;
+    };
+    auto gload = [&](int64_t i, int tid) __attribute__((always_inline)) {
+      const int64_t k = k0 + i * stride;
+      const u32x4_t* src0 = (const u32x4_t*)(kbase + k * kRowBytes);
+      const u32x4_t* src1 = src0;
+      Step st;
+      st.zero = 0;
+      if (PG) {
+        const int64_t mask = ((int64_t)1 << pm.shift) - 1;
+        const int id0 = __builtin_amdgcn_readlane(tid, 0);
+        const int id1 = __builtin_amdgcn_readlane(tid, 1);
+        const bool ok0 = id0 >= 0 && id0 < pm.pool_blocks;
+        const bool ok1 = id1 >= 0 && id1 < pm.pool_blocks;
+        st.zero = (ok0 ? 0 : 1) | (ok1 ? 0 : 2);
+        src0 = (const u32x4_t*)(k_idx + (ok0 ? ((((int64_t)id0) << pm.shift) + (k & mask)) * kRowBytes : 0));
+        src1 = (const u32x4_t*)(k_idx + (ok1 ? ((((int64_t)id1) << pm.shift) + ((k + 32) & mask)) * kRowBytes : 0));
+      }
 #pragma unroll
       for (int j = 0; j < kStageLoads; ++j) {
         int piece = lane + 64 * j;
         piece = piece < kStagePieces ? piece : kStagePieces - 1;
-        v.v[j] = src[piece];
+        if (PG) st.v.v[j] = piece < kHalf ? src0[piece] : src1[piece - kHalf];
+        else st.v.v[j] = src0[piece];
       }
-      return v;
+      return st;
     };
-    auto stage_and_score = [&](int64_t i, const U4Array<kStageLoads>& v)
-                               __attribute__((always_inline)) {
+    auto stage_and_score = [&](int64_t i, const Step& v) __attribute__((always_inline)) {
       wave_lds_sync();  // earlier reads of the region are ordered before these writes
 #pragma unroll
-      for (int j = 0; j < kStageLoads; ++j) st_lds[stage_slot<KFMT>(lane + 64 * j)] = v.v[j];
+      for (int j = 0; j < kStageLoads; ++j) {
+        const int piece = lane + 64 * j;
+        const bool z = PG && ((v.zero >> (piece < kHalf ? 0 : 1)) & 1);
+        st_lds[stage_slot<KFMT>(piece)] = z ? u32x4_t{0u, 0u, 0u, 0u} : v.v.v[j];
+      }
       wave_lds_sync();
       KeyRaw f[kTilesPerIter];
 #pragma unroll
@@ -337,16 +373,22 @@ __global__ void __launch_bounds__(kIdxThreads) index_scores_mfma(
     // leave loads pending into the other set, and the wait that then guards
     // that set would stall every iteration); the last one or two steps are
     // peeled, and no step is read twice.
-    U4Array<kStageLoads> sa = gload(0), sb;
+    // ids of step i + 2 are read right after step i's keys (ta: even steps,
+    // tb: odd steps)
+    int ta = tload(0), tb = tload(1);
+    Step sa = gload(0, ta), sb;
+    ta = tload(2);
     int64_t i = 0;
     for (; i + 2 < n_full; i += 2) {
-      sb = gload(i + 1);
+      sb = gload(i + 1, tb);
+      tb = tload(i + 3);
       stage_and_score(i, sa);
-      sa = gload(i + 2);
+      sa = gload(i + 2, ta);
+      ta = tload(i + 4);
       stage_and_score(i + 1, sb);
     }
     if (i + 1 < n_full) {
-      sb = gload(i + 1);
+      sb = gload(i + 1, tb);
       stage_and_score(i, sa);
       stage_and_score(i + 1, sb);
     } else {
@@ -356,11 +398,25 @@ __global__ void __launch_bounds__(kIdxThreads) index_scores_mfma(
   const int64_t kt = k0 + n_full * stride;
   if (kt < end) {
     KeyRaw f[kTilesPerIter];
+    bool zk[kTilesPerIter];
 #pragma unroll
     for (int nt = 0; nt < kTilesPerIter; ++nt) {
       int64_t key = kt + 16 * nt + r16;
       key = key < end ? key : end - 1;
+      zk[nt] = false;
+      if (PG) {
+        const int64_t pr = paged_row(pm, b, key);
+        zk[nt] = pr < 0;
+        key = pr < 0 ? 0 : pr;
+      }
       load_key<KFMT>(kbase + key * kRowBytes, kq, f[nt]);
+    }
+    if (PG) {
+#pragma unroll
+      for (int nt = 0; nt < kTilesPerIter; ++nt)
+        if (zk[nt])
+#pragma unroll
+          for (int w = 0; w < 16; ++w) f[nt].w[w] = 0u;
     }
     score_tiles(kt, f);
   }
@@ -390,12 +446,20 @@ constexpr int kSplitStep = 256;   // keys per work-group step
 constexpr int kSplitDepth = 2;    // loader register sets (even)
 constexpr int64_t kSplitTargetWgs = 256;
 
-template <int HT>
+//
+// Block cache (PG): the keys sit in a pool of blocks of at least 32 keys, so
+// each 32-key half of a quarter is one contiguous run of 264 pieces in one
+// block.  The two block ids of a step are read by ordinary vector loads
+// issued right after the key loads of the step kSplitDepth earlier, so by the
+// time a step's loads are issued its ids have arrived without a wait on any
+// later key load.  A half whose block is unallocated is read from the pool's
+// first block and staged as zeros.
+template <int HT, bool PG>
 __global__ void __launch_bounds__(kSplitThreads) index_scores_split(
     const uint16_t* __restrict__ q_idx, const float* __restrict__ w_idx,
     const uint8_t* __restrict__ k_idx, const int32_t* __restrict__ pos, int ratio, int Q,
     int64_t Nmax, int64_t row_off, float* __restrict__ scores,
-    int32_t* __restrict__ n_vis_out, uint32_t* __restrict__ hist_g, int bf16_scores) {
+    int32_t* __restrict__ n_vis_out, uint32_t* __restrict__ hist_g, int bf16_scores, PageMap pm) {
   constexpr int KFMT = CSA_FP8_MX32;
   constexpr int64_t kRowBytes = 132;
   constexpr int kSub = kSplitStep / 4;                 // keys per quarter (one wave)
@@ -421,44 +485,86 @@ __global__ void __launch_bounds__(kSplitThreads) index_scores_split(
   if (x0 >= nv) return;
   const int64_t n_steps = (nv - x0 + G * kSplitStep - 1) / (G * kSplitStep);
   const int64_t n_iter = (n_steps + kSplitDepth - 1) / kSplitDepth * kSplitDepth;
-  const uint8_t* kbase = k_idx + b * Nmax * kRowBytes;
+  const uint8_t* kbase = PG ? k_idx : k_idx + b * Nmax * kRowBytes;
   const int64_t end = nv;
+  constexpr int kHalf = 32 * (int)kRowBytes / 16;      // 264 pieces: 32 keys
 
   for (int i = t; i < kHistBins; i += kSplitThreads) hist[i] = 0;
   __syncthreads();
 
   if (loader) {
-    // the quarter's stream of step i, clamped to whole visible rows
-    auto gload = [&](int64_t i, U4Array<kLoads>& v) __attribute__((always_inline)) {
+    auto step_key = [&](int64_t i) __attribute__((always_inline)) {
       int64_t k = (i * G + blockIdx.x) * kSplitStep + kSub * j;
       if (i >= n_steps || k >= end) k = 0;
+      return k;
+    };
+    // block ids of step i's two halves: lane 0 reads the first, lane 1 the
+    // second (a lane-dependent address, so a vector load)
+    auto tload = [&](int64_t i) __attribute__((always_inline)) {
+      if (!PG) return 0;
+      const int64_t k = step_key(i);
+      int64_t l = (k + 32 * (lane & 1)) >> pm.shift;
+      l = l < pm.max_blocks ? l : pm.max_blocks - 1;
+      return pm.table[b * pm.max_blocks + l];
+    };
+    // the quarter's stream of step i, clamped to whole visible rows; zero
+    // gets bit h set when half h's block is unallocated
+    auto gload = [&](int64_t i, U4Array<kLoads>& v, int tid, int& zero)
+                     __attribute__((always_inline)) {
+      const int64_t k = step_key(i);
       const int64_t nk = end - k < kSub ? end - k : kSub;
       const int last = (int)((nk * kRowBytes - 1) / 16);
-      const u32x4_t* src = (const u32x4_t*)(kbase + k * kRowBytes);
+      const u32x4_t* src0 = (const u32x4_t*)(kbase + k * kRowBytes);
+      const u32x4_t* src1 = src0;
+      zero = 0;
+      if (PG) {
+        const int64_t mask = ((int64_t)1 << pm.shift) - 1;
+        const int id0 = __builtin_amdgcn_readlane(tid, 0);
+        const int id1 = __builtin_amdgcn_readlane(tid, 1);
+        const bool ok0 = id0 >= 0 && id0 < pm.pool_blocks;
+        const bool ok1 = id1 >= 0 && id1 < pm.pool_blocks;
+        zero = (ok0 ? 0 : 1) | (ok1 ? 0 : 2);
+        src0 = (const u32x4_t*)(k_idx + (ok0 ? ((((int64_t)id0) << pm.shift) + (k & mask)) * kRowBytes : 0));
+        src1 = (const u32x4_t*)(k_idx + (ok1 ? ((((int64_t)id1) << pm.shift) + ((k + 32) & mask)) * kRowBytes : 0));
+      }
 #pragma unroll
       for (int l = 0; l < kLoads; ++l) {
         const int piece = lane + 64 * l;
-        v.v[l] = src[piece < last ? piece : last];
+        const int p = piece < last ? piece : last;
+        if (PG) v.v[l] = p < kHalf ? src0[p] : src1[p - kHalf];
+        else v.v[l] = src0[p];
       }
     };
-    auto stage = [&](int bi, const U4Array<kLoads>& v) __attribute__((always_inline)) {
+    auto stage = [&](int bi, const U4Array<kLoads>& v, int zero) __attribute__((always_inline)) {
       u32x4_t* st = buf[bi][j];
 #pragma unroll
-      for (int l = 0; l < kLoads; ++l) st[lane + 64 * l] = v.v[l];
+      for (int l = 0; l < kLoads; ++l) {
+        const int piece = lane + 64 * l;
+        const bool z = PG && ((zero >> (piece < kHalf ? 0 : 1)) & 1);
+        st[piece] = z ? u32x4_t{0u, 0u, 0u, 0u} : v.v[l];
+      }
     };
     U4Array<kLoads> r[kSplitDepth];
+    int tb[kSplitDepth], zr[kSplitDepth];
 #pragma unroll
-    for (int u = 0; u < kSplitDepth; ++u) gload(u, r[u]);
-    stage(0, r[0]);
+    for (int u = 0; u < kSplitDepth; ++u) tb[u] = tload(u);
+#pragma unroll
+    for (int u = 0; u < kSplitDepth; ++u) {
+      gload(u, r[u], tb[u], zr[u]);
+      tb[u] = tload(u + kSplitDepth);
+    }
+    stage(0, r[0], zr[0]);
     __syncthreads();
     for (int64_t k = 0; k < n_iter; k += kSplitDepth) {
 #pragma unroll
       for (int u = 0; u < kSplitDepth; ++u) {
         // r[u] held step k + u, staged before the previous barrier: refill it
-        // with step k + u + kSplitDepth, and stage step k + u + 1 (buffer
+        // with step k + u + kSplitDepth (whose block ids tb[u] were read
+        // with the previous refill), and stage step k + u + 1 (buffer
         // parity (u + 1) & 1, as k is even) before the barrier ending step k + u
-        gload(k + u + kSplitDepth, r[u]);
-        stage((u + 1) & 1, r[(u + 1) % kSplitDepth]);
+        gload(k + u + kSplitDepth, r[u], tb[u], zr[u]);
+        tb[u] = tload(k + u + 2 * kSplitDepth);
+        stage((u + 1) & 1, r[(u + 1) % kSplitDepth], zr[(u + 1) % kSplitDepth]);
         __syncthreads();
       }
     }
@@ -600,7 +706,7 @@ __global__ void __launch_bounds__(kIdxThreads) index_scores_f32(
     const float* __restrict__ q_idx, const float* __restrict__ w_idx,
     const float* __restrict__ k_idx, const int32_t* __restrict__ pos, int ratio, int Q, int Hi,
     int64_t Nmax, int64_t row_off, float* __restrict__ scores, int32_t* __restrict__ n_vis_out,
-    uint32_t* __restrict__ hist_g, int bf16_scores) {
+    uint32_t* __restrict__ hist_g, int bf16_scores, PageMap pm) {
   __shared__ float qs[128 * kIndexDim];
   __shared__ float ws[128];
   __shared__ uint32_t hist[kHistBins];
@@ -618,10 +724,12 @@ __global__ void __launch_bounds__(kIdxThreads) index_scores_f32(
   __syncthreads();
   const int64_t key = base + t;
   if (key < nv) {
-    const float* kr = k_idx + (b * Nmax + key) * kIndexDim;
+    // a key in an unallocated block of a block cache reads as zeros
+    const int64_t pr = pm.table ? paged_row(pm, b, key) : b * Nmax + key;
+    const float* kr = k_idx + (pr < 0 ? 0 : pr) * kIndexDim;
     float kv[kIndexDim];
 #pragma unroll
-    for (int c = 0; c < kIndexDim; ++c) kv[c] = kr[c];
+    for (int c = 0; c < kIndexDim; ++c) kv[c] = pr < 0 ? 0.f : kr[c];
     float p = 0.f;
     for (int h = 0; h < Hi; ++h) {
       float d = 0.f;
@@ -639,11 +747,12 @@ __global__ void __launch_bounds__(kIdxThreads) index_scores_f32(
     if (hist[i]) atomicAdd(&g[i], hist[i]);
 }
 
-template <int HT>
-hipError_t launch_mfma(const void* q_idx, const float* w_idx, const void* k_idx, int k_fmt,
-                       const int32_t* pos, int ratio, int Q, int64_t R, int64_t Nmax,
-                       float* scores, int32_t* n_vis, uint32_t* hist, int bf16s, hipStream_t s) {
-  if (k_fmt == CSA_BF16 && Q >= kQT) {
+template <int HT, bool PG>
+hipError_t launch_mfma_pg(const void* q_idx, const float* w_idx, const void* k_idx, int k_fmt,
+                          const int32_t* pos, int ratio, int Q, int64_t R, int64_t Nmax,
+                          float* scores, int32_t* n_vis, uint32_t* hist, int bf16s, PageMap pm,
+                          hipStream_t s) {
+  if (!PG && k_fmt == CSA_BF16 && Q >= kQT) {
     // even ranges of at most kQKeysPerWg keys, whole steps
     const int64_t splits = (Nmax + kQKeysPerWg - 1) / kQKeysPerWg;
     int64_t kpw = (Nmax + splits - 1) / splits;
@@ -666,10 +775,10 @@ hipError_t launch_mfma(const void* q_idx, const float* w_idx, const void* k_idx,
     gx = gx < 1 ? 1 : gx;
     for (int64_t r0 = 0; r0 < R; r0 += 65535) {
       int64_t nr = R - r0 < 65535 ? R - r0 : 65535;
-      hipLaunchKernelGGL((index_scores_split<HT>), dim3((unsigned)gx, (unsigned)nr),
+      hipLaunchKernelGGL((index_scores_split<HT, PG>), dim3((unsigned)gx, (unsigned)nr),
                          dim3(kSplitThreads), 0, s, (const uint16_t*)q_idx, w_idx,
                          (const uint8_t*)k_idx, pos, ratio, Q, Nmax, r0, scores, n_vis, hist,
-                         bf16s);
+                         bf16s, pm);
     }
     return hipGetLastError();
   }
@@ -679,17 +788,29 @@ hipError_t launch_mfma(const void* q_idx, const float* w_idx, const void* k_idx,
   for (int64_t r0 = 0; r0 < R; r0 += 65535) {
     int64_t nr = R - r0 < 65535 ? R - r0 : 65535;
     if (k_fmt == CSA_FP4_MX32)
-      hipLaunchKernelGGL((index_scores_mfma<HT, CSA_FP4_MX32>), dim3((unsigned)gx, (unsigned)nr),
+      hipLaunchKernelGGL((index_scores_mfma<HT, CSA_FP4_MX32, PG>), dim3((unsigned)gx, (unsigned)nr),
                          dim3(kIdxThreads), 0, s, (const uint16_t*)q_idx, w_idx,
                          (const uint8_t*)k_idx, pos, ratio, Q, Nmax, r0, scores, n_vis, hist,
-                         bf16s);
+                         bf16s, pm);
     else
-      hipLaunchKernelGGL((index_scores_mfma<HT, CSA_BF16>), dim3((unsigned)gx, (unsigned)nr),
+      hipLaunchKernelGGL((index_scores_mfma<HT, CSA_BF16, PG>), dim3((unsigned)gx, (unsigned)nr),
                          dim3(kIdxThreads), 0, s, (const uint16_t*)q_idx, w_idx,
                          (const uint8_t*)k_idx, pos, ratio, Q, Nmax, r0, scores, n_vis, hist,
-                         bf16s);
+                         bf16s, pm);
   }
   return hipGetLastError();
+}
+
+template <int HT>
+hipError_t launch_mfma(const void* q_idx, const float* w_idx, const void* k_idx, int k_fmt,
+                       const int32_t* pos, int ratio, int Q, int64_t R, int64_t Nmax,
+                       float* scores, int32_t* n_vis, uint32_t* hist, int bf16s, PageMap pm,
+                       hipStream_t s) {
+  if (pm.table)
+    return launch_mfma_pg<HT, true>(q_idx, w_idx, k_idx, k_fmt, pos, ratio, Q, R, Nmax, scores,
+                                    n_vis, hist, bf16s, pm, s);
+  return launch_mfma_pg<HT, false>(q_idx, w_idx, k_idx, k_fmt, pos, ratio, Q, R, Nmax, scores,
+                                   n_vis, hist, bf16s, pm, s);
 }
 
 }  // namespace
@@ -697,7 +818,7 @@ hipError_t launch_mfma(const void* q_idx, const float* w_idx, const void* k_idx,
 hipError_t launch_index_scores(const void* q_idx, int q_fmt, const float* w_idx,
                                const void* k_idx, int k_fmt, const int32_t* pos, int ratio, int B,
                                int Q, int Hi, int64_t Nmax, float* scores, int32_t* n_vis,
-                               TopkWs w, int bf16_scores, hipStream_t s) {
+                               TopkWs w, int bf16_scores, hipStream_t s, PageMap pm) {
   const int64_t R = (int64_t)B * Q;
   if (k_fmt == CSA_F32) {
     int64_t gx = (Nmax + kF32Keys - 1) / kF32Keys;
@@ -705,20 +826,20 @@ hipError_t launch_index_scores(const void* q_idx, int q_fmt, const float* w_idx,
       int64_t nr = R - r0 < 65535 ? R - r0 : 65535;
       hipLaunchKernelGGL(index_scores_f32, dim3((unsigned)gx, (unsigned)nr), dim3(kIdxThreads), 0,
                          s, (const float*)q_idx, w_idx, (const float*)k_idx, pos, ratio, Q, Hi,
-                         Nmax, r0, scores, n_vis, w.hist, bf16_scores);
+                         Nmax, r0, scores, n_vis, w.hist, bf16_scores, pm);
     }
     return hipGetLastError();
   }
   (void)q_fmt;
   switch (Hi / 16) {
-    case 1: return launch_mfma<1>(q_idx, w_idx, k_idx, k_fmt, pos, ratio, Q, R, Nmax, scores, n_vis, w.hist, bf16_scores, s);
-    case 2: return launch_mfma<2>(q_idx, w_idx, k_idx, k_fmt, pos, ratio, Q, R, Nmax, scores, n_vis, w.hist, bf16_scores, s);
-    case 3: return launch_mfma<3>(q_idx, w_idx, k_idx, k_fmt, pos, ratio, Q, R, Nmax, scores, n_vis, w.hist, bf16_scores, s);
-    case 4: return launch_mfma<4>(q_idx, w_idx, k_idx, k_fmt, pos, ratio, Q, R, Nmax, scores, n_vis, w.hist, bf16_scores, s);
-    case 5: return launch_mfma<5>(q_idx, w_idx, k_idx, k_fmt, pos, ratio, Q, R, Nmax, scores, n_vis, w.hist, bf16_scores, s);
-    case 6: return launch_mfma<6>(q_idx, w_idx, k_idx, k_fmt, pos, ratio, Q, R, Nmax, scores, n_vis, w.hist, bf16_scores, s);
-    case 7: return launch_mfma<7>(q_idx, w_idx, k_idx, k_fmt, pos, ratio, Q, R, Nmax, scores, n_vis, w.hist, bf16_scores, s);
-    case 8: return launch_mfma<8>(q_idx, w_idx, k_idx, k_fmt, pos, ratio, Q, R, Nmax, scores, n_vis, w.hist, bf16_scores, s);
+    case 1: return launch_mfma<1>(q_idx, w_idx, k_idx, k_fmt, pos, ratio, Q, R, Nmax, scores, n_vis, w.hist, bf16_scores, pm, s);
+    case 2: return launch_mfma<2>(q_idx, w_idx, k_idx, k_fmt, pos, ratio, Q, R, Nmax, scores, n_vis, w.hist, bf16_scores, pm, s);
+    case 3: return launch_mfma<3>(q_idx, w_idx, k_idx, k_fmt, pos, ratio, Q, R, Nmax, scores, n_vis, w.hist, bf16_scores, pm, s);
+    case 4: return launch_mfma<4>(q_idx, w_idx, k_idx, k_fmt, pos, ratio, Q, R, Nmax, scores, n_vis, w.hist, bf16_scores, pm, s);
+    case 5: return launch_mfma<5>(q_idx, w_idx, k_idx, k_fmt, pos, ratio, Q, R, Nmax, scores, n_vis, w.hist, bf16_scores, pm, s);
+    case 6: return launch_mfma<6>(q_idx, w_idx, k_idx, k_fmt, pos, ratio, Q, R, Nmax, scores, n_vis, w.hist, bf16_scores, pm, s);
+    case 7: return launch_mfma<7>(q_idx, w_idx, k_idx, k_fmt, pos, ratio, Q, R, Nmax, scores, n_vis, w.hist, bf16_scores, pm, s);
+    case 8: return launch_mfma<8>(q_idx, w_idx, k_idx, k_fmt, pos, ratio, Q, R, Nmax, scores, n_vis, w.hist, bf16_scores, pm, s);
     default: return hipErrorInvalidValue;
   }
 }

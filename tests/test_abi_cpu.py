@@ -217,3 +217,53 @@ def test_index_topk_noalloc_rejects_oversize_on_host():
     r = L.csa_index_topk_noalloc(A16, _lib.BF16, A16, A16, _lib.FP8_MX32, A16, 4, B, 1, Hi, N, k,
                                  A16, None, None)
     assert r == EWS and "scratch" in _detail()
+
+
+def test_block_cache_validation():
+    """Block-table descriptors and slot pools are checked on the host."""
+    L = _lib.lib()
+    ws = 1 << 30
+
+    def topk(be=32, maxb=100, pool=50, table=A16, kt=True, bf16=0):
+        t = _lib.BlockTable(table, maxb, be, pool)
+        return L.csa_index_topk_paged(A16, _lib.BF16, A16, A16, _lib.FP8_MX32,
+                                      ctypes.byref(t) if kt else None, A16, 4, 2, 1, 64, 512, bf16,
+                                      A16, None, A16, ws, None)
+
+    assert topk(kt=False) == EINVAL
+    assert topk(table=None) == EINVAL
+    assert topk(be=16) == EINVAL                      # index keys need >= 32 per block
+    assert topk(be=48) == EINVAL                      # not a power of two
+    assert topk(be=2048) == EINVAL
+    assert topk(maxb=0) == EINVAL
+    assert topk(pool=0) == EINVAL
+    assert topk(maxb=(1 << 30) // 32 + 1) == EINVAL   # logical capacity above 2^30
+    assert topk(bf16=2) == EINVAL
+    assert "block_entries" in (topk(be=16) and _detail())
+
+    def attn(be=32, pool=50, slot=A16, slots=16, B=8, hca=False):
+        t = _lib.BlockTable(A16, 100, be, pool)
+        if hca:
+            return L.hca_attn_decode_paged(A16, 1, A16, 2, slot, slots, A16, 2, ctypes.byref(t),
+                                           128, A16, B, 1, 64, A16, 0.044, A16, A16, 100, A16, 1,
+                                           A16, ws, None)
+        return L.csa_sparse_attn_decode_paged(A16, 1, A16, 2, slot, slots, A16, 2, ctypes.byref(t),
+                                              A16, 512, A16, B, 1, 64, A16, 0.044, A16, A16, 100,
+                                              A16, 1, A16, ws, None)
+
+    assert attn(slots=0) == EINVAL
+    assert attn(slot=None, slots=4, B=8) == EINVAL    # no slot map needs a slot per sequence
+    assert attn(be=3) == EINVAL
+    assert attn(be=1024, pool=(1 << 21) + 1) == EINVAL  # pool rows above 2^31 - 1
+    assert attn(hca=True, be=0) == EINVAL
+
+    a = _lib.CompressArgs(1, 4, 1024, 4, 512, 0, A16, 0, A16, A16, 0, A16, A16, 1e-6, A16, A16,
+                          100, A16, A16, A16, A16, 0, 0, A16, 8, 33, 4, None, 0)
+    assert L.csa_compress(ctypes.byref(a), A16, 1 << 20, None) == EINVAL  # 33 per block
+    a.block_entries = 32
+    a.entries = None
+    assert L.csa_compress(ctypes.byref(a), A16, 1 << 20, None) == EINVAL  # pool pointer
+    a.entries = A16
+    a.state_slot = A16
+    a.state_slots = 0
+    assert L.csa_compress(ctypes.byref(a), A16, 1 << 20, None) == EINVAL
