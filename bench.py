@@ -15,8 +15,14 @@ HIP events on the stream it runs on.  cpu_baseline times the float64 oracle
 (test infrastructure) on a bounded sample of the same workload.
 
   python bench.py [--steps K] [--warmup W] [--workload csa_1m_fp8|csa_1m_mxfp4|
-                  csa_64k_bf16|hca_1m_bf16|csa_prefill_32k_bf16] [--copies C]
-                  [--no-cpu-baseline]
+                  csa_1m_fp4idx|csa_1m_fp8_layer|csa_1m_fp8_paged|csa2_m1_256k|
+                  csa_64k_bf16|hca_1m_bf16|hca_1m_bf16_paged|csa_prefill_32k_bf16]
+                  [--copies C] [--no-cpu-baseline]
+
+The *_paged workloads run the same step from a block cache: entries and index
+keys in pools of blocks (32 CSA entries or 1 HCA entry per block) found
+through per-sequence block tables, windows and compressor slots in a pool of
+state slots.
 
 The chunked-prefill workload (32,768 new tokens on a 262,144-token prefix,
 batch 1) reports prefill tokens/s per layer; its roofline object is the
@@ -39,8 +45,8 @@ HBM_PEAK_GBS = 8000.0
 MFMA_BF16_PEAK_TFLOPS = 2500.0
 
 WORKLOADS = {"csa_1m_fp8": 5, "csa_1m_mxfp4": 5, "csa_1m_fp4idx": 5, "csa_1m_fp8_layer": 5,
-             "csa2_m1_256k": 6, "csa_64k_bf16": 2,
-             "hca_1m_bf16": 3, "csa_prefill_32k_bf16": 4}
+             "csa_1m_fp8_paged": 5, "csa2_m1_256k": 6, "csa_64k_bf16": 2,
+             "hca_1m_bf16": 3, "hca_1m_bf16_paged": 3, "csa_prefill_32k_bf16": 4}
 
 
 # the default workload's metric; the others name what they measure
@@ -54,6 +60,10 @@ METRICS = {
                         "window write and output projection included); achieved HBM GB/s vs peak",
     "csa2_m1_256k": "CSA2 m=1 layer-group decode tokens/s per layer at 256K ctx (6 layers sharing "
                     "main KV and top-512 ids); achieved HBM GB/s vs peak",
+    "csa_1m_fp8_paged": "CSA top-512 decode tokens/s per layer at 1M ctx from a block cache (32 "
+                        "entries per block, state slots); achieved HBM GB/s vs peak",
+    "hca_1m_bf16_paged": "HCA decode tokens/s per layer at 1M ctx (bf16 cache) from a block cache "
+                         "(1 entry per block, state slots); achieved HBM GB/s vs peak",
 }
 
 
@@ -104,6 +114,15 @@ def algorithmic_bytes(w):
         out["hca_attn_decode"] = B * (n_vis * row_bytes(w.ent_fmt, 512)
                                       + 128 * row_bytes(w.win_fmt, 512)
                                       + 2 * w.H * 512 * qb) + w.H * 4
+    pg = w.extra.get("paged")
+    if pg:  # block ids read through the tables (4 B each) and the slot map
+        bs = pg["block_entries"]
+        n_vis = min((w.t + 1) // w.ratio, N)
+        if w.ratio != 128:
+            out["csa_index_topk"] += B * (-(-n_vis // bs)) * 4
+            out["csa_sparse_attn_decode"] += B * (min(w.topk, n_vis) * 4 + 4)
+        else:
+            out["hca_attn_decode"] += B * (-(-n_vis // bs) * 4 + 4)
     return out
 
 
@@ -427,6 +446,8 @@ def main():
         w = synth.fp4_indexer_variant(w)
     if a.workload == "csa_1m_fp8_layer":
         w = synth.layer_variant(w)
+    if a.workload.endswith("_paged"):
+        w = synth.paged_variant(w)
     print(f"# building {a.workload}: B={w.B} ctx={w.ctx} entries={w.n_entries}", file=sys.stderr,
           flush=True)
     t0 = time.time()

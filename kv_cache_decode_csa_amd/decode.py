@@ -10,6 +10,13 @@ points in order; it computes nothing itself.  A CSA step at position t is:
 
 and an HCA step is csa_compress (ratio 128) followed by hca_attn_decode.
 
+With a block cache (workload extra "paged") the same steps run through the
+paged calls: entries and index keys sit in pools of blocks placed by a
+seeded permutation and found through block tables, and the window rings and
+compressor slots sit in a pool of state slots (csa_index_topk_paged,
+csa_sparse_attn_decode_paged, hca_attn_decode_paged; the compressors take
+the table and slot map in their arguments).
+
 With a layer configuration (workload extra "layer") the CSA step also runs
 the layer's steps on either side of the path: csa_layer_input first (query
 path, index queries and head weights, window-entry write, all from the
@@ -36,19 +43,55 @@ def _dev_rows(x, fmt, device):
     return out
 
 
+class BlockCache:
+    """Block tables and state slots of a paged workload: logical block j of
+    sequence b sits in pool block table[b][j] (a seeded permutation of all
+    blocks), and sequence b's window ring and compressor slots in state slot
+    slot[b] of a pool of n_slots."""
+
+    def __init__(self, w, device="cuda"):
+        cfg = w.extra["paged"]
+        self.bs = cfg["block_entries"]
+        self.n_slots = cfg["slots"]
+        assert w.n_entries % self.bs == 0
+        self.nb = w.n_entries // self.bs
+        g = torch.Generator().manual_seed(w.seed)
+        self.perm = torch.randperm(w.B * self.nb, generator=g).to(device)
+        self.table = self.perm.reshape(w.B, self.nb).to(torch.int32)
+        self.slot = torch.randperm(self.n_slots, generator=g)[:w.B].to(torch.int32).to(device)
+        self.bt = _lib.make_block_table(self.table, self.bs, w.B * self.nb)
+
+    def pool(self, rows):
+        """Logical rows [B, N, ...] -> the pool [blocks, bs, ...] they fill."""
+        B = rows.shape[0]
+        blocks = rows.reshape((B * self.nb, self.bs) + tuple(rows.shape[2:]))
+        out = torch.empty_like(blocks)
+        out[self.perm] = blocks
+        return out
+
+    def slots(self, rows):
+        """Per-sequence state [B, ...] -> the slot pool [n_slots, ...]."""
+        out = torch.zeros((self.n_slots,) + tuple(rows.shape[1:]), dtype=rows.dtype,
+                          device=rows.device)
+        out[self.slot.long()] = rows
+        return out
+
+
 class Compressor:
-    """Weights, slot state and output rows of one compressor on the device."""
+    """Weights, slot state and output rows of one compressor on the device
+    (with a BlockCache: `entries` is a block pool and the state a slot pool)."""
 
     def __init__(self, w, head_dim, ratio, rotate, entries, entry_fmt, rope, device="cuda",
-                 indexer=False):
+                 indexer=False, cache=None):
         wkv, wg, ape, norm = synth.compressor_weights(w, head_dim, ratio, indexer=indexer)
         dt = torch.bfloat16 if w.q_fmt == "bf16" else torch.float32
         self.wkv = torch.from_numpy(wkv).to(device).to(dt)
         self.wg = torch.from_numpy(wg).to(device).to(dt)
         self.ape = torch.from_numpy(ape).to(device)
         self.norm = torch.from_numpy(norm).to(device)
+        self.cache = cache
         coff = 2 if ratio == 4 else 1
-        shape = (w.B, coff * ratio, coff * head_dim)
+        shape = (w.B if cache is None else cache.n_slots, coff * ratio, coff * head_dim)
         self.kv = torch.zeros(shape, dtype=torch.float32, device=device)
         self.sc = torch.full(shape, float("-inf"), dtype=torch.float32, device=device)
         self.w, self.head_dim, self.ratio, self.rotate = w, head_dim, ratio, rotate
@@ -59,12 +102,16 @@ class Compressor:
 
     def args(self, x, start_pos):
         B, T = x.shape[0], x.shape[1]
-        return _lib.make_compress_args(
-            B=B, T=T, dim=self.w.dim, ratio=self.ratio, head_dim=self.head_dim,
-            rotate=self.rotate, x=x, x_fmt=self.x_fmt, w_kv=self.wkv, w_gate=self.wg,
-            w_fmt=self.x_fmt, ape=self.ape, norm_w=self.norm, eps=1e-6, rope_cos=self.cos,
-            rope_sin=self.sin, start_pos=start_pos, kv_state=self.kv, score_state=self.sc,
-            entries=self.entries, entry_fmt=self.entry_fmt, entries_cap=self.entries.shape[1])
+        kw = dict(B=B, T=T, dim=self.w.dim, ratio=self.ratio, head_dim=self.head_dim,
+                  rotate=self.rotate, x=x, x_fmt=self.x_fmt, w_kv=self.wkv, w_gate=self.wg,
+                  w_fmt=self.x_fmt, ape=self.ape, norm_w=self.norm, eps=1e-6, rope_cos=self.cos,
+                  rope_sin=self.sin, start_pos=start_pos, kv_state=self.kv, score_state=self.sc,
+                  entries=self.entries, entry_fmt=self.entry_fmt)
+        c = self.cache
+        if c is None:
+            return _lib.make_compress_args(**kw, entries_cap=self.entries.shape[1])
+        return _lib.make_compress_args(**kw, block_table=c.table, block_entries=c.bs,
+                                       pool_blocks=self.entries.shape[0], state_slot=c.slot)
 
     def __call__(self, x, start_pos):
         a = self.args(x, start_pos)
@@ -96,8 +143,14 @@ class CsaDecodeLayer:
         # lines from the 256 MB last-level cache
         ent = _dev_rows(synth.entries(w), w.ent_fmt, device)
         keys = _dev_rows(synth.index_keys(w), w.key_fmt, device)
-        self.sets = [(ent, keys)] + [(ent.clone(), keys.clone()) for _ in range(copies - 1)]
         self.win = _dev_rows(synth.window_rows(w), w.win_fmt, device)
+        self.cache = BlockCache(w, device) if w.extra.get("paged") else None
+        if self.cache is not None:
+            assert not w.extra.get("layer") and not w.extra.get("reuse"), \
+                "the block cache serves the path's calls only"
+            ent, keys = self.cache.pool(ent), self.cache.pool(keys)
+            self.win = self.cache.slots(self.win)
+        self.sets = [(ent, keys)] + [(ent.clone(), keys.clone()) for _ in range(copies - 1)]
         q, sink = synth.queries(w)
         qi, wi = synth.index_queries(w)
         qdt = torch.bfloat16 if w.q_fmt == "bf16" else torch.float32
@@ -126,8 +179,10 @@ class CsaDecodeLayer:
         for c in range(copies):
             ent, keys = self.sets[c]
             self.comp.append((
-                Compressor(w, 512, w.ratio, 0, ent, w.ent_fmt, self.rope, device),
-                Compressor(w, 128, w.ratio, 1, keys, w.key_fmt, self.rope, device, indexer=True)))
+                Compressor(w, 512, w.ratio, 0, ent, w.ent_fmt, self.rope, device,
+                           cache=self.cache),
+                Compressor(w, 128, w.ratio, 1, keys, w.key_fmt, self.rope, device, indexer=True,
+                           cache=self.cache)))
         # fill the compressor states from the tokens before t (positions t-7 .. t-1)
         if hidden_tail:
             tail = torch.from_numpy(synth.normal_batched(
@@ -217,6 +272,21 @@ class CsaDecodeLayer:
                                         1, w.H, self.sink, 512 ** -0.5, self.rope[0],
                                         self.rope[1], self.out, w.q_fmt, self.ws_att)
 
+        pc = self.cache
+        if pc is not None:
+            def index_topk():  # noqa: F811 -- the block-cache form of the same call
+                _lib.csa_index_topk_paged(self.qi, w.q_fmt, self.wi, keys, key_fmt, pc.bt,
+                                          self.pos, w.ratio, B, 1, w.Hi, w.topk,
+                                          int(key_fmt == "fp4_mx32"), self.topk, None,
+                                          self.ws_idx)
+
+            def sparse_attn():  # noqa: F811
+                _lib.csa_sparse_attn_decode_paged(self.q, w.q_fmt, self.win, win_fmt, pc.slot,
+                                                  pc.n_slots, ent, ent_fmt, pc.bt, self.topk,
+                                                  w.topk, self.pos, B, 1, w.H, self.sink,
+                                                  512 ** -0.5, self.rope[0], self.rope[1],
+                                                  self.out, w.q_fmt, self.ws_att)
+
         core = [("csa_compress", compress), ("csa_index_topk", index_topk),
                 ("csa_sparse_attn_decode", sparse_attn)]
         if self.reuse:
@@ -256,8 +326,12 @@ class HcaDecodeLayer:
         B, N = w.B, w.n_entries
         self.rope = rope_tables(w.ctx + 1, w.yarn, device)
         ent = _dev_rows(synth.entries(w), w.ent_fmt, device)
-        self.sets = [ent] + [ent.clone() for _ in range(copies - 1)]
         self.win = _dev_rows(synth.window_rows(w), w.win_fmt, device)
+        self.cache = BlockCache(w, device) if w.extra.get("paged") else None
+        if self.cache is not None:
+            ent = self.cache.pool(ent)
+            self.win = self.cache.slots(self.win)
+        self.sets = [ent] + [ent.clone() for _ in range(copies - 1)]
         q, sink = synth.queries(w)
         qdt = torch.bfloat16 if w.q_fmt == "bf16" else torch.float32
         self.q = torch.from_numpy(q).to(device).to(qdt).reshape(B, 1, w.H, 512)
@@ -269,7 +343,8 @@ class HcaDecodeLayer:
             synth.normal_batched(w.seed, synth.T_X, B, (1, w.dim))).to(device).to(qdt)
         self.out = torch.empty((B, 1, w.H, 512), dtype=qdt, device=device)
         self.ws_att = _lib.workspace(_lib.hca_attn_workspace_size(B, 1, w.H, N))
-        self.comp = [Compressor(w, 512, w.ratio, 0, e, w.ent_fmt, self.rope, device)
+        self.comp = [Compressor(w, 512, w.ratio, 0, e, w.ent_fmt, self.rope, device,
+                                cache=self.cache)
                      for e in self.sets]
         if hidden_tail:
             tail = torch.from_numpy(synth.normal_batched(
@@ -289,6 +364,13 @@ class HcaDecodeLayer:
             cm(self.x, self.start)
 
         def hca_attn():
+            pc = self.cache
+            if pc is not None:
+                _lib.hca_attn_decode_paged(self.q, w.q_fmt, self.win, w.win_fmt, pc.slot,
+                                           pc.n_slots, ent, w.ent_fmt, pc.bt, w.ratio, self.pos,
+                                           w.B, 1, w.H, self.sink, 512 ** -0.5, self.rope[0],
+                                           self.rope[1], self.out, w.q_fmt, self.ws_att)
+                return
             _lib.hca_attn_decode(self.q, w.q_fmt, self.win, w.win_fmt, _lib.WIN_RING128, None, 128,
                                  ent, w.ent_fmt, w.n_entries, w.ratio, self.pos, w.B, 1, w.H,
                                  self.sink, 512 ** -0.5, self.rope[0], self.rope[1], self.out,

@@ -109,6 +109,18 @@ def fp4_indexer_variant(w):
     return dataclasses.replace(w, name="csa_1m_fp4idx", key_fmt="fp4_mx32")
 
 
+def paged_variant(w):
+    """The same workload served from a block cache ("DeepSeek-V4 deep dive"
+    section 9.4): entries and index keys in a pool of blocks of one 128-token
+    block's worth (32 CSA entries, 1 HCA entry), placed by a seeded random
+    permutation and found through per-sequence block tables; window rings
+    and compressor slots in a pool of 2B state slots, B of them in use."""
+    import dataclasses
+    be = 128 // w.ratio
+    return dataclasses.replace(w, name=w.name + "_paged",
+                               extra=dict(w.extra, paged=dict(block_entries=be, slots=2 * w.B)))
+
+
 def rng(seed, tid, idx=0):
     return np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, tid, idx])))
 
