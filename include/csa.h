@@ -392,7 +392,7 @@ csa_status csa_index_topk_paged(const void* q_idx, int q_fmt, const float* w_idx
  * absent, like an id outside [0, Nmax).  Entry pools hold at most 2^31 - 1
  * rows (pool_blocks * block_entries).
  * Workspace: csa_sparse_attn_workspace_size(B, Q, H, topk) and
- * hca_attn_workspace_size(B, Q, H, Nmax).  Errors as for the contiguous
+ * hca_attn_workspace_size(B, Q, H, Nmax) (sized for either HCA call).  Errors as for the contiguous
  * calls, and CSA_EINVAL for a bad table descriptor.                       */
 csa_status csa_sparse_attn_decode_paged(const void* q, int q_fmt, const void* win_pool,
                                         int win_fmt, const int32_t* win_slot,

@@ -422,7 +422,12 @@ size_t hca_attn_workspace_size(int B, int Q, int H, int64_t Nmax) {
   if (B < 1 || Q < 1 || H < 16 || Nmax < 0) return 0;
   AttnArgs a{};
   a.B = B; a.Q = Q; a.H = H; a.Nmax = Nmax; a.q_fmt = CSA_BF16; a.ratio = 128; a.dense = 1;
-  return attn_ws_bytes(a);
+  const size_t plain = attn_ws_bytes(a);
+  // a paged list may be split into more chunks: enough for either call
+  static const int32_t kAnyTable = 0;
+  a.ent_pages = PageMap{&kAnyTable, 1, 1, 0};
+  const size_t paged = attn_ws_bytes(a);
+  return plain > paged ? plain : paged;
 }
 
 static csa_status run_attn(const AttnArgs& a, void* ws, size_t ws_bytes, hipStream_t s) {

@@ -46,6 +46,12 @@ struct RowRef {
   int fmt;
 };
 
+// Dense lists from a block cache: a work-group resolves its chunk's rows
+// through the block table once, into LDS (dynamic shared memory, 4 bytes per
+// row), so the row loads of the tile loop keep their usual depth.  Chunks of
+// paged dense lists never exceed this (the launcher picks the kernel so).
+constexpr int kPagedIdsMax = 2048;
+
 // The window of sequence b: b itself, or its state slot (-1 when the slot
 // lies outside the pool: the window rows are then absent).
 __device__ __forceinline__ int64_t win_seq(const AttnArgs& a, int64_t b) {
@@ -343,29 +349,19 @@ __device__ __forceinline__ void attend_tile(const uint4 (&fr)[2][4], uint32_t vm
 // Rows [j0, j1) of the list, all in format F.  Two register sets alternate:
 // while one tile is computed the next tile's rows are in flight.  Absent rows
 // (and rows past j1) are loaded from `stand_in`, a row of the same buffer, and
-// zeroed by the validity mask.  pre(j) reads a per-row token (a block id of a
-// block cache; a constant otherwise) that row_of(j, token) turns into the
-// row's address.  Tokens are read two tiles ahead, right after the loads of
-// the tile before, so that waiting for them never waits for a later tile.
-template <int F, class PreFn, class RowFn>
-__device__ __forceinline__ void run_rows(int64_t j0, int64_t j1, PreFn pre, RowFn row_of,
+// zeroed by the validity mask.
+template <int F, class RowFn>
+__device__ __forceinline__ void run_rows(int64_t j0, int64_t j1, RowFn row_of,
                                          const uint8_t* stand_in, const uint4 (&qa)[4],
                                          float zscale, int w, int lane, uint16_t* R,
                                          float4 (*Sp)[2][64], SoftmaxState& st) {
   const int r16 = lane & 15, kq = lane >> 4;
-  auto pre_tile = [&](int64_t jt, int32_t (&tk)[2]) {
-#pragma unroll
-    for (int rt = 0; rt < 2; ++rt) {
-      const int64_t j = jt + 16 * rt + r16;
-      tk[rt] = j < j1 ? pre(j) : 0;
-    }
-  };
-  auto load_tile = [&](int64_t jt, const int32_t (&tk)[2], Raw<F> (&f)[2], uint32_t& vm) {
+  auto load_tile = [&](int64_t jt, Raw<F> (&f)[2], uint32_t& vm) {
     vm = 0;
 #pragma unroll
     for (int rt = 0; rt < 2; ++rt) {
       const int64_t j = jt + 16 * rt + r16;
-      const uint8_t* p = j < j1 ? row_of(j, tk[rt]) : nullptr;
+      const uint8_t* p = j < j1 ? row_of(j) : nullptr;
       const unsigned long long bal = __ballot(p != nullptr);
       vm |= (uint32_t)(bal & 0xffffull) << (16 * rt);
       load_raw<F>(p ? p : stand_in, w, kq, f[rt]);
@@ -386,25 +382,26 @@ __device__ __forceinline__ void run_rows(int64_t j0, int64_t j1, PreFn pre, RowF
   };
   Raw<F> fa[2], fb[2];
   uint32_t va = 0, vb = 0;
-  int32_t ta[2], tb[2];  // tokens of the even / odd tiles
-  pre_tile(j0, ta);
-  load_tile(j0, ta, fa, va);
-  pre_tile(j0 + kTile, tb);
-  pre_tile(j0 + 2 * kTile, ta);
+  load_tile(j0, fa, va);
   for (int64_t jt = j0; jt < j1; jt += 2 * kTile) {
-    load_tile(jt + kTile, tb, fb, vb);
-    pre_tile(jt + 3 * kTile, tb);
+    load_tile(jt + kTile, fb, vb);
     compute_tile(fa, va);
-    load_tile(jt + 2 * kTile, ta, fa, va);
-    pre_tile(jt + 4 * kTile, ta);
+    load_tile(jt + 2 * kTile, fa, va);
     if (jt + kTile < j1) compute_tile(fb, vb);
   }
 }
 
-// No per-row token (contiguous rows, or addresses already resolved).
-struct NoToken {
-  __device__ __forceinline__ int32_t operator()(int64_t) const { return 0; }
-};
+// Pool rows of the dense chunk's entry rows [je, j_end) into ids[j - j_begin]
+// (-1 where absent), by the whole work-group; ends with a barrier.
+__device__ __forceinline__ void stage_paged_rows(const AttnArgs& a, int64_t be, int64_t j_begin,
+                                                 int64_t je, int64_t j_end, int64_t nvis,
+                                                 int32_t* ids) {
+  for (int64_t j = je + threadIdx.x; j < j_end; j += kAttnThreads) {
+    const int64_t e = j - kWindow;
+    ids[j - j_begin] = e < nvis ? (int32_t)paged_row(a.ent_pages, be, e) : -1;
+  }
+  __syncthreads();
+}
 
 // Query slices for one wave: head tile ht of the work-group, dims
 // 128 w + 32 s + 8 kq .. +8, with the last 64 dims rotated at row rr.  Every
@@ -638,24 +635,14 @@ __global__ void __launch_bounds__(kAttnThreads, HT <= 2 ? 2 : 1) attn_dense_all_
     for (int dt = 0; dt < 8; ++dt) o[ht][dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   uint16_t* R = Rl[w];
 
-  // as run_rows: pre(j) reads a per-row token two tiles ahead, row_of(j, token)
-  // gives the row's address
-  auto run = [&](auto fmt_tag, int64_t j0, int64_t j1, auto pre, auto row_of,
-                 const uint8_t* stand_in) {
+  auto run = [&](auto fmt_tag, int64_t j0, int64_t j1, auto row_of, const uint8_t* stand_in) {
     constexpr int F = decltype(fmt_tag)::value;
-    auto pre_tile = [&](int64_t jt, int32_t (&tk)[2]) {
-#pragma unroll
-      for (int rt = 0; rt < 2; ++rt) {
-        const int64_t j = jt + 16 * rt + r16;
-        tk[rt] = j < j1 ? pre(j) : 0;
-      }
-    };
-    auto load_tile = [&](int64_t jt, const int32_t (&tk)[2], Raw<F> (&f)[2], uint32_t& vm) {
+    auto load_tile = [&](int64_t jt, Raw<F> (&f)[2], uint32_t& vm) {
       vm = 0;
 #pragma unroll
       for (int rt = 0; rt < 2; ++rt) {
         const int64_t j = jt + 16 * rt + r16;
-        const uint8_t* p = j < j1 ? row_of(j, tk[rt]) : nullptr;
+        const uint8_t* p = j < j1 ? row_of(j) : nullptr;
         const unsigned long long bal = __ballot(p != nullptr);
         vm |= (uint32_t)(bal & 0xffffull) << (16 * rt);
         load_raw<F>(p ? p : stand_in, w, kq, f[rt]);
@@ -676,17 +663,11 @@ __global__ void __launch_bounds__(kAttnThreads, HT <= 2 ? 2 : 1) attn_dense_all_
     };
     Raw<F> fa[2], fb[2];
     uint32_t va = 0, vb = 0;
-    int32_t ta[2], tb[2];
-    pre_tile(j0, ta);
-    load_tile(j0, ta, fa, va);
-    pre_tile(j0 + kTile, tb);
-    pre_tile(j0 + 2 * kTile, ta);
+    load_tile(j0, fa, va);
     for (int64_t jt = j0; jt < j1; jt += 2 * kTile) {
-      load_tile(jt + kTile, tb, fb, vb);
-      pre_tile(jt + 3 * kTile, tb);
+      load_tile(jt + kTile, fb, vb);
       compute_tile(fa, va);
-      load_tile(jt + 2 * kTile, ta, fa, va);
-      pre_tile(jt + 4 * kTile, ta);
+      load_tile(jt + 2 * kTile, fa, va);
       if (jt + kTile < j1) compute_tile(fb, vb);
     }
   };
@@ -694,43 +675,31 @@ __global__ void __launch_bounds__(kAttnThreads, HT <= 2 ? 2 : 1) attn_dense_all_
   // window rows [j_begin, min(j_end, 128))
   const int64_t jw = j_end < kWindow ? j_end : kWindow;
   if (j_begin < jw) {
-    auto win_row = [&](int64_t j, int32_t) -> const uint8_t* {
+    auto win_row = [&](int64_t j) -> const uint8_t* {
       return resolve_row(a, unit, b, wsq, t, j, nvis, a.win_rb, a.ent_rb).p;
     };
     const uint8_t* win0 =
         (const uint8_t*)a.win + (size_t)(wsq < 0 ? 0 : wsq) * (size_t)a.win_rows * a.win_rb;
-    run(std::integral_constant<int, WF>{}, j_begin, jw, NoToken{}, win_row, win0);
+    run(std::integral_constant<int, WF>{}, j_begin, jw, win_row, win0);
   }
   // entry rows [max(j_begin, 128), j_end)
   const int64_t je = j_begin > kWindow ? j_begin : kWindow;
   if (je < j_end && a.Nmax > 0) {
     const uint8_t* ebase = ent_base(a, be);
-    if (!SPARSE && a.ent_pages.table) {
-      // block cache: the token is the row's block id
-      const PageMap pm = a.ent_pages;
-      const int64_t mask = ((int64_t)1 << pm.shift) - 1;
-      auto pre = [&](int64_t j) -> int32_t {
-        const int64_t e = j - kWindow;
-        return e < nvis ? pm.table[be * pm.max_blocks + (e >> pm.shift)] : -1;
-      };
-      auto ent_row = [&](int64_t j, int32_t blk) -> const uint8_t* {
-        const int64_t e = j - kWindow;
-        return (e < nvis && blk >= 0 && blk < pm.pool_blocks)
-                   ? ebase + (size_t)((((int64_t)blk) << pm.shift) + (e & mask)) * a.ent_rb
-                   : nullptr;
-      };
-      run(std::integral_constant<int, EF>{}, je, j_end, pre, ent_row, ebase);
-    } else {
-      auto ent_row = [&](int64_t j, int32_t) -> const uint8_t* {
-        if (SPARSE) {
-          const int32_t e = Ids[j - j_begin];
-          return e >= 0 ? ebase + (size_t)e * a.ent_rb : nullptr;
-        }
-        const int64_t e = j - kWindow;
-        return e < nvis ? ebase + (size_t)e * a.ent_rb : nullptr;
-      };
-      run(std::integral_constant<int, EF>{}, je, j_end, NoToken{}, ent_row, ebase);
-    }
+    // a dense list from a block cache: the chunk's pool rows, staged in LDS
+    extern __shared__ int32_t PgIds[];
+    const bool pg = !SPARSE && a.ent_pages.table != nullptr;
+    if (pg) stage_paged_rows(a, be, j_begin, je, j_end, nvis, PgIds);
+    auto ent_row = [&](int64_t j) -> const uint8_t* {
+      if (SPARSE) {
+        const int32_t e = Ids[j - j_begin];
+        return e >= 0 ? ebase + (size_t)e * a.ent_rb : nullptr;
+      }
+      const int64_t e = j - kWindow;
+      const int64_t r = pg ? (int64_t)PgIds[j - j_begin] : (e < nvis ? e : -1);
+      return r >= 0 ? ebase + (size_t)r * a.ent_rb : nullptr;
+    };
+    run(std::integral_constant<int, EF>{}, je, j_end, ent_row, ebase);
   }
 
   if (SPARSE && nchunks == 1) {
@@ -889,40 +858,30 @@ __global__ void __launch_bounds__(kAttnThreads) attn_mfma_kernel(AttnArgs a, int
   // window rows [j_begin, min(j_end, 128))
   const int64_t jw = j_end < kWindow ? j_end : kWindow;
   if (j_begin < jw) {
-    auto win_row = [&](int64_t j, int32_t) -> const uint8_t* {
+    auto win_row = [&](int64_t j) -> const uint8_t* {
       return resolve_row(a, unit, b, wsq, t, j, nvis, a.win_rb, a.ent_rb).p;
     };
     const uint8_t* win0 =
         (const uint8_t*)a.win + (size_t)(wsq < 0 ? 0 : wsq) * (size_t)a.win_rows * a.win_rb;
-    run_rows<WF>(j_begin, jw, NoToken{}, win_row, win0, qa, zscale, w, lane, R, Sp, st);
+    run_rows<WF>(j_begin, jw, win_row, win0, qa, zscale, w, lane, R, Sp, st);
   }
   // entry rows [max(j_begin, 128), j_end)
   const int64_t je = j_begin > kWindow ? j_begin : kWindow;
   if (je < j_end && a.Nmax > 0) {
     const uint8_t* ebase = ent_base(a, be);
-    if (a.dense && a.ent_pages.table) {
-      // block cache: the token is the row's block id
-      const PageMap pm = a.ent_pages;
-      const int64_t mask = ((int64_t)1 << pm.shift) - 1;
-      auto pre = [&](int64_t j) -> int32_t {
+    if (a.dense) {
+      // a dense list from a block cache: the chunk's pool rows, staged in LDS
+      extern __shared__ int32_t PgIds[];
+      const bool pg = a.ent_pages.table != nullptr;
+      if (pg) stage_paged_rows(a, be, j_begin, je, j_end, nvis, PgIds);
+      auto ent_row = [&](int64_t j) -> const uint8_t* {
         const int64_t e = j - kWindow;
-        return e < nvis ? pm.table[be * pm.max_blocks + (e >> pm.shift)] : -1;
+        const int64_t r = pg ? (int64_t)PgIds[j - j_begin] : (e < nvis ? e : -1);
+        return r >= 0 ? ebase + (size_t)r * a.ent_rb : nullptr;
       };
-      auto ent_row = [&](int64_t j, int32_t blk) -> const uint8_t* {
-        const int64_t e = j - kWindow;
-        return (e < nvis && blk >= 0 && blk < pm.pool_blocks)
-                   ? ebase + (size_t)((((int64_t)blk) << pm.shift) + (e & mask)) * a.ent_rb
-                   : nullptr;
-      };
-      run_rows<EF>(je, j_end, pre, ent_row, ebase, qa, zscale, w, lane, R, Sp, st);
-    } else if (a.dense) {
-      auto ent_row = [&](int64_t j, int32_t) -> const uint8_t* {
-        const int64_t e = j - kWindow;
-        return e < nvis ? ebase + (size_t)e * a.ent_rb : nullptr;
-      };
-      run_rows<EF>(je, j_end, NoToken{}, ent_row, ebase, qa, zscale, w, lane, R, Sp, st);
+      run_rows<EF>(je, j_end, ent_row, ebase, qa, zscale, w, lane, R, Sp, st);
     } else {
-      auto ent_row = [&](int64_t j, int32_t) -> const uint8_t* {
+      auto ent_row = [&](int64_t j) -> const uint8_t* {
         int32_t e = -1;
         if (LONG) {
           e = Ids[j - j_begin];
@@ -935,7 +894,7 @@ __global__ void __launch_bounds__(kAttnThreads) attn_mfma_kernel(AttnArgs a, int
         }
         return e >= 0 ? ebase + (size_t)e * a.ent_rb : nullptr;
       };
-      run_rows<EF>(je, j_end, NoToken{}, ent_row, ebase, qa, zscale, w, lane, R, Sp, st);
+      run_rows<EF>(je, j_end, ent_row, ebase, qa, zscale, w, lane, R, Sp, st);
     }
   }
 
@@ -1140,20 +1099,30 @@ constexpr int kSparseHsplit = 2;
 static bool attn_sparse_all_heads(const AttnArgs& a) {
   return attn_long_chunks(a) && a.H == 64;
 }
-static bool attn_all_heads(const AttnArgs& a) {
-  return (a.dense && a.H <= 64 && a.q_fmt != CSA_F32) || attn_sparse_all_heads(a);
-}
-
 int64_t attn_list_len(const AttnArgs& a) {
   return kWindow + (a.dense ? a.Nmax : (int64_t)a.topk);
+}
+
+// Rows per chunk of a dense list in the all-heads kernel: at least
+// kChunkDense, at most kMergeChunks chunks per list.
+static int64_t dense_all_chunk_rows(const AttnArgs& a) {
+  const int64_t per = (attn_list_len(a) + kMergeChunks - 1) / kMergeChunks;
+  const int64_t cr = (per + kTile - 1) / kTile * kTile;
+  return cr > kChunkDense ? cr : kChunkDense;
+}
+
+// A paged dense list takes the all-heads kernel only while its chunks fit
+// the LDS row staging; longer ones take the head-group kernel's 1024-row chunks.
+static bool attn_all_heads(const AttnArgs& a) {
+  if (a.dense && a.H <= 64 && a.q_fmt != CSA_F32)
+    return !a.ent_pages.table || dense_all_chunk_rows(a) <= kPagedIdsMax;
+  return attn_sparse_all_heads(a);
 }
 
 int attn_chunk_rows(const AttnArgs& a) {
   if (attn_long_chunks(a)) return kChunkCsaLong;
   if (!attn_all_heads(a)) return a.dense ? kChunkHca : kChunkCsa;
-  const int64_t per = (attn_list_len(a) + kMergeChunks - 1) / kMergeChunks;
-  const int64_t cr = (per + kTile - 1) / kTile * kTile;
-  return (int)(cr > kChunkDense ? cr : kChunkDense);
+  return (int)dense_all_chunk_rows(a);
 }
 
 static int attn_nchunks(const AttnArgs& a) {
@@ -1169,18 +1138,24 @@ size_t attn_ws_bytes(const AttnArgs& a) {
   return (size_t)a.B * a.Q * (a.H / 16) * nc * sizeof(Partial);
 }
 
+// Dynamic LDS of a launch: the paged dense chunk's pool rows.
+static size_t attn_dyn_lds(const AttnArgs& a, int cr) {
+  return (a.dense && a.ent_pages.table) ? (size_t)cr * sizeof(int32_t) : 0;
+}
+
 template <int WF, bool LONG>
 static void launch_mfma_wl(const AttnArgs& a, int nc, int64_t nu, dim3 grid, Partial* part,
                            hipStream_t s) {
   const int cr = attn_chunk_rows(a);
+  const size_t lds = attn_dyn_lds(a, cr);
   if (a.ent_fmt == CSA_BF16)
-    hipLaunchKernelGGL((attn_mfma_kernel<WF, CSA_BF16, LONG>), grid, dim3(kAttnThreads), 0, s, a, cr, nc, nu, part);
+    hipLaunchKernelGGL((attn_mfma_kernel<WF, CSA_BF16, LONG>), grid, dim3(kAttnThreads), lds, s, a, cr, nc, nu, part);
   else if (a.ent_fmt == CSA_FP8_MX32)
-    hipLaunchKernelGGL((attn_mfma_kernel<WF, CSA_FP8_MX32, LONG>), grid, dim3(kAttnThreads), 0, s, a, cr, nc, nu, part);
+    hipLaunchKernelGGL((attn_mfma_kernel<WF, CSA_FP8_MX32, LONG>), grid, dim3(kAttnThreads), lds, s, a, cr, nc, nu, part);
   else if (a.ent_fmt == CSA_MIX576)
-    hipLaunchKernelGGL((attn_mfma_kernel<WF, CSA_MIX576, LONG>), grid, dim3(kAttnThreads), 0, s, a, cr, nc, nu, part);
+    hipLaunchKernelGGL((attn_mfma_kernel<WF, CSA_MIX576, LONG>), grid, dim3(kAttnThreads), lds, s, a, cr, nc, nu, part);
   else
-    hipLaunchKernelGGL((attn_mfma_kernel<WF, CSA_FP4_E4M3_16, LONG>), grid, dim3(kAttnThreads), 0, s, a, cr, nc, nu, part);
+    hipLaunchKernelGGL((attn_mfma_kernel<WF, CSA_FP4_E4M3_16, LONG>), grid, dim3(kAttnThreads), lds, s, a, cr, nc, nu, part);
 }
 
 template <int WF>
@@ -1214,12 +1189,13 @@ static void launch_all_heads_e(const AttnArgs& a, int nc, int64_t nu, Partial* p
   const int hsplit = (G % 2 == 0 && items < kDenseSplitBelow) ? 2 : 1;
   const int HT = G / hsplit;
   const int cr = attn_chunk_rows(a);
+  const size_t lds = attn_dyn_lds(a, cr);
   const dim3 grid((unsigned)(hsplit == 1 ? items : (items + 7) / 8 * 8 * hsplit));
   switch (HT) {
-    case 1: hipLaunchKernelGGL((attn_dense_all_kernel<WF, EF, 1>), grid, dim3(kAttnThreads), 0, s, a, cr, nc, nu, hsplit, part); break;
-    case 2: hipLaunchKernelGGL((attn_dense_all_kernel<WF, EF, 2>), grid, dim3(kAttnThreads), 0, s, a, cr, nc, nu, hsplit, part); break;
-    case 3: hipLaunchKernelGGL((attn_dense_all_kernel<WF, EF, 3>), grid, dim3(kAttnThreads), 0, s, a, cr, nc, nu, hsplit, part); break;
-    default: hipLaunchKernelGGL((attn_dense_all_kernel<WF, EF, 4>), grid, dim3(kAttnThreads), 0, s, a, cr, nc, nu, hsplit, part); break;
+    case 1: hipLaunchKernelGGL((attn_dense_all_kernel<WF, EF, 1>), grid, dim3(kAttnThreads), lds, s, a, cr, nc, nu, hsplit, part); break;
+    case 2: hipLaunchKernelGGL((attn_dense_all_kernel<WF, EF, 2>), grid, dim3(kAttnThreads), lds, s, a, cr, nc, nu, hsplit, part); break;
+    case 3: hipLaunchKernelGGL((attn_dense_all_kernel<WF, EF, 3>), grid, dim3(kAttnThreads), lds, s, a, cr, nc, nu, hsplit, part); break;
+    default: hipLaunchKernelGGL((attn_dense_all_kernel<WF, EF, 4>), grid, dim3(kAttnThreads), lds, s, a, cr, nc, nu, hsplit, part); break;
   }
 }
 
@@ -1253,6 +1229,9 @@ hipError_t launch_attention(const AttnArgs& a0, void* ws, hipStream_t s) {
   a.ent_rb = kv_row_bytes(a.ent_fmt, kHeadDim);
   const int64_t units = (int64_t)a.B * a.Q;
   const int nc = attn_nchunks(a);
+  static_assert(kChunkHca <= kPagedIdsMax, "paged dense chunks are staged in LDS");
+  if (a.q_fmt != CSA_F32 && a.dense && a.ent_pages.table && attn_chunk_rows(a) > kPagedIdsMax)
+    return hipErrorInvalidConfiguration;
   // units per launch: at most 65535 (grid y of the merge) and few enough that
   // the 1-D MFMA grid stays below 2^32 work-items
   const int64_t max_items = (((int64_t)1 << 32) - 1) / ((int64_t)kAttnThreads * (a.H / 16)) - 8;
