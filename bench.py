@@ -322,17 +322,40 @@ def time_phases(layer, steps, torch):
     return {k: float(np.mean(v)) for k, v in acc.items()}
 
 
-def cpu_baseline(w, n_seq, min_seconds=10.0):
-    """The oracle on n_seq sequences of the workload: decode the stored index
-    keys, score, select, gather and attend (untimed: building the stored
-    bytes with the oracle's codec).  The timed part is repeated over the same
-    sequences until it has run for at least min_seconds."""
+def _blas_threads():
+    """Threads of the BLAS library NumPy calls (threadpoolctl), else the
+    affinity count."""
+    try:
+        from threadpoolctl import threadpool_info
+        n = [i["num_threads"] for i in threadpool_info() if i.get("user_api") == "blas"]
+        if n:
+            return max(n)
+    except ImportError:
+        pass
+    return len(os.sched_getaffinity(0))
+
+
+def cpu_baseline(w, n_seq=None, min_seconds=10.0):
+    """The oracle on n_seq sequences of the workload (default: the whole
+    batch) for one decode step each: the compressors on the new token (main
+    KV and, for CSA, index keys, continuing a state built from the 7 tokens
+    before it), decoding the stored index keys, scoring, top-k, decoding the
+    selected rows and the window, attention.  Building the stored bytes with
+    the oracle's codec and the compressor states is not timed.  The timed part
+    is repeated over the same sequences until it has run for at least
+    min_seconds; then one sequence's step is timed again with the BLAS pool
+    held to a single thread."""
     from kv_cache_decode_csa_amd import synth
-    from oracle import attention, codec, indexer, rope
+    from oracle import attention, codec, compressor, indexer, rope
     from oracle import topk as TK
+    n_seq = w.B if n_seq is None else min(n_seq, w.B)
     om = rope.frequencies(160000.0, rope.V4_YARN if w.yarn else None)
-    threads = os.environ.get("OMP_NUM_THREADS") or str(len(os.sched_getaffinity(0)))
-    t_total = 0.0
+    t = w.t
+    tail = 7
+    comps = [(512, 0, False)] + ([(128, 1, True)] if w.ratio != 128 else [])
+    cw = {d: tuple(np.asarray(a, np.float64) for a in synth.compressor_weights(w, d, w.ratio,
+                                                                              indexer=ix))
+          for d, _, ix in comps}
     prepared = []
     for b in range(n_seq):
         br = [b]
@@ -349,8 +372,16 @@ def cpu_baseline(w, n_seq, min_seconds=10.0):
                  for layer in range(1, w.extra.get("reuse", 0) + 1)]
         reuse = [(rq[0].astype(np.float64), rs, codec.store(rw[0], w.win_fmt)[0])
                  for rq, rs, rw in reuse]
-        prepared.append((q, sink, win_st, ent, keys_st, qi, wi, reuse))
-    t = w.t
+        x = synth.normal_batched(w.seed, synth.T_X, w.B, (1, w.dim), b_range=br)[0]
+        xt = synth.normal_batched(w.seed, synth.T_XTAIL, w.B, (tail, w.dim), b_range=br)[0]
+        states = {}
+        for d, rot, _ in comps:
+            wkv, wg, ape, nw = cw[d]
+            _, states[d] = compressor.compress_stream(
+                np.asarray(xt, np.float64), t - tail, wkv, wg, ape, nw, om, w.ratio, d,
+                rotate=bool(rot))
+        prepared.append((q, sink, win_st, ent, keys_st, qi, wi, reuse,
+                         np.asarray(x, np.float64), states))
     cfg = w.extra.get("layer")
     if cfg:  # the layer's input and output steps are timed too
         from oracle import layer as OL
@@ -358,47 +389,73 @@ def cpu_baseline(w, n_seq, min_seconds=10.0):
             w.seed, w.dim, cfg["q_rank"], w.H, w.Hi, cfg["groups"], cfg["o_rank"]).items()}
         lw.update(H=w.H, Hi=w.Hi)
         xs = [synth.hidden(w, 1, idx=b)[0].astype(np.float64) for b in range(n_seq)]
-    passes = 0
+
+    def one(si):
+        """One sequence's decode step; returns its timed seconds."""
+        q, sink, win_st, ent, keys_st, qi, wi, reuse, x, states = prepared[si]
+        dt = 0.0
+        t0 = time.perf_counter()
+        if cfg:
+            OL.layer_input(xs[si], t, lw, om)
+        for d, rot, _ in comps:
+            wkv, wg, ape, nw = cw[d]
+            compressor.compress_stream(x, t, wkv, wg, ape, nw, om, w.ratio, d, rotate=bool(rot),
+                                       state=states[d])
+        if w.ratio != 128:
+            K = codec.load(keys_st, w.key_fmt, 128)
+            nv = int(indexer.n_visible(t, w.ratio, w.n_entries))
+            S = indexer.scores(qi[0].astype(np.float64), wi[0], K, nv)
+            ids = TK.topk(S.astype(np.float32), w.topk, nv)
+            dt += time.perf_counter() - t0
+            rows_st = codec.store(ent[np.maximum(ids, 0)], w.ent_fmt)[0]  # stored rows read
+        else:
+            dt += time.perf_counter() - t0
+            ids = attention.hca_ids(t, w.ratio, w.n_entries)
+            rows_st = codec.store(ent[ids], w.ent_fmt)[0]
+        t0 = time.perf_counter()
+        E = codec.load(rows_st, w.ent_fmt, 512)
+        Wv = codec.load(win_st, w.win_fmt, 512)
+        wid = attention.window_ids(t)
+        rows = np.concatenate([Wv[np.maximum(wid, 0)], E])
+        valid = np.concatenate([wid >= 0, ids >= 0])
+        o = attention.attend(q[0].astype(np.float64), rows, valid, sink, 512 ** -0.5, t, om)
+        if cfg:
+            OL.output_projection(o, lw["wo_a"], lw["wo_b"])
+        for rq, rs, rw_st in reuse:  # reuse layers: their own q and window
+            Rv = codec.load(rw_st, w.win_fmt, 512)
+            rows = np.concatenate([Rv[np.maximum(wid, 0)], E])
+            attention.attend(rq, rows, valid, rs, 512 ** -0.5, t, om)
+        return dt + time.perf_counter() - t0
+
+    threads = _blas_threads()
+    t_total, passes = 0.0, 0
     while t_total < min_seconds and passes < 50:
         passes += 1
-        for si, (q, sink, win_st, ent, keys_st, qi, wi, reuse) in enumerate(prepared):
-            if cfg:
-                t0 = time.perf_counter()
-                OL.layer_input(xs[si], t, lw, om)
-                t_total += time.perf_counter() - t0
-            if w.ratio != 128:
-                t0 = time.perf_counter()
-                K = codec.load(keys_st, w.key_fmt, 128)
-                nv = int(indexer.n_visible(t, w.ratio, w.n_entries))
-                S = indexer.scores(qi[0].astype(np.float64), wi[0], K, nv)
-                ids = TK.topk(S.astype(np.float32), w.topk, nv)
-                t_total += time.perf_counter() - t0
-                rows_st = codec.store(ent[np.maximum(ids, 0)], w.ent_fmt)[0]  # stored rows read
-            else:
-                ids = attention.hca_ids(t, w.ratio, w.n_entries)
-                rows_st = codec.store(ent[ids], w.ent_fmt)[0]
-            t0 = time.perf_counter()
-            E = codec.load(rows_st, w.ent_fmt, 512)
-            Wv = codec.load(win_st, w.win_fmt, 512)
-            wid = attention.window_ids(t)
-            rows = np.concatenate([Wv[np.maximum(wid, 0)], E])
-            valid = np.concatenate([wid >= 0, ids >= 0])
-            o = attention.attend(q[0].astype(np.float64), rows, valid, sink, 512 ** -0.5, t, om)
-            if cfg:
-                OL.output_projection(o, lw["wo_a"], lw["wo_b"])
-            for rq, rs, rw_st in reuse:  # reuse layers: their own q and window
-                Rv = codec.load(rw_st, w.win_fmt, 512)
-                rows = np.concatenate([Rv[np.maximum(wid, 0)], E])
-                attention.attend(rq, rows, valid, rs, 512 ** -0.5, t, om)
-            t_total += time.perf_counter() - t0
-    n_tok = passes * n_seq * (1 + len(prepared[0][7]))
+        for si in range(n_seq):
+            t_total += one(si)
+    single = None
+    try:
+        from threadpoolctl import threadpool_limits
+        with threadpool_limits(limits=1, user_api="blas"):
+            single = one(0)
+    except ImportError:
+        pass
+    layers = 1 + len(prepared[0][7])
+    n_tok = passes * n_seq * layers
+    timed = ("compressors (main KV" + (" and index keys" if w.ratio != 128 else "") + "), "
+             + ("layer input steps, " if cfg else "")
+             + ("key decode, scoring, top-k, " if w.ratio != 128 else "")
+             + "row decode and attention" + (", output projection" if cfg else ""))
+    scope = ("the whole batch" if n_seq == w.B else f"{n_seq} of {w.B} sequences")
     return {"value": n_tok / t_total, "unit": "tokens/s/layer", "cores": int(threads),
             "kind": "oracle",
-            "sample": f"{n_seq} of {w.B} sequences of the same workload at full context "
-                      f"({w.n_entries} entries each), {passes} passes ({n_tok} layer-token steps); "
-                      f"timed: {'layer input steps, ' if cfg else ''}key decode, scoring, "
-                      f"top-k, row decode and attention{', output projection' if cfg else ''} "
-                      f"in float64 NumPy, {t_total:.1f} s"}
+            "blas_threads": int(threads),
+            "seconds_per_step_whole_batch": t_total / passes * (w.B / n_seq),
+            "single_thread_seconds_one_sequence": single,
+            "sample": f"{scope} of the same workload at full context ({w.n_entries} entries "
+                      f"each), {passes} passes ({n_tok} layer-token steps); timed: {timed} in "
+                      f"float64 NumPy with {threads} BLAS threads, {t_total:.1f} s; then one "
+                      f"sequence's step on one thread"}
 
 
 def main():
@@ -411,7 +468,8 @@ def main():
                     help="independent cache copies rotated per step (default: at least 4 and "
                          "at least 1 GB of step reads in all, so that no step finds the cache "
                          "lines of an earlier step in the 256 MB last-level cache)")
-    ap.add_argument("--cpu-seqs", type=int, default=2)
+    ap.add_argument("--cpu-seqs", type=int, default=None,
+                    help="sequences the oracle baseline times (default: the whole batch)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-flush", action="store_true",
                     help="skip the flushed-cache steps (kernel-trace runs: their averages then "

@@ -89,3 +89,16 @@ def test_multi_gpu_is_refused():
                        capture_output=True, text=True, timeout=120)
     assert r.returncode == 2
     assert "one GPU" in r.stderr
+
+
+def test_cpu_baseline_runs_whole_batch_and_single_thread():
+    """The oracle baseline times the whole batch by default, including the
+    compressors, and reports the BLAS thread count and a single-thread time
+    for one sequence (tiny fp32 workload, CPU)."""
+    import bench
+    w = synth.WORKLOADS[1]
+    r = bench.cpu_baseline(w, min_seconds=0.01)
+    assert r["kind"] == "oracle" and r["value"] > 0
+    assert r["blas_threads"] >= 1 and r["cores"] == r["blas_threads"]
+    assert r["single_thread_seconds_one_sequence"] > 0
+    assert "compressors" in r["sample"] and "the whole batch" in r["sample"]
