@@ -162,9 +162,10 @@ __device__ __forceinline__ void wave_lds_sync() {
 // data of one step's tiles (get(nt, f)), forms the 16 heads x 16 keys MFMA
 // products of every head tile, applies ReLU and the head weights, adds up the
 // heads and records the step's scores.
-template <int HT, int KFMT>
+template <int HT, int KFMT, int TILES = tiles_per_iter<KFMT>()>
 struct Scorer {
-  static constexpr int kTiles = tiles_per_iter<KFMT>();
+  static constexpr int kTiles = TILES;
+  static_assert(TILES == 2 || TILES == 4, "a step is two or four 16-key tiles");
   uint4 qa[HT][4];  // A operand: head 16 mt + r16, dims 32 kq + 8 s .. +8
   float wv[HT][4];  // head weights in the D layout: head 16 mt + 4 kq + r
   int r16, kq;
@@ -426,34 +427,54 @@ __global__ void __launch_bounds__(kIdxThreads) index_scores_mfma(
     if (hist[i]) atomicAdd(&g[i], hist[i]);
 }
 
-// FP8 keys, producer/consumer form.  A work-group of 8 waves takes steps of
-// 256 keys: the G work-groups of a row sweep it together, step i of
-// work-group x covering keys [(i G + x) 256, +256).  Waves 4..7 only load:
-// loader j keeps kSplitDepth steps of its 64-key quarter in flight in
-// registers (the same contiguous stream as above, pieces clamped into the
-// visible rows) and copies the oldest one into a double-buffered LDS region.
-// Waves 0..3 only score: scorer j scores quarter j of the step in LDS.  One
-// work-group barrier per step hands a buffer from the loaders to the scorers
-// and back, so the loads never wait for the scoring.  Every wave runs the
-// same number of steps, rounded up to a multiple of kSplitDepth; steps past
-// the work-group's last one read the row's first keys (in L2 after the first
-// read) and are scored but not recorded.  With about one work-group per CU,
-// two register sets per loader measured fastest: four or six put more
-// requests in flight and made the scan slower, and half the work-groups
-// made it slower too.
-constexpr int kSplitThreads = 512;
-constexpr int kSplitStep = 256;   // keys per work-group step
-constexpr int kSplitDepth = 2;    // loader register sets (even)
-constexpr int64_t kSplitTargetWgs = 256;
-
+// FP8 keys, producer/consumer form.  A work-group of 12 waves takes steps of
+// 256 keys: the G work-groups of a row split its visible steps into G
+// contiguous ranges of ceil(steps / G) (a contiguous stream per work-group
+// measured faster than interleaved steps).  Waves 8..11 only load:
+// loader j copies its 64-key quarter of a step (8,448 contiguous bytes, 16 B
+// per lane, pieces clamped into the visible rows) straight from global memory
+// into LDS with the gfx950 direct-to-LDS loads, kSplitBufs - 1 steps ahead
+// of the scorers, into a ring of kSplitBufs LDS buffers; no registers hold
+// the data on the way.  Waves 0..7 only score: scorer s scores the 32 keys
+// [32 s, 32 s + 32) of the step in LDS, two scorers per SIMD so that one's
+// MFMAs overlap the other's vector work.  One work-group barrier per step:
+// before it each loader
+// waits (vmcnt) for its own loads of the step about to be scored; after it
+// the loaders refill the buffer the scorers have just finished with.  Every
+// wave runs n_steps iterations; loads past the work-group's last step repeat
+// the last step's keys (just read, so in L2).
 //
 // Block cache (PG): the keys sit in a pool of blocks of at least 32 keys, so
 // each 32-key half of a quarter is one contiguous run of 264 pieces in one
-// block.  The two block ids of a step are read by ordinary vector loads
-// issued right after the key loads of the step kSplitDepth earlier, so by the
-// time a step's loads are issued its ids have arrived without a wait on any
-// later key load.  A half whose block is unallocated is read from the pool's
-// first block and staged as zeros.
+// block.  The two block ids of a step are read by scalar loads (their own
+// counter, so waiting for them never waits for key loads) issued
+// kSplitBufs - 1 steps before the step's keys.  A half whose block is
+// unallocated is read from the pool's first block and overwritten with zeros
+// in LDS before the barrier.
+constexpr int kSplitScorers = 8;  // scorer waves, 32 keys each
+constexpr int kSplitThreads = 64 * (kSplitScorers + 4);
+constexpr int kSplitStep = 256;   // keys per work-group step
+constexpr int kSplitBufs = 3;     // LDS buffers in the ring (steps in flight + 1)
+constexpr int64_t kSplitTargetWgs = 256;
+
+// s_waitcnt with vmcnt <= n and the other counters unconstrained (gfx9
+// encoding: vmcnt bits [3:0] and [15:14], expcnt [6:4], lgkmcnt [11:8]).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
+// A work-group barrier that orders no memory by itself: the compiler may not
+// move memory operations across it, and no wait for outstanding loads or
+// stores is implied.  The caller waits for what the other side will read
+// (the loaders: their loads into LDS, by vmcnt).
+__device__ __forceinline__ void barrier_no_fence() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 template <int HT, bool PG>
 __global__ void __launch_bounds__(kSplitThreads) index_scores_split(
     const uint16_t* __restrict__ q_idx, const float* __restrict__ w_idx,
@@ -463,28 +484,29 @@ __global__ void __launch_bounds__(kSplitThreads) index_scores_split(
   constexpr int KFMT = CSA_FP8_MX32;
   constexpr int64_t kRowBytes = 132;
   constexpr int kSub = kSplitStep / 4;                 // keys per quarter (one wave)
-  static_assert(kSub == 16 * tiles_per_iter<KFMT>(), "a quarter is one scorer step");
+  static_assert(kSub == 32 * kSplitScorers / 4, "a quarter is two scorers' steps");
   constexpr int kPieces = kSub * (int)kRowBytes / 16;  // 528 pieces of 16 B
-  constexpr int kLoads = (kPieces + 63) / 64;          // 9 per lane
-  static_assert(kSplitDepth % 2 == 0, "buffer parity follows the step");
+  constexpr int kLoads = (kPieces + 63) / 64;          // 9 per lane, the last one 16 lanes
+  constexpr int kLastLanes = kPieces - 64 * (kLoads - 1);
   __shared__ uint32_t hist[kHistBins];
-  __shared__ u32x4_t buf[2][4][kLoads * 64];
+  __shared__ __attribute__((aligned(16))) u32x4_t buf[kSplitBufs][4][kPieces];
 
   const int t = threadIdx.x;
   const int lane = t & 63;
-  const int wave = t >> 6;
-  const int j = wave & 3;          // quarter of the step
-  const bool loader = wave >= 4;
+  const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
+  const bool loader = wave >= kSplitScorers;
+  const int j = loader ? wave - kSplitScorers : wave >> 1;  // quarter of the step
   const int64_t row = row_off + blockIdx.y;
   const int64_t b = row / Q;
   int64_t nv = ((int64_t)pos[row] + 1) / ratio;
   nv = nv < 0 ? 0 : (nv > Nmax ? Nmax : nv);
   if (blockIdx.x == 0 && t == 0) n_vis_out[row] = (int32_t)nv;
   const int64_t G = gridDim.x;
-  const int64_t x0 = (int64_t)blockIdx.x * kSplitStep;
-  if (x0 >= nv) return;
-  const int64_t n_steps = (nv - x0 + G * kSplitStep - 1) / (G * kSplitStep);
-  const int64_t n_iter = (n_steps + kSplitDepth - 1) / kSplitDepth * kSplitDepth;
+  const int64_t row_steps = (nv + kSplitStep - 1) / kSplitStep;
+  const int64_t per_wg = (row_steps + G - 1) / G;
+  const int64_t s0 = (int64_t)blockIdx.x * per_wg;     // this work-group's first step
+  if (s0 >= row_steps) return;
+  const int64_t n_steps = row_steps - s0 < per_wg ? row_steps - s0 : per_wg;
   const uint8_t* kbase = PG ? k_idx : k_idx + b * Nmax * kRowBytes;
   const int64_t end = nv;
   constexpr int kHalf = 32 * (int)kRowBytes / 16;      // 264 pieces: 32 keys
@@ -493,92 +515,117 @@ __global__ void __launch_bounds__(kSplitThreads) index_scores_split(
   __syncthreads();
 
   if (loader) {
+    // the quarter's first key in step i; steps past the last repeat it
     auto step_key = [&](int64_t i) __attribute__((always_inline)) {
-      int64_t k = (i * G + blockIdx.x) * kSplitStep + kSub * j;
-      if (i >= n_steps || k >= end) k = 0;
-      return k;
+      const int64_t ii = s0 + (i < n_steps ? i : n_steps - 1);
+      const int64_t k = ii * kSplitStep + kSub * j;
+      return k < end ? k : ii * kSplitStep;
     };
-    // block ids of step i's two halves: lane 0 reads the first, lane 1 the
-    // second (a lane-dependent address, so a vector load)
+    // block ids of step i's two halves (uniform addresses: scalar loads)
+    struct Ids { int h0, h1; };
     auto tload = [&](int64_t i) __attribute__((always_inline)) {
-      if (!PG) return 0;
+      if (!PG) return Ids{0, 0};
       const int64_t k = step_key(i);
-      int64_t l = (k + 32 * (lane & 1)) >> pm.shift;
-      l = l < pm.max_blocks ? l : pm.max_blocks - 1;
-      return pm.table[b * pm.max_blocks + l];
+      const int64_t l0 = k >> pm.shift;
+      int64_t l1 = (k + 32) >> pm.shift;
+      l1 = l1 < pm.max_blocks ? l1 : pm.max_blocks - 1;
+      // the table is read-only here: through the constant address space the
+      // uniform loads become scalar loads
+      typedef const __attribute__((address_space(4))) int32_t* ctab_t;
+      const ctab_t tr = (ctab_t)(pm.table + b * pm.max_blocks);
+      return Ids{tr[l0], tr[l1]};
     };
-    // the quarter's stream of step i, clamped to whole visible rows; zero
-    // gets bit h set when half h's block is unallocated
-    auto gload = [&](int64_t i, U4Array<kLoads>& v, int tid, int& zero)
-                     __attribute__((always_inline)) {
+    // issue step i's loads into LDS buffer `slot`; returns the zero bits
+    // (bit h: half h's block is unallocated)
+    auto issue = [&](int64_t i, int slot, Ids tid) __attribute__((always_inline)) {
       const int64_t k = step_key(i);
       const int64_t nk = end - k < kSub ? end - k : kSub;
       const int last = (int)((nk * kRowBytes - 1) / 16);
       const u32x4_t* src0 = (const u32x4_t*)(kbase + k * kRowBytes);
       const u32x4_t* src1 = src0;
-      zero = 0;
+      int zero = 0;
       if (PG) {
         const int64_t mask = ((int64_t)1 << pm.shift) - 1;
-        const int id0 = __builtin_amdgcn_readlane(tid, 0);
-        const int id1 = __builtin_amdgcn_readlane(tid, 1);
+        const int id0 = tid.h0, id1 = tid.h1;
         const bool ok0 = id0 >= 0 && id0 < pm.pool_blocks;
         const bool ok1 = id1 >= 0 && id1 < pm.pool_blocks;
         zero = (ok0 ? 0 : 1) | (ok1 ? 0 : 2);
         src0 = (const u32x4_t*)(k_idx + (ok0 ? ((((int64_t)id0) << pm.shift) + (k & mask)) * kRowBytes : 0));
-        src1 = (const u32x4_t*)(k_idx + (ok1 ? ((((int64_t)id1) << pm.shift) + ((k + 32) & mask)) * kRowBytes : 0));
+        src1 = (const u32x4_t*)(k_idx + (ok1 ? ((((int64_t)id1) << pm.shift) + ((k + 32) & mask)) * kRowBytes : 0)) - kHalf;
       }
+      u32x4_t* dst = buf[slot][j];
 #pragma unroll
       for (int l = 0; l < kLoads; ++l) {
         const int piece = lane + 64 * l;
         const int p = piece < last ? piece : last;
-        if (PG) v.v[l] = p < kHalf ? src0[p] : src1[p - kHalf];
-        else v.v[l] = src0[p];
+        const u32x4_t* g = (PG && p >= kHalf) ? src1 + p : src0 + p;
+        if (l < kLoads - 1 || lane < kLastLanes)
+          __builtin_amdgcn_global_load_lds((const void*)g,
+                                           (__attribute__((address_space(3))) void*)(dst + 64 * l),
+                                           16, 0, 0);
       }
+      return zero;
     };
-    auto stage = [&](int bi, const U4Array<kLoads>& v, int zero) __attribute__((always_inline)) {
-      u32x4_t* st = buf[bi][j];
-#pragma unroll
-      for (int l = 0; l < kLoads; ++l) {
-        const int piece = lane + 64 * l;
-        const bool z = PG && ((zero >> (piece < kHalf ? 0 : 1)) & 1);
-        st[piece] = z ? u32x4_t{0u, 0u, 0u, 0u} : v.v[l];
-      }
+    // overwrite the unallocated halves of this quarter in buffer `slot`
+    auto zero_halves = [&](int slot, int zero) __attribute__((always_inline)) {
+      u32x4_t* dst = buf[slot][j];
+      for (int piece = lane; piece < kPieces; piece += 64)
+        if ((zero >> (piece < kHalf ? 0 : 1)) & 1) dst[piece] = u32x4_t{0u, 0u, 0u, 0u};
     };
-    U4Array<kLoads> r[kSplitDepth];
-    int tb[kSplitDepth], zr[kSplitDepth];
+    // loads outstanding after a step's keys when the wait for that step is
+    // issued: the later steps in flight
+    constexpr int kAfter = (kSplitBufs - 2) * kLoads;
+    // id pipeline (PG): tq[u] serves the steps issued at iterations
+    // k = u mod (kSplitBufs - 1)
+    constexpr int kT = kSplitBufs - 1;
+    Ids tq[kT];
+    int zr[kSplitBufs];
 #pragma unroll
-    for (int u = 0; u < kSplitDepth; ++u) tb[u] = tload(u);
-#pragma unroll
-    for (int u = 0; u < kSplitDepth; ++u) {
-      gload(u, r[u], tb[u], zr[u]);
-      tb[u] = tload(u + kSplitDepth);
+    for (int u = 0; u < kT; ++u) {
+      const Ids ids = tload(u);
+      zr[u] = issue(u, u, ids);
+      tq[u] = tload(u + kT);
     }
-    stage(0, r[0], zr[0]);
-    __syncthreads();
-    for (int64_t k = 0; k < n_iter; k += kSplitDepth) {
+    zr[kSplitBufs - 1] = 0;
+    int slot = 0;                      // buffer of step k
+    auto body = [&](int64_t k, Ids& tqu) __attribute__((always_inline)) {
+      wait_vmcnt<kAfter>();            // this wave's loads of step k are in LDS
+      int zk = 0;
 #pragma unroll
-      for (int u = 0; u < kSplitDepth; ++u) {
-        // r[u] held step k + u, staged before the previous barrier: refill it
-        // with step k + u + kSplitDepth (whose block ids tb[u] were read
-        // with the previous refill), and stage step k + u + 1 (buffer
-        // parity (u + 1) & 1, as k is even) before the barrier ending step k + u
-        gload(k + u + kSplitDepth, r[u], tb[u], zr[u]);
-        tb[u] = tload(k + u + 2 * kSplitDepth);
-        stage((u + 1) & 1, r[(u + 1) % kSplitDepth], zr[(u + 1) % kSplitDepth]);
-        __syncthreads();
+      for (int u = 0; u < kSplitBufs; ++u) zk = u == slot ? zr[u] : zk;
+      if (PG && zk) {
+        zero_halves(slot, zk);
+        __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the zeros are in LDS
       }
+      barrier_no_fence();              // step k to the scorers; step k - 1's buffer is free
+      const int fill = slot == 0 ? kSplitBufs - 1 : slot - 1;
+      const int zn = issue(k + kT, fill, tqu);
+#pragma unroll
+      for (int u = 0; u < kSplitBufs; ++u) zr[u] = u == fill ? zn : zr[u];
+      tqu = tload(k + 2 * kT);
+      slot = slot + 1 == kSplitBufs ? 0 : slot + 1;
+    };
+    for (int64_t k = 0; k < n_steps; k += kT) {
+#pragma unroll
+      for (int u = 0; u < kT; ++u)
+        if (k + u < n_steps) body(k + u, tq[u]);
     }
+    wait_vmcnt<0>();                   // no load into LDS outlives the kernel
   } else {
-    Scorer<HT, KFMT> sc;
+    Scorer<HT, KFMT, 2> sc;
     sc.load(q_idx, w_idx, row, lane, bf16_scores);
     float* srow = scores + row * Nmax;
-    __syncthreads();
-    for (int64_t k = 0; k < n_iter; ++k) {
-      const u32x4_t* st = buf[k & 1][j];
-      sc.score((k * G + blockIdx.x) * kSplitStep + kSub * j, k < n_steps, end,
-               [&](int nt, KeyRaw& f) { stage_read<KFMT>(st, 16 * nt + sc.r16, sc.kq, f); },
+    const int h = wave & 1;            // half of the quarter: keys 32 h .. 32 h + 31
+    int slot = 0;
+    for (int64_t k = 0; k < n_steps; ++k) {
+      barrier_no_fence();              // the loaders have waited for step k's loads
+      const u32x4_t* st = buf[slot][j];
+      sc.score((s0 + k) * kSplitStep + kSub * j + 32 * h, true, end,
+               [&](int nt, KeyRaw& f) {
+                 stage_read<KFMT>(st, 32 * h + 16 * nt + sc.r16, sc.kq, f);
+               },
                srow, hist);
-      __syncthreads();
+      slot = slot + 1 == kSplitBufs ? 0 : slot + 1;
     }
   }
   __syncthreads();
