@@ -193,21 +193,29 @@ def measured_traffic(workload):
     """HBM bytes per csa_index_topk call from the committed counter summary
     (FETCH_SIZE + WRITE_SIZE runs, copy-calibrated), or None when there is no
     summary for this workload or the kernel sources changed since it was taken."""
+    return traffic_with_status(workload)[0]
+
+
+def traffic_with_status(workload):
+    """(bytes or None, status): status says whether the counters were taken on
+    the current kernel sources, are stale, or do not exist for this workload."""
     if workload != "csa_1m_fp8" or not os.path.exists(TRAFFIC_PROFILE):
-        return None
+        return None, "no counter run for this workload"
     text = open(TRAFFIC_PROFILE).read()
     m_b = re.search(r"traffic_bytes_per_call: (\d+)", text)
     m_h = re.search(r"sources_sha256: ([0-9a-f]+)", text)
     m_s = re.search(r"sources: (.+)", text)
     if not (m_b and m_h and m_s):
-        return None
+        return None, "counter summary unreadable"
     h = hashlib.sha256()
     for f in m_s.group(1).split():
         path = os.path.join(ROOT, f)
         if not os.path.exists(path):
-            return None
+            return None, f"stale: {f} no longer exists"
         h.update(open(path, "rb").read())
-    return int(m_b.group(1)) if h.hexdigest() == m_h.group(1) else None
+    if h.hexdigest() != m_h.group(1):
+        return None, "stale: kernel sources changed since the counters were taken"
+    return int(m_b.group(1)), "counters taken on the current kernel sources"
 
 
 def time_steps(layer, steps, torch):
@@ -528,6 +536,7 @@ def main():
     dom = "csa_index_topk" if w.ratio != 128 else "hca_attn_decode"
     layers = 1 + w.extra.get("reuse", 0)  # layers per step (a layer group with reuse)
     dom_gbs = ab[dom] / (phases[dom] * 1e-3) / 1e9
+    traffic, traffic_status = traffic_with_status(a.workload)
     step_bytes = sum(ab.values())
     res = {
         "metric": METRICS.get(w.name, METRICS["csa_1m_fp8"]),
@@ -548,8 +557,8 @@ def main():
                    "index_key_format": w.key_fmt, "cache_copies": a.copies,
                    "layers_per_step": layers},
         "roofline": {"bound": "hbm", "achieved": dom_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": dom_gbs / HBM_PEAK_GBS, "traffic": measured_traffic(a.workload),
-                     "kernel": dom,
+                     "frac": dom_gbs / HBM_PEAK_GBS, "traffic": traffic,
+                     "traffic_status": traffic_status, "kernel": dom,
                      "bytes_per_launch": ab[dom], "ms_per_launch": phases[dom]},
         "step_hbm_GBps": step_bytes / (ms * 1e-3) / 1e9,
         "step_ms_percentiles": pct,
