@@ -88,7 +88,10 @@ def algorithmic_bytes(w):
                                 + 2 * 2 * B * coff * w.ratio * coff * 128 * 4
                                 + B * row_bytes(w.key_fmt, 128))
         n_vis = min((w.t + 1) // w.ratio, N)
-        out["csa_index_topk"] = B * (n_vis * row_bytes(w.key_fmt, 128) + w.Hi * 128 * qb
+        # q_idx: bf16, or MXFP4 rows for the FP4 indexer (as the decode layer passes them)
+        q_idx = (row_bytes("fp4_mx32", 128) if w.key_fmt == "fp4_mx32" and not w.extra.get("layer")
+                 else 128 * qb)
+        out["csa_index_topk"] = B * (n_vis * row_bytes(w.key_fmt, 128) + w.Hi * q_idx
                                      + w.Hi * 4 + w.topk * 4)
         k = min(w.topk, n_vis)
         out["csa_sparse_attn_decode"] = B * (k * row_bytes(w.ent_fmt, 512) + k * 4

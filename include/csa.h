@@ -228,12 +228,17 @@ csa_status csa_compress_many(const csa_compress_args* a, int n, void* ws, size_t
  * FP8 keys are decoded exactly), then the top min(topk, n_vis) entries are
  * returned in out_idx[b][q][0..topk) ordered by descending score, equal scores
  * by ascending index, -0 == +0, NaN last; the remaining slots hold -1.
- * q_idx: [B][Q][Hi][128] in q_fmt (F32 or BF16); w_idx: [B][Q][Hi] float, with
- * the 128^-1/2 * Hi^-1/2 factor already applied; k_idx: [B][Nmax] rows of 128
- * values in k_fmt (F32, BF16 or FP8_MX32 = 132 B); pos: [B][Q] int32.
+ * q_idx: [B][Q][Hi][128] in q_fmt (F32 or BF16), or [B][Q][Hi] rows of 68 B
+ * in q_fmt FP4_MX32 (the key codec's MXFP4 rows); w_idx: [B][Q][Hi] float,
+ * with the 128^-1/2 * Hi^-1/2 factor already applied; k_idx: [B][Nmax] rows of
+ * 128 values in k_fmt (F32, BF16, FP8_MX32 = 132 B or FP4_MX32 = 68 B);
+ * pos: [B][Q] int32.
  * out_scores (nullable): [B][Q][Nmax] float, entries s < n_vis are written.
  * Requirements: Hi % 16 == 0 and Hi <= 128 (any Hi for F32); 1 <= topk <= 2048;
- * k_fmt F32 requires q_fmt F32 and BF16/FP8 require q_fmt BF16.             */
+ * k_fmt F32 requires q_fmt F32, BF16/FP8 require q_fmt BF16, and FP4_MX32
+ * keys take q_fmt BF16 or FP4_MX32.  With FP4_MX32 queries and keys a 16 x 16
+ * block of head-key products is one block-scaled FP4 MFMA over all 128 dims
+ * (E2M1 products are exact; float32 accumulation).                          */
 size_t csa_index_topk_workspace_size(int B, int Q, int64_t Nmax, int topk);
 csa_status csa_index_topk(const void* q_idx, int q_fmt, const float* w_idx, const void* k_idx,
                           int k_fmt, const int32_t* pos, int ratio, int B, int Q, int Hi,
@@ -246,9 +251,9 @@ csa_status csa_index_topk(const void* q_idx, int q_fmt, const float* w_idx, cons
  * (round to nearest even; NaN stays NaN) before it is stored in out_scores and
  * ranked.  Ties that the rounding creates are broken by the smaller index, as
  * in csa_index_topk.  Meant for k_fmt = CSA_FP4_MX32 keys (68 B per key) with
- * bf16 queries that carry FP4 values (an E2M1 code times a power of two is
- * exact in bf16); any k_fmt that csa_index_topk accepts is accepted.  Same
- * arguments, workspace size and errors.                                      */
+ * FP4_MX32 queries (or bf16 queries that carry FP4 values: an E2M1 code times
+ * a power of two is exact in bf16); any k_fmt that csa_index_topk accepts is
+ * accepted.  Same arguments, workspace size and errors.                      */
 csa_status csa_index_topk_bf16(const void* q_idx, int q_fmt, const float* w_idx,
                                const void* k_idx, int k_fmt, const int32_t* pos, int ratio,
                                int B, int Q, int Hi, int64_t Nmax, int topk, int32_t* out_idx,

@@ -317,7 +317,9 @@ static csa_status index_topk(const void* q_idx, int q_fmt, const float* w_idx, c
   } else {
     REQUIRE(k_fmt == CSA_BF16 || k_fmt == CSA_FP8_MX32 || k_fmt == CSA_FP4_MX32,
             CSA_EUNSUPPORTED, "k_fmt must be F32, BF16, FP8_MX32 or FP4_MX32");
-    REQUIRE(q_fmt == CSA_BF16, CSA_EUNSUPPORTED, "BF16/FP8 keys need BF16 queries");
+    REQUIRE(q_fmt == CSA_BF16 || (q_fmt == CSA_FP4_MX32 && k_fmt == CSA_FP4_MX32),
+            CSA_EUNSUPPORTED,
+            "BF16/FP8 keys need BF16 queries; FP4_MX32 keys take BF16 or FP4_MX32 queries");
     REQUIRE(Hi % 16 == 0 && Hi <= 128, CSA_EUNSUPPORTED, "Hi must be a multiple of 16, <= 128");
   }
   REQUIRE_PTR(q_idx);

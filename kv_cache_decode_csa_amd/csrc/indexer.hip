@@ -162,11 +162,20 @@ __device__ __forceinline__ void wave_lds_sync() {
 // data of one step's tiles (get(nt, f)), forms the 16 heads x 16 keys MFMA
 // products of every head tile, applies ReLU and the head weights, adds up the
 // heads and records the step's scores.
-template <int HT, int KFMT, int TILES = tiles_per_iter<KFMT>()>
+//
+// QF4: the queries are MXFP4-MX32 rows too (68 B per head), and one
+// block-scaled FP4 MFMA (16 x 16 x 128, E8M0 scales) forms a tile's products
+// over all 128 dims: lane (r16, kq) hands it the 32 E2M1 codes of block kq of
+// head or key r16 with that block's scale, which is exactly how both rows are
+// stored, so nothing is decoded.  The products of two scaled E2M1 values are
+// exact, as they are in the bf16 MFMA of the decoded values.
+template <int HT, int KFMT, int TILES = tiles_per_iter<KFMT>(), bool QF4 = false>
 struct Scorer {
   static constexpr int kTiles = TILES;
   static_assert(TILES == 2 || TILES == 4, "a step is two or four 16-key tiles");
-  uint4 qa[HT][4];  // A operand: head 16 mt + r16, dims 32 kq + 8 s .. +8
+  static_assert(!QF4 || KFMT == CSA_FP4_MX32, "FP4 queries go with FP4 keys");
+  uint4 qa[HT][4];  // A operand: head 16 mt + r16, dims 32 kq + 8 s .. +8 (QF4: qa[mt][0]
+                    // the codes of block kq, qa[mt][1].x its scale byte)
   float wv[HT][4];  // head weights in the D layout: head 16 mt + 4 kq + r
   int r16, kq;
   bool bf16s;       // scores rounded to bf16 (RNE) before they are stored and ranked
@@ -177,12 +186,24 @@ struct Scorer {
     r16 = lane & 15;
     kq = lane >> 4;
     bf16s = bf16_scores != 0;
-    const uint16_t* qrow = q_idx + row * (int64_t)Hi * kIndexDim;
+    if (QF4) {
+      constexpr int kQRow = key_row_bytes<CSA_FP4_MX32>();  // 68 B per head
+      const uint8_t* qrow = (const uint8_t*)q_idx + row * (int64_t)Hi * kQRow;
 #pragma unroll
-    for (int mt = 0; mt < HT; ++mt)
+      for (int mt = 0; mt < HT; ++mt) {
+        const uint8_t* h = qrow + (16 * mt + r16) * kQRow;
+        const uint32_t* c = (const uint32_t*)(h + 16 * kq);  // 68-B rows: dword aligned
+        qa[mt][0] = make_uint4(c[0], c[1], c[2], c[3]);
+        qa[mt][1].x = h[64 + kq];
+      }
+    } else {
+      const uint16_t* qrow = q_idx + row * (int64_t)Hi * kIndexDim;
 #pragma unroll
-      for (int s = 0; s < 4; ++s)
-        qa[mt][s] = *(const uint4*)(qrow + (16 * mt + r16) * kIndexDim + 32 * kq + 8 * s);
+      for (int mt = 0; mt < HT; ++mt)
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+          qa[mt][s] = *(const uint4*)(qrow + (16 * mt + r16) * kIndexDim + 32 * kq + 8 * s);
+    }
     const float* wrow = w_idx + row * (int64_t)Hi;
 #pragma unroll
     for (int mt = 0; mt < HT; ++mt)
@@ -193,6 +214,20 @@ struct Scorer {
   // The HT head tiles are independent accumulation chains: they are issued
   // round-robin so consecutive MFMAs do not wait on each other.
   __device__ __forceinline__ void tile_mfma(const KeyRaw& f, f32x4_t (&acc)[HT]) const {
+    if (QF4) {
+      typedef int v8i_t __attribute__((ext_vector_type(8)));
+      const v8i_t kb = {(int)f.w[0], (int)f.w[1], (int)f.w[2], (int)f.w[3], 0, 0, 0, 0};
+      const f32x4_t z = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int mt = 0; mt < HT; ++mt) {
+        const uint4 c = qa[mt][0];
+        const v8i_t qb = {(int)c.x, (int)c.y, (int)c.z, (int)c.w, 0, 0, 0, 0};
+        // formats 4 / 4: E2M1 operands; the scale operands' byte 0 is used
+        acc[mt] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+            qb, kb, z, 4, 4, 0, (int)qa[mt][1].x, 0, (int)f.w[8]);
+      }
+      return;
+    }
     bf16x8_t kb[4];
 #pragma unroll
     for (int s = 0; s < 4; ++s) kb[s] = key_frag<KFMT>(f, s);
@@ -427,33 +462,36 @@ __global__ void __launch_bounds__(kIdxThreads) index_scores_mfma(
     if (hist[i]) atomicAdd(&g[i], hist[i]);
 }
 
-// FP8 keys, producer/consumer form.  A work-group of 12 waves takes steps of
-// 256 keys: the G work-groups of a row split its visible steps into G
-// contiguous ranges of ceil(steps / G) (a contiguous stream per work-group
-// measured faster than interleaved steps).  Waves 8..11 only load:
-// loader j copies its 64-key quarter of a step (8,448 contiguous bytes, 16 B
-// per lane, pieces clamped into the visible rows) straight from global memory
-// into LDS with the gfx950 direct-to-LDS loads, kSplitBufs - 1 steps ahead
-// of the scorers, into a ring of kSplitBufs LDS buffers; no registers hold
-// the data on the way.  Waves 0..7 only score: scorer s scores the 32 keys
-// [32 s, 32 s + 32) of the step in LDS, two scorers per SIMD so that one's
-// MFMAs overlap the other's vector work.  One work-group barrier per step:
-// before it each loader
-// waits (vmcnt) for its own loads of the step about to be scored; after it
-// the loaders refill the buffer the scorers have just finished with.  Every
-// wave runs n_steps iterations; loads past the work-group's last step repeat
-// the last step's keys (just read, so in L2).
+// FP8 and FP4 keys, producer/consumer form.  A work-group of 12 waves takes
+// steps of 256 FP8 or 512 FP4 keys (33,792 or 34,816 bytes): the G
+// work-groups of a row split its visible steps into G contiguous ranges of
+// ceil(steps / G) (a contiguous stream per work-group measured faster than
+// interleaved steps).  Waves 8..11 only load: loader j copies its quarter of
+// a step (16 B per lane, pieces clamped into the visible rows) straight from
+// global memory into LDS with the gfx950 direct-to-LDS loads, kSplitBufs - 1
+// steps ahead of the scorers, into a ring of kSplitBufs LDS buffers; no
+// registers hold the data on the way.  Waves 0..7 only score: the two
+// scorers of a quarter take one half of it each (32 FP8 or 64 FP4 keys), two
+// scorers per SIMD so that one's MFMAs overlap the other's vector work.  One
+// work-group barrier per step: before it each loader waits (vmcnt) for its
+// own loads of the step about to be scored; after it the loaders refill the
+// buffer the scorers have just finished with.  Every wave runs n_steps
+// iterations; loads past the work-group's last step repeat the last step's
+// keys (just read, so in L2).  A step has a fixed cost of about 0.9 us (the
+// barrier and each scorer's chain of LDS reads, MFMAs and score stores) on
+// top of its bytes, so FP4 steps hold twice the keys: with 256-key steps the
+// FP4 scan ran at 3.3 TB/s, and taking away three quarters of its MFMAs or
+// its whole E2M1 decode did not change that.
 //
 // Block cache (PG): the keys sit in a pool of blocks of at least 32 keys, so
-// each 32-key half of a quarter is one contiguous run of 264 pieces in one
-// block.  The two block ids of a step are read by scalar loads (their own
-// counter, so waiting for them never waits for key loads) issued
-// kSplitBufs - 1 steps before the step's keys.  A half whose block is
-// unallocated is read from the pool's first block and overwritten with zeros
-// in LDS before the barrier.
-constexpr int kSplitScorers = 8;  // scorer waves, 32 keys each
+// each 32-key run of a quarter is contiguous in one block.  The block ids of
+// a step's runs are read by scalar loads (their own counter, so waiting for
+// them never waits for key loads) issued kSplitBufs - 1 steps before the
+// step's keys.  A run whose block is unallocated is read from the pool's
+// first block and overwritten with zeros in LDS before the barrier.
+constexpr int kSplitScorers = 8;  // scorer waves, half a quarter each
 constexpr int kSplitThreads = 64 * (kSplitScorers + 4);
-constexpr int kSplitStep = 256;   // keys per work-group step
+template <int KF> constexpr int split_step() { return KF == CSA_FP8_MX32 ? 256 : 512; }
 constexpr int kSplitBufs = 3;     // LDS buffers in the ring (steps in flight + 1)
 constexpr int64_t kSplitTargetWgs = 256;
 
@@ -475,19 +513,24 @@ __device__ __forceinline__ void barrier_no_fence() {
   asm volatile("" ::: "memory");
 }
 
-template <int HT, bool PG>
+template <int HT, int KFMT, bool PG, bool QF4 = false>
 __global__ void __launch_bounds__(kSplitThreads) index_scores_split(
     const uint16_t* __restrict__ q_idx, const float* __restrict__ w_idx,
     const uint8_t* __restrict__ k_idx, const int32_t* __restrict__ pos, int ratio, int Q,
     int64_t Nmax, int64_t row_off, float* __restrict__ scores,
     int32_t* __restrict__ n_vis_out, uint32_t* __restrict__ hist_g, int bf16_scores, PageMap pm) {
-  constexpr int KFMT = CSA_FP8_MX32;
-  constexpr int64_t kRowBytes = 132;
-  constexpr int kSub = kSplitStep / 4;                 // keys per quarter (one wave)
-  static_assert(kSub == 32 * kSplitScorers / 4, "a quarter is two scorers' steps");
-  constexpr int kPieces = kSub * (int)kRowBytes / 16;  // 528 pieces of 16 B
-  constexpr int kLoads = (kPieces + 63) / 64;          // 9 per lane, the last one 16 lanes
+  static_assert(KFMT == CSA_FP8_MX32 || KFMT == CSA_FP4_MX32, "packed key rows");
+  constexpr int64_t kRowBytes = key_row_bytes<KFMT>();
+  constexpr int kStep = split_step<KFMT>();
+  constexpr int kSub = kStep / 4;                      // keys per quarter (one loader)
+  constexpr int kHalfKeys = kSub / 2;                  // keys per scorer
+  constexpr int kTiles = kHalfKeys / 16;               // 16-key MFMA tiles per scorer
+  constexpr int kPieces = kSub * (int)kRowBytes / 16;  // 528 (FP8) or 544 pieces of 16 B
+  constexpr int kLoads = (kPieces + 63) / 64;          // 9 per lane, the last one partial
   constexpr int kLastLanes = kPieces - 64 * (kLoads - 1);
+  constexpr int kRuns = kSub / 32;                     // 32-key runs per quarter
+  constexpr int kRun = 32 * (int)kRowBytes / 16;       // pieces per run: 264 or 136
+  static_assert(kSub * (int)kRowBytes % 16 == 0 && kRuns <= 4, "whole pieces, at most 4 runs");
   __shared__ uint32_t hist[kHistBins];
   __shared__ __attribute__((aligned(16))) u32x4_t buf[kSplitBufs][4][kPieces];
 
@@ -502,14 +545,13 @@ __global__ void __launch_bounds__(kSplitThreads) index_scores_split(
   nv = nv < 0 ? 0 : (nv > Nmax ? Nmax : nv);
   if (blockIdx.x == 0 && t == 0) n_vis_out[row] = (int32_t)nv;
   const int64_t G = gridDim.x;
-  const int64_t row_steps = (nv + kSplitStep - 1) / kSplitStep;
+  const int64_t row_steps = (nv + kStep - 1) / kStep;
   const int64_t per_wg = (row_steps + G - 1) / G;
   const int64_t s0 = (int64_t)blockIdx.x * per_wg;     // this work-group's first step
   if (s0 >= row_steps) return;
   const int64_t n_steps = row_steps - s0 < per_wg ? row_steps - s0 : per_wg;
   const uint8_t* kbase = PG ? k_idx : k_idx + b * Nmax * kRowBytes;
   const int64_t end = nv;
-  constexpr int kHalf = 32 * (int)kRowBytes / 16;      // 264 pieces: 32 keys
 
   for (int i = t; i < kHistBins; i += kSplitThreads) hist[i] = 0;
   __syncthreads();
@@ -518,47 +560,62 @@ __global__ void __launch_bounds__(kSplitThreads) index_scores_split(
     // the quarter's first key in step i; steps past the last repeat it
     auto step_key = [&](int64_t i) __attribute__((always_inline)) {
       const int64_t ii = s0 + (i < n_steps ? i : n_steps - 1);
-      const int64_t k = ii * kSplitStep + kSub * j;
-      return k < end ? k : ii * kSplitStep;
+      const int64_t k = ii * kStep + kSub * j;
+      return k < end ? k : ii * kStep;
     };
-    // block ids of step i's two halves (uniform addresses: scalar loads)
-    struct Ids { int h0, h1; };
+    // block ids of step i's runs (uniform addresses: scalar loads)
+    struct Ids { int id[kRuns]; };
     auto tload = [&](int64_t i) __attribute__((always_inline)) {
-      if (!PG) return Ids{0, 0};
+      Ids r;
+#pragma unroll
+      for (int u = 0; u < kRuns; ++u) r.id[u] = 0;
+      if (!PG) return r;
       const int64_t k = step_key(i);
-      const int64_t l0 = k >> pm.shift;
-      int64_t l1 = (k + 32) >> pm.shift;
-      l1 = l1 < pm.max_blocks ? l1 : pm.max_blocks - 1;
       // the table is read-only here: through the constant address space the
       // uniform loads become scalar loads
       typedef const __attribute__((address_space(4))) int32_t* ctab_t;
       const ctab_t tr = (ctab_t)(pm.table + b * pm.max_blocks);
-      return Ids{tr[l0], tr[l1]};
+#pragma unroll
+      for (int u = 0; u < kRuns; ++u) {
+        int64_t l = (k + 32 * u) >> pm.shift;
+        l = l < pm.max_blocks ? l : pm.max_blocks - 1;
+        r.id[u] = tr[l];
+      }
+      return r;
     };
     // issue step i's loads into LDS buffer `slot`; returns the zero bits
-    // (bit h: half h's block is unallocated)
-    auto issue = [&](int64_t i, int slot, Ids tid) __attribute__((always_inline)) {
+    // (bit u: run u's block is unallocated)
+    auto issue = [&](int64_t i, int slot, const Ids& tid) __attribute__((always_inline)) {
       const int64_t k = step_key(i);
       const int64_t nk = end - k < kSub ? end - k : kSub;
       const int last = (int)((nk * kRowBytes - 1) / 16);
-      const u32x4_t* src0 = (const u32x4_t*)(kbase + k * kRowBytes);
-      const u32x4_t* src1 = src0;
+      const u32x4_t* src[kRuns];
       int zero = 0;
+#pragma unroll
+      for (int u = 0; u < kRuns; ++u) src[u] = (const u32x4_t*)(kbase + k * kRowBytes);
       if (PG) {
         const int64_t mask = ((int64_t)1 << pm.shift) - 1;
-        const int id0 = tid.h0, id1 = tid.h1;
-        const bool ok0 = id0 >= 0 && id0 < pm.pool_blocks;
-        const bool ok1 = id1 >= 0 && id1 < pm.pool_blocks;
-        zero = (ok0 ? 0 : 1) | (ok1 ? 0 : 2);
-        src0 = (const u32x4_t*)(k_idx + (ok0 ? ((((int64_t)id0) << pm.shift) + (k & mask)) * kRowBytes : 0));
-        src1 = (const u32x4_t*)(k_idx + (ok1 ? ((((int64_t)id1) << pm.shift) + ((k + 32) & mask)) * kRowBytes : 0)) - kHalf;
+#pragma unroll
+        for (int u = 0; u < kRuns; ++u) {
+          const int id = tid.id[u];
+          const bool ok = id >= 0 && id < pm.pool_blocks;
+          zero |= ok ? 0 : 1 << u;
+          src[u] = (const u32x4_t*)(k_idx + (ok ? ((((int64_t)id) << pm.shift) +
+                                                   ((k + 32 * u) & mask)) * kRowBytes : 0)) -
+                   kRun * u;
+        }
       }
       u32x4_t* dst = buf[slot][j];
 #pragma unroll
       for (int l = 0; l < kLoads; ++l) {
         const int piece = lane + 64 * l;
         const int p = piece < last ? piece : last;
-        const u32x4_t* g = (PG && p >= kHalf) ? src1 + p : src0 + p;
+        const u32x4_t* g = src[0] + p;
+        if (PG) {
+          const int run = p / kRun;
+#pragma unroll
+          for (int u = 1; u < kRuns; ++u) g = run == u ? src[u] + p : g;
+        }
         if (l < kLoads - 1 || lane < kLastLanes)
           __builtin_amdgcn_global_load_lds((const void*)g,
                                            (__attribute__((address_space(3))) void*)(dst + 64 * l),
@@ -566,11 +623,11 @@ __global__ void __launch_bounds__(kSplitThreads) index_scores_split(
       }
       return zero;
     };
-    // overwrite the unallocated halves of this quarter in buffer `slot`
-    auto zero_halves = [&](int slot, int zero) __attribute__((always_inline)) {
+    // overwrite the unallocated runs of this quarter in buffer `slot`
+    auto zero_runs = [&](int slot, int zero) __attribute__((always_inline)) {
       u32x4_t* dst = buf[slot][j];
       for (int piece = lane; piece < kPieces; piece += 64)
-        if ((zero >> (piece < kHalf ? 0 : 1)) & 1) dst[piece] = u32x4_t{0u, 0u, 0u, 0u};
+        if ((zero >> (piece / kRun)) & 1) dst[piece] = u32x4_t{0u, 0u, 0u, 0u};
     };
     // loads outstanding after a step's keys when the wait for that step is
     // issued: the later steps in flight
@@ -594,7 +651,7 @@ __global__ void __launch_bounds__(kSplitThreads) index_scores_split(
 #pragma unroll
       for (int u = 0; u < kSplitBufs; ++u) zk = u == slot ? zr[u] : zk;
       if (PG && zk) {
-        zero_halves(slot, zk);
+        zero_runs(slot, zk);
         __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the zeros are in LDS
       }
       barrier_no_fence();              // step k to the scorers; step k - 1's buffer is free
@@ -612,17 +669,17 @@ __global__ void __launch_bounds__(kSplitThreads) index_scores_split(
     }
     wait_vmcnt<0>();                   // no load into LDS outlives the kernel
   } else {
-    Scorer<HT, KFMT, 2> sc;
+    Scorer<HT, KFMT, kTiles, QF4> sc;
     sc.load(q_idx, w_idx, row, lane, bf16_scores);
     float* srow = scores + row * Nmax;
-    const int h = wave & 1;            // half of the quarter: keys 32 h .. 32 h + 31
+    const int h = wave & 1;            // half of the quarter
     int slot = 0;
     for (int64_t k = 0; k < n_steps; ++k) {
       barrier_no_fence();              // the loaders have waited for step k's loads
       const u32x4_t* st = buf[slot][j];
-      sc.score((s0 + k) * kSplitStep + kSub * j + 32 * h, true, end,
+      sc.score((s0 + k) * kStep + kSub * j + kHalfKeys * h, true, end,
                [&](int nt, KeyRaw& f) {
-                 stage_read<KFMT>(st, 32 * h + 16 * nt + sc.r16, sc.kq, f);
+                 stage_read<KFMT>(st, kHalfKeys * h + 16 * nt + sc.r16, sc.kq, f);
                },
                srow, hist);
       slot = slot + 1 == kSplitBufs ? 0 : slot + 1;
@@ -795,7 +852,7 @@ __global__ void __launch_bounds__(kIdxThreads) index_scores_f32(
 }
 
 template <int HT, bool PG>
-hipError_t launch_mfma_pg(const void* q_idx, const float* w_idx, const void* k_idx, int k_fmt,
+hipError_t launch_mfma_pg(const void* q_idx, int q_fmt, const float* w_idx, const void* k_idx, int k_fmt,
                           const int32_t* pos, int ratio, int Q, int64_t R, int64_t Nmax,
                           float* scores, int32_t* n_vis, uint32_t* hist, int bf16s, PageMap pm,
                           hipStream_t s) {
@@ -814,18 +871,23 @@ hipError_t launch_mfma_pg(const void* q_idx, const float* w_idx, const void* k_i
     }
     return hipGetLastError();
   }
-  if (k_fmt == CSA_FP8_MX32) {
+  if (k_fmt == CSA_FP8_MX32 || k_fmt == CSA_FP4_MX32) {
     // about one work-group per CU in all, at least one step each
     int64_t gx = (kSplitTargetWgs + R - 1) / R;
-    const int64_t steps = (Nmax + kSplitStep - 1) / kSplitStep;
+    const int kStep = k_fmt == CSA_FP8_MX32 ? split_step<CSA_FP8_MX32>() : split_step<CSA_FP4_MX32>();
+    const int64_t steps = (Nmax + kStep - 1) / kStep;
     gx = gx < steps ? gx : steps;
     gx = gx < 1 ? 1 : gx;
     for (int64_t r0 = 0; r0 < R; r0 += 65535) {
       int64_t nr = R - r0 < 65535 ? R - r0 : 65535;
-      hipLaunchKernelGGL((index_scores_split<HT, PG>), dim3((unsigned)gx, (unsigned)nr),
-                         dim3(kSplitThreads), 0, s, (const uint16_t*)q_idx, w_idx,
-                         (const uint8_t*)k_idx, pos, ratio, Q, Nmax, r0, scores, n_vis, hist,
-                         bf16s, pm);
+      auto go = [&](auto kern) {
+        hipLaunchKernelGGL(kern, dim3((unsigned)gx, (unsigned)nr), dim3(kSplitThreads), 0, s,
+                           (const uint16_t*)q_idx, w_idx, (const uint8_t*)k_idx, pos, ratio, Q,
+                           Nmax, r0, scores, n_vis, hist, bf16s, pm);
+      };
+      if (k_fmt == CSA_FP8_MX32) go(index_scores_split<HT, CSA_FP8_MX32, PG>);
+      else if (q_fmt == CSA_FP4_MX32) go(index_scores_split<HT, CSA_FP4_MX32, PG, true>);
+      else go(index_scores_split<HT, CSA_FP4_MX32, PG>);
     }
     return hipGetLastError();
   }
@@ -834,29 +896,23 @@ hipError_t launch_mfma_pg(const void* q_idx, const float* w_idx, const void* k_i
   const int64_t gx = (Nmax + kpw - 1) / kpw;
   for (int64_t r0 = 0; r0 < R; r0 += 65535) {
     int64_t nr = R - r0 < 65535 ? R - r0 : 65535;
-    if (k_fmt == CSA_FP4_MX32)
-      hipLaunchKernelGGL((index_scores_mfma<HT, CSA_FP4_MX32, PG>), dim3((unsigned)gx, (unsigned)nr),
-                         dim3(kIdxThreads), 0, s, (const uint16_t*)q_idx, w_idx,
-                         (const uint8_t*)k_idx, pos, ratio, Q, Nmax, r0, scores, n_vis, hist,
-                         bf16s, pm);
-    else
-      hipLaunchKernelGGL((index_scores_mfma<HT, CSA_BF16, PG>), dim3((unsigned)gx, (unsigned)nr),
-                         dim3(kIdxThreads), 0, s, (const uint16_t*)q_idx, w_idx,
-                         (const uint8_t*)k_idx, pos, ratio, Q, Nmax, r0, scores, n_vis, hist,
-                         bf16s, pm);
+    hipLaunchKernelGGL((index_scores_mfma<HT, CSA_BF16, PG>), dim3((unsigned)gx, (unsigned)nr),
+                       dim3(kIdxThreads), 0, s, (const uint16_t*)q_idx, w_idx,
+                       (const uint8_t*)k_idx, pos, ratio, Q, Nmax, r0, scores, n_vis, hist,
+                       bf16s, pm);
   }
   return hipGetLastError();
 }
 
 template <int HT>
-hipError_t launch_mfma(const void* q_idx, const float* w_idx, const void* k_idx, int k_fmt,
+hipError_t launch_mfma(const void* q_idx, int q_fmt, const float* w_idx, const void* k_idx, int k_fmt,
                        const int32_t* pos, int ratio, int Q, int64_t R, int64_t Nmax,
                        float* scores, int32_t* n_vis, uint32_t* hist, int bf16s, PageMap pm,
                        hipStream_t s) {
   if (pm.table)
-    return launch_mfma_pg<HT, true>(q_idx, w_idx, k_idx, k_fmt, pos, ratio, Q, R, Nmax, scores,
+    return launch_mfma_pg<HT, true>(q_idx, q_fmt, w_idx, k_idx, k_fmt, pos, ratio, Q, R, Nmax, scores,
                                     n_vis, hist, bf16s, pm, s);
-  return launch_mfma_pg<HT, false>(q_idx, w_idx, k_idx, k_fmt, pos, ratio, Q, R, Nmax, scores,
+  return launch_mfma_pg<HT, false>(q_idx, q_fmt, w_idx, k_idx, k_fmt, pos, ratio, Q, R, Nmax, scores,
                                    n_vis, hist, bf16s, pm, s);
 }
 
@@ -877,16 +933,15 @@ hipError_t launch_index_scores(const void* q_idx, int q_fmt, const float* w_idx,
     }
     return hipGetLastError();
   }
-  (void)q_fmt;
   switch (Hi / 16) {
-    case 1: return launch_mfma<1>(q_idx, w_idx, k_idx, k_fmt, pos, ratio, Q, R, Nmax, scores, n_vis, w.hist, bf16_scores, pm, s);
-    case 2: return launch_mfma<2>(q_idx, w_idx, k_idx, k_fmt, pos, ratio, Q, R, Nmax, scores, n_vis, w.hist, bf16_scores, pm, s);
-    case 3: return launch_mfma<3>(q_idx, w_idx, k_idx, k_fmt, pos, ratio, Q, R, Nmax, scores, n_vis, w.hist, bf16_scores, pm, s);
-    case 4: return launch_mfma<4>(q_idx, w_idx, k_idx, k_fmt, pos, ratio, Q, R, Nmax, scores, n_vis, w.hist, bf16_scores, pm, s);
-    case 5: return launch_mfma<5>(q_idx, w_idx, k_idx, k_fmt, pos, ratio, Q, R, Nmax, scores, n_vis, w.hist, bf16_scores, pm, s);
-    case 6: return launch_mfma<6>(q_idx, w_idx, k_idx, k_fmt, pos, ratio, Q, R, Nmax, scores, n_vis, w.hist, bf16_scores, pm, s);
-    case 7: return launch_mfma<7>(q_idx, w_idx, k_idx, k_fmt, pos, ratio, Q, R, Nmax, scores, n_vis, w.hist, bf16_scores, pm, s);
-    case 8: return launch_mfma<8>(q_idx, w_idx, k_idx, k_fmt, pos, ratio, Q, R, Nmax, scores, n_vis, w.hist, bf16_scores, pm, s);
+    case 1: return launch_mfma<1>(q_idx, q_fmt, w_idx, k_idx, k_fmt, pos, ratio, Q, R, Nmax, scores, n_vis, w.hist, bf16_scores, pm, s);
+    case 2: return launch_mfma<2>(q_idx, q_fmt, w_idx, k_idx, k_fmt, pos, ratio, Q, R, Nmax, scores, n_vis, w.hist, bf16_scores, pm, s);
+    case 3: return launch_mfma<3>(q_idx, q_fmt, w_idx, k_idx, k_fmt, pos, ratio, Q, R, Nmax, scores, n_vis, w.hist, bf16_scores, pm, s);
+    case 4: return launch_mfma<4>(q_idx, q_fmt, w_idx, k_idx, k_fmt, pos, ratio, Q, R, Nmax, scores, n_vis, w.hist, bf16_scores, pm, s);
+    case 5: return launch_mfma<5>(q_idx, q_fmt, w_idx, k_idx, k_fmt, pos, ratio, Q, R, Nmax, scores, n_vis, w.hist, bf16_scores, pm, s);
+    case 6: return launch_mfma<6>(q_idx, q_fmt, w_idx, k_idx, k_fmt, pos, ratio, Q, R, Nmax, scores, n_vis, w.hist, bf16_scores, pm, s);
+    case 7: return launch_mfma<7>(q_idx, q_fmt, w_idx, k_idx, k_fmt, pos, ratio, Q, R, Nmax, scores, n_vis, w.hist, bf16_scores, pm, s);
+    case 8: return launch_mfma<8>(q_idx, q_fmt, w_idx, k_idx, k_fmt, pos, ratio, Q, R, Nmax, scores, n_vis, w.hist, bf16_scores, pm, s);
     default: return hipErrorInvalidValue;
   }
 }

@@ -157,14 +157,18 @@ class CsaDecodeLayer:
         self.q = torch.from_numpy(q).to(device).to(qdt).reshape(B, 1, w.H, 512)
         self.sink = torch.from_numpy(sink).to(device)
         self.qi = torch.from_numpy(qi).to(device).to(qdt).reshape(B, 1, w.Hi, 128)
+        # the index call's queries: bf16 values, or for the FP4 indexer the
+        # MXFP4 rows themselves (scored by the block-scaled FP4 MFMA); self.qi
+        # keeps their values in bf16 (exact)
+        self.qi_arg = (self.qi, w.q_fmt)
         if w.key_fmt == "fp4_mx32":
-            # the FP4 indexer's queries carry MXFP4 values: quantize and decode
-            # them with the library's codec (exact in bf16)
             n = B * w.Hi
             rows = torch.empty((n, _lib.kv_row_bytes("fp4_mx32", 128)), dtype=torch.uint8,
                                device=device)
             _lib.kv_quantize(self.qi.reshape(n, 128), "bf16", rows, "fp4_mx32", n, 128)
             _lib.kv_dequantize(rows, "fp4_mx32", self.qi.reshape(n, 128), "bf16", n, 128)
+            if not w.extra.get("layer"):  # the layer's input step writes bf16 queries
+                self.qi_arg = (rows.reshape(B, 1, w.Hi, rows.shape[1]), "fp4_mx32")
         self.wi = torch.from_numpy(wi).to(device).reshape(B, 1, w.Hi)
         self.t = w.t
         self.pos = torch.full((B, 1), self.t, dtype=torch.int32, device=device)
@@ -263,7 +267,7 @@ class CsaDecodeLayer:
         index_fn = _lib.csa_index_topk_bf16 if key_fmt == "fp4_mx32" else _lib.csa_index_topk
 
         def index_topk():
-            index_fn(self.qi, w.q_fmt, self.wi, keys, key_fmt, self.pos, w.ratio, B, 1, w.Hi, N,
+            index_fn(*self.qi_arg, self.wi, keys, key_fmt, self.pos, w.ratio, B, 1, w.Hi, N,
                      w.topk, self.topk, None, self.ws_idx)
 
         def sparse_attn():
@@ -275,7 +279,7 @@ class CsaDecodeLayer:
         pc = self.cache
         if pc is not None:
             def index_topk():  # noqa: F811 -- the block-cache form of the same call
-                _lib.csa_index_topk_paged(self.qi, w.q_fmt, self.wi, keys, key_fmt, pc.bt,
+                _lib.csa_index_topk_paged(*self.qi_arg, self.wi, keys, key_fmt, pc.bt,
                                           self.pos, w.ratio, B, 1, w.Hi, w.topk,
                                           int(key_fmt == "fp4_mx32"), self.topk, None,
                                           self.ws_idx)

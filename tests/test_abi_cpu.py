@@ -93,6 +93,10 @@ def test_index_topk_validation():
     assert call(args(Hi=256)) == EUNSUP
     assert call(args(kf=3)) == EUNSUP           # FP4 keys: not on this path
     assert call(args(qf=0)) == EUNSUP           # bf16/fp8 keys need bf16 queries
+    assert call(args(qf=4)) == EUNSUP           # FP4 queries need FP4 keys
+    assert call(args(qf=4, kf=1)) == EUNSUP
+    assert call(args(qf=4, kf=4, Hi=24)) == EUNSUP
+    assert call(args(qf=4, kf=4, q=None)) == EINVAL
     assert call(args(kf=0)) == EUNSUP           # f32 keys need f32 queries
     assert call(args(topk=0)) == EUNSUP
     assert call(args(N=0)) == EINVAL

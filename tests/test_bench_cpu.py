@@ -64,14 +64,15 @@ def test_prefill_flops():
 
 
 def test_csa2_and_layer_bytes():
-    """CSA2 at m = 1: 262,144 FP4 index keys of 68 B per sequence, MXFP4 rows
+    """CSA2 at m = 1: 262,144 FP4 index keys of 68 B per sequence (and 64 FP4
+    query rows of 68 B), MXFP4 rows
     of 288 B read once for the group of 6 layers, each with its own window,
     q and output.
     The layer variant: every weight once (bf16) plus the token's inputs and
     outputs."""
     w = synth.WORKLOADS[6]
     ab = bench.algorithmic_bytes(w)
-    assert ab["csa_index_topk"] == 8 * (262144 * 68 + 64 * 128 * 2 + 64 * 4 + 512 * 4)
+    assert ab["csa_index_topk"] == 8 * (262144 * 68 + 64 * 68 + 64 * 4 + 512 * 4)
     assert ab["csa_sparse_attn_group"] == (8 * (512 * 288 + 512 * 4)
                                            + 6 * 8 * (128 * 528 + 2 * 64 * 512 * 2) + 6 * 64 * 4)
     assert "csa_sparse_attn_decode" not in ab

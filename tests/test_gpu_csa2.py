@@ -34,7 +34,7 @@ def test_csa2_m1_layer_group():
     ent_dev, keys_dev = layer.sets[0]
     sc = torch.empty((B, 1, N), dtype=torch.float32, device="cuda")
     ids2 = torch.empty_like(layer.topk)
-    _lib.csa_index_topk_bf16(layer.qi, "bf16", layer.wi, keys_dev, w.key_fmt, layer.pos, 1, B, 1,
+    _lib.csa_index_topk_bf16(*layer.qi_arg, layer.wi, keys_dev, w.key_fmt, layer.pos, 1, B, 1,
                              w.Hi, N, w.topk, ids2, sc, layer.ws_idx)
     torch.cuda.synchronize()
     ids = layer.topk.cpu().numpy()[:, 0]

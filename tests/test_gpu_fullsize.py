@@ -192,7 +192,7 @@ def test_fullsize_fp4_indexer():
     keys_dev = layer.sets[0][1]
     sc = torch.empty((B, 1, N), dtype=torch.float32, device="cuda")
     ids2 = torch.empty_like(layer.topk)
-    _lib.csa_index_topk_bf16(layer.qi, "bf16", layer.wi, keys_dev, "fp4_mx32", layer.pos, 4, B, 1,
+    _lib.csa_index_topk_bf16(*layer.qi_arg, layer.wi, keys_dev, "fp4_mx32", layer.pos, 4, B, 1,
                              w.Hi, N, w.topk, ids2, sc, layer.ws_idx)
     torch.cuda.synchronize()
     ids = layer.topk.cpu().numpy()[:, 0]

@@ -136,6 +136,59 @@ def test_fp4_keys_against_oracle(Hi, N):
             check_selection(out[b, qq], sc[b, qq], S_ref, tol, nv, k)
 
 
+@pytest.mark.parametrize("Hi,N,bf16_scores", [(64, 3000, False), (32, 5001, False),
+                                               (64, 4000, True), (16, 700, True)])
+def test_fp4_queries_and_keys(Hi, N, bf16_scores):
+    """FP4 queries and FP4 keys (MXFP4-MX32 rows of 68 B on both sides): the
+    block-scaled FP4 MFMA path.  Scores against the oracle's scores of the
+    decoded values within the float32 bound, the selection against the
+    oracle's, and both against the call that takes the same queries as bf16
+    values (the bf16 MFMA of the decoded values): E2M1 products are exact on
+    both paths, so the scores agree within the float32 accumulation bound and
+    the bf16-rounded scores' selections are checked as in the bf16 test."""
+    need_gpu()
+    B, Q, k = 2, 2, 512
+    w = synth.Workload(94, "t", B=B, ctx=4 * N, ratio=4, n_entries=N, Hi=Hi, key_fmt="fp4_mx32")
+    K = synth.index_keys(w)
+    qraw = synth.normal_batched(w.seed, synth.T_QIDX, B, (Q, Hi, 128))
+    qrows, qi = codec.store(qraw, "fp4_mx32")
+    qi = qi.astype(np.float32)
+    wi = synth.normal_batched(w.seed, synth.T_WIDX, B, (Q, Hi), (128 * Hi) ** -0.5)
+    pos = np.array([[4 * N - 1, 2047], [5, 4 * N + 900]], np.int32)
+    say(f"index_topk fp4 queries Hi={Hi} N={N} bf16_scores={bf16_scores}")
+    kdev = upload_rows(K, "fp4_mx32")
+    qdev = upload_rows(qraw, "fp4_mx32")
+    assert np.array_equal(qdev.cpu().numpy(), qrows)            # the oracle codec's bytes
+    Kv = codec.store(K, "fp4_mx32")[1]
+    fn = _lib.csa_index_topk_bf16 if bf16_scores else _lib.csa_index_topk
+    ws = _lib.workspace(_lib.csa_index_topk_workspace_size(B, Q, N, k))
+    res = {}
+    for qf, qa in (("fp4_mx32", qdev), ("bf16", bf16(qi))):
+        out = torch.empty((B, Q, k), dtype=torch.int32, device="cuda")
+        sc = torch.full((B, Q, N), float("nan"), dtype=torch.float32, device="cuda")
+        fn(qa, qf, f32(wi), kdev, "fp4_mx32", i32(pos), 4, B, Q, Hi, N, k, out, sc, ws)
+        res[qf] = (out.cpu().numpy(), sc.cpu().numpy())
+    out, sc = res["fp4_mx32"]
+    for b in range(B):
+        for qq in range(Q):
+            nv = int(indexer.n_visible(pos[b, qq], 4, N))
+            S_ref = indexer.scores(qi[b, qq].astype(np.float64), wi[b, qq], Kv[b], nv)
+            tol = score_bound(qi[b, qq].astype(np.float64), wi[b, qq].astype(np.float64),
+                              Kv[b][:nv])
+            if bf16_scores:
+                # the bf16-rounded scores: one bf16 step beyond the float32 bound
+                tol = tol + np.abs(S_ref) * 2.0 ** -8
+                s32 = sc[b, qq, :nv]
+                assert np.array_equal(codec.round_to_bf16(s32).astype(np.float32).view(np.uint32),
+                                      s32.view(np.uint32))
+                assert np.array_equal(out[b, qq], _TK.topk(s32, k, nv)), (b, qq)
+            err = np.abs(sc[b, qq, :nv] - S_ref)
+            assert np.all(err <= tol), (b, qq, err.max())
+            check_selection(out[b, qq], sc[b, qq], S_ref, tol, nv, k)
+            d = np.abs(sc[b, qq, :nv] - res["bf16"][1][b, qq, :nv])
+            assert np.all(d <= 2 * tol), (b, qq, d.max())
+
+
 @pytest.mark.parametrize("kfmt,Q", [("fp4_mx32", 2), ("fp8_mx32", 2), ("bf16", 13)])
 def test_bf16_scores(kfmt, Q):
     """csa_index_topk_bf16 (every kernel: per-query FP4, split FP8, query-tiled

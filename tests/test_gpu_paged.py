@@ -52,10 +52,14 @@ def make_pool(logical, counts, bs, rng, spare=5, holes=()):
 # ------------------------------------------------------------------ index + top-k
 @pytest.mark.parametrize("kfmt,bs,Hi,N", [("fp8_mx32", 32, 64, 3000), ("fp8_mx32", 64, 32, 2080),
                                           ("fp8_mx32", 128, 16, 1029), ("fp4_mx32", 32, 64, 3000),
+                                          ("fp4q", 32, 64, 3000), ("fp4q", 64, 16, 1029),
                                           ("bf16", 32, 32, 2000), ("f32", 32, 8, 700)])
 def test_index_topk_paged_equals_contiguous(kfmt, bs, Hi, N):
     """Several work-groups per row, ragged visible counts (n_vis not a multiple
-    of 32 or of a step), bf16 and float32 scores."""
+    of 32 or of a step), bf16 and float32 scores; fp4q: FP4 keys with FP4
+    queries (the block-scaled MFMA path)."""
+    fp4q = kfmt == "fp4q"
+    kfmt = "fp4_mx32" if fp4q else kfmt
     need_gpu()
     rng = np.random.default_rng(sum(map(ord, kfmt)) + bs)
     B, Q, k = 3, 2, 512
@@ -73,6 +77,8 @@ def test_index_topk_paged_equals_contiguous(kfmt, bs, Hi, N):
     kt = _lib.make_block_table(tdev, bs, pool.shape[0])
     up = f32 if qf == "f32" else bf16
     qd, wd, pd = up(qi), f32(wi), i32(pos)
+    if fp4q:
+        qf, qd = "fp4_mx32", upload_rows(qi, "fp4_mx32")
     ws = _lib.workspace(_lib.csa_index_topk_workspace_size(B, Q, Nmax, k))
     for bf in (0, 1):
         say(f"index_topk_paged {kfmt} bs={bs} Hi={Hi} N={N} bf16_scores={bf}")
