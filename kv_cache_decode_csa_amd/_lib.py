@@ -192,8 +192,11 @@ def make_compress_args(*, B, T, dim, ratio, head_dim, rotate, x, x_fmt, w_kv, w_
                        pool_blocks=0, state_slot=None):
     """block_table ([B, max_blocks] int32) makes `entries` a pool of
     pool_blocks blocks of block_entries rows; state_slot ([B] int32) makes
-    kv_state / score_state pools of slots (their first dimension)."""
-    return CompressArgs(int(B), int(T), int(dim), int(ratio), int(head_dim), int(rotate),
+    kv_state / score_state pools of slots (their first dimension).  The struct
+    holds only addresses, so it keeps the tensors alive: a temporary passed
+    here would otherwise be freed, and its memory handed to the next
+    allocation (a workspace, say), before the call that reads it."""
+    a = CompressArgs(int(B), int(T), int(dim), int(ratio), int(head_dim), int(rotate),
                         _ptr(x), _fmt(x_fmt), _ptr(w_kv), _ptr(w_gate), _fmt(w_fmt), _ptr(ape),
                         _ptr(norm_w), float(eps), _ptr(rope_cos), _ptr(rope_sin),
                         int(rope_cos.shape[0]), _ptr(start_pos), _ptr(kv_state),
@@ -202,12 +205,17 @@ def make_compress_args(*, B, T, dim, ratio, head_dim, rotate, x, x_fmt, w_kv, w_
                         int(block_table.shape[1]) if block_table is not None else 0,
                         int(block_entries), int(pool_blocks), _ptr(state_slot),
                         int(kv_state.shape[0]) if state_slot is not None else 0)
+    a._tensors = (x, w_kv, w_gate, ape, norm_w, rope_cos, rope_sin, start_pos, kv_state,
+                  score_state, entries, block_table, state_slot)
+    return a
 
 
 def make_block_table(table, block_entries, pool_blocks):
-    """csa_block_table over a [B, max_blocks] int32 device tensor (kept alive
-    by the caller while the struct is in use)."""
-    return BlockTable(_ptr(table), int(table.shape[1]), int(block_entries), int(pool_blocks))
+    """csa_block_table over a [B, max_blocks] int32 device tensor (the struct
+    keeps it alive)."""
+    bt = BlockTable(_ptr(table), int(table.shape[1]), int(block_entries), int(pool_blocks))
+    bt._tensors = (table,)
+    return bt
 
 
 def csa_compress_workspace_size(args):

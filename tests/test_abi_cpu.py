@@ -271,3 +271,38 @@ def test_block_cache_validation():
     a.state_slot = A16
     a.state_slots = 0
     assert L.csa_compress(ctypes.byref(a), A16, 1 << 20, None) == EINVAL
+
+
+def test_arg_structs_keep_their_tensors_alive(monkeypatch):
+    """The compress-args and block-table structs hold raw addresses, so they keep
+    the tensors they were built from: a temporary passed to the builder stays
+    allocated until the struct goes, and its memory cannot be handed to a
+    later allocation (a workspace) before the library call reads it.  (Host
+    tensors stand in for device tensors: only the references are checked.)"""
+    import gc
+    import weakref
+
+    import torch
+
+    def t(*shape, dtype=torch.float32):
+        return torch.zeros(shape, dtype=dtype)
+
+    monkeypatch.setattr(_lib, "_ptr", lambda x: 0 if x is None else x.data_ptr())
+    refs = []
+
+    def tracked(x):
+        refs.append(weakref.ref(x))
+        return x
+
+    a = _lib.make_compress_args(
+        B=1, T=4, dim=8, ratio=4, head_dim=128, rotate=0, x=tracked(t(1, 4, 8)), x_fmt="f32",
+        w_kv=tracked(t(8, 512)), w_gate=tracked(t(8, 512)), w_fmt="f32", ape=tracked(t(4, 512)),
+        norm_w=tracked(t(128)), eps=1e-6, rope_cos=tracked(t(8, 32)), rope_sin=tracked(t(8, 32)),
+        start_pos=tracked(t(1, dtype=torch.int32)), kv_state=tracked(t(1, 8, 256)),
+        score_state=tracked(t(1, 8, 256)), entries=tracked(t(1, 1, 128)), entry_fmt="f32")
+    bt = _lib.make_block_table(tracked(t(1, 4, dtype=torch.int32)), 32, 4)
+    gc.collect()
+    assert all(r() is not None for r in refs)
+    del a, bt
+    gc.collect()
+    assert all(r() is None for r in refs)
