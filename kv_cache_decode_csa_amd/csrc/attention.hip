@@ -309,8 +309,7 @@ __device__ __forceinline__ void attend_tile(const uint4 (&fr)[2][4], uint32_t vm
       z[rt][r] = ok ? z[rt][r] * zscale : -INFINITY;
       tmax = fmaxf(tmax, z[rt][r]);
     }
-  tmax = fmaxf(tmax, shfl_xor_f(tmax, 16));
-  tmax = fmaxf(tmax, shfl_xor_f(tmax, 32));
+  tmax = col_max4(tmax);
   const float m_new = fmaxf(st.m, tmax);
   const float alpha = (m_new == -INFINITY) ? 1.f : exp2f(st.m - m_new);
   float p[2][4];
@@ -322,8 +321,7 @@ __device__ __forceinline__ void attend_tile(const uint4 (&fr)[2][4], uint32_t vm
       p[rt][r] = (z[rt][r] == -INFINITY) ? 0.f : exp2f(z[rt][r] - m_new);
       psum += p[rt][r];
     }
-  psum += shfl_xor_f(psum, 16);
-  psum += shfl_xor_f(psum, 32);
+  psum = col_sum4(psum);
   st.l = st.l * alpha + psum;
   st.m = m_new;
   // k index 8 kq + i <-> row 4 kq + i (i < 4) or 16 + 4 kq + i - 4, as in the logits
@@ -515,8 +513,7 @@ __device__ __forceinline__ void attend_tile_all(const uint4 (&fr)[2][4], uint32_
         z[rt][r] = ok ? z[rt][r] * zscale : -INFINITY;
         tmax = fmaxf(tmax, z[rt][r]);
       }
-    tmax = fmaxf(tmax, shfl_xor_f(tmax, 16));
-    tmax = fmaxf(tmax, shfl_xor_f(tmax, 32));
+    tmax = col_max4(tmax);
     const float m_new = fmaxf(sm, tmax);
     const float alpha = (m_new == -INFINITY) ? 1.f : exp2f(sm - m_new);
     float p[2][4];
@@ -528,8 +525,7 @@ __device__ __forceinline__ void attend_tile_all(const uint4 (&fr)[2][4], uint32_
         p[rt][r] = (z[rt][r] == -INFINITY) ? 0.f : exp2f(z[rt][r] - m_new);
         psum += p[rt][r];
       }
-    psum += shfl_xor_f(psum, 16);
-    psum += shfl_xor_f(psum, 32);
+    psum = col_sum4(psum);
     sl = sl * alpha + psum;
     sm = m_new;
     Pl[w * 64 + lane] = make_uint4(pack_bf16x2(p[0][0], p[0][1]), pack_bf16x2(p[0][2], p[0][3]),

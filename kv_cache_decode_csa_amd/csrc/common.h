@@ -230,6 +230,29 @@ __device__ __forceinline__ void swap_halves32(float& x, float& y) {
   y = __builtin_bit_cast(float, b);
 }
 
+// Max / sum over the four lanes l, l ^ 16, l ^ 32, l ^ 48 (one column of a
+// 16 x 16 MFMA result), left in all four: the same values and the same
+// pairings as xor shuffles by 16 then 32 (max and + are commutative), with
+// row swaps on the vector ALU instead of LDS-crossbar permutes.
+__device__ __forceinline__ float col_max4(float v) {
+  float a = v, b = v;
+  swap_rows16(a, b);   // a, b: this lane's row and its partner row (l ^ 16)
+  v = fmaxf(a, b);
+  a = v;
+  b = v;
+  swap_halves32(a, b);
+  return fmaxf(a, b);
+}
+__device__ __forceinline__ float col_sum4(float v) {
+  float a = v, b = v;
+  swap_rows16(a, b);
+  v = a + b;
+  a = v;
+  b = v;
+  swap_halves32(a, b);
+  return a + b;
+}
+
 // Inclusive prefix sum over the 64 lanes of a wave: shifts within rows of 16
 // lanes, then the row totals carried up (vector ALU lane moves only).
 __device__ __forceinline__ uint32_t wave_prefix_incl(uint32_t v) {
