@@ -263,14 +263,23 @@ struct SoftmaxState {
   float m;      // running max (log2 units) of head r16
   float l;      // running denominator (without the sink)
   f32x4_t o[8]; // O for heads 4 kq + r, dims 128 w + 16 dt + r16
+  int par;      // which of the two partial-logit buffers the next tile uses
 };
 
 // One 32-row tile: partial logits over this wave's dims, fixed-order sum of
-// the 4 waves' partials through LDS, online softmax, O += P C.
+// the 4 waves' partials through LDS, online softmax, O += P C.  One barrier
+// per tile: R is this wave's own region (its earlier reads come first in
+// program order), and consecutive tiles write alternate partial-logit
+// buffers, so a wave that starts tile t + 1 cannot overwrite what a slower
+// wave still reads of tile t (reaching tile t + 2 takes every wave past tile
+// t + 1's barrier).
 __device__ __forceinline__ void attend_tile(const uint4 (&fr)[2][4], uint32_t vmask,
                                             const uint4 (&qa)[4], float zscale, int w, int lane,
-                                            uint16_t* R, float4 (*Sp)[2][64], SoftmaxState& st) {
+                                            uint16_t* R, float4 (*Spp)[4][2][64],
+                                            SoftmaxState& st) {
   const int r16 = lane & 15, kq = lane >> 4;
+  float4 (*Sp)[2][64] = Spp[st.par];
+  st.par ^= 1;
   f32x4_t sacc[2];
 #pragma unroll
   for (int rt = 0; rt < 2; ++rt) {
@@ -279,7 +288,6 @@ __device__ __forceinline__ void attend_tile(const uint4 (&fr)[2][4], uint32_t vm
     for (int s = 0; s < 4; ++s)
       sacc[rt] = mfma16x16x32(as_bf16x8(fr[rt][s]), as_bf16x8(qa[s]), sacc[rt]);
   }
-  __syncthreads();  // the previous tile's readers of Sp / R are done
   Sp[w][0][lane] = make_float4(sacc[0][0], sacc[0][1], sacc[0][2], sacc[0][3]);
   Sp[w][1][lane] = make_float4(sacc[1][0], sacc[1][1], sacc[1][2], sacc[1][3]);
 #pragma unroll
@@ -352,7 +360,7 @@ template <int F, class RowFn>
 __device__ __forceinline__ void run_rows(int64_t j0, int64_t j1, RowFn row_of,
                                          const uint8_t* stand_in, const uint4 (&qa)[4],
                                          float zscale, int w, int lane, uint16_t* R,
-                                         float4 (*Sp)[2][64], SoftmaxState& st) {
+                                         float4 (*Sp)[4][2][64], SoftmaxState& st) {
   const int r16 = lane & 15, kq = lane >> 4;
   auto load_tile = [&](int64_t jt, Raw<F> (&f)[2], uint32_t& vm) {
     vm = 0;
@@ -479,7 +487,10 @@ __device__ __forceinline__ void attend_tile_all(const uint4 (&fr)[2][4], uint32_
 #pragma unroll
       for (int rt = 0; rt < 2; ++rt)
         sacc[ht][rt] = mfma16x16x32(as_bf16x8(fr[rt][s]), as_bf16x8(qa[ht][s]), sacc[ht][rt]);
-  __syncthreads();  // the previous tile's readers of Sp / R / Pl / Al are done
+  // No barrier before the writes: R is this wave's own region, the previous
+  // tile's reads of Sp all come before its P barrier (which this wave has
+  // passed), and Pl / Al are written only after the next barrier, which every
+  // wave reaches after its previous P.C.
 #pragma unroll
   for (int ht = 0; ht < HT; ++ht)
 #pragma unroll
@@ -782,7 +793,7 @@ __global__ void __launch_bounds__(kAttnThreads) attn_mfma_kernel(AttnArgs a, int
                                                                  int nchunks, int64_t units,
                                                                  Partial* part) {
   __shared__ uint16_t Rl[4][kTile * kRPitch];
-  __shared__ float4 Sp[4][2][64];
+  __shared__ float4 Sp[2][4][2][64];
   __shared__ int32_t Ids[LONG ? kChunkCsaLong : 1];
 
   const AttnItem it = attn_item(a, nchunks, units);
@@ -847,6 +858,7 @@ __global__ void __launch_bounds__(kAttnThreads) attn_mfma_kernel(AttnArgs a, int
   SoftmaxState st;
   st.m = -INFINITY;
   st.l = 0.f;
+  st.par = 0;
 #pragma unroll
   for (int dt = 0; dt < 8; ++dt) st.o[dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   uint16_t* R = Rl[w];
