@@ -308,6 +308,13 @@ csa_status csa_topk(const float* scores, const int32_t* n_valid, int64_t R, int6
  * F32 (only with q_fmt F32), BF16, FP8_MX32, FP4_E4M3_16; sink: [H] float;
  * rope tables [rope_rows][32] (positions clamped to the last row); out:
  * [B][Q][H][512] in out_fmt (F32 or BF16, rounded once).
+ * Batch invariance ("DeepSeek-V4 deep dive" section 10.5, the systems box's
+ * batch-invariant decode attention): a unit's output depends only on its own
+ * inputs, never on B or on the other units.  The
+ * library combines a list's fixed 64-row chunks in chunk order whether one
+ * work-group takes the whole list (large batches) or each chunk has its own
+ * work-group (small batches); the workspace, which holds the chunks' partial
+ * results in the second case, may be empty (size 0) in the first.
  * Requirements: H % 16 == 0; win_rows >= 128 in ring mode; 0 <= topk <= 8192.
  */
 size_t csa_sparse_attn_workspace_size(int B, int Q, int H, int topk);

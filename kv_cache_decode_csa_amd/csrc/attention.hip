@@ -142,6 +142,40 @@ __device__ __forceinline__ void store_out(const AttnArgs& a, int64_t unit, int h
   else ((uint16_t*)a.out)[i] = f32_to_bf16(v);
 }
 
+// The chunks of a list are combined in chunk order by an online merge: a
+// running maximum M and sum L per head (log2 units) and O rescaled at every
+// step.  The merge kernel and the whole-list kernel both combine with these
+// functions, in the same order, so they give the same bits.
+// Folds chunk (mc, lc) into (M, L); false for an empty chunk (mc = -inf),
+// else fa and fb, the factors of the old O and of the chunk's O.
+__device__ __forceinline__ bool merge_step(float& M, float& L, float mc, float lc, float& fa,
+                                           float& fb) {
+  if (mc == -INFINITY) return false;
+  const float mn = fmaxf(M, mc);
+  fa = exp2f(M - mn);  // 0 while M is -inf
+  fb = exp2f(mc - mn);
+  L = fmaf(lc, fb, L * fa);
+  M = mn;
+  return true;
+}
+__device__ __forceinline__ float merge_o(float o, float oc, float fa, float fb) {
+  return fmaf(oc, fb, o * fa);
+}
+// 1 / (L + 2^(sink - M)), the sink counted in the denominator only; 0 for a
+// list with no visible row.
+__device__ __forceinline__ float merge_inv(float M, float L, float sink2) {
+  const float den = (M == -INFINITY) ? 0.f : L + exp2f(sink2 - M);
+  return den > 0.f ? 1.f / den : 0.f;
+}
+// Inverse rotation of the pair (x, y) of dims (2k, 2k + 1) by the angle with
+// cosine c and sine s.
+__device__ __forceinline__ float unrot_even(float x, float y, float c, float s) {
+  return fmaf(x, c, y * s);
+}
+__device__ __forceinline__ float unrot_odd(float x, float y, float c, float s) {
+  return fmaf(y, c, -(x * s));
+}
+
 // ------------------------------------------------------------------ MFMA kernel
 typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2_t;
 typedef short v4i16_t __attribute__((ext_vector_type(4)));
@@ -355,12 +389,14 @@ __device__ __forceinline__ void attend_tile(const uint4 (&fr)[2][4], uint32_t vm
 // Rows [j0, j1) of the list, all in format F.  Two register sets alternate:
 // while one tile is computed the next tile's rows are in flight.  Absent rows
 // (and rows past j1) are loaded from `stand_in`, a row of the same buffer, and
-// zeroed by the validity mask.
-template <int F, class RowFn>
+// zeroed by the validity mask.  after_pair() runs after every two tiles, that
+// is after rows [j0 + 64 i, j0 + 64 (i + 1)).
+template <int F, class RowFn, class PairFn>
 __device__ __forceinline__ void run_rows(int64_t j0, int64_t j1, RowFn row_of,
                                          const uint8_t* stand_in, const uint4 (&qa)[4],
                                          float zscale, int w, int lane, uint16_t* R,
-                                         float4 (*Sp)[4][2][64], SoftmaxState& st) {
+                                         float4 (*Sp)[4][2][64], SoftmaxState& st,
+                                         PairFn after_pair) {
   const int r16 = lane & 15, kq = lane >> 4;
   auto load_tile = [&](int64_t jt, Raw<F> (&f)[2], uint32_t& vm) {
     vm = 0;
@@ -394,6 +430,7 @@ __device__ __forceinline__ void run_rows(int64_t j0, int64_t j1, RowFn row_of,
     compute_tile(fa, va);
     load_tile(jt + 2 * kTile, fa, va);
     if (jt + kTile < j1) compute_tile(fb, vb);
+    after_pair();  // rows [jt, jt + 64) done
   }
 }
 
@@ -786,12 +823,23 @@ __device__ __forceinline__ AttnItem attn_item(const AttnArgs& a, int nchunks, in
   return it;
 }
 
-// LONG: chunks of kChunkCsaLong rows, whose top-k ids are staged in LDS
-// (otherwise chunks of kChunkCsa rows, ids held in registers).
-template <int WF, int EF, bool LONG>
+// MODE kAttnChunks: chunks of kChunkCsa rows, ids held in registers, a
+// partial per chunk.  MODE kAttnLong: chunks of kChunkCsaLong rows, whose
+// top-k ids are staged in LDS.  MODE kAttnWhole: one work-group per list of
+// at most kChunkCsaLong rows (ids in LDS) that runs the kChunkCsa-row chunks
+// of kAttnChunks one after another, each with its own softmax state, and
+// folds every chunk into a running merge as it ends, with the merge kernel's
+// arithmetic and order: the output is bit for bit that of kAttnChunks and
+// the merge, without partials in memory.
+enum { kAttnChunks = 0, kAttnLong = 1, kAttnWhole = 2 };
+template <int WF, int EF, int MODE>
 __global__ void __launch_bounds__(kAttnThreads) attn_mfma_kernel(AttnArgs a, int chunk_rows,
                                                                  int nchunks, int64_t units,
                                                                  Partial* part) {
+  constexpr bool LONG = MODE != kAttnChunks;  // ids staged in LDS
+  constexpr bool WHOLE = MODE == kAttnWhole;
+  static_assert(kChunkCsa == 2 * kTile, "a 64-row chunk is one pair of tiles of run_rows");
+  static_assert(kWindow % kChunkCsa == 0, "chunks do not straddle the window and the entries");
   __shared__ uint16_t Rl[4][kTile * kRPitch];
   __shared__ float4 Sp[2][4][2][64];
   __shared__ int32_t Ids[LONG ? kChunkCsaLong : 1];
@@ -863,6 +911,35 @@ __global__ void __launch_bounds__(kAttnThreads) attn_mfma_kernel(AttnArgs a, int
   for (int dt = 0; dt < 8; ++dt) st.o[dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   uint16_t* R = Rl[w];
 
+  // whole lists: the running merge of the chunks ended so far (head r16 for
+  // M and L; O for heads 4 kq + r, dims 128 w + 16 dt + r16, as st.o)
+  float Mw = -INFINITY, Lw = 0.f;
+  f32x4_t ow[8];
+#pragma unroll
+  for (int dt = 0; dt < 8; ++dt) ow[dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  auto after_pair = [&]() {
+    if (!WHOLE) return;
+    float fa = 1.f, fb = 0.f;
+    const int live = merge_step(Mw, Lw, st.m, st.l, fa, fb) ? 1 : 0;
+    float ga[4], gb[4];
+    int gl[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      ga[r] = __shfl(fa, 4 * kq + r, 64);
+      gb[r] = __shfl(fb, 4 * kq + r, 64);
+      gl[r] = __shfl(live, 4 * kq + r, 64);
+    }
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        if (gl[r]) ow[dt][r] = merge_o(ow[dt][r], st.o[dt][r], ga[r], gb[r]);
+      st.o[dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    }
+    st.m = -INFINITY;
+    st.l = 0.f;
+  };
+
   // window rows [j_begin, min(j_end, 128))
   const int64_t jw = j_end < kWindow ? j_end : kWindow;
   if (j_begin < jw) {
@@ -871,7 +948,7 @@ __global__ void __launch_bounds__(kAttnThreads) attn_mfma_kernel(AttnArgs a, int
     };
     const uint8_t* win0 =
         (const uint8_t*)a.win + (size_t)(wsq < 0 ? 0 : wsq) * (size_t)a.win_rows * a.win_rb;
-    run_rows<WF>(j_begin, jw, win_row, win0, qa, zscale, w, lane, R, Sp, st);
+    run_rows<WF>(j_begin, jw, win_row, win0, qa, zscale, w, lane, R, Sp, st, after_pair);
   }
   // entry rows [max(j_begin, 128), j_end)
   const int64_t je = j_begin > kWindow ? j_begin : kWindow;
@@ -887,7 +964,7 @@ __global__ void __launch_bounds__(kAttnThreads) attn_mfma_kernel(AttnArgs a, int
         const int64_t r = pg ? (int64_t)PgIds[j - j_begin] : (e < nvis ? e : -1);
         return r >= 0 ? ebase + (size_t)r * a.ent_rb : nullptr;
       };
-      run_rows<EF>(je, j_end, ent_row, ebase, qa, zscale, w, lane, R, Sp, st);
+      run_rows<EF>(je, j_end, ent_row, ebase, qa, zscale, w, lane, R, Sp, st, after_pair);
     } else {
       auto ent_row = [&](int64_t j) -> const uint8_t* {
         int32_t e = -1;
@@ -902,11 +979,34 @@ __global__ void __launch_bounds__(kAttnThreads) attn_mfma_kernel(AttnArgs a, int
         }
         return e >= 0 ? ebase + (size_t)e * a.ent_rb : nullptr;
       };
-      run_rows<EF>(je, j_end, ent_row, ebase, qa, zscale, w, lane, R, Sp, st);
+      run_rows<EF>(je, j_end, ent_row, ebase, qa, zscale, w, lane, R, Sp, st, after_pair);
     }
   }
 
   // ---- chunk result
+  if (WHOLE) {  // the merge kernel's finish on the running merge
+    const float inv = merge_inv(Mw, Lw, sinks[16 * hg + r16] * kLog2e);
+    float iv[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) iv[r] = __shfl(inv, 4 * kq + r, 64);
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) {
+      const int d = 128 * w + 16 * dt + r16;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        float v = ow[dt][r] * iv[r];
+        const float nb = shfl_xor_f(v, 1);  // pair partner (d ^ 1)
+        if (d >= kHeadDim - kRopeDims) {
+          const int k = (d - (kHeadDim - kRopeDims)) >> 1;
+          const float c = a.rope_cos[(int64_t)rr * 32 + k];
+          const float sn = a.rope_sin[(int64_t)rr * 32 + k];
+          v = (d & 1) ? unrot_odd(nb, v, c, sn) : unrot_even(v, nb, c, sn);
+        }
+        store_out(a, unit, 16 * hg + 4 * kq + r, d, v);
+      }
+    }
+    return;
+  }
   if (nchunks > 1) {
     Partial* P = part + (unit * (a.H / 16) + hg) * (int64_t)nchunks + chunk;
     if (w == 0 && lane < 16) {
@@ -947,8 +1047,8 @@ __global__ void __launch_bounds__(kAttnThreads) attn_mfma_kernel(AttnArgs a, int
 
 // ------------------------------------------------------------------ merge
 // One work-group per (unit, head group, 64-dim slice); thread t owns head t/16
-// and 4 dims.  Chunks are combined in index order; each batch of 16 chunks is
-// loaded before any is combined, so the loads overlap.
+// and 4 dims.  Chunks are folded in index order by the online merge; each
+// batch of 16 chunks is loaded before any is folded, so the loads overlap.
 constexpr int kMergeBatch = 16;
 static_assert(kMergeChunks <= kMergeBatch, "a dense list merges in one round");
 
@@ -967,48 +1067,28 @@ __global__ void __launch_bounds__(kAttnThreads) attn_merge_kernel(AttnArgs a, in
   float M = -INFINITY;
   float L = 0.f;
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-  auto fold = [&](float mc, float lc, float4 oc) {
-    if (mc == -INFINITY) return;
-    const float wgt = exp2f(mc - M);
-    L += lc * wgt;
-    acc.x += oc.x * wgt; acc.y += oc.y * wgt; acc.z += oc.z * wgt; acc.w += oc.w * wgt;
-  };
-  if (nchunks <= kMergeBatch) {
-    // every chunk's values in one round of loads
+  for (int c0 = 0; c0 < nchunks; c0 += kMergeBatch) {
+    // a batch of chunks loaded in one round, then folded in chunk order
     float mc[kMergeBatch], lc[kMergeBatch];
     float4 oc[kMergeBatch];
 #pragma unroll
     for (int i = 0; i < kMergeBatch; ++i) {
-      const int c = i < nchunks ? i : nchunks - 1;
+      const int c = c0 + i < nchunks ? c0 + i : nchunks - 1;
       mc[i] = P[c].m[h];
       lc[i] = P[c].l[h];
       oc[i] = *(const float4*)(P[c].o + h * kHeadDim + d0);
     }
 #pragma unroll
-    for (int i = 0; i < kMergeBatch; ++i)
-      if (i < nchunks) M = fmaxf(M, mc[i]);
-#pragma unroll
-    for (int i = 0; i < kMergeBatch; ++i)
-      if (i < nchunks) fold(mc[i], lc[i], oc[i]);
-  } else {
-    for (int c = 0; c < nchunks; ++c) M = fmaxf(M, P[c].m[h]);
-    for (int c0 = 0; c0 < nchunks; c0 += kMergeBatch) {
-      float mc[kMergeBatch], lc[kMergeBatch];
-      float4 oc[kMergeBatch];
-#pragma unroll
-      for (int i = 0; i < kMergeBatch; ++i) {
-        const int c = c0 + i < nchunks ? c0 + i : nchunks - 1;
-        mc[i] = P[c].m[h];
-        lc[i] = P[c].l[h];
-        oc[i] = *(const float4*)(P[c].o + h * kHeadDim + d0);
-      }
-#pragma unroll
-      for (int i = 0; i < kMergeBatch; ++i)
-        if (c0 + i < nchunks) fold(mc[i], lc[i], oc[i]);
+    for (int i = 0; i < kMergeBatch; ++i) {
+      float fa, fb;
+      if (c0 + i >= nchunks || !merge_step(M, L, mc[i], lc[i], fa, fb)) continue;
+      acc.x = merge_o(acc.x, oc[i].x, fa, fb);
+      acc.y = merge_o(acc.y, oc[i].y, fa, fb);
+      acc.z = merge_o(acc.z, oc[i].z, fa, fb);
+      acc.w = merge_o(acc.w, oc[i].w, fa, fb);
     }
   }
-  const float den = (M == -INFINITY) ? 0.f : L + exp2f(sink2 - M);
-  const float inv = den > 0.f ? 1.f / den : 0.f;
+  const float inv = merge_inv(M, L, sink2);
   float v[4] = {acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv};
   if (d0 >= kHeadDim - kRopeDims) {
 #pragma unroll
@@ -1017,8 +1097,8 @@ __global__ void __launch_bounds__(kAttnThreads) attn_merge_kernel(AttnArgs a, in
       const float c = a.rope_cos[(int64_t)rr * 32 + k];
       const float sn = a.rope_sin[(int64_t)rr * 32 + k];
       const float x = v[2 * j], y = v[2 * j + 1];
-      v[2 * j] = x * c + y * sn;
-      v[2 * j + 1] = -x * sn + y * c;
+      v[2 * j] = unrot_even(x, y, c, sn);
+      v[2 * j + 1] = unrot_odd(x, y, c, sn);
     }
   }
   const int64_t obase = (unit * a.H + 16 * hg + h) * (int64_t)kHeadDim + d0;
@@ -1127,8 +1207,22 @@ static bool attn_all_heads(const AttnArgs& a) {
   return attn_sparse_all_heads(a);
 }
 
+// Top-k lists of at most kChunkCsaLong rows take one work-group per list
+// (kAttnWhole) once the batch gives at least one (unit, head group) item per
+// CU; smaller batches split each list over work-groups of kChunkCsa rows and
+// merge the partials.  Both fold the same 64-row chunks in the same order with
+// the same arithmetic, so the output does not depend on which runs, or on the
+// batch.  Measured at top-512, FP8 rows, 64 heads: 56 against 65 us at 64
+// sequences, 76 against 125 us at 128; at 48 sequences 54 against 52 us.
+constexpr int64_t kWholeMinItems = 256;
+static bool attn_whole_lists(const AttnArgs& a) {
+  return !a.dense && a.q_fmt != CSA_F32 && !attn_long_chunks(a) &&
+         attn_list_len(a) <= kChunkCsaLong &&
+         (int64_t)a.B * a.Q * (a.H / 16) >= kWholeMinItems;
+}
+
 int attn_chunk_rows(const AttnArgs& a) {
-  if (attn_long_chunks(a)) return kChunkCsaLong;
+  if (attn_long_chunks(a) || attn_whole_lists(a)) return kChunkCsaLong;
   if (!attn_all_heads(a)) return a.dense ? kChunkHca : kChunkCsa;
   return (int)dense_all_chunk_rows(a);
 }
@@ -1151,26 +1245,27 @@ static size_t attn_dyn_lds(const AttnArgs& a, int cr) {
   return (a.dense && a.ent_pages.table) ? (size_t)cr * sizeof(int32_t) : 0;
 }
 
-template <int WF, bool LONG>
+template <int WF, int MODE>
 static void launch_mfma_wl(const AttnArgs& a, int nc, int64_t nu, dim3 grid, Partial* part,
                            hipStream_t s) {
   const int cr = attn_chunk_rows(a);
   const size_t lds = attn_dyn_lds(a, cr);
   if (a.ent_fmt == CSA_BF16)
-    hipLaunchKernelGGL((attn_mfma_kernel<WF, CSA_BF16, LONG>), grid, dim3(kAttnThreads), lds, s, a, cr, nc, nu, part);
+    hipLaunchKernelGGL((attn_mfma_kernel<WF, CSA_BF16, MODE>), grid, dim3(kAttnThreads), lds, s, a, cr, nc, nu, part);
   else if (a.ent_fmt == CSA_FP8_MX32)
-    hipLaunchKernelGGL((attn_mfma_kernel<WF, CSA_FP8_MX32, LONG>), grid, dim3(kAttnThreads), lds, s, a, cr, nc, nu, part);
+    hipLaunchKernelGGL((attn_mfma_kernel<WF, CSA_FP8_MX32, MODE>), grid, dim3(kAttnThreads), lds, s, a, cr, nc, nu, part);
   else if (a.ent_fmt == CSA_MIX576)
-    hipLaunchKernelGGL((attn_mfma_kernel<WF, CSA_MIX576, LONG>), grid, dim3(kAttnThreads), lds, s, a, cr, nc, nu, part);
+    hipLaunchKernelGGL((attn_mfma_kernel<WF, CSA_MIX576, MODE>), grid, dim3(kAttnThreads), lds, s, a, cr, nc, nu, part);
   else
-    hipLaunchKernelGGL((attn_mfma_kernel<WF, CSA_FP4_E4M3_16, LONG>), grid, dim3(kAttnThreads), lds, s, a, cr, nc, nu, part);
+    hipLaunchKernelGGL((attn_mfma_kernel<WF, CSA_FP4_E4M3_16, MODE>), grid, dim3(kAttnThreads), lds, s, a, cr, nc, nu, part);
 }
 
 template <int WF>
 static void launch_mfma_w(const AttnArgs& a, int nc, int64_t nu, dim3 grid, Partial* part,
                           hipStream_t s) {
-  if (attn_long_chunks(a)) launch_mfma_wl<WF, true>(a, nc, nu, grid, part, s);
-  else launch_mfma_wl<WF, false>(a, nc, nu, grid, part, s);
+  if (attn_long_chunks(a)) launch_mfma_wl<WF, kAttnLong>(a, nc, nu, grid, part, s);
+  else if (attn_whole_lists(a)) launch_mfma_wl<WF, kAttnWhole>(a, nc, nu, grid, part, s);
+  else launch_mfma_wl<WF, kAttnChunks>(a, nc, nu, grid, part, s);
 }
 
 // Fewer than two work-groups per CU would leave one wave per SIMD with a

@@ -177,6 +177,63 @@ def test_csa_many_queries_other_head_counts(tables, H, k):
         close_bf16(got[0, qq], ref)
 
 
+@pytest.mark.parametrize("efmt,wfmt,k,H,B", [("fp8_mx32", "fp8_mx32", 512, 64, 70),
+                                             ("bf16", "bf16", 512, 64, 70),
+                                             ("fp4_e4m3_16", "fp8_mx32", 37, 64, 70),
+                                             ("mix576", "fp8_mx32", 512, 64, 70),
+                                             ("fp8_mx32", "bf16", 200, 128, 34)])
+def test_batch_invariant_whole_lists(tables, efmt, wfmt, k, H, B):
+    """A batch with at least 256 (sequence, 16-head group) items runs one
+    work-group per list; a small batch splits each list into 64-row chunks
+    and merges them.  Every sequence's output must be the same bits either
+    way (the decode output does not depend on the batch), and equal the
+    oracle within the bf16 tolerance."""
+    cos, sin = tables
+    N, sub = 600, 10
+    assert _lib.csa_sparse_attn_workspace_size(B, 1, H, k) <= 1   # one work-group per list
+    assert _lib.csa_sparse_attn_workspace_size(sub, 1, H, k) > 1  # chunks and partials
+    rng = np.random.default_rng(4000 + k + H)
+    q = synth.bf16_round(rng.standard_normal((B, 1, H, 512)).astype(np.float32))
+    win = rng.standard_normal((B, 128, 512)).astype(np.float32)
+    ent = rng.standard_normal((B, N, 512)).astype(np.float32)
+    if efmt == "bf16":
+        ent = synth.bf16_round(ent)
+    if wfmt == "bf16":
+        win = synth.bf16_round(win)
+    sink = rng.standard_normal(H).astype(np.float32)
+    # full lists, padded lists (few visible entries) and partial windows
+    pos = rng.integers(4 * N - 8, 4 * N + 5000, size=(B, 1)).astype(np.int32)
+    pos[1::7, 0] = rng.integers(100, 4 * k, size=len(pos[1::7]))
+    ids = np.stack([gen_ids(rng, min((int(pos[b, 0]) + 1) // 4, N), k, N)
+                    for b in range(B)]).reshape(B, 1, k)
+    say(f"batch invariance {efmt}/{wfmt} k={k} H={H}: B={B} against sub-batches of {sub}")
+    qd, wd, ed = bf16(q), upload_rows(win, wfmt), upload_rows(ent, efmt)
+    idd, pd, sd = i32(ids), i32(pos), f32(sink)
+
+    def run(b0, b1):
+        n = b1 - b0
+        sl = [t[b0:b1].clone() for t in (qd, wd, ed, idd, pd)]  # fresh, aligned buffers
+        out = torch.empty((n, 1, H, 512), dtype=torch.bfloat16, device="cuda")
+        ws = _lib.workspace(_lib.csa_sparse_attn_workspace_size(n, 1, H, k))
+        _lib.csa_sparse_attn_decode(sl[0], "bf16", sl[1], wfmt, _lib.WIN_RING128, None, 128,
+                                    sl[2], efmt, N, sl[3], k, sl[4], n, 1, H, sd,
+                                    512 ** -0.5, cos, sin, out, "bf16", ws)
+        return out
+
+    whole = run(0, B)
+    split = torch.cat([run(b0, min(b0 + sub, B)) for b0 in range(0, B, sub)])
+    torch.cuda.synchronize()
+    same = torch.eq(whole.view(torch.int16), split.view(torch.int16))
+    assert bool(same.all()), f"{int((~same).sum())} outputs differ between the two work splits"
+    got = to_np(whole)
+    winv = codec.store(win[[0, 1, B - 1]], wfmt)[1]
+    entv = codec.store(ent[[0, 1, B - 1]], efmt)[1]
+    for i, b in enumerate([0, 1, B - 1]):
+        ref = oracle_sparse(q[b, 0].astype(np.float64), winv[i], entv[i], ids[b, 0], sink,
+                            int(pos[b, 0]))
+        close_bf16(got[b, 0], ref)
+
+
 @pytest.mark.parametrize("efmt", ["bf16", "fp8_mx32", "fp4_e4m3_16", "mix576"])
 def test_hca_decode(tables, efmt):
     cos, sin = tables
