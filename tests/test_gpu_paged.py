@@ -161,19 +161,20 @@ def _slots(B, n_slots, rng):
     return rng.permutation(n_slots)[:B].astype(np.int32)
 
 
-@pytest.mark.parametrize("Q,H,qf,ef,bs", [(1, 64, "bf16", "fp8_mx32", 32),
-                                          (1, 32, "bf16", "fp4_e4m3_16", 64),
-                                          (16, 64, "bf16", "fp8_mx32", 32),
-                                          (16, 32, "bf16", "bf16", 32),
-                                          (1, 16, "f32", "f32", 32)])
-def test_sparse_attn_paged_equals_contiguous(Q, H, qf, ef, bs):
+@pytest.mark.parametrize("Q,H,qf,ef,bs,B,N", [(1, 64, "bf16", "fp8_mx32", 32, 3, 1500),
+                                              (1, 32, "bf16", "fp4_e4m3_16", 64, 3, 1500),
+                                              (16, 64, "bf16", "fp8_mx32", 32, 3, 1500),
+                                              (16, 32, "bf16", "bf16", 32, 3, 1500),
+                                              (1, 16, "f32", "f32", 32, 3, 1500),
+                                              (1, 64, "bf16", "fp8_mx32", 32, 70, 600)])
+def test_sparse_attn_paged_equals_contiguous(Q, H, qf, ef, bs, B, N):
     """64-row chunks (one query), 640-row chunks (16 queries; 64 heads take the
-    all-heads kernel), the float32 kernel.  Ids include -1, ids past Nmax and
-    ids in an unallocated block; those are absent, as -1 is in the
-    contiguous call."""
+    all-heads kernel), the float32 kernel, and one work-group per whole list
+    (70 sequences of 64 heads).  Ids include -1, ids past Nmax and ids in an
+    unallocated block; those are absent, as -1 is in the contiguous call."""
     need_gpu()
     rng = np.random.default_rng(Q * 100 + H)
-    B, k, N = 3, 512, 1500
+    k = 512
     Nmax = -(-N // bs) * bs
     E = rng.standard_normal((B, Nmax, 512)).astype(np.float32)
     win = rng.standard_normal((B, 128, 512)).astype(np.float32)
