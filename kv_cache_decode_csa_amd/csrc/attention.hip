@@ -144,22 +144,22 @@ __device__ __forceinline__ void store_out(const AttnArgs& a, int64_t unit, int h
 
 // The chunks of a list are combined in chunk order by an online merge: a
 // running maximum M and sum L per head (log2 units) and O rescaled at every
-// step.  The merge kernel and the whole-list kernel both combine with these
-// functions, in the same order, so they give the same bits.
-// Folds chunk (mc, lc) into (M, L); false for an empty chunk (mc = -inf),
-// else fa and fb, the factors of the old O and of the chunk's O.
-__device__ __forceinline__ bool merge_step(float& M, float& L, float mc, float lc, float& fa,
-                                           float& fb) {
-  if (mc == -INFINITY) return false;
+// step; a chunk with no visible row (mc = -inf) is skipped.  The merge kernel
+// and the whole-list kernel both combine with these functions, in the same
+// order, so they give the same bits.
+// The running maximum after chunk mc, and the factors of the old sums (fa)
+// and of the chunk's (fb).
+// (The hardware exponential: both arguments are <= 0, and a factor below
+// 2^-126 only scales terms that the factor-1 chunk outweighs.)
+__device__ __forceinline__ float merge_factors(float M, float mc, float& fa, float& fb) {
   const float mn = fmaxf(M, mc);
-  fa = exp2f(M - mn);  // 0 while M is -inf
-  fb = exp2f(mc - mn);
-  L = fmaf(lc, fb, L * fa);
-  M = mn;
-  return true;
+  fa = __builtin_amdgcn_exp2f(M - mn);  // 0 while M is -inf
+  fb = __builtin_amdgcn_exp2f(mc - mn);
+  return mn;
 }
-__device__ __forceinline__ float merge_o(float o, float oc, float fa, float fb) {
-  return fmaf(oc, fb, o * fa);
+// One sum (L, or an element of O) after folding in the chunk's value xc.
+__device__ __forceinline__ float merge_o(float x, float xc, float fa, float fb) {
+  return fmaf(xc, fb, x * fa);
 }
 // 1 / (L + 2^(sink - M)), the sink counted in the denominator only; 0 for a
 // list with no visible row.
@@ -920,7 +920,11 @@ __global__ void __launch_bounds__(kAttnThreads) attn_mfma_kernel(AttnArgs a, int
   auto after_pair = [&]() {
     if (!WHOLE) return;
     float fa = 1.f, fb = 0.f;
-    const int live = merge_step(Mw, Lw, st.m, st.l, fa, fb) ? 1 : 0;
+    const int live = st.m != -INFINITY ? 1 : 0;
+    if (live) {
+      Mw = merge_factors(Mw, st.m, fa, fb);
+      Lw = merge_o(Lw, st.l, fa, fb);
+    }
     float ga[4], gb[4];
     int gl[4];
 #pragma unroll
@@ -1078,14 +1082,24 @@ __global__ void __launch_bounds__(kAttnThreads) attn_merge_kernel(AttnArgs a, in
       lc[i] = P[c].l[h];
       oc[i] = *(const float4*)(P[c].o + h * kHeadDim + d0);
     }
+    // the factors of every chunk first (the running maximum needs only the
+    // chunk maxima, so the exponentials are independent), then the sums;
+    // skipped chunks are dropped by selects, not branches
+    bool live[kMergeBatch];
+    float fa[kMergeBatch], fb[kMergeBatch];
 #pragma unroll
     for (int i = 0; i < kMergeBatch; ++i) {
-      float fa, fb;
-      if (c0 + i >= nchunks || !merge_step(M, L, mc[i], lc[i], fa, fb)) continue;
-      acc.x = merge_o(acc.x, oc[i].x, fa, fb);
-      acc.y = merge_o(acc.y, oc[i].y, fa, fb);
-      acc.z = merge_o(acc.z, oc[i].z, fa, fb);
-      acc.w = merge_o(acc.w, oc[i].w, fa, fb);
+      live[i] = c0 + i < nchunks && mc[i] != -INFINITY;
+      const float mn = merge_factors(M, mc[i], fa[i], fb[i]);
+      M = live[i] ? mn : M;
+    }
+#pragma unroll
+    for (int i = 0; i < kMergeBatch; ++i) {
+      L = live[i] ? merge_o(L, lc[i], fa[i], fb[i]) : L;
+      acc.x = live[i] ? merge_o(acc.x, oc[i].x, fa[i], fb[i]) : acc.x;
+      acc.y = live[i] ? merge_o(acc.y, oc[i].y, fa[i], fb[i]) : acc.y;
+      acc.z = live[i] ? merge_o(acc.z, oc[i].z, fa[i], fb[i]) : acc.z;
+      acc.w = live[i] ? merge_o(acc.w, oc[i].w, fa[i], fb[i]) : acc.w;
     }
   }
   const float inv = merge_inv(M, L, sink2);
