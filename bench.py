@@ -16,8 +16,12 @@ HIP events on the stream it runs on.  cpu_baseline times the float64 oracle
 
   python bench.py [--steps K] [--warmup W] [--workload csa_1m_fp8|csa_1m_mxfp4|
                   csa_1m_fp4idx|csa_1m_fp8_layer|csa_1m_fp8_paged|csa2_m1_256k|
-                  csa_64k_bf16|hca_1m_bf16|hca_1m_bf16_paged|csa_prefill_32k_bf16]
-                  [--copies C] [--no-cpu-baseline]
+                  csa_64k_bf16|csa_64k_bf16_b128|hca_1m_bf16|hca_1m_bf16_paged|
+                  csa_prefill_32k_bf16] [--copies C] [--no-cpu-baseline]
+
+csa_64k_bf16_b128 is the 64K workload at batch 128, where the decode attention
+takes one work-group per whole list instead of 64-row chunks and a merge (the
+same bits either way).
 
 The *_paged workloads run the same step from a block cache: entries and index
 keys in pools of blocks (32 CSA entries or 1 HCA entry per block) found
@@ -45,7 +49,7 @@ HBM_PEAK_GBS = 8000.0
 MFMA_BF16_PEAK_TFLOPS = 2500.0
 
 WORKLOADS = {"csa_1m_fp8": 5, "csa_1m_mxfp4": 5, "csa_1m_fp4idx": 5, "csa_1m_fp8_layer": 5,
-             "csa_1m_fp8_paged": 5, "csa2_m1_256k": 6, "csa_64k_bf16": 2,
+             "csa_1m_fp8_paged": 5, "csa2_m1_256k": 6, "csa_64k_bf16": 2, "csa_64k_bf16_b128": 2,
              "hca_1m_bf16": 3, "hca_1m_bf16_paged": 3, "csa_prefill_32k_bf16": 4}
 
 
@@ -54,6 +58,8 @@ METRICS = {
     "csa_1m_fp8": "CSA top-512 decode tokens/s per layer at 1M ctx; achieved HBM GB/s vs peak",
     "csa_64k_bf16": "CSA top-512 decode tokens/s per layer at 64K ctx (bf16 cache); achieved HBM "
                     "GB/s vs peak",
+    "csa_64k_bf16_b128": "CSA top-512 decode tokens/s per layer at 64K ctx (bf16 cache), batch "
+                         "128; achieved HBM GB/s vs peak",
     "hca_1m_bf16": "HCA decode tokens/s per layer at 1M ctx (bf16 cache); achieved HBM GB/s vs "
                    "peak",
     "csa_1m_fp8_layer": "CSA top-512 decode tokens/s per layer at 1M ctx, whole layer (query path, "
@@ -517,6 +523,8 @@ def main():
         w = synth.layer_variant(w)
     if a.workload.endswith("_paged"):
         w = synth.paged_variant(w)
+    if a.workload == "csa_64k_bf16_b128":
+        w = synth.batch_variant(w, 128)
     print(f"# building {a.workload}: B={w.B} ctx={w.ctx} entries={w.n_entries}", file=sys.stderr,
           flush=True)
     t0 = time.time()

@@ -212,7 +212,8 @@ csa_status csa_compress(const csa_compress_args* a, void* ws, size_t ws_bytes,
  * same token).  The result equals calling csa_compress on a[0], ..., a[n-1]
  * in order; the calls must not share state or entries buffers.  When every
  * call is single-token (T == 1) with bf16 x and weights, dim % 256 == 0 and
- * the same B, their projections run as one launch and their emits as another.
+ * the same B <= 1024, their projections run as one launch and their emits as
+ * another.  A sequence's entries and slot state do not depend on B.
  * n in [1, 4].  Workspace: csa_compress_many_workspace_size(a, n) bytes
  * (16-byte aligned); errors as for csa_compress, reported for the first
  * failing call before anything is enqueued.                             */

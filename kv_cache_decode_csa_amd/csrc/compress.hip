@@ -194,12 +194,17 @@ __global__ void __launch_bounds__(kProjThreads) proj_mfma_kernel(const uint16_t*
 }
 
 // Single-token (decode) projection split over K: work-group (column block,
-// k slice ks) is one wave that takes 16 weight rows over k in [ks K/8,
-// (ks+1) K/8) -- all of its loads in flight together -- and writes the 16x16
-// partial products to part[ks][m][n].  The emit kernel adds the eight slices
-// in order, the same summation as the one-work-group projection above.
+// k slice ks, block of 64 token rows) is one wave that takes 16 weight rows
+// over k in [ks K/8, (ks+1) K/8) -- all of its loads in flight together -- and
+// writes the 16 x (up to 64) partial products to part[ks][m][n].  The emit
+// kernel adds the eight slices in order, the same summation as the
+// one-work-group projection above.  Batches of more than 64 tokens take
+// several row blocks, each streaming the weights again (through L2 when the
+// row blocks of a column block run together).
 constexpr int kKSlices = 8;
-constexpr int kMaxJobs = 4;  // compressors fused into one launch
+constexpr int kMaxJobs = 4;       // compressors fused into one launch
+constexpr int kSliceRows = 64;    // token rows per work-group
+constexpr int kSliceMaxM = 1024;  // larger single-token batches take the tiled GEMM
 
 struct ProjJob {
   const uint16_t* x;    // [M][K] bf16
@@ -228,6 +233,7 @@ __global__ void __launch_bounds__(64) proj_slice_kernel(ProjJobs jobs, int M) {
   const int N = 2 * CD;
   const int cb = (int)blockIdx.x - J.blk0;
   const int n = cb * 16 + r16;
+  const int m0 = (int)blockIdx.z * kSliceRows;  // this work-group's token rows
   const uint16_t* wrow = n < CD ? J.wkv + (int64_t)n * K : J.wg + (int64_t)(n - CD) * K;
   constexpr int kB = MT <= 2 ? 16 : 8;
   const int nks = K / 256;
@@ -245,7 +251,7 @@ __global__ void __launch_bounds__(64) proj_slice_kernel(ProjJobs jobs, int M) {
       bw[u] = *(const u32x4_t*)(wrow + k);
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
-        const int m = 16 * mt + r16 < M ? 16 * mt + r16 : M - 1;
+        const int m = m0 + 16 * mt + r16 < M ? m0 + 16 * mt + r16 : M - 1;
         ax[u][mt] = *(const u32x4_t*)(x + (int64_t)m * K + k);
       }
     }
@@ -254,7 +260,7 @@ __global__ void __launch_bounds__(64) proj_slice_kernel(ProjJobs jobs, int M) {
       const bool step_ok = ks0 + u < nks;
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
-        const u32x4_t av = (step_ok && 16 * mt + r16 < M) ? ax[u][mt] : u32x4_t{0u, 0u, 0u, 0u};
+        const u32x4_t av = (step_ok && m0 + 16 * mt + r16 < M) ? ax[u][mt] : u32x4_t{0u, 0u, 0u, 0u};
         acc[mt] = mfma16x16x32(as_bf16x8(av), as_bf16x8(bw[u]), acc[mt]);
       }
     }
@@ -264,7 +270,7 @@ __global__ void __launch_bounds__(64) proj_slice_kernel(ProjJobs jobs, int M) {
   for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const int m = 16 * mt + 4 * (lane >> 4) + r;
+      const int m = m0 + 16 * mt + 4 * (lane >> 4) + r;
       if (m < M) dst[(int64_t)m * N] = acc[mt][r];
     }
 }
@@ -1072,10 +1078,17 @@ static bool use_mfma_proj(const csa_compress_args* a) {
   return a->x_fmt == CSA_BF16 && a->w_fmt == CSA_BF16 && M <= kMfmaMaxM && a->dim % 256 == 0;
 }
 
+// Single-token calls with bf16 operands take the K-sliced projection and the
+// single-token emit.
+static bool use_t1_slices(const csa_compress_args* a) {
+  return a->T == 1 && a->x_fmt == CSA_BF16 && a->w_fmt == CSA_BF16 && a->dim % 256 == 0 &&
+         (int64_t)a->B <= kSliceMaxM;
+}
+
 size_t compress_ws_bytes(const csa_compress_args* a) {
   const int coff = a->ratio == 4 ? 2 : 1;
   const int CD = coff * a->head_dim;
-  if (a->T == 1 && use_mfma_proj(a)) {  // per-slice partial products
+  if (use_t1_slices(a)) {  // per-slice partial products
     size_t b = align_up((size_t)kKSlices * a->B * 2 * CD * sizeof(float), 256);
     if (a->ratio == 128)  // pooled rows and slice sums of squares
       b += align_up((size_t)a->B * a->head_dim * sizeof(float), 256) +
@@ -1125,7 +1138,7 @@ static CompArgs comp_args(const csa_compress_args* in, float* P) {
 static bool fusable(const csa_compress_args* in, int n) {
   if (n < 1 || n > kMaxJobs) return false;
   for (int i = 0; i < n; ++i)
-    if (in[i].T != 1 || !use_mfma_proj(&in[i]) || in[i].B != in[0].B ||
+    if (!use_t1_slices(&in[i]) || in[i].B != in[0].B ||
         (n > 1 && in[i].ratio == 128))
       return false;
   return true;
@@ -1150,8 +1163,8 @@ static hipError_t launch_fused_t1(const csa_compress_args* in, int n, void* ws, 
   }
   pj.n = n;
   const int M = in[0].B;
-  const int mt = (M + 15) / 16;
-  const dim3 grid(blocks, kKSlices);
+  const int mt = M >= kSliceRows ? 4 : (M + 15) / 16;
+  const dim3 grid(blocks, kKSlices, (M + kSliceRows - 1) / kSliceRows);
   if (mt == 1) hipLaunchKernelGGL(proj_slice_kernel<1>, grid, dim3(64), 0, s, pj, M);
   else if (mt == 2) hipLaunchKernelGGL(proj_slice_kernel<2>, grid, dim3(64), 0, s, pj, M);
   else if (mt == 3) hipLaunchKernelGGL(proj_slice_kernel<3>, grid, dim3(64), 0, s, pj, M);
@@ -1192,7 +1205,7 @@ hipError_t launch_compress_many(const csa_compress_args* in, int n, void* ws, hi
 }
 
 hipError_t launch_compress(const csa_compress_args* in, void* ws, hipStream_t s) {
-  if (in->T == 1 && use_mfma_proj(in)) return launch_fused_t1(in, 1, ws, s);
+  if (use_t1_slices(in)) return launch_fused_t1(in, 1, ws, s);
   CompArgs a = comp_args(in, (float*)ws);
   float* P = (float*)ws;
   const int64_t M = (int64_t)in->B * in->T;

@@ -109,6 +109,13 @@ def fp4_indexer_variant(w):
     return dataclasses.replace(w, name="csa_1m_fp4idx", key_fmt="fp4_mx32")
 
 
+def batch_variant(w, B):
+    """The same workload at another batch size (each sequence's data depends
+    only on its own index, so the first sequences are the base workload's)."""
+    import dataclasses
+    return dataclasses.replace(w, name=f"{w.name}_b{B}", B=B)
+
+
 def paged_variant(w):
     """The same workload served from a block cache ("DeepSeek-V4 deep dive"
     section 9.4): entries and index keys in a pool of blocks of one 128-token

@@ -85,6 +85,19 @@ def test_csa2_and_layer_bytes():
         + 8 * 4096 * 2
 
 
+def test_batch_variant_scales_bytes_and_keeps_sequences():
+    """The batch-128 variant of the 64K workload: the same per-sequence bytes,
+    128 sequences, and the base workload's seeded data for its first ones."""
+    base = synth.WORKLOADS[2]
+    big = synth.batch_variant(base, 128)
+    assert big.B == 128 and big.name == "csa_64k_bf16_b128" and big.seed == base.seed
+    assert per_seq_read_bytes(big) == per_seq_read_bytes(base)
+    assert "csa_64k_bf16_b128" in bench.WORKLOADS and big.name in bench.METRICS
+    a = synth.normal_batched(base.seed, 3, base.B, (2, 4))
+    b = synth.normal_batched(big.seed, 3, big.B, (2, 4))
+    assert (a == b[:base.B]).all()
+
+
 def test_multi_gpu_is_refused():
     r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
                        capture_output=True, text=True, timeout=120)

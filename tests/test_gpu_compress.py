@@ -229,6 +229,39 @@ def test_compress_many_equals_separate_calls(tables):
         assert torch.equal(gf.sc, gs.sc)
 
 
+@pytest.mark.parametrize("ratio,d,rotate,efmt", [(4, 512, 0, "fp8_mx32"), (4, 128, 1, "fp8_mx32"),
+                                                (128, 512, 0, "bf16")])
+def test_decode_large_batch_equals_sub_batches(tables, ratio, d, rotate, efmt):
+    """Single-token calls for 130 sequences (the projection then spans three
+    64-row blocks) leave exactly the entries and slot state that the same
+    sequences leave in calls of 10, over steps that complete blocks: a
+    sequence's result does not depend on its batch."""
+    B, sub, dim = 130, 10, 512
+    rng = np.random.default_rng(ratio * 1000 + d)
+    wkv, wg, ape = (synth.bf16_round(w) for w in weights(rng, dim, d, ratio))
+    base = 40 if ratio == 4 else 120
+    start = (base + rng.integers(0, 2 * ratio if ratio == 4 else 12, size=B)).astype(np.int32)
+    cap = 32 if ratio == 4 else 4
+    big = GpuCompressor(B, dim, ratio, d, rotate, wkv, wg, ape, "bf16", efmt, cap, tables)
+    smalls = [GpuCompressor(min(sub, B - b0), dim, ratio, d, rotate, wkv, wg, ape, "bf16", efmt,
+                            cap, tables) for b0 in range(0, B, sub)]
+    say(f"compress large batch ratio={ratio} d={d} {efmt}: B={B} against calls of {sub}")
+    for step in range(6):
+        x = synth.bf16_round(rng.standard_normal((B, 1, dim)).astype(np.float32))
+        pos = start + step
+        big(x, pos)
+        for i, g in enumerate(smalls):
+            g(x[i * sub:i * sub + g.B], pos[i * sub:i * sub + g.B])
+    done = 0
+    for i, g in enumerate(smalls):
+        b0, b1 = i * sub, i * sub + g.B
+        assert torch.equal(big.entries[b0:b1], g.entries), i
+        assert torch.equal(big.kv[b0:b1], g.kv), i
+        assert torch.equal(big.sc[b0:b1].view(torch.int32), g.sc.view(torch.int32)), i
+        done += int((g.entries != 0).any(dim=2).sum())
+    assert done > 0  # some blocks completed
+
+
 @pytest.mark.parametrize("entry_fmt", ["bf16", "fp8_mx32"])
 def test_hca_decode_steps_bf16(tables, entry_fmt):
     """Single-token calls of the 128-token compressor across block boundaries
