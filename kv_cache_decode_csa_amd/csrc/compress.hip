@@ -275,6 +275,81 @@ __global__ void __launch_bounds__(64) proj_slice_kernel(ProjJobs jobs, int M) {
     }
 }
 
+// The same products for batches of more than 64 tokens: one wave per (64
+// output columns, K/8 slice, 64 token rows) with 4 x 4 MFMA tiles per k-step,
+// so each x fragment it loads serves four column tiles (a quarter of the x
+// reads of the 16-column form).  Every output takes the same MFMA steps in
+// the same order as in proj_slice_kernel, so the two give the same bits.
+// Job column blocks (blk0) count 64-column blocks here (2 CD is a multiple of
+// 64: head dims are 128 or 512).
+__global__ void __launch_bounds__(64) proj_slice_wide_kernel(ProjJobs jobs, int M) {
+  int jb = 0;
+#pragma unroll
+  for (int q = 1; q < kMaxJobs; ++q)
+    if (q < jobs.n && (int)blockIdx.x >= jobs.j[q].blk0) jb = q;
+  const ProjJob& J = jobs.j[jb];
+  const int K = J.K, CD = J.CD;
+  const int N = 2 * CD;
+  const int lane = threadIdx.x;
+  const int r16 = lane & 15, kq = lane >> 4;
+  const int cb = (int)blockIdx.x - J.blk0;      // 64-column block
+  const int m0 = (int)blockIdx.z * kSliceRows;  // this work-group's token rows
+  const uint16_t* wrow[4];
+  const uint16_t* xrow[4];
+  bool mok[4];
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    const int n = 64 * cb + 16 * t + r16;
+    wrow[t] = n < CD ? J.wkv + (int64_t)n * K : J.wg + (int64_t)(n - CD) * K;
+    const int m = m0 + 16 * t + r16;
+    mok[t] = m < M;
+    xrow[t] = J.x + (int64_t)(m < M ? m : M - 1) * K;
+  }
+  constexpr int kB = 4;
+  const int nks = K / 256;
+  const int kb = blockIdx.y * (K / kKSlices);
+  f32x4_t acc[4][4];
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt) acc[mt][nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  for (int ks0 = 0; ks0 < nks; ks0 += kB) {
+    u32x4_t bw[kB][4], ax[kB][4];
+#pragma unroll
+    for (int u = 0; u < kB; ++u) {
+      const int ks = ks0 + u < nks ? ks0 + u : nks - 1;
+      const int k = kb + 32 * ks + 8 * kq;
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        bw[u][t] = *(const u32x4_t*)(wrow[t] + k);
+        ax[u][t] = *(const u32x4_t*)(xrow[t] + k);
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);  // every load of the step group issued first
+#pragma unroll
+    for (int u = 0; u < kB; ++u) {
+      const bool step_ok = ks0 + u < nks;
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) {
+        const u32x4_t av = (step_ok && mok[mt]) ? ax[u][mt] : u32x4_t{0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt)
+          acc[mt][nt] = mfma16x16x32(as_bf16x8(av), as_bf16x8(bw[u][nt]), acc[mt][nt]);
+      }
+    }
+  }
+  float* dst = J.part + (int64_t)blockIdx.y * M * N + 64 * cb + (lane & 15);
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int m = m0 + 16 * mt + 4 * (lane >> 4) + r;
+      if (m >= M) continue;
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt) dst[(int64_t)m * N + 16 * nt] = acc[mt][nt][r];
+    }
+}
+
 // Many-token (prefill) projection on MFMA: P[m][n] = sum_k x[m][k] W[n][k]
 // with bf16 operands and float32 accumulation; x and W are both k-contiguous,
 // so each operand row is read straight in the MFMA operand layout.  A
@@ -1163,12 +1238,25 @@ static hipError_t launch_fused_t1(const csa_compress_args* in, int n, void* ws, 
   }
   pj.n = n;
   const int M = in[0].B;
-  const int mt = M >= kSliceRows ? 4 : (M + 15) / 16;
-  const dim3 grid(blocks, kKSlices, (M + kSliceRows - 1) / kSliceRows);
-  if (mt == 1) hipLaunchKernelGGL(proj_slice_kernel<1>, grid, dim3(64), 0, s, pj, M);
-  else if (mt == 2) hipLaunchKernelGGL(proj_slice_kernel<2>, grid, dim3(64), 0, s, pj, M);
-  else if (mt == 3) hipLaunchKernelGGL(proj_slice_kernel<3>, grid, dim3(64), 0, s, pj, M);
-  else hipLaunchKernelGGL(proj_slice_kernel<4>, grid, dim3(64), 0, s, pj, M);
+  if (M > kSliceRows) {  // several row blocks: the 64-column form
+    ProjJobs pw = pj;
+    int wblocks = 0;
+    for (int i = 0; i < n; ++i) {
+      pw.j[i].blk0 = wblocks;
+      wblocks += 2 * pj.j[i].CD / 64;
+    }
+    for (int i = n; i < kMaxJobs; ++i) pw.j[i] = pw.j[0];
+    hipLaunchKernelGGL(proj_slice_wide_kernel,
+                       dim3(wblocks, kKSlices, (M + kSliceRows - 1) / kSliceRows), dim3(64), 0, s,
+                       pw, M);
+  } else {
+    const int mt = (M + 15) / 16;
+    const dim3 grid(blocks, kKSlices);
+    if (mt == 1) hipLaunchKernelGGL(proj_slice_kernel<1>, grid, dim3(64), 0, s, pj, M);
+    else if (mt == 2) hipLaunchKernelGGL(proj_slice_kernel<2>, grid, dim3(64), 0, s, pj, M);
+    else if (mt == 3) hipLaunchKernelGGL(proj_slice_kernel<3>, grid, dim3(64), 0, s, pj, M);
+    else hipLaunchKernelGGL(proj_slice_kernel<4>, grid, dim3(64), 0, s, pj, M);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (n == 1 && in[0].ratio == 128) {  // pooling over 128 slots: split by channels
