@@ -1056,7 +1056,7 @@ __global__ void __launch_bounds__(kAttnThreads) attn_mfma_kernel(AttnArgs a, int
 constexpr int kMergeBatch = 16;
 static_assert(kMergeChunks <= kMergeBatch, "a dense list merges in one round");
 
-__global__ void __launch_bounds__(kAttnThreads) attn_merge_kernel(AttnArgs a, int nchunks,
+__global__ void __launch_bounds__(kAttnThreads, 4) attn_merge_kernel(AttnArgs a, int nchunks,
                                                                   const Partial* part) {
   const int tid = threadIdx.x;
   const int64_t unit = a.unit_off + blockIdx.y;
