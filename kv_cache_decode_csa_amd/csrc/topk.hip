@@ -817,7 +817,7 @@ hipError_t launch_topk_select(const float* scores, const int32_t* n_valid, int64
                               int topk, int32_t* out_idx, TopkWs w, hipStream_t s) {
   static_assert(sizeof(RowInfo) <= 32, "row info slot");
   // at least kCollectWgs work-groups where the rows allow it
-  constexpr int64_t kCollectWgs = 256;
+  constexpr int64_t kCollectWgs = 512;
   int ch = kChunk;
   while (ch > kChunk / 4 && R * ((ld + ch - 1) / ch) < kCollectWgs) ch >>= 1;
   const int64_t gx = (ld + ch - 1) / ch;
