@@ -19,6 +19,7 @@ namespace csa {
 namespace {
 
 constexpr int kThreads = 256;
+constexpr int kEmitT1Threads = 512;  // single-token emit: one channel per thread at d = 512
 
 // Orders one wave's LDS accesses (LDS operations of a wave execute in order).
 __device__ __forceinline__ void wave_lds_sync() {
@@ -622,19 +623,23 @@ __device__ float pool_block(const CompArgs& a, int64_t b, int64_t st, int64_t p0
 }
 
 // Norm weights and rotation factors at position i * r of this thread's
-// channels (d <= 512 = 2 kThreads).
-struct NormRope {
-  float gw[2], gp[2], cs[2], sn[2];
+// channels (d <= 512 = kPer TT, for work-groups of TT threads).
+template <int TT = kThreads>
+struct NormRopeT {
+  static constexpr int kPer = 512 / TT;
+  float gw[kPer], gp[kPer], cs[kPer], sn[kPer];
 };
-__device__ __forceinline__ NormRope load_norm_rope(const CompArgs& a, int64_t i) {
+using NormRope = NormRopeT<>;
+template <int TT = kThreads>
+__device__ __forceinline__ NormRopeT<TT> load_norm_rope(const CompArgs& a, int64_t i) {
   const int tid = threadIdx.x;
   const int d = a.d;
   int64_t rrow = i * a.ratio;
   rrow = rrow < 0 ? 0 : (rrow >= a.rope_rows ? a.rope_rows - 1 : rrow);
-  NormRope f;
+  NormRopeT<TT> f;
 #pragma unroll
-  for (int u = 0; u < 2; ++u) {
-    const int c = tid + u * kThreads;
+  for (int u = 0; u < NormRopeT<TT>::kPer; ++u) {
+    const int c = tid + u * TT;
     f.gw[u] = f.gp[u] = f.cs[u] = 1.f;
     f.sn[u] = 0.f;
     if (c < d) {
@@ -654,20 +659,25 @@ __device__ __forceinline__ NormRope load_norm_rope(const CompArgs& a, int64_t i)
 // the pooled block in y; writes entry i of sequence b.  z: LDS scratch of d
 // floats; f: load_norm_rope(a, i), fetched early so that its latency overlaps
 // earlier work.
+template <int TT = kThreads>
 __device__ void finish_block(const CompArgs& a, int64_t b, int64_t i, float* y, float* z,
-                             float* red, float sq, const NormRope& f) {
+                             float* red, float sq, const NormRopeT<TT>& f) {
+  static_assert(TT == 256 || TT == 512, "4 or 8 waves");
+  constexpr int kPer = NormRopeT<TT>::kPer;
   const int tid = threadIdx.x;
   const int d = a.d;
-  const float (&gw)[2] = f.gw, (&gp)[2] = f.gp, (&cs)[2] = f.cs, (&sn)[2] = f.sn;
+  const float (&gw)[kPer] = f.gw, (&gp)[kPer] = f.gp, (&cs)[kPer] = f.cs, (&sn)[kPer] = f.sn;
   sq = wave_sum(sq);
   if ((tid & 63) == 0) red[tid >> 6] = sq;
   __syncthreads();
-  const float ms = ((red[0] + red[1]) + (red[2] + red[3])) / (float)d;
+  float ss = (red[0] + red[1]) + (red[2] + red[3]);  // wave sums, pairwise in a fixed order
+  if (TT == 512) ss = ss + ((red[4] + red[5]) + (red[6] + red[7]));
+  const float ms = ss / (float)d;
   const float inv = 1.0f / sqrtf(ms + a.eps);
   // normalise, and rotate the last 64 dims at position i * r (pairs 2k, 2k+1)
 #pragma unroll
-  for (int u = 0; u < 2; ++u) {
-    const int c = tid + u * kThreads;
+  for (int u = 0; u < kPer; ++u) {
+    const int c = tid + u * TT;
     if (c >= d) continue;
     const float v = y[c] * inv * gw[u];
     float out = v;
@@ -684,7 +694,7 @@ __device__ void finish_block(const CompArgs& a, int64_t b, int64_t i, float* y, 
     const bool one_wave = d <= 128;
     if (!one_wave || tid < 64) {
       for (int h = 1; h < d; h <<= 1) {
-        for (int q = tid; q < d / 2; q += kThreads) {
+        for (int q = tid; q < d / 2; q += TT) {
           const int lo = (q / h) * 2 * h + (q % h);
           const float u = z[lo], v = z[lo + h];
           z[lo] = u + v;
@@ -695,17 +705,17 @@ __device__ void finish_block(const CompArgs& a, int64_t b, int64_t i, float* y, 
     }
     if (one_wave) __syncthreads();
     const float sc = 1.0f / sqrtf((float)d);
-    for (int c = tid; c < d; c += kThreads) z[c] *= sc;
+    for (int c = tid; c < d; c += TT) z[c] *= sc;
     __syncthreads();
   }
   uint8_t* row = entry_row(a, b, i);
   if (row == nullptr) return;
   if (a.entry_fmt == CSA_F32) {
-    for (int c = tid; c < d; c += kThreads) ((float*)row)[c] = z[c];
+    for (int c = tid; c < d; c += TT) ((float*)row)[c] = z[c];
   } else if (a.entry_fmt == CSA_BF16) {
-    for (int c = tid; c < d; c += kThreads) ((uint16_t*)row)[c] = f32_to_bf16(z[c]);
+    for (int c = tid; c < d; c += TT) ((uint16_t*)row)[c] = f32_to_bf16(z[c]);
   } else {
-    for (int c0 = 0; c0 < d; c0 += kThreads) {  // uniform trip count: whole waves call
+    for (int c0 = 0; c0 < d; c0 += TT) {  // uniform trip count: whole waves call
       const int c = c0 + tid;
       const bool live = c < d;
       store_elem(a.entry_fmt, live ? z[c] : 0.f, c, d, live, row);
@@ -813,20 +823,21 @@ __global__ void __launch_bounds__(kThreads) state_kernel(CompArgs a) {
 // 8 slots of its channels, and the norm weights and rotation factors of the
 // block the token belongs to -- is loaded in one round, so the load phase is
 // one round of memory latency.
+template <int TT>
 __device__ void emit_t1_overlap(const CompArgs& a, int64_t b, int64_t st, int64_t p0, float* y,
                                 float* z, float* red) {
   const int r = 4, d = a.d, CD = a.CD, tid = threadIdx.x;
   const int N = 2 * CD;
   const int64_t sb = st * (int64_t)(2 * r) * CD;
-  const NormRope nr = load_norm_rope(a, p0 < 0 ? 0 : p0 / r);
-  constexpr int kPer = 2;  // channels per thread (d <= 512 = 2 kThreads)
+  const NormRopeT<TT> nr = load_norm_rope<TT>(a, p0 < 0 ? 0 : p0 / r);
+  constexpr int kPer = NormRopeT<TT>::kPer;  // channels per thread (d <= 512 = kPer TT)
   float pv[kPer][2][kKSlices], ps[kPer][2][kKSlices];  // slices of v and score, halves 0/1
   float ap[kPer][2][4];                                 // slot bias rows 0..3
   float sv[kPer][8], ssc[kPer][8];                      // slots 0..7 at their pooled column
   float c4v[kPer][4], c4s[kPer][4];                     // slots 4..7 at column c (shift)
 #pragma unroll
   for (int u = 0; u < kPer; ++u) {
-    const int c = tid + u * kThreads < d ? tid + u * kThreads : d - 1;
+    const int c = tid + u * TT < d ? tid + u * TT : d - 1;
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       const float* pp = a.P + b * (int64_t)N + c + h * d;
@@ -857,7 +868,7 @@ __device__ void emit_t1_overlap(const CompArgs& a, int64_t b, int64_t st, int64_
   float sq = 0.f;
 #pragma unroll
   for (int u = 0; u < kPer; ++u) {
-    const int c = tid + u * kThreads;
+    const int c = tid + u * TT;
     if (c >= d) continue;
     float nv[2], nsc[2];
 #pragma unroll
@@ -915,17 +926,18 @@ __device__ void emit_t1_overlap(const CompArgs& a, int64_t b, int64_t st, int64_
     sq = fmaf(C, C, sq);
   }
   if (!done) return;
-  finish_block(a, b, p0 / r, y, z, red, sq, nr);
+  finish_block<TT>(a, b, p0 / r, y, z, red, sq, nr);
 }
 
 struct CompJobs {
   CompArgs c[kMaxJobs];
 };
 
-__global__ void __launch_bounds__(kThreads) emit_t1_kernel(CompJobs jobs) {
+template <int TT>
+__global__ void __launch_bounds__(TT) emit_t1_kernel(CompJobs jobs) {
   __shared__ float y[512];
   __shared__ float z[512];
-  __shared__ float red[4];
+  __shared__ float red[TT / 64];
   const CompArgs& a = jobs.c[blockIdx.y];
   const int64_t b = blockIdx.x;
   const int64_t p0 = a.start_pos[b];
@@ -937,7 +949,7 @@ __global__ void __launch_bounds__(kThreads) emit_t1_kernel(CompJobs jobs) {
   if (st < 0) return;
   const int64_t sb = st * (int64_t)nslots * a.CD;
   if (a.coff == 2) {  // ratio 4 with overlap: 8 slots
-    emit_t1_overlap(a, b, st, p0, y, z, red);
+    emit_t1_overlap<TT>(a, b, st, p0, y, z, red);
     return;
   }
   if (p0 < 0) return;
@@ -946,7 +958,7 @@ __global__ void __launch_bounds__(kThreads) emit_t1_kernel(CompJobs jobs) {
   const int64_t i = p0 / r;
   const float* apr = a.ape + (int64_t)(p0 % r) * a.CD;
   float sq = 0.f;
-  for (int c = tid; c < d; c += kThreads) {
+  for (int c = tid; c < d; c += TT) {
     // new token: columns c (and d + c with overlap) of v and of the score
     float nv[2], nsc[2];
     const int halves = a.coff;
@@ -1037,7 +1049,7 @@ __global__ void __launch_bounds__(kThreads) emit_t1_kernel(CompJobs jobs) {
     sq = fmaf(C, C, sq);
   }
   if (!done) return;
-  finish_block(a, b, i, y, z, red, sq, load_norm_rope(a, i));
+  finish_block<TT>(a, b, i, y, z, red, sq, load_norm_rope<TT>(a, i));
 }
 
 // ---- single-token calls of the 128-token (no overlap) compressor
@@ -1271,7 +1283,7 @@ static hipError_t launch_fused_t1(const csa_compress_args* in, int n, void* ws, 
                        (const float*)ybuf, (const float*)sqbuf);
     return hipGetLastError();
   }
-  hipLaunchKernelGGL(emit_t1_kernel, dim3(M, n), dim3(kThreads), 0, s, cj);
+  hipLaunchKernelGGL(emit_t1_kernel<kEmitT1Threads>, dim3(M, n), dim3(kEmitT1Threads), 0, s, cj);
   return hipGetLastError();
 }
 
