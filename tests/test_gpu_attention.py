@@ -234,6 +234,52 @@ def test_batch_invariant_whole_lists(tables, efmt, wfmt, k, H, B):
         close_bf16(got[b, 0], ref)
 
 
+def test_batch_invariant_whole_lists_multi_query(tables):
+    """Three queries per sequence (consecutive positions, as in speculative
+    decoding): 22 sequences x 3 queries x 4 head groups take one work-group
+    per list, pairs of sequences take 64-row chunks and the merge; the same
+    bits either way, and the oracle's values."""
+    cos, sin = tables
+    B, Q, H, N, k, sub = 22, 3, 64, 700, 300, 2
+    rng = np.random.default_rng(4321)
+    q = synth.bf16_round(rng.standard_normal((B, Q, H, 512)).astype(np.float32))
+    win = rng.standard_normal((B, 128, 512)).astype(np.float32)
+    ent = rng.standard_normal((B, N, 512)).astype(np.float32)
+    sink = rng.standard_normal(H).astype(np.float32)
+    p0 = rng.integers(130, 4 * N, size=B).astype(np.int32)
+    pos = (p0[:, None] + np.arange(Q, dtype=np.int32)[None]).astype(np.int32)
+    ids = np.stack([np.stack([gen_ids(rng, min((int(p) + 1) // 4, N), k, N) for p in pos[b]])
+                    for b in range(B)])
+    assert _lib.csa_sparse_attn_workspace_size(B, Q, H, k) <= 1
+    assert _lib.csa_sparse_attn_workspace_size(sub, Q, H, k) > 1
+    say(f"batch invariance, {Q} queries per sequence: B={B} against sub-batches of {sub}")
+    qd, wd, ed = bf16(q), upload_rows(win, "fp8_mx32"), upload_rows(ent, "fp8_mx32")
+    idd, pd, sd = i32(ids), i32(pos), f32(sink)
+
+    def run(b0, b1):
+        n = b1 - b0
+        sl = [t[b0:b1].clone() for t in (qd, wd, ed, idd, pd)]
+        out = torch.empty((n, Q, H, 512), dtype=torch.bfloat16, device="cuda")
+        ws = _lib.workspace(_lib.csa_sparse_attn_workspace_size(n, Q, H, k))
+        _lib.csa_sparse_attn_decode(sl[0], "bf16", sl[1], "fp8_mx32", _lib.WIN_RING128, None, 128,
+                                    sl[2], "fp8_mx32", N, sl[3], k, sl[4], n, Q, H, sd,
+                                    512 ** -0.5, cos, sin, out, "bf16", ws)
+        return out
+
+    whole = run(0, B)
+    split = torch.cat([run(b0, min(b0 + sub, B)) for b0 in range(0, B, sub)])
+    torch.cuda.synchronize()
+    assert torch.equal(whole.view(torch.int16), split.view(torch.int16))
+    got = to_np(whole)
+    winv = codec.store(win[[0, B - 1]], "fp8_mx32")[1]
+    entv = codec.store(ent[[0, B - 1]], "fp8_mx32")[1]
+    for i, b in enumerate([0, B - 1]):
+        for qq in range(Q):
+            ref = oracle_sparse(q[b, qq].astype(np.float64), winv[i], entv[i], ids[b, qq], sink,
+                                int(pos[b, qq]))
+            close_bf16(got[b, qq], ref)
+
+
 @pytest.mark.parametrize("efmt", ["bf16", "fp8_mx32", "fp4_e4m3_16", "mix576"])
 def test_hca_decode(tables, efmt):
     cos, sin = tables
