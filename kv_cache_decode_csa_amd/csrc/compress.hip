@@ -1055,14 +1055,18 @@ __global__ void __launch_bounds__(TT) emit_t1_kernel(CompJobs jobs) {
 // ---- single-token calls of the 128-token (no overlap) compressor
 // Pass 1, work-group (sequence b, 64-channel slice): the new token's slot from
 // the projection slices (score plus slot bias); if the token completes a
-// block, 4 threads per channel pool 32 slots each -- all of their loads in
-// flight together -- and the 4 partial softmax sums are merged in order.
+// block, 8 threads per channel pool 16 slots each -- all of their loads in
+// flight together -- and the 8 partial softmax sums are merged in order.
 // Writes the pooled channels and the slice's sum of squares.
 constexpr int kPoolChannels = 64;
+constexpr int kPoolGroups = 8;                  // slot groups: one wave each
+constexpr int kPoolSlots = 128 / kPoolGroups;   // slots per thread
+constexpr int kPoolThreads = 64 * kPoolGroups;
 
-__global__ void __launch_bounds__(kThreads) pool128_t1_kernel(CompJobs jobs, float* ybuf,
+__global__ void __launch_bounds__(kPoolThreads) pool128_t1_kernel(CompJobs jobs, float* ybuf,
                                                                 float* sqbuf) {
-  __shared__ float pm[4][kPoolChannels], pl[4][kPoolChannels], pa[4][kPoolChannels];
+  __shared__ float pm[kPoolGroups][kPoolChannels], pl[kPoolGroups][kPoolChannels],
+      pa[kPoolGroups][kPoolChannels];
   const CompArgs& a = jobs.c[0];
   const int64_t b = blockIdx.x;
   const int slice = blockIdx.y;
@@ -1077,7 +1081,7 @@ __global__ void __launch_bounds__(kThreads) pool128_t1_kernel(CompJobs jobs, flo
   const int c = slice * kPoolChannels + cl;
   const int N = 2 * a.CD;
   const int64_t sb = st * (int64_t)r * a.CD;
-  const bool own = (ns >> 5) == g;          // this slot group holds the new token
+  const bool own = ns / kPoolSlots == g;     // this slot group holds the new token
   float nv = 0.f, nsc = 0.f;
   if (own) {
     const float* pp = a.P + b * (int64_t)N + c;
@@ -1093,17 +1097,17 @@ __global__ void __launch_bounds__(kThreads) pool128_t1_kernel(CompJobs jobs, flo
     a.score_state[sb + (int64_t)ns * a.CD + c] = nsc;
   }
   if (!done) return;
-  float vv[32], ss[32];
+  float vv[kPoolSlots], ss[kPoolSlots];
 #pragma unroll
-  for (int j = 0; j < 32; ++j) {
-    const int sl = 32 * g + j;
+  for (int j = 0; j < kPoolSlots; ++j) {
+    const int sl = kPoolSlots * g + j;
     const int64_t si = sb + (int64_t)sl * a.CD + c;
     vv[j] = sl == ns ? nv : a.kv_state[si];
     ss[j] = sl == ns ? nsc : a.score_state[si];
   }
   float m = -INFINITY, l = 0.f, acc = 0.f;
 #pragma unroll
-  for (int j = 0; j < 32; ++j) {
+  for (int j = 0; j < kPoolSlots; ++j) {
     if (ss[j] == -INFINITY) continue;
     const float mn = fmaxf(m, ss[j]);
     const float scl = expf(m - mn);
@@ -1119,10 +1123,10 @@ __global__ void __launch_bounds__(kThreads) pool128_t1_kernel(CompJobs jobs, flo
   if (g != 0) return;
   float M = -INFINITY;
 #pragma unroll
-  for (int q = 0; q < 4; ++q) M = fmaxf(M, pm[q][cl]);
+  for (int q = 0; q < kPoolGroups; ++q) M = fmaxf(M, pm[q][cl]);
   float L = 0.f, A = 0.f;
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
+  for (int q = 0; q < kPoolGroups; ++q) {
     if (pm[q][cl] == -INFINITY) continue;
     const float wq = expf(pm[q][cl] - M);
     L += pl[q][cl] * wq;
@@ -1275,7 +1279,7 @@ static hipError_t launch_fused_t1(const csa_compress_args* in, int n, void* ws, 
     const int CD = in[0].head_dim;
     float* ybuf = (float*)((char*)ws + align_up((size_t)kKSlices * M * 2 * CD * sizeof(float), 256));
     float* sqbuf = (float*)((char*)ybuf + align_up((size_t)M * in[0].head_dim * sizeof(float), 256));
-    hipLaunchKernelGGL(pool128_t1_kernel, dim3(M, in[0].head_dim / kPoolChannels), dim3(kThreads),
+    hipLaunchKernelGGL(pool128_t1_kernel, dim3(M, in[0].head_dim / kPoolChannels), dim3(kPoolThreads),
                        0, s, cj, ybuf, sqbuf);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
