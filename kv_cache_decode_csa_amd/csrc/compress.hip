@@ -1140,25 +1140,26 @@ __global__ void __launch_bounds__(kPoolThreads) pool128_t1_kernel(CompJobs jobs,
 
 // Pass 2, one work-group per sequence whose block completed: RMSNorm -> RoPE
 // -> storage rounding of the pooled row (slice sums of squares added in order).
-__global__ void __launch_bounds__(kThreads) finish128_t1_kernel(CompJobs jobs,
+__global__ void __launch_bounds__(kEmitT1Threads) finish128_t1_kernel(CompJobs jobs,
                                                                   const float* ybuf,
                                                                   const float* sqbuf) {
   __shared__ float y[512];
   __shared__ float z[512];
-  __shared__ float red[4];
+  __shared__ float red[kEmitT1Threads / 64];
   const CompArgs& a = jobs.c[0];
   const int64_t b = blockIdx.x;
   const int64_t p0 = a.start_pos[b];
   if (p0 < 0 || (p0 + 1) % a.ratio != 0 || state_seq(a, b) < 0) return;
   const int tid = threadIdx.x;
-  for (int c = tid; c < a.d; c += kThreads) y[c] = ybuf[b * (int64_t)a.d + c];
+  for (int c = tid; c < a.d; c += kEmitT1Threads) y[c] = ybuf[b * (int64_t)a.d + c];
   float sq = 0.f;
   if (tid == 0) {
     const int ns = a.d / kPoolChannels;
     for (int q = 0; q < ns; ++q) sq += sqbuf[b * ns + q];
   }
   __syncthreads();
-  finish_block(a, b, p0 / a.ratio, y, z, red, sq, load_norm_rope(a, p0 / a.ratio));
+  finish_block<kEmitT1Threads>(a, b, p0 / a.ratio, y, z, red, sq,
+                               load_norm_rope<kEmitT1Threads>(a, p0 / a.ratio));
 }
 
 }  // namespace
@@ -1283,7 +1284,7 @@ static hipError_t launch_fused_t1(const csa_compress_args* in, int n, void* ws, 
                        0, s, cj, ybuf, sqbuf);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(finish128_t1_kernel, dim3(M), dim3(kThreads), 0, s, cj,
+    hipLaunchKernelGGL(finish128_t1_kernel, dim3(M), dim3(kEmitT1Threads), 0, s, cj,
                        (const float*)ybuf, (const float*)sqbuf);
     return hipGetLastError();
   }
