@@ -134,6 +134,22 @@ def test_attention_validation():
                              0.044, A16, A16, 100, A16, 1, A16, ws, None) == EINVAL  # ratio 0
 
 
+def test_attention_workspace_follows_the_work_split():
+    """Decode lists of at most 640 rows take one work-group per list from 256
+    (unit, 16-head group) items on, with no partials (workspace 0); smaller
+    batches split lists into 64-row chunks and need one partial per chunk;
+    16+ queries per sequence take 640-row chunks (one chunk: no partials)."""
+    L = _lib.lib()
+    part = (16 + 16 + 16 * 512) * 4  # m, l, O of one (unit, head group, chunk)
+    assert L.csa_sparse_attn_workspace_size(8, 1, 64, 512) == 8 * 4 * 10 * part
+    assert L.csa_sparse_attn_workspace_size(63, 1, 64, 512) == 63 * 4 * 10 * part
+    assert L.csa_sparse_attn_workspace_size(64, 1, 64, 512) == 0
+    assert L.csa_sparse_attn_workspace_size(32, 1, 128, 512) == 0
+    assert L.csa_sparse_attn_workspace_size(22, 3, 64, 300) == 0
+    assert L.csa_sparse_attn_workspace_size(64, 1, 64, 600) > 0      # 728 rows: chunks
+    assert L.csa_sparse_attn_workspace_size(2, 20, 64, 512) == 0     # one 640-row chunk
+
+
 def test_compress_validation():
     L = _lib.lib()
     a = _lib.CompressArgs(1, 4, 1024, 4, 512, 0, A16, 0, A16, A16, 0, A16, A16, 1e-6, A16, A16,
