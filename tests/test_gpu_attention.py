@@ -181,7 +181,8 @@ def test_csa_many_queries_other_head_counts(tables, H, k):
                                              ("bf16", "bf16", 512, 64, 70),
                                              ("fp4_e4m3_16", "fp8_mx32", 37, 64, 70),
                                              ("mix576", "fp8_mx32", 512, 64, 70),
-                                             ("fp8_mx32", "bf16", 200, 128, 34)])
+                                             ("fp8_mx32", "bf16", 200, 128, 34),
+                                             ("fp8_mx32", "fp8_mx32", 0, 64, 70)])
 def test_batch_invariant_whole_lists(tables, efmt, wfmt, k, H, B):
     """A batch with at least 256 (sequence, 16-head group) items runs one
     work-group per list; a small batch splits each list into 64-row chunks
@@ -203,7 +204,7 @@ def test_batch_invariant_whole_lists(tables, efmt, wfmt, k, H, B):
     sink = rng.standard_normal(H).astype(np.float32)
     # full lists, padded lists (few visible entries) and partial windows
     pos = rng.integers(4 * N - 8, 4 * N + 5000, size=(B, 1)).astype(np.int32)
-    pos[1::7, 0] = rng.integers(100, 4 * k, size=len(pos[1::7]))
+    pos[1::7, 0] = rng.integers(100, max(4 * k, 200), size=len(pos[1::7]))
     ids = np.stack([gen_ids(rng, min((int(pos[b, 0]) + 1) // 4, N), k, N)
                     for b in range(B)]).reshape(B, 1, k)
     say(f"batch invariance {efmt}/{wfmt} k={k} H={H}: B={B} against sub-batches of {sub}")
