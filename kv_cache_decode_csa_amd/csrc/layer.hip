@@ -189,9 +189,12 @@ __device__ __forceinline__ int64_t rope_row(int64_t p, int64_t rows) {
 // RoPE -> stored into ring slot pos mod 128; head weights scaled.  Every load
 // that does not depend on another is issued first, so the kernel waits for
 // memory about twice (the loads, then the rotation factors at the position).
-__global__ void __launch_bounds__(kThreads) layer_in_kernel(InArgs a) {
-  constexpr int kL = kMaxRank / kThreads;
-  __shared__ float red[2][4];
+template <int TT>
+__global__ void __launch_bounds__(TT) layer_in_kernel(InArgs a) {
+  static_assert(TT == 256 || TT == 512, "4 or 8 waves");
+  constexpr int kL = kMaxRank / TT;
+  constexpr int kW = kHeadDim / TT;  // window dims per thread
+  __shared__ float red[2][TT / 64];
   __shared__ float z[kHeadDim];
   const int m = blockIdx.x, tid = threadIdx.x;
   const int64_t stride = (int64_t)a.M * a.ldy;
@@ -200,21 +203,21 @@ __global__ void __launch_bounds__(kThreads) layer_in_kernel(InArgs a) {
   float lv[kL], gq[kL];
 #pragma unroll
   for (int u = 0; u < kL; ++u) {
-    const int c = tid + u * kThreads;
+    const int c = tid + u * TT;
     lv[u] = c < a.QR ? slice_sum(row, a.ks, stride, c) : 0.f;
     gq[u] = c < a.QR ? a.q_norm[c] : 0.f;
   }
-  float v[2], gk[2];
+  float v[kW], gk[kW];
 #pragma unroll
-  for (int u = 0; u < 2; ++u) {
-    v[u] = slice_sum(row, a.ks, stride, a.QR + tid + u * kThreads);
-    gk[u] = a.kv_norm[tid + u * kThreads];
+  for (int u = 0; u < kW; ++u) {
+    v[u] = slice_sum(row, a.ks, stride, a.QR + tid + u * TT);
+    gk[u] = a.kv_norm[tid + u * TT];
   }
   const float wv = tid < a.Hi ? slice_sum(row, a.ks, stride, a.QR + kHeadDim + tid) : 0.f;
-  // rotation factors of this thread's second window dim (the rotated dims
-  // 448..511 are all second dims: tid + 256 >= 448)
+  // rotation factors of this thread's last window dim (the rotated dims
+  // 448..511 are all last dims: tid + (kW - 1) TT >= 448)
   const int64_t rr = rope_row(p, a.rope_rows);
-  const int c1 = tid + kThreads;
+  const int c1 = tid + (kW - 1) * TT;
   float cs = 1.f, sn = 0.f;
   if (c1 >= kHeadDim - kRopeDims) {
     const int k = (c1 - (kHeadDim - kRopeDims)) >> 1;
@@ -225,7 +228,9 @@ __global__ void __launch_bounds__(kThreads) layer_in_kernel(InArgs a) {
   float sq = 0.f;
 #pragma unroll
   for (int u = 0; u < kL; ++u) sq += lv[u] * lv[u];
-  float sk = v[0] * v[0] + v[1] * v[1];
+  float sk = 0.f;
+#pragma unroll
+  for (int u = 0; u < kW; ++u) sk += v[u] * v[u];
   sq = wave_sum(sq);
   sk = wave_sum(sk);
   if ((tid & 63) == 0) {
@@ -233,25 +238,30 @@ __global__ void __launch_bounds__(kThreads) layer_in_kernel(InArgs a) {
     red[1][tid >> 6] = sk;
   }
   __syncthreads();
-  const float inv_q =
-      1.0f / sqrtf(((red[0][0] + red[0][1]) + (red[0][2] + red[0][3])) / (float)a.QR + a.eps);
-  const float inv_k =
-      1.0f / sqrtf(((red[1][0] + red[1][1]) + (red[1][2] + red[1][3])) / (float)kHeadDim + a.eps);
+  // wave sums, pairwise in a fixed order
+  float tq = (red[0][0] + red[0][1]) + (red[0][2] + red[0][3]);
+  float tk = (red[1][0] + red[1][1]) + (red[1][2] + red[1][3]);
+  if (TT == 512) {
+    tq = tq + ((red[0][4] + red[0][5]) + (red[0][6] + red[0][7]));
+    tk = tk + ((red[1][4] + red[1][5]) + (red[1][6] + red[1][7]));
+  }
+  const float inv_q = 1.0f / sqrtf(tq / (float)a.QR + a.eps);
+  const float inv_k = 1.0f / sqrtf(tk / (float)kHeadDim + a.eps);
 #pragma unroll
   for (int u = 0; u < kL; ++u) {
-    const int c = tid + u * kThreads;
+    const int c = tid + u * TT;
     if (c < a.QR) a.qr[(int64_t)m * a.QR + c] = f32_to_bf16(lv[u] * inv_q * gq[u]);
   }
   if (tid < a.Hi) a.w_idx[(int64_t)m * a.Hi + tid] = wv * a.w_scale;
 #pragma unroll
-  for (int u = 0; u < 2; ++u) z[tid + u * kThreads] = v[u] * inv_k * gk[u];
+  for (int u = 0; u < kW; ++u) z[tid + u * TT] = v[u] * inv_k * gk[u];
   __syncthreads();
   if (p < 0) return;
   const int b = m / a.T;
   uint8_t* dst = a.win + ((int64_t)b * kWindow + p % kWindow) * a.win_rb;
 #pragma unroll
-  for (int u = 0; u < 2; ++u) {
-    const int c = tid + u * kThreads;
+  for (int u = 0; u < kW; ++u) {
+    const int c = tid + u * TT;
     float out = z[c];
     if (c >= kHeadDim - kRopeDims) {
       const float pv = z[c ^ 1];
@@ -446,7 +456,7 @@ hipError_t launch_layer_input(const csa_layer_weights* w, const void* x, const i
   ia.win = (uint8_t*)win;
   ia.win_fmt = win_fmt;
   ia.win_rb = win_rb;
-  layer_in_kernel<<<M, kThreads, 0, s>>>(ia);
+  layer_in_kernel<512><<<M, 512, 0, s>>>(ia);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   e = launch_linear(p.b, s);
